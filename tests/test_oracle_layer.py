@@ -1,0 +1,199 @@
+"""Pins for the oracle's layer forward/backward (CPU only).
+
+Independent references: scalar per-token loops in plain Python (brute force),
+the dense SwiGLU MLP as torch CPU computes it (E=1, k=1, w=1), bit-exact
+reproduction of y under one-hot weights, central finite differences, torch
+autograd in fp64, and the two-way router-weight-gradient identity.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import bf16, layer, mxfp8, schedule
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def scalar_silu(v):
+    return v / (1.0 + math.exp(-v))
+
+
+def test_forward_full_brute_force_micro():
+    inp = workloads.make_full_layer("micro")
+    sh = inp["shape"]
+    ref = layer.forward_full(inp)
+    x = bf16.decode(inp["x"]); wg = bf16.decode(inp["w_gate"]); wu = bf16.decode(inp["w_up"])
+    wd = bf16.decode(inp["w_down"])
+    idx, w = ref["topk_idx"], ref["topk_w"]
+    for t in range(sh.T):
+        out = [0.0] * sh.H
+        for j in range(sh.k):
+            e = int(idx[t, j])
+            a = []
+            for i in range(sh.I):
+                g = sum(x[t, h] * wg[e, i, h] for h in range(sh.H))
+                u = sum(x[t, h] * wu[e, i, h] for h in range(sh.H))
+                a.append(scalar_silu(g) * u)
+            for h in range(sh.H):
+                y = sum(a[i] * wd[e, h, i] for i in range(sh.I))
+                out[h] += float(w[t, j]) * y
+        assert np.allclose(ref["out"][t], out, rtol=0, atol=1e-12 * max(1.0, rms(ref["out"])))
+
+
+def test_forward_reduces_to_dense_swiglu_mlp():
+    rng = np.random.default_rng(0)
+    R, H, I = 37, 48, 24
+    inp = {
+        "shape": None,
+        "x": workloads.bf16_bits(rng.standard_normal((R, H)).astype(np.float32)),
+        "w_gate": workloads.bf16_bits(rng.standard_normal((1, I, H)).astype(np.float32) / 7),
+        "w_up": workloads.bf16_bits(rng.standard_normal((1, I, H)).astype(np.float32) / 7),
+        "w_down": workloads.bf16_bits(rng.standard_normal((1, H, I)).astype(np.float32) / 5),
+        "row_expert": np.zeros(R, dtype=np.int32),
+        "row_w": np.ones(R, dtype=np.float32),
+    }
+    out = layer.forward_share(inp)["out"]
+    tx = torch.from_numpy(bf16.decode(inp["x"]))
+    g = tx @ torch.from_numpy(bf16.decode(inp["w_gate"])[0]).T
+    u = tx @ torch.from_numpy(bf16.decode(inp["w_up"])[0]).T
+    y = (torch.nn.functional.silu(g) * u) @ torch.from_numpy(bf16.decode(inp["w_down"])[0]).T
+    assert np.allclose(out, y.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_combine_one_hot_weights_reproduce_y_bitwise():
+    inp = workloads.make_full_layer("tiny")
+    sh = inp["shape"]
+    ref = layer.forward_full(inp)
+    # with one-hot weights the combine is a copy of the chosen expert's row
+    T, k, H = sh.T, sh.k, sh.H
+    yk = ref["y"].reshape(T, k, H)
+    for j in range(k):
+        onehot = np.zeros((T, k), dtype=np.float32); onehot[:, j] = 1.0
+        out = np.zeros((T, H))
+        for jj in range(k):
+            out += onehot[:, jj, None].astype(np.float64) * yk[:, jj]
+        assert np.array_equal(out, yk[:, j])
+
+
+def test_forward_share_invariant_to_schedule_and_rows():
+    """The oracle computes per row; each row's output only depends on that row."""
+    inp = workloads.make_expert_share("micro")
+    ref = layer.forward_share(inp)
+    perm = np.random.default_rng(1).permutation(inp["shape"].R)
+    inp2 = dict(inp)
+    inp2["x"] = inp["x"][perm]; inp2["row_expert"] = inp["row_expert"][perm]; inp2["row_w"] = inp["row_w"][perm]
+    ref2 = layer.forward_share(inp2)
+    assert np.allclose(ref2["out"], ref["out"][perm], rtol=1e-13, atol=1e-13)
+
+
+def loss_share(inp, x, wg, wu, wd, w):
+    re = inp["row_expert"]
+    dY = bf16.decode(inp["dY"])
+    tot = 0.0
+    for e in range(wg.shape[0]):
+        sel = np.nonzero(re == e)[0]
+        _, _, _, y = layer.expert_ffn(x[sel], wg[e], wu[e], wd[e])
+        tot += float(np.sum(dY[sel] * (w[sel, None] * y)))
+    return tot
+
+
+def test_backward_finite_differences():
+    inp = workloads.make_expert_share("micro")
+    g = layer.backward_share(inp)
+    x = bf16.decode(inp["x"]); wg = bf16.decode(inp["w_gate"]); wu = bf16.decode(inp["w_up"])
+    wd = bf16.decode(inp["w_down"]); w = inp["row_w"].astype(np.float64)
+    rng = np.random.default_rng(9)
+    args = {"x": x, "wg": wg, "wu": wu, "wd": wd, "w": w}
+    grads = {"x": g["dX"], "wg": g["dW_gate"], "wu": g["dW_up"], "wd": g["dW_down"], "w": g["d_row_w"]}
+    eps = 1e-5
+    for name, val in args.items():
+        d = rng.standard_normal(val.shape)
+        plus = dict(args); plus[name] = val + eps * d
+        minus = dict(args); minus[name] = val - eps * d
+        fd = (loss_share(inp, **plus) - loss_share(inp, **minus)) / (2 * eps)
+        an = float(np.sum(grads[name] * d))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), name
+
+
+def test_backward_matches_torch_autograd():
+    inp = workloads.make_expert_share("micro")
+    g = layer.backward_share(inp)
+    re = torch.from_numpy(inp["row_expert"].astype(np.int64))
+    x = torch.tensor(bf16.decode(inp["x"]), requires_grad=True)
+    wg = torch.tensor(bf16.decode(inp["w_gate"]), requires_grad=True)
+    wu = torch.tensor(bf16.decode(inp["w_up"]), requires_grad=True)
+    wd = torch.tensor(bf16.decode(inp["w_down"]), requires_grad=True)
+    w = torch.tensor(inp["row_w"].astype(np.float64), requires_grad=True)
+    gsel = torch.einsum("rh,rih->ri", x, wg[re])
+    usel = torch.einsum("rh,rih->ri", x, wu[re])
+    a = torch.nn.functional.silu(gsel) * usel
+    y = torch.einsum("ri,rhi->rh", a, wd[re])
+    out = w[:, None] * y
+    (out * torch.from_numpy(bf16.decode(inp["dY"]))).sum().backward()
+    assert np.allclose(g["dX"], x.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(g["dW_gate"], wg.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(g["dW_up"], wu.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(g["dW_down"], wd.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(g["d_row_w"], w.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_router_weight_gradient_two_ways():
+    inp = workloads.make_expert_share("small")
+    g = layer.backward_share(inp)
+    assert np.allclose(g["d_row_w"], g["d_row_w_alt"], rtol=1e-9, atol=1e-9)
+
+
+def test_mxfp8_forward_brute_force_rows():
+    inp = workloads.make_expert_share("micro")
+    ref = layer.forward_share_mxfp8(inp)
+    x = bf16.decode(inp["x"])
+    qg = mxfp8.quantize(bf16.decode(inp["w_gate"])); qu = mxfp8.quantize(bf16.decode(inp["w_up"]))
+    qd = mxfp8.quantize(bf16.decode(inp["w_down"]))
+    for r in range(0, inp["shape"].R, 5):
+        e = int(inp["row_expert"][r])
+        xc, xs = mxfp8.quantize(x[r:r + 1])
+        assert np.array_equal(xc, ref["x_codes"][r:r + 1]) and np.array_equal(xs, ref["x_scales"][r:r + 1])
+        xd = mxfp8.e4m3_decode(xc[0]) * np.repeat(2.0 ** (xs[0].astype(np.float64) - 127), 32)
+        I = qg[0].shape[1]
+        a = np.zeros(I)
+        for i in range(I):
+            wgd = mxfp8.e4m3_decode(qg[0][e, i]) * np.repeat(2.0 ** (qg[1][e, i].astype(np.float64) - 127), 32)
+            wud = mxfp8.e4m3_decode(qu[0][e, i]) * np.repeat(2.0 ** (qu[1][e, i].astype(np.float64) - 127), 32)
+            gg = math.fsum(xd * wgd); uu = math.fsum(xd * wud)
+            a[i] = bf16.decode(bf16.encode(np.array(scalar_silu(gg) * uu)))
+        assert np.array_equal(bf16.encode(a), ref["a_bits"][r])
+        ac, as_ = mxfp8.quantize(a[None, :])
+        ad = mxfp8.e4m3_decode(ac[0]) * np.repeat(2.0 ** (as_[0].astype(np.float64) - 127), 32)
+        for h in range(0, inp["shape"].H, 7):
+            wdd = mxfp8.e4m3_decode(qd[0][e, h]) * np.repeat(2.0 ** (qd[1][e, h].astype(np.float64) - 127), 32)
+            y = math.fsum(ad * wdd)
+            assert abs(ref["y"][r, h] - y) <= 1e-12 * max(1.0, abs(y))
+
+
+def test_mxfp8_forward_close_to_bf16_forward():
+    """Quantisation error of the whole MXFP8 layer stays near E4M3's ~2^-4
+    relative precision (a sanity band, not the parity bound)."""
+    inp = workloads.make_expert_share("small")
+    q = layer.forward_share_mxfp8(inp)["out"]
+    b = layer.forward_share(inp)["out"]
+    assert rms(q - b) < 0.1 * rms(b)
+
+
+def test_ring_contents_wrap():
+    inp = workloads.make_full_layer("tiny")
+    ref = layer.forward_full(inp)
+    re = ref["row_expert"]
+    MB = 128
+    s = schedule.build(re, 8, MB, 2 * MB, 64)
+    src = np.arange(len(re)) // 2
+    ring, written = layer.ring_contents(s, inp["x"], src)
+    assert written.all()
+    # the ring ends up holding the last two minibatches
+    for p in range(2 * MB, 4 * MB):
+        r = s.inv[p]
+        assert np.array_equal(ring[p % (2 * MB)], inp["x"][src[r]])
