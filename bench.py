@@ -1,0 +1,320 @@
+"""Benchmark of the one-GPU MoE layer hot path on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-breakdown] [--no-cpu-baseline]
+
+Prints ONE JSON line.  ``value`` is routed rows/s of the full single-GPU layer
+forward (T=4096 tokens, H=2048, I=768, 128 experts, top-8 renormalised router
+with a biased logit): one step = route + build_schedule + forward (permute,
+expert GEMMs, combine), inputs resident in HBM.  ``breakdown`` adds the
+expert-share shapes (EP=64 forward in bf16 and MXFP8, backward in bf16), each
+with rows/s, grouped-GEMM TFLOP/s and per-kernel roofline fractions.  Kernel
+durations come from HIP events the library records around each phase on the
+stream it launches on, over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # dense MFMA flop/s
+PEAK_FP8 = 5.0e15
+METRIC = "MoE layer routed rows/s + grouped-GEMM TFLOP/s (fwd/bwd, bf16 & MXFP8), 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="run one workload only (full, ep64_fwd, ep64_mxfp8, ep_bwd)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# algorithmic work per phase (flops, bytes) -- minimum traffic: every operand
+# read once and every result written once
+# --------------------------------------------------------------------------
+def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True):
+    ab = 1 if mx else 2                       # bytes per GEMM operand element
+    sc = 1.0 / 32 if mx else 0.0             # MXFP8 scale bytes per element
+    w = {}
+    if kind == "forward":
+        w["route"] = (2.0 * T * E * H, T * H * 2 + E * H * 2 + T * k * 8)
+        w["permute"] = (0.0, R * H * 2 + R * H * (ab + sc))
+        w["gemm1"] = (4.0 * R * H * I, R * H * (ab + sc) + E * 2 * I * H * (ab + sc) + R * I * 2
+                      + (R * 2 * I * 4 if save_ctx else 0))
+        if mx:
+            w["quant_a"] = (0.0, R * I * 2 + R * I * (1 + 1 / 32))
+        w["gemm2"] = (2.0 * R * I * H, R * I * (ab + sc) + E * H * I * (ab + sc) + (R * H * 2 if share else R * H * 4))
+        if not share:
+            w["combine"] = (0.0, R * H * 4 + T * H * 2 + R * 8)
+    else:
+        w["bwd_gather"] = (0.0, 2.0 * R * H * 2)
+        w["bwd_dact"] = (2.0 * R * H * I, R * H * 2 + E * I * H * 2 + R * 2 * I * 4 + R * 2 * I * 2 + R * I * 2)
+        w["bwd_dx"] = (4.0 * R * I * H, R * 2 * I * 2 + E * H * 2 * I * 2 + R * H * 2)
+        w["wgrad_down"] = (2.0 * R * H * I, R * H * 2 + R * I * 2 + E * H * I * 4)
+        w["wgrad_gate_up"] = (4.0 * R * H * I, R * 2 * I * 2 + R * H * 2 + E * 2 * I * H * 4)
+    return w
+
+
+def roofline(flops, nbytes, ms, mx=False):
+    peak_f = PEAK_FP8 if mx else PEAK_BF16
+    t_f = flops / peak_f
+    t_b = nbytes / PEAK_HBM
+    s = ms * 1e-3
+    if t_f >= t_b and flops > 0:
+        ach = flops / s / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f / 1e12, "unit": "TFLOP/s",
+                "frac": round(ach / (peak_f / 1e12), 4)}
+    ach = nbytes / s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(ach / (PEAK_HBM / 1e9), 4)}
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "mixture_experts_layer_device_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        e = d[workload][kernel]
+        if e["src_hash"] != src_hash(e["src_files"]):
+            return None
+        return e["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+# --------------------------------------------------------------------------
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(sharding across GPUs is a design note, not built)"}))
+        sys.exit(2)
+    import torch
+
+    import workloads
+    from mixture_experts_layer_device_amd import binding as B
+    from mixture_experts_layer_device_amd.layer import MoELayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+
+    def log(*m):
+        print(*m, file=sys.stderr, flush=True)
+
+    def timed(step, L, steps, warmup):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        B.mk_timing_read(L.ws)                      # drop warm-up events
+        B.mk_timing_enable(L.ws, True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        B.mk_timing_enable(L.ws, False)
+        ph = B.mk_timing_read(L.ws)
+        per = {k: (v[0] / steps, v[1] / steps) for k, v in ph.items() if v[1] > 0}
+        return dt, per
+
+    def summarize(name, R, T, H, I, E, k, dt, per, steps, kind, mx=False, share=True, save_ctx=False):
+        work = phase_work(kind, R, T, H, I, E, k, mx=mx, save_ctx=save_ctx, share=share)
+        phases = {}
+        gemm_flops = gemm_ms = 0.0
+        for p, (ms, n) in per.items():
+            f, b = work.get(p, (0.0, 0.0))
+            ent = {"ms": round(ms, 4), "launches": n}
+            if f or b:
+                ent["roofline"] = roofline(f, b, ms, mx=mx and p.startswith("gemm"))
+            phases[p] = ent
+            if f and p != "route":
+                gemm_flops += f
+                gemm_ms += ms
+        ms_step = dt / steps * 1e3
+        return {
+            "workload": name, "routed_rows": R, "ms_per_step": round(ms_step, 4),
+            "rows_per_s": round(R / (ms_step * 1e-3), 1),
+            "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
+            "gemm_tflops_over_step": round(gemm_flops / (ms_step * 1e-3) / 1e12, 2),
+            "phases": phases,
+        }
+
+    results = {}
+    want = set(a.only.split(",")) if a.only else {"full", "ep64_fwd", "ep64_mxfp8", "ep_bwd"}
+    if a.no_breakdown:
+        want = {"full"}
+
+    # ---- main line: full single-GPU layer forward ------------------------
+    main = None
+    full_inp = None
+    if "full" in want:
+        log("[bench] full layer forward: T=4096 H=2048 I=768 E=128 k=8")
+        inp = full_inp = workloads.make_full_layer("full")
+        sh = inp["shape"]
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm)
+        x = up(inp["x"]); wr = up(inp["w_router"]); bias = up(inp["bias"])
+        packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]))
+        out = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
+        idx = torch.empty((sh.T, sh.k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((sh.T, sh.k), dtype=torch.float32, device="cuda")
+        s = torch.cuda.current_stream()
+
+        def step():
+            B.mk_route(L.ws, x, wr, bias, sh.T, idx, wts, s)
+            B.mk_build_schedule(L.ws, idx, sh.R, s)
+            B.mk_forward(L.ws, B.MK_FULL_LAYER, x, wts, packed, out, None, s)
+
+        dt, per = timed(step, L, a.steps, a.warmup)
+        main = summarize("full", sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False)
+        main["err"] = L.device_error()
+        L.close()
+        del packed
+        log(json.dumps(main))
+
+    # ---- expert-share shapes ---------------------------------------------
+    if want & {"ep64_fwd", "ep64_mxfp8"}:
+        inp = workloads.make_expert_share("ep64_fwd", with_dy=False)
+        sh = inp["shape"]
+        x = up(inp["x"]); re = up(inp["row_expert"]); rw = up(inp["row_w"])
+        wg, wu, wd = up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"])
+        for prec, key in (("bf16", "ep64_fwd"), ("mxfp8", "ep64_mxfp8")):
+            if key not in want:
+                continue
+            log(f"[bench] EP=64 expert share forward {prec}: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096")
+            L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=4096)
+            packed = L.prepare_weights(wg, wu, wd)
+            out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
+            s = torch.cuda.current_stream()
+
+            def step():
+                B.mk_build_schedule(L.ws, re, sh.R, s)
+                B.mk_forward(L.ws, B.MK_EXPERT_SHARE, x, rw, packed, out, None, s)
+
+            dt, per = timed(step, L, a.steps, a.warmup)
+            results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "forward",
+                                     mx=prec == "mxfp8")
+            results[key]["err"] = L.device_error()
+            L.close()
+            del packed
+            log(json.dumps(results[key]))
+        del x, wg, wu, wd
+
+    if "ep_bwd" in want:
+        inp = workloads.make_expert_share("ep_bwd")
+        sh = inp["shape"]
+        log(f"[bench] expert share backward bf16: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096 (ring wraps)")
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, minibatch_rows=4096, enable_backward=True)
+        x = up(inp["x"]); re = up(inp["row_expert"]); rw = up(inp["row_w"]); dY = up(inp["dY"])
+        packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]), for_backward=True)
+        out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
+        ctx = L.new_fwd_ctx()
+        s = torch.cuda.current_stream()
+        B.mk_build_schedule(L.ws, re, sh.R, s)
+        B.mk_forward(L.ws, B.MK_EXPERT_SHARE, x, rw, packed, out, ctx, s)     # fwd_ctx, untimed
+        g = {"dX": torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda"),
+             "dW_gate": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
+             "dW_up": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
+             "dW_down": torch.empty((sh.E, sh.H, sh.I), dtype=torch.float32, device="cuda"),
+             "d_row_w": torch.empty((sh.R,), dtype=torch.float32, device="cuda")}
+
+        def step():
+            B.mk_backward(L.ws, B.MK_EXPERT_SHARE, ctx, x, rw, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
+                          g["dW_down"], g["d_row_w"], s)
+
+        dt, per = timed(step, L, a.steps, a.warmup)
+        results["ep_bwd"] = summarize("ep_bwd", sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "backward")
+        results["ep_bwd"]["err"] = L.device_error()
+        L.close()
+        log(json.dumps(results["ep_bwd"]))
+
+    # ---- CPU baseline: the oracle on a bounded sample of the main workload --
+    cpu = None
+    if main is not None and not a.no_cpu_baseline:
+        cpu = cpu_baseline(log, full_inp)
+
+    if main is None:
+        main = next(iter(results.values()))
+    dom = max(((p, v) for p, v in main["phases"].items() if "roofline" in v), key=lambda kv: kv[1]["ms"])
+    roof = dict(dom[1]["roofline"])
+    roof["kernel"] = dom[0]
+    f, b = phase_work("forward", 32768, 4096, 2048, 768, 128, 8, share=False)[dom[0]] if main["workload"] == "full" \
+        else (None, None)
+    tr = traffic_for(dom[0], main["workload"])
+    roof["traffic"] = tr
+    roof["algorithmic"] = b if roof["bound"] == "hbm" else f
+    line = {
+        "metric": METRIC, "value": main["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": main["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full single-GPU MoE layer forward: route + build_schedule + permute + expert "
+                               "GEMMs (SwiGLU) + combine; T=4096 tokens, H=2048, I=768, 128 experts, top-8 "
+                               "renormalised softmax router with per-expert logit bias",
+                   "tokens": 4096, "routed_rows": 32768, "H": 2048, "I": 768, "E": 128, "k": 8},
+        "gemm_tflops": main["gemm_tflops"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "phases": main["phases"],
+        "breakdown": results,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(log, inp):
+    """The oracle, as it stands, on a sample of the main workload: route,
+    expert FFN and combine of the first 1024 of its 4096 tokens; rows/s counts
+    the routed rows of the sample."""
+    import threadpoolctl
+
+    from oracle import bf16, layer, route
+
+    sh = inp["shape"]
+    n_tok = 1024
+    toks = np.arange(n_tok)
+    with threadpoolctl.threadpool_limits(limits=None):
+        info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    x = bf16.decode(inp["x"][:n_tok]).astype(np.float32)
+    idx, w, _ = route.route(x, bf16.decode(inp["w_router"]).astype(np.float32), inp["bias"], sh.k, sh.renorm)
+    t1 = time.perf_counter()
+    sub = dict(inp)
+    sub["x"] = inp["x"][:n_tok]
+    layer.forward_full_tokens(sub, idx, w, toks)
+    t2 = time.perf_counter()
+    rows = n_tok * sh.k
+    log(f"[bench] cpu oracle: route {t1 - t0:.2f}s, ffn+combine {t2 - t1:.2f}s for {rows} routed rows")
+    return {"value": round(rows / (t2 - t0), 1), "unit": "rows/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"full-layer forward (route + expert FFN + combine, fp64 numpy) of {n_tok} of the 4096 "
+                      f"tokens ({rows} routed rows); cores = numpy BLAS threads"}
+
+
+if __name__ == "__main__":
+    main()

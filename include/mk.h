@@ -1,0 +1,257 @@
+/*
+ * mk.h -- C ABI of the one-GPU MoE layer hot path for AMD MI355X (gfx950).
+ *
+ * The calls follow the functional API of Mixture-of-Kittens (MoK) as the
+ * agentlenshq project card "Mixture-of-Kittens (MoK)" states it ("Use the
+ * functional API", "Core concepts"): a config, a workspace created once per
+ * model and reused, build_schedule from the routed expert ids, forward
+ * returning the output plus a forward context, and backward consuming that
+ * context.  The same card's "Core concepts" names the MXFP8 quantise op used
+ * to pre-quantise weights.  Routing is added in front because the pages take
+ * the top-k expert ids as an input.
+ *
+ * Conventions (every entry point):
+ *  - Every pointer argument named *_dev is DEVICE memory on the current HIP
+ *    device; the caller allocates and owns it.  The library owns only the
+ *    workspace and what it allocates inside it.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it: they never synchronise with the host, never copy
+ *    device data to the host and never size a launch from device-side counts.
+ *  - bf16 tensors are raw 16-bit bf16 patterns (uint16), row-major.
+ *  - Return value: MK_OK (0) or a negative MK_ERR_* code, detected on the
+ *    host before anything is enqueued.  Problems only the device can see
+ *    set bits in the workspace's device error word (MK_DEVERR_*); read it
+ *    with mk_device_error.  No call hangs on bad data and no exception
+ *    crosses this boundary.
+ *  - One workspace serves one stream at a time; calls on one workspace must
+ *    be ordered (same stream, or externally synchronised).
+ */
+#ifndef MK_H_
+#define MK_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MK_OK               0
+#define MK_ERR_NULL        -1  /* a required pointer is NULL                 */
+#define MK_ERR_SHAPE       -2  /* unsupported shape (see each call)           */
+#define MK_ERR_RING        -3  /* ring smaller than one minibatch             */
+#define MK_ERR_LIMIT       -4  /* above a workspace limit (rows, experts, k)  */
+#define MK_ERR_HIP         -5  /* a HIP runtime call failed                   */
+#define MK_ERR_STATE       -6  /* call out of order (e.g. forward before schedule) */
+#define MK_ERR_UNSUPPORTED -7  /* combination not implemented                 */
+#define MK_ERR_CONFIG      -8  /* invalid config field                        */
+
+/* ---- device error word bits (OR-ed; cleared by mk_build_schedule) ------ */
+#define MK_DEVERR_EXPERT_RANGE   0x1u  /* a row_expert id outside [0, E): row dropped, its output is 0 */
+#define MK_DEVERR_SCHED_OVERFLOW 0x2u  /* work table above capacity: trailing tiles dropped            */
+
+/* ---- enums --------------------------------------------------------------- */
+#define MK_BF16   0
+#define MK_MXFP8  1
+
+#define MK_FULL_LAYER   0  /* rows r = t*k + j of T tokens; combine sums the k rows of a token */
+#define MK_EXPERT_SHARE 1  /* rows already resident in arrival order; out_rows[r] = w[r]*y(r)   */
+
+/*
+ * Config (the card's MoKConfig knobs that apply to one GPU; "Core concepts",
+ * "Limitations": minibatch granularity, macrobatch size via the ring, schedule
+ * capacity multiplier).  The communication-SM knob has no one-GPU meaning.
+ *   minibatch_rows      rows per minibatch (MB); 0 = all rows in one.  In
+ *                       MK_FULL_LAYER mode a multiple of k.
+ *   ring_bytes          ring token buffer capacity; the ring holds
+ *                       MB * floor(ring_bytes / (MB * row_bytes)) rows, a whole
+ *                       number of minibatches (the macrobatch).  row_bytes is
+ *                       2H (bf16) or H + H/32 (MXFP8).
+ *   sched_capacity_mult work-table capacity as a multiple of the worst case
+ *                       ceil(rows/256) + minibatches*E; >= 1 never overflows.
+ *   precision           MK_BF16 or MK_MXFP8.
+ *   renorm              router weights: 1 = softmax over the k chosen logits,
+ *                       0 = full softmax over all E read at the chosen ones.
+ *   enable_backward     1 = also allocate the backward's buffers.
+ */
+typedef struct mk_config {
+  int32_t minibatch_rows;
+  int32_t precision;
+  int64_t ring_bytes;
+  float   sched_capacity_mult;
+  int32_t renorm;
+  int32_t enable_backward;
+  int32_t reserved[3];
+} mk_config;
+
+typedef struct mk_workspace mk_workspace;   /* opaque */
+
+/* Fill *cfg with defaults: MB = 0, bf16, 256 MiB ring, capacity 1.0,
+ * renorm 1, no backward. */
+void mk_config_default(mk_config* cfg);
+
+/*
+ * Workspace ("Core concepts": created once per model, reused).  Allocates the
+ * ring, schedule tables, intermediate activations and the error word on the
+ * current device.  Limits: max_rows >= 1 routed rows per call; H % 256 == 0,
+ * I % 128 == 0 (I % 256 == 0 with enable_backward); 1 <= E <= 1024;
+ * 1 <= k <= 32; ring_bytes below 2 GiB.  Returns MK_ERR_SHAPE / _LIMIT / _RING /
+ * _CONFIG on a bad argument, MK_ERR_HIP if an allocation fails.
+ */
+int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32_t I,
+                        int32_t E, int32_t k, mk_workspace** out);
+int mk_workspace_destroy(mk_workspace* ws);
+
+/* Host-known sizes of a workspace, for callers and tests. */
+#define MK_Q_RING_ROWS      0   /* rows the ring holds                         */
+#define MK_Q_MINIBATCH_ROWS 1   /* MB                                          */
+#define MK_Q_NUM_MB         2   /* minibatches of the last schedule            */
+#define MK_Q_ITEM_CAPACITY  3   /* work-table capacity (items)                 */
+#define MK_Q_TILE_M         4   /* rows per work item (GEMM m-tile)            */
+#define MK_Q_ROWS           5   /* R of the last schedule                      */
+#define MK_Q_NUM_CU         6   /* compute units the persistent grids use      */
+#define MK_Q_PACKED_BYTES   7   /* bytes of packed weights (forward only)      */
+#define MK_Q_PACKED_BYTES_BWD 8 /* bytes of packed weights incl. backward copies */
+#define MK_Q_FWD_CTX_BYTES  9   /* bytes of fwd_ctx for max_rows               */
+int64_t mk_query(const mk_workspace* ws, int32_t what);
+
+/*
+ * Router: z[t,e] = sum_h x[t,h]*w_router[e,h] accumulated in fp32 in ascending
+ * h from +0, plus bias[e] (fp32) if bias_dev is not NULL; top-k by descending
+ * z with ties to the lower expert id (slot 0 = largest); weights from the
+ * softmax selected by cfg.renorm.
+ *   x_dev        [T, H] bf16          w_router_dev [E, H] bf16
+ *   bias_dev     [E] fp32 or NULL
+ *   topk_idx_dev [T, k] int32 (out)   topk_w_dev   [T, k] fp32 (out)
+ * MK_ERR_LIMIT if T*k > max_rows.
+ */
+int mk_route(mk_workspace* ws, const void* x_dev, const void* w_router_dev,
+             const float* bias_dev, int32_t T, int32_t* topk_idx_dev, float* topk_w_dev,
+             void* stream);
+
+/*
+ * Dispatch schedule ([MTP] = MarkTechPost "Cursor Open-Sources
+ * Mixture-of-Kittens (MoK)...", "Three design decisions that matter": one
+ * schedule table serves dispatch, combine and both backward directions).
+ * From row_expert_dev [R] int32 (full-layer mode: the flattened topk_idx,
+ * row r = t*k + j) builds, on the device, per-expert and per-minibatch counts
+ * and offsets, the stable expert-grouped position of every row, its inverse,
+ * and the GEMM work items.  Rows with an expert id outside [0, E) are dropped
+ * and flagged (MK_DEVERR_EXPERT_RANGE).  Clears the device error word first.
+ * MK_ERR_LIMIT if R > max_rows; MK_ERR_SHAPE if R < 0, or in full-layer use if
+ * MB is not a multiple of k (checked at forward).
+ */
+int mk_build_schedule(mk_workspace* ws, const int32_t* row_expert_dev, int32_t R, void* stream);
+
+/* Copy one schedule table (device) into dst_dev (device, >= bytes). */
+#define MK_TAB_COUNTS     0   /* [E]        int32                                   */
+#define MK_TAB_OFFSETS    1   /* [E+1]      int32                                   */
+#define MK_TAB_MB_COUNTS  2   /* [nb, E]    int32                                   */
+#define MK_TAB_MB_OFFSETS 3   /* [nb, E+1]  int32 (within each minibatch)           */
+#define MK_TAB_SORTED_POS 4   /* [R]        int32, -1 for a dropped row             */
+#define MK_TAB_INV        5   /* [nb*MB]    int32, -1 where no row                  */
+#define MK_TAB_ITEMS      6   /* [capacity, 4] int32 (row_begin, rows, expert, mb)  */
+#define MK_TAB_MB_ITEMS   7   /* [nb+1]     int32 first item of each minibatch      */
+#define MK_TAB_RING       8   /* ring contents, ring_rows * row_bytes bytes         */
+int mk_schedule_copy(const mk_workspace* ws, int32_t table, void* dst_dev, int64_t bytes,
+                     void* stream);
+
+/*
+ * MXFP8 quantise (the card's ops.mxfp8_quantize; OCP MX v1.0 with E4M3
+ * elements): blocks of 32 along K; E8M0 scale s = clamp(floor(log2 amax) - 8,
+ * -127, 127) + 127 (0 for an all-zero block); codes are E4M3-FN of v/2^(s-127)
+ * rounded to nearest even and saturated at +-448, sign kept.
+ *   in_dev [rows, K] bf16 -> codes_dev [rows, K] uint8, scales_dev [rows, K/32] uint8
+ * MK_ERR_SHAPE unless K % 32 == 0.  Needs no workspace.
+ */
+int mk_mxfp8_quantize(const void* in_dev, int64_t rows, int32_t K, uint8_t* codes_dev,
+                      uint8_t* scales_dev, void* stream);
+
+/*
+ * Weight packing (outside the timed path; the card's "Limitations": MXFP8
+ * weights are pre-quantised).  Inputs, one row per output feature:
+ *   w_gate_dev [E, I, H] bf16, w_up_dev [E, I, H] bf16, w_down_dev [E, H, I] bf16
+ * packed_dev receives mk_query(MK_Q_PACKED_BYTES[_BWD]) bytes: gate and up
+ * rows interleaved in blocks of 16 (GEMM1's B), the down rows (GEMM2's B),
+ * in MXFP8 mode as E4M3 codes + E8M0 scales along each GEMM's K; with
+ * for_backward = 1 also the transposed bf16 copies the backward GEMMs read.
+ */
+int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_up_dev,
+                       const void* w_down_dev, int32_t for_backward, void* packed_dev,
+                       void* stream);
+
+/*
+ * Forward ([MTP] "Three design decisions that matter" and the paragraph after
+ * them): permute rows into the ring minibatch by minibatch (MXFP8: quantised
+ * on the way), expert-grouped GEMM1 (gate/up) with SwiGLU, GEMM2 (down), then
+ * the router-weighted combine in a fixed order (bitwise repeatable).
+ *   mode MK_FULL_LAYER:   x_src_dev [T, H] bf16, row r = t*k + j comes from
+ *                         token t; row_w_dev = topk_w [T*k] fp32;
+ *                         out_dev [T, H] bf16, out[t] = sum_j w[t,j] y(t,j), j ascending.
+ *   mode MK_EXPERT_SHARE: x_src_dev [R, H] bf16 in arrival order; row_w_dev [R];
+ *                         out_dev [R, H] bf16, out[r] = w[r] * y(r).
+ *   fwd_ctx_dev: NULL, or mk_query(MK_Q_FWD_CTX_BYTES) bytes that receive what
+ *                the backward needs (g and u in fp32).
+ * Uses the schedule of the last mk_build_schedule (MK_ERR_STATE if none).
+ * MK_ERR_UNSUPPORTED for MXFP8 with fwd_ctx (MXFP8 backward is not built).
+ */
+int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const float* row_w_dev,
+               const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
+
+/*
+ * Backward, expert-share mode, bf16 ([MTP]: the ring is walked in reverse to
+ * minimise forward-activation replay; the router-weight gradient is fused into
+ * the SwiGLU backward).  Loss gradient dY_dev [R, H] bf16 in arrival order.
+ *   dX_dev      [R, H] bf16 (arrival order)
+ *   dW_gate_dev [E, I, H] fp32, dW_up_dev [E, I, H] fp32, dW_down_dev [E, H, I] fp32
+ *   d_row_w_dev [R] fp32
+ * Weight gradients are reduced in a fixed order (minibatches in reverse walk
+ * order, rows ascending inside each) with no float atomics: bitwise repeatable
+ * at a fixed minibatch size.  Must follow the mk_forward (with fwd_ctx) of the
+ * same rows on this workspace with no other forward in between; packed_dev must
+ * have been prepared with for_backward = 1.  MK_ERR_UNSUPPORTED for full-layer
+ * mode or MXFP8; MK_ERR_CONFIG if the workspace has no backward buffers.
+ */
+int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const void* x_src_dev,
+                const float* row_w_dev, const void* packed_dev, const void* dY_dev,
+                void* dX_dev, float* dW_gate_dev, float* dW_up_dev, float* dW_down_dev,
+                float* d_row_w_dev, void* stream);
+
+/*
+ * Per-phase timing (for benchmarks): with timing on, every launch sequence
+ * records a HIP event pair on the caller's stream around each phase, and
+ * mk_timing_read (HOST call: waits for the recorded events) adds up the
+ * milliseconds per phase since the last read into ms_out[MK_PH_COUNT] and
+ * launch counts into launches_out[MK_PH_COUNT] (either may be NULL), then
+ * resets.  Costs one event record per phase boundary; off by default.
+ */
+#define MK_PH_ROUTE      0
+#define MK_PH_SCHEDULE   1
+#define MK_PH_PERMUTE    2   /* permute into the ring (MXFP8: fused quantise) */
+#define MK_PH_GEMM1      3
+#define MK_PH_QUANT_A    4   /* MXFP8: quantise a along I                    */
+#define MK_PH_GEMM2      5   /* expert share: includes the fused weighted unpermute */
+#define MK_PH_COMBINE    6   /* full layer combine / zeroing of dropped rows  */
+#define MK_PH_BWD_GATHER 7
+#define MK_PH_BWD_DACT   8
+#define MK_PH_BWD_DW     9
+#define MK_PH_BWD_DX     10
+#define MK_PH_WGRAD_DOWN 11
+#define MK_PH_WGRAD_GU   12
+#define MK_PH_COUNT      13
+int mk_timing_enable(mk_workspace* ws, int32_t on);
+int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
+
+/* Enqueue a copy of the device error word into dst_dev (device uint32). */
+int mk_device_error(const mk_workspace* ws, uint32_t* dst_dev, void* stream);
+
+/* Minibatch floor of the two-wave rule ([MTP] "Three design decisions that
+ * matter", overlap granularity): ceil(2 * n_cu * tile_m * tile_n / min(2I, H)). */
+int64_t mk_two_wave_rows(int32_t H, int32_t I, int32_t n_cu, int32_t tile_m, int32_t tile_n);
+
+const char* mk_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H_ */

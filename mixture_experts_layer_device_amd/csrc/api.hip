@@ -1,0 +1,551 @@
+// C ABI of the MoE layer library (declared in include/mk.h): argument
+// checks, the workspace, and the launch sequences of forward and backward.
+// Every call only enqueues work on the caller's stream.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "mk_device.h"
+#include "mk_internal.h"
+
+using namespace mk;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + std::max<size_t>(bytes, 1));
+    return o;
+  }
+};
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+int64_t packed_bytes(const mk_workspace* ws, bool bwd) {
+  const int64_t E = ws->E, H = ws->H, I = ws->I;
+  if (ws->cfg.precision == MK_MXFP8) {
+    return (int64_t)align_up(E * 2 * I * H) + (int64_t)align_up(E * 2 * I * H / 32) +
+           (int64_t)align_up(E * H * I) + (int64_t)align_up(E * H * I / 32);
+  }
+  int64_t b = (int64_t)align_up(E * 2 * I * H * 2) + (int64_t)align_up(E * H * I * 2);
+  if (bwd) b += (int64_t)align_up(E * I * H * 2) + (int64_t)align_up(E * H * 2 * I * 2);
+  return b;
+}
+
+struct PackedBF16 {
+  uint16_t *wgu, *wd, *wdT, *wguT;
+};
+PackedBF16 packed_bf16(const mk_workspace* ws, void* base) {
+  const int64_t E = ws->E, H = ws->H, I = ws->I;
+  char* p = (char*)base;
+  PackedBF16 r;
+  r.wgu = (uint16_t*)p;
+  p += align_up(E * 2 * I * H * 2);
+  r.wd = (uint16_t*)p;
+  p += align_up(E * H * I * 2);
+  r.wdT = (uint16_t*)p;
+  p += align_up(E * I * H * 2);
+  r.wguT = (uint16_t*)p;
+  return r;
+}
+
+struct PackedMX {
+  uint8_t *wgu_c, *wgu_s, *wd_c, *wd_s;
+};
+PackedMX packed_mx(const mk_workspace* ws, void* base) {
+  const int64_t E = ws->E, H = ws->H, I = ws->I;
+  char* p = (char*)base;
+  PackedMX r;
+  r.wgu_c = (uint8_t*)p;
+  p += align_up(E * 2 * I * H);
+  r.wgu_s = (uint8_t*)p;
+  p += align_up(E * 2 * I * H / 32);
+  r.wd_c = (uint8_t*)p;
+  p += align_up(E * H * I);
+  r.wd_s = (uint8_t*)p;
+  return r;
+}
+
+ItemRange item_range(const mk_workspace* ws, int mb_lo, int mb_hi) {
+  ItemRange ir;
+  ir.items = ws->items;
+  ir.mb_items = ws->mb_items;
+  ir.mb_lo = mb_lo;
+  ir.mb_hi = mb_hi;
+  ir.item_cap = ws->item_cap;
+  return ir;
+}
+
+int check_launch() { return hipGetLastError() == hipSuccess ? MK_OK : MK_ERR_HIP; }
+
+// Scope that brackets one phase with a pair of events when timing is on.
+struct Phase {
+  mk_workspace* ws;
+  hipStream_t s;
+  mk_phase_event ev;
+  bool on;
+  Phase(mk_workspace* w, int phase, hipStream_t st) : ws(w), s(st), on(w->timing != 0) {
+    if (!on) return;
+    ev.phase = phase;
+    if (hipEventCreate(&ev.start) != hipSuccess || hipEventCreate(&ev.stop) != hipSuccess) {
+      on = false;
+      return;
+    }
+    (void)hipEventRecord(ev.start, s);
+  }
+  ~Phase() {
+    if (!on) return;
+    (void)hipEventRecord(ev.stop, s);
+    ws->events->push_back(ev);
+  }
+};
+
+}  // namespace
+
+// quantise packed gate/up rows (see launch_pack_gate_up) straight to MXFP8
+namespace mk {
+void launch_quant_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+}
+
+extern "C" {
+
+void mk_config_default(mk_config* cfg) {
+  if (!cfg) return;
+  memset(cfg, 0, sizeof(*cfg));
+  cfg->minibatch_rows = 0;
+  cfg->precision = MK_BF16;
+  cfg->ring_bytes = (int64_t)256 << 20;
+  cfg->sched_capacity_mult = 1.0f;
+  cfg->renorm = 1;
+  cfg->enable_backward = 0;
+}
+
+int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32_t I, int32_t E, int32_t k,
+                        mk_workspace** out) {
+  if (!cfg || !out) return MK_ERR_NULL;
+  *out = nullptr;
+  if (max_rows < 1 || H < 256 || I < 128 || H % 256 || I % 128) return MK_ERR_SHAPE;
+  if (E < 1 || E > MK_MAX_EXPERTS || k < 1 || k > MK_MAX_TOPK) return MK_ERR_LIMIT;
+  if (cfg->precision != MK_BF16 && cfg->precision != MK_MXFP8) return MK_ERR_CONFIG;
+  if (cfg->minibatch_rows < 0 || !(cfg->sched_capacity_mult > 0.f) || cfg->ring_bytes <= 0) return MK_ERR_CONFIG;
+  if (cfg->ring_bytes >= ((int64_t)1 << 31)) return MK_ERR_LIMIT;
+  if (cfg->enable_backward && cfg->precision != MK_BF16) return MK_ERR_UNSUPPORTED;
+  if (cfg->enable_backward && I % 256) return MK_ERR_SHAPE;
+
+  mk_workspace* ws = (mk_workspace*)calloc(1, sizeof(mk_workspace));
+  if (!ws) return MK_ERR_HIP;
+  ws->events = new std::vector<mk_phase_event>();
+  ws->cfg = *cfg;
+  ws->max_rows = max_rows;
+  ws->H = H;
+  ws->I = I;
+  ws->E = E;
+  ws->k = k;
+  ws->MB = cfg->minibatch_rows > 0 ? cfg->minibatch_rows : max_rows;
+  ws->row_bytes = cfg->precision == MK_MXFP8 ? H + H / 32 : 2 * H;
+  const int64_t mbs_in_ring = cfg->ring_bytes / ((int64_t)ws->MB * ws->row_bytes);
+  if (mbs_in_ring < 1) {
+    delete ws->events;
+    free(ws);
+    return MK_ERR_RING;
+  }
+  if ((int64_t)ws->MB * mbs_in_ring > INT32_MAX / 2) {
+    delete ws->events;
+    free(ws);
+    return MK_ERR_LIMIT;
+  }
+  ws->ring_rows = (int32_t)((int64_t)ws->MB * mbs_in_ring);
+  ws->nb_max = (max_rows + ws->MB - 1) / ws->MB;
+  ws->npos = (int64_t)ws->nb_max * ws->MB;
+  ws->cpm = (ws->MB + MK_SCHED_CHUNK - 1) / MK_SCHED_CHUNK;
+  const double worst = (double)((max_rows + MK_TILE_M - 1) / MK_TILE_M) + (double)ws->nb_max * E;
+  ws->item_cap = (int32_t)std::max(1.0, std::ceil(cfg->sched_capacity_mult * worst));
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    delete ws->events;
+    free(ws);
+    return MK_ERR_HIP;
+  }
+  ws->device = dev;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8) {
+    delete ws->events;
+    free(ws);
+    return MK_ERR_HIP;
+  }
+  ws->n_cu = ncu / 8 * 8;
+
+  const int64_t npos = ws->npos;
+  Carver c;
+  const size_t o_err = c.take(256);
+  const size_t o_cc = c.take((size_t)ws->nb_max * ws->cpm * E * 4);
+  const size_t o_mbc = c.take((size_t)ws->nb_max * E * 4);
+  const size_t o_mbo = c.take((size_t)ws->nb_max * (E + 1) * 4);
+  const size_t o_cnt = c.take((size_t)E * 4);
+  const size_t o_off = c.take((size_t)(E + 1) * 4);
+  const size_t o_sp = c.take((size_t)max_rows * 4);
+  const size_t o_inv = c.take((size_t)npos * 4);
+  const size_t o_items = c.take((size_t)ws->item_cap * 16);
+  const size_t o_mbi = c.take((size_t)(ws->nb_max + 1) * 4);
+  const size_t o_ring = c.take((size_t)ws->ring_rows * ws->row_bytes);
+  const size_t o_a = c.take((size_t)npos * I * 2);
+  size_t o_ac = 0, o_as = 0;
+  if (cfg->precision == MK_MXFP8) {
+    o_ac = c.take((size_t)npos * I);
+    o_as = c.take((size_t)npos * I / 32);
+  }
+  const size_t o_y = c.take((size_t)npos * H * 4);
+  size_t o_dye = 0, o_dgdu = 0, o_wa = 0, o_dwp = 0;
+  if (cfg->enable_backward) {
+    o_dye = c.take((size_t)npos * H * 2);
+    o_dgdu = c.take((size_t)npos * 2 * I * 2);
+    o_wa = c.take((size_t)npos * I * 2);
+    o_dwp = c.take((size_t)npos * (I / 64) * 4);
+  }
+  ws->bytes = c.off;
+  if (hipMalloc(&ws->base, ws->bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete ws->events;
+    free(ws);
+    return MK_ERR_HIP;
+  }
+  char* b = (char*)ws->base;
+  ws->err = (uint32_t*)(b + o_err);
+  ws->chunk_counts = (int32_t*)(b + o_cc);
+  ws->mb_counts = (int32_t*)(b + o_mbc);
+  ws->mb_offsets = (int32_t*)(b + o_mbo);
+  ws->counts = (int32_t*)(b + o_cnt);
+  ws->offsets = (int32_t*)(b + o_off);
+  ws->sorted_pos = (int32_t*)(b + o_sp);
+  ws->inv = (int32_t*)(b + o_inv);
+  ws->items = (int32_t*)(b + o_items);
+  ws->mb_items = (int32_t*)(b + o_mbi);
+  ws->ring = (uint8_t*)(b + o_ring);
+  ws->a_buf = (uint16_t*)(b + o_a);
+  if (cfg->precision == MK_MXFP8) {
+    ws->a_codes = (uint8_t*)(b + o_ac);
+    ws->a_scales = (uint8_t*)(b + o_as);
+  }
+  ws->y_buf = (float*)(b + o_y);
+  if (cfg->enable_backward) {
+    ws->dye = (uint16_t*)(b + o_dye);
+    ws->dgdu = (uint16_t*)(b + o_dgdu);
+    ws->wa = (uint16_t*)(b + o_wa);
+    ws->dw_part = (float*)(b + o_dwp);
+  }
+  // error word starts clear
+  launch_fill_u32(ws->err, 0u, 1, nullptr);
+  if (hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(ws->base);
+    delete ws->events;
+    free(ws);
+    return MK_ERR_HIP;
+  }
+  *out = ws;
+  return MK_OK;
+}
+
+int mk_workspace_destroy(mk_workspace* ws) {
+  if (!ws) return MK_ERR_NULL;
+  int rc = MK_OK;
+  for (auto& ev : *ws->events) {
+    (void)hipEventDestroy(ev.start);
+    (void)hipEventDestroy(ev.stop);
+  }
+  delete ws->events;
+  if (ws->base && hipFree(ws->base) != hipSuccess) rc = MK_ERR_HIP;
+  free(ws);
+  return rc;
+}
+
+int64_t mk_query(const mk_workspace* ws, int32_t what) {
+  if (!ws) return MK_ERR_NULL;
+  switch (what) {
+    case MK_Q_RING_ROWS: return ws->ring_rows;
+    case MK_Q_MINIBATCH_ROWS: return ws->MB;
+    case MK_Q_NUM_MB: return ws->have_sched ? ws->nb : 0;
+    case MK_Q_ITEM_CAPACITY: return ws->item_cap;
+    case MK_Q_TILE_M: return MK_TILE_M;
+    case MK_Q_ROWS: return ws->have_sched ? ws->R : 0;
+    case MK_Q_NUM_CU: return ws->n_cu;
+    case MK_Q_PACKED_BYTES: return packed_bytes(ws, false);
+    case MK_Q_PACKED_BYTES_BWD: return packed_bytes(ws, true);
+    case MK_Q_FWD_CTX_BYTES: return ws->npos * 2 * ws->I * 4;
+    default: return MK_ERR_CONFIG;
+  }
+}
+
+int mk_route(mk_workspace* ws, const void* x, const void* w_router, const float* bias, int32_t T, int32_t* topk_idx,
+             float* topk_w, void* stream) {
+  if (!ws || !x || !w_router || !topk_idx || !topk_w) return MK_ERR_NULL;
+  if (T < 0) return MK_ERR_SHAPE;
+  if ((int64_t)T * ws->k > ws->max_rows) return MK_ERR_LIMIT;
+  if (ws->k > ws->E) return MK_ERR_SHAPE;
+  Phase ph(ws, MK_PH_ROUTE, as_stream(stream));
+  launch_route((const uint16_t*)x, (const uint16_t*)w_router, bias, T, ws->H, ws->E, ws->k, ws->cfg.renorm, topk_idx,
+               topk_w, as_stream(stream));
+  return check_launch();
+}
+
+int mk_build_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, void* stream) {
+  if (!ws || (!row_expert && R > 0)) return MK_ERR_NULL;
+  if (R < 0) return MK_ERR_SHAPE;
+  if (R > ws->max_rows) return MK_ERR_LIMIT;
+  {
+    Phase ph(ws, MK_PH_SCHEDULE, as_stream(stream));
+    launch_schedule(ws, row_expert, R, as_stream(stream));
+  }
+  ws->R = R;
+  ws->nb = R > 0 ? (R + ws->MB - 1) / ws->MB : 0;
+  ws->have_sched = 1;
+  return check_launch();
+}
+
+int mk_schedule_copy(const mk_workspace* ws, int32_t table, void* dst, int64_t bytes, void* stream) {
+  if (!ws || !dst) return MK_ERR_NULL;
+  const void* src = nullptr;
+  int64_t have = 0;
+  const int nb = ws->have_sched ? ws->nb : 0;
+  switch (table) {
+    case MK_TAB_COUNTS: src = ws->counts; have = (int64_t)ws->E * 4; break;
+    case MK_TAB_OFFSETS: src = ws->offsets; have = (int64_t)(ws->E + 1) * 4; break;
+    case MK_TAB_MB_COUNTS: src = ws->mb_counts; have = (int64_t)nb * ws->E * 4; break;
+    case MK_TAB_MB_OFFSETS: src = ws->mb_offsets; have = (int64_t)nb * (ws->E + 1) * 4; break;
+    case MK_TAB_SORTED_POS: src = ws->sorted_pos; have = (int64_t)(ws->have_sched ? ws->R : 0) * 4; break;
+    case MK_TAB_INV: src = ws->inv; have = (int64_t)nb * ws->MB * 4; break;
+    case MK_TAB_ITEMS: src = ws->items; have = (int64_t)ws->item_cap * 16; break;
+    case MK_TAB_MB_ITEMS: src = ws->mb_items; have = (int64_t)(nb + 1) * 4; break;
+    case MK_TAB_RING: src = ws->ring; have = (int64_t)ws->ring_rows * ws->row_bytes; break;
+    default: return MK_ERR_CONFIG;
+  }
+  if (bytes < 0 || bytes > have) return MK_ERR_LIMIT;
+  if (bytes == 0) return MK_OK;
+  return hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess
+             ? MK_OK
+             : MK_ERR_HIP;
+}
+
+int mk_mxfp8_quantize(const void* in, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows > 0 && (!in || !codes || !scales)) return MK_ERR_NULL;
+  if (rows < 0 || K <= 0 || K % 32) return MK_ERR_SHAPE;
+  launch_quantize((const uint16_t*)in, rows, K, codes, scales, as_stream(stream));
+  return check_launch();
+}
+
+int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, const void* w_down,
+                       int32_t for_backward, void* packed, void* stream) {
+  if (!ws || !w_gate || !w_up || !w_down || !packed) return MK_ERR_NULL;
+  hipStream_t s = as_stream(stream);
+  const int E = ws->E, H = ws->H, I = ws->I;
+  if (ws->cfg.precision == MK_MXFP8) {
+    if (for_backward) return MK_ERR_UNSUPPORTED;
+    PackedMX p = packed_mx(ws, packed);
+    launch_quant_pack_gate_up((const uint16_t*)w_gate, (const uint16_t*)w_up, E, I, H, p.wgu_c, p.wgu_s, s);
+    launch_quantize((const uint16_t*)w_down, (int64_t)E * H, I, p.wd_c, p.wd_s, s);
+    return check_launch();
+  }
+  PackedBF16 p = packed_bf16(ws, packed);
+  launch_pack_gate_up((const uint16_t*)w_gate, (const uint16_t*)w_up, E, I, H, p.wgu, s);
+  launch_copy(w_down, p.wd, (int64_t)E * H * I * 2, s);
+  if (for_backward) {
+    launch_transpose(p.wd, E, H, I, p.wdT, s);         // [E, H, I] -> [E, I, H]
+    launch_transpose(p.wgu, E, 2 * I, H, p.wguT, s);   // [E, 2I, H] -> [E, H, 2I]
+  }
+  return check_launch();
+}
+
+int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* row_w, const void* packed,
+               void* out, void* fwd_ctx, void* stream) {
+  if (!ws) return MK_ERR_NULL;
+  if (!ws->have_sched) return MK_ERR_STATE;
+  const int R = ws->R;
+  if (R > 0 && (!x_src || !row_w || !packed || !out)) return MK_ERR_NULL;
+  if (mode != MK_FULL_LAYER && mode != MK_EXPERT_SHARE) return MK_ERR_CONFIG;
+  const int H = ws->H, I = ws->I, MB = ws->MB, k = ws->k;
+  int src_div = 1, kk = 1;
+  if (mode == MK_FULL_LAYER) {
+    if (R % k || MB % k) return MK_ERR_SHAPE;
+    src_div = k;
+    kk = k;
+  }
+  const bool mx = ws->cfg.precision == MK_MXFP8;
+  if (mx && fwd_ctx) return MK_ERR_UNSUPPORTED;
+  if (R == 0) return MK_OK;
+  hipStream_t s = as_stream(stream);
+  const int nb = ws->nb;
+  const int ring_mbs = ws->ring_rows / MB;
+  const uint16_t* x = (const uint16_t*)x_src;
+  const bool share = mode == MK_EXPERT_SHARE;
+  // expert share: GEMM2 writes w*y straight to arrival order (one rounding);
+  // full layer: GEMM2 keeps y in fp32 and the combine sums the k rows
+  uint16_t* out_fused = share ? (uint16_t*)out : nullptr;
+  if (!mx) {
+    PackedBF16 p = packed_bf16(ws, (void*)packed);
+    for (int b0 = 0; b0 < nb; b0 += ring_mbs) {
+      const int b1 = std::min(nb, b0 + ring_mbs);
+      {
+        Phase ph(ws, MK_PH_PERMUTE, s);
+        launch_gather_rows(x, H, ws->inv, src_div, (int64_t)b0 * MB, (int64_t)b1 * MB, ws->ring_rows,
+                           (uint16_t*)ws->ring, ws->n_cu, s);
+      }
+      Phase ph(ws, MK_PH_GEMM1, s);
+      launch_gemm1_bf16(item_range(ws, b0, b1), (const uint16_t*)ws->ring, ws->ring_rows, p.wgu, H, I, ws->a_buf,
+                        (float*)fwd_ctx, ws->n_cu, s);
+    }
+    Phase ph(ws, MK_PH_GEMM2, s);
+    launch_gemm2_bf16(item_range(ws, 0, nb), ws->a_buf, p.wd, H, I, ws->y_buf, out_fused, ws->inv, row_w, ws->n_cu,
+                      s);
+  } else {
+    PackedMX p = packed_mx(ws, (void*)packed);
+    uint8_t* rc = ws->ring;
+    uint8_t* rsc = ws->ring + (size_t)ws->ring_rows * H;
+    for (int b0 = 0; b0 < nb; b0 += ring_mbs) {
+      const int b1 = std::min(nb, b0 + ring_mbs);
+      {
+        Phase ph(ws, MK_PH_PERMUTE, s);
+        launch_gather_rows_mxfp8(x, H, ws->inv, src_div, (int64_t)b0 * MB, (int64_t)b1 * MB, ws->ring_rows, rc,
+                                 rsc, ws->n_cu, s);
+      }
+      Phase ph(ws, MK_PH_GEMM1, s);
+      launch_gemm1_mxfp8(item_range(ws, b0, b1), rc, rsc, ws->ring_rows, p.wgu_c, p.wgu_s, H, I, ws->a_buf,
+                         ws->n_cu, s);
+    }
+    {
+      Phase ph(ws, MK_PH_QUANT_A, s);
+      launch_quantize(ws->a_buf, (int64_t)nb * MB, I, ws->a_codes, ws->a_scales, s);
+    }
+    Phase ph(ws, MK_PH_GEMM2, s);
+    launch_gemm2_mxfp8(item_range(ws, 0, nb), ws->a_codes, ws->a_scales, p.wd_c, p.wd_s, H, I, ws->y_buf, out_fused,
+                       ws->inv, row_w, ws->n_cu, s);
+  }
+  Phase ph(ws, MK_PH_COMBINE, s);
+  if (share)
+    launch_zero_dropped_rows(ws->sorted_pos, R, (uint16_t*)out, H, s);
+  else
+    launch_combine(ws->y_buf, H, ws->sorted_pos, row_w, kk, (int64_t)R / kk, (uint16_t*)out, ws->n_cu, s);
+  return check_launch();
+}
+
+int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const void* x_src, const float* row_w,
+                const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up, float* dW_down,
+                float* d_row_w, void* stream) {
+  if (!ws) return MK_ERR_NULL;
+  if (!ws->have_sched) return MK_ERR_STATE;
+  if (mode != MK_EXPERT_SHARE || ws->cfg.precision != MK_BF16) return MK_ERR_UNSUPPORTED;
+  if (!ws->cfg.enable_backward) return MK_ERR_CONFIG;
+  if (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !dW_gate || !dW_up || !dW_down || !d_row_w)
+    return MK_ERR_NULL;
+  hipStream_t s = as_stream(stream);
+  const int H = ws->H, I = ws->I, MB = ws->MB, R = ws->R, nb = ws->nb;
+  PackedBF16 p = packed_bf16(ws, (void*)packed);
+  const ItemRange all = item_range(ws, 0, nb);
+  // pull the loss gradient into expert order (share of the reverse combine)
+  {
+    Phase ph(ws, MK_PH_BWD_GATHER, s);
+    launch_gather_rows((const uint16_t*)dY, H, ws->inv, 1, 0, (int64_t)nb * MB, 0, ws->dye, ws->n_cu, s);
+  }
+  // dA' GEMM with the SwiGLU backward and router-weight gradient fused
+  {
+    Phase ph(ws, MK_PH_BWD_DACT, s);
+    launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, ws->inv, row_w, ws->dgdu, ws->wa, ws->dw_part,
+                    ws->n_cu, s);
+  }
+  {
+    Phase ph(ws, MK_PH_BWD_DW, s);
+    launch_dw_finalize(ws->dw_part, I / 64, ws->sorted_pos, R, d_row_w, (uint16_t*)dX, H, s);
+  }
+  // dX GEMM, rows written back to arrival order (share of the reverse dispatch)
+  {
+    Phase ph(ws, MK_PH_BWD_DX, s);
+    launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, ws->inv, (uint16_t*)dX, ws->n_cu, s);
+  }
+  // weight gradients: row segments in reverse walk order; minibatches still in
+  // the ring are read there, the evicted ones are replayed from x_src
+  WgradArgs wa;
+  wa.E = ws->E;
+  wa.nb = nb;
+  wa.MB = MB;
+  wa.mb_counts = ws->mb_counts;
+  wa.mb_offsets = ws->mb_offsets;
+  wa.inv = ws->inv;
+  wa.src_div = 1;
+  const int ring_mbs = ws->ring_rows / MB;
+  const int first_resident = std::max(0, nb - ring_mbs);
+  {
+    Phase ph(ws, MK_PH_WGRAD_DOWN, s);
+    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->n_cu, s);
+  }
+  Phase ph(ws, MK_PH_WGRAD_GU, s);
+  launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, first_resident,
+                       (const uint16_t*)x_src, H, I, dW_gate, dW_up, ws->n_cu, s);
+  return check_launch();
+}
+
+int mk_timing_enable(mk_workspace* ws, int32_t on) {
+  if (!ws) return MK_ERR_NULL;
+  ws->timing = on ? 1 : 0;
+  return MK_OK;
+}
+
+int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out) {
+  if (!ws) return MK_ERR_NULL;
+  float ms[MK_PH_COUNT] = {0};
+  int32_t n[MK_PH_COUNT] = {0};
+  int rc = MK_OK;
+  for (auto& ev : *ws->events) {
+    float t = 0.f;
+    if (hipEventSynchronize(ev.stop) != hipSuccess || hipEventElapsedTime(&t, ev.start, ev.stop) != hipSuccess)
+      rc = MK_ERR_HIP;
+    if (ev.phase >= 0 && ev.phase < MK_PH_COUNT) {
+      ms[ev.phase] += t;
+      n[ev.phase] += 1;
+    }
+    (void)hipEventDestroy(ev.start);
+    (void)hipEventDestroy(ev.stop);
+  }
+  ws->events->clear();
+  for (int i = 0; i < MK_PH_COUNT; ++i) {
+    if (ms_out) ms_out[i] = ms[i];
+    if (launches_out) launches_out[i] = n[i];
+  }
+  return rc;
+}
+
+int mk_device_error(const mk_workspace* ws, uint32_t* dst, void* stream) {
+  if (!ws || !dst) return MK_ERR_NULL;
+  return hipMemcpyAsync(dst, ws->err, 4, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess ? MK_OK
+                                                                                                   : MK_ERR_HIP;
+}
+
+int64_t mk_two_wave_rows(int32_t H, int32_t I, int32_t n_cu, int32_t tile_m, int32_t tile_n) {
+  if (H <= 0 || I <= 0 || n_cu <= 0 || tile_m <= 0 || tile_n <= 0) return MK_ERR_SHAPE;
+  const int64_t num = 2LL * n_cu * tile_m * tile_n;
+  const int64_t den = std::min<int64_t>(2LL * I, H);
+  return (num + den - 1) / den;
+}
+
+const char* mk_status_string(int status) {
+  switch (status) {
+    case MK_OK: return "ok";
+    case MK_ERR_NULL: return "a required pointer is NULL";
+    case MK_ERR_SHAPE: return "unsupported shape";
+    case MK_ERR_RING: return "ring smaller than one minibatch";
+    case MK_ERR_LIMIT: return "above a workspace limit";
+    case MK_ERR_HIP: return "HIP runtime call failed";
+    case MK_ERR_STATE: return "call out of order";
+    case MK_ERR_UNSUPPORTED: return "combination not implemented";
+    case MK_ERR_CONFIG: return "invalid config field";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

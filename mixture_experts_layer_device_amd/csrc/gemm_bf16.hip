@@ -1,0 +1,453 @@
+// Expert-grouped bf16 GEMMs on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
+//
+// Every GEMM here is a persistent grid (one 512-thread workgroup per compute
+// unit, 132 KiB of LDS) that walks the device-side work table built by the
+// schedule: an item is (first sorted row, rows, expert, minibatch) and each
+// item is cut into 256-column tiles.  Tile counts are read on the device, so
+// the host never learns per-expert counts.  Each 256x256 output tile is
+// computed by one workgroup with a fixed K order, so results do not depend
+// on which workgroup takes which tile (bitwise repeatable).
+//
+// Mainloop: K in steps of 64; A and B tiles (256 x 64 bf16 each) go global ->
+// LDS with the asynchronous LDS-DMA loads (XOR-swizzled 16-byte granules),
+// double-buffered so the next step's loads overlap this step's MFMAs.  8 waves
+// as 2 (M) x 4 (N); a wave owns 128 x 64 outputs = 8 x 4 MFMA 16x16 fragments.
+// Epilogues stage their bf16 results through LDS and store whole rows with
+// 16-byte stores.
+//
+// Fragment layouts (measured on gfx950): A/B lane l holds row/col l%16 and
+// k = 8*(l/16) .. +7; the 16x16 fp32 result in lane l is column l%16, rows
+// 4*(l/16) .. +3.
+#include "gemm_common.h"
+
+namespace mk {
+namespace {
+
+constexpr int BM = G_BM, BN = G_BN, BK = 64, NT = G_NT;
+constexpr int FM = G_FM, FN = G_FN;
+constexpr int TILE_BYTES = BM * BK * 2;        // 32 KiB per operand tile
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int LDS_BYTES = 2 * STAGE_BYTES > STAGE_LDS_BYTES ? 2 * STAGE_BYTES : STAGE_LDS_BYTES;
+
+typedef GAcc Acc;
+
+__device__ __forceinline__ void zero_acc(Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const char* sA = st;
+  const char* sB = st + TILE_BYTES;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int g = ks * 4 + (lane >> 4);
+    bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[i] = *(const bf16x8_t*)(sA + lds_swz(wm * 128 + i * 16 + (lane & 15), g));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = *(const bf16x8_t*)(sB + lds_swz(wn * 64 + j * 16 + (lane & 15), g));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// C[256 x 256] = A[256 x K] * B[256 x K]^T, both K-contiguous.  arow(r) / brow(n)
+// return a pointer to element 0 of tile row r / tile column n.  Tiles go
+// global -> LDS directly (no staging registers): wave w fills rows
+// 32w .. 32w+31 of each operand, 8 rows (1 KiB) per instruction, and each lane
+// reads the granule that the swizzle puts in its slot.
+template <typename ARow, typename BRow>
+__device__ __forceinline__ void mainloop_nt(ARow arow, BRow brow, int K, char* lds, Acc& acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char* ap[4];
+  const char* bp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 32 + j * 8 + (lane >> 3);
+    const int g = lds_unswz(r, lane & 7);
+    ap[j] = (const char*)arow(r) + g * 16;
+    bp[j] = (const char*)brow(r) + g * 16;
+  }
+  const int wbase = wave * 4096;
+  auto issue = [&](int64_t kb, char* st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g2lds16(ap[j] + kb, st + wbase + j * 1024);
+      g2lds16(bp[j] + kb, st + TILE_BYTES + wbase + j * 1024);
+    }
+  };
+  zero_acc(acc);
+  issue(0, lds);
+  wait_all_mem();
+  __syncthreads();
+  const int KT = K / BK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) issue((int64_t)(kt + 1) * BK * 2, lds + (cur ^ 1) * STAGE_BYTES);
+    mma_stage(lds + cur * STAGE_BYTES, acc);
+    wait_all_mem();
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- GEMM1 ----
+// a[p, i] = silu(g) * u with [g | u] = ring[p] . W_gu[e]^T; W_gu is packed so
+// that each 32-column group holds 16 gate columns then the 16 up columns of
+// the same i.  a is a bf16 GEMM operand (stored [p, I]); optionally g and u
+// are saved in fp32 (packed order, [p, 2I]) for the backward.
+__global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ ring,
+                                                        int ring_rows, const uint16_t* __restrict__ wgu, int H,
+                                                        int I, uint16_t* __restrict__ a_out,
+                                                        float* __restrict__ gu_save) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = 2 * I / BN;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto arow = [&](int r) {
+      const int p = ti.pos0 + min(r, ti.rows - 1);
+      return ring + (int64_t)(p % ring_rows) * H;
+    };
+    auto brow = [&](int n) { return wgu + ((int64_t)ti.e * 2 * I + ti.n0 + n) * H; };
+    Acc acc;
+    mainloop_nt(arow, brow, H, lds, acc);
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = frag_row(i, v);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
+          stage_put(lds, r, wn * 32 + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+          if (gu_save && r < ti.rows) {
+            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * 64 + q * 32 + (lane & 15);
+            dst[0] = g;
+            dst[16] = u;
+          }
+        }
+      }
+    stage_flush<128>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
+    });
+  });
+}
+
+// ---------------------------------------------------------------- GEMM2 ----
+// y[p] = a[p] . W_d[e]^T  (W_d stored [E, H, I]).
+// SHARE: the router-weighted unpermute is fused: out[inv[p]] = bf16(w * y),
+//        one rounding, rows stored straight to arrival order.
+// else : y is kept in fp32 ([p, H]) for the full-layer combine.
+template <bool SHARE>
+__global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ a,
+                                                        const uint16_t* __restrict__ wd, int H, int I,
+                                                        float* __restrict__ y32, uint16_t* __restrict__ out,
+                                                        const int32_t* __restrict__ inv,
+                                                        const float* __restrict__ row_w) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = H / BN;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
+    auto brow = [&](int n) { return wd + ((int64_t)ti.e * H + ti.n0 + n) * I; };
+    Acc acc;
+    mainloop_nt(arow, brow, I, lds, acc);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = frag_row(i, v);
+        if (SHARE) {
+          const float w = r < ti.rows ? row_w[inv[ti.pos0 + r]] : 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), w * acc[i][j][v]);
+        } else if (r < ti.rows) {
+          float* dst = y32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
+        }
+      }
+    if (SHARE)
+      stage_flush<256>(lds, [&](int r) -> uint16_t* {
+        return r < ti.rows ? out + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
+      });
+  });
+}
+
+// ------------------------------------------------- backward: dA' + SwiGLU ----
+// dA'[p, i] = dYe[p] . W_d[e][:, i]  (B = W_d^T stored [E, I, H]).  Epilogue,
+// from the forward's fp32 g, u: a = silu(g) u; dw partial = sum_i dA' a over
+// this wave's 64 columns; dA = w dA'; dg = dA u s (1 + g (1 - s)); du = dA
+// silu(g) (bf16 GEMM operands, packed like W_gu); w*a (bf16 operand of the
+// down-projection weight gradient).
+__global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16_t* __restrict__ dye,
+                                                      const uint16_t* __restrict__ wdT, int H, int I,
+                                                      const float* __restrict__ gu,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ row_w,
+                                                      uint16_t* __restrict__ dgdu, uint16_t* __restrict__ wa,
+                                                      float* __restrict__ dw_part) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = I / BN;
+  const int slices = I / 64;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto arow = [&](int r) { return dye + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * H; };
+    auto brow = [&](int n) { return wdT + ((int64_t)ti.e * I + ti.n0 + n) * H; };
+    Acc acc;
+    mainloop_nt(arow, brow, H, lds, acc);
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
+    const int slice = (ti.n0 + wn * 64) / 64;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = frag_row(i, v);
+        const bool valid = r < ti.rows;
+        const int64_t p = ti.pos0 + (valid ? r : 0);
+        const float w = valid ? row_w[inv[p]] : 0.f;
+        float dws = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int ii = ti.n0 + frag_col(j);
+          const int gc = 32 * (ii >> 4) + (ii & 15);
+          float g = 0.f, u = 0.f;
+          if (valid) {
+            g = gu[p * 2 * I + gc];
+            u = gu[p * 2 * I + gc + 16];
+          }
+          const float s = sigmoidf_(g);
+          const float sl = g * s;
+          const float aa = sl * u;
+          const float dap = acc[i][j][v];
+          dws += dap * aa;
+          const float da = w * dap;
+          if (valid) {
+            dgdu[p * 2 * I + gc] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
+            dgdu[p * 2 * I + gc + 16] = (uint16_t)f32_to_bf16(da * sl);
+          }
+          stage_put(lds, r, frag_col(j), w * aa);
+        }
+        // fixed butterfly over the 16 lanes that share this row
+        dws += __shfl_xor(dws, 1);
+        dws += __shfl_xor(dws, 2);
+        dws += __shfl_xor(dws, 4);
+        dws += __shfl_xor(dws, 8);
+        if (valid && (lane & 15) == 0) dw_part[p * slices + slice] = dws;
+      }
+    stage_flush<256>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? wa + (int64_t)(ti.pos0 + r) * I + ti.n0 : nullptr;
+    });
+  });
+}
+
+// ------------------------------------------------------ backward: dX ----
+// dX[inv[p]] = dgdu[p] . W_gu[e]  (B = packed W_gu^T stored [E, H, 2I]); rows
+// are stored straight back to arrival order.
+__global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t* __restrict__ dgdu,
+                                                    const uint16_t* __restrict__ wguT, int H, int I,
+                                                    const int32_t* __restrict__ inv, uint16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = H / BN;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto arow = [&](int r) { return dgdu + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * 2 * I; };
+    auto brow = [&](int n) { return wguT + ((int64_t)ti.e * H + ti.n0 + n) * 2 * I; };
+    Acc acc;
+    mainloop_nt(arow, brow, 2 * I, lds, acc);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) stage_put(lds, frag_row(i, v), frag_col(j), acc[i][j][v]);
+    stage_flush<256>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? dX + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
+    });
+  });
+}
+
+// ----------------------------------------------------------- weight grads ----
+// C[m, n] = sum over the rows p of expert e of A[p, m] * B[p, n]: both operands
+// are row-major over p, so each loader thread fetches an 8 (rows) x 8 (columns)
+// bf16 block, transposes it in registers and stores 8 K-contiguous granules.
+// The K loop walks expert e's row segments minibatch by minibatch in reverse
+// (nb-1 .. 0), rows ascending inside each: a fixed order, no atomics.
+struct SegIter {
+  int b, k0, start, len;
+};
+
+__device__ __forceinline__ bool seg_next(SegIter& it, const WgradArgs& w, int e) {
+  it.k0 += BK;
+  while (it.k0 >= it.len) {
+    if (--it.b < 0) return false;
+    it.start = it.b * w.MB + w.mb_offsets[it.b * (w.E + 1) + e];
+    it.len = w.mb_counts[it.b * w.E + e];
+    it.k0 = 0;
+  }
+  return true;
+}
+
+template <int MODE>
+struct WgradOperands {
+  // MODE 0: A = dYe [p, H], B = w*a [p, I]          -> dW_down [E, H, I]
+  // MODE 1: A = dgdu [p, 2I] (packed), B = x rows   -> dW_gate / dW_up [E, I, H]
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  const uint16_t* ring;
+  int ring_rows, first_resident;
+  const uint16_t* x_src;
+  int64_t ldx;
+};
+
+template <int MODE>
+__device__ __forceinline__ void wgrad_load(const WgradOperands<MODE>& op, const WgradArgs& w,
+                                           const SegIter& it, int m0, int n0, u32x4_t (&v)[8]) {
+  const int tid = threadIdx.x;
+  const bool isB = tid >= 256;
+  const int lt = tid & 255, mc = lt & 31, kc = lt >> 5;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int kk = it.k0 + kc * 8 + c;
+    if (kk < it.len) {
+      const int64_t p = it.start + kk;
+      const uint16_t* ptr;
+      if (!isB) {
+        ptr = op.A + p * op.lda + m0 + mc * 8;
+      } else if (MODE == 0) {
+        ptr = op.B + p * op.ldb + n0 + mc * 8;
+      } else if (it.b >= op.first_resident) {
+        ptr = op.ring + (int64_t)(p % op.ring_rows) * op.ldx + n0 + mc * 8;
+      } else {
+        ptr = op.x_src + (int64_t)(w.inv[p] / w.src_div) * op.ldx + n0 + mc * 8;
+      }
+      v[c] = *(const u32x4_t*)ptr;
+    } else {
+      v[c] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void wgrad_store(char* st, const u32x4_t (&v)[8]) {
+  const int tid = threadIdx.x;
+  char* base = st + (tid >= 256 ? TILE_BYTES : 0);
+  const int lt = tid & 255, mc = lt & 31, kc = lt >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4_t lo, hi;   // columns 2j and 2j+1, 8 k values each
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x0 = v[2 * d][j], x1 = v[2 * d + 1][j];
+      lo[d] = (x0 & 0xFFFFu) | (x1 << 16);
+      hi[d] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+    }
+    *(u32x4_t*)(base + lds_swz(mc * 8 + 2 * j, kc)) = lo;
+    *(u32x4_t*)(base + lds_swz(mc * 8 + 2 * j + 1, kc)) = hi;
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MODE> op, int M, int N, int I,
+                                                      float* __restrict__ out0, float* __restrict__ out1) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int tm = M / BM, tn = N / BN;
+  const int per_e = tm * tn;
+  const int total = w.E * per_e;
+  for (int t = xcd_logical_block(); t < total; t += gridDim.x) {
+    const int e = t / per_e;
+    int mt, nt;
+    tile_coords(t - e * per_e, tm, tn, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    Acc acc;
+    zero_acc(acc);
+    SegIter cur{w.nb, 0, 0, 0};
+    bool have = seg_next(cur, w, e);
+    if (have) {
+      u32x4_t v[8];
+      wgrad_load<MODE>(op, w, cur, m0, n0, v);
+      wgrad_store(lds, v);
+      __syncthreads();
+      int stage = 0;
+      while (true) {
+        SegIter nxt = cur;
+        const bool more = seg_next(nxt, w, e);
+        if (more) wgrad_load<MODE>(op, w, nxt, m0, n0, v);
+        mma_stage(lds + stage * STAGE_BYTES, acc);
+        if (more) wgrad_store(lds + (stage ^ 1) * STAGE_BYTES, v);
+        __syncthreads();
+        if (!more) break;
+        cur = nxt;
+        stage ^= 1;
+      }
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int m = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + vv;
+        float* dst;
+        if (MODE == 0) {
+          dst = out0 + ((int64_t)e * M + m) * N;
+        } else {
+          const int ii = (m >> 5) * 16 + (m & 15);
+          dst = ((m & 31) < 16 ? out0 : out1) + ((int64_t)e * I + ii) * N;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[n0 + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][vv];
+      }
+  }
+}
+
+}  // namespace
+
+void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_rows, const uint16_t* wgu,
+                       int H, int I, uint16_t* a_out, float* gu_save, int n_cu, hipStream_t s) {
+  hipLaunchKernelGGL(gemm1_bf16_kernel, dim3(n_cu), dim3(NT), 0, s, ir, ring, ring_rows, wgu, H, I, a_out,
+                     gu_save);
+}
+
+void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* wd, int H, int I, float* y32,
+                       uint16_t* out, const int32_t* inv, const float* row_w, int n_cu, hipStream_t s) {
+  if (out)
+    hipLaunchKernelGGL(gemm2_bf16_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv, row_w);
+  else
+    hipLaunchKernelGGL(gemm2_bf16_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv,
+                       row_w);
+}
+
+void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,
+                     const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part, int n_cu,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(bwd_dact_kernel, dim3(n_cu), dim3(NT), 0, s, ir, dye, wdT, H, I, gu, inv, row_w, dgdu, wa,
+                     dw_part);
+}
+
+void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wguT, int H, int I,
+                   const int32_t* inv, uint16_t* dX, int n_cu, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX);
+}
+
+void launch_wgrad_down(const WgradArgs& w, const uint16_t* dye, const uint16_t* wa, int H, int I,
+                       float* dW_down, int n_cu, hipStream_t s) {
+  WgradOperands<0> op{dye, H, wa, I, nullptr, 1, 0, nullptr, 0};
+  hipLaunchKernelGGL(wgrad_kernel<0>, dim3(n_cu), dim3(NT), 0, s, w, op, H, I, I, dW_down, (float*)nullptr);
+}
+
+void launch_wgrad_gate_up(const WgradArgs& w, const uint16_t* dgdu, const uint16_t* ring, int32_t ring_rows,
+                          int first_resident, const uint16_t* x_src, int H, int I, float* dW_gate, float* dW_up,
+                          int n_cu, hipStream_t s) {
+  WgradOperands<1> op{dgdu, 2 * (int64_t)I, nullptr, 0, ring, ring_rows, first_resident, x_src, H};
+  hipLaunchKernelGGL(wgrad_kernel<1>, dim3(n_cu), dim3(NT), 0, s, w, op, 2 * I, H, I, dW_gate, dW_up);
+}
+
+}  // namespace mk

@@ -1,0 +1,87 @@
+// Pieces shared by the expert-grouped GEMM kernels: the persistent walk over
+// the device work table, the XCD-aware block numbering, and the LDS-staged
+// epilogue that turns the MFMA fragment layout into coalesced row stores.
+#pragma once
+#include "mk_device.h"
+#include "mk_internal.h"
+
+namespace mk {
+
+constexpr int G_BM = 256, G_BN = 256, G_NT = 512;
+constexpr int G_FM = 8, G_FN = 4;             // 16x16 fragments per wave (128 x 64)
+constexpr int STAGE_ROW_BYTES = 528;          // 512 + 16 pad: conflict-light fragment writes
+constexpr int STAGE_LDS_BYTES = G_BM * STAGE_ROW_BYTES;
+
+typedef f32x4_t GAcc[G_FM][G_FN];
+
+// Blocks are dealt to the 8 XCDs round-robin; renumber them so that
+// consecutive logical ids share an XCD (and its L2).
+__device__ __forceinline__ int xcd_logical_block() {
+  const int b = blockIdx.x, G = gridDim.x;
+  return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+// Tile t -> (item, n-tile), in groups of 4 items so that tiles running at the
+// same time on one XCD share A rows (same item) and B columns (same n).
+__device__ __forceinline__ void tile_coords(int t, int n_items, int ntn, int& item, int& nt) {
+  constexpr int GM = 4;
+  const int group = GM * ntn;
+  const int g = t / group;
+  const int first = g * GM;
+  const int gm = min(GM, n_items - first);
+  const int local = t - g * group;
+  item = first + local % gm;
+  nt = local / gm;
+}
+
+struct TileInfo {
+  int pos0, rows, e, n0;
+};
+
+// Persistent walk over the tiles of the items of minibatches [mb_lo, mb_hi).
+template <typename Body>
+__device__ __forceinline__ void for_each_tile(const ItemRange& ir, int ntn, Body body) {
+  const int i_lo = min(ir.mb_items[ir.mb_lo], ir.item_cap);
+  const int i_hi = min(ir.mb_items[ir.mb_hi], ir.item_cap);
+  const int n_items = i_hi - i_lo;
+  const int total = n_items * ntn;
+  for (int t = xcd_logical_block(); t < total; t += gridDim.x) {
+    int it, nt;
+    tile_coords(t, n_items, ntn, it, nt);
+    const int* item = ir.items + 4 * (i_lo + it);
+    TileInfo ti{item[0], item[1], item[2], nt * G_BN};
+    body(ti);
+  }
+}
+
+__device__ __forceinline__ int frag_row(int i, int v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave >> 2) * 128 + i * 16 + 4 * (lane >> 4) + v;
+}
+__device__ __forceinline__ int frag_col(int j) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave & 3) * 64 + j * 16 + (lane & 15);
+}
+
+// Stage a tile of bf16 values through LDS and store each row's COLS values
+// (COLS * 2 bytes, contiguous) with 16-byte stores.
+//   put(stage)            : the caller writes its fragments with stage_put()
+//   row_dst(r) -> uint16* : destination of tile row r, or nullptr to skip it
+// Must be called by the whole workgroup; LDS is free on entry and on exit.
+__device__ __forceinline__ void stage_put(char* lds, int row, int col, float v) {
+  *(uint16_t*)(lds + row * STAGE_ROW_BYTES + col * 2) = (uint16_t)f32_to_bf16(v);
+}
+
+template <int COLS, typename RowDst>
+__device__ __forceinline__ void stage_flush(char* lds, RowDst row_dst) {
+  constexpr int CPR = COLS / 8;                 // 16-byte chunks per row
+  __syncthreads();
+  for (int id = threadIdx.x; id < G_BM * CPR; id += G_NT) {
+    const int r = id / CPR, c = id - r * CPR;
+    uint16_t* dst = row_dst(r);
+    if (dst) *(u32x4_t*)(dst + c * 8) = *(const u32x4_t*)(lds + r * STAGE_ROW_BYTES + c * 16);
+  }
+  __syncthreads();
+}
+
+}  // namespace mk

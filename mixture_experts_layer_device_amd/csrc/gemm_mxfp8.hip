@@ -1,0 +1,200 @@
+// Expert-grouped MXFP8 GEMMs on gfx950 block-scaled MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3, one E8M0 scale per 32 K).
+//
+// Same persistent walk, tile shape (256 x 256, 8 waves of 128 x 64) and
+// double-buffered LDS pipeline as the bf16 GEMMs; a K step is 128 codes (one
+// MFMA deep), i.e. 4 MX blocks whose 4 scale bytes per row travel as one
+// dword next to the tile.
+//
+// Operand layout of the block-scaled MFMA (measured on gfx950): lane group
+// g = l/16 of a 16-row fragment supplies k in [16g, 16g+16) in its bytes
+// 0..15 and k in [64+16g, 64+16g+16) in bytes 16..31, and its scale applies to
+// k in [32g, 32g+32).  So lane group g takes 16-byte granules g and g+4 of the
+// 128-byte K step (MX block g = granules 2g and 2g+1 land in hardware block g)
+// and passes scale byte g.
+#include "gemm_common.h"
+
+namespace mk {
+namespace {
+
+constexpr int BM = G_BM, BN = G_BN, BKB = 128, NT = G_NT;   // BKB: K bytes (= codes) per step
+constexpr int FM = G_FM, FN = G_FN;
+constexpr int TILE_BYTES = BM * BKB;                      // 32 KiB codes per operand
+constexpr int SCALE_BYTES = BM * 4;                       // one dword per row
+constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * SCALE_BYTES;
+constexpr int LDS_BYTES = 2 * STAGE_BYTES > STAGE_LDS_BYTES ? 2 * STAGE_BYTES : STAGE_LDS_BYTES;
+
+typedef GAcc Acc;
+
+__device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const char* sA = st;
+  const char* sB = st + TILE_BYTES;
+  const uint32_t* scA = (const uint32_t*)(st + 2 * TILE_BYTES);
+  const uint32_t* scB = scA + BM;
+  const int g = lane >> 4;
+  i32x8_t bfr[FN];
+  int sb[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int row = wn * 64 + j * 16 + (lane & 15);
+    const u32x4_t lo = *(const u32x4_t*)(sB + lds_swz(row, g));
+    const u32x4_t hi = *(const u32x4_t*)(sB + lds_swz(row, g + 4));
+    bfr[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    sb[j] = (int)((scB[row] >> (8 * g)) & 0xFFu);
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = wm * 128 + i * 16 + (lane & 15);
+    const u32x4_t lo = *(const u32x4_t*)(sA + lds_swz(row, g));
+    const u32x4_t hi = *(const u32x4_t*)(sA + lds_swz(row, g + 4));
+    const i32x8_t af = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const int sa = (int)((scA[row] >> (8 * g)) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[j], acc[i][j], 0, 0, 0, sa, 0, sb[j]);
+  }
+}
+
+// C = A . B^T over K codes; arow/brow give the code row, ascale/bscale the
+// scale row.  Codes go global -> LDS directly as in the bf16 mainloop; waves
+// 0-3 also fetch A's scale dwords (64 rows each) and waves 4-7 B's.
+template <typename ARow, typename BRow, typename ASc, typename BSc>
+__device__ __forceinline__ void mainloop(ARow arow, BRow brow, ASc ascale, BSc bscale, int K, char* lds, Acc& acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint8_t* ap[4];
+  const uint8_t* bp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 32 + j * 8 + (lane >> 3);
+    const int g = lds_unswz(r, lane & 7);
+    ap[j] = arow(r) + g * 16;
+    bp[j] = brow(r) + g * 16;
+  }
+  const uint8_t* sp = wave < 4 ? ascale(wave * 64 + lane) : bscale((wave - 4) * 64 + lane);
+  const int wbase = wave * 4096;
+  const int sbase = 2 * TILE_BYTES + wave * 256;
+  auto issue = [&](int kt, char* st) {
+    const int64_t kb = (int64_t)kt * BKB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g2lds16(ap[j] + kb, st + wbase + j * 1024);
+      g2lds16(bp[j] + kb, st + TILE_BYTES + wbase + j * 1024);
+    }
+    g2lds4(sp + kt * 4, st + sbase);
+  };
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0, lds);
+  wait_all_mem();
+  __syncthreads();
+  const int KT = K / BKB;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) issue(kt + 1, lds + (cur ^ 1) * STAGE_BYTES);
+    mma_stage(lds + cur * STAGE_BYTES, acc);
+    wait_all_mem();
+    __syncthreads();
+  }
+}
+
+// a[p, i] = silu(g) * u (bf16) from MXFP8 ring rows and packed MXFP8 W_gu.
+__global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ rc,
+                                                         const uint8_t* __restrict__ rsc, int ring_rows,
+                                                         const uint8_t* __restrict__ wc,
+                                                         const uint8_t* __restrict__ wsc, int H, int I,
+                                                         uint16_t* __restrict__ a_out) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = 2 * I / BN;
+  const int nbh = H / 32;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto rrow = [&](int r) { return (int64_t)((ti.pos0 + min(r, ti.rows - 1)) % ring_rows); };
+    auto arow = [&](int r) { return rc + rrow(r) * H; };
+    auto asc = [&](int r) { return rsc + rrow(r) * nbh; };
+    auto brow = [&](int n) { return wc + ((int64_t)ti.e * 2 * I + ti.n0 + n) * H; };
+    auto bsc = [&](int n) { return wsc + ((int64_t)ti.e * 2 * I + ti.n0 + n) * nbh; };
+    Acc acc;
+    mainloop(arow, brow, asc, bsc, H, lds, acc);
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
+          stage_put(lds, frag_row(i, v), wn * 32 + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+        }
+    stage_flush<128>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
+    });
+  });
+}
+
+// y[p] = D(a_q[p]) . D(W_d[e])^T with W_d codes [E, H, I] + scales [E, H, I/32];
+// SHARE: out[inv[p]] = bf16(w * y) (fused weighted unpermute); else fp32 y.
+template <bool SHARE>
+__global__ __launch_bounds__(NT) void gemm2_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ ac,
+                                                         const uint8_t* __restrict__ asc_,
+                                                         const uint8_t* __restrict__ wc,
+                                                         const uint8_t* __restrict__ wsc, int H, int I,
+                                                         float* __restrict__ y32, uint16_t* __restrict__ out,
+                                                         const int32_t* __restrict__ inv,
+                                                         const float* __restrict__ row_w) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = H / BN;
+  const int nbi = I / 32;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto prow = [&](int r) { return (int64_t)(ti.pos0 + min(r, ti.rows - 1)); };
+    auto arow = [&](int r) { return ac + prow(r) * I; };
+    auto asc = [&](int r) { return asc_ + prow(r) * nbi; };
+    auto brow = [&](int n) { return wc + ((int64_t)ti.e * H + ti.n0 + n) * I; };
+    auto bsc = [&](int n) { return wsc + ((int64_t)ti.e * H + ti.n0 + n) * nbi; };
+    Acc acc;
+    mainloop(arow, brow, asc, bsc, I, lds, acc);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = frag_row(i, v);
+        if (SHARE) {
+          const float w = r < ti.rows ? row_w[inv[ti.pos0 + r]] : 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), w * acc[i][j][v]);
+        } else if (r < ti.rows) {
+          float* dst = y32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
+        }
+      }
+    if (SHARE)
+      stage_flush<256>(lds, [&](int r) -> uint16_t* {
+        return r < ti.rows ? out + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
+      });
+  });
+}
+
+}  // namespace
+
+void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const uint8_t* ring_scales,
+                        int32_t ring_rows, const uint8_t* wgu_codes, const uint8_t* wgu_scales, int H, int I,
+                        uint16_t* a_out, int n_cu, hipStream_t s) {
+  hipLaunchKernelGGL(gemm1_mxfp8_kernel, dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales, ring_rows,
+                     wgu_codes, wgu_scales, H, I, a_out);
+}
+
+void launch_gemm2_mxfp8(const ItemRange& ir, const uint8_t* a_codes, const uint8_t* a_scales,
+                        const uint8_t* wd_codes, const uint8_t* wd_scales, int H, int I, float* y32,
+                        uint16_t* out, const int32_t* inv, const float* row_w, int n_cu, hipStream_t s) {
+  if (out)
+    hipLaunchKernelGGL(gemm2_mxfp8_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, a_codes, a_scales, wd_codes,
+                       wd_scales, H, I, y32, out, inv, row_w);
+  else
+    hipLaunchKernelGGL(gemm2_mxfp8_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, a_codes, a_scales, wd_codes,
+                       wd_scales, H, I, y32, out, inv, row_w);
+}
+
+}  // namespace mk

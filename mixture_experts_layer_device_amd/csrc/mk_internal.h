@@ -1,0 +1,125 @@
+// Host-side internals of the MoE layer library: the workspace and the
+// launchers each kernel file exports to the C ABI in api.hip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mk.h"
+
+#define MK_TILE_M 256        // rows per GEMM work item
+#define MK_TILE_N 256
+#define MK_SCHED_CHUNK 256   // rows per schedule workgroup
+#define MK_MAX_EXPERTS 1024
+#define MK_MAX_TOPK 32
+
+#include <vector>
+
+struct mk_phase_event {
+  int phase;
+  hipEvent_t start, stop;
+};
+
+struct mk_workspace {
+  mk_config cfg;
+  int32_t max_rows, H, I, E, k;
+  int32_t MB, ring_rows, row_bytes, nb_max, cpm, item_cap, n_cu, device;
+  int64_t npos;               // nb_max * MB sorted positions
+  // last schedule
+  int32_t R, nb, have_sched;
+  // device memory
+  void* base;
+  size_t bytes;
+  uint32_t* err;
+  int32_t *chunk_counts, *mb_counts, *mb_offsets, *counts, *offsets;
+  int32_t *sorted_pos, *inv, *items, *mb_items;
+  uint8_t* ring;              // bf16 rows, or MXFP8 codes [ring_rows, H] then scales [ring_rows, H/32]
+  uint16_t* a_buf;            // [npos, I] bf16 SwiGLU output, expert order
+  uint8_t *a_codes, *a_scales;// MXFP8 copy of a
+  float* y_buf;               // [npos, H] fp32 expert outputs, expert order (full-layer combine)
+  uint16_t *dye, *dgdu, *wa;  // backward: [npos, H], [npos, 2I], [npos, I]
+  float* dw_part;             // [npos, I/64]
+  // optional per-phase timing
+  int timing;
+  std::vector<mk_phase_event>* events;
+};
+
+namespace mk {
+
+// ---- schedule.hip --------------------------------------------------------
+void launch_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, hipStream_t s);
+
+// ---- route.hip -----------------------------------------------------------
+void launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H,
+                  int E, int k, int renorm, int32_t* idx, float* w, hipStream_t s);
+
+// ---- rows.hip ------------------------------------------------------------
+// dst row (p mod ring_rows, or p if ring_rows == 0) <- src row src_of(inv[p]),
+// for sorted positions p in [p_lo, p_hi); src_of(r) = r / src_div.
+void launch_gather_rows(const uint16_t* src, int64_t H, const int32_t* inv, int src_div,
+                        int64_t p_lo, int64_t p_hi, int32_t ring_rows, uint16_t* dst,
+                        int n_cu, hipStream_t s);
+void launch_gather_rows_mxfp8(const uint16_t* src, int64_t H, const int32_t* inv, int src_div,
+                              int64_t p_lo, int64_t p_hi, int32_t ring_rows, uint8_t* codes,
+                              uint8_t* scales, int n_cu, hipStream_t s);
+void launch_combine(const float* y, int64_t H, const int32_t* sorted_pos, const float* row_w,
+                    int k, int64_t n_out, uint16_t* out, int n_cu, hipStream_t s);
+// zero the out rows whose sorted_pos is -1 (dropped rows; expert-share mode)
+void launch_zero_dropped_rows(const int32_t* sorted_pos, int64_t R, uint16_t* out, int64_t H, hipStream_t s);
+void launch_quantize(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                     hipStream_t s);
+void launch_dw_finalize(const float* dw_part, int slices, const int32_t* sorted_pos, int64_t R,
+                        float* d_row_w, uint16_t* dX, int64_t H, hipStream_t s);
+void launch_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H,
+                         uint16_t* out, hipStream_t s);
+void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+void launch_transpose(const uint16_t* in, int batch, int rows, int cols, uint16_t* out,
+                      hipStream_t s);
+void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+
+// ---- gemm_bf16.hip -------------------------------------------------------
+struct ItemRange {
+  const int32_t* items;     // [cap, 4]
+  const int32_t* mb_items;  // [nb+1]
+  int32_t mb_lo, mb_hi;     // minibatches covered by this launch
+  int32_t item_cap;
+};
+
+void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_rows,
+                       const uint16_t* wgu, int H, int I, uint16_t* a_out, float* gu_save,
+                       int n_cu, hipStream_t s);
+// out != nullptr: expert share, out[inv[p]] = bf16(row_w[inv[p]] * y[p]); else y32[p] = y[p]
+void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* wd, int H, int I,
+                       float* y32, uint16_t* out, const int32_t* inv, const float* row_w, int n_cu,
+                       hipStream_t s);
+void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I,
+                     const float* gu, const int32_t* inv, const float* row_w, uint16_t* dgdu,
+                     uint16_t* wa, float* dw_part, int n_cu, hipStream_t s);
+void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wguT, int H, int I,
+                   const int32_t* inv, uint16_t* dX, int n_cu, hipStream_t s);
+
+struct WgradArgs {
+  int E, nb, MB;
+  const int32_t* mb_counts;    // [nb, E]
+  const int32_t* mb_offsets;   // [nb, E+1]
+  const int32_t* inv;
+  int src_div;
+};
+// dW_down[e] (H x I) = sum_p dye[p]^T (x) wa[p]
+void launch_wgrad_down(const WgradArgs& wa_args, const uint16_t* dye, const uint16_t* wa, int H,
+                       int I, float* dW_down, int n_cu, hipStream_t s);
+// dW_gate/dW_up[e] (I x H) from dgdu (packed 2I) and the x rows: minibatches
+// b >= first_resident come from the ring, earlier ones straight from x_src.
+void launch_wgrad_gate_up(const WgradArgs& wa_args, const uint16_t* dgdu, const uint16_t* ring,
+                          int32_t ring_rows, int first_resident, const uint16_t* x_src, int H,
+                          int I, float* dW_gate, float* dW_up, int n_cu, hipStream_t s);
+
+// ---- gemm_mxfp8.hip -----------------------------------------------------
+void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const uint8_t* ring_scales,
+                        int32_t ring_rows, const uint8_t* wgu_codes, const uint8_t* wgu_scales,
+                        int H, int I, uint16_t* a_out, int n_cu, hipStream_t s);
+void launch_gemm2_mxfp8(const ItemRange& ir, const uint8_t* a_codes, const uint8_t* a_scales,
+                        const uint8_t* wd_codes, const uint8_t* wd_scales, int H, int I,
+                        float* y32, uint16_t* out, const int32_t* inv, const float* row_w, int n_cu,
+                        hipStream_t s);
+
+}  // namespace mk

@@ -1,0 +1,290 @@
+// Row-granular HBM kernels: the permute into the ring (bf16 copy or fused
+// MXFP8 quantise), the backward's dY gather, the fixed-order combine, the
+// standalone MXFP8 quantiser, the router-weight-gradient finalisation and the
+// one-off weight packing.
+//
+// Every row here is a contiguous run of >= 512 bytes, so one wave per row
+// with 16-byte lane accesses is fully coalesced as it stands; the loads of a
+// row are all issued before its stores so each lane keeps several in flight.
+#include "mk_device.h"
+#include "mk_internal.h"
+
+#include <algorithm>
+
+namespace mk {
+namespace {
+
+constexpr int RT = 256;   // threads per block in the row kernels
+
+__device__ __forceinline__ int64_t wave_id() { return ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; }
+__device__ __forceinline__ int64_t wave_count() { return ((int64_t)gridDim.x * blockDim.x) >> 6; }
+
+// dst row (p mod ring_rows, or p) <- src row inv[p] / src_div
+__global__ __launch_bounds__(RT) void gather_rows_kernel(const uint16_t* __restrict__ src, int64_t H,
+                                                         const int32_t* __restrict__ inv, int src_div,
+                                                         int64_t p_lo, int64_t p_hi, int32_t ring_rows,
+                                                         uint16_t* __restrict__ dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n16 = H / 8;
+  for (int64_t p = p_lo + wave_id(); p < p_hi; p += wave_count()) {
+    const int r = inv[p];
+    if (r < 0) continue;
+    const u32x4_t* s = (const u32x4_t*)(src + (int64_t)(r / src_div) * H);
+    u32x4_t* d = (u32x4_t*)(dst + (ring_rows ? p % ring_rows : p) * H);
+    for (int64_t g0 = lane; g0 < n16; g0 += 64 * 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (g0 + 64 * u < n16) v[u] = __builtin_nontemporal_load(s + g0 + 64 * u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (g0 + 64 * u < n16) d[g0 + 64 * u] = v[u];
+    }
+  }
+}
+
+// Quantise one 32-element block (4 x 16 bytes of bf16) -> 32 codes + scale.
+__device__ __forceinline__ uint32_t quant_block(const u32x4_t (&v)[4], u32x4_t (&c)[2]) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      amax = max(amax, v[q][d] & 0x7FFFu);
+      amax = max(amax, (v[q][d] >> 16) & 0x7FFFu);
+    }
+  const int s = mx_scale_code(amax);
+  const int se = s - 127;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int d = 0; d < 4; d += 2) {
+      const uint32_t b0 = mx_encode(v[q][d] & 0xFFFFu, se), b1 = mx_encode(v[q][d] >> 16, se);
+      const uint32_t b2 = mx_encode(v[q][d + 1] & 0xFFFFu, se), b3 = mx_encode(v[q][d + 1] >> 16, se);
+      c[q >> 1][(q & 1) * 2 + (d >> 1)] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+  return (uint32_t)s;
+}
+
+// MXFP8 rows: codes[dst] / scales[dst] <- quantised src row (inv == nullptr: dst row = src row = p).
+__global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t H,
+                                                               const int32_t* __restrict__ inv, int src_div,
+                                                               int64_t p_lo, int64_t p_hi, int32_t ring_rows,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nblk = H / 32;
+  for (int64_t p = p_lo + wave_id(); p < p_hi; p += wave_count()) {
+    int64_t sr = p;
+    if (inv) {
+      const int r = inv[p];
+      if (r < 0) continue;
+      sr = r / src_div;
+    }
+    const int64_t dr = ring_rows ? p % ring_rows : p;
+    const u32x4_t* s = (const u32x4_t*)(src + sr * H);
+    u32x4_t* dc = (u32x4_t*)(codes + dr * H);
+    uint8_t* ds = scales + dr * nblk;
+    for (int64_t b = lane; b < nblk; b += 64) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = __builtin_nontemporal_load(s + b * 4 + q);
+      u32x4_t c[2];
+      const uint32_t sc = quant_block(v, c);
+      dc[b * 2] = c[0];
+      dc[b * 2 + 1] = c[1];
+      ds[b] = (uint8_t)sc;
+    }
+  }
+}
+
+// out[o] = sum_{j < kk} w[o*kk + j] * y[sorted_pos[o*kk + j]], j ascending, fp32,
+// one rounding to bf16 (y is the fp32 GEMM2 output).  A dropped row
+// (sorted_pos -1) adds nothing.
+__global__ __launch_bounds__(RT) void combine_kernel(const float* __restrict__ y, int64_t H,
+                                                     const int32_t* __restrict__ sorted_pos,
+                                                     const float* __restrict__ row_w, int kk, int64_t n_out,
+                                                     uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n8 = H / 8;
+  for (int64_t o = wave_id(); o < n_out; o += wave_count()) {
+    for (int64_t g = lane; g < n8; g += 64) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int j = 0; j < kk; ++j) {
+        const int64_t r = o * kk + j;
+        const int pos = sorted_pos[r];
+        if (pos < 0) continue;
+        const float w = row_w[r];
+        const f32x4_t* src = (const f32x4_t*)(y + (int64_t)pos * H + g * 8);
+        const f32x4_t v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[q] += w * v0[q];
+          acc[4 + q] += w * v1[q];
+        }
+      }
+      u32x4_t ov;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) ov[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
+      __builtin_nontemporal_store(ov, (u32x4_t*)(out + o * H + g * 8));
+    }
+  }
+}
+
+__global__ void zero_dropped_rows_kernel(const int32_t* __restrict__ sorted_pos, int64_t R,
+                                         uint16_t* __restrict__ out, int64_t H) {
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    if (sorted_pos[r] >= 0) continue;
+    for (int64_t h = threadIdx.x; h < H; h += blockDim.x) out[r * H + h] = 0;
+  }
+}
+
+// d_row_w[r] = sum over slices (ascending) of dw_part[sorted_pos[r]]; a dropped
+// row gets 0 and a zero dX row.
+__global__ void dw_finalize_kernel(const float* __restrict__ dw_part, int slices,
+                                   const int32_t* __restrict__ sorted_pos, int64_t R, float* __restrict__ d_row_w,
+                                   uint16_t* __restrict__ dX, int64_t H) {
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < R; r += (int64_t)gridDim.x * blockDim.x) {
+    const int pos = sorted_pos[r];
+    if (pos >= 0) {
+      float s = 0.f;
+      for (int i = 0; i < slices; ++i) s += dw_part[(int64_t)pos * slices + i];
+      d_row_w[r] = s;
+    } else {
+      d_row_w[r] = 0.f;
+      for (int64_t h = 0; h < H; ++h) dX[r * H + h] = 0;
+    }
+  }
+}
+
+// packed row c of expert e: gate row (c/32)*16 + c%16 if c%32 < 16, else up row.
+__global__ void pack_gate_up_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu, int I, int H,
+                                    uint16_t* __restrict__ out) {
+  const int64_t row = blockIdx.x;            // e * 2I + c
+  const int e = (int)(row / (2 * I)), c = (int)(row % (2 * I));
+  const int i = (c >> 5) * 16 + (c & 15);
+  const uint16_t* src = ((c & 31) < 16 ? wg : wu) + ((int64_t)e * I + i) * H;
+  const u32x4_t* s = (const u32x4_t*)src;
+  u32x4_t* d = (u32x4_t*)(out + row * H);
+  for (int g = threadIdx.x; g < H / 8; g += blockDim.x) d[g] = s[g];
+}
+
+// MXFP8 codes/scales of packed gate/up row e*2I + c (row mapping as above),
+// one wave per row.
+__global__ __launch_bounds__(RT) void quant_pack_gate_up_kernel(const uint16_t* __restrict__ wg,
+                                                                const uint16_t* __restrict__ wu, int64_t n_rows,
+                                                                int I, int H, uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nblk = H / 32;
+  for (int64_t row = wave_id(); row < n_rows; row += wave_count()) {
+    const int e = (int)(row / (2 * I)), c = (int)(row % (2 * I));
+    const int i = (c >> 5) * 16 + (c & 15);
+    const u32x4_t* s = (const u32x4_t*)(((c & 31) < 16 ? wg : wu) + ((int64_t)e * I + i) * H);
+    u32x4_t* dc = (u32x4_t*)(codes + row * H);
+    uint8_t* ds = scales + row * nblk;
+    for (int64_t b = lane; b < nblk; b += 64) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = s[b * 4 + q];
+      u32x4_t cc[2];
+      const uint32_t sc = quant_block(v, cc);
+      dc[b * 2] = cc[0];
+      dc[b * 2 + 1] = cc[1];
+      ds[b] = (uint8_t)sc;
+    }
+  }
+}
+
+// out[b][c][r] = in[b][r][c], 64 x 64 tiles through LDS.
+__global__ void transpose_kernel(const uint16_t* __restrict__ in, int rows, int cols, uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* src = in + b * rows * (int64_t)cols;
+  uint16_t* dst = out + b * rows * (int64_t)cols;
+  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
+    const int r = r0 + i, c = c0 + threadIdx.x;
+    if (r < rows && c < cols) tile[i][threadIdx.x] = src[(int64_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
+    const int c = c0 + i, r = r0 + threadIdx.x;
+    if (c < cols && r < rows) dst[(int64_t)c * rows + r] = tile[threadIdx.x][i];
+  }
+}
+
+int row_grid(int64_t rows, int n_cu) {
+  const int64_t want = (rows + (RT / 64) - 1) / (RT / 64);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)n_cu * 8));
+}
+
+}  // namespace
+
+void launch_gather_rows(const uint16_t* src, int64_t H, const int32_t* inv, int src_div, int64_t p_lo,
+                        int64_t p_hi, int32_t ring_rows, uint16_t* dst, int n_cu, hipStream_t s) {
+  if (p_hi <= p_lo) return;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(row_grid(p_hi - p_lo, n_cu)), dim3(RT), 0, s, src, H, inv, src_div,
+                     p_lo, p_hi, ring_rows, dst);
+}
+
+void launch_gather_rows_mxfp8(const uint16_t* src, int64_t H, const int32_t* inv, int src_div, int64_t p_lo,
+                              int64_t p_hi, int32_t ring_rows, uint8_t* codes, uint8_t* scales, int n_cu,
+                              hipStream_t s) {
+  if (p_hi <= p_lo) return;
+  hipLaunchKernelGGL(gather_rows_mxfp8_kernel, dim3(row_grid(p_hi - p_lo, n_cu)), dim3(RT), 0, s, src, H, inv,
+                     src_div, p_lo, p_hi, ring_rows, codes, scales);
+}
+
+void launch_quantize(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(gather_rows_mxfp8_kernel, dim3(row_grid(rows, 256)), dim3(RT), 0, s, in, (int64_t)K,
+                     (const int32_t*)nullptr, 1, (int64_t)0, rows, 0, codes, scales);
+}
+
+void launch_zero_dropped_rows(const int32_t* sorted_pos, int64_t R, uint16_t* out, int64_t H, hipStream_t s) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(zero_dropped_rows_kernel, dim3((unsigned)std::min<int64_t>(R, 4096)), dim3(256), 0, s,
+                     sorted_pos, R, out, H);
+}
+
+void launch_combine(const float* y, int64_t H, const int32_t* sorted_pos, const float* row_w, int k,
+                    int64_t n_out, uint16_t* out, int n_cu, hipStream_t s) {
+  if (n_out <= 0) return;
+  hipLaunchKernelGGL(combine_kernel, dim3(row_grid(n_out, n_cu)), dim3(RT), 0, s, y, H, sorted_pos, row_w, k,
+                     n_out, out);
+}
+
+void launch_dw_finalize(const float* dw_part, int slices, const int32_t* sorted_pos, int64_t R, float* d_row_w,
+                        uint16_t* dX, int64_t H, hipStream_t s) {
+  if (R <= 0) return;
+  const int blocks = (int)std::min<int64_t>((R + 255) / 256, 2048);
+  hipLaunchKernelGGL(dw_finalize_kernel, dim3(blocks), dim3(256), 0, s, dw_part, slices, sorted_pos, R, d_row_w,
+                     dX, H);
+}
+
+void launch_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint16_t* out,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(pack_gate_up_kernel, dim3((unsigned)((int64_t)E * 2 * I)), dim3(256), 0, s, wg, wu, I, H,
+                     out);
+}
+
+void launch_quant_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s) {
+  const int64_t n_rows = (int64_t)E * 2 * I;
+  hipLaunchKernelGGL(quant_pack_gate_up_kernel, dim3(row_grid(n_rows, 256)), dim3(RT), 0, s, wg, wu, n_rows, I, H,
+                     codes, scales);
+}
+
+void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  (void)hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice, s);
+}
+
+void launch_transpose(const uint16_t* in, int batch, int rows, int cols, uint16_t* out, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(64, 4), 0, s, in, rows, cols, out);
+}
+
+}  // namespace mk

@@ -1,0 +1,216 @@
+// Device-built dispatch schedule: three small launches, all sized from R and
+// the minibatch size (host-known), never from per-expert counts.
+//
+//  count   (minibatch b, chunk c of 256 rows): per-chunk expert histogram in
+//          LDS; also marks every sorted position of the chunk's range empty.
+//  scan    (one workgroup): per (b, e) prefix over chunks, per-minibatch
+//          expert offsets, global counts/offsets, and the GEMM work items
+//          (one per 256-row m-tile of each (b, e) run) with their offsets.
+//  scatter (b, c): stable rank of each row among the earlier rows of its
+//          chunk with the same expert; sorted_pos and its inverse.
+//
+// Integer work only, no float and no order-dependent atomics (the LDS
+// histogram uses integer atomics, whose result is order independent), so the
+// tables are bit-exact and repeatable.
+#include "mk_device.h"
+#include "mk_internal.h"
+
+#include <algorithm>
+
+namespace mk {
+namespace {
+
+constexpr int CH = MK_SCHED_CHUNK;
+
+__global__ __launch_bounds__(CH) void sched_count_kernel(const int32_t* __restrict__ row_expert, int R, int E,
+                                                         int MB, int cpm, int32_t* __restrict__ chunk_counts,
+                                                         int32_t* __restrict__ inv, uint32_t* __restrict__ err) {
+  __shared__ int hist[MK_MAX_EXPERTS];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  for (int e = tid; e < E; e += CH) hist[e] = 0;
+  __syncthreads();
+  const int off = c * CH + tid;
+  const int64_t p = (int64_t)b * MB + off;
+  if (off < MB) {
+    inv[p] = -1;
+    if (p < R) {
+      const int e = row_expert[p];
+      if (e >= 0 && e < E)
+        atomicAdd(&hist[e], 1);
+      else
+        atomicOr(err, MK_DEVERR_EXPERT_RANGE);
+    }
+  }
+  __syncthreads();
+  int32_t* out = chunk_counts + ((int64_t)b * cpm + c) * E;
+  for (int e = tid; e < E; e += CH) out[e] = hist[e];
+}
+
+constexpr int SCAN_T = 1024;
+
+// Exclusive scan of one value per thread over the workgroup; *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
+  const int tid = threadIdx.x;
+  sbuf[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < SCAN_T; o <<= 1) {
+    const int t = tid >= o ? sbuf[tid - o] : 0;
+    __syncthreads();
+    sbuf[tid] += t;
+    __syncthreads();
+  }
+  const int incl = sbuf[tid];
+  *total = sbuf[SCAN_T - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int nb, int cpm, int tile_m,
+                                                            int item_cap, int32_t* __restrict__ chunk_counts,
+                                                            int32_t* __restrict__ mb_counts,
+                                                            int32_t* __restrict__ mb_offsets,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ items,
+                                                            int32_t* __restrict__ mb_items,
+                                                            uint32_t* __restrict__ err) {
+  __shared__ int sbuf[SCAN_T];
+  const int tid = threadIdx.x;
+  const int nbe = nb * E;
+  // per (b, e): exclusive prefix over the chunks of minibatch b (in place)
+  for (int be = tid; be < nbe; be += SCAN_T) {
+    const int b = be / E, e = be - b * E;
+    int32_t* cc = chunk_counts + (int64_t)b * cpm * E + e;
+    int run = 0;
+    for (int c = 0; c < cpm; ++c) {
+      const int v = cc[(int64_t)c * E];
+      cc[(int64_t)c * E] = run;
+      run += v;
+    }
+    mb_counts[be] = run;
+  }
+  __syncthreads();
+  // per minibatch: exclusive scan over experts
+  for (int b = 0; b < nb; ++b) {
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += SCAN_T) {
+      const int e = e0 + tid;
+      const int v = e < E ? mb_counts[b * E + e] : 0;
+      int tot;
+      const int ex = block_exclusive_scan(v, sbuf, &tot);
+      if (e < E) mb_offsets[b * (E + 1) + e] = carry + ex;
+      carry += tot;
+    }
+    if (tid == 0) mb_offsets[b * (E + 1) + E] = carry;
+  }
+  // global per-expert counts and offsets
+  {
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += SCAN_T) {
+      const int e = e0 + tid;
+      int v = 0;
+      if (e < E)
+        for (int b = 0; b < nb; ++b) v += mb_counts[b * E + e];
+      int tot;
+      const int ex = block_exclusive_scan(v, sbuf, &tot);
+      if (e < E) {
+        counts[e] = v;
+        offsets[e] = carry + ex;
+      }
+      carry += tot;
+    }
+    if (tid == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  // work items, ordered (b, e, m)
+  int carry = 0;
+  for (int be0 = 0; be0 < nbe; be0 += SCAN_T) {
+    const int be = be0 + tid;
+    int cnt = 0, nm = 0;
+    if (be < nbe) {
+      cnt = mb_counts[be];
+      nm = (cnt + tile_m - 1) / tile_m;
+    }
+    int tot;
+    const int start = carry + block_exclusive_scan(nm, sbuf, &tot);
+    if (be < nbe) {
+      const int b = be / E, e = be - b * E;
+      const int base = b * MB + mb_offsets[b * (E + 1) + e];
+      for (int m = 0; m < nm; ++m) {
+        const int idx = start + m;
+        if (idx < item_cap) {
+          int32_t* it = items + 4 * (int64_t)idx;
+          it[0] = base + m * tile_m;
+          it[1] = min(tile_m, cnt - m * tile_m);
+          it[2] = e;
+          it[3] = b;
+        }
+      }
+      if (e == 0) mb_items[b] = start;
+    }
+    carry += tot;
+  }
+  if (tid == 0) {
+    mb_items[nb] = carry;
+    if (carry > item_cap) atomicOr(err, MK_DEVERR_SCHED_OVERFLOW);
+  }
+}
+
+__global__ __launch_bounds__(CH) void sched_scatter_kernel(const int32_t* __restrict__ row_expert, int R, int E,
+                                                           int MB, int cpm,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           const int32_t* __restrict__ mb_offsets,
+                                                           int32_t* __restrict__ sorted_pos,
+                                                           int32_t* __restrict__ inv) {
+  __shared__ int ex[CH];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int off = c * CH + tid;
+  const int64_t r = (int64_t)b * MB + off;
+  const bool live = off < MB && r < R;
+  int e = -1;
+  if (live) {
+    e = row_expert[r];
+    if (e < 0 || e >= E) e = -1;
+  }
+  ex[tid] = e;
+  __syncthreads();
+  if (e >= 0) {
+    int rank = 0;
+    for (int j = 0; j < tid; ++j) rank += (ex[j] == e);
+    const int pos = b * MB + mb_offsets[b * (E + 1) + e] + chunk_base[((int64_t)b * cpm + c) * E + e] + rank;
+    sorted_pos[r] = pos;
+    inv[pos] = (int32_t)r;
+  } else if (live) {
+    sorted_pos[r] = -1;
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
+}
+
+void launch_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, hipStream_t s) {
+  const int MB = ws->MB, E = ws->E, cpm = ws->cpm;
+  const int nb = R > 0 ? (R + MB - 1) / MB : 0;
+  launch_fill_u32(ws->err, 0u, 1, s);
+  if (nb > 0)
+    hipLaunchKernelGGL(sched_count_kernel, dim3(cpm, nb), dim3(CH), 0, s, row_expert, R, E, MB, cpm,
+                       ws->chunk_counts, ws->inv, ws->err);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(SCAN_T), 0, s, E, MB, nb, cpm, MK_TILE_M, ws->item_cap,
+                     ws->chunk_counts, ws->mb_counts, ws->mb_offsets, ws->counts, ws->offsets, ws->items,
+                     ws->mb_items, ws->err);
+  if (nb > 0)
+    hipLaunchKernelGGL(sched_scatter_kernel, dim3(cpm, nb), dim3(CH), 0, s, row_expert, R, E, MB, cpm,
+                       ws->chunk_counts, ws->mb_offsets, ws->sorted_pos, ws->inv);
+}
+
+}  // namespace mk

@@ -1,0 +1,113 @@
+"""Device-memory plumbing around the C ABI: torch tensors as buffers, the
+current torch stream as the HIP stream.  No arithmetic of the layer happens
+here; every call below is one libmk.so entry point.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+PRECISION = {"bf16": B.MK_BF16, "mxfp8": B.MK_MXFP8}
+TABLE = {
+    "counts": B.MK_TAB_COUNTS, "offsets": B.MK_TAB_OFFSETS, "mb_counts": B.MK_TAB_MB_COUNTS,
+    "mb_offsets": B.MK_TAB_MB_OFFSETS, "sorted_pos": B.MK_TAB_SORTED_POS, "inv": B.MK_TAB_INV,
+    "items": B.MK_TAB_ITEMS, "mb_items": B.MK_TAB_MB_ITEMS, "ring": B.MK_TAB_RING,
+}
+
+
+def to_device_bits(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 patterns -> device int16 tensor (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+class MoELayer:
+    """A workspace plus the calls that use it (one per model, reused)."""
+
+    def __init__(self, H, I, E, k, max_rows, precision="bf16", minibatch_rows=0, ring_bytes=256 << 20,
+                 renorm=1, enable_backward=False, capacity_mult=1.0, device="cuda"):
+        cfg = B.mk_config_default()
+        cfg.minibatch_rows = minibatch_rows
+        cfg.precision = PRECISION[precision]
+        cfg.ring_bytes = ring_bytes
+        cfg.sched_capacity_mult = capacity_mult
+        cfg.renorm = renorm
+        cfg.enable_backward = int(enable_backward)
+        self.H, self.I, self.E, self.k = H, I, E, k
+        self.precision = precision
+        self.device = device
+        self.ws = B.mk_workspace_create(cfg, max_rows, H, I, E, k)
+
+    def close(self):
+        if self.ws:
+            B.mk_workspace_destroy(self.ws)
+            self.ws = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def query(self, what: str) -> int:
+        return B.mk_query(self.ws, getattr(B, "MK_Q_" + what.upper()))
+
+    # ---- calls ---------------------------------------------------------
+    def prepare_weights(self, w_gate, w_up, w_down, for_backward=False) -> torch.Tensor:
+        nbytes = self.query("packed_bytes_bwd" if for_backward else "packed_bytes")
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        B.mk_prepare_weights(self.ws, w_gate, w_up, w_down, for_backward, packed, stream())
+        return packed
+
+    def route(self, x, w_router, bias, T):
+        idx = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+        w = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
+        B.mk_route(self.ws, x, w_router, bias, T, idx, w, stream())
+        return idx, w
+
+    def build_schedule(self, row_expert, R):
+        B.mk_build_schedule(self.ws, row_expert, R, stream())
+
+    def forward(self, mode, x_src, row_w, packed, n_out, out=None, fwd_ctx=None):
+        if out is None:
+            out = torch.empty((n_out, self.H), dtype=torch.int16, device=self.device)
+        B.mk_forward(self.ws, mode, x_src, row_w, packed, out, fwd_ctx, stream())
+        return out
+
+    def new_fwd_ctx(self) -> torch.Tensor:
+        return torch.empty(self.query("fwd_ctx_bytes"), dtype=torch.uint8, device=self.device)
+
+    def backward(self, fwd_ctx, x_src, row_w, packed, dY, R, grads=None):
+        E, H, I = self.E, self.H, self.I
+        if grads is None:
+            grads = {
+                "dX": torch.empty((R, H), dtype=torch.int16, device=self.device),
+                "dW_gate": torch.empty((E, I, H), dtype=torch.float32, device=self.device),
+                "dW_up": torch.empty((E, I, H), dtype=torch.float32, device=self.device),
+                "dW_down": torch.empty((E, H, I), dtype=torch.float32, device=self.device),
+                "d_row_w": torch.empty((R,), dtype=torch.float32, device=self.device),
+            }
+        g = grads
+        B.mk_backward(self.ws, B.MK_EXPERT_SHARE, fwd_ctx, x_src, row_w, packed, dY, g["dX"], g["dW_gate"],
+                      g["dW_up"], g["dW_down"], g["d_row_w"], stream())
+        return g
+
+    def table(self, name: str, n: int, dtype=torch.int32) -> torch.Tensor:
+        item = torch.empty(0, dtype=dtype).element_size()
+        t = torch.empty(n, dtype=dtype, device=self.device)
+        B.mk_schedule_copy(self.ws, TABLE[name], t, n * item, stream())
+        return t
+
+    def device_error(self) -> int:
+        t = torch.zeros(1, dtype=torch.int32, device=self.device)
+        B.mk_device_error(self.ws, t, stream())
+        return int(t.item()) & 0xFFFFFFFF

@@ -17,9 +17,17 @@ Expert share (one GPU under expert parallelism): out_rows[r] = w[r] * y(r);
 the sum over a token's k experts happens at the token's source GPU and is not
 part of this share.
 
-Everything here is fp64 on exact bf16 inputs, except where a step's own
-precision is part of the method (the MXFP8 path rounds a to bf16 before
-quantising it).  Results are returned unrounded (fp64) unless noted.
+Precision.  The pages' BF16 mode (and the MXFP8 mode's "accumulate in fp32,
+bf16 output") is read as: every GEMM operand is a bf16 tensor, every GEMM
+accumulates exactly (here fp64, on the device fp32), and the layer's outputs
+are bf16 tensors.  With ``bf16_mode=True`` (the default) the oracle therefore
+rounds, once each and to nearest even, exactly the values that are bf16
+tensors in that reading -- the SwiGLU output a (GEMM2 operand), the layer
+output, and in the backward dg/du (operands of the dX and gate/up weight
+GEMMs), w*a (operand of the down weight GEMM) and dX -- and computes all
+else in fp64.  ``bf16_mode=False`` is the exact-math layer, pinned by finite
+differences and autograd; the bf16 mode is pinned against it within bf16's
+error bound.
 """
 from __future__ import annotations
 
@@ -37,11 +45,17 @@ def silu(v):
     return v * sigmoid(v)
 
 
-def expert_ffn(x, wg, wu, wd):
-    """One expert on rows x [n, H]: -> (g, u, a, y), fp64."""
+def rnd(v, on: bool):
+    """Round to bf16 (nearest even) when on, else leave exact."""
+    return bf16.round_rne(v) if on else v
+
+
+def expert_ffn(x, wg, wu, wd, bf16_mode: bool = False):
+    """One expert on rows x [n, H]: -> (g, u, a, y), fp64.  In bf16 mode a is
+    the bf16 GEMM2 operand."""
     g = x @ wg.T
     u = x @ wu.T
-    a = silu(g) * u
+    a = rnd(silu(g) * u, bf16_mode)
     y = a @ wd.T
     return g, u, a, y
 
@@ -50,7 +64,7 @@ def _weights(inp):
     return (bf16.decode(inp["w_gate"]), bf16.decode(inp["w_up"]), bf16.decode(inp["w_down"]))
 
 
-def rows_ffn(x_rows, row_expert, wg, wu, wd):
+def rows_ffn(x_rows, row_expert, wg, wu, wd, bf16_mode: bool = False):
     """FFN of each row under its own expert, arrival order.  Rows whose expert
     id is out of range get zeros."""
     R, H = x_rows.shape
@@ -60,12 +74,13 @@ def rows_ffn(x_rows, row_expert, wg, wu, wd):
         sel = np.nonzero(row_expert == e)[0]
         if sel.size == 0:
             continue
-        g[sel], u[sel], a[sel], y[sel] = expert_ffn(x_rows[sel], wg[e], wu[e], wd[e])
+        g[sel], u[sel], a[sel], y[sel] = expert_ffn(x_rows[sel], wg[e], wu[e], wd[e], bf16_mode)
     return g, u, a, y
 
 
-def forward_full(inp, renorm: int | None = None):
-    """Full layer, bf16 mode: route, expert FFN, combine.  -> dict."""
+def forward_full(inp, renorm: int | None = None, bf16_mode: bool = True):
+    """Full layer: route, expert FFN, combine.  -> dict (out in bf16 mode is
+    the bf16 output, out_exact the value before that rounding)."""
     sh = inp["shape"]
     x = bf16.decode(inp["x"])
     bias = inp["bias"]
@@ -74,24 +89,25 @@ def forward_full(inp, renorm: int | None = None):
     wg, wu, wd = _weights(inp)
     row_expert = idx.reshape(-1)
     x_rows = np.repeat(x, sh.k, axis=0)                 # row r = t*k + j comes from token t
-    g, u, a, y = rows_ffn(x_rows, row_expert, wg, wu, wd)
+    g, u, a, y = rows_ffn(x_rows, row_expert, wg, wu, wd, bf16_mode)
     T, H = x.shape
     out = np.zeros((T, H))
     yk = y.reshape(T, sh.k, H)
     for j in range(sh.k):                               # fixed ascending order
         out += w[:, j, None].astype(np.float64) * yk[:, j]
     return {"topk_idx": idx, "topk_w": w, "logits": z, "row_expert": row_expert,
-            "g": g, "u": u, "a": a, "y": y, "out": out}
+            "g": g, "u": u, "a": a, "y": y, "out": rnd(out, bf16_mode), "out_exact": out}
 
 
-def forward_share(inp):
-    """Expert share, bf16 mode: out_rows[r] = w[r] * y(r), arrival order."""
+def forward_share(inp, bf16_mode: bool = True):
+    """Expert share: out_rows[r] = w[r] * y(r), arrival order."""
     x = bf16.decode(inp["x"])
     wg, wu, wd = _weights(inp)
     re = inp["row_expert"]
-    g, u, a, y = rows_ffn(x, re, wg, wu, wd)
+    g, u, a, y = rows_ffn(x, re, wg, wu, wd, bf16_mode)
     w = inp["row_w"].astype(np.float64)
-    return {"g": g, "u": u, "a": a, "y": y, "out": w[:, None] * y}
+    out = w[:, None] * y
+    return {"g": g, "u": u, "a": a, "y": y, "out": rnd(out, bf16_mode), "out_exact": out}
 
 
 def quantized_weights(inp):
@@ -129,11 +145,12 @@ def forward_share_mxfp8(inp, qw=None):
         ac, as_ = mxfp8.quantize(bf16.decode(a_bits[sel]))
         y[sel] = mxfp8.dequantize(ac, as_) @ wd[e].T
     w = inp["row_w"].astype(np.float64)
-    return {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "y": y, "out": w[:, None] * y}
+    out = w[:, None] * y
+    return {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "y": y, "out": bf16.round_rne(out), "out_exact": out}
 
 
-def backward_share(inp):
-    """Expert share backward, bf16 mode, loss L = sum_r <dY[r], out_rows[r]>.
+def backward_share(inp, bf16_mode: bool = True):
+    """Expert share backward, loss L = sum_r <dY[r], out_rows[r]>.
 
     dA' = dY W_d[e]            (gradient w.r.t. a, before the router weight)
     dw[r] = <dA'[r], a[r]>     (= <dY[r], y[r]>: router-weight gradient)
@@ -141,7 +158,9 @@ def backward_share(inp):
     dg  = dA * u * s * (1 + g (1 - s)),  s = sigmoid(g)
     du  = dA * silu(g)
     dX  = dg W_g[e] + du W_u[e]
-    dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = (w dY)_e^T a_e
+    dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = dY_e^T (w a)_e
+    In bf16 mode dg, du, w*a and dX are bf16 tensors (GEMM operands / output);
+    g, u, a, dA' and the fp32 outputs dW, dw are exact.
     """
     x = bf16.decode(inp["x"])
     wg, wu, wd = _weights(inp)
@@ -164,14 +183,113 @@ def backward_share(inp):
         dw_alt[sel] = np.einsum("rh,rh->r", dYe, y)
         dA = w[sel, None] * dAp
         s = sigmoid(g)
-        dg = dA * u * s * (1.0 + g * (1.0 - s))
-        du = dA * silu(g)
-        dX[sel] = dg @ wg[e] + du @ wu[e]
+        dg = rnd(dA * u * s * (1.0 + g * (1.0 - s)), bf16_mode)
+        du = rnd(dA * silu(g), bf16_mode)
+        dX[sel] = rnd(dg @ wg[e] + du @ wu[e], bf16_mode)
         dWg[e] = dg.T @ xe
         dWu[e] = du.T @ xe
-        dWd[e] = (w[sel, None] * dYe).T @ a
+        dWd[e] = dYe.T @ rnd(w[sel, None] * a, bf16_mode)
     return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd,
             "d_row_w": dw, "d_row_w_alt": dw_alt}
+
+
+def forward_share_rows(inp, rows):
+    """forward_share's out for the given arrival rows only (each row is
+    independent of every other)."""
+    rows = np.asarray(rows)
+    re = inp["row_expert"]
+    out = np.zeros((len(rows), inp["x"].shape[1]))
+    for e in np.unique(re[rows]):
+        e = int(e)
+        sel = np.nonzero(re[rows] == e)[0]
+        x = bf16.decode(inp["x"][rows[sel]])
+        _, _, _, y = expert_ffn(x, bf16.decode(inp["w_gate"][e]), bf16.decode(inp["w_up"][e]),
+                                bf16.decode(inp["w_down"][e]), bf16_mode=True)
+        out[sel] = inp["row_w"][rows[sel], None].astype(np.float64) * y
+    return bf16.round_rne(out)
+
+
+def forward_full_tokens(inp, idx, w, tokens):
+    """Full-layer out for the given tokens under routing (idx, w)."""
+    tokens = np.asarray(tokens)
+    x = bf16.decode(inp["x"][tokens])
+    out = np.zeros((len(tokens), x.shape[1]))
+    sub = idx[tokens]
+    ys = {}
+    for e in np.unique(sub):
+        e = int(e)
+        _, _, _, ys[e] = expert_ffn(x, bf16.decode(inp["w_gate"][e]), bf16.decode(inp["w_up"][e]),
+                                    bf16.decode(inp["w_down"][e]), bf16_mode=True)
+    for n, t in enumerate(tokens):
+        for j in range(idx.shape[1]):                    # fixed ascending order
+            out[n] += float(w[t, j]) * ys[int(idx[t, j])][n]
+    return bf16.round_rne(out)
+
+
+def quantized_weights_expert(inp, e):
+    """MXFP8 codes/scales of one expert's weights (gate/up along H, down along I)."""
+    return {"gate": mxfp8.quantize(bf16.decode(inp["w_gate"][e])),
+            "up": mxfp8.quantize(bf16.decode(inp["w_up"][e])),
+            "down": mxfp8.quantize(bf16.decode(inp["w_down"][e]))}
+
+
+def forward_share_mxfp8_rows(inp, rows):
+    """forward_share_mxfp8's out (and a) for the given arrival rows only."""
+    rows = np.asarray(rows)
+    re = inp["row_expert"]
+    H = inp["x"].shape[1]
+    out = np.zeros((len(rows), H))
+    for e in np.unique(re[rows]):
+        q = quantized_weights_expert(inp, int(e))
+        wg = mxfp8.dequantize(*q["gate"]); wu = mxfp8.dequantize(*q["up"]); wd = mxfp8.dequantize(*q["down"])
+        sel = np.nonzero(re[rows] == e)[0]
+        xc, xs = mxfp8.quantize(bf16.decode(inp["x"][rows[sel]]))
+        xd = mxfp8.dequantize(xc, xs)
+        g = xd @ wg.T
+        u = xd @ wu.T
+        a = bf16.decode(bf16.encode(silu(g) * u))
+        ad = mxfp8.dequantize(*mxfp8.quantize(a))
+        out[sel] = inp["row_w"][rows[sel], None].astype(np.float64) * (ad @ wd.T)
+    return bf16.round_rne(out)
+
+
+def backward_share_sampled(inp, rows, gate_up_rows, down_cols):
+    """Entries of backward_share (bf16 mode) computed one by one.
+
+    rows          arrival rows r -> dX[r], d_row_w[r]
+    gate_up_rows  (e, i) pairs   -> dW_gate[e, i, :], dW_up[e, i, :]
+    down_cols     (e, i) pairs   -> dW_down[e, :, i]
+    """
+    re = inp["row_expert"]
+    w = inp["row_w"].astype(np.float64)
+    out = {"dX": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
+    for r in rows:
+        e = int(re[r])
+        x = bf16.decode(inp["x"][r:r + 1]); dY = bf16.decode(inp["dY"][r:r + 1])
+        wg = bf16.decode(inp["w_gate"][e]); wu = bf16.decode(inp["w_up"][e]); wd = bf16.decode(inp["w_down"][e])
+        g, u, a, y = expert_ffn(x, wg, wu, wd)
+        dAp = dY @ wd
+        s = sigmoid(g)
+        dA = w[r] * dAp
+        dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
+        du = bf16.round_rne(dA * silu(g))
+        out["dX"].append(bf16.round_rne(dg @ wg + du @ wu)[0])
+        out["d_row_w"].append(float(np.sum(dAp * a)))
+    for (e, i) in gate_up_rows:
+        sel = np.nonzero(re == e)[0]
+        X = bf16.decode(inp["x"][sel]); dY = bf16.decode(inp["dY"][sel])
+        g = X @ bf16.decode(inp["w_gate"][e, i]); u = X @ bf16.decode(inp["w_up"][e, i])
+        dAp = dY @ bf16.decode(inp["w_down"][e][:, i])
+        s = sigmoid(g)
+        dA = w[sel] * dAp
+        out["dW_gate"].append(bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s))) @ X)
+        out["dW_up"].append(bf16.round_rne(dA * silu(g)) @ X)
+    for (e, i) in down_cols:
+        sel = np.nonzero(re == e)[0]
+        X = bf16.decode(inp["x"][sel]); dY = bf16.decode(inp["dY"][sel])
+        a = silu(X @ bf16.decode(inp["w_gate"][e, i])) * (X @ bf16.decode(inp["w_up"][e, i]))
+        out["dW_down"].append(bf16.round_rne(w[sel] * a) @ dY)
+    return {k: np.asarray(v) for k, v in out.items()}
 
 
 def ring_contents(sched, x_bits, src_of_row):

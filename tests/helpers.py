@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU tests: device upload, result download, the
+float-tolerance rule.  No arithmetic of the layer lives here."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import bf16
+
+BF16_TOL = 2e-2     # max |err| <= 2e-2 * RMS(oracle tensor), bf16 outputs and gradients
+MXFP8_TOL = 6e-2    # same rule for MXFP8 outputs against the MXFP8-emulating oracle
+ROUTER_W_ATOL = 2e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits_or_array, device="cuda"):
+    a = np.ascontiguousarray(bits_or_array)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def host_bf16(t: torch.Tensor) -> np.ndarray:
+    """Device bf16 bits (int16) -> fp64 values."""
+    return bf16.decode(t.cpu().numpy().view(np.uint16))
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(np.asarray(a, dtype=np.float64)))))
+
+
+def ulp_bf16(v):
+    """Spacing of bf16 values at |v|."""
+    _, e = np.frexp(np.abs(np.asarray(v, dtype=np.float64)))
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def assert_close(got, ref, tol, what, bf16_out=False):
+    """max|got - ref| <= tol * RMS(ref).
+
+    bf16_out: got and ref are both bf16 tensors (ref = the oracle's value
+    rounded once to bf16).  Two correct implementations that round slightly
+    different fp32/fp64 sums once can land on adjacent bf16 values, so the rule
+    is applied at the output format's resolution: each element's error less
+    one bf16 ulp at the reference value must stay within tol * RMS(ref).  The
+    raw ratio and the share of differing elements are printed alongside."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    r = rms(ref)
+    d = np.abs(got - ref)
+    err = float(np.max(d)) if ref.size else 0.0
+    msg = f"  {what}: max|err| = {err:.3e}, RMS(ref) = {r:.3e}, ratio = {err / max(r, 1e-300):.3e} (tol {tol})"
+    if not bf16_out:
+        say(msg)
+        assert err <= tol * r, f"{what}: max|err| {err:.4e} > {tol} * RMS {r:.4e}"
+        return
+    u = ulp_bf16(ref)
+    beyond = np.maximum(d - u, 0.0)
+    ex = float(np.max(beyond)) if ref.size else 0.0
+    say(msg + f"; beyond 1 ulp: {ex / max(r, 1e-300):.3e}; differ: {np.mean(d > 0):.2%}, "
+        f"> 1 ulp: {np.mean(d > u):.4%}")
+    assert ex <= tol * r, f"{what}: error beyond one bf16 ulp {ex:.4e} > {tol} * RMS {r:.4e}"

@@ -1,0 +1,82 @@
+"""The C-ABI library loads and exports what include/mk.h declares, and its
+host-side checks reject bad arguments before touching the GPU (CPU only)."""
+import json
+import os
+
+import pytest
+
+from mixture_experts_layer_device_amd import binding as B  # noqa: E402  (fails loudly if not built)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_every_declared_function_is_exported():
+    names = B.declared_functions()
+    assert len(names) >= 14
+    missing = [n for n in names if not hasattr(B.lib, n)]
+    assert not missing, missing
+
+
+def test_header_constants_parsed():
+    assert B.MK_OK == 0 and B.MK_ERR_SHAPE == -2 and B.MK_DEVERR_SCHED_OVERFLOW == 2
+    assert B.MK_FULL_LAYER == 0 and B.MK_EXPERT_SHARE == 1 and B.MK_MXFP8 == 1
+
+
+def test_two_wave_rule_host_side():
+    g = json.load(open(os.path.join(GOLDEN, "two_wave_floor.json")))
+    assert B.mk_two_wave_rows(g["H"], g["I"], g["n_cu"], g["tile_m"], g["tile_n"]) == g["rows"]
+    assert B.mk_two_wave_rows(7168, 2048, 256, 256, 256) == 8192
+
+
+def test_config_defaults():
+    c = B.mk_config_default()
+    assert c.minibatch_rows == 0 and c.precision == B.MK_BF16 and c.ring_bytes == 256 << 20
+    assert c.sched_capacity_mult == 1.0 and c.renorm == 1 and c.enable_backward == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=100), B.MK_ERR_SHAPE), (dict(I=96), B.MK_ERR_SHAPE), (dict(max_rows=0), B.MK_ERR_SHAPE),
+    (dict(E=0), B.MK_ERR_LIMIT), (dict(E=2000), B.MK_ERR_LIMIT), (dict(k=33), B.MK_ERR_LIMIT),
+])
+def test_workspace_rejects_bad_shapes(kw, code):
+    args = dict(max_rows=1024, H=256, I=128, E=8, k=2)
+    args.update(kw)
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(B.mk_config_default(), **args)
+    assert ei.value.status == code
+
+
+def test_workspace_rejects_bad_config():
+    c = B.mk_config_default()
+    c.minibatch_rows = 4096
+    c.ring_bytes = 4096 * 512 - 1            # smaller than one minibatch of H=256 bf16 rows
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 8192, 256, 128, 8, 2)
+    assert ei.value.status == B.MK_ERR_RING
+    c = B.mk_config_default(); c.precision = 7
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 8192, 256, 128, 8, 2)
+    assert ei.value.status == B.MK_ERR_CONFIG
+    c = B.mk_config_default(); c.sched_capacity_mult = 0.0
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 8192, 256, 128, 8, 2)
+    assert ei.value.status == B.MK_ERR_CONFIG
+    c = B.mk_config_default(); c.precision = B.MK_MXFP8; c.enable_backward = 1
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 8192, 256, 128, 8, 2)
+    assert ei.value.status == B.MK_ERR_UNSUPPORTED
+    c = B.mk_config_default(); c.enable_backward = 1
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 8192, 256, 384, 8, 2)
+    assert ei.value.status == B.MK_ERR_SHAPE
+
+
+def test_quantize_rejects_bad_k_without_gpu():
+    with pytest.raises(B.MkError) as ei:
+        B.mk_mxfp8_quantize(1, 4, 48, 1, 1)
+    assert ei.value.status == B.MK_ERR_SHAPE
+
+
+def test_status_strings():
+    assert B.mk_status_string(0) == "ok"
+    assert "ring" in B.mk_status_string(B.MK_ERR_RING)

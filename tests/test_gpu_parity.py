@@ -1,0 +1,381 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer results (routing indices, schedule tables, ring contents, MXFP8 codes
+and scales) must match bit for bit; bf16 outputs and gradients within
+max|err| <= 2e-2 * RMS(oracle tensor), MXFP8 outputs within 6e-2 * RMS of the
+MXFP8-emulating oracle.  At full workload sizes the oracle evaluates sampled
+rows / columns one by one (each output row depends only on its own inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import bf16, layer, mxfp8, route, schedule
+from tests.helpers import (BF16_TOL, MXFP8_TOL, ROUTER_W_ATOL, assert_close, dev, host_bf16, rms, say)
+
+pytestmark = pytest.mark.gpu
+
+from mixture_experts_layer_device_amd import binding as B  # noqa: E402
+from mixture_experts_layer_device_amd.layer import MoELayer  # noqa: E402
+
+_CACHE = {}
+
+
+def share_inputs(name):
+    if name not in _CACHE:
+        _CACHE[name] = workloads.make_expert_share(name)
+    return _CACHE[name]
+
+
+def full_inputs(name):
+    key = "full:" + name
+    if key not in _CACHE:
+        _CACHE[key] = workloads.make_full_layer(name)
+    return _CACHE[key]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def sched_tables(L, R, E, MB):
+    nb = -(-R // MB) if R else 0
+    t = {
+        "counts": L.table("counts", E), "offsets": L.table("offsets", E + 1),
+        "mb_counts": L.table("mb_counts", nb * E), "mb_offsets": L.table("mb_offsets", nb * (E + 1)),
+        "sorted_pos": L.table("sorted_pos", R), "inv": L.table("inv", nb * MB),
+        "mb_items": L.table("mb_items", nb + 1),
+    }
+    t["items"] = L.table("items", 4 * L.query("item_capacity"))
+    sync()
+    return {k: v.cpu().numpy() for k, v in t.items()}
+
+
+def check_schedule(L, re, E, MB, ring_rows):
+    R = len(re)
+    ref = schedule.build(re, E, MB, ring_rows, L.query("tile_m"))
+    got = sched_tables(L, R, E, MB)
+    for k in ("counts", "offsets", "sorted_pos", "inv", "mb_items"):
+        assert np.array_equal(got[k], getattr(ref, k).reshape(-1)), k
+    assert np.array_equal(got["mb_counts"], ref.mb_counts.reshape(-1))
+    assert np.array_equal(got["mb_offsets"], ref.mb_offsets.reshape(-1))
+    n_items = len(ref.items)
+    assert np.array_equal(got["items"][: 4 * n_items], ref.items.reshape(-1))
+    return ref
+
+
+# ----------------------------------------------------------------- schedule --
+SCHED_CASES = [
+    # (name, R, E, MB, seed)
+    ("zipf4_mb4096", 16384, 4, 4096, 2),
+    ("zipf8_mb4096", 24576, 8, 4096, 4),
+    ("uniform128_one_mb", 32768, 128, 32768, 1),
+    ("ragged37", 1000, 37, 300, 7),
+    ("single_row", 1, 3, 1, 8),
+]
+
+
+@pytest.mark.parametrize("case", SCHED_CASES, ids=[c[0] for c in SCHED_CASES])
+def test_schedule_bit_exact(case):
+    name, R, E, MB, seed = case
+    say(f"[schedule] {name} R={R} E={E} MB={MB}")
+    rng = np.random.default_rng(seed)
+    re = rng.choice(E, size=R, p=workloads.zipf_local_weights(E, 1.2)).astype(np.int32)
+    L = MoELayer(H=256, I=128, E=E, k=1, max_rows=R, minibatch_rows=MB, ring_bytes=2 * MB * 512)
+    L.build_schedule(dev(re), R)
+    sync()
+    check_schedule(L, re, E, MB, L.query("ring_rows"))
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_schedule_empty_and_invalid_ids():
+    say("[schedule] empty input and out-of-range ids")
+    L = MoELayer(H=256, I=128, E=4, k=1, max_rows=64, minibatch_rows=16)
+    L.build_schedule(None, 0)
+    sync()
+    assert L.table("mb_items", 1).cpu().item() == 0
+    re = np.array([0, 5, 1, -1, 3, 3, 0, 2, 9, 1], dtype=np.int32)
+    L.build_schedule(dev(re), len(re))
+    sync()
+    check_schedule(L, re, 4, 16, L.query("ring_rows"))
+    assert L.device_error() == B.MK_DEVERR_EXPERT_RANGE
+    L.build_schedule(dev(np.zeros(4, np.int32)), 4)      # the next schedule clears the error word
+    sync()
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_schedule_capacity_overflow_flags_and_returns():
+    say("[schedule] work-table overflow")
+    R, E = 4096, 16
+    re = np.arange(R, dtype=np.int32) % E
+    L = MoELayer(H=256, I=128, E=E, k=1, max_rows=R, minibatch_rows=256, capacity_mult=0.1)
+    L.build_schedule(dev(re), R)
+    sync()
+    assert L.device_error() & B.MK_DEVERR_SCHED_OVERFLOW
+    L.close()
+
+
+# -------------------------------------------------------------------- route --
+@pytest.mark.parametrize("name", ["tiny", "full"])
+def test_route_bit_exact(name):
+    inp = full_inputs(name)
+    sh = inp["shape"]
+    say(f"[route] {name} T={sh.T} H={sh.H} E={sh.E} k={sh.k} renorm={sh.renorm}")
+    x = bf16.decode(inp["x"]).astype(np.float32)
+    wr = bf16.decode(inp["w_router"]).astype(np.float32)
+    idx_ref, w_ref, _ = route.route(x, wr, inp["bias"], sh.k, sh.renorm)
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm)
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    idx, w = L.route(dev(inp["x"]), dev(inp["w_router"]), bias, sh.T)
+    sync()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    err = float(np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_ref)))
+    say(f"  router weights max|err| = {err:.2e}")
+    assert err <= ROUTER_W_ATOL
+    L.close()
+
+
+# -------------------------------------------------------------- quantiser --
+def test_mxfp8_quantize_bit_exact():
+    say("[mxfp8_quantize] all finite bf16 patterns + wide-range random rows")
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    allbits = allbits[((allbits >> 7) & 0xFF) != 0xFF]
+    rng = np.random.default_rng(5)
+    allbits = rng.permutation(allbits)
+    allbits = allbits[: (len(allbits) // 256) * 256].reshape(-1, 256)
+    wide = workloads.bf16_bits((rng.standard_normal((512, 1024)) * np.exp(rng.standard_normal((512, 32)).repeat(32, 1)
+                                * 6)).astype(np.float32))
+    special = np.zeros((4, 256), dtype=np.uint16)
+    special[1, :] = 0x8000                                # -0 block
+    special[2, :32] = 0x0001                              # smallest subnormal
+    special[3, :] = 0x7F7F                                # largest finite
+    for bits in (allbits, wide, special):
+        rows, K = bits.shape
+        codes = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
+        B.mk_mxfp8_quantize(dev(bits), rows, K, codes, scales, torch.cuda.current_stream())
+        sync()
+        rc, rs = mxfp8.quantize(bf16.decode(bits))
+        assert np.array_equal(scales.cpu().numpy(), rs)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+# ------------------------------------------------------------ full layer --
+def run_full_layer(inp, precision="bf16", MB=0, ring_bytes=256 << 20):
+    sh = inp["shape"]
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, precision=precision,
+                 minibatch_rows=MB, ring_bytes=ring_bytes)
+    x = dev(inp["x"])
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]))
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    idx, w = L.route(x, dev(inp["w_router"]), bias, sh.T)
+    L.build_schedule(idx.view(-1), sh.R)
+    out = L.forward(B.MK_FULL_LAYER, x, w.view(-1), packed, sh.T)
+    sync()
+    return L, idx, w, out
+
+
+def test_forward_full_layer_tiny():
+    inp = full_inputs("tiny")
+    say("[forward full layer] tiny T=256 H=256 I=128 E=8 k=2, one minibatch and a wrapping ring")
+    ref = layer.forward_full(inp)
+    for MB, ring in ((0, 256 << 20), (128, 2 * 128 * 512)):
+        L, idx, w, out = run_full_layer(inp, MB=MB, ring_bytes=ring)
+        assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+        assert_close(host_bf16(out), ref["out"], BF16_TOL, f"out (MB={MB})", bf16_out=True)
+        if MB:
+            # ring after the forward: the last two minibatches, bit-exact
+            s = schedule.build(ref["row_expert"], 8, MB, L.query("ring_rows"), L.query("tile_m"))
+            ring_ref, written = layer.ring_contents(s, inp["x"], np.arange(512) // 2)
+            ring = L.table("ring", L.query("ring_rows") * 256 // 2).cpu().numpy().view(np.uint16)
+            ring = ring.reshape(-1, 256)
+            assert written.all() and np.array_equal(ring, ring_ref)
+        L.close()
+
+
+def test_forward_full_layer_full_sampled():
+    inp = full_inputs("full")
+    sh = inp["shape"]
+    say("[forward full layer] T=4096 H=2048 I=768 E=128 k=8 renorm, biased router")
+    x = bf16.decode(inp["x"]).astype(np.float32)
+    idx_ref, w_ref, _ = route.route(x, bf16.decode(inp["w_router"]).astype(np.float32), inp["bias"], sh.k,
+                                    sh.renorm)
+    L, idx, w, out = run_full_layer(inp)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    toks = np.random.default_rng(0).choice(sh.T, 96, replace=False)
+    ref = layer.forward_full_tokens(inp, idx_ref, w_ref, toks)
+    assert_close(host_bf16(out)[toks], ref, BF16_TOL, "out (96 sampled tokens)", bf16_out=True)
+    L.close()
+
+
+# ---------------------------------------------------------- expert share --
+def run_share(inp, precision="bf16", MB=0, ring_bytes=256 << 20, fwd_ctx=False, backward=False):
+    sh = inp["shape"]
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=precision, minibatch_rows=MB,
+                 ring_bytes=ring_bytes, enable_backward=backward)
+    x = dev(inp["x"])
+    row_w = dev(inp["row_w"])
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=backward)
+    L.build_schedule(dev(inp["row_expert"]), sh.R)
+    ctx = L.new_fwd_ctx() if fwd_ctx else None
+    out = L.forward(B.MK_EXPERT_SHARE, x, row_w, packed, sh.R, fwd_ctx=ctx)
+    sync()
+    return L, out, (x, row_w, packed, ctx)
+
+
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (256, 2)], ids=["one_mb", "mb256_ring2"])
+def test_forward_share_bf16_small(MB, ring_mbs):
+    inp = share_inputs("small")
+    sh = inp["shape"]
+    say(f"[forward share bf16] small R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * 2 * sh.H
+    L, out, _ = run_share(inp, MB=MB, ring_bytes=ring)
+    ref = layer.forward_share(inp)["out"]
+    assert_close(host_bf16(out), ref, BF16_TOL, "out_rows", bf16_out=True)
+    L.close()
+
+
+def test_forward_share_bf16_ep64_sampled():
+    inp = share_inputs("ep64_fwd")
+    sh = inp["shape"]
+    say(f"[forward share bf16] EP=64 share R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096, 256 MiB ring")
+    L, out, _ = run_share(inp, MB=4096)
+    rows = np.sort(np.random.default_rng(1).choice(sh.R, 64, replace=False))
+    ref = layer.forward_share_rows(inp, rows)
+    assert_close(host_bf16(out)[rows], ref, BF16_TOL, "out_rows (64 sampled rows)", bf16_out=True)
+    # ring holds every row, bit-exact, at sorted_pos mod ring_rows
+    sp = L.table("sorted_pos", sh.R).cpu().numpy()
+    ring = L.table("ring", L.query("ring_rows") * sh.H // 2).cpu().numpy().view(np.uint16).reshape(-1, sh.H)
+    s = schedule.build(inp["row_expert"], sh.E, 4096, L.query("ring_rows"), L.query("tile_m"))
+    assert np.array_equal(sp, s.sorted_pos)
+    assert np.array_equal(ring[s.ring_pos], inp["x"])
+    L.close()
+
+
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (256, 2)], ids=["one_mb", "mb256_ring2"])
+def test_forward_share_mxfp8_small(MB, ring_mbs):
+    inp = share_inputs("small")
+    sh = inp["shape"]
+    say(f"[forward share mxfp8] small R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * (sh.H + sh.H // 32)
+    L, out, _ = run_share(inp, precision="mxfp8", MB=MB, ring_bytes=ring)
+    ref = layer.forward_share_mxfp8(inp)
+    assert_close(host_bf16(out), ref["out"], MXFP8_TOL, "out_rows", bf16_out=True)
+    if not MB:
+        rr = L.query("ring_rows")
+        raw = L.table("ring", rr * (sh.H + sh.H // 32) // 4).cpu().numpy().view(np.uint8)
+        codes = raw[: rr * sh.H].reshape(rr, sh.H)
+        scales = raw[rr * sh.H:].reshape(rr, sh.H // 32)
+        sp = L.table("sorted_pos", sh.R).cpu().numpy()
+        assert np.array_equal(codes[sp], ref["x_codes"])
+        assert np.array_equal(scales[sp], ref["x_scales"])
+    L.close()
+
+
+def test_forward_share_mxfp8_ep64_sampled():
+    inp = share_inputs("ep64_fwd")
+    sh = inp["shape"]
+    say(f"[forward share mxfp8] EP=64 share R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096")
+    L, out, _ = run_share(inp, precision="mxfp8", MB=4096)
+    rows = np.sort(np.random.default_rng(2).choice(sh.R, 48, replace=False))
+    ref = layer.forward_share_mxfp8_rows(inp, rows)
+    assert_close(host_bf16(out)[rows], ref, MXFP8_TOL, "out_rows (48 sampled rows)", bf16_out=True)
+    rr = L.query("ring_rows")
+    raw = L.table("ring", rr * (sh.H + sh.H // 32) // 4).cpu().numpy().view(np.uint8)
+    codes = raw[: rr * sh.H].reshape(rr, sh.H)
+    scales = raw[rr * sh.H:].reshape(rr, sh.H // 32)
+    sp = L.table("sorted_pos", sh.R).cpu().numpy()
+    xc, xs = mxfp8.quantize(bf16.decode(inp["x"][rows]))
+    assert np.array_equal(codes[sp[rows]], xc)
+    assert np.array_equal(scales[sp[rows]], xs)
+    L.close()
+
+
+# ---------------------------------------------------------------- backward --
+def run_backward(inp, MB=0, ring_bytes=256 << 20):
+    sh = inp["shape"]
+    L, out, (x, row_w, packed, ctx) = run_share(inp, MB=MB, ring_bytes=ring_bytes, fwd_ctx=True, backward=True)
+    g = L.backward(ctx, x, row_w, packed, dev(inp["dY"]), sh.R)
+    sync()
+    return L, out, g
+
+
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (256, 2)], ids=["one_mb", "mb256_ring2_replay"])
+def test_backward_small8(MB, ring_mbs):
+    inp = share_inputs("small8")
+    sh = inp["shape"]
+    say(f"[backward] small8 R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * 2 * sh.H
+    L, out, g = run_backward(inp, MB=MB, ring_bytes=ring)
+    ref = layer.backward_share(inp)
+    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
+    for k in ("dW_gate", "dW_up", "dW_down", "d_row_w"):
+        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
+    L.close()
+
+
+def test_backward_ep_bwd_sampled():
+    inp = share_inputs("ep_bwd")
+    sh = inp["shape"]
+    say(f"[backward] EP share R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096, 256 MiB ring (wraps: replay)")
+    L, out, g = run_backward(inp, MB=4096)
+    assert L.query("ring_rows") < sh.R
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(sh.R, 32, replace=False))
+    pairs = [(0, 5), (3, 2047), (7, 1000)]
+    ref = layer.backward_share_sampled(inp, rows, pairs, pairs)
+    assert_close(host_bf16(g["dX"])[rows], ref["dX"], BF16_TOL, "dX (32 sampled rows)", bf16_out=True)
+    assert_close(g["d_row_w"].cpu().numpy()[rows], ref["d_row_w"], BF16_TOL, "d_row_w (32 sampled rows)")
+    gate = np.stack([g["dW_gate"][e, i].cpu().numpy() for e, i in pairs])
+    up = np.stack([g["dW_up"][e, i].cpu().numpy() for e, i in pairs])
+    down = np.stack([g["dW_down"][e, :, i].cpu().numpy() for e, i in pairs])
+    assert_close(gate, ref["dW_gate"], BF16_TOL, "dW_gate (3 rows)")
+    assert_close(up, ref["dW_up"], BF16_TOL, "dW_up (3 rows)")
+    assert_close(down, ref["dW_down"], BF16_TOL, "dW_down (3 columns)")
+    L.close()
+
+
+# ----------------------------------------------------- determinism, errors --
+def test_repeat_runs_bitwise_and_minibatch_invariance():
+    inp = share_inputs("small8")
+    sh = inp["shape"]
+    say("[determinism] small8: repeated forward/backward, and MB / ring size invariance")
+    L1, out1, g1 = run_backward(inp, MB=256, ring_bytes=2 * 256 * 2 * sh.H)
+    # repeat on the same workspace
+    x = dev(inp["x"]); row_w = dev(inp["row_w"])
+    packed = L1.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+    L1.build_schedule(dev(inp["row_expert"]), sh.R)
+    ctx = L1.new_fwd_ctx()
+    out1b = L1.forward(B.MK_EXPERT_SHARE, x, row_w, packed, sh.R, fwd_ctx=ctx)
+    g1b = L1.backward(ctx, x, row_w, packed, dev(inp["dY"]), sh.R)
+    sync()
+    assert torch.equal(out1, out1b)
+    for k in g1:
+        assert torch.equal(g1[k], g1b[k]), k
+    # another minibatch size and ring: out, dX and d_row_w bitwise equal
+    L2, out2, g2 = run_backward(inp, MB=512, ring_bytes=256 << 20)
+    assert torch.equal(out1, out2)
+    assert torch.equal(g1["dX"], g2["dX"])
+    assert torch.equal(g1["d_row_w"], g2["d_row_w"])
+    L1.close()
+    L2.close()
+
+
+def test_invalid_expert_rows_are_zero_and_flagged():
+    inp = dict(share_inputs("small"))
+    sh = inp["shape"]
+    say("[errors] out-of-range expert ids in an expert-share forward")
+    re = inp["row_expert"].copy()
+    bad = np.array([3, 400, 999])
+    re[bad] = [-1, 4, 1 << 20]
+    inp["row_expert"] = re
+    L, out, _ = run_share(inp)
+    assert L.device_error() == B.MK_DEVERR_EXPERT_RANGE
+    got = host_bf16(out)
+    assert np.all(got[bad] == 0)
+    ref = layer.forward_share(inp)["out"]
+    assert_close(got, ref, BF16_TOL, "out_rows with dropped rows", bf16_out=True)
+    L.close()

@@ -26,7 +26,7 @@ def scalar_silu(v):
 def test_forward_full_brute_force_micro():
     inp = workloads.make_full_layer("micro")
     sh = inp["shape"]
-    ref = layer.forward_full(inp)
+    ref = layer.forward_full(inp, bf16_mode=False)
     x = bf16.decode(inp["x"]); wg = bf16.decode(inp["w_gate"]); wu = bf16.decode(inp["w_up"])
     wd = bf16.decode(inp["w_down"])
     idx, w = ref["topk_idx"], ref["topk_w"]
@@ -57,7 +57,7 @@ def test_forward_reduces_to_dense_swiglu_mlp():
         "row_expert": np.zeros(R, dtype=np.int32),
         "row_w": np.ones(R, dtype=np.float32),
     }
-    out = layer.forward_share(inp)["out"]
+    out = layer.forward_share(inp, bf16_mode=False)["out"]
     tx = torch.from_numpy(bf16.decode(inp["x"]))
     g = tx @ torch.from_numpy(bf16.decode(inp["w_gate"])[0]).T
     u = tx @ torch.from_numpy(bf16.decode(inp["w_up"])[0]).T
@@ -68,7 +68,7 @@ def test_forward_reduces_to_dense_swiglu_mlp():
 def test_combine_one_hot_weights_reproduce_y_bitwise():
     inp = workloads.make_full_layer("tiny")
     sh = inp["shape"]
-    ref = layer.forward_full(inp)
+    ref = layer.forward_full(inp, bf16_mode=False)
     # with one-hot weights the combine is a copy of the chosen expert's row
     T, k, H = sh.T, sh.k, sh.H
     yk = ref["y"].reshape(T, k, H)
@@ -104,7 +104,7 @@ def loss_share(inp, x, wg, wu, wd, w):
 
 def test_backward_finite_differences():
     inp = workloads.make_expert_share("micro")
-    g = layer.backward_share(inp)
+    g = layer.backward_share(inp, bf16_mode=False)
     x = bf16.decode(inp["x"]); wg = bf16.decode(inp["w_gate"]); wu = bf16.decode(inp["w_up"])
     wd = bf16.decode(inp["w_down"]); w = inp["row_w"].astype(np.float64)
     rng = np.random.default_rng(9)
@@ -122,7 +122,7 @@ def test_backward_finite_differences():
 
 def test_backward_matches_torch_autograd():
     inp = workloads.make_expert_share("micro")
-    g = layer.backward_share(inp)
+    g = layer.backward_share(inp, bf16_mode=False)
     re = torch.from_numpy(inp["row_expert"].astype(np.int64))
     x = torch.tensor(bf16.decode(inp["x"]), requires_grad=True)
     wg = torch.tensor(bf16.decode(inp["w_gate"]), requires_grad=True)
@@ -197,3 +197,67 @@ def test_ring_contents_wrap():
     for p in range(2 * MB, 4 * MB):
         r = s.inv[p]
         assert np.array_equal(ring[p % (2 * MB)], inp["x"][src[r]])
+
+
+def test_sampled_helpers_match_full_oracle():
+    inp = workloads.make_expert_share("small")
+    full = layer.forward_share(inp)["out"]
+    rows = np.array([0, 7, 500, 999])
+    assert np.allclose(layer.forward_share_rows(inp, rows), full[rows], rtol=1e-12, atol=1e-12)
+    fq = layer.forward_share_mxfp8(inp)["out"]
+    assert np.allclose(layer.forward_share_mxfp8_rows(inp, rows), fq[rows], rtol=1e-12, atol=1e-12)
+    g = layer.backward_share(inp)
+    pairs = [(0, 3), (2, 255), (3, 0)]
+    smp = layer.backward_share_sampled(inp, rows, pairs, pairs)
+    assert np.allclose(smp["dX"], g["dX"][rows], rtol=1e-10, atol=1e-12)
+    assert np.allclose(smp["d_row_w"], g["d_row_w"][rows], rtol=1e-10, atol=1e-12)
+    for n, (e, i) in enumerate(pairs):
+        assert np.allclose(smp["dW_gate"][n], g["dW_gate"][e, i], rtol=1e-10, atol=1e-12)
+        assert np.allclose(smp["dW_up"][n], g["dW_up"][e, i], rtol=1e-10, atol=1e-12)
+        assert np.allclose(smp["dW_down"][n], g["dW_down"][e, :, i], rtol=1e-10, atol=1e-12)
+
+
+def test_full_layer_token_helper_matches_full_oracle():
+    inp = workloads.make_full_layer("tiny")
+    ref = layer.forward_full(inp)
+    toks = [0, 5, 255]
+    got = layer.forward_full_tokens(inp, ref["topk_idx"], ref["topk_w"], toks)
+    assert np.allclose(got, ref["out"][toks], rtol=1e-12, atol=1e-12)
+
+
+def ulp_bf16(v):
+    """Spacing of bf16 values at |v| (2^-133 below the normal range)."""
+    _, e = np.frexp(np.abs(v))
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def test_bf16_mode_forward_within_rounding_bound_of_exact():
+    """bf16 mode differs from the exact layer only by the roundings it names:
+    |out - out_exact| <= half an output ulp + |w| sum_i |W_d[h, i]| half-ulp(a_i)."""
+    inp = workloads.make_expert_share("small")
+    b = layer.forward_share(inp, bf16_mode=True)
+    x = layer.forward_share(inp, bf16_mode=False)
+    assert np.array_equal(bf16.round_rne(b["out"]), b["out"])            # outputs are bf16 values
+    assert np.array_equal(bf16.round_rne(b["a"]), b["a"])                # a is a bf16 operand
+    wd = bf16.decode(inp["w_down"])
+    w = np.abs(inp["row_w"].astype(np.float64))
+    re = inp["row_expert"]
+    bound = np.zeros_like(b["out"])
+    for e in range(wd.shape[0]):
+        sel = np.nonzero(re == e)[0]
+        bound[sel] = w[sel, None] * ((0.5 * ulp_bf16(x["a"][sel])) @ np.abs(wd[e]).T)
+    err = np.abs(b["out"] - x["out"])
+    assert np.all(err <= bound * (1 + 1e-9) + 0.5 * ulp_bf16(b["out"]) + 1e-300)
+    assert np.any(err > 0)
+
+
+def test_bf16_mode_backward_close_to_exact():
+    inp = workloads.make_expert_share("small")
+    b = layer.backward_share(inp, bf16_mode=True)
+    x = layer.backward_share(inp, bf16_mode=False)
+    for k in ("dX", "dW_gate", "dW_up", "dW_down", "d_row_w"):
+        rel = np.linalg.norm(b[k] - x[k]) / np.linalg.norm(x[k])
+        assert rel < 4e-3, (k, rel)
+        if k != "d_row_w":
+            assert rel > 0, k          # the roundings really happen
+    assert np.array_equal(bf16.round_rne(b["dX"]), b["dX"])

@@ -97,7 +97,7 @@ EXPERT_SHARE = {
     # still spanning several GEMM tiles and ragged tails
     "small": ExpertShareShape("small", R=1000, H=512, I=256, E=4,
                               sources=8, zipf_s=1.2, seed=21),
-    "small8": ExpertShareShape("small8", R=1536, H=384, I=320, E=8,
+    "small8": ExpertShareShape("small8", R=1536, H=768, I=512, E=8,
                                sources=8, zipf_s=1.2, seed=22),
     "micro": ExpertShareShape("micro", R=48, H=64, I=32, E=4,
                               sources=4, zipf_s=1.2, seed=23),
