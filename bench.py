@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="run one workload only (full, ep64_fwd, ep64_mxfp8, ep_bwd)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (torch) 3 times: the known-size reference that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return ap.parse_args()
 
 
@@ -254,6 +257,15 @@ def main():
         results["ep_bwd"]["err"] = L.device_error()
         L.close()
         log(json.dumps(results["ep_bwd"]))
+
+    if a.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 1 GiB read + 1 GiB written")
+        del src, dst
 
     # ---- CPU baseline: the oracle on a bounded sample of the main workload --
     cpu = None
