@@ -209,7 +209,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     o_dye = c.take((size_t)npos * H * 2);
     o_dgdu = c.take((size_t)npos * 2 * I * 2);
     o_wa = c.take((size_t)npos * I * 2);
-    o_dwp = c.take((size_t)npos * (I / 64) * 4);
+    o_dwp = c.take((size_t)npos * (I / 128) * 4);
   }
   ws->bytes = c.off;
   if (hipMalloc(&ws->base, ws->bytes) != hipSuccess) {
@@ -461,7 +461,7 @@ int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const void*
   }
   {
     Phase ph(ws, MK_PH_BWD_DW, s);
-    launch_dw_finalize(ws->dw_part, I / 64, ws->sorted_pos, R, d_row_w, (uint16_t*)dX, H, s);
+    launch_dw_finalize(ws->dw_part, I / 128, ws->sorted_pos, R, d_row_w, (uint16_t*)dX, H, s);
   }
   // dX GEMM, rows written back to arrival order (share of the reverse dispatch)
   {

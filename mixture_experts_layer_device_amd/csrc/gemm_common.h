@@ -2,17 +2,30 @@
 // the device work table, the XCD-aware block numbering, and the LDS-staged
 // epilogue that turns the MFMA fragment layout into coalesced row stores.
 #pragma once
+#include <utility>
 #include "mk_device.h"
 #include "mk_internal.h"
 
 namespace mk {
 
-constexpr int G_BM = 256, G_BN = 256, G_NT = 512;
-constexpr int G_FM = 8, G_FN = 4;             // 16x16 fragments per wave (128 x 64)
+constexpr int G_BM = 256, G_BN = 256, G_NT = 256;
+constexpr int G_FM = 8, G_FN = 8;             // 16x16 fragments per wave (128 x 128), 4 waves as 2 x 2
 constexpr int STAGE_ROW_BYTES = 528;          // 512 + 16 pad: conflict-light fragment writes
 constexpr int STAGE_LDS_BYTES = G_BM * STAGE_ROW_BYTES;
 
 typedef f32x4_t GAcc[G_FM][G_FN];
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
+// Epilogues index the accumulator array through it: a body too large for the
+// loop unroller would otherwise leave the array in scratch memory.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that
 // consecutive logical ids share an XCD (and its L2).
@@ -49,19 +62,31 @@ __device__ __forceinline__ void for_each_tile(const ItemRange& ir, int ntn, Body
     int it, nt;
     tile_coords(t, n_items, ntn, it, nt);
     const int* item = ir.items + 4 * (i_lo + it);
-    TileInfo ti{item[0], item[1], item[2], nt * G_BN};
+    // the same for the whole workgroup: keep them in scalar registers, so that
+    // buffer descriptors built from them are uniform
+    TileInfo ti{__builtin_amdgcn_readfirstlane(item[0]), __builtin_amdgcn_readfirstlane(item[1]),
+                __builtin_amdgcn_readfirstlane(item[2]), nt * G_BN};
     body(ti);
   }
 }
 
 __device__ __forceinline__ int frag_row(int i, int v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave >> 2) * 128 + i * 16 + 4 * (lane >> 4) + v;
+  return (wave >> 1) * 128 + i * 16 + 4 * (lane >> 4) + v;
 }
 __device__ __forceinline__ int frag_col(int j) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave & 3) * 64 + j * 16 + (lane & 15);
+  return (wave & 1) * 128 + j * 16 + (lane & 15);
 }
+
+// Row-constant XOR swizzle of the 16-byte granules of a 128-byte LDS row, for
+// the GEMM tiles filled by DMA: key = (row >> 1) & 7.  Measured on gfx950 the
+// MFMA fragment reads (16 consecutive rows, one granule) then run at the LDS's
+// full rate in either k half, and because the key only uses bits 1..3 of the
+// row, a lane's key is the same for every 16-row fragment it reads, so all of
+// its fragment addresses are one register plus immediate offsets.
+__device__ __forceinline__ int tkey(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int tswz(int row, int g) { return row * 128 + (((g ^ tkey(row)) & 7) << 4); }
 
 // Stage a tile of bf16 values through LDS and store each row's COLS values
 // (COLS * 2 bytes, contiguous) with 16-byte stores.
