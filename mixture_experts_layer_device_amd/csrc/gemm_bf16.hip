@@ -62,75 +62,104 @@ __device__ __forceinline__ void read_half(const char* st, int ks, HalfFrags& f) 
   }
 }
 
-// 64 MFMAs on one k half.  The scheduling barriers around it keep the
-// compiler from moving LDS reads, waits or workgroup barriers into the MFMA
-// run (each would stall the wave in front of the matrix core).
-__device__ __forceinline__ void mfma_half(const HalfFrags& f, Acc& acc) {
-  __builtin_amdgcn_sched_barrier(0);
+// 64 MFMAs on one k half, free to be scheduled around (the caller places
+// them with scheduling group barriers).
+__device__ __forceinline__ void mfma_half_free(const HalfFrags& f, Acc& acc) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
-// C[256 x 256] = A[256 x K] * B[256 x K]^T, both K-contiguous.  Row r of the A
-// tile starts at abase + aoff(r) bytes, column n of B at bbase + boff(n); the
-// bases are uniform and the offsets fit in 32 bits.  Tiles go global -> LDS
-// directly (no staging registers): wave w fills rows 64w .. 64w+63 of each
-// operand, 8 full 128-byte rows (1 KiB) per instruction, each lane fetching
-// the granule that the swizzle puts in its slot.
+// The same as one block: the scheduling barriers keep LDS reads, waits and
+// workgroup barriers from being moved into the MFMA run.
+__device__ __forceinline__ void mfma_half(const HalfFrags& f, Acc& acc) {
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_half_free(f, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  pin_acc(acc);
+}
+
+// ------------------------------------------------------- NT mainloop ----
+// C[256 x 256] = A[256 x K] * B[256 x K]^T, both K-contiguous.
 //
-// Pipeline (two LDS stages, two register halves f0/f1): step s runs the MFMAs
-// of half 0 of stage s, then waits for stage s+1 to land and for every wave
-// to be done reading stage s (one workgroup barrier), starts the DMA of stage
-// s+2 into the buffer stage s leaves, reads half 0 of stage s+1 while the
-// MFMAs of half 1 of stage s run, and finally reads half 1 of stage s+1.  A
-// half's reads so always have a whole 64-MFMA run to land.
-template <typename AOff, typename BOff>
+// K advances in steps of 64 through two LDS stages (A and B slices of 256 x
+// 64, 128-byte rows, 32 KiB each), filled global -> LDS by the buffer DMA:
+// wave w loads rows 64w .. 64w+63 of both operands, 8 rows (1 KiB) per
+// instruction, the lane's granule chosen so that slot s of row r holds
+// granule s ^ tkey(r).  A step is two halves of 64 MFMAs with one workgroup
+// barrier between them:
+//   half 1: MFMAs on k 0..31 of stage kt, while this wave reads k 32..63;
+//   barrier (stage kt+1 landed, stage kt read by every wave);
+//   half 2: MFMAs on k 32..63, while the DMA of stage kt+2 refills stage kt's
+//           buffer and this wave reads k 0..31 of stage kt+1.
+// The LDS reads and DMA issues are interleaved one by one between the MFMAs
+// (scheduling group barriers), so the matrix core is fed while the LDS and
+// the memory pipeline work; issuing them as a block in front of the MFMAs
+// stalls all four waves on the LDS after every barrier.  Steps have no
+// branches: past the last stage the DMA re-reads the last stage into the idle
+// buffer and the reads go unused, which keeps the schedule in one block.
+template <typename AOff>
 __device__ __forceinline__ void mainloop_nt(const char* abase, AOff aoff, uint32_t a_bytes, const char* bbase,
-                                            BOff boff, uint32_t b_bytes, int K, char* lds, Acc& acc) {
+                                            uint32_t b_bytes, int K, char* lds, Acc& acc) {
+  constexpr int NR = FM + FN;           // LDS reads per k half
+  constexpr int NM = FM * FN;           // MFMAs per k half
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t ao[8], bo[8];
+  const uint32_t brow = (uint32_t)K * 2;
+  uint32_t ao[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wave * 64 + j * 8 + (lane >> 3);
-    const uint32_t g16 = (uint32_t)(((lane & 7) ^ tkey(r)) & 7) << 4;
-    ao[j] = aoff(r) + g16;
-    bo[j] = boff(r) + g16;
+    ao[j] = aoff(r) + ((uint32_t)(((lane & 7) ^ tkey(r)) & 7) << 4);
   }
-  const int wbase = wave * 8192;
+  // B rows are evenly spaced; tkey(r0 + 8j) = (tkey(r0) + 4j) & 7 only depends on j's parity
+  const int r0 = wave * 64 + (lane >> 3);
+  const uint32_t bo_even = (uint32_t)r0 * brow + ((uint32_t)(((lane & 7) ^ tkey(r0)) & 7) << 4);
+  const uint32_t bo_odd = (uint32_t)r0 * brow + ((uint32_t)(((lane & 7) ^ tkey(r0 + 8)) & 7) << 4);
   const buf_rsrc_t ra = make_rsrc(abase, a_bytes), rb = make_rsrc(bbase, b_bytes);
-  auto issue = [&](uint32_t kb, char* st) {
+  auto issue = [&](int s, int buf) {
+    char* st = lds + buf * STAGE_BYTES + wave * 8192;
+    const uint32_t kb = (uint32_t)s * BK * 2;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      b2lds16(ra, ao[j], kb, st + wbase + j * 1024);
-      b2lds16(rb, bo[j], kb, st + TILE_BYTES + wbase + j * 1024);
+      b2lds16(ra, ao[j], kb, st + j * 1024);
+      b2lds16(rb, (j & 1) ? bo_odd : bo_even, kb + (uint32_t)j * 8 * brow, st + TILE_BYTES + j * 1024);
     }
   };
   zero_acc(acc);
+  pin_acc(acc);
   const int KT = K / BK;
-  issue(0, lds);
+  issue(0, 0);
   wait_all_mem();
   __syncthreads();
-  if (KT > 1) issue(BK * 2, lds + STAGE_BYTES);
-  HalfFrags f0, f1;
-  read_half<tkey>(lds, 0, f0);
-  read_half<tkey>(lds, 1, f1);
+  issue(KT > 1 ? 1 : 0, 1);
+  HalfFrags h0, h1;
+  read_half<tkey>(lds, 0, h0);
   for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    char* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-    mfma_half(f0, acc);
-    if (more) {
-      wait_all_mem();
-      __syncthreads();
-      if (kt + 2 < KT) issue((uint32_t)(kt + 2) * BK * 2, lds + (kt & 1) * STAGE_BYTES);
-      read_half<tkey>(nxt, 0, f0);
+    const int buf = kt & 1;
+    read_half<tkey>(lds + buf * STAGE_BYTES, 1, h1);
+    mfma_half_free(h0, acc);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);      // MFMAs
     }
-    mfma_half(f1, acc);
-    if (more) read_half<tkey>(nxt, 1, f1);
+    wait_all_mem();
+    __syncthreads();
+    issue(kt + 2 < KT ? kt + 2 : KT - 1, buf);
+    read_half<tkey>(lds + (buf ^ 1) * STAGE_BYTES, 0, h0);
+    mfma_half_free(h1, acc);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // 1 memory load (DMA)
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR - NM / NR / 2, 0);
+    }
+    pin_acc(acc);
   }
-  // every wave is done with both buffers before an epilogue reuses the LDS
+  // all DMA landed and every wave done with the LDS before an epilogue reuses it
+  wait_all_mem();
   __syncthreads();
 }
 
@@ -150,13 +179,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       const int p = ti.pos0 + min(r, ti.rows - 1);
       return (uint32_t)(p % ring_rows) * (uint32_t)(H * 2);
     };
-    auto boff = [&](int n) { return (uint32_t)n * (uint32_t)(H * 2); };
     Acc acc;
     mainloop_nt((const char*)ring, aoff, (uint32_t)ring_rows * (uint32_t)(H * 2),
-                (const char*)(wgu + ((int64_t)ti.e * 2 * I + ti.n0) * H), boff, (uint32_t)(BN * H * 2), H, lds, acc);
+                (const char*)(wgu + ((int64_t)ti.e * 2 * I + ti.n0) * H), (uint32_t)(BN * H * 2), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+    static_for<FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = frag_row(i, v);
@@ -171,6 +199,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           }
         }
       }
+    });
     stage_flush<128>(lds, [&](int r) -> uint16_t* {
       return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
     });
@@ -192,12 +221,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int ntn = H / BN;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto aoff = [&](int r) { return (uint32_t)min(r, ti.rows - 1) * (uint32_t)(I * 2); };
-    auto boff = [&](int n) { return (uint32_t)n * (uint32_t)(I * 2); };
     Acc acc;
     mainloop_nt((const char*)(a + (int64_t)ti.pos0 * I), aoff, (uint32_t)ti.rows * (uint32_t)(I * 2),
-                (const char*)(wd + ((int64_t)ti.e * H + ti.n0) * I), boff, (uint32_t)(BN * I * 2), I, lds, acc);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+                (const char*)(wd + ((int64_t)ti.e * H + ti.n0) * I), (uint32_t)(BN * I * 2), I, lds, acc);
+    static_for<FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = frag_row(i, v);
@@ -211,6 +239,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
         }
       }
+    });
     if (SHARE)
       stage_flush<256>(lds, [&](int r) -> uint16_t* {
         return r < ti.rows ? out + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
@@ -236,10 +265,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int slices = I / 128;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto aoff = [&](int r) { return (uint32_t)min(r, ti.rows - 1) * (uint32_t)(H * 2); };
-    auto boff = [&](int n) { return (uint32_t)n * (uint32_t)(H * 2); };
     Acc acc;
     mainloop_nt((const char*)(dye + (int64_t)ti.pos0 * H), aoff, (uint32_t)ti.rows * (uint32_t)(H * 2),
-                (const char*)(wdT + ((int64_t)ti.e * I + ti.n0) * H), boff, (uint32_t)(BN * H * 2), H, lds, acc);
+                (const char*)(wdT + ((int64_t)ti.e * I + ti.n0) * H), (uint32_t)(BN * H * 2), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
     const int slice = (ti.n0 + wn * 128) / 128;
     static_for<FM>([&](auto ic) {
@@ -294,10 +322,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int ntn = H / BN;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto aoff = [&](int r) { return (uint32_t)min(r, ti.rows - 1) * (uint32_t)(I * 4); };
-    auto boff = [&](int n) { return (uint32_t)n * (uint32_t)(I * 4); };
     Acc acc;
     mainloop_nt((const char*)(dgdu + (int64_t)ti.pos0 * 2 * I), aoff, (uint32_t)ti.rows * (uint32_t)(I * 4),
-                (const char*)(wguT + ((int64_t)ti.e * H + ti.n0) * 2 * I), boff, (uint32_t)(BN * I * 4), 2 * I, lds,
+                (const char*)(wguT + ((int64_t)ti.e * H + ti.n0) * 2 * I), (uint32_t)(BN * I * 4), 2 * I, lds,
                 acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)

@@ -15,6 +15,17 @@ constexpr int STAGE_LDS_BYTES = G_BM * STAGE_ROW_BYTES;
 
 typedef f32x4_t GAcc[G_FM][G_FN];
 
+// Ties every accumulator to the accumulation registers at this point (an
+// empty asm with an AGPR operand): keeps the register allocator from moving
+// some of them into ordinary VGPRs, which a long epilogue otherwise invites
+// and which then spills inside the K loop.
+__device__ __forceinline__ void pin_acc(GAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < G_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G_FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
 // f(integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
 // Epilogues index the accumulator array through it: a body too large for the
 // loop unroller would otherwise leave the array in scratch memory.
@@ -34,10 +45,11 @@ __device__ __forceinline__ int xcd_logical_block() {
   return (b & 7) * (G >> 3) + (b >> 3);
 }
 
-// Tile t -> (item, n-tile), in groups of 4 items so that tiles running at the
-// same time on one XCD share A rows (same item) and B columns (same n).
+// Tile t -> (item, n-tile), item fastest within groups of 8 items: the 32
+// tiles an XCD holds at a time (consecutive logical ids) are then 8 items x
+// 4 n-tiles, whose A and B slices (12 distinct per K step) its L2 shares.
 __device__ __forceinline__ void tile_coords(int t, int n_items, int ntn, int& item, int& nt) {
-  constexpr int GM = 4;
+  constexpr int GM = 8;
   const int group = GM * ntn;
   const int g = t / group;
   const int first = g * GM;
@@ -70,6 +82,7 @@ __device__ __forceinline__ void for_each_tile(const ItemRange& ir, int ntn, Body
   }
 }
 
+// Fragment coordinates in the tile: 2 x 2 waves of 128 x 128.
 __device__ __forceinline__ int frag_row(int i, int v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   return (wave >> 1) * 128 + i * 16 + 4 * (lane >> 4) + v;

@@ -68,6 +68,7 @@ __device__ __forceinline__ void mfma_quarter(const Quarter& qa, const Quarter& q
     });
   });
   __builtin_amdgcn_sched_barrier(0);
+  pin_acc(acc);
 }
 
 // C = A . B^T over K codes.  A row r's codes start at abase + aoff(r), its
@@ -128,6 +129,7 @@ __device__ __forceinline__ void mainloop(const MxOperand& A, AOff aoff, ASOff as
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  pin_acc(acc);
   const int KT = K / BKB;
   issue(0, lds);
   wait_all_mem();

@@ -5,69 +5,130 @@
 // multiply-then-add round the same), then + bias.  Fixing the order makes the
 // logits, and with them the top-k decision, bit-identical to any other
 // implementation that follows the same order.  An MFMA or tree reduction
-// would not.
+// would not, so the parallelism comes from the (token, expert) pairs only.
 //
-// Workgroup = one thread per expert (E rounded up to 64) x TT tokens; the x
-// chunk is staged in LDS and broadcast, each thread streams its own router
-// row.  Top-k then runs one wave per token: k rounds of a wave-wide
-// (max logit, min id) reduction.
+// Workgroup = RT tokens x all experts, in chunks of RE experts.  x and the
+// router rows are staged through LDS per RH-wide slice of h, converted to fp32
+// and transposed once ([h][token], [h][expert]), double-buffered with the
+// next slice's global loads in registers.  Thread (tx, ty) keeps the chains of
+// tokens 2ty, 2ty+1 x experts 4tx .. 4tx+3: per h one 8-byte and one 16-byte
+// LDS read (broadcast across the lanes that share them) feed 8 FMAs.  Top-k
+// then runs one wave per token over the logits kept in LDS: k rounds of a
+// wave-wide (max logit, min id) reduction.
 #include "mk_device.h"
 #include "mk_internal.h"
 
 namespace mk {
 namespace {
 
-constexpr int TT = 8;      // tokens per workgroup
-constexpr int HC = 64;     // h per LDS chunk
+constexpr int RT = 16;     // tokens per workgroup
+constexpr int RE = 128;    // experts per chunk
+constexpr int RH = 64;     // h per LDS slice
+constexpr int RNT = 256;   // threads
 
 __device__ __forceinline__ bool better(float za, int ea, float zb, int eb) {
   return za > zb || (za == zb && ea < eb);
 }
 
-__global__ void route_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                             const float* __restrict__ bias, int T, int H, int E, int k, int renorm,
-                             int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  extern __shared__ float zbuf[];                              // [TT][E]
-  __shared__ __attribute__((aligned(16))) uint16_t xs[TT][HC];
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int t0 = blockIdx.x * TT;
-  const int e = tid;
-  float acc[TT];
+__global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                    const float* __restrict__ bias, int T, int H, int E, int k,
+                                                    int renorm, int32_t* __restrict__ idx_out,
+                                                    float* __restrict__ w_out) {
+  extern __shared__ float zbuf[];                                  // [RT][E]
+  __shared__ __attribute__((aligned(16))) float xs[2][RH][RT];
+  __shared__ __attribute__((aligned(16))) float ws[2][RH][RE];
+  const int tid = threadIdx.x;
+  const int tx = tid & 31, ty = tid >> 5;
+  const int t0 = blockIdx.x * RT;
+  // staging roles: router row e0 + (tid & 127), h half (tid >> 7) of the
+  // slice (32 h); threads 0..127 also stage token tid >> 3, h eighth (tid & 7)
+  const int se = tid & 127, sh = (tid >> 7) * 32;
+  const int st_tok = tid >> 3, sq = (tid & 7) * 8;
+  const bool x_stager = tid < 128 && t0 + st_tok < T;
+  for (int e0 = 0; e0 < E; e0 += RE) {
+    const bool w_valid = e0 + se < E;
+    const uint16_t* wrow = w + (int64_t)(w_valid ? e0 + se : 0) * H + sh;
+    const uint16_t* xrow = x + (int64_t)(x_stager ? t0 + st_tok : 0) * H + sq;
+    u32x4_t wr[4], xr{0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-  const uint16_t* wrow = w + (int64_t)min(e, E - 1) * H;
-  for (int h0 = 0; h0 < H; h0 += HC) {
-    __syncthreads();
-    for (int g = tid; g < TT * HC / 8; g += nthr) {
-      const int t = g / (HC / 8), c = g % (HC / 8);
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (t0 + t < T) v = *(const u32x4_t*)(x + (int64_t)(t0 + t) * H + h0 + c * 8);
-      *(u32x4_t*)(&xs[t][c * 8]) = v;
-    }
-    __syncthreads();
+    for (int q = 0; q < 4; ++q) wr[q] = u32x4_t{0u, 0u, 0u, 0u};
+    auto load = [&](int h0) {
+      if (w_valid) {
 #pragma unroll
-    for (int c = 0; c < HC / 8; ++c) {
-      const u32x4_t wv = *(const u32x4_t*)(wrow + h0 + c * 8);
+        for (int q = 0; q < 4; ++q) wr[q] = *(const u32x4_t*)(wrow + h0 + 8 * q);
+      }
+      if (x_stager) xr = *(const u32x4_t*)(xrow + h0);
+    };
+    auto stage = [&](int buf) {
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const u32x4_t xv = *(const u32x4_t*)(&xs[t][c * 8]);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          acc[t] = __builtin_fmaf(bf16_to_f32(xv[d] & 0xFFFFu), bf16_to_f32(wv[d] & 0xFFFFu), acc[t]);
-          acc[t] = __builtin_fmaf(bf16_to_f32(xv[d] >> 16), bf16_to_f32(wv[d] >> 16), acc[t]);
+          ws[buf][sh + 8 * q + 2 * d][se] = bf16_to_f32(wr[q][d] & 0xFFFFu);
+          ws[buf][sh + 8 * q + 2 * d + 1][se] = bf16_to_f32(wr[q][d] >> 16);
+        }
+      if (tid < 128) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          xs[buf][sq + 2 * d][st_tok] = bf16_to_f32(xr[d] & 0xFFFFu);
+          xs[buf][sq + 2 * d + 1][st_tok] = bf16_to_f32(xr[d] >> 16);
         }
       }
-    }
-  }
-  if (e < E) {
-    const float b = bias ? bias[e] : 0.f;
+    };
+    float acc[2][4];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) zbuf[t * E + e] = bias ? acc[t] + b : acc[t];
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    load(0);
+    for (int h0 = 0, buf = 0; h0 < H; h0 += RH, buf ^= 1) {
+      stage(buf);
+      __syncthreads();
+      if (h0 + RH < H) load(h0 + RH);
+      // groups of 4 h, the next group's LDS reads issued before this
+      // group's FMAs so their latency is covered
+      f32x4_t wa[4], wb[4];
+      float2 xa[4], xb[4];
+      auto rdg = [&](int h, f32x4_t (&wv)[4], float2 (&xv)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wv[u] = *(const f32x4_t*)&ws[buf][h + u][4 * tx];
+          xv[u] = *(const float2*)&xs[buf][h + u][2 * ty];
+        }
+      };
+      auto fmg = [&](const f32x4_t (&wv)[4], const float2 (&xv)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[0][j] = __builtin_fmaf(xv[u].x, wv[u][j], acc[0][j]);
+            acc[1][j] = __builtin_fmaf(xv[u].y, wv[u][j], acc[1][j]);
+          }
+      };
+      rdg(0, wa, xa);
+#pragma unroll
+      for (int h = 0; h < RH; h += 8) {
+        rdg(h + 4, wb, xb);
+        fmg(wa, xa);
+        if (h + 8 < RH) rdg(h + 8, wa, xa);
+        fmg(wb, xb);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 4 * tx + j;
+      if (e < E) {
+        const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) zbuf[(2 * ty + i) * E + e] = bias ? acc[i][j] + b : acc[i][j];
+      }
+    }
+    // the next chunk's first staging reuses the slice buffers
+    __syncthreads();
   }
-  __syncthreads();
   // top-k: one wave per token
-  const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-  for (int t = wave; t < TT; t += nwaves) {
+  const int lane = tid & 63, wave = tid >> 6, nwaves = RNT >> 6;
+  for (int t = wave; t < RT; t += nwaves) {
     if (t0 + t >= T) break;
     const float* z = zbuf + t * E;
     uint32_t taken = 0;                       // bit i: expert lane + 64 i chosen
@@ -127,10 +188,9 @@ __global__ void route_kernel(const uint16_t* __restrict__ x, const uint16_t* __r
 void launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E, int k,
                   int renorm, int32_t* idx, float* w, hipStream_t s) {
   if (T <= 0) return;
-  const int threads = ((E + 63) / 64) * 64;
-  const int blocks = (T + TT - 1) / TT;
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(threads), TT * E * sizeof(float), s, x, w_router, bias, T,
-                     H, E, k, renorm, idx, w);
+  const int blocks = (T + RT - 1) / RT;
+  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(RNT), RT * E * sizeof(float), s, x, w_router, bias, T, H, E,
+                     k, renorm, idx, w);
 }
 
 }  // namespace mk

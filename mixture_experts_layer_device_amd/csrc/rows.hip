@@ -108,21 +108,43 @@ __global__ __launch_bounds__(RT) void combine_kernel(const float* __restrict__ y
   const int lane = threadIdx.x & 63;
   const int64_t n8 = H / 8;
   for (int64_t o = wave_id(); o < n_out; o += wave_count()) {
+    // lane j (< kk, kk <= 64) holds the j-th routed row's position and weight
+    const int pj = lane < kk ? sorted_pos[o * kk + lane] : -1;
+    const float wj = lane < kk ? row_w[o * kk + lane] : 0.f;
     for (int64_t g = lane; g < n8; g += 64) {
       float acc[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int j = 0; j < kk; ++j) {
-        const int64_t r = o * kk + j;
-        const int pos = sorted_pos[r];
-        if (pos < 0) continue;
-        const float w = row_w[r];
-        const f32x4_t* src = (const f32x4_t*)(y + (int64_t)pos * H + g * 8);
-        const f32x4_t v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
+      // rows in batches of 8: all loads of a batch in flight, then summed in
+      // row order (the fixed order of the combine)
+      for (int j0 = 0; j0 < kk; j0 += 8) {
+        f32x4_t v[8][2];
+        float wv[8];
+        bool live[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[q] += w * v0[q];
-          acc[4 + q] += w * v1[q];
+        for (int u = 0; u < 8; ++u) {
+          const int j = j0 + u;
+          const int pos = __shfl(pj, j < kk ? j : 0);
+          wv[u] = __shfl(wj, j < kk ? j : 0);
+          live[u] = j < kk && pos >= 0;
+          if (live[u]) {
+            const f32x4_t* src = (const f32x4_t*)(y + (int64_t)pos * H + g * 8);
+            v[u][0] = __builtin_nontemporal_load(src);
+            v[u][1] = __builtin_nontemporal_load(src + 1);
+          } else {
+            v[u][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            v[u][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            wv[u] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (!live[u]) continue;   // a dropped row adds nothing
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[q] += wv[u] * v[u][0][q];
+            acc[4 + q] += wv[u] * v[u][1][q];
+          }
         }
       }
       u32x4_t ov;

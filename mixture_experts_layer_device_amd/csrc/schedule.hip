@@ -77,17 +77,53 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
   __shared__ int sbuf[SCAN_T];
   const int tid = threadIdx.x;
   const int nbe = nb * E;
-  // per (b, e): exclusive prefix over the chunks of minibatch b (in place)
-  for (int be = tid; be < nbe; be += SCAN_T) {
-    const int b = be / E, e = be - b * E;
-    int32_t* cc = chunk_counts + (int64_t)b * cpm * E + e;
-    int run = 0;
-    for (int c = 0; c < cpm; ++c) {
-      const int v = cc[(int64_t)c * E];
-      cc[(int64_t)c * E] = run;
-      run += v;
+  // per (b, e): exclusive prefix over the chunks of minibatch b (in place).
+  // SG consecutive lanes share one (b, e) column, each taking a contiguous
+  // run of chunks: a batched pass for the run sums, a shuffle scan across the
+  // SG lanes, a second pass writing the prefixes.
+  {
+    constexpr int SG = 8;
+    const int sub = tid & (SG - 1);
+    const int per = (cpm + SG - 1) / SG;
+    const int c_lo = min(cpm, sub * per), c_hi = min(cpm, c_lo + per);
+    for (int be0 = 0; be0 < nbe; be0 += SCAN_T / SG) {
+      const int be = be0 + tid / SG;
+      const bool on = be < nbe;
+      int32_t* cc = chunk_counts + (on ? (int64_t)(be / E) * cpm * E + (be % E) : 0);
+      int sum = 0;
+      if (on) {
+        int c = c_lo;
+        for (; c + 4 <= c_hi; c += 4) {
+          const int v0 = cc[(int64_t)c * E], v1 = cc[(int64_t)(c + 1) * E];
+          const int v2 = cc[(int64_t)(c + 2) * E], v3 = cc[(int64_t)(c + 3) * E];
+          sum += v0 + v1 + v2 + v3;
+        }
+        for (; c < c_hi; ++c) sum += cc[(int64_t)c * E];
+      }
+      // inclusive scan over the SG lanes of the group (groups never straddle a wave)
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < SG; o <<= 1) {
+        const int t = __shfl_up(incl, o, SG);
+        if (sub >= o) incl += t;
+      }
+      const int total = __shfl(incl, SG - 1, SG);
+      if (on) {
+        int run = incl - sum;
+        for (int c = c_lo; c < c_hi; c += 8) {
+          int v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = c + i < c_hi ? cc[(int64_t)(c + i) * E] : 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (c + i < c_hi) {
+              cc[(int64_t)(c + i) * E] = run;
+              run += v[i];
+            }
+        }
+        if (sub == 0) mb_counts[be] = total;
+      }
     }
-    mb_counts[be] = run;
   }
   __syncthreads();
   // per minibatch: exclusive scan over experts
