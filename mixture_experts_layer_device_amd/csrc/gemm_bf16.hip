@@ -81,13 +81,18 @@ __device__ __forceinline__ void mfma_half(const HalfFrags& f, Acc& acc) {
 }
 
 // ------------------------------------------------------- NT mainloop ----
-// C[256 x 256] = A[256 x K] * B[256 x K]^T, both K-contiguous.
+// C[256 x 256] = A[256 x K] * B[256 x K]^T.  A is row-major (K-contiguous
+// rows); B comes in the tiled layout, btile pointing at this tile's K / 64
+// blocks, each the LDS image of one stage's B slice.
 //
 // K advances in steps of 64 through two LDS stages (A and B slices of 256 x
 // 64, 128-byte rows, 32 KiB each), filled global -> LDS by the buffer DMA:
 // wave w loads rows 64w .. 64w+63 of both operands, 8 rows (1 KiB) per
-// instruction, the lane's granule chosen so that slot s of row r holds
-// granule s ^ tkey(r).  A step is two halves of 64 MFMAs with one workgroup
+// instruction.  For A each lane fetches the granule that the swizzle puts
+// in its slot (slot s of row r holds granule s ^ tkey(r)); B's block already
+// has that order, so its copies are 1 KiB contiguous (whole DRAM bursts
+// instead of 128-byte pieces of rows 4 KiB or more apart, which stream from
+// HBM markedly slower).  A step is two halves of 64 MFMAs with one workgroup
 // barrier between them:
 //   half 1: MFMAs on k 0..31 of stage kt, while this wave reads k 32..63;
 //   barrier (stage kt+1 landed, stage kt read by every wave);
@@ -100,35 +105,32 @@ __device__ __forceinline__ void mfma_half(const HalfFrags& f, Acc& acc) {
 // branches: past the last stage the DMA re-reads the last stage into the idle
 // buffer and the reads go unused, which keeps the schedule in one block.
 template <typename AOff>
-__device__ __forceinline__ void mainloop_nt(const char* abase, AOff aoff, uint32_t a_bytes, const char* bbase,
-                                            uint32_t b_bytes, int K, char* lds, Acc& acc) {
+__device__ __forceinline__ void mainloop_nt(const char* abase, AOff aoff, uint32_t a_bytes, const uint16_t* btile,
+                                            int K, char* lds, Acc& acc) {
   constexpr int NR = FM + FN;           // LDS reads per k half
   constexpr int NM = FM * FN;           // MFMAs per k half
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t brow = (uint32_t)K * 2;
+  const int KT = K / BK;
   uint32_t ao[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wave * 64 + j * 8 + (lane >> 3);
     ao[j] = aoff(r) + ((uint32_t)(((lane & 7) ^ tkey(r)) & 7) << 4);
   }
-  // B rows are evenly spaced; tkey(r0 + 8j) = (tkey(r0) + 4j) & 7 only depends on j's parity
-  const int r0 = wave * 64 + (lane >> 3);
-  const uint32_t bo_even = (uint32_t)r0 * brow + ((uint32_t)(((lane & 7) ^ tkey(r0)) & 7) << 4);
-  const uint32_t bo_odd = (uint32_t)r0 * brow + ((uint32_t)(((lane & 7) ^ tkey(r0 + 8)) & 7) << 4);
-  const buf_rsrc_t ra = make_rsrc(abase, a_bytes), rb = make_rsrc(bbase, b_bytes);
+  const uint32_t bo = (uint32_t)(wave * 8192 + lane * 16);
+  const buf_rsrc_t ra = make_rsrc(abase, a_bytes), rb = make_rsrc(btile, (uint32_t)KT * STAGE_BYTES / 2);
   auto issue = [&](int s, int buf) {
     char* st = lds + buf * STAGE_BYTES + wave * 8192;
     const uint32_t kb = (uint32_t)s * BK * 2;
+    const uint32_t bb = (uint32_t)s * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       b2lds16(ra, ao[j], kb, st + j * 1024);
-      b2lds16(rb, (j & 1) ? bo_odd : bo_even, kb + (uint32_t)j * 8 * brow, st + TILE_BYTES + j * 1024);
+      b2lds16(rb, bo, bb + (uint32_t)j * 1024, st + TILE_BYTES + j * 1024);
     }
   };
   zero_acc(acc);
   pin_acc(acc);
-  const int KT = K / BK;
   issue(0, 0);
   wait_all_mem();
   __syncthreads();
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     };
     Acc acc;
     mainloop_nt((const char*)ring, aoff, (uint32_t)ring_rows * (uint32_t)(H * 2),
-                (const char*)(wgu + ((int64_t)ti.e * 2 * I + ti.n0) * H), (uint32_t)(BN * H * 2), H, lds, acc);
+                wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
     static_for<FM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 }
 
 // ---------------------------------------------------------------- GEMM2 ----
-// y[p] = a[p] . W_d[e]^T  (W_d stored [E, H, I]).
+// y[p] = a[p] . W_d[e]^T  (W_d as the tiled B of [E, H, I]).
 // SHARE: the router-weighted unpermute is fused: out[inv[p]] = bf16(w * y),
 //        one rounding, rows stored straight to arrival order.
 // else : y is kept in fp32 ([p, H]) for the full-layer combine.
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     auto aoff = [&](int r) { return (uint32_t)min(r, ti.rows - 1) * (uint32_t)(I * 2); };
     Acc acc;
     mainloop_nt((const char*)(a + (int64_t)ti.pos0 * I), aoff, (uint32_t)ti.rows * (uint32_t)(I * 2),
-                (const char*)(wd + ((int64_t)ti.e * H + ti.n0) * I), (uint32_t)(BN * I * 2), I, lds, acc);
+                wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
     static_for<FM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
 #pragma unroll
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 }
 
 // ------------------------------------------------- backward: dA' + SwiGLU ----
-// dA'[p, i] = dYe[p] . W_d[e][:, i]  (B = W_d^T stored [E, I, H]).  Epilogue,
+// dA'[p, i] = dYe[p] . W_d[e][:, i]  (B = W_d^T, tiled [E, I, H]).  Epilogue,
 // from the forward's fp32 g, u: a = silu(g) u; dw partial = sum_i dA' a over
 // this wave's 128 columns; dA = w dA'; dg = dA u s (1 + g (1 - s)); du = dA
 // silu(g) (bf16 GEMM operands, packed like W_gu); w*a (bf16 operand of the
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     auto aoff = [&](int r) { return (uint32_t)min(r, ti.rows - 1) * (uint32_t)(H * 2); };
     Acc acc;
     mainloop_nt((const char*)(dye + (int64_t)ti.pos0 * H), aoff, (uint32_t)ti.rows * (uint32_t)(H * 2),
-                (const char*)(wdT + ((int64_t)ti.e * I + ti.n0) * H), (uint32_t)(BN * H * 2), H, lds, acc);
+                wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
     const int slice = (ti.n0 + wn * 128) / 128;
     static_for<FM>([&](auto ic) {
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 }
 
 // ------------------------------------------------------ backward: dX ----
-// dX[inv[p]] = dgdu[p] . W_gu[e]  (B = packed W_gu^T stored [E, H, 2I]); rows
+// dX[inv[p]] = dgdu[p] . W_gu[e]  (B = packed W_gu^T, tiled [E, H, 2I]); rows
 // are stored straight back to arrival order.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_kernel(ItemRange ir, const uint16_t* __restrict__ dgdu,
                                                     const uint16_t* __restrict__ wguT, int H, int I,
@@ -324,8 +326,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     auto aoff = [&](int r) { return (uint32_t)min(r, ti.rows - 1) * (uint32_t)(I * 4); };
     Acc acc;
     mainloop_nt((const char*)(dgdu + (int64_t)ti.pos0 * 2 * I), aoff, (uint32_t)ti.rows * (uint32_t)(I * 4),
-                (const char*)(wguT + ((int64_t)ti.e * H + ti.n0) * 2 * I), (uint32_t)(BN * I * 4), 2 * I, lds,
-                acc);
+                wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, lds, acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll

@@ -92,13 +92,9 @@ __device__ __forceinline__ int frag_col(int j) {
   return (wave & 1) * 128 + j * 16 + (lane & 15);
 }
 
-// Row-constant XOR swizzle of the 16-byte granules of a 128-byte LDS row, for
-// the GEMM tiles filled by DMA: key = (row >> 1) & 7.  Measured on gfx950 the
-// MFMA fragment reads (16 consecutive rows, one granule) then run at the LDS's
-// full rate in either k half, and because the key only uses bits 1..3 of the
-// row, a lane's key is the same for every 16-row fragment it reads, so all of
-// its fragment addresses are one register plus immediate offsets.
-__device__ __forceinline__ int tkey(int row) { return (row >> 1) & 7; }
+// The GEMM stages keep A and B slices in LDS as 128-byte rows swizzled with
+// tkey (see the tiled B layout); tswz gives the byte offset of granule g of
+// a row.
 __device__ __forceinline__ int tswz(int row, int g) { return row * 128 + (((g ^ tkey(row)) & 7) << 4); }
 
 // Stage a tile of bf16 values through LDS and store each row's COLS values
