@@ -2,41 +2,17 @@
 // the device work table, the XCD-aware block numbering, and the LDS-staged
 // epilogue that turns the MFMA fragment layout into coalesced row stores.
 #pragma once
-#include <utility>
 #include "mk_device.h"
 #include "mk_internal.h"
 
 namespace mk {
 
-constexpr int G_BM = 256, G_BN = 256, G_NT = 256;
-constexpr int G_FM = 8, G_FN = 8;             // 16x16 fragments per wave (128 x 128), 4 waves as 2 x 2
+constexpr int G_BM = 256, G_BN = 256, G_NT = 512;
+constexpr int G_FM = 8, G_FN = 4;             // 16x16 fragments per wave (128 x 64)
 constexpr int STAGE_ROW_BYTES = 528;          // 512 + 16 pad: conflict-light fragment writes
 constexpr int STAGE_LDS_BYTES = G_BM * STAGE_ROW_BYTES;
 
 typedef f32x4_t GAcc[G_FM][G_FN];
-
-// Ties every accumulator to the accumulation registers at this point (an
-// empty asm with an AGPR operand): keeps the register allocator from moving
-// some of them into ordinary VGPRs, which a long epilogue otherwise invites
-// and which then spills inside the K loop.
-__device__ __forceinline__ void pin_acc(GAcc& acc) {
-#pragma unroll
-  for (int i = 0; i < G_FM; ++i)
-#pragma unroll
-    for (int j = 0; j < G_FN; ++j) asm volatile("" : "+a"(acc[i][j]));
-}
-
-// f(integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
-// Epilogues index the accumulator array through it: a body too large for the
-// loop unroller would otherwise leave the array in scratch memory.
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that
 // consecutive logical ids share an XCD (and its L2).
@@ -45,11 +21,10 @@ __device__ __forceinline__ int xcd_logical_block() {
   return (b & 7) * (G >> 3) + (b >> 3);
 }
 
-// Tile t -> (item, n-tile), item fastest within groups of 8 items: the 32
-// tiles an XCD holds at a time (consecutive logical ids) are then 8 items x
-// 4 n-tiles, whose A and B slices (12 distinct per K step) its L2 shares.
+// Tile t -> (item, n-tile), in groups of 4 items so that tiles running at the
+// same time on one XCD share A rows (same item) and B columns (same n).
 __device__ __forceinline__ void tile_coords(int t, int n_items, int ntn, int& item, int& nt) {
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int group = GM * ntn;
   const int g = t / group;
   const int first = g * GM;
@@ -74,28 +49,19 @@ __device__ __forceinline__ void for_each_tile(const ItemRange& ir, int ntn, Body
     int it, nt;
     tile_coords(t, n_items, ntn, it, nt);
     const int* item = ir.items + 4 * (i_lo + it);
-    // the same for the whole workgroup: keep them in scalar registers, so that
-    // buffer descriptors built from them are uniform
-    TileInfo ti{__builtin_amdgcn_readfirstlane(item[0]), __builtin_amdgcn_readfirstlane(item[1]),
-                __builtin_amdgcn_readfirstlane(item[2]), nt * G_BN};
+    TileInfo ti{item[0], item[1], item[2], nt * G_BN};
     body(ti);
   }
 }
 
-// Fragment coordinates in the tile: 2 x 2 waves of 128 x 128.
 __device__ __forceinline__ int frag_row(int i, int v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave >> 1) * 128 + i * 16 + 4 * (lane >> 4) + v;
+  return (wave >> 2) * 128 + i * 16 + 4 * (lane >> 4) + v;
 }
 __device__ __forceinline__ int frag_col(int j) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave & 1) * 128 + j * 16 + (lane & 15);
+  return (wave & 3) * 64 + j * 16 + (lane & 15);
 }
-
-// The GEMM stages keep A and B slices in LDS as 128-byte rows swizzled with
-// tkey (see the tiled B layout); tswz gives the byte offset of granule g of
-// a row.
-__device__ __forceinline__ int tswz(int row, int g) { return row * 128 + (((g ^ tkey(row)) & 7) << 4); }
 
 // Stage a tile of bf16 values through LDS and store each row's COLS values
 // (COLS * 2 bytes, contiguous) with 16-byte stores.

@@ -75,16 +75,14 @@ __device__ __forceinline__ uint32_t mx_encode(uint32_t bits, int se) {
   return sign | code;
 }
 
-// XOR swizzle of 16-byte granules in a 128-byte-per-row LDS tile.  The key
-// was picked by timing ds_read_b128 / ds_write_b128 patterns on gfx950: with
-// it the MFMA fragment reads (16 consecutive rows, one granule) run at the
-// LDS's full rate for either k half, and the weight-gradient kernel's
-// transposed writes (rows 8m + c over m) lose the least.
-__device__ __forceinline__ int swz_key(int row) { return ((row >> 1) ^ (row >> 3) ^ (row >> 5)) & 7; }
-__device__ __forceinline__ int lds_swz(int row, int g) { return row * 128 + (((g ^ swz_key(row)) & 7) << 4); }
+// XOR swizzle of 16-byte granules in a 128-byte-per-row LDS tile: conflict
+// free for 8 or 16 consecutive rows reading the same logical granule.
+__device__ __forceinline__ int lds_swz(int row, int g) {
+  return row * 128 + ((((g ^ row ^ (row >> 3))) & 7) << 4);
+}
 
 // Inverse of lds_swz inside a row: the logical granule that lands in slot s.
-__device__ __forceinline__ int lds_unswz(int row, int s) { return (s ^ swz_key(row)) & 7; }
+__device__ __forceinline__ int lds_unswz(int row, int s) { return (s ^ row ^ (row >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -97,43 +95,5 @@ __device__ __forceinline__ void g2lds4(const void* src, char* wave_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)wave_dst, 4, 0, 0);
 }
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// ---- tiled GEMM B operand ("LDS image" layout) ----------------------------
-//
-// A bf16 B operand B[e][n][k] (N a multiple of 256, K of 64) is stored as
-// 32 KiB blocks, one per (e, n / 256, k / 64) in that order, each holding the
-// 256 x 64 slice exactly as the GEMM stage keeps it in LDS: 128-byte rows,
-// the row's 16-byte granule g (k = 8g .. 8g+7 of the slice) in slot
-// g ^ tkey(row).  A stage's B slice then arrives with 1 KiB contiguous DMA
-// copies.  tkey = (row >> 1) & 7 makes the MFMA fragment reads (16 rows, one
-// granule) conflict-free and, using bits 1..3 of the row only, is the same for
-// every 16-row fragment a lane reads.
-__device__ __forceinline__ int tkey(int row) { return (row >> 1) & 7; }
-constexpr int BT_ROWS = 256, BT_K = 64, BT_BLOCK = BT_ROWS * BT_K;   // elements per block
-__device__ __forceinline__ int64_t btile_block(int e, int nt, int kt, int N, int K) {
-  return (((int64_t)e * (N / BT_ROWS) + nt) * (K / BT_K) + kt) * BT_BLOCK;
-}
-// element offset of the 16-byte granule holding B[e][n][k .. k+7] (k % 8 == 0)
-__device__ __forceinline__ int64_t btile_granule(int e, int n, int k, int N, int K) {
-  const int r = n % BT_ROWS, g = (k % BT_K) / 8;
-  return btile_block(e, n / BT_ROWS, k / BT_K, N, K) + r * BT_K + ((g ^ tkey(r)) & 7) * 8;
-}
-
-// Raw buffer resource over [base, base + bytes) (word 3: 32-bit data format,
-// the plain raw-buffer setting on gfx9).  Loads through it past `bytes`
-// return zeros instead of touching memory.
-typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
-__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// Asynchronous buffer -> LDS copy: lane i's bytes at voff + soff land at
-// wave_dst + size*i.  The offsets are 32-bit, the base lives in scalar
-// registers, so a whole tile's addresses cost one register per row group.
-__device__ __forceinline__ void b2lds16(buf_rsrc_t r, uint32_t voff, uint32_t soff, char* wave_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_dst, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void b2lds4(buf_rsrc_t r, uint32_t voff, uint32_t soff, char* wave_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_dst, 4, voff, soff, 0, 0);
-}
 
 }  // namespace mk
