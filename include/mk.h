@@ -173,8 +173,11 @@ int mk_mxfp8_quantize(const void* in_dev, int64_t rows, int32_t K, uint8_t* code
  *   w_gate_dev [E, I, H] bf16, w_up_dev [E, I, H] bf16, w_down_dev [E, H, I] bf16
  * packed_dev receives mk_query(MK_Q_PACKED_BYTES[_BWD]) bytes: gate and up
  * rows interleaved in blocks of 16 (GEMM1's B), the down rows (GEMM2's B),
- * in MXFP8 mode as E4M3 codes + E8M0 scales along each GEMM's K; with
- * for_backward = 1 also the transposed bf16 copies the backward GEMMs read.
+ * with for_backward = 1 also the transposed copies the backward GEMMs read.
+ * bf16 mode stores each of them as 32 KiB blocks of 256 rows x 64 K in the
+ * order (expert, row block, K block), every block laid out as the GEMM keeps
+ * it in LDS; MXFP8 mode as row-major E4M3 codes + E8M0 scales along each
+ * GEMM's K.  The layout is internal: only this library reads the buffer.
  */
 int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_up_dev,
                        const void* w_down_dev, int32_t for_backward, void* packed_dev,

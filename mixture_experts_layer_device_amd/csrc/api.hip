@@ -110,7 +110,7 @@ struct Phase {
 
 }  // namespace
 
-// quantise packed gate/up rows (see launch_pack_gate_up) straight to MXFP8
+// quantise packed gate/up rows (16 gate rows, then the 16 up rows of the same i) straight to MXFP8
 namespace mk {
 void launch_quant_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint8_t* codes,
                                uint8_t* scales, hipStream_t s);
@@ -354,11 +354,12 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, c
     return check_launch();
   }
   PackedBF16 p = packed_bf16(ws, packed);
-  launch_pack_gate_up((const uint16_t*)w_gate, (const uint16_t*)w_up, E, I, H, p.wgu, s);
-  launch_copy(w_down, p.wd, (int64_t)E * H * I * 2, s);
+  const uint16_t *wg = (const uint16_t*)w_gate, *wu = (const uint16_t*)w_up, *wd = (const uint16_t*)w_down;
+  launch_tile_rows(wg, wu, 1, E, 2 * I, H, p.wgu, s);      // GEMM1 B: [E][2I][H]
+  launch_tile_rows(wd, nullptr, 0, E, H, I, p.wd, s);      // GEMM2 B: [E][H][I]
   if (for_backward) {
-    launch_transpose(p.wd, E, H, I, p.wdT, s);         // [E, H, I] -> [E, I, H]
-    launch_transpose(p.wgu, E, 2 * I, H, p.wguT, s);   // [E, 2I, H] -> [E, H, 2I]
+    launch_tile_cols(wd, nullptr, 0, E, I, H, p.wdT, s);   // dA' B: W_d^T [E][I][H]
+    launch_tile_cols(wg, wu, 1, E, H, 2 * I, p.wguT, s);   // dX B: W_gu^T [E][H][2I]
   }
   return check_launch();
 }

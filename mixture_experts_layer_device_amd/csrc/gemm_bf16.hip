@@ -38,6 +38,16 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// LDS offset of granule g of tile row r: the NT GEMMs' stages use the tkey
+// swizzle (the tiled B layout's), the weight-gradient stages lds_swz.
+struct SwzT {
+  __device__ static int off(int r, int g) { return r * 128 + (((g ^ tkey(r)) & 7) << 4); }
+};
+struct SwzW {
+  __device__ static int off(int r, int g) { return lds_swz(r, g); }
+};
+
+template <typename Swz>
 __device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -48,11 +58,9 @@ __device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
     const int g = ks * 4 + (lane >> 4);
     bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[i] = *(const bf16x8_t*)(sA + lds_swz(wm * 128 + i * 16 + (lane & 15), g));
+    for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)(sA + Swz::off(wm * 128 + i * 16 + (lane & 15), g));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[j] = *(const bf16x8_t*)(sB + lds_swz(wn * 64 + j * 16 + (lane & 15), g));
+    for (int j = 0; j < FN; ++j) bfr[j] = *(const bf16x8_t*)(sB + Swz::off(wn * 64 + j * 16 + (lane & 15), g));
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -61,29 +69,30 @@ __device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
   }
 }
 
-// C[256 x 256] = A[256 x K] * B[256 x K]^T, both K-contiguous.  arow(r) / brow(n)
-// return a pointer to element 0 of tile row r / tile column n.  Tiles go
-// global -> LDS directly (no staging registers): wave w fills rows
-// 32w .. 32w+31 of each operand, 8 rows (1 KiB) per instruction, and each lane
-// reads the granule that the swizzle puts in its slot.
-template <typename ARow, typename BRow>
-__device__ __forceinline__ void mainloop_nt(ARow arow, BRow brow, int K, char* lds, Acc& acc) {
+// C[256 x 256] = A[256 x K] * B[256 x K]^T.  arow(r) returns a pointer to
+// element 0 of A tile row r (K-contiguous rows); B comes in the tiled layout,
+// btile pointing at this tile's K / 64 blocks, each the LDS image of one
+// stage's B slice.  Tiles go global -> LDS directly (no staging registers):
+// wave w fills rows 32w .. 32w+31 of each operand, 8 rows (1 KiB) per
+// instruction; for A each lane reads the granule that the swizzle puts in its
+// slot, for B the copy is 1 KiB contiguous.
+template <typename ARow>
+__device__ __forceinline__ void mainloop_nt(ARow arow, const uint16_t* btile, int K, char* lds, Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const char* ap[4];
-  const char* bp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = wave * 32 + j * 8 + (lane >> 3);
-    const int g = lds_unswz(r, lane & 7);
-    ap[j] = (const char*)arow(r) + g * 16;
-    bp[j] = (const char*)brow(r) + g * 16;
+    ap[j] = (const char*)arow(r) + (((lane & 7) ^ tkey(r)) & 7) * 16;
   }
   const int wbase = wave * 4096;
+  const char* bp = (const char*)btile + wbase + lane * 16;
   auto issue = [&](int64_t kb, char* st) {
+    const char* b = bp + kb / (BK * 2) * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       g2lds16(ap[j] + kb, st + wbase + j * 1024);
-      g2lds16(bp[j] + kb, st + TILE_BYTES + wbase + j * 1024);
+      g2lds16(b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
     }
   };
   zero_acc(acc);
@@ -94,7 +103,7 @@ __device__ __forceinline__ void mainloop_nt(ARow arow, BRow brow, int K, char* l
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) issue((int64_t)(kt + 1) * BK * 2, lds + (cur ^ 1) * STAGE_BYTES);
-    mma_stage(lds + cur * STAGE_BYTES, acc);
+    mma_stage<SwzT>(lds + cur * STAGE_BYTES, acc);
     wait_all_mem();
     __syncthreads();
   }
@@ -116,9 +125,8 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
       const int p = ti.pos0 + min(r, ti.rows - 1);
       return ring + (int64_t)(p % ring_rows) * H;
     };
-    auto brow = [&](int n) { return wgu + ((int64_t)ti.e * 2 * I + ti.n0 + n) * H; };
     Acc acc;
-    mainloop_nt(arow, brow, H, lds, acc);
+    mainloop_nt(arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
 }
 
 // ---------------------------------------------------------------- GEMM2 ----
-// y[p] = a[p] . W_d[e]^T  (W_d stored [E, H, I]).
+// y[p] = a[p] . W_d[e]^T  (W_d as the tiled B of [E, H, I]).
 // SHARE: the router-weighted unpermute is fused: out[inv[p]] = bf16(w * y),
 //        one rounding, rows stored straight to arrival order.
 // else : y is kept in fp32 ([p, H]) for the full-layer combine.
@@ -157,9 +165,8 @@ __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint
   const int ntn = H / BN;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
-    auto brow = [&](int n) { return wd + ((int64_t)ti.e * H + ti.n0 + n) * I; };
     Acc acc;
-    mainloop_nt(arow, brow, I, lds, acc);
+    mainloop_nt(arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint
 }
 
 // ------------------------------------------------- backward: dA' + SwiGLU ----
-// dA'[p, i] = dYe[p] . W_d[e][:, i]  (B = W_d^T stored [E, I, H]).  Epilogue,
+// dA'[p, i] = dYe[p] . W_d[e][:, i]  (B = W_d^T, tiled [E, I, H]).  Epilogue,
 // from the forward's fp32 g, u: a = silu(g) u; dw partial = sum_i dA' a over
 // this wave's 64 columns; dA = w dA'; dg = dA u s (1 + g (1 - s)); du = dA
 // silu(g) (bf16 GEMM operands, packed like W_gu); w*a (bf16 operand of the
@@ -200,9 +207,8 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
   const int slices = I / 64;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dye + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * H; };
-    auto brow = [&](int n) { return wdT + ((int64_t)ti.e * I + ti.n0 + n) * H; };
     Acc acc;
-    mainloop_nt(arow, brow, H, lds, acc);
+    mainloop_nt(arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
     const int slice = (ti.n0 + wn * 64) / 64;
 #pragma unroll
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
 }
 
 // ------------------------------------------------------ backward: dX ----
-// dX[inv[p]] = dgdu[p] . W_gu[e]  (B = packed W_gu^T stored [E, H, 2I]); rows
+// dX[inv[p]] = dgdu[p] . W_gu[e]  (B = packed W_gu^T, tiled [E, H, 2I]); rows
 // are stored straight back to arrival order.
 __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t* __restrict__ dgdu,
                                                     const uint16_t* __restrict__ wguT, int H, int I,
@@ -258,9 +264,8 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t
   const int ntn = H / BN;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dgdu + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * 2 * I; };
-    auto brow = [&](int n) { return wguT + ((int64_t)ti.e * H + ti.n0 + n) * 2 * I; };
     Acc acc;
-    mainloop_nt(arow, brow, 2 * I, lds, acc);
+    mainloop_nt(arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, lds, acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
         SegIter nxt = cur;
         const bool more = seg_next(nxt, w, e);
         if (more) wgrad_load<MODE>(op, w, nxt, m0, n0, v);
-        mma_stage(lds + stage * STAGE_BYTES, acc);
+        mma_stage<SwzW>(lds + stage * STAGE_BYTES, acc);
         if (more) wgrad_store(lds + (stage ^ 1) * STAGE_BYTES, v);
         __syncthreads();
         if (!more) break;

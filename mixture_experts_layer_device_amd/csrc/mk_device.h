@@ -84,6 +84,27 @@ __device__ __forceinline__ int lds_swz(int row, int g) {
 // Inverse of lds_swz inside a row: the logical granule that lands in slot s.
 __device__ __forceinline__ int lds_unswz(int row, int s) { return (s ^ row ^ (row >> 3)) & 7; }
 
+// ---- tiled GEMM B operand ("LDS image" layout) ----------------------------
+//
+// A bf16 B operand B[e][n][k] (N a multiple of 256, K of 64) is stored as
+// 32 KiB blocks, one per (e, n / 256, k / 64) in that order, each holding the
+// 256 x 64 slice exactly as the GEMM stage keeps it in LDS: 128-byte rows,
+// the row's 16-byte granule g (k = 8g .. 8g+7 of the slice) in slot
+// g ^ tkey(row).  A stage's B slice then arrives with 1 KiB contiguous DMA
+// copies.  tkey = (row >> 1) & 7 makes the MFMA fragment reads (16 rows, one
+// granule) conflict-free and, using bits 1..3 of the row only, is the same for
+// every 16-row fragment a lane reads.
+__device__ __forceinline__ int tkey(int row) { return (row >> 1) & 7; }
+constexpr int BT_ROWS = 256, BT_K = 64, BT_BLOCK = BT_ROWS * BT_K;   // elements per block
+__device__ __forceinline__ int64_t btile_block(int e, int nt, int kt, int N, int K) {
+  return (((int64_t)e * (N / BT_ROWS) + nt) * (K / BT_K) + kt) * BT_BLOCK;
+}
+// element offset of the 16-byte granule holding B[e][n][k .. k+7] (k % 8 == 0)
+__device__ __forceinline__ int64_t btile_granule(int e, int n, int k, int N, int K) {
+  const int r = n % BT_ROWS, g = (k % BT_K) / 8;
+  return btile_block(e, n / BT_ROWS, k / BT_K, N, K) + r * BT_K + ((g ^ tkey(r)) & 7) * 8;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Asynchronous global -> LDS copy (global_load_lds_dwordx4 / _dword): lane i's

@@ -69,10 +69,12 @@ void launch_quantize(const uint16_t* in, int64_t rows, int K, uint8_t* codes, ui
                      hipStream_t s);
 void launch_dw_finalize(const float* dw_part, int slices, const int32_t* sorted_pos, int64_t R,
                         float* d_row_w, uint16_t* dX, int64_t H, hipStream_t s);
-void launch_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H,
-                         uint16_t* out, hipStream_t s);
-void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
-void launch_transpose(const uint16_t* in, int batch, int rows, int cols, uint16_t* out,
+// tiled B operands (btile_* layout in mk_device.h); source rows: mode 0 rows of
+// src_a, mode 1 the gate/up interleave of src_a (gate) and src_b (up)
+//   tile_rows: B[e][n][k] = row(e, n)[k]    tile_cols: B[e][n][k] = row(e, k)[n]
+void launch_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K, uint16_t* out,
+                      hipStream_t s);
+void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K, uint16_t* out,
                       hipStream_t s);
 void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 

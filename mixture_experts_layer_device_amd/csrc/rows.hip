@@ -182,18 +182,62 @@ __global__ void dw_finalize_kernel(const float* __restrict__ dw_part, int slices
 }
 
 // packed row c of expert e: gate row (c/32)*16 + c%16 if c%32 < 16, else up row.
-__global__ void pack_gate_up_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu, int I, int H,
-                                    uint16_t* __restrict__ out) {
-  const int64_t row = blockIdx.x;            // e * 2I + c
-  const int e = (int)(row / (2 * I)), c = (int)(row % (2 * I));
-  const int i = (c >> 5) * 16 + (c & 15);
-  const uint16_t* src = ((c & 31) < 16 ? wg : wu) + ((int64_t)e * I + i) * H;
-  const u32x4_t* s = (const u32x4_t*)src;
-  u32x4_t* d = (u32x4_t*)(out + row * H);
-  for (int g = threadIdx.x; g < H / 8; g += blockDim.x) d[g] = s[g];
+// Source row of the B operand rows: mode 0 -> src_a + (e * R + row) * len;
+// mode 1 (gate/up) -> packed row c of expert e: 32-row groups of 16 gate rows
+// then the 16 up rows of the same i (R = 2I).
+__device__ __forceinline__ const uint16_t* b_src_row(const uint16_t* src_a, const uint16_t* src_b, int mode, int e,
+                                                     int row, int R, int64_t len) {
+  if (mode == 0) return src_a + ((int64_t)e * R + row) * len;
+  const int I = R / 2, i = (row >> 5) * 16 + (row & 15);
+  return ((row & 31) < 16 ? src_a : src_b) + ((int64_t)e * I + i) * len;
 }
 
-// MXFP8 codes/scales of packed gate/up row e*2I + c (row mapping as above),
+// Tiled B from source rows: B[e][n][k] = row(e, n)[k].  One thread per
+// 16-byte granule, k fastest (reads of a row are contiguous).
+__global__ void tile_rows_kernel(const uint16_t* __restrict__ src_a, const uint16_t* __restrict__ src_b, int mode,
+                                 int E, int N, int K, uint16_t* __restrict__ out) {
+  const int64_t kg = K / 8, total = (int64_t)E * N * kg;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+    const int k = (int)(q % kg) * 8;
+    const int64_t en = q / kg;
+    const int e = (int)(en / N), n = (int)(en % N);
+    const u32x4_t v = *(const u32x4_t*)(b_src_row(src_a, src_b, mode, e, n, N, K) + k);
+    *(u32x4_t*)(out + btile_granule(e, n, k, N, K)) = v;
+  }
+}
+
+// Tiled B from transposed source rows: B[e][n][k] = row(e, k)[n] (rows of
+// length N, R = K rows per expert).  One workgroup per 256 x 64 block: the 64
+// source row pieces (512 bytes each) go through LDS, then each thread
+// assembles 8 output granules.
+__global__ __launch_bounds__(256) void tile_cols_kernel(const uint16_t* __restrict__ src_a,
+                                                        const uint16_t* __restrict__ src_b, int mode, int N, int K,
+                                                        uint16_t* __restrict__ out) {
+  constexpr int LD = BT_ROWS + 8;
+  __shared__ uint16_t t[BT_K][LD];
+  const int nt = blockIdx.x, kt = blockIdx.y, e = blockIdx.z, tid = threadIdx.x;
+  const int n0 = nt * BT_ROWS, k0 = kt * BT_K;
+  for (int q = tid; q < BT_K * (BT_ROWS / 8); q += 256) {
+    const int kk = q / (BT_ROWS / 8), c = (q % (BT_ROWS / 8)) * 8;
+    const u32x4_t v = *(const u32x4_t*)(b_src_row(src_a, src_b, mode, e, k0 + kk, K, N) + n0 + c);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      t[kk][c + 2 * d] = (uint16_t)(v[d] & 0xFFFFu);
+      t[kk][c + 2 * d + 1] = (uint16_t)(v[d] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* blk = out + btile_block(e, nt, kt, N, K);
+  for (int q = tid; q < BT_ROWS * (BT_K / 8); q += 256) {
+    const int r = q / (BT_K / 8), g = q % (BT_K / 8);
+    u32x4_t v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = (uint32_t)t[8 * g + 2 * d][r] | ((uint32_t)t[8 * g + 2 * d + 1][r] << 16);
+    *(u32x4_t*)(blk + r * BT_K + ((g ^ tkey(r)) & 7) * 8) = v;
+  }
+}
+
+// MXFP8 codes/scales of packed gate/up row e*2I + c (the b_src_row mapping),
 // one wave per row.
 __global__ __launch_bounds__(RT) void quant_pack_gate_up_kernel(const uint16_t* __restrict__ wg,
                                                                 const uint16_t* __restrict__ wu, int64_t n_rows,
@@ -221,23 +265,6 @@ __global__ __launch_bounds__(RT) void quant_pack_gate_up_kernel(const uint16_t* 
 }
 
 // out[b][c][r] = in[b][r][c], 64 x 64 tiles through LDS.
-__global__ void transpose_kernel(const uint16_t* __restrict__ in, int rows, int cols, uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[64][65];
-  const int64_t b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* src = in + b * rows * (int64_t)cols;
-  uint16_t* dst = out + b * rows * (int64_t)cols;
-  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
-    const int r = r0 + i, c = c0 + threadIdx.x;
-    if (r < rows && c < cols) tile[i][threadIdx.x] = src[(int64_t)r * cols + c];
-  }
-  __syncthreads();
-  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
-    const int c = c0 + i, r = r0 + threadIdx.x;
-    if (c < cols && r < rows) dst[(int64_t)c * rows + r] = tile[threadIdx.x][i];
-  }
-}
-
 int row_grid(int64_t rows, int n_cu) {
   const int64_t want = (rows + (RT / 64) - 1) / (RT / 64);
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)n_cu * 8));
@@ -287,9 +314,16 @@ void launch_dw_finalize(const float* dw_part, int slices, const int32_t* sorted_
                      dX, H);
 }
 
-void launch_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint16_t* out,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(pack_gate_up_kernel, dim3((unsigned)((int64_t)E * 2 * I)), dim3(256), 0, s, wg, wu, I, H,
+void launch_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K, uint16_t* out,
+                      hipStream_t s) {
+  const int64_t total = (int64_t)E * N * (K / 8);
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(tile_rows_kernel, dim3(blocks), dim3(256), 0, s, src_a, src_b, mode, E, N, K, out);
+}
+
+void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K, uint16_t* out,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(tile_cols_kernel, dim3(N / BT_ROWS, K / BT_K, E), dim3(256), 0, s, src_a, src_b, mode, N, K,
                      out);
 }
 
@@ -300,13 +334,5 @@ void launch_quant_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, in
                      codes, scales);
 }
 
-void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
-  (void)hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice, s);
-}
-
-void launch_transpose(const uint16_t* in, int batch, int rows, int cols, uint16_t* out, hipStream_t s) {
-  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(64, 4), 0, s, in, rows, cols, out);
-}
 
 }  // namespace mk
