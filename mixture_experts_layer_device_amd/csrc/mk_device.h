@@ -39,41 +39,16 @@ __device__ __forceinline__ int mx_scale_code(uint32_t amax_bits) {
   return se + 127;
 }
 
-// E4M3-FN code of (bf16 value) / 2^se, nearest-even, saturating at 448,
-// sign kept.  Works on integer significands: exact for every bf16 input.
-__device__ __forceinline__ uint32_t mx_encode(uint32_t bits, int se) {
-  uint32_t sign = (bits >> 8) & 0x80u;
-  int E = (int)((bits >> 7) & 0xFF);
-  int m = (int)(bits & 0x7F);
-  if (E == 0 && m == 0) return sign;
-  int S, x;                                  // |v| = S * 2^x
-  if (E) { S = 128 | m; x = E - 134; } else { S = m; x = -133; }
-  int pb = 31 - __clz(S);                    // msb of S
-  int eq = pb + x - se;                      // floor(log2 |v / 2^se|)
-  bool normal = eq >= -6;
-  int shift = normal ? pb - 3 : -(x - se + 9);
-  uint32_t keep;
-  if (shift <= 0) {
-    keep = (uint32_t)S << (-shift);
-  } else if (shift > 24) {
-    keep = 0;
-  } else {
-    keep = (uint32_t)S >> shift;
-    uint32_t rem = (uint32_t)S & ((1u << shift) - 1u);
-    uint32_t half = 1u << (shift - 1);
-    if (rem > half || (rem == half && (keep & 1u))) ++keep;
-  }
-  uint32_t code;
-  if (normal) {
-    if (keep == 16) { keep = 8; ++eq; }
-    if (eq > 8) return sign | 0x7Eu;
-    code = ((uint32_t)(eq + 7) << 3) | (keep - 8);
-    if (code > 0x7Eu) code = 0x7Eu;
-  } else {
-    code = keep;                              // 0..8 (8 = smallest normal, code 0x08)
-  }
-  return sign | code;
+// The same code through the hardware conversion: the fp32 value times the
+// power of two 2^-se (exact: the product is a normal fp32 number, or below
+// 2^-126 and so far under E4M3's smallest subnormal that it encodes to a
+// signed zero either way), clamped to +-448 (every value at or beyond 448
+// encodes to 448 under saturating nearest-even rounding), then
+// v_cvt_pk_fp8_f32 (OCP E4M3, nearest-even).
+__device__ __forceinline__ float e4m3_prescale(float x, float inv_scale) {
+  return fminf(fmaxf(x * inv_scale, -448.f), 448.f);
 }
+
 
 // XOR swizzle of 16-byte granules in a 128-byte-per-row LDS tile: conflict
 // free for 8 or 16 consecutive rows reading the same logical granule.

@@ -54,14 +54,19 @@ __device__ __forceinline__ uint32_t quant_block(const u32x4_t (&v)[4], u32x4_t (
       amax = max(amax, (v[q][d] >> 16) & 0x7FFFu);
     }
   const int s = mx_scale_code(amax);
-  const int se = s - 127;
+  // 2^-se as an fp32 power of two (se in [-127, 119]: exponent field 8 .. 254)
+  const float inv = __uint_as_float((uint32_t)(254 - s) << 23);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int d = 0; d < 4; d += 2) {
-      const uint32_t b0 = mx_encode(v[q][d] & 0xFFFFu, se), b1 = mx_encode(v[q][d] >> 16, se);
-      const uint32_t b2 = mx_encode(v[q][d + 1] & 0xFFFFu, se), b3 = mx_encode(v[q][d + 1] >> 16, se);
-      c[q >> 1][(q & 1) * 2 + (d >> 1)] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      float x[4] = {bf16_to_f32(v[q][d] & 0xFFFFu), bf16_to_f32(v[q][d] >> 16), bf16_to_f32(v[q][d + 1] & 0xFFFFu),
+                    bf16_to_f32(v[q][d + 1] >> 16)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = e4m3_prescale(x[u], inv);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+      c[q >> 1][(q & 1) * 2 + (d >> 1)] = (uint32_t)w;
     }
   return (uint32_t)s;
 }

@@ -163,6 +163,36 @@ def test_mxfp8_quantize_bit_exact():
         assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+def test_mxfp8_quantize_every_value_at_every_scale():
+    """Every finite bf16 magnitude (both signs) quantised at every block scale
+    that can hold it: a power-of-two anchor 2^fl in slot 0 fixes the block's
+    largest magnitude and so its E8M0 scale, the other 31 slots run through
+    all patterns no larger than the anchor.  fl spans the whole bf16 range
+    (-133 .. 127), which covers every scale code the encoder can produce."""
+    say("[mxfp8_quantize] every (value, scale) pair, 8.6M elements")
+    mag = np.arange(0x7F80, dtype=np.uint32)
+    blocks = []
+    for fl in range(-133, 128):
+        a = (fl + 127) << 7 if fl >= -126 else 1 << (fl + 133)
+        vals = mag[mag <= a]
+        vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
+        n = (len(vals) + 30) // 31
+        body = np.resize(vals, n * 31).reshape(n, 31)
+        blocks.append(np.concatenate([np.full((n, 1), a, dtype=np.uint16), body], axis=1).reshape(-1))
+    bits = np.concatenate(blocks)
+    bits = np.concatenate([bits, np.zeros((-len(bits)) % 256, dtype=np.uint16)]).reshape(-1, 256)
+    rows, K = bits.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
+    B.mk_mxfp8_quantize(dev(bits), rows, K, codes, scales, torch.cuda.current_stream())
+    sync()
+    rc, rs = mxfp8.quantize(bf16.decode(bits))
+    got_s, got_c = scales.cpu().numpy(), codes.cpu().numpy()
+    assert np.array_equal(got_s, rs)
+    bad = np.argwhere(got_c != rc)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}: bits {bits[tuple(bad[0])]:#06x} got {got_c[tuple(bad[0])]:#04x} want {rc[tuple(bad[0])]:#04x}"
+
+
 # ------------------------------------------------------------ full layer --
 def run_full_layer(inp, precision="bf16", MB=0, ring_bytes=256 << 20):
     sh = inp["shape"]
