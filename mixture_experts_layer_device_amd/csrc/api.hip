@@ -110,11 +110,6 @@ struct Phase {
 
 }  // namespace
 
-// quantise packed gate/up rows (16 gate rows, then the 16 up rows of the same i) straight to MXFP8
-namespace mk {
-void launch_quant_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s);
-}
 
 extern "C" {
 
@@ -349,8 +344,8 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, c
   if (ws->cfg.precision == MK_MXFP8) {
     if (for_backward) return MK_ERR_UNSUPPORTED;
     PackedMX p = packed_mx(ws, packed);
-    launch_quant_pack_gate_up((const uint16_t*)w_gate, (const uint16_t*)w_up, E, I, H, p.wgu_c, p.wgu_s, s);
-    launch_quantize((const uint16_t*)w_down, (int64_t)E * H, I, p.wd_c, p.wd_s, s);
+    launch_quant_tile_rows((const uint16_t*)w_gate, (const uint16_t*)w_up, 1, E, 2 * I, H, p.wgu_c, p.wgu_s, s);
+    launch_quant_tile_rows((const uint16_t*)w_down, nullptr, 0, E, H, I, p.wd_c, p.wd_s, s);
     return check_launch();
   }
   PackedBF16 p = packed_bf16(ws, packed);

@@ -39,16 +39,16 @@ __device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int row = wn * 64 + j * 16 + (lane & 15);
-    const u32x4_t lo = *(const u32x4_t*)(sB + lds_swz(row, g));
-    const u32x4_t hi = *(const u32x4_t*)(sB + lds_swz(row, g + 4));
+    const u32x4_t lo = *(const u32x4_t*)(sB + tswz(row, g));
+    const u32x4_t hi = *(const u32x4_t*)(sB + tswz(row, g + 4));
     bfr[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     sb[j] = (int)((scB[row] >> (8 * g)) & 0xFFu);
   }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int row = wm * 128 + i * 16 + (lane & 15);
-    const u32x4_t lo = *(const u32x4_t*)(sA + lds_swz(row, g));
-    const u32x4_t hi = *(const u32x4_t*)(sA + lds_swz(row, g + 4));
+    const u32x4_t lo = *(const u32x4_t*)(sA + tswz(row, g));
+    const u32x4_t hi = *(const u32x4_t*)(sA + tswz(row, g + 4));
     const i32x8_t af = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     const int sa = (int)((scA[row] >> (8 * g)) & 0xFFu);
 #pragma unroll
@@ -57,32 +57,37 @@ __device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
   }
 }
 
-// C = A . B^T over K codes; arow/brow give the code row, ascale/bscale the
-// scale row.  Codes go global -> LDS directly as in the bf16 mainloop; waves
-// 0-3 also fetch A's scale dwords (64 rows each) and waves 4-7 B's.
-template <typename ARow, typename BRow, typename ASc, typename BSc>
-__device__ __forceinline__ void mainloop(ARow arow, BRow brow, ASc ascale, BSc bscale, int K, char* lds, Acc& acc) {
+// C = A . B^T over K codes.  arow / ascale give A's code row and scale row;
+// B comes in the tiled MXFP8 layout: bcodes / bscales point at this tile's
+// K / 128 code blocks (each the LDS image of a stage's B slice) and scale
+// blocks.  Codes go global -> LDS directly as in the bf16 mainloop (A: each
+// lane fetches the granule the swizzle puts in its slot; B: 1 KiB contiguous
+// copies); waves 0-3 also fetch A's scale dwords (64 rows each) and waves
+// 4-7 B's.
+template <typename ARow, typename ASc>
+__device__ __forceinline__ void mainloop(ARow arow, ASc ascale, const uint8_t* bcodes, const uint8_t* bscales,
+                                         int K, char* lds, Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint8_t* ap[4];
-  const uint8_t* bp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = wave * 32 + j * 8 + (lane >> 3);
-    const int g = lds_unswz(r, lane & 7);
-    ap[j] = arow(r) + g * 16;
-    bp[j] = brow(r) + g * 16;
+    ap[j] = arow(r) + (((lane & 7) ^ tkey(r)) & 7) * 16;
   }
-  const uint8_t* sp = wave < 4 ? ascale(wave * 64 + lane) : bscale((wave - 4) * 64 + lane);
   const int wbase = wave * 4096;
+  const uint8_t* bp = bcodes + wbase + lane * 16;
+  const uint8_t* sp = wave < 4 ? ascale(wave * 64 + lane) : bscales + (wave - 4) * 256 + lane * 4;
+  const int sstep = wave < 4 ? 4 : MXT_SCALES;     // bytes between K steps in the scale source
   const int sbase = 2 * TILE_BYTES + wave * 256;
   auto issue = [&](int kt, char* st) {
     const int64_t kb = (int64_t)kt * BKB;
+    const uint8_t* b = bp + (int64_t)kt * MXT_CODES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       g2lds16(ap[j] + kb, st + wbase + j * 1024);
-      g2lds16(bp[j] + kb, st + TILE_BYTES + wbase + j * 1024);
+      g2lds16(b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
     }
-    g2lds4(sp + kt * 4, st + sbase);
+    g2lds4(sp + (int64_t)kt * sstep, st + sbase);
   };
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -114,10 +119,9 @@ __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uin
     auto rrow = [&](int r) { return (int64_t)((ti.pos0 + min(r, ti.rows - 1)) % ring_rows); };
     auto arow = [&](int r) { return rc + rrow(r) * H; };
     auto asc = [&](int r) { return rsc + rrow(r) * nbh; };
-    auto brow = [&](int n) { return wc + ((int64_t)ti.e * 2 * I + ti.n0 + n) * H; };
-    auto bsc = [&](int n) { return wsc + ((int64_t)ti.e * 2 * I + ti.n0 + n) * nbh; };
+    const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, 2 * I, H);
     Acc acc;
-    mainloop(arow, brow, asc, bsc, H, lds, acc);
+    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -151,10 +155,9 @@ __global__ __launch_bounds__(NT) void gemm2_mxfp8_kernel(ItemRange ir, const uin
     auto prow = [&](int r) { return (int64_t)(ti.pos0 + min(r, ti.rows - 1)); };
     auto arow = [&](int r) { return ac + prow(r) * I; };
     auto asc = [&](int r) { return asc_ + prow(r) * nbi; };
-    auto brow = [&](int n) { return wc + ((int64_t)ti.e * H + ti.n0 + n) * I; };
-    auto bsc = [&](int n) { return wsc + ((int64_t)ti.e * H + ti.n0 + n) * nbi; };
+    const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, H, I);
     Acc acc;
-    mainloop(arow, brow, asc, bsc, I, lds, acc);
+    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, I, lds, acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll

@@ -70,6 +70,8 @@ __device__ __forceinline__ int lds_unswz(int row, int s) { return (s ^ row ^ (ro
 // granule) conflict-free and, using bits 1..3 of the row only, is the same for
 // every 16-row fragment a lane reads.
 __device__ __forceinline__ int tkey(int row) { return (row >> 1) & 7; }
+// byte offset of granule g of a 128-byte LDS row swizzled with tkey
+__device__ __forceinline__ int tswz(int row, int g) { return row * 128 + (((g ^ tkey(row)) & 7) << 4); }
 constexpr int BT_ROWS = 256, BT_K = 64, BT_BLOCK = BT_ROWS * BT_K;   // elements per block
 __device__ __forceinline__ int64_t btile_block(int e, int nt, int kt, int N, int K) {
   return (((int64_t)e * (N / BT_ROWS) + nt) * (K / BT_K) + kt) * BT_BLOCK;
@@ -78,6 +80,18 @@ __device__ __forceinline__ int64_t btile_block(int e, int nt, int kt, int N, int
 __device__ __forceinline__ int64_t btile_granule(int e, int n, int k, int N, int K) {
   const int r = n % BT_ROWS, g = (k % BT_K) / 8;
   return btile_block(e, n / BT_ROWS, k / BT_K, N, K) + r * BT_K + ((g ^ tkey(r)) & 7) * 8;
+}
+
+// ---- tiled MXFP8 B operand -------------------------------------------------
+//
+// MXFP8 weights B[e][n][k] (E4M3 codes, one E8M0 scale per 32 k) are stored
+// per (e, n / 256, k / 128), in that order, as a 32 KiB block of codes (256
+// rows x 128 codes, the LDS image of one MXFP8 GEMM stage: 16-code granule g
+// of row r in slot g ^ tkey(r)) and a 1 KiB block of scales (row r's four
+// scale bytes of the K step at 4r).
+constexpr int MXT_ROWS = 256, MXT_K = 128, MXT_CODES = MXT_ROWS * MXT_K, MXT_SCALES = MXT_ROWS * 4;
+__device__ __forceinline__ int64_t mxt_index(int e, int nt, int kt, int N, int K) {
+  return ((int64_t)e * (N / MXT_ROWS) + nt) * (K / MXT_K) + kt;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;

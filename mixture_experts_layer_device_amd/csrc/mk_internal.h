@@ -76,6 +76,9 @@ void launch_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, in
                       hipStream_t s);
 void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K, uint16_t* out,
                       hipStream_t s);
+// tiled MXFP8 B operand (mxt_* layout in mk_device.h), source rows as above
+void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
+                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 
 // ---- gemm_bf16.hip -------------------------------------------------------

@@ -242,34 +242,36 @@ __global__ __launch_bounds__(256) void tile_cols_kernel(const uint16_t* __restri
   }
 }
 
-// MXFP8 codes/scales of packed gate/up row e*2I + c (the b_src_row mapping),
-// one wave per row.
-__global__ __launch_bounds__(RT) void quant_pack_gate_up_kernel(const uint16_t* __restrict__ wg,
-                                                                const uint16_t* __restrict__ wu, int64_t n_rows,
-                                                                int I, int H, uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ scales) {
+// Tiled MXFP8 B from source rows (the b_src_row mapping): one wave per row
+// (e, n), one 32-element MX block per lane step, codes and scale written to
+// their places in the tiled layout.
+__global__ __launch_bounds__(RT) void quant_tile_rows_kernel(const uint16_t* __restrict__ src_a,
+                                                             const uint16_t* __restrict__ src_b, int mode,
+                                                             int64_t n_rows, int N, int K,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
-  const int64_t nblk = H / 32;
+  const int nblk = K / 32;
   for (int64_t row = wave_id(); row < n_rows; row += wave_count()) {
-    const int e = (int)(row / (2 * I)), c = (int)(row % (2 * I));
-    const int i = (c >> 5) * 16 + (c & 15);
-    const u32x4_t* s = (const u32x4_t*)(((c & 31) < 16 ? wg : wu) + ((int64_t)e * I + i) * H);
-    u32x4_t* dc = (u32x4_t*)(codes + row * H);
-    uint8_t* ds = scales + row * nblk;
-    for (int64_t b = lane; b < nblk; b += 64) {
+    const int e = (int)(row / N), n = (int)(row % N);
+    const int r = n % MXT_ROWS;
+    const u32x4_t* s = (const u32x4_t*)b_src_row(src_a, src_b, mode, e, n, N, K);
+    for (int b = lane; b < nblk; b += 64) {
       u32x4_t v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = s[b * 4 + q];
       u32x4_t cc[2];
       const uint32_t sc = quant_block(v, cc);
-      dc[b * 2] = cc[0];
-      dc[b * 2 + 1] = cc[1];
-      ds[b] = (uint8_t)sc;
+      const int64_t t = mxt_index(e, n / MXT_ROWS, b / 4, N, K);
+      uint8_t* blk = codes + t * MXT_CODES + r * MXT_K;
+      const int g0 = (b % 4) * 2;
+      *(u32x4_t*)(blk + (((g0 ^ tkey(r)) & 7) << 4)) = cc[0];
+      *(u32x4_t*)(blk + ((((g0 + 1) ^ tkey(r)) & 7) << 4)) = cc[1];
+      scales[t * MXT_SCALES + r * 4 + (b % 4)] = (uint8_t)sc;
     }
   }
 }
 
-// out[b][c][r] = in[b][r][c], 64 x 64 tiles through LDS.
 int row_grid(int64_t rows, int n_cu) {
   const int64_t want = (rows + (RT / 64) - 1) / (RT / 64);
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)n_cu * 8));
@@ -332,11 +334,11 @@ void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, in
                      out);
 }
 
-void launch_quant_pack_gate_up(const uint16_t* wg, const uint16_t* wu, int E, int I, int H, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s) {
-  const int64_t n_rows = (int64_t)E * 2 * I;
-  hipLaunchKernelGGL(quant_pack_gate_up_kernel, dim3(row_grid(n_rows, 256)), dim3(RT), 0, s, wg, wu, n_rows, I, H,
-                     codes, scales);
+void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
+                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t n_rows = (int64_t)E * N;
+  hipLaunchKernelGGL(quant_tile_rows_kernel, dim3(row_grid(n_rows, 256)), dim3(RT), 0, s, src_a, src_b, mode, n_rows,
+                     N, K, codes, scales);
 }
 
 
