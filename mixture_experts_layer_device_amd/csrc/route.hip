@@ -9,10 +9,11 @@
 //
 // Workgroup = RT tokens x all experts, in chunks of RE experts.  x and the
 // router rows are staged through LDS per RH-wide slice of h, converted to fp32
-// and transposed once ([h][token], [h][expert]), double-buffered with the
-// next slice's global loads in registers.  Thread (tx, ty) keeps the chains of
-// tokens 2ty, 2ty+1 x experts 4tx .. 4tx+3: per h one 8-byte and one 16-byte
-// LDS read (broadcast across the lanes that share them) feed 8 FMAs.  Top-k
+// once (x as [token][h], the router rows transposed to [h][expert]), double-
+// buffered with the next slice's global loads in registers.  Thread (tx, ty)
+// keeps the chains of tokens 2ty, 2ty+1 x experts 4tx .. 4tx+3: per 8 h, four
+// 16-byte x reads and eight 16-byte router reads (broadcast across the lanes
+// that share them) feed 64 FMAs, read one group ahead.  Top-k
 // then runs one wave per token over the logits kept in LDS: k rounds of a
 // wave-wide (max logit, min id) reduction.
 #include "mk_device.h"
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
                                                     int renorm, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out) {
   extern __shared__ float zbuf[];                                  // [RT][E]
-  __shared__ __attribute__((aligned(16))) float xs[2][RH][RT];
+  __shared__ __attribute__((aligned(16))) float xs[2][RT][RH];
   __shared__ __attribute__((aligned(16))) float ws[2][RH][RE];
   const int tid = threadIdx.x;
   const int tx = tid & 31, ty = tid >> 5;
@@ -68,11 +69,16 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
           ws[buf][sh + 8 * q + 2 * d + 1][se] = bf16_to_f32(wr[q][d] >> 16);
         }
       if (tid < 128) {
+        f32x4_t lo, hi;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          xs[buf][sq + 2 * d][st_tok] = bf16_to_f32(xr[d] & 0xFFFFu);
-          xs[buf][sq + 2 * d + 1][st_tok] = bf16_to_f32(xr[d] >> 16);
+        for (int d = 0; d < 2; ++d) {
+          lo[2 * d] = bf16_to_f32(xr[d] & 0xFFFFu);
+          lo[2 * d + 1] = bf16_to_f32(xr[d] >> 16);
+          hi[2 * d] = bf16_to_f32(xr[d + 2] & 0xFFFFu);
+          hi[2 * d + 1] = bf16_to_f32(xr[d + 2] >> 16);
         }
+        *(f32x4_t*)&xs[buf][st_tok][sq] = lo;
+        *(f32x4_t*)&xs[buf][st_tok][sq + 4] = hi;
       }
     };
     float acc[2][4];
@@ -85,32 +91,34 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
       stage(buf);
       __syncthreads();
       if (h0 + RH < H) load(h0 + RH);
-      // groups of 4 h, the next group's LDS reads issued before this
-      // group's FMAs so their latency is covered
-      f32x4_t wa[4], wb[4];
-      float2 xa[4], xb[4];
-      auto rdg = [&](int h, f32x4_t (&wv)[4], float2 (&xv)[4]) {
+      // groups of 8 h, the next group's LDS reads issued before this group's
+      // FMAs so their latency is covered; per group: 8 h of each of the
+      // thread's 2 tokens (two 16-byte reads each) and 4 experts per h
+      f32x4_t wa[8], wb[8];
+      f32x4_t xa[2][2], xb[2][2];
+      auto rdg = [&](int h, f32x4_t (&wv)[8], f32x4_t (&xv)[2][2]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          wv[u] = *(const f32x4_t*)&ws[buf][h + u][4 * tx];
-          xv[u] = *(const float2*)&xs[buf][h + u][2 * ty];
-        }
+        for (int u = 0; u < 8; ++u) wv[u] = *(const f32x4_t*)&ws[buf][h + u][4 * tx];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) xv[i][q] = *(const f32x4_t*)&xs[buf][2 * ty + i][h + 4 * q];
       };
-      auto fmg = [&](const f32x4_t (&wv)[4], const float2 (&xv)[4]) {
+      auto fmg = [&](const f32x4_t (&wv)[8], const f32x4_t (&xv)[2][2]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            acc[0][j] = __builtin_fmaf(xv[u].x, wv[u][j], acc[0][j]);
-            acc[1][j] = __builtin_fmaf(xv[u].y, wv[u][j], acc[1][j]);
+            acc[0][j] = __builtin_fmaf(xv[0][u / 4][u % 4], wv[u][j], acc[0][j]);
+            acc[1][j] = __builtin_fmaf(xv[1][u / 4][u % 4], wv[u][j], acc[1][j]);
           }
       };
       rdg(0, wa, xa);
 #pragma unroll
-      for (int h = 0; h < RH; h += 8) {
-        rdg(h + 4, wb, xb);
+      for (int h = 0; h < RH; h += 16) {
+        rdg(h + 8, wb, xb);
         fmg(wa, xa);
-        if (h + 8 < RH) rdg(h + 8, wa, xa);
+        if (h + 16 < RH) rdg(h + 16, wa, xa);
         fmg(wb, xb);
       }
     }
