@@ -131,22 +131,49 @@ def main():
     def log(*m):
         print(*m, file=sys.stderr, flush=True)
 
-    def timed(step, L, steps, warmup):
+    def timed(step, L, steps, warmup, outputs=()):
+        """Warm-up, then exactly `steps` timed steps (wall clock around the
+        block, HIP events between steps for the median and the per-phase
+        events of the library).  `outputs`: tensors the step writes; their
+        bits after the timed steps are compared with a snapshot taken after
+        warm-up (bitwise repeatability)."""
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
+        snap = [t.clone() for t in outputs]
         B.mk_timing_read(L.ws)                      # drop warm-up events
         B.mk_timing_enable(L.ws, True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             step()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         B.mk_timing_enable(L.ws, False)
         ph = B.mk_timing_read(L.ws)
         per = {k: (v[0] / steps, v[1] / steps) for k, v in ph.items() if v[1] > 0}
-        return dt, per
+        step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        extra = {"step_ms_median": round(step_ms[steps // 2], 4)}
+        if outputs:
+            extra["repeatable"] = all(torch.equal(a, b) for a, b in zip(snap, outputs))
+        # cold: the 256 MB last-level cache evicted before each step by writing
+        # 512 MB elsewhere (the write is outside the timed interval)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(5):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        extra["step_ms_cold_median"] = round(sorted(cold)[2], 4)
+        return dt, per, extra
 
     def summarize(name, R, T, H, I, E, k, dt, per, steps, kind, mx=False, share=True, save_ctx=False):
         work = phase_work(kind, R, T, H, I, E, k, mx=mx, save_ctx=save_ctx, share=share)
@@ -195,8 +222,9 @@ def main():
             B.mk_build_schedule(L.ws, idx, sh.R, s)
             B.mk_forward(L.ws, B.MK_FULL_LAYER, x, wts, packed, out, None, s)
 
-        dt, per = timed(step, L, a.steps, a.warmup)
+        dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=(out, idx, wts))
         main = summarize("full", sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False)
+        main.update(extra)
         main["err"] = L.device_error()
         L.close()
         del packed
@@ -221,9 +249,10 @@ def main():
                 B.mk_build_schedule(L.ws, re, sh.R, s)
                 B.mk_forward(L.ws, B.MK_EXPERT_SHARE, x, rw, packed, out, None, s)
 
-            dt, per = timed(step, L, a.steps, a.warmup)
+            dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=(out,))
             results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "forward",
                                      mx=prec == "mxfp8")
+            results[key].update(extra)
             results[key]["err"] = L.device_error()
             L.close()
             del packed
@@ -252,8 +281,9 @@ def main():
             B.mk_backward(L.ws, B.MK_EXPERT_SHARE, ctx, x, rw, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
                           g["dW_down"], g["d_row_w"], s)
 
-        dt, per = timed(step, L, a.steps, a.warmup)
+        dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
         results["ep_bwd"] = summarize("ep_bwd", sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "backward")
+        results["ep_bwd"].update(extra)
         results["ep_bwd"]["err"] = L.device_error()
         L.close()
         log(json.dumps(results["ep_bwd"]))
@@ -291,6 +321,7 @@ def main():
                                "renormalised softmax router with per-expert logit bias",
                    "tokens": 4096, "routed_rows": 32768, "H": 2048, "I": 768, "E": 128, "k": 8},
         "gemm_tflops": main["gemm_tflops"],
+        "protocol": {k: main.get(k) for k in ("step_ms_median", "step_ms_cold_median", "repeatable")},
         "roofline": roof,
         "cpu_baseline": cpu,
         "phases": main["phases"],
