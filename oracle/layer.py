@@ -8,6 +8,10 @@ expert outputs are combined back to token order weighted by the router
 weights.  The backward computes dX and all weight gradients, and the gradient
 of the router weight inside the SwiGLU backward (the SonicMoE-style
 calculation the pages name).  No token is dropped ([MTP] "Key Takeaways").
+The full-layer backward also carries the gradient through the router (the
+pages take routing as an input, so this part is the plain chain rule through
+the softmax top-k router that the route module states: softmax Jacobian,
+then the linear logit map).
 
 Notation (weights stored one row per output feature, see ``workloads``):
     g = x W_g[e]^T,  u = x W_u[e]^T,  a = silu(g) * u,  y = a W_d[e]^T
@@ -149,24 +153,21 @@ def forward_share_mxfp8(inp, qw=None):
     return {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "y": y, "out": bf16.round_rne(out), "out_exact": out}
 
 
-def backward_share(inp, bf16_mode: bool = True):
-    """Expert share backward, loss L = sum_r <dY[r], out_rows[r]>.
+def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool):
+    """Expert backward of routed rows (arrival order), loss
+    L = sum_r <dY[r], w[r] y(r)>:
 
     dA' = dY W_d[e]            (gradient w.r.t. a, before the router weight)
     dw[r] = <dA'[r], a[r]>     (= <dY[r], y[r]>: router-weight gradient)
     dA  = w * dA'
     dg  = dA * u * s * (1 + g (1 - s)),  s = sigmoid(g)
     du  = dA * silu(g)
-    dX  = dg W_g[e] + du W_u[e]
+    dX_rows = dg W_g[e] + du W_u[e]          (not rounded here)
     dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = dY_e^T (w a)_e
-    In bf16 mode dg, du, w*a and dX are bf16 tensors (GEMM operands / output);
-    g, u, a, dA' and the fp32 outputs dW, dw are exact.
+    In bf16 mode dg, du and w*a are bf16 tensors (GEMM operands); g, u, a,
+    dA' and the fp32 outputs dW, dw are exact.  Rows whose expert id is out
+    of range get zeros.
     """
-    x = bf16.decode(inp["x"])
-    wg, wu, wd = _weights(inp)
-    re = inp["row_expert"]
-    w = inp["row_w"].astype(np.float64)
-    dY = bf16.decode(inp["dY"])
     R, H = x.shape
     E, I, _ = wg.shape
     dX = np.zeros((R, H)); dw = np.zeros(R); dw_alt = np.zeros(R)
@@ -185,12 +186,92 @@ def backward_share(inp, bf16_mode: bool = True):
         s = sigmoid(g)
         dg = rnd(dA * u * s * (1.0 + g * (1.0 - s)), bf16_mode)
         du = rnd(dA * silu(g), bf16_mode)
-        dX[sel] = rnd(dg @ wg[e] + du @ wu[e], bf16_mode)
+        dX[sel] = dg @ wg[e] + du @ wu[e]
         dWg[e] = dg.T @ xe
         dWu[e] = du.T @ xe
         dWd[e] = dYe.T @ rnd(w[sel, None] * a, bf16_mode)
-    return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd,
+    return {"dX_rows": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd,
             "d_row_w": dw, "d_row_w_alt": dw_alt}
+
+
+def backward_share(inp, bf16_mode: bool = True):
+    """Expert share backward (rows in arrival order), see ``_backward_rows``;
+    dX is each row's dX_rows, a bf16 tensor in bf16 mode."""
+    wg, wu, wd = _weights(inp)
+    g = _backward_rows(bf16.decode(inp["x"]), inp["row_expert"], inp["row_w"].astype(np.float64),
+                       bf16.decode(inp["dY"]), wg, wu, wd, bf16_mode)
+    g["dX"] = rnd(g.pop("dX_rows"), bf16_mode)
+    return g
+
+
+def router_logit_grad(z, idx, d_w, renorm: int):
+    """Gradient of the loss w.r.t. the router logits z [T, E], given its
+    gradient d_w [T, k] w.r.t. the router weights of the chosen experts idx.
+
+    The choice itself is piecewise constant in z (no gradient).  With
+    renorm=1 the weights are the softmax q of the chosen logits, so the chosen
+    logits get J_q^T d_w with the softmax Jacobian J_q = diag(q) - q q^T and
+    the others get 0; with renorm=0 they are the full softmax p read at the
+    chosen experts, so with g = d_w scattered into an E-vector (0 elsewhere),
+    dz = (diag(p) - p p^T) g.  Both written out as matrices, fp64.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    T, E = z.shape
+    dz = np.zeros((T, E))
+    for t in range(T):
+        sel = idx[t].astype(np.int64)
+        if renorm:
+            ex = np.exp(z[t, sel] - z[t, sel].max())
+            q = ex / ex.sum()
+            J = np.diag(q) - np.outer(q, q)
+            dz[t, sel] = J.T @ d_w[t]
+        else:
+            ex = np.exp(z[t] - z[t].max())
+            p = ex / ex.sum()
+            gfull = np.zeros(E)
+            gfull[sel] = d_w[t]
+            J = np.diag(p) - np.outer(p, p)
+            dz[t] = J.T @ gfull
+    return dz
+
+
+def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router: bool = True):
+    """Full-layer backward, loss L = sum_t <dY[t], out[t]>.
+
+    Routing (indices, weights, logits) is recomputed as in the forward.  Row
+    r = t*k + j carries token t to its j-th expert with dY_rows[r] = dY[t];
+    the expert part is ``_backward_rows`` on these rows, and
+        d_topk_w[t, j] = dw[t*k + j]
+        dX[t] = sum_j dX_rows[t*k + j]            (j ascending)
+    With ``router`` the gradient also flows through the router:
+        dz = router_logit_grad(z, idx, d_topk_w)  [T, E]
+        dW_router = dz^T x  [E, H],  d_bias = sum_t dz[t]
+        dX[t] += dz[t] W_router
+    In bf16 mode dX (after both sums) is one bf16 tensor; dz, dW_router and
+    d_bias are exact.
+    """
+    sh = inp["shape"]
+    rn = sh.renorm if renorm is None else renorm
+    k = sh.k
+    x = bf16.decode(inp["x"])
+    wr = bf16.decode(inp["w_router"])
+    idx, w, z = _route(x.astype(np.float32), wr.astype(np.float32), inp["bias"], k, rn)
+    wg, wu, wd = _weights(inp)
+    T, H = x.shape
+    g = _backward_rows(np.repeat(x, k, axis=0), idx.reshape(-1), w.reshape(-1).astype(np.float64),
+                       np.repeat(bf16.decode(inp["dY"]), k, axis=0), wg, wu, wd, bf16_mode)
+    d_topk_w = g["d_row_w"].reshape(T, k)
+    dXr = g.pop("dX_rows").reshape(T, k, H)
+    dX = np.zeros((T, H))
+    for j in range(k):                                   # fixed ascending order
+        dX += dXr[:, j]
+    out = dict(g, topk_idx=idx, topk_w=w, logits=z, d_topk_w=d_topk_w)
+    if router:
+        dz = router_logit_grad(z, idx, d_topk_w, rn)
+        dX += dz @ wr
+        out.update(dz=dz, dW_router=dz.T @ x, d_bias=dz.sum(axis=0))
+    out["dX"] = rnd(dX, bf16_mode)
+    return out
 
 
 def forward_share_rows(inp, rows):
