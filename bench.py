@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="run one workload only (full, ep64_fwd, ep64_mxfp8, ep_bwd)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, full_bwd)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) 3 times: the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -64,11 +65,18 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True):
         if not share:
             w["combine"] = (0.0, R * H * 4 + T * H * 2 + R * 8)
     else:
-        w["bwd_gather"] = (0.0, 2.0 * R * H * 2)
+        # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
+        w["bwd_gather"] = (0.0, (R if share else T) * H * 2 + R * H * 2)
         w["bwd_dact"] = (2.0 * R * H * I, R * H * 2 + E * I * H * 2 + R * 2 * I * 4 + R * 2 * I * 2 + R * I * 2)
-        w["bwd_dx"] = (4.0 * R * I * H, R * 2 * I * 2 + E * H * 2 * I * 2 + R * H * 2)
+        # share: bf16 rows to arrival order; full layer: fp32 rows for the k-sum
+        w["bwd_dx"] = (4.0 * R * I * H, R * 2 * I * 2 + E * H * 2 * I * 2 + R * H * (2 if share else 4))
         w["wgrad_down"] = (2.0 * R * H * I, R * H * 2 + R * I * 2 + E * H * I * 4)
         w["wgrad_gate_up"] = (4.0 * R * H * I, R * 2 * I * 2 + R * H * 2 + E * 2 * I * H * 4)
+        if not share:
+            # k-sum of fp32 rows + router term (k rows of W_r per token, L2-resident)
+            w["bwd_combine"] = (2.0 * R * H, R * H * 4 + T * H * 2 + R * 4 + T * E * 4 + E * H * 2)
+            # logit gradient + dW_router = dz^T x (k nonzeros per token) + d_bias
+            w["router_bwd"] = (2.0 * R * H, T * k * 12 + T * E * 4 * 2 + T * H * 2 + E * H * 4)
     return w
 
 
@@ -185,7 +193,7 @@ def main():
             if f or b:
                 ent["roofline"] = roofline(f, b, ms, mx=mx and p.startswith("gemm"))
             phases[p] = ent
-            if f and p != "route":
+            if f and p not in ("route", "bwd_combine", "router_bwd"):
                 gemm_flops += f
                 gemm_ms += ms
         ms_step = dt / steps * 1e3
@@ -198,7 +206,7 @@ def main():
         }
 
     results = {}
-    want = set(a.only.split(",")) if a.only else {"full", "ep64_fwd", "ep64_mxfp8", "ep_bwd"}
+    want = set(a.only.split(",")) if a.only else {"full", "ep64_fwd", "ep64_mxfp8", "ep_bwd", "full_bwd"}
     if a.no_breakdown:
         want = {"full"}
 
@@ -287,6 +295,40 @@ def main():
         results["ep_bwd"]["err"] = L.device_error()
         L.close()
         log(json.dumps(results["ep_bwd"]))
+
+    if "full_bwd" in want:
+        inp = workloads.make_full_layer("full")
+        sh = inp["shape"]
+        log(f"[bench] full layer backward incl. router bf16: T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k}")
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, enable_backward=True)
+        x = up(inp["x"]); wr = up(inp["w_router"]); bias = up(inp["bias"]); dY = up(inp["dY"])
+        packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]), for_backward=True)
+        out = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
+        ctx = L.new_fwd_ctx()
+        s = torch.cuda.current_stream()
+        idx, wts = L.route(x, wr, bias, sh.T)                                 # forward, untimed
+        B.mk_build_schedule(L.ws, idx, sh.R, s)
+        B.mk_forward(L.ws, B.MK_FULL_LAYER, x, wts, packed, out, ctx, s)
+        g = {"dX": torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda"),
+             "dW_gate": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
+             "dW_up": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
+             "dW_down": torch.empty((sh.E, sh.H, sh.I), dtype=torch.float32, device="cuda"),
+             "dW_router": torch.empty((sh.E, sh.H), dtype=torch.float32, device="cuda"),
+             "d_bias": torch.empty((sh.E,), dtype=torch.float32, device="cuda"),
+             "d_topk_w": torch.empty((sh.R,), dtype=torch.float32, device="cuda")}
+
+        def step():
+            B.mk_backward_layer(L.ws, ctx, x, wr, bias, idx, wts, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
+                                g["dW_down"], g["dW_router"], g["d_bias"], g["d_topk_w"], s)
+
+        dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
+        results["full_bwd"] = summarize("full_bwd", sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps,
+                                        "backward", share=False)
+        results["full_bwd"].update(extra)
+        results["full_bwd"]["err"] = L.device_error()
+        L.close()
+        del packed
+        log(json.dumps(results["full_bwd"]))
 
     if a.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

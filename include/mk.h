@@ -176,8 +176,10 @@ int mk_mxfp8_quantize(const void* in_dev, int64_t rows, int32_t K, uint8_t* code
  * with for_backward = 1 also the transposed copies the backward GEMMs read.
  * bf16 mode stores each of them as 32 KiB blocks of 256 rows x 64 K in the
  * order (expert, row block, K block), every block laid out as the GEMM keeps
- * it in LDS; MXFP8 mode as row-major E4M3 codes + E8M0 scales along each
- * GEMM's K.  The layout is internal: only this library reads the buffer.
+ * it in LDS; MXFP8 mode quantises along each GEMM's K and stores, per
+ * (expert, 256-row block, 128-K block), a 32 KiB block of E4M3 codes in the
+ * same LDS-image form and a 1 KiB block of the rows' E8M0 scales.  The layout
+ * is internal: only this library reads the buffer.
  */
 int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_up_dev,
                        const void* w_down_dev, int32_t for_backward, void* packed_dev,
@@ -202,23 +204,54 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const floa
                const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
 
 /*
- * Backward, expert-share mode, bf16 ([MTP]: the ring is walked in reverse to
- * minimise forward-activation replay; the router-weight gradient is fused into
- * the SwiGLU backward).  Loss gradient dY_dev [R, H] bf16 in arrival order.
- *   dX_dev      [R, H] bf16 (arrival order)
+ * Backward, bf16 ([MTP]: the ring is walked in reverse to minimise
+ * forward-activation replay; the router-weight gradient is fused into the
+ * SwiGLU backward), for the loss L = <dY, out> of mk_forward.
+ *   mode MK_EXPERT_SHARE: x_src_dev [R, H], row_w_dev [R], dY_dev [R, H] and
+ *       dX_dev [R, H] in arrival order; d_row_w_dev [R] fp32.
+ *   mode MK_FULL_LAYER: x_src_dev [T, H], row_w_dev = topk_w [T*k],
+ *       dY_dev [T, H], dX_dev [T, H] = sum over j ascending of the k routed
+ *       rows' input gradients in fp32, rounded once; d_row_w_dev [T*k] =
+ *       gradient w.r.t. topk_w.  The router is taken as external (its inputs
+ *       topk_idx/topk_w are leaves); mk_backward_layer also differentiates it.
  *   dW_gate_dev [E, I, H] fp32, dW_up_dev [E, I, H] fp32, dW_down_dev [E, H, I] fp32
- *   d_row_w_dev [R] fp32
  * Weight gradients are reduced in a fixed order (minibatches in reverse walk
  * order, rows ascending inside each) with no float atomics: bitwise repeatable
  * at a fixed minibatch size.  Must follow the mk_forward (with fwd_ctx) of the
- * same rows on this workspace with no other forward in between; packed_dev must
- * have been prepared with for_backward = 1.  MK_ERR_UNSUPPORTED for full-layer
- * mode or MXFP8; MK_ERR_CONFIG if the workspace has no backward buffers.
+ * same rows and mode on this workspace with no other forward in between;
+ * packed_dev must have been prepared with for_backward = 1.  MK_ERR_UNSUPPORTED
+ * for MXFP8; MK_ERR_CONFIG if the workspace has no backward buffers;
+ * MK_ERR_SHAPE in full-layer mode unless R and MB are multiples of k.
  */
 int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const void* x_src_dev,
                 const float* row_w_dev, const void* packed_dev, const void* dY_dev,
                 void* dX_dev, float* dW_gate_dev, float* dW_up_dev, float* dW_down_dev,
                 float* d_row_w_dev, void* stream);
+
+/*
+ * Full-layer backward including the router (gradient through the softmax
+ * top-k router that mk_route computes; the pages take routing as an input,
+ * so this is the plain chain rule through that router).  The expert choice is
+ * piecewise constant and carries no gradient; with d_topk_w the gradient
+ * w.r.t. the top-k weights, the logit gradient dz [T, E] is the softmax
+ * Jacobian applied to it: cfg.renorm = 1: dz[t, idx_j] = w_j (d_w_j - S),
+ * other experts 0, S = sum_j w_j d_w_j; cfg.renorm = 0: dz[t, e] = p_e (g_e - S)
+ * over all E, p the full softmax (recomputed from x, w_router and bias), g_e =
+ * d_w_j where e = idx_j, else 0.  Then
+ *   dW_router_dev [E, H] fp32 = dz^T x     d_bias_dev [E] fp32 = sum_t dz (NULL: skipped)
+ *   dX_dev [T, H] bf16 = sum_j (routed rows' input gradients, j ascending)
+ *                        + sum_e dz[t, e] w_router[e] (e ascending), fp32, one rounding
+ *   d_topk_w_dev [T*k] fp32, dW_gate/up/down as mk_backward.
+ * x_dev, w_router_dev, bias_dev (NULL if the router has none), topk_idx_dev and
+ * topk_w_dev are the ones mk_route and mk_forward saw; the schedule must be the
+ * one built from topk_idx.  Every sum runs in a fixed order: bitwise
+ * repeatable.  Errors as mk_backward.
+ */
+int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx_dev, const void* x_dev,
+                      const void* w_router_dev, const float* bias_dev, const int32_t* topk_idx_dev,
+                      const float* topk_w_dev, const void* packed_dev, const void* dY_dev,
+                      void* dX_dev, float* dW_gate_dev, float* dW_up_dev, float* dW_down_dev,
+                      float* dW_router_dev, float* d_bias_dev, float* d_topk_w_dev, void* stream);
 
 /*
  * Per-phase timing (for benchmarks): with timing on, every launch sequence
@@ -241,7 +274,9 @@ int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const v
 #define MK_PH_BWD_DX     10
 #define MK_PH_WGRAD_DOWN 11
 #define MK_PH_WGRAD_GU   12
-#define MK_PH_COUNT      13
+#define MK_PH_BWD_COMBINE 13  /* full layer: k-sum of dX rows (+ router term) */
+#define MK_PH_ROUTER_BWD 14   /* router backward: logit gradient, dW_router, d_bias */
+#define MK_PH_COUNT      15
 int mk_timing_enable(mk_workspace* ws, int32_t on);
 int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
 

@@ -70,6 +70,7 @@ _SIGS = {
     "mk_prepare_weights": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "mk_forward": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mk_backward": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mk_backward_layer": (ctypes.c_int, [_vp] * 17),
     "mk_device_error": (ctypes.c_int, [_vp, _vp, _vp]),
     "mk_timing_enable": (ctypes.c_int, [_vp, _i32]),
     "mk_timing_read": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_i32)]),
@@ -170,6 +171,14 @@ def mk_backward(ws, mode, fwd_ctx, x_src, row_w, packed, dY, dX, dW_gate, dW_up,
                                           _p(dW_gate), _p(dW_up), _p(dW_down), _p(d_row_w), _s(stream)))
 
 
+def mk_backward_layer(ws, fwd_ctx, x, w_router, bias, topk_idx, topk_w, packed, dY, dX, dW_gate, dW_up, dW_down,
+                      dW_router, d_bias, d_topk_w, stream=None):
+    _check("mk_backward_layer", lib.mk_backward_layer(ws, _p(fwd_ctx), _p(x), _p(w_router), _p(bias), _p(topk_idx),
+                                                      _p(topk_w), _p(packed), _p(dY), _p(dX), _p(dW_gate),
+                                                      _p(dW_up), _p(dW_down), _p(dW_router), _p(d_bias),
+                                                      _p(d_topk_w), _s(stream)))
+
+
 def mk_device_error(ws, dst, stream=None):
     _check("mk_device_error", lib.mk_device_error(ws, _p(dst), _s(stream)))
 
@@ -179,7 +188,7 @@ def mk_timing_enable(ws, on: bool) -> None:
 
 
 PHASES = ["route", "schedule", "permute", "gemm1", "quant_a", "gemm2", "combine", "bwd_gather", "bwd_dact",
-          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up"]
+          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd"]
 
 
 def mk_timing_read(ws) -> dict:

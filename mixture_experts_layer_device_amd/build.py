@@ -18,7 +18,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmk.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "schedule.hip", "route.hip", "rows.hip", "gemm_bf16.hip", "gemm_mxfp8.hip"]
+SOURCES = ["api.hip", "schedule.hip", "route.hip", "rows.hip", "router_bwd.hip", "gemm_bf16.hip", "gemm_mxfp8.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

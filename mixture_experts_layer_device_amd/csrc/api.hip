@@ -108,6 +108,99 @@ struct Phase {
   }
 };
 
+// Router inputs/outputs of the full-layer backward with the router backward.
+struct RouterGrad {
+  const uint16_t* w_router;   // [E, H] bf16
+  const float* bias;          // [E] or null
+  const int32_t* topk_idx;    // [T, k]
+  float* dW_router;           // [E, H]
+  float* d_bias;              // [E] or null
+};
+
+// The backward of both modes.  Expert share: rows in arrival order, dX rows
+// straight from the dX GEMM.  Full layer: row r = t*k + j is token t's j-th
+// routed row; the dX GEMM keeps its rows in fp32 (reusing the forward's y
+// buffer, dead by now) and a combine sums each token's k rows in slot order,
+// adds the router term when rg is given, and rounds once.
+int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const void* x_src, const float* row_w,
+                  const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up, float* dW_down,
+                  float* d_row_w, const RouterGrad* rg, void* stream) {
+  if (!ws) return MK_ERR_NULL;
+  if (!ws->have_sched) return MK_ERR_STATE;
+  if (mode != MK_EXPERT_SHARE && mode != MK_FULL_LAYER) return MK_ERR_CONFIG;
+  if (ws->cfg.precision != MK_BF16) return MK_ERR_UNSUPPORTED;
+  if (!ws->cfg.enable_backward) return MK_ERR_CONFIG;
+  if (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !dW_gate || !dW_up || !dW_down || !d_row_w)
+    return MK_ERR_NULL;
+  const bool full = mode == MK_FULL_LAYER;
+  const int H = ws->H, I = ws->I, MB = ws->MB, R = ws->R, nb = ws->nb, k = ws->k, E = ws->E;
+  if (full && (R % k || MB % k)) return MK_ERR_SHAPE;
+  const int src_div = full ? k : 1;
+  const int T = R / src_div;
+  hipStream_t s = as_stream(stream);
+  PackedBF16 p = packed_bf16(ws, (void*)packed);
+  const ItemRange all = item_range(ws, 0, nb);
+  // pull the loss gradient into expert order (share of the reverse combine)
+  {
+    Phase ph(ws, MK_PH_BWD_GATHER, s);
+    launch_gather_rows((const uint16_t*)dY, H, ws->inv, src_div, 0, (int64_t)nb * MB, 0, ws->dye, ws->n_cu, s);
+  }
+  // dA' GEMM with the SwiGLU backward and router-weight gradient fused
+  {
+    Phase ph(ws, MK_PH_BWD_DACT, s);
+    launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, ws->inv, row_w, ws->dgdu, ws->wa, ws->dw_part,
+                    ws->n_cu, s);
+  }
+  {
+    Phase ph(ws, MK_PH_BWD_DW, s);
+    launch_dw_finalize(ws->dw_part, I / 64, ws->sorted_pos, R, d_row_w, full ? nullptr : (uint16_t*)dX, H, s);
+  }
+  // dX GEMM: expert share stores rows back to arrival order (share of the
+  // reverse dispatch); the full layer keeps fp32 rows for the k-sum
+  {
+    Phase ph(ws, MK_PH_BWD_DX, s);
+    launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, ws->inv, full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
+  }
+  if (full) {
+    if (rg) {
+      Phase ph(ws, MK_PH_ROUTER_BWD, s);
+      if (!ws->cfg.renorm)
+        launch_route_logits((const uint16_t*)x_src, rg->w_router, rg->bias, T, H, E, ws->dz, s);
+      launch_router_dz(d_row_w, row_w, rg->topk_idx, T, E, k, ws->cfg.renorm, ws->dz, s);
+    }
+    {
+      Phase ph(ws, MK_PH_BWD_COMBINE, s);
+      launch_dx_combine(ws->y_buf, H, ws->sorted_pos, k, T, rg ? ws->dz : nullptr, rg ? rg->w_router : nullptr, E,
+                        (uint16_t*)dX, ws->n_cu, s);
+    }
+    if (rg) {
+      Phase ph(ws, MK_PH_ROUTER_BWD, s);
+      const int ns = router_wgrad_splits(T, E, H, ws->rsplits_max);
+      launch_router_wgrad(ws->dz, (const uint16_t*)x_src, T, H, E, ns, ws->rpart, rg->dW_router, rg->d_bias, s);
+    }
+  }
+  // weight gradients: row segments in reverse walk order; minibatches still in
+  // the ring are read there, the evicted ones are replayed from x_src
+  WgradArgs wa;
+  wa.E = E;
+  wa.nb = nb;
+  wa.MB = MB;
+  wa.mb_counts = ws->mb_counts;
+  wa.mb_offsets = ws->mb_offsets;
+  wa.inv = ws->inv;
+  wa.src_div = src_div;
+  const int ring_mbs = ws->ring_rows / MB;
+  const int first_resident = std::max(0, nb - ring_mbs);
+  {
+    Phase ph(ws, MK_PH_WGRAD_DOWN, s);
+    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->n_cu, s);
+  }
+  Phase ph(ws, MK_PH_WGRAD_GU, s);
+  launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, first_resident,
+                       (const uint16_t*)x_src, H, I, dW_gate, dW_up, ws->n_cu, s);
+  return check_launch();
+}
+
 }  // namespace
 
 
@@ -199,12 +292,18 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     o_as = c.take((size_t)npos * I / 32);
   }
   const size_t o_y = c.take((size_t)npos * H * 4);
-  size_t o_dye = 0, o_dgdu = 0, o_wa = 0, o_dwp = 0;
+  size_t o_dye = 0, o_dgdu = 0, o_wa = 0, o_dwp = 0, o_dz = 0, o_rp = 0;
   if (cfg->enable_backward) {
     o_dye = c.take((size_t)npos * H * 2);
     o_dgdu = c.take((size_t)npos * 2 * I * 2);
     o_wa = c.take((size_t)npos * I * 2);
     o_dwp = c.take((size_t)npos * (I / 64) * 4);
+    o_dz = c.take((size_t)((max_rows + k - 1) / k) * E * 4);
+    // token splits of the router weight gradient: ~256 tokens each, partials
+    // capped at 64 MiB
+    const int64_t per_split = (int64_t)E * (H + 1) * 4;
+    ws->rsplits_max = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ((int64_t)64 << 20) / per_split));
+    o_rp = c.take((size_t)ws->rsplits_max * per_split);
   }
   ws->bytes = c.off;
   if (hipMalloc(&ws->base, ws->bytes) != hipSuccess) {
@@ -236,6 +335,8 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     ws->dgdu = (uint16_t*)(b + o_dgdu);
     ws->wa = (uint16_t*)(b + o_wa);
     ws->dw_part = (float*)(b + o_dwp);
+    ws->dz = (float*)(b + o_dz);
+    ws->rpart = (float*)(b + o_rp);
   }
   // error word starts clear
   launch_fill_u32(ws->err, 0u, 1, nullptr);
@@ -434,56 +535,19 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
 int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const void* x_src, const float* row_w,
                 const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up, float* dW_down,
                 float* d_row_w, void* stream) {
+  return backward_impl(ws, mode, fwd_ctx, x_src, row_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_row_w, nullptr,
+                       stream);
+}
+
+int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx, const void* x, const void* w_router, const float* bias,
+                      const int32_t* topk_idx, const float* topk_w, const void* packed, const void* dY, void* dX,
+                      float* dW_gate, float* dW_up, float* dW_down, float* dW_router, float* d_bias,
+                      float* d_topk_w, void* stream) {
   if (!ws) return MK_ERR_NULL;
-  if (!ws->have_sched) return MK_ERR_STATE;
-  if (mode != MK_EXPERT_SHARE || ws->cfg.precision != MK_BF16) return MK_ERR_UNSUPPORTED;
-  if (!ws->cfg.enable_backward) return MK_ERR_CONFIG;
-  if (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !dW_gate || !dW_up || !dW_down || !d_row_w)
-    return MK_ERR_NULL;
-  hipStream_t s = as_stream(stream);
-  const int H = ws->H, I = ws->I, MB = ws->MB, R = ws->R, nb = ws->nb;
-  PackedBF16 p = packed_bf16(ws, (void*)packed);
-  const ItemRange all = item_range(ws, 0, nb);
-  // pull the loss gradient into expert order (share of the reverse combine)
-  {
-    Phase ph(ws, MK_PH_BWD_GATHER, s);
-    launch_gather_rows((const uint16_t*)dY, H, ws->inv, 1, 0, (int64_t)nb * MB, 0, ws->dye, ws->n_cu, s);
-  }
-  // dA' GEMM with the SwiGLU backward and router-weight gradient fused
-  {
-    Phase ph(ws, MK_PH_BWD_DACT, s);
-    launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, ws->inv, row_w, ws->dgdu, ws->wa, ws->dw_part,
-                    ws->n_cu, s);
-  }
-  {
-    Phase ph(ws, MK_PH_BWD_DW, s);
-    launch_dw_finalize(ws->dw_part, I / 64, ws->sorted_pos, R, d_row_w, (uint16_t*)dX, H, s);
-  }
-  // dX GEMM, rows written back to arrival order (share of the reverse dispatch)
-  {
-    Phase ph(ws, MK_PH_BWD_DX, s);
-    launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, ws->inv, (uint16_t*)dX, ws->n_cu, s);
-  }
-  // weight gradients: row segments in reverse walk order; minibatches still in
-  // the ring are read there, the evicted ones are replayed from x_src
-  WgradArgs wa;
-  wa.E = ws->E;
-  wa.nb = nb;
-  wa.MB = MB;
-  wa.mb_counts = ws->mb_counts;
-  wa.mb_offsets = ws->mb_offsets;
-  wa.inv = ws->inv;
-  wa.src_div = 1;
-  const int ring_mbs = ws->ring_rows / MB;
-  const int first_resident = std::max(0, nb - ring_mbs);
-  {
-    Phase ph(ws, MK_PH_WGRAD_DOWN, s);
-    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->n_cu, s);
-  }
-  Phase ph(ws, MK_PH_WGRAD_GU, s);
-  launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, first_resident,
-                       (const uint16_t*)x_src, H, I, dW_gate, dW_up, ws->n_cu, s);
-  return check_launch();
+  if (!w_router || !topk_idx || !dW_router) return MK_ERR_NULL;
+  RouterGrad rg{(const uint16_t*)w_router, bias, topk_idx, dW_router, d_bias};
+  return backward_impl(ws, MK_FULL_LAYER, fwd_ctx, x, topk_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_topk_w, &rg,
+                       stream);
 }
 
 int mk_timing_enable(mk_workspace* ws, int32_t on) {

@@ -255,11 +255,14 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
 }
 
 // ------------------------------------------------------ backward: dX ----
-// dX[inv[p]] = dgdu[p] . W_gu[e]  (B = packed W_gu^T, tiled [E, H, 2I]); rows
-// are stored straight back to arrival order.
+// dX_row[p] = dgdu[p] . W_gu[e]  (B = packed W_gu^T, tiled [E, H, 2I]).
+// ROWS16: rows stored as bf16 straight back to arrival order, dX[inv[p]];
+// else : kept in fp32 at position p ([p, H]) for the full layer's k-sum.
+template <bool ROWS16>
 __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t* __restrict__ dgdu,
                                                     const uint16_t* __restrict__ wguT, int H, int I,
-                                                    const int32_t* __restrict__ inv, uint16_t* __restrict__ dX) {
+                                                    const int32_t* __restrict__ inv, uint16_t* __restrict__ dX,
+                                                    float* __restrict__ dx32) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = H / BN;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
@@ -269,12 +272,21 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 4; ++v) {
+        const int r = frag_row(i, v);
+        if (ROWS16) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) stage_put(lds, frag_row(i, v), frag_col(j), acc[i][j][v]);
-    stage_flush<256>(lds, [&](int r) -> uint16_t* {
-      return r < ti.rows ? dX + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
-    });
+          for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), acc[i][j][v]);
+        } else if (r < ti.rows) {
+          float* dst = dx32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
+        }
+      }
+    if (ROWS16)
+      stage_flush<256>(lds, [&](int r) -> uint16_t* {
+        return r < ti.rows ? dX + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
+      });
   });
 }
 
@@ -438,8 +450,11 @@ void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* w
 }
 
 void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wguT, int H, int I,
-                   const int32_t* inv, uint16_t* dX, int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX);
+                   const int32_t* inv, uint16_t* dX, float* dx32, int n_cu, hipStream_t s) {
+  if (dX)
+    hipLaunchKernelGGL(bwd_dx_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
+  else
+    hipLaunchKernelGGL(bwd_dx_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
 }
 
 void launch_wgrad_down(const WgradArgs& w, const uint16_t* dye, const uint16_t* wa, int H, int I,

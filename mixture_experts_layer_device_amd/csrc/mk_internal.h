@@ -38,6 +38,9 @@ struct mk_workspace {
   float* y_buf;               // [npos, H] fp32 expert outputs, expert order (full-layer combine)
   uint16_t *dye, *dgdu, *wa;  // backward: [npos, H], [npos, 2I], [npos, I]
   float* dw_part;             // [npos, I/64]
+  float* dz;                  // [ceil(max_rows / k), E]: router logit gradient (and logits)
+  float* rpart;               // [rsplits_max, E, H + 1]: router weight-gradient partials
+  int32_t rsplits_max;
   // optional per-phase timing
   int timing;
   std::vector<mk_phase_event>* events;
@@ -51,6 +54,24 @@ void launch_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, hip
 // ---- route.hip -----------------------------------------------------------
 void launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H,
                   int E, int k, int renorm, int32_t* idx, float* w, hipStream_t s);
+// the router logits alone, z [T, E] fp32, bit-identical to launch_route's
+void launch_route_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H,
+                         int E, float* z, hipStream_t s);
+
+// ---- router_bwd.hip ------------------------------------------------------
+// dz [T, E] = gradient w.r.t. the logits from d_w = gradient w.r.t. the top-k
+// weights (renorm 0: dz holds the logits on entry and is overwritten)
+void launch_router_dz(const float* d_w, const float* w, const int32_t* idx, int T, int E, int k, int renorm,
+                      float* dz, hipStream_t s);
+// dX[t] = bf16(sum_j dx32[sorted_pos[t*k + j]] + sum_e dz[t, e] w_router[e]); dz may be null
+void launch_dx_combine(const float* dx32, int64_t H, const int32_t* sorted_pos, int k, int64_t T,
+                       const float* dz, const uint16_t* w_router, int E, uint16_t* dX, int n_cu,
+                       hipStream_t s);
+// dW_router [E, H] = dz^T x, d_bias [E] = sum_t dz (d_bias may be null), over NS
+// token splits; part holds NS * E * (H + 1) floats
+int router_wgrad_splits(int T, int E, int H, int max_splits);
+void launch_router_wgrad(const float* dz, const uint16_t* x, int T, int H, int E, int NS, float* part,
+                         float* dW_router, float* d_bias, hipStream_t s);
 
 // ---- rows.hip ------------------------------------------------------------
 // dst row (p mod ring_rows, or p if ring_rows == 0) <- src row src_of(inv[p]),
@@ -67,6 +88,7 @@ void launch_combine(const float* y, int64_t H, const int32_t* sorted_pos, const 
 void launch_zero_dropped_rows(const int32_t* sorted_pos, int64_t R, uint16_t* out, int64_t H, hipStream_t s);
 void launch_quantize(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
                      hipStream_t s);
+// dX (arrival-order rows, may be null) gets zero rows where a row was dropped
 void launch_dw_finalize(const float* dw_part, int slices, const int32_t* sorted_pos, int64_t R,
                         float* d_row_w, uint16_t* dX, int64_t H, hipStream_t s);
 // tiled B operands (btile_* layout in mk_device.h); source rows: mode 0 rows of
@@ -99,8 +121,9 @@ void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* w
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I,
                      const float* gu, const int32_t* inv, const float* row_w, uint16_t* dgdu,
                      uint16_t* wa, float* dw_part, int n_cu, hipStream_t s);
+// dX != nullptr: dX[inv[p]] = bf16(dX_row[p]) (expert share); else dx32[p] = dX_row[p]
 void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wguT, int H, int I,
-                   const int32_t* inv, uint16_t* dX, int n_cu, hipStream_t s);
+                   const int32_t* inv, uint16_t* dX, float* dx32, int n_cu, hipStream_t s);
 
 struct WgradArgs {
   int E, nb, MB;

@@ -15,7 +15,8 @@
 // 16-byte x reads and eight 16-byte router reads (broadcast across the lanes
 // that share them) feed 64 FMAs, read one group ahead.  Top-k
 // then runs one wave per token over the logits kept in LDS: k rounds of a
-// wave-wide (max logit, min id) reduction.
+// wave-wide (max logit, min id) reduction.  The LOGITS variant stops after
+// the logits and stores them (the router backward needs the full softmax).
 #include "mk_device.h"
 #include "mk_internal.h"
 
@@ -31,10 +32,11 @@ __device__ __forceinline__ bool better(float za, int ea, float zb, int eb) {
   return za > zb || (za == zb && ea < eb);
 }
 
+template <bool LOGITS>
 __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                     const float* __restrict__ bias, int T, int H, int E, int k,
                                                     int renorm, int32_t* __restrict__ idx_out,
-                                                    float* __restrict__ w_out) {
+                                                    float* __restrict__ w_out, float* __restrict__ z_out) {
   extern __shared__ float zbuf[];                                  // [RT][E]
   __shared__ __attribute__((aligned(16))) float xs[2][RT][RH];
   __shared__ __attribute__((aligned(16))) float ws[2][RH][RE];
@@ -128,12 +130,20 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
       if (e < E) {
         const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) zbuf[(2 * ty + i) * E + e] = bias ? acc[i][j] + b : acc[i][j];
+        for (int i = 0; i < 2; ++i) {
+          const float z = bias ? acc[i][j] + b : acc[i][j];
+          if (LOGITS) {
+            if (t0 + 2 * ty + i < T) z_out[(int64_t)(t0 + 2 * ty + i) * E + e] = z;
+          } else {
+            zbuf[(2 * ty + i) * E + e] = z;
+          }
+        }
       }
     }
     // the next chunk's first staging reuses the slice buffers
     __syncthreads();
   }
+  if (LOGITS) return;
   // top-k: one wave per token
   const int lane = tid & 63, wave = tid >> 6, nwaves = RNT >> 6;
   for (int t = wave; t < RT; t += nwaves) {
@@ -197,8 +207,16 @@ void launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias
                   int renorm, int32_t* idx, float* w, hipStream_t s) {
   if (T <= 0) return;
   const int blocks = (T + RT - 1) / RT;
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(RNT), RT * E * sizeof(float), s, x, w_router, bias, T, H, E,
-                     k, renorm, idx, w);
+  hipLaunchKernelGGL(route_kernel<false>, dim3(blocks), dim3(RNT), RT * E * sizeof(float), s, x, w_router, bias, T,
+                     H, E, k, renorm, idx, w, nullptr);
+}
+
+void launch_route_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
+                         float* z, hipStream_t s) {
+  if (T <= 0) return;
+  const int blocks = (T + RT - 1) / RT;
+  hipLaunchKernelGGL(route_kernel<true>, dim3(blocks), dim3(RNT), 0, s, x, w_router, bias, T, H, E, 0, 0, nullptr,
+                     nullptr, z);
 }
 
 }  // namespace mk

@@ -169,7 +169,7 @@ __global__ void zero_dropped_rows_kernel(const int32_t* __restrict__ sorted_pos,
 }
 
 // d_row_w[r] = sum over slices (ascending) of dw_part[sorted_pos[r]]; a dropped
-// row gets 0 and a zero dX row.
+// row gets 0 and (expert share, dX given) a zero dX row.
 __global__ void dw_finalize_kernel(const float* __restrict__ dw_part, int slices,
                                    const int32_t* __restrict__ sorted_pos, int64_t R, float* __restrict__ d_row_w,
                                    uint16_t* __restrict__ dX, int64_t H) {
@@ -181,7 +181,8 @@ __global__ void dw_finalize_kernel(const float* __restrict__ dw_part, int slices
       d_row_w[r] = s;
     } else {
       d_row_w[r] = 0.f;
-      for (int64_t h = 0; h < H; ++h) dX[r * H + h] = 0;
+      if (dX)
+        for (int64_t h = 0; h < H; ++h) dX[r * H + h] = 0;
     }
   }
 }

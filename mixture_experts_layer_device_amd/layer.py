@@ -86,19 +86,35 @@ class MoELayer:
     def new_fwd_ctx(self) -> torch.Tensor:
         return torch.empty(self.query("fwd_ctx_bytes"), dtype=torch.uint8, device=self.device)
 
-    def backward(self, fwd_ctx, x_src, row_w, packed, dY, R, grads=None):
+    def _grads(self, n_x, R):
         E, H, I = self.E, self.H, self.I
-        if grads is None:
-            grads = {
-                "dX": torch.empty((R, H), dtype=torch.int16, device=self.device),
-                "dW_gate": torch.empty((E, I, H), dtype=torch.float32, device=self.device),
-                "dW_up": torch.empty((E, I, H), dtype=torch.float32, device=self.device),
-                "dW_down": torch.empty((E, H, I), dtype=torch.float32, device=self.device),
-                "d_row_w": torch.empty((R,), dtype=torch.float32, device=self.device),
-            }
-        g = grads
-        B.mk_backward(self.ws, B.MK_EXPERT_SHARE, fwd_ctx, x_src, row_w, packed, dY, g["dX"], g["dW_gate"],
+        return {
+            "dX": torch.empty((n_x, H), dtype=torch.int16, device=self.device),
+            "dW_gate": torch.empty((E, I, H), dtype=torch.float32, device=self.device),
+            "dW_up": torch.empty((E, I, H), dtype=torch.float32, device=self.device),
+            "dW_down": torch.empty((E, H, I), dtype=torch.float32, device=self.device),
+            "d_row_w": torch.empty((R,), dtype=torch.float32, device=self.device),
+        }
+
+    def backward(self, fwd_ctx, x_src, row_w, packed, dY, R, grads=None, mode=B.MK_EXPERT_SHARE):
+        """mk_backward; full-layer mode takes x/dY/dX as [R/k, H] token rows."""
+        g = grads if grads is not None else self._grads(R if mode == B.MK_EXPERT_SHARE else R // self.k, R)
+        B.mk_backward(self.ws, mode, fwd_ctx, x_src, row_w, packed, dY, g["dX"], g["dW_gate"],
                       g["dW_up"], g["dW_down"], g["d_row_w"], stream())
+        return g
+
+    def backward_layer(self, fwd_ctx, x, w_router, bias, topk_idx, topk_w, packed, dY, T, grads=None):
+        """mk_backward_layer: full layer including the router; d_row_w is the
+        gradient w.r.t. topk_w (flattened), d_bias is None without a bias."""
+        if grads is None:
+            grads = self._grads(T, T * self.k)
+            grads["dW_router"] = torch.empty((self.E, self.H), dtype=torch.float32, device=self.device)
+            grads["d_bias"] = (torch.empty((self.E,), dtype=torch.float32, device=self.device)
+                               if bias is not None else None)
+        g = grads
+        B.mk_backward_layer(self.ws, fwd_ctx, x, w_router, bias, topk_idx, topk_w, packed, dY, g["dX"],
+                            g["dW_gate"], g["dW_up"], g["dW_down"], g["dW_router"], g["d_bias"], g["d_row_w"],
+                            stream())
         return g
 
     def table(self, name: str, n: int, dtype=torch.int32) -> torch.Tensor:

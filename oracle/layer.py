@@ -274,6 +274,47 @@ def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router
     return out
 
 
+def backward_full_tokens(inp, idx, w, z, tokens, renorm: int):
+    """backward_full's per-token results (bf16 mode) for the given tokens
+    only, under routing (idx, w, z): dX, d_topk_w and the logit gradient dz.
+    Each depends only on the token's own k rows."""
+    tokens = np.asarray(tokens)
+    k = idx.shape[1]
+    wg, wu, wd = _weights(inp)
+    x = bf16.decode(inp["x"][tokens])
+    wr = bf16.decode(inp["w_router"])
+    g = _backward_rows(np.repeat(x, k, axis=0), idx[tokens].reshape(-1), w[tokens].reshape(-1).astype(np.float64),
+                       np.repeat(bf16.decode(inp["dY"][tokens]), k, axis=0), wg, wu, wd, True)
+    n, H = x.shape
+    d_topk_w = g["d_row_w"].reshape(n, k)
+    dXr = g["dX_rows"].reshape(n, k, H)
+    dX = np.zeros((n, H))
+    for j in range(k):                                   # fixed ascending order
+        dX += dXr[:, j]
+    dz = router_logit_grad(z[tokens], idx[tokens], d_topk_w, renorm)
+    dX += dz @ wr
+    return {"dX": rnd(dX, True), "d_topk_w": d_topk_w, "dz": dz}
+
+
+def backward_full_expert(inp, idx, w, z, e, renorm: int):
+    """backward_full's gradients of expert e's weights and router row (bf16
+    mode), from the rows routed to e and, for the router row, the tokens
+    whose logit gradient at e is nonzero: with renorm=1 those that chose e,
+    with renorm=0 every token."""
+    k = idx.shape[1]
+    T = idx.shape[0]
+    wg, wu, wd = _weights(inp)
+    rows = np.nonzero(idx.reshape(-1) == e)[0]
+    tok = rows // k
+    g = _backward_rows(bf16.decode(inp["x"][tok]), np.full(rows.size, e),
+                       w.reshape(-1)[rows].astype(np.float64), bf16.decode(inp["dY"][tok]), wg, wu, wd, True)
+    toks = np.unique(tok) if renorm else np.arange(T)
+    dz_e = backward_full_tokens(inp, idx, w, z, toks, renorm)["dz"][:, e]
+    x = bf16.decode(inp["x"][toks])
+    return {"dW_gate": g["dW_gate"][e], "dW_up": g["dW_up"][e], "dW_down": g["dW_down"][e],
+            "dW_router": dz_e @ x, "d_bias": dz_e.sum()}
+
+
 def forward_share_rows(inp, rows):
     """forward_share's out for the given arrival rows only (each row is
     independent of every other)."""

@@ -6,6 +6,8 @@ max|err| <= 2e-2 * RMS(oracle tensor), MXFP8 outputs within 6e-2 * RMS of the
 MXFP8-emulating oracle.  At full workload sizes the oracle evaluates sampled
 rows / columns one by one (each output row depends only on its own inputs).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -365,6 +367,112 @@ def test_backward_ep_bwd_sampled():
     assert_close(gate, ref["dW_gate"], BF16_TOL, "dW_gate (3 rows)")
     assert_close(up, ref["dW_up"], BF16_TOL, "dW_up (3 rows)")
     assert_close(down, ref["dW_down"], BF16_TOL, "dW_down (3 columns)")
+    L.close()
+
+
+# ------------------------------------------------- full-layer backward --
+def full_variant(name, **over):
+    key = "full:" + name + repr(sorted(over.items()))
+    if key not in _CACHE:
+        sh = workloads.FULL_LAYER[name]
+        _CACHE[key] = workloads.make_full_layer(dataclasses.replace(sh, **over) if over else sh)
+    return _CACHE[key]
+
+
+def run_full_backward(inp, MB=0, ring_bytes=256 << 20, router=True):
+    sh = inp["shape"]
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, minibatch_rows=MB,
+                 ring_bytes=ring_bytes, enable_backward=True)
+    x = dev(inp["x"])
+    wr = dev(inp["w_router"])
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+    idx, w = L.route(x, wr, bias, sh.T)
+    L.build_schedule(idx.view(-1), sh.R)
+    ctx = L.new_fwd_ctx()
+    out = L.forward(B.MK_FULL_LAYER, x, w.view(-1), packed, sh.T, fwd_ctx=ctx)
+    dY = dev(inp["dY"])
+    if router:
+        g = L.backward_layer(ctx, x, wr, bias, idx, w, packed, dY, sh.T)
+    else:
+        g = L.backward(ctx, x, w.view(-1), packed, dY, sh.R, mode=B.MK_FULL_LAYER)
+    sync()
+    return L, idx, w, out, g, (x, wr, bias, packed, ctx, dY)
+
+
+# the backward tiles I by 256: the tiny shape with I = 256
+FULL_BWD_CASES = [("renorm0", {"I": 256}), ("renorm1_bias", {"I": 256, "renorm": 1, "bias_var": 0.5})]
+
+
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (128, 2)], ids=["one_mb", "mb128_ring2_replay"])
+@pytest.mark.parametrize("case", FULL_BWD_CASES, ids=[c[0] for c in FULL_BWD_CASES])
+def test_backward_full_layer_tiny(case, MB, ring_mbs):
+    inp = full_variant("tiny", **case[1])
+    sh = inp["shape"]
+    say(f"[backward full layer] tiny {case[0]} T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k} "
+        f"renorm={sh.renorm} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * 2 * sh.H
+    L, idx, w, out, g, (x, wr, bias, packed, ctx, dY) = run_full_backward(inp, MB=MB, ring_bytes=ring)
+    ref = layer.backward_full(inp)
+    assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+    if MB:
+        assert L.query("ring_rows") < sh.R          # the walk replays evicted minibatches
+    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
+    for key in ("dW_gate", "dW_up", "dW_down", "dW_router"):
+        assert_close(g[key].cpu().numpy(), ref[key], BF16_TOL, key)
+    assert_close(g["d_row_w"].cpu().numpy(), ref["d_topk_w"].reshape(-1), BF16_TOL, "d_topk_w")
+    if bias is not None:
+        assert_close(g["d_bias"].cpu().numpy(), ref["d_bias"], BF16_TOL, "d_bias")
+    # the same call again on the same workspace: bitwise equal
+    g2 = L.backward_layer(ctx, x, wr, bias, idx, w, packed, dY, sh.T)
+    sync()
+    for key, t in g.items():
+        if t is not None:
+            assert torch.equal(t, g2[key]), key
+    L.close()
+
+
+def test_backward_full_layer_router_external_tiny():
+    inp = full_variant("tiny", I=256, renorm=1, bias_var=0.5)
+    sh = inp["shape"]
+    say("[backward full layer] tiny (I=256), router as an external input (mk_backward, MK_FULL_LAYER)")
+    L, idx, w, out, g, _ = run_full_backward(inp, router=False)
+    ref = layer.backward_full(inp, router=False)
+    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX (expert part)", bf16_out=True)
+    assert_close(g["d_row_w"].cpu().numpy(), ref["d_topk_w"].reshape(-1), BF16_TOL, "d_topk_w")
+    for key in ("dW_gate", "dW_up", "dW_down"):
+        assert_close(g[key].cpu().numpy(), ref[key], BF16_TOL, key)
+    L.close()
+
+
+def test_backward_full_layer_full_sampled():
+    inp = full_inputs("full")
+    sh = inp["shape"]
+    say(f"[backward full layer] T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k} renorm={sh.renorm}, biased router")
+    x = bf16.decode(inp["x"]).astype(np.float32)
+    idx_ref, w_ref, z_ref = route.route(x, bf16.decode(inp["w_router"]).astype(np.float32), inp["bias"], sh.k,
+                                        sh.renorm)
+    L, idx, w, out, g, _ = run_full_backward(inp)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    toks = np.sort(np.random.default_rng(4).choice(sh.T, 48, replace=False))
+    t = layer.backward_full_tokens(inp, idx_ref, w_ref, z_ref, toks, sh.renorm)
+    assert_close(host_bf16(g["dX"])[toks], t["dX"], BF16_TOL, "dX (48 sampled tokens)", bf16_out=True)
+    assert_close(g["d_row_w"].cpu().numpy().reshape(sh.T, sh.k)[toks], t["d_topk_w"], BF16_TOL,
+                 "d_topk_w (48 sampled tokens)")
+    counts = np.bincount(idx_ref.reshape(-1), minlength=sh.E)
+    order = np.argsort(counts, kind="stable")
+    experts = [int(order[sh.E // 2]), int(order[3])]
+    db_ref = []
+    for e in experts:
+        say(f"  expert {e}: {counts[e]} rows")
+        r = layer.backward_full_expert(inp, idx_ref, w_ref, z_ref, e, sh.renorm)
+        for key in ("dW_gate", "dW_up", "dW_down", "dW_router"):
+            assert_close(g[key][e].cpu().numpy(), r[key], BF16_TOL, f"{key}[{e}]")
+        db_ref.append(r["d_bias"])
+    assert_close(g["d_bias"].cpu().numpy()[experts], np.array(db_ref), BF16_TOL, "d_bias (2 experts)")
+    # every row of the softmax Jacobian sums to zero, so d_bias does too
+    db = g["d_bias"].double().cpu().numpy()
+    assert abs(db.sum()) <= 1e-4 * np.abs(db).sum()
     L.close()
 
 

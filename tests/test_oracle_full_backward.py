@@ -152,3 +152,20 @@ def test_full_backward_bf16_mode_close_to_exact():
         rel = np.linalg.norm(b[key] - x[key]) / np.linalg.norm(x[key])
         assert rel < 4e-3, (key, rel)
     assert np.array_equal(bf16.round_rne(b["dX"]), b["dX"])
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_sampled_full_backward_helpers_match_full_oracle(renorm):
+    inp, rn = _inputs("tiny", renorm, bias_var=0.5)
+    g = layer.backward_full(inp, renorm=rn)
+    idx, w, z = g["topk_idx"], g["topk_w"], g["logits"]
+    toks = np.array([0, 17, 255])
+    t = layer.backward_full_tokens(inp, idx, w, z, toks, rn)
+    assert np.allclose(t["dX"], g["dX"][toks], rtol=1e-12, atol=1e-12)
+    assert np.allclose(t["d_topk_w"], g["d_topk_w"][toks], rtol=1e-12, atol=1e-13)
+    assert np.allclose(t["dz"], g["dz"][toks], rtol=1e-12, atol=1e-13)
+    for e in (0, 5):
+        x = layer.backward_full_expert(inp, idx, w, z, e, rn)
+        for key in ("dW_gate", "dW_up", "dW_down", "dW_router"):
+            assert np.allclose(x[key], g[key][e], rtol=1e-10, atol=1e-12), key
+        assert np.isclose(x["d_bias"], g["d_bias"][e], rtol=1e-10, atol=1e-13)
