@@ -138,6 +138,7 @@ def forward_share_mxfp8(inp, qw=None):
     R, H = x.shape
     I = wg.shape[1]
     a_bits = np.zeros((R, I), dtype=np.uint16)
+    G = np.zeros((R, I)); U = np.zeros((R, I))
     y = np.zeros((R, H))
     for e in range(wg.shape[0]):
         sel = np.nonzero(re == e)[0]
@@ -145,12 +146,14 @@ def forward_share_mxfp8(inp, qw=None):
             continue
         g = xd[sel] @ wg[e].T
         u = xd[sel] @ wu[e].T
+        G[sel], U[sel] = g, u
         a_bits[sel] = bf16.encode(silu(g) * u)
         ac, as_ = mxfp8.quantize(bf16.decode(a_bits[sel]))
         y[sel] = mxfp8.dequantize(ac, as_) @ wd[e].T
     w = inp["row_w"].astype(np.float64)
     out = w[:, None] * y
-    return {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "y": y, "out": bf16.round_rne(out), "out_exact": out}
+    return {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "g": G, "u": U, "y": y, "out": bf16.round_rne(out),
+            "out_exact": out}
 
 
 def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool):
@@ -313,6 +316,121 @@ def backward_full_expert(inp, idx, w, z, e, renorm: int):
     x = bf16.decode(inp["x"][toks])
     return {"dW_gate": g["dW_gate"][e], "dW_up": g["dW_up"][e], "dW_down": g["dW_down"][e],
             "dW_router": dz_e @ x, "d_bias": dz_e.sum()}
+
+
+def qd(v):
+    """MXFP8 quantise-dequantise along the last axis (blocks of 32)."""
+    return mxfp8.dequantize(*mxfp8.quantize(v))
+
+
+def gu_order(I: int) -> np.ndarray:
+    """Order of the 2I gate/up features along the dX GEMM's contraction, as
+    indices into [gate (I) | up (I)]: groups of 16 gate features followed by
+    the 16 up features of the same indices (the packed weights' order; the MX
+    blocks of 32 along it hold 16 gate and 16 up values of the same features)."""
+    blocks = [np.r_[16 * b:16 * b + 16, I + 16 * b:I + 16 * b + 16] for b in range(I // 16)]
+    return np.concatenate(blocks)
+
+
+def _dact_mxfp8(dYq, wdTq, g, u, w):
+    """dA' = D(Q_H(dY)) D(Q_H(W_d^T))^T and the SwiGLU backward from the
+    forward's g, u: -> dA', a (exact silu(g) u), dw, dg, du (bf16)."""
+    dAp = dYq @ wdTq.T
+    a = silu(g) * u
+    dw = np.einsum("ri,ri->r", dAp, a)
+    dA = w[:, None] * dAp
+    s = sigmoid(g)
+    dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
+    du = bf16.round_rne(dA * silu(g))
+    return dAp, a, dw, dg, du
+
+
+def backward_share_mxfp8(inp, fwd=None):
+    """Expert share backward in MXFP8 mode, loss L = sum_r <dY[r], out_rows[r]>
+    with out_rows from forward_share_mxfp8.
+
+    The two data-gradient GEMMs take MXFP8 operands quantised along their
+    contraction, blocks of 32 (the forward's rule carried to the backward):
+        dA' = D(Q_H(dY)) . D(Q_H(W_d[e]^T))^T
+        dX  = bf16( D(Q(P)) . D(Q(W_P[e]^T))^T ),  P = [dg | du] and
+              W_P = [W_g[e] ; W_u[e]] both in gu_order
+    g and u are the MXFP8 forward's (exact products of its dequantised
+    operands); a = silu(g) u; dw, dA, dg, du (bf16) as in the bf16 backward.
+    The weight gradients stay bf16 GEMMs, as in the bf16 backward:
+        dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = dY_e^T bf16(w a)_e
+    """
+    fwd = forward_share_mxfp8(inp) if fwd is None else fwd
+    x = bf16.decode(inp["x"])
+    wg, wu, wd = _weights(inp)
+    re = inp["row_expert"]
+    w = inp["row_w"].astype(np.float64)
+    dY = bf16.decode(inp["dY"])
+    dYq = qd(dY)
+    R, H = x.shape
+    E, I, _ = wg.shape
+    order = gu_order(I)
+    dX = np.zeros((R, H)); dw = np.zeros(R)
+    dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    for e in range(E):
+        sel = np.nonzero(re == e)[0]
+        if sel.size == 0:
+            continue
+        g, u = fwd["g"][sel], fwd["u"][sel]
+        _, a, dw[sel], dg, du = _dact_mxfp8(dYq[sel], qd(wd[e].T), g, u, w[sel])
+        P = np.concatenate([dg, du], axis=1)[:, order]
+        WP = np.concatenate([wg[e], wu[e]], axis=0)[order]          # [2I, H]
+        dX[sel] = bf16.round_rne(qd(P) @ qd(WP.T).T)
+        xe = x[sel]
+        dWg[e] = dg.T @ xe
+        dWu[e] = du.T @ xe
+        dWd[e] = dY[sel].T @ bf16.round_rne(w[sel, None] * a)
+    return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "d_row_w": dw}
+
+
+def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols):
+    """Entries of backward_share_mxfp8 computed one by one (each needs only
+    its own rows, or the rows of one expert)."""
+    re = inp["row_expert"]
+    w = inp["row_w"].astype(np.float64)
+    I = inp["w_gate"].shape[1]
+    order = gu_order(I)
+    out = {"dX": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            wg = bf16.decode(inp["w_gate"][e]); wu = bf16.decode(inp["w_up"][e]); wd = bf16.decode(inp["w_down"][e])
+            q = quantized_weights_expert(inp, e)
+            cache[e] = {"gq": mxfp8.dequantize(*q["gate"]), "uq": mxfp8.dequantize(*q["up"]),
+                        "wdTq": qd(wd.T), "WPTq": qd(np.concatenate([wg, wu], axis=0)[order].T)}
+        return cache[e]
+
+    def fwd_gu(e, sel):
+        c = expert(e)
+        xd = qd(bf16.decode(inp["x"][sel]))
+        return xd @ c["gq"].T, xd @ c["uq"].T
+
+    for r in rows:
+        e = int(re[r])
+        c = expert(e)
+        g, u = fwd_gu(e, [r])
+        _, _, dw, dg, du = _dact_mxfp8(qd(bf16.decode(inp["dY"][r:r + 1])), c["wdTq"], g, u, w[[r]])
+        P = np.concatenate([dg, du], axis=1)[:, order]
+        out["dX"].append(bf16.round_rne(qd(P) @ c["WPTq"].T)[0])
+        out["d_row_w"].append(float(dw[0]))
+    for key, pairs in (("gate_up", gate_up_rows), ("down", down_cols)):
+        for (e, i) in pairs:
+            sel = np.nonzero(re == e)[0]
+            c = expert(e)
+            g, u = fwd_gu(e, sel)
+            _, a, _, dg, du = _dact_mxfp8(qd(bf16.decode(inp["dY"][sel])), c["wdTq"], g, u, w[sel])
+            if key == "gate_up":
+                X = bf16.decode(inp["x"][sel])
+                out["dW_gate"].append(dg[:, i] @ X)
+                out["dW_up"].append(du[:, i] @ X)
+            else:
+                out["dW_down"].append(bf16.round_rne(w[sel] * a[:, i]) @ bf16.decode(inp["dY"][sel]))
+    return {k: np.asarray(v) for k, v in out.items()}
 
 
 def forward_share_rows(inp, rows):
