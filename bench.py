@@ -6,8 +6,9 @@ Prints ONE JSON line.  ``value`` is routed rows/s of the full single-GPU layer
 forward (T=4096 tokens, H=2048, I=768, 128 experts, top-8 renormalised router
 with a biased logit): one step = route + build_schedule + forward (permute,
 expert GEMMs, combine), inputs resident in HBM.  ``breakdown`` adds the
-expert-share shapes (EP=64 forward in bf16 and MXFP8, backward in bf16), each
-with rows/s, grouped-GEMM TFLOP/s and per-kernel roofline fractions.  Kernel
+expert-share shapes (EP=64 forward and the backward, each in bf16 and MXFP8)
+and the full-layer backward including the router, each with rows/s,
+grouped-GEMM TFLOP/s and per-kernel roofline fractions.  Kernel
 durations come from HIP events the library records around each phase on the
 stream it launches on, over the timed steps.
 """
@@ -39,7 +40,8 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, full_bwd)")
+                    help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, "
+                         "full_bwd)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) 3 times: the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -50,7 +52,7 @@ def parse():
 # algorithmic work per phase (flops, bytes) -- minimum traffic: every operand
 # read once and every result written once
 # --------------------------------------------------------------------------
-def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True):
+def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, replay_rows=0):
     ab = 1 if mx else 2                       # bytes per GEMM operand element
     sc = 1.0 / 32 if mx else 0.0             # MXFP8 scale bytes per element
     w = {}
@@ -66,12 +68,20 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True):
             w["combine"] = (0.0, R * H * 4 + T * H * 2 + R * 8)
     else:
         # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
-        w["bwd_gather"] = (0.0, (R if share else T) * H * 2 + R * H * 2)
-        w["bwd_dact"] = (2.0 * R * H * I, R * H * 2 + E * I * H * 2 + R * 2 * I * 4 + R * 2 * I * 2 + R * I * 2)
+        # (MXFP8: read twice, written as bf16 rows and as codes + scales)
+        src = (R if share else T) * H * 2
+        w["bwd_gather"] = (0.0, src + R * H * 2 + (src + R * H * (ab + sc) if mx else 0))
+        w["bwd_dact"] = (2.0 * R * H * I, R * H * (ab + sc) + E * I * H * (ab + sc) + R * 2 * I * 4 + R * 2 * I * 2
+                         + R * I * 2)
+        if mx:
+            w["quant_a"] = (0.0, R * 2 * I * 2 + R * 2 * I * (1 + 1 / 32))     # dg/du quantised along 2I
         # share: bf16 rows to arrival order; full layer: fp32 rows for the k-sum
-        w["bwd_dx"] = (4.0 * R * I * H, R * 2 * I * 2 + E * H * 2 * I * 2 + R * H * (2 if share else 4))
+        w["bwd_dx"] = (4.0 * R * I * H, R * 2 * I * (ab + sc) + E * H * 2 * I * (ab + sc)
+                       + R * H * (2 if share else 4))
         w["wgrad_down"] = (2.0 * R * H * I, R * H * 2 + R * I * 2 + E * H * I * 4)
         w["wgrad_gate_up"] = (4.0 * R * H * I, R * 2 * I * 2 + R * H * 2 + E * 2 * I * H * 4)
+        # x rows of the minibatches evicted from the ring gathered again
+        w["replay"] = (0.0, replay_rows * H * 2 * 2)
         if not share:
             # k-sum of fp32 rows + router term (k rows of W_r per token, L2-resident)
             w["bwd_combine"] = (2.0 * R * H, R * H * 4 + T * H * 2 + R * 4 + T * E * 4 + E * H * 2)
@@ -183,15 +193,15 @@ def main():
         extra["step_ms_cold_median"] = round(sorted(cold)[2], 4)
         return dt, per, extra
 
-    def summarize(name, R, T, H, I, E, k, dt, per, steps, kind, mx=False, share=True, save_ctx=False):
-        work = phase_work(kind, R, T, H, I, E, k, mx=mx, save_ctx=save_ctx, share=share)
+    def summarize(name, R, T, H, I, E, k, dt, per, steps, kind, mx=False, share=True, save_ctx=False, replay_rows=0):
+        work = phase_work(kind, R, T, H, I, E, k, mx=mx, save_ctx=save_ctx, share=share, replay_rows=replay_rows)
         phases = {}
         gemm_flops = gemm_ms = 0.0
         for p, (ms, n) in per.items():
             f, b = work.get(p, (0.0, 0.0))
             ent = {"ms": round(ms, 4), "launches": n}
             if f or b:
-                ent["roofline"] = roofline(f, b, ms, mx=mx and p.startswith("gemm"))
+                ent["roofline"] = roofline(f, b, ms, mx=mx and p in ("gemm1", "gemm2", "bwd_dact", "bwd_dx"))
             phases[p] = ent
             if f and p not in ("route", "bwd_combine", "router_bwd"):
                 gemm_flops += f
@@ -206,7 +216,8 @@ def main():
         }
 
     results = {}
-    want = set(a.only.split(",")) if a.only else {"full", "ep64_fwd", "ep64_mxfp8", "ep_bwd", "full_bwd"}
+    want = set(a.only.split(",")) if a.only else {"full", "ep64_fwd", "ep64_mxfp8", "ep_bwd", "ep_bwd_mxfp8",
+                                                   "full_bwd"}
     if a.no_breakdown:
         want = {"full"}
 
@@ -267,11 +278,14 @@ def main():
             log(json.dumps(results[key]))
         del x, wg, wu, wd
 
-    if "ep_bwd" in want:
+    for prec, key in (("bf16", "ep_bwd"), ("mxfp8", "ep_bwd_mxfp8")):
+        if key not in want:
+            continue
         inp = workloads.make_expert_share("ep_bwd")
         sh = inp["shape"]
-        log(f"[bench] expert share backward bf16: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096 (ring wraps)")
-        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, minibatch_rows=4096, enable_backward=True)
+        log(f"[bench] expert share backward {prec}: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096 (ring wraps)")
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=4096,
+                     enable_backward=True)
         x = up(inp["x"]); re = up(inp["row_expert"]); rw = up(inp["row_w"]); dY = up(inp["dY"])
         packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]), for_backward=True)
         out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
@@ -290,11 +304,16 @@ def main():
                           g["dW_down"], g["d_row_w"], s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
-        results["ep_bwd"] = summarize("ep_bwd", sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "backward")
-        results["ep_bwd"].update(extra)
-        results["ep_bwd"]["err"] = L.device_error()
+        MB = L.query("minibatch_rows")
+        nb = -(-sh.R // MB)
+        replay_mbs = nb if prec == "mxfp8" else max(0, nb - L.query("ring_rows") // MB)
+        results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "backward",
+                                 mx=prec == "mxfp8", replay_rows=min(sh.R, replay_mbs * MB))
+        results[key].update(extra)
+        results[key]["err"] = L.device_error()
         L.close()
-        log(json.dumps(results["ep_bwd"]))
+        del packed, g, x, dY
+        log(json.dumps(results[key]))
 
     if "full_bwd" in want:
         inp = workloads.make_full_layer("full")

@@ -196,17 +196,23 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_u
  *   mode MK_EXPERT_SHARE: x_src_dev [R, H] bf16 in arrival order; row_w_dev [R];
  *                         out_dev [R, H] bf16, out[r] = w[r] * y(r).
  *   fwd_ctx_dev: NULL, or mk_query(MK_Q_FWD_CTX_BYTES) bytes that receive what
- *                the backward needs (g and u in fp32).
+ *                the backward needs (g and u in fp32; in MXFP8 mode the
+ *                products of the dequantised operands).
  * Uses the schedule of the last mk_build_schedule (MK_ERR_STATE if none).
- * MK_ERR_UNSUPPORTED for MXFP8 with fwd_ctx (MXFP8 backward is not built).
  */
 int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const float* row_w_dev,
                const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
 
 /*
- * Backward, bf16 ([MTP]: the ring is walked in reverse to minimise
+ * Backward ([MTP]: the ring is walked in reverse to minimise
  * forward-activation replay; the router-weight gradient is fused into the
- * SwiGLU backward), for the loss L = <dY, out> of mk_forward.
+ * SwiGLU backward), for the loss L = <dY, out> of mk_forward.  In MXFP8 mode
+ * the two data-gradient GEMMs take MXFP8 operands quantised along their
+ * contraction (dY and W_d^T along H; dg/du and W_gu^T along the 2I packed
+ * gate/up features, blocks of 32), fp32 accumulation; the weight gradients
+ * are bf16 GEMMs as in bf16 mode.  Evicted minibatches (an MXFP8 ring holds
+ * codes, so all of them) have their x rows gathered again before the
+ * gate/up weight gradient.
  *   mode MK_EXPERT_SHARE: x_src_dev [R, H], row_w_dev [R], dY_dev [R, H] and
  *       dX_dev [R, H] in arrival order; d_row_w_dev [R] fp32.
  *   mode MK_FULL_LAYER: x_src_dev [T, H], row_w_dev = topk_w [T*k],
@@ -219,8 +225,8 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const floa
  * order, rows ascending inside each) with no float atomics: bitwise repeatable
  * at a fixed minibatch size.  Must follow the mk_forward (with fwd_ctx) of the
  * same rows and mode on this workspace with no other forward in between;
- * packed_dev must have been prepared with for_backward = 1.  MK_ERR_UNSUPPORTED
- * for MXFP8; MK_ERR_CONFIG if the workspace has no backward buffers;
+ * packed_dev must have been prepared with for_backward = 1.  MK_ERR_CONFIG if
+ * the workspace has no backward buffers;
  * MK_ERR_SHAPE in full-layer mode unless R and MB are multiples of k.
  */
 int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const void* x_src_dev,
@@ -276,7 +282,8 @@ int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx_dev, const void* x_d
 #define MK_PH_WGRAD_GU   12
 #define MK_PH_BWD_COMBINE 13  /* full layer: k-sum of dX rows (+ router term) */
 #define MK_PH_ROUTER_BWD 14   /* router backward: logit gradient, dW_router, d_bias */
-#define MK_PH_COUNT      15
+#define MK_PH_REPLAY     15   /* re-gather of the x rows of minibatches evicted from the ring */
+#define MK_PH_COUNT      16
 int mk_timing_enable(mk_workspace* ws, int32_t on);
 int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
 

@@ -188,7 +188,7 @@ def mk_timing_enable(ws, on: bool) -> None:
 
 
 PHASES = ["route", "schedule", "permute", "gemm1", "quant_a", "gemm2", "combine", "bwd_gather", "bwd_dact",
-          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd"]
+          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd", "replay"]
 
 
 def mk_timing_read(ws) -> dict:

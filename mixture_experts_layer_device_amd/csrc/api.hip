@@ -32,8 +32,12 @@ hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 int64_t packed_bytes(const mk_workspace* ws, bool bwd) {
   const int64_t E = ws->E, H = ws->H, I = ws->I;
   if (ws->cfg.precision == MK_MXFP8) {
-    return (int64_t)align_up(E * 2 * I * H) + (int64_t)align_up(E * 2 * I * H / 32) +
-           (int64_t)align_up(E * H * I) + (int64_t)align_up(E * H * I / 32);
+    int64_t b = (int64_t)align_up(E * 2 * I * H) + (int64_t)align_up(E * 2 * I * H / 32) +
+                (int64_t)align_up(E * H * I) + (int64_t)align_up(E * H * I / 32);
+    if (bwd)
+      b += (int64_t)align_up(E * I * H) + (int64_t)align_up(E * I * H / 32) + (int64_t)align_up(E * H * 2 * I) +
+           (int64_t)align_up(E * H * 2 * I / 32);
+    return b;
   }
   int64_t b = (int64_t)align_up(E * 2 * I * H * 2) + (int64_t)align_up(E * H * I * 2);
   if (bwd) b += (int64_t)align_up(E * I * H * 2) + (int64_t)align_up(E * H * 2 * I * 2);
@@ -59,6 +63,7 @@ PackedBF16 packed_bf16(const mk_workspace* ws, void* base) {
 
 struct PackedMX {
   uint8_t *wgu_c, *wgu_s, *wd_c, *wd_s;
+  uint8_t *wdT_c, *wdT_s, *wguT_c, *wguT_s;     // backward copies (W_d^T along H, W_gu^T along 2I)
 };
 PackedMX packed_mx(const mk_workspace* ws, void* base) {
   const int64_t E = ws->E, H = ws->H, I = ws->I;
@@ -71,6 +76,14 @@ PackedMX packed_mx(const mk_workspace* ws, void* base) {
   r.wd_c = (uint8_t*)p;
   p += align_up(E * H * I);
   r.wd_s = (uint8_t*)p;
+  p += align_up(E * H * I / 32);
+  r.wdT_c = (uint8_t*)p;
+  p += align_up(E * I * H);
+  r.wdT_s = (uint8_t*)p;
+  p += align_up(E * I * H / 32);
+  r.wguT_c = (uint8_t*)p;
+  p += align_up(E * H * 2 * I);
+  r.wguT_s = (uint8_t*)p;
   return r;
 }
 
@@ -128,8 +141,8 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   if (!ws) return MK_ERR_NULL;
   if (!ws->have_sched) return MK_ERR_STATE;
   if (mode != MK_EXPERT_SHARE && mode != MK_FULL_LAYER) return MK_ERR_CONFIG;
-  if (ws->cfg.precision != MK_BF16) return MK_ERR_UNSUPPORTED;
   if (!ws->cfg.enable_backward) return MK_ERR_CONFIG;
+  const bool mx = ws->cfg.precision == MK_MXFP8;
   if (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !dW_gate || !dW_up || !dW_down || !d_row_w)
     return MK_ERR_NULL;
   const bool full = mode == MK_FULL_LAYER;
@@ -139,17 +152,29 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   const int T = R / src_div;
   hipStream_t s = as_stream(stream);
   PackedBF16 p = packed_bf16(ws, (void*)packed);
+  PackedMX pm = packed_mx(ws, (void*)packed);
   const ItemRange all = item_range(ws, 0, nb);
-  // pull the loss gradient into expert order (share of the reverse combine)
+  const int64_t npos_used = (int64_t)nb * MB;
+  // pull the loss gradient into expert order (share of the reverse combine);
+  // MXFP8: quantised along H for the dA' GEMM in the same pass, which also
+  // keeps the bf16 rows for the down-projection weight gradient
   {
     Phase ph(ws, MK_PH_BWD_GATHER, s);
-    launch_gather_rows((const uint16_t*)dY, H, ws->inv, src_div, 0, (int64_t)nb * MB, 0, ws->dye, ws->n_cu, s);
+    if (mx)
+      launch_gather_rows_mxfp8((const uint16_t*)dY, H, ws->inv, src_div, 0, npos_used, 0, ws->dye_c, ws->dye_s,
+                               ws->n_cu, s, ws->dye);
+    else
+      launch_gather_rows((const uint16_t*)dY, H, ws->inv, src_div, 0, npos_used, 0, ws->dye, ws->n_cu, s);
   }
   // dA' GEMM with the SwiGLU backward and router-weight gradient fused
   {
     Phase ph(ws, MK_PH_BWD_DACT, s);
-    launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, ws->inv, row_w, ws->dgdu, ws->wa, ws->dw_part,
-                    ws->n_cu, s);
+    if (mx)
+      launch_bwd_dact_mxfp8(all, ws->dye_c, ws->dye_s, pm.wdT_c, pm.wdT_s, H, I, (const float*)fwd_ctx, ws->inv,
+                            row_w, ws->dgdu, ws->wa, ws->dw_part, ws->n_cu, s);
+    else
+      launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, ws->inv, row_w, ws->dgdu, ws->wa,
+                      ws->dw_part, ws->n_cu, s);
   }
   {
     Phase ph(ws, MK_PH_BWD_DW, s);
@@ -157,9 +182,17 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   }
   // dX GEMM: expert share stores rows back to arrival order (share of the
   // reverse dispatch); the full layer keeps fp32 rows for the k-sum
+  if (mx) {
+    Phase ph(ws, MK_PH_QUANT_A, s);
+    launch_quantize(ws->dgdu, npos_used, 2 * I, ws->dgdu_c, ws->dgdu_s, s);
+  }
   {
     Phase ph(ws, MK_PH_BWD_DX, s);
-    launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, ws->inv, full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
+    if (mx)
+      launch_bwd_dx_mxfp8(all, ws->dgdu_c, ws->dgdu_s, pm.wguT_c, pm.wguT_s, H, I, ws->inv,
+                          full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
+    else
+      launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, ws->inv, full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
   }
   if (full) {
     if (rg) {
@@ -195,9 +228,20 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
     Phase ph(ws, MK_PH_WGRAD_DOWN, s);
     launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->n_cu, s);
   }
+  // replay (the reverse walk's share of re-pulling evicted rows): the x rows
+  // of the minibatches no longer in the ring (an MXFP8 ring holds codes: all
+  // of them) are gathered again, into the dY rows' buffer, free once the
+  // down-projection gradient has read it; the weight-gradient loader reads
+  // them there by position
+  const int replay_mbs = mx ? nb : first_resident;
+  if (replay_mbs > 0) {
+    Phase ph(ws, MK_PH_REPLAY, s);
+    launch_gather_rows((const uint16_t*)x_src, H, ws->inv, src_div, 0, (int64_t)replay_mbs * MB, 0, ws->dye,
+                       ws->n_cu, s);
+  }
   Phase ph(ws, MK_PH_WGRAD_GU, s);
-  launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, first_resident,
-                       (const uint16_t*)x_src, H, I, dW_gate, dW_up, ws->n_cu, s);
+  launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, replay_mbs, ws->dye, H, I, dW_gate,
+                       dW_up, ws->n_cu, s);
   return check_launch();
 }
 
@@ -226,7 +270,6 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   if (cfg->precision != MK_BF16 && cfg->precision != MK_MXFP8) return MK_ERR_CONFIG;
   if (cfg->minibatch_rows < 0 || !(cfg->sched_capacity_mult > 0.f) || cfg->ring_bytes <= 0) return MK_ERR_CONFIG;
   if (cfg->ring_bytes >= ((int64_t)1 << 31)) return MK_ERR_LIMIT;
-  if (cfg->enable_backward && cfg->precision != MK_BF16) return MK_ERR_UNSUPPORTED;
   if (cfg->enable_backward && I % 256) return MK_ERR_SHAPE;
 
   mk_workspace* ws = (mk_workspace*)calloc(1, sizeof(mk_workspace));
@@ -292,13 +335,19 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     o_as = c.take((size_t)npos * I / 32);
   }
   const size_t o_y = c.take((size_t)npos * H * 4);
-  size_t o_dye = 0, o_dgdu = 0, o_wa = 0, o_dwp = 0, o_dz = 0, o_rp = 0;
+  size_t o_dye = 0, o_dgdu = 0, o_wa = 0, o_dwp = 0, o_dz = 0, o_rp = 0, o_dyc = 0, o_dys = 0, o_gc = 0, o_gs = 0;
   if (cfg->enable_backward) {
     o_dye = c.take((size_t)npos * H * 2);
     o_dgdu = c.take((size_t)npos * 2 * I * 2);
     o_wa = c.take((size_t)npos * I * 2);
     o_dwp = c.take((size_t)npos * (I / 64) * 4);
     o_dz = c.take((size_t)((max_rows + k - 1) / k) * E * 4);
+    if (cfg->precision == MK_MXFP8) {
+      o_dyc = c.take((size_t)npos * H);
+      o_dys = c.take((size_t)npos * H / 32);
+      o_gc = c.take((size_t)npos * 2 * I);
+      o_gs = c.take((size_t)npos * 2 * I / 32);
+    }
     // token splits of the router weight gradient: ~256 tokens each, partials
     // capped at 64 MiB
     const int64_t per_split = (int64_t)E * (H + 1) * 4;
@@ -337,6 +386,12 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     ws->dw_part = (float*)(b + o_dwp);
     ws->dz = (float*)(b + o_dz);
     ws->rpart = (float*)(b + o_rp);
+    if (cfg->precision == MK_MXFP8) {
+      ws->dye_c = (uint8_t*)(b + o_dyc);
+      ws->dye_s = (uint8_t*)(b + o_dys);
+      ws->dgdu_c = (uint8_t*)(b + o_gc);
+      ws->dgdu_s = (uint8_t*)(b + o_gs);
+    }
   }
   // error word starts clear
   launch_fill_u32(ws->err, 0u, 1, nullptr);
@@ -443,10 +498,14 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, c
   hipStream_t s = as_stream(stream);
   const int E = ws->E, H = ws->H, I = ws->I;
   if (ws->cfg.precision == MK_MXFP8) {
-    if (for_backward) return MK_ERR_UNSUPPORTED;
     PackedMX p = packed_mx(ws, packed);
-    launch_quant_tile_rows((const uint16_t*)w_gate, (const uint16_t*)w_up, 1, E, 2 * I, H, p.wgu_c, p.wgu_s, s);
-    launch_quant_tile_rows((const uint16_t*)w_down, nullptr, 0, E, H, I, p.wd_c, p.wd_s, s);
+    const uint16_t *wg = (const uint16_t*)w_gate, *wu = (const uint16_t*)w_up, *wd = (const uint16_t*)w_down;
+    launch_quant_tile_rows(wg, wu, 1, E, 2 * I, H, p.wgu_c, p.wgu_s, s);      // GEMM1 B along H
+    launch_quant_tile_rows(wd, nullptr, 0, E, H, I, p.wd_c, p.wd_s, s);       // GEMM2 B along I
+    if (for_backward) {
+      launch_quant_tile_cols(wd, nullptr, 0, E, I, H, p.wdT_c, p.wdT_s, s);   // dA' B: W_d^T along H
+      launch_quant_tile_cols(wg, wu, 1, E, H, 2 * I, p.wguT_c, p.wguT_s, s);  // dX B: W_gu^T along 2I
+    }
     return check_launch();
   }
   PackedBF16 p = packed_bf16(ws, packed);
@@ -475,7 +534,6 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
     kk = k;
   }
   const bool mx = ws->cfg.precision == MK_MXFP8;
-  if (mx && fwd_ctx) return MK_ERR_UNSUPPORTED;
   if (R == 0) return MK_OK;
   hipStream_t s = as_stream(stream);
   const int nb = ws->nb;
@@ -514,7 +572,7 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
       }
       Phase ph(ws, MK_PH_GEMM1, s);
       launch_gemm1_mxfp8(item_range(ws, b0, b1), rc, rsc, ws->ring_rows, p.wgu_c, p.wgu_s, H, I, ws->a_buf,
-                         ws->n_cu, s);
+                         (float*)fwd_ctx, ws->n_cu, s);
     }
     {
       Phase ph(ws, MK_PH_QUANT_A, s);

@@ -204,53 +204,11 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
                                                       float* __restrict__ dw_part) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = I / BN;
-  const int slices = I / 64;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dye + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * H; };
     Acc acc;
     mainloop_nt(arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, lds, acc);
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
-    const int slice = (ti.n0 + wn * 64) / 64;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = frag_row(i, v);
-        const bool valid = r < ti.rows;
-        const int64_t p = ti.pos0 + (valid ? r : 0);
-        const float w = valid ? row_w[inv[p]] : 0.f;
-        float dws = 0.f;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int ii = ti.n0 + frag_col(j);
-          const int gc = 32 * (ii >> 4) + (ii & 15);
-          float g = 0.f, u = 0.f;
-          if (valid) {
-            g = gu[p * 2 * I + gc];
-            u = gu[p * 2 * I + gc + 16];
-          }
-          const float s = sigmoidf_(g);
-          const float sl = g * s;
-          const float aa = sl * u;
-          const float dap = acc[i][j][v];
-          dws += dap * aa;
-          const float da = w * dap;
-          if (valid) {
-            dgdu[p * 2 * I + gc] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
-            dgdu[p * 2 * I + gc + 16] = (uint16_t)f32_to_bf16(da * sl);
-          }
-          stage_put(lds, r, frag_col(j), w * aa);
-        }
-        // fixed butterfly over the 16 lanes that share this row
-        dws += __shfl_xor(dws, 1);
-        dws += __shfl_xor(dws, 2);
-        dws += __shfl_xor(dws, 4);
-        dws += __shfl_xor(dws, 8);
-        if (valid && (lane & 15) == 0) dw_part[p * slices + slice] = dws;
-      }
-    stage_flush<256>(lds, [&](int r) -> uint16_t* {
-      return r < ti.rows ? wa + (int64_t)(ti.pos0 + r) * I + ti.n0 : nullptr;
-    });
+    dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
   });
 }
 
@@ -269,24 +227,7 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t
     auto arow = [&](int r) { return dgdu + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * 2 * I; };
     Acc acc;
     mainloop_nt(arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, lds, acc);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = frag_row(i, v);
-        if (ROWS16) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), acc[i][j][v]);
-        } else if (r < ti.rows) {
-          float* dst = dx32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
-        }
-      }
-    if (ROWS16)
-      stage_flush<256>(lds, [&](int r) -> uint16_t* {
-        return r < ti.rows ? dX + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
-      });
+    dx_epilogue<ROWS16>(ti, acc, lds, H, inv, dX, dx32);
   });
 }
 
@@ -321,7 +262,7 @@ struct WgradOperands {
   int64_t ldb;
   const uint16_t* ring;
   int ring_rows, first_resident;
-  const uint16_t* x_src;
+  const uint16_t* replay;      // x rows of minibatches < first_resident, at their positions p
   int64_t ldx;
 };
 
@@ -344,7 +285,7 @@ __device__ __forceinline__ void wgrad_load(const WgradOperands<MODE>& op, const 
       } else if (it.b >= op.first_resident) {
         ptr = op.ring + (int64_t)(p % op.ring_rows) * op.ldx + n0 + mc * 8;
       } else {
-        ptr = op.x_src + (int64_t)(w.inv[p] / w.src_div) * op.ldx + n0 + mc * 8;
+        ptr = op.replay + p * op.ldx + n0 + mc * 8;
       }
       v[c] = *(const u32x4_t*)ptr;
     } else {
@@ -464,9 +405,9 @@ void launch_wgrad_down(const WgradArgs& w, const uint16_t* dye, const uint16_t* 
 }
 
 void launch_wgrad_gate_up(const WgradArgs& w, const uint16_t* dgdu, const uint16_t* ring, int32_t ring_rows,
-                          int first_resident, const uint16_t* x_src, int H, int I, float* dW_gate, float* dW_up,
+                          int first_resident, const uint16_t* replay, int H, int I, float* dW_gate, float* dW_up,
                           int n_cu, hipStream_t s) {
-  WgradOperands<1> op{dgdu, 2 * (int64_t)I, nullptr, 0, ring, ring_rows, first_resident, x_src, H};
+  WgradOperands<1> op{dgdu, 2 * (int64_t)I, nullptr, 0, ring, ring_rows, first_resident, replay, H};
   hipLaunchKernelGGL(wgrad_kernel<1>, dim3(n_cu), dim3(NT), 0, s, w, op, 2 * I, H, I, dW_gate, dW_up);
 }
 

@@ -84,4 +84,88 @@ __device__ __forceinline__ void stage_flush(char* lds, RowDst row_dst) {
   __syncthreads();
 }
 
+// ---- backward epilogues shared by the bf16 and MXFP8 kernels --------------
+
+// dA' tile -> SwiGLU backward, from the forward's fp32 g, u (gu, packed like
+// W_gu): a = silu(g) u; dw partial = sum of dA' a over this wave's 64
+// columns (one slice of I/64, added up later in slice order); dA = w dA';
+// dg = dA u s (1 + g (1 - s)), du = dA silu(g) (bf16, packed like W_gu); and
+// w*a (bf16, the down-projection weight gradient's operand).
+__device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, char* lds, int I,
+                                              const float* __restrict__ gu, const int32_t* __restrict__ inv,
+                                              const float* __restrict__ row_w, uint16_t* __restrict__ dgdu,
+                                              uint16_t* __restrict__ wa, float* __restrict__ dw_part) {
+  constexpr int FM = G_FM, FN = G_FN;
+  const int slices = I / 64;
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
+  const int slice = (ti.n0 + wn * 64) / 64;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = frag_row(i, v);
+      const bool valid = r < ti.rows;
+      const int64_t p = ti.pos0 + (valid ? r : 0);
+      const float w = valid ? row_w[inv[p]] : 0.f;
+      float dws = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int ii = ti.n0 + frag_col(j);
+        const int gc = 32 * (ii >> 4) + (ii & 15);
+        float g = 0.f, u = 0.f;
+        if (valid) {
+          g = gu[p * 2 * I + gc];
+          u = gu[p * 2 * I + gc + 16];
+        }
+        const float s = sigmoidf_(g);
+        const float sl = g * s;
+        const float aa = sl * u;
+        const float dap = acc[i][j][v];
+        dws += dap * aa;
+        const float da = w * dap;
+        if (valid) {
+          dgdu[p * 2 * I + gc] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
+          dgdu[p * 2 * I + gc + 16] = (uint16_t)f32_to_bf16(da * sl);
+        }
+        stage_put(lds, r, frag_col(j), w * aa);
+      }
+      // fixed butterfly over the 16 lanes that share this row
+      dws += __shfl_xor(dws, 1);
+      dws += __shfl_xor(dws, 2);
+      dws += __shfl_xor(dws, 4);
+      dws += __shfl_xor(dws, 8);
+      if (valid && (lane & 15) == 0) dw_part[p * slices + slice] = dws;
+    }
+  stage_flush<256>(lds, [&](int r) -> uint16_t* {
+    return r < ti.rows ? wa + (int64_t)(ti.pos0 + r) * I + ti.n0 : nullptr;
+  });
+}
+
+// dX tile -> ROWS16: bf16 rows straight to arrival order, dX[inv[p]]; else
+// fp32 rows at their position p ([p, H]) for the full layer's k-sum.
+template <bool ROWS16>
+__device__ __forceinline__ void dx_epilogue(const TileInfo& ti, GAcc& acc, char* lds, int H,
+                                            const int32_t* __restrict__ inv, uint16_t* __restrict__ dX,
+                                            float* __restrict__ dx32) {
+  constexpr int FM = G_FM, FN = G_FN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = frag_row(i, v);
+      if (ROWS16) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), acc[i][j][v]);
+      } else if (r < ti.rows) {
+        float* dst = dx32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
+      }
+    }
+  if (ROWS16)
+    stage_flush<256>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? dX + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
+    });
+}
+
 }  // namespace mk

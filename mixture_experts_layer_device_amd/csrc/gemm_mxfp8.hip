@@ -107,11 +107,13 @@ __device__ __forceinline__ void mainloop(ARow arow, ASc ascale, const uint8_t* b
 }
 
 // a[p, i] = silu(g) * u (bf16) from MXFP8 ring rows and packed MXFP8 W_gu.
+// SAVE: also store g and u (fp32, packed like W_gu) as the backward's context.
+template <bool SAVE>
 __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ rc,
                                                          const uint8_t* __restrict__ rsc, int ring_rows,
                                                          const uint8_t* __restrict__ wc,
                                                          const uint8_t* __restrict__ wsc, int H, int I,
-                                                         uint16_t* __restrict__ a_out) {
+                                                         uint16_t* __restrict__ a_out, float* __restrict__ gu_save) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = 2 * I / BN;
   const int nbh = H / 32;
@@ -130,7 +132,13 @@ __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uin
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
-          stage_put(lds, frag_row(i, v), wn * 32 + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+          const int r = frag_row(i, v);
+          stage_put(lds, r, wn * 32 + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+          if (SAVE && r < ti.rows) {
+            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * 64 + q * 32 + (lane & 15);
+            dst[0] = g;
+            dst[16] = u;
+          }
         }
     stage_flush<128>(lds, [&](int r) -> uint16_t* {
       return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
@@ -180,13 +188,87 @@ __global__ __launch_bounds__(NT) void gemm2_mxfp8_kernel(ItemRange ir, const uin
   });
 }
 
+// ------------------------------------------------- backward: dA' + SwiGLU ----
+// dA'[p, i] = D(dY_q[p]) . D(W_d^T[e][i]) with dY quantised along H (rows at
+// their positions p) and W_d^T in the tiled MXFP8 layout [E, I, H]; the
+// SwiGLU backward epilogue is the bf16 kernel's (bf16 dg/du and w*a).
+__global__ __launch_bounds__(NT) void bwd_dact_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ dyc,
+                                                            const uint8_t* __restrict__ dys,
+                                                            const uint8_t* __restrict__ wc,
+                                                            const uint8_t* __restrict__ wsc, int H, int I,
+                                                            const float* __restrict__ gu,
+                                                            const int32_t* __restrict__ inv,
+                                                            const float* __restrict__ row_w,
+                                                            uint16_t* __restrict__ dgdu, uint16_t* __restrict__ wa,
+                                                            float* __restrict__ dw_part) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = I / BN;
+  const int nbh = H / 32;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto prow = [&](int r) { return (int64_t)(ti.pos0 + min(r, ti.rows - 1)); };
+    auto arow = [&](int r) { return dyc + prow(r) * H; };
+    auto asc = [&](int r) { return dys + prow(r) * nbh; };
+    const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, I, H);
+    Acc acc;
+    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
+    dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
+  });
+}
+
+// ------------------------------------------------------ backward: dX ----
+// dX_row[p] = D(dgdu_q[p]) . D(W_gu^T[e]) over the 2I packed features, dgdu
+// quantised along them and W_gu^T in the tiled MXFP8 layout [E, H, 2I].
+template <bool ROWS16>
+__global__ __launch_bounds__(NT) void bwd_dx_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ gc_,
+                                                          const uint8_t* __restrict__ gs_,
+                                                          const uint8_t* __restrict__ wc,
+                                                          const uint8_t* __restrict__ wsc, int H, int I,
+                                                          const int32_t* __restrict__ inv,
+                                                          uint16_t* __restrict__ dX, float* __restrict__ dx32) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int ntn = H / BN;
+  const int nbk = 2 * I / 32;
+  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+    auto prow = [&](int r) { return (int64_t)(ti.pos0 + min(r, ti.rows - 1)); };
+    auto arow = [&](int r) { return gc_ + prow(r) * 2 * I; };
+    auto asc = [&](int r) { return gs_ + prow(r) * nbk; };
+    const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, H, 2 * I);
+    Acc acc;
+    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, 2 * I, lds, acc);
+    dx_epilogue<ROWS16>(ti, acc, lds, H, inv, dX, dx32);
+  });
+}
+
 }  // namespace
+
+void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const uint8_t* dy_scales,
+                           const uint8_t* wdT_codes, const uint8_t* wdT_scales, int H, int I, const float* gu,
+                           const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part,
+                           int n_cu, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_dact_mxfp8_kernel, dim3(n_cu), dim3(NT), 0, s, ir, dy_codes, dy_scales, wdT_codes,
+                     wdT_scales, H, I, gu, inv, row_w, dgdu, wa, dw_part);
+}
+
+void launch_bwd_dx_mxfp8(const ItemRange& ir, const uint8_t* dgdu_codes, const uint8_t* dgdu_scales,
+                         const uint8_t* wguT_codes, const uint8_t* wguT_scales, int H, int I, const int32_t* inv,
+                         uint16_t* dX, float* dx32, int n_cu, hipStream_t s) {
+  if (dX)
+    hipLaunchKernelGGL(bwd_dx_mxfp8_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, dgdu_codes, dgdu_scales,
+                       wguT_codes, wguT_scales, H, I, inv, dX, dx32);
+  else
+    hipLaunchKernelGGL(bwd_dx_mxfp8_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, dgdu_codes, dgdu_scales,
+                       wguT_codes, wguT_scales, H, I, inv, dX, dx32);
+}
 
 void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const uint8_t* ring_scales,
                         int32_t ring_rows, const uint8_t* wgu_codes, const uint8_t* wgu_scales, int H, int I,
-                        uint16_t* a_out, int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL(gemm1_mxfp8_kernel, dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales, ring_rows,
-                     wgu_codes, wgu_scales, H, I, a_out);
+                        uint16_t* a_out, float* gu_save, int n_cu, hipStream_t s) {
+  if (gu_save)
+    hipLaunchKernelGGL(gemm1_mxfp8_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales, ring_rows,
+                       wgu_codes, wgu_scales, H, I, a_out, gu_save);
+  else
+    hipLaunchKernelGGL(gemm1_mxfp8_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales, ring_rows,
+                       wgu_codes, wgu_scales, H, I, a_out, gu_save);
 }
 
 void launch_gemm2_mxfp8(const ItemRange& ir, const uint8_t* a_codes, const uint8_t* a_scales,

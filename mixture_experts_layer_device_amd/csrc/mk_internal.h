@@ -38,6 +38,8 @@ struct mk_workspace {
   float* y_buf;               // [npos, H] fp32 expert outputs, expert order (full-layer combine)
   uint16_t *dye, *dgdu, *wa;  // backward: [npos, H], [npos, 2I], [npos, I]
   float* dw_part;             // [npos, I/64]
+  uint8_t *dye_c, *dye_s;     // MXFP8 backward: dY rows quantised along H  [npos, H], [npos, H/32]
+  uint8_t *dgdu_c, *dgdu_s;   //                 dg/du quantised along 2I   [npos, 2I], [npos, 2I/32]
   float* dz;                  // [ceil(max_rows / k), E]: router logit gradient (and logits)
   float* rpart;               // [rsplits_max, E, H + 1]: router weight-gradient partials
   int32_t rsplits_max;
@@ -79,9 +81,10 @@ void launch_router_wgrad(const float* dz, const uint16_t* x, int T, int H, int E
 void launch_gather_rows(const uint16_t* src, int64_t H, const int32_t* inv, int src_div,
                         int64_t p_lo, int64_t p_hi, int32_t ring_rows, uint16_t* dst,
                         int n_cu, hipStream_t s);
+// (copy: NULL, or also the bf16 rows at their positions p, [p, H])
 void launch_gather_rows_mxfp8(const uint16_t* src, int64_t H, const int32_t* inv, int src_div,
                               int64_t p_lo, int64_t p_hi, int32_t ring_rows, uint8_t* codes,
-                              uint8_t* scales, int n_cu, hipStream_t s);
+                              uint8_t* scales, int n_cu, hipStream_t s, uint16_t* copy = nullptr);
 void launch_combine(const float* y, int64_t H, const int32_t* sorted_pos, const float* row_w,
                     int k, int64_t n_out, uint16_t* out, int n_cu, hipStream_t s);
 // zero the out rows whose sorted_pos is -1 (dropped rows; expert-share mode)
@@ -98,8 +101,12 @@ void launch_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, in
                       hipStream_t s);
 void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K, uint16_t* out,
                       hipStream_t s);
-// tiled MXFP8 B operand (mxt_* layout in mk_device.h), source rows as above
+// tiled MXFP8 B operand (mxt_* layout in mk_device.h), source rows as above,
+// quantised along k:  quant_tile_rows: B[e][n][k] = row(e, n)[k]
+//                     quant_tile_cols: B[e][n][k] = row(e, k)[n]
 void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
+                            uint8_t* codes, uint8_t* scales, hipStream_t s);
+void launch_quant_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
                             uint8_t* codes, uint8_t* scales, hipStream_t s);
 void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 
@@ -136,15 +143,26 @@ struct WgradArgs {
 void launch_wgrad_down(const WgradArgs& wa_args, const uint16_t* dye, const uint16_t* wa, int H,
                        int I, float* dW_down, int n_cu, hipStream_t s);
 // dW_gate/dW_up[e] (I x H) from dgdu (packed 2I) and the x rows: minibatches
-// b >= first_resident come from the ring, earlier ones straight from x_src.
+// b >= first_resident come from the ring, earlier (evicted) ones from replay,
+// the x rows re-gathered at their positions p ([p, H]).
 void launch_wgrad_gate_up(const WgradArgs& wa_args, const uint16_t* dgdu, const uint16_t* ring,
-                          int32_t ring_rows, int first_resident, const uint16_t* x_src, int H,
+                          int32_t ring_rows, int first_resident, const uint16_t* replay, int H,
                           int I, float* dW_gate, float* dW_up, int n_cu, hipStream_t s);
 
 // ---- gemm_mxfp8.hip -----------------------------------------------------
+// gu_save: NULL, or the forward context (g and u in fp32, [p, 2I] packed like W_gu)
 void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const uint8_t* ring_scales,
                         int32_t ring_rows, const uint8_t* wgu_codes, const uint8_t* wgu_scales,
-                        int H, int I, uint16_t* a_out, int n_cu, hipStream_t s);
+                        int H, int I, uint16_t* a_out, float* gu_save, int n_cu, hipStream_t s);
+// MXFP8 data-gradient GEMMs (operands quantised along their contraction);
+// epilogues as launch_bwd_dact / launch_bwd_dx
+void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const uint8_t* dy_scales,
+                           const uint8_t* wdT_codes, const uint8_t* wdT_scales, int H, int I, const float* gu,
+                           const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part,
+                           int n_cu, hipStream_t s);
+void launch_bwd_dx_mxfp8(const ItemRange& ir, const uint8_t* dgdu_codes, const uint8_t* dgdu_scales,
+                         const uint8_t* wguT_codes, const uint8_t* wguT_scales, int H, int I, const int32_t* inv,
+                         uint16_t* dX, float* dx32, int n_cu, hipStream_t s);
 void launch_gemm2_mxfp8(const ItemRange& ir, const uint8_t* a_codes, const uint8_t* a_scales,
                         const uint8_t* wd_codes, const uint8_t* wd_scales, int H, int I,
                         float* y32, uint16_t* out, const int32_t* inv, const float* row_w, int n_cu,

@@ -72,11 +72,13 @@ __device__ __forceinline__ uint32_t quant_block(const u32x4_t (&v)[4], u32x4_t (
 }
 
 // MXFP8 rows: codes[dst] / scales[dst] <- quantised src row (inv == nullptr: dst row = src row = p).
+// (copy != nullptr: the bf16 row is also stored there, at row p)
 __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t H,
                                                                const int32_t* __restrict__ inv, int src_div,
                                                                int64_t p_lo, int64_t p_hi, int32_t ring_rows,
                                                                uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ scales) {
+                                                               uint8_t* __restrict__ scales,
+                                                               uint16_t* __restrict__ copy) {
   const int lane = threadIdx.x & 63;
   const int64_t nblk = H / 32;
   for (int64_t p = p_lo + wave_id(); p < p_hi; p += wave_count()) {
@@ -94,6 +96,11 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
       u32x4_t v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = __builtin_nontemporal_load(s + b * 4 + q);
+      if (copy) {
+        u32x4_t* cp = (u32x4_t*)(copy + p * H);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cp[b * 4 + q] = v[q];
+      }
       u32x4_t c[2];
       const uint32_t sc = quant_block(v, c);
       dc[b * 2] = c[0];
@@ -289,16 +296,16 @@ void launch_gather_rows(const uint16_t* src, int64_t H, const int32_t* inv, int 
 
 void launch_gather_rows_mxfp8(const uint16_t* src, int64_t H, const int32_t* inv, int src_div, int64_t p_lo,
                               int64_t p_hi, int32_t ring_rows, uint8_t* codes, uint8_t* scales, int n_cu,
-                              hipStream_t s) {
+                              hipStream_t s, uint16_t* copy) {
   if (p_hi <= p_lo) return;
   hipLaunchKernelGGL(gather_rows_mxfp8_kernel, dim3(row_grid(p_hi - p_lo, n_cu)), dim3(RT), 0, s, src, H, inv,
-                     src_div, p_lo, p_hi, ring_rows, codes, scales);
+                     src_div, p_lo, p_hi, ring_rows, codes, scales, copy);
 }
 
 void launch_quantize(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   if (rows <= 0) return;
   hipLaunchKernelGGL(gather_rows_mxfp8_kernel, dim3(row_grid(rows, 256)), dim3(RT), 0, s, in, (int64_t)K,
-                     (const int32_t*)nullptr, 1, (int64_t)0, rows, 0, codes, scales);
+                     (const int32_t*)nullptr, 1, (int64_t)0, rows, 0, codes, scales, (uint16_t*)nullptr);
 }
 
 void launch_zero_dropped_rows(const int32_t* sorted_pos, int64_t R, uint16_t* out, int64_t H, hipStream_t s) {
@@ -333,6 +340,52 @@ void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, in
                       hipStream_t s) {
   hipLaunchKernelGGL(tile_cols_kernel, dim3(N / BT_ROWS, K / BT_K, E), dim3(256), 0, s, src_a, src_b, mode, N, K,
                      out);
+}
+
+// Tiled MXFP8 B from source columns: B[e][n][k] = row(e, k)[n], quantised
+// along k.  Workgroup (n block of 256, k block of 128, e): the 128 source rows'
+// 256-value slices go to LDS (16-byte granules), then each thread gathers a
+// 32-value column segment, quantises it and stores its two code granules and
+// its scale byte in the block.
+__global__ __launch_bounds__(256) void quant_tile_cols_kernel(const uint16_t* __restrict__ src_a,
+                                                              const uint16_t* __restrict__ src_b, int mode, int N,
+                                                              int K, uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  constexpr int LD = MXT_ROWS + 8;            // row stride 528 bytes: 16-byte aligned
+  __shared__ __attribute__((aligned(16))) uint16_t t[MXT_K][LD];
+  const int nt = blockIdx.x, kt = blockIdx.y, e = blockIdx.z, tid = threadIdx.x;
+  const int n0 = nt * MXT_ROWS, k0 = kt * MXT_K;
+  for (int q = tid; q < MXT_K * (MXT_ROWS / 8); q += 256) {
+    const int kk = q / (MXT_ROWS / 8), c = (q % (MXT_ROWS / 8)) * 8;
+    *(u32x4_t*)&t[kk][c] = *(const u32x4_t*)(b_src_row(src_a, src_b, mode, e, k0 + kk, K, N) + n0 + c);
+  }
+  __syncthreads();
+  const int64_t ti = mxt_index(e, nt, kt, N, K);
+  uint8_t* cblk = codes + ti * MXT_CODES;
+  uint8_t* sblk = scales + ti * MXT_SCALES;
+  for (int q = tid; q < MXT_ROWS * (MXT_K / 32); q += 256) {
+    const int r = q % MXT_ROWS, kb = q / MXT_ROWS;
+    u32x4_t v[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int k = kb * 32 + g * 8 + 2 * d;
+        v[g][d] = (uint32_t)t[k][r] | ((uint32_t)t[k + 1][r] << 16);
+      }
+    u32x4_t cc[2];
+    const uint32_t sc = quant_block(v, cc);
+    const int g0 = kb * 2;
+    *(u32x4_t*)(cblk + r * MXT_K + (((g0 ^ tkey(r)) & 7) << 4)) = cc[0];
+    *(u32x4_t*)(cblk + r * MXT_K + ((((g0 + 1) ^ tkey(r)) & 7) << 4)) = cc[1];
+    sblk[r * 4 + kb] = (uint8_t)sc;
+  }
+}
+
+void launch_quant_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
+                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  hipLaunchKernelGGL(quant_tile_cols_kernel, dim3(N / MXT_ROWS, K / MXT_K, E), dim3(256), 0, s, src_a, src_b, mode, N,
+                     K, codes, scales);
 }
 
 void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,

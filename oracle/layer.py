@@ -418,18 +418,32 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols):
         P = np.concatenate([dg, du], axis=1)[:, order]
         out["dX"].append(bf16.round_rne(qd(P) @ c["WPTq"].T)[0])
         out["d_row_w"].append(float(dw[0]))
+    rows_q = {}
+
+    def expert_rows(e):
+        # the rows of expert e: x and dY (bf16) and their MXFP8 forms
+        if e not in rows_q:
+            sel = np.nonzero(re == e)[0]
+            X = bf16.decode(inp["x"][sel]); dY = bf16.decode(inp["dY"][sel])
+            rows_q[e] = (sel, X, dY, qd(X), qd(dY))
+        return rows_q[e]
+
     for key, pairs in (("gate_up", gate_up_rows), ("down", down_cols)):
         for (e, i) in pairs:
-            sel = np.nonzero(re == e)[0]
-            c = expert(e)
-            g, u = fwd_gu(e, sel)
-            _, a, _, dg, du = _dact_mxfp8(qd(bf16.decode(inp["dY"][sel])), c["wdTq"], g, u, w[sel])
+            # feature i only: one column of g, u and dA' (as _dact_mxfp8 computes
+            # them); the weights are quantised per row along H, so the rows
+            # for feature i are quantised alone
+            sel, X, dY, xd, dyq = expert_rows(e)
+            g = xd @ qd(bf16.decode(inp["w_gate"][e, i]))
+            u = xd @ qd(bf16.decode(inp["w_up"][e, i]))
+            dAp = dyq @ qd(bf16.decode(inp["w_down"][e][:, i]))
+            s = sigmoid(g)
+            dA = w[sel] * dAp
             if key == "gate_up":
-                X = bf16.decode(inp["x"][sel])
-                out["dW_gate"].append(dg[:, i] @ X)
-                out["dW_up"].append(du[:, i] @ X)
+                out["dW_gate"].append(bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s))) @ X)
+                out["dW_up"].append(bf16.round_rne(dA * silu(g)) @ X)
             else:
-                out["dW_down"].append(bf16.round_rne(w[sel] * a[:, i]) @ bf16.decode(inp["dY"][sel]))
+                out["dW_down"].append(bf16.round_rne(w[sel] * silu(g) * u) @ dY)
     return {k: np.asarray(v) for k, v in out.items()}
 
 

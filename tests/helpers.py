@@ -9,6 +9,12 @@ from oracle import bf16
 
 BF16_TOL = 2e-2     # max |err| <= 2e-2 * RMS(oracle tensor), bf16 outputs and gradients
 MXFP8_TOL = 6e-2    # same rule for MXFP8 outputs against the MXFP8-emulating oracle
+# dX of the MXFP8 backward: its GEMM's A operand (dg, du) is quantised from a
+# GEMM output, so an implementation that is not bit-identical to the fp64
+# oracle decides some E4M3 codes differently; one flipped code of a large
+# element moves dX by about 8.5% of RMS (reproduced on the CPU by a 2^-16
+# relative perturbation of dA'), so the bound adds one such flip to 6e-2.
+MXFP8_BWD_DX_TOL = 0.12
 ROUTER_W_ATOL = 2e-5
 
 

@@ -61,10 +61,11 @@ def test_workspace_rejects_bad_config():
     with pytest.raises(B.MkError) as ei:
         B.mk_workspace_create(c, 8192, 256, 128, 8, 2)
     assert ei.value.status == B.MK_ERR_CONFIG
+    # a workspace with the backward (bf16 or MXFP8) tiles I by 256
     c = B.mk_config_default(); c.precision = B.MK_MXFP8; c.enable_backward = 1
     with pytest.raises(B.MkError) as ei:
         B.mk_workspace_create(c, 8192, 256, 128, 8, 2)
-    assert ei.value.status == B.MK_ERR_UNSUPPORTED
+    assert ei.value.status == B.MK_ERR_SHAPE
     c = B.mk_config_default(); c.enable_backward = 1
     with pytest.raises(B.MkError) as ei:
         B.mk_workspace_create(c, 8192, 256, 384, 8, 2)

@@ -14,7 +14,8 @@ import torch
 
 import workloads
 from oracle import bf16, layer, mxfp8, route, schedule
-from tests.helpers import (BF16_TOL, MXFP8_TOL, ROUTER_W_ATOL, assert_close, dev, host_bf16, rms, say)
+from tests.helpers import (BF16_TOL, MXFP8_BWD_DX_TOL, MXFP8_TOL, ROUTER_W_ATOL, assert_close, dev, host_bf16,
+                           rms, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -367,6 +368,53 @@ def test_backward_ep_bwd_sampled():
     assert_close(gate, ref["dW_gate"], BF16_TOL, "dW_gate (3 rows)")
     assert_close(up, ref["dW_up"], BF16_TOL, "dW_up (3 rows)")
     assert_close(down, ref["dW_down"], BF16_TOL, "dW_down (3 columns)")
+    L.close()
+
+
+# ----------------------------------------------------- MXFP8 backward --
+def run_backward_mxfp8(inp, MB=0, ring_bytes=256 << 20):
+    sh = inp["shape"]
+    L, out, (x, row_w, packed, ctx) = run_share(inp, precision="mxfp8", MB=MB, ring_bytes=ring_bytes, fwd_ctx=True,
+                                               backward=True)
+    g = L.backward(ctx, x, row_w, packed, dev(inp["dY"]), sh.R)
+    sync()
+    return L, out, g
+
+
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (256, 2)], ids=["one_mb", "mb256_ring2"])
+def test_backward_mxfp8_small8(MB, ring_mbs):
+    inp = share_inputs("small8")
+    sh = inp["shape"]
+    say(f"[backward mxfp8] small8 R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * (sh.H + sh.H // 32)
+    L, out, g = run_backward_mxfp8(inp, MB=MB, ring_bytes=ring)
+    fwd = layer.forward_share_mxfp8(inp)
+    ref = layer.backward_share_mxfp8(inp, fwd)
+    assert_close(host_bf16(out), fwd["out"], MXFP8_TOL, "out (mxfp8 forward)", bf16_out=True)
+    assert_close(host_bf16(g["dX"]), ref["dX"], MXFP8_BWD_DX_TOL, "dX", bf16_out=True)
+    for k in ("dW_gate", "dW_up", "dW_down", "d_row_w"):
+        assert_close(g[k].cpu().numpy(), ref[k], MXFP8_TOL, k)
+    L.close()
+
+
+def test_backward_mxfp8_ep_bwd_sampled():
+    inp = share_inputs("ep_bwd")
+    sh = inp["shape"]
+    say(f"[backward mxfp8] EP share R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096, sampled from experts 3 and 7")
+    L, out, g = run_backward_mxfp8(inp, MB=4096)
+    rng = np.random.default_rng(5)
+    re = inp["row_expert"]
+    rows = np.sort(np.concatenate([rng.choice(np.nonzero(re == e)[0], 12, replace=False) for e in (3, 7)]))
+    pairs = [(3, 5), (7, 2047), (7, 1000)]
+    ref = layer.backward_share_mxfp8_sampled(inp, rows, pairs, pairs)
+    assert_close(host_bf16(g["dX"])[rows], ref["dX"], MXFP8_BWD_DX_TOL, "dX (24 sampled rows)", bf16_out=True)
+    assert_close(g["d_row_w"].cpu().numpy()[rows], ref["d_row_w"], MXFP8_TOL, "d_row_w (24 sampled rows)")
+    gate = np.stack([g["dW_gate"][e, i].cpu().numpy() for e, i in pairs])
+    up = np.stack([g["dW_up"][e, i].cpu().numpy() for e, i in pairs])
+    down = np.stack([g["dW_down"][e, :, i].cpu().numpy() for e, i in pairs])
+    assert_close(gate, ref["dW_gate"], MXFP8_TOL, "dW_gate (3 rows)")
+    assert_close(up, ref["dW_up"], MXFP8_TOL, "dW_up (3 rows)")
+    assert_close(down, ref["dW_down"], MXFP8_TOL, "dW_down (3 columns)")
     L.close()
 
 
