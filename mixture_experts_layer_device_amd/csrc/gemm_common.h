@@ -91,54 +91,75 @@ __device__ __forceinline__ void stage_flush(char* lds, RowDst row_dst) {
 // columns (one slice of I/64, added up later in slice order); dA = w dA';
 // dg = dA u s (1 + g (1 - s)), du = dA silu(g) (bf16, packed like W_gu); and
 // w*a (bf16, the down-projection weight gradient's operand).
+// g and u of the tile (256 rows x 512 packed columns, 2 KiB per row) are
+// brought through LDS in four chunks of 64 rows with coalesced 16-byte loads
+// (the chunk's rows are the fragments 2c and 2c+1 of both row halves); the
+// row stride of 516 floats puts the 4 row groups a fragment read touches on
+// different banks.  LDS must be free on entry (it is after the mainloop) and
+// is free on exit.
 __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, char* lds, int I,
                                               const float* __restrict__ gu, const int32_t* __restrict__ inv,
                                               const float* __restrict__ row_w, uint16_t* __restrict__ dgdu,
                                               uint16_t* __restrict__ wa, float* __restrict__ dw_part) {
   constexpr int FM = G_FM, FN = G_FN;
-  const int slices = I / 64;
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
-  const int slice = (ti.n0 + wn * 64) / 64;
+  constexpr int GS = 516;                       // LDS row stride (floats)
+  float* sg = (float*)lds;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int slices = I / 64, slice = (ti.n0 + wn * 64) / 64;
+  const float* gtile = gu + (int64_t)2 * ti.n0;          // the tile's 512 packed columns
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = frag_row(i, v);
-      const bool valid = r < ti.rows;
-      const int64_t p = ti.pos0 + (valid ? r : 0);
-      const float w = valid ? row_w[inv[p]] : 0.f;
-      float dws = 0.f;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int ii = ti.n0 + frag_col(j);
-        const int gc = 32 * (ii >> 4) + (ii & 15);
-        float g = 0.f, u = 0.f;
-        if (valid) {
-          g = gu[p * 2 * I + gc];
-          u = gu[p * 2 * I + gc + 16];
-        }
-        const float s = sigmoidf_(g);
-        const float sl = g * s;
-        const float aa = sl * u;
-        const float dap = acc[i][j][v];
-        dws += dap * aa;
-        const float da = w * dap;
-        if (valid) {
-          dgdu[p * 2 * I + gc] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
-          dgdu[p * 2 * I + gc + 16] = (uint16_t)f32_to_bf16(da * sl);
-        }
-        stage_put(lds, r, frag_col(j), w * aa);
-      }
-      // fixed butterfly over the 16 lanes that share this row
-      dws += __shfl_xor(dws, 1);
-      dws += __shfl_xor(dws, 2);
-      dws += __shfl_xor(dws, 4);
-      dws += __shfl_xor(dws, 8);
-      if (valid && (lane & 15) == 0) dw_part[p * slices + slice] = dws;
+  for (int c = 0; c < FM / 2; ++c) {
+    for (int q = threadIdx.x; q < 64 * 128; q += G_NT) {
+      const int lr = q >> 7, col = (q & 127) * 4;
+      const int r = (lr >> 5) * 128 + c * 32 + (lr & 31);
+      if (r < ti.rows)
+        *(f32x4_t*)(sg + lr * GS + col) = *(const f32x4_t*)(gtile + (int64_t)(ti.pos0 + r) * 2 * I + col);
     }
-  stage_flush<256>(lds, [&](int r) -> uint16_t* {
-    return r < ti.rows ? wa + (int64_t)(ti.pos0 + r) * I + ti.n0 : nullptr;
-  });
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * c + h;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = frag_row(i, v);
+        const int lr = wm * 32 + h * 16 + 4 * (lane >> 4) + v;
+        const bool valid = r < ti.rows;
+        const int64_t p = ti.pos0 + (valid ? r : 0);
+        const float w = valid ? row_w[inv[p]] : 0.f;
+        float dws = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int f = wn * 64 + j * 16 + (lane & 15);        // feature within the tile
+          const int lc = 32 * (f >> 4) + (f & 15);               // its gate column; up at +16
+          float g = 0.f, u = 0.f;
+          if (valid) {
+            g = sg[lr * GS + lc];
+            u = sg[lr * GS + lc + 16];
+          }
+          const float s = sigmoidf_(g);
+          const float sl = g * s;
+          const float aa = sl * u;
+          const float dap = acc[i][j][v];
+          dws += dap * aa;
+          const float da = w * dap;
+          if (valid) {
+            uint16_t* dst = dgdu + p * 2 * I + 2 * ti.n0 + lc;
+            dst[0] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
+            dst[16] = (uint16_t)f32_to_bf16(da * sl);
+            wa[p * I + ti.n0 + f] = (uint16_t)f32_to_bf16(w * aa);
+          }
+        }
+        // fixed butterfly over the 16 lanes that share this row
+        dws += __shfl_xor(dws, 1);
+        dws += __shfl_xor(dws, 2);
+        dws += __shfl_xor(dws, 4);
+        dws += __shfl_xor(dws, 8);
+        if (valid && (lane & 15) == 0) dw_part[p * slices + slice] = dws;
+      }
+    }
+    __syncthreads();                            // the next chunk reuses the LDS
+  }
 }
 
 // dX tile -> ROWS16: bf16 rows straight to arrival order, dX[inv[p]]; else
