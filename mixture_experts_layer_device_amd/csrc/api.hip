@@ -226,7 +226,7 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   const int first_resident = std::max(0, nb - ring_mbs);
   {
     Phase ph(ws, MK_PH_WGRAD_DOWN, s);
-    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->n_cu, s);
+    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->zero_row, ws->n_cu, s);
   }
   // replay (the reverse walk's share of re-pulling evicted rows): the x rows
   // of the minibatches no longer in the ring (an MXFP8 ring holds codes: all
@@ -241,7 +241,7 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   }
   Phase ph(ws, MK_PH_WGRAD_GU, s);
   launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, replay_mbs, ws->dye, H, I, dW_gate,
-                       dW_up, ws->n_cu, s);
+                       dW_up, ws->zero_row, ws->n_cu, s);
   return check_launch();
 }
 
@@ -318,6 +318,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   const int64_t npos = ws->npos;
   Carver c;
   const size_t o_err = c.take(256);
+  const size_t o_zero = c.take(512);
   const size_t o_cc = c.take((size_t)ws->nb_max * ws->cpm * E * 4);
   const size_t o_mbc = c.take((size_t)ws->nb_max * E * 4);
   const size_t o_mbo = c.take((size_t)ws->nb_max * (E + 1) * 4);
@@ -363,6 +364,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   }
   char* b = (char*)ws->base;
   ws->err = (uint32_t*)(b + o_err);
+  ws->zero_row = (uint16_t*)(b + o_zero);
   ws->chunk_counts = (int32_t*)(b + o_cc);
   ws->mb_counts = (int32_t*)(b + o_mbc);
   ws->mb_offsets = (int32_t*)(b + o_mbo);
@@ -393,8 +395,9 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
       ws->dgdu_s = (uint8_t*)(b + o_gs);
     }
   }
-  // error word starts clear
+  // error word starts clear; the zero row is zero
   launch_fill_u32(ws->err, 0u, 1, nullptr);
+  launch_fill_u32((uint32_t*)ws->zero_row, 0u, 128, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(ws->base);
     delete ws->events;

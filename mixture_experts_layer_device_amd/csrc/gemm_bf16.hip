@@ -38,13 +38,10 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// LDS offset of granule g of tile row r: the NT GEMMs' stages use the tkey
-// swizzle (the tiled B layout's), the weight-gradient stages lds_swz.
+// LDS offset of granule g of tile row r in the NT GEMMs' stages: the tkey
+// swizzle (the tiled B layout's).
 struct SwzT {
   __device__ static int off(int r, int g) { return r * 128 + (((g ^ tkey(r)) & 7) << 4); }
-};
-struct SwzW {
-  __device__ static int off(int r, int g) { return lds_swz(r, g); }
 };
 
 template <typename Swz>
@@ -233,8 +230,16 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t
 
 // ----------------------------------------------------------- weight grads ----
 // C[m, n] = sum over the rows p of expert e of A[p, m] * B[p, n]: both operands
-// are row-major over p, so each loader thread fetches an 8 (rows) x 8 (columns)
-// bf16 block, transposes it in registers and stores 8 K-contiguous granules.
+// are row-major over p (the contraction), i.e. k-major for the MFMA.  A stage
+// holds 64 rows x 256 columns of each operand in LDS exactly as they lie in
+// memory, brought in by the LDS DMA like the other GEMMs' tiles; the MFMA
+// fragments (8 consecutive k of one row m) are then built with the gfx950
+// transpose read ds_read_b64_tr_b16: in each 16-lane group, lanes 4q..4q+3
+// supply the 16 columns of tile row q and lane l receives column l of those
+// 4 rows (measured on gfx950), so two reads give a lane its 8 k.  The 32-byte
+// column chunks of tile row k sit at chunk slot c ^ trkey(k), which puts the
+// 16 rows one read touches on different banks.  Rows past the end of a
+// segment load a zero row.
 // The K loop walks expert e's row segments minibatch by minibatch in reverse
 // (nb-1 .. 0), rows ascending inside each: a fixed order, no atomics.
 struct SegIter {
@@ -264,51 +269,78 @@ struct WgradOperands {
   int ring_rows, first_resident;
   const uint16_t* replay;      // x rows of minibatches < first_resident, at their positions p
   int64_t ldx;
+  const uint16_t* zero;        // 512 zero bytes
 };
 
-template <int MODE>
-__device__ __forceinline__ void wgrad_load(const WgradOperands<MODE>& op, const WgradArgs& w,
-                                           const SegIter& it, int m0, int n0, u32x4_t (&v)[8]) {
-  const int tid = threadIdx.x;
-  const bool isB = tid >= 256;
-  const int lt = tid & 255, mc = lt & 31, kc = lt >> 5;
+__device__ __forceinline__ int trkey(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_t;
+__device__ __forceinline__ v4i16_t lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(__attribute__((address_space(3))) char*)p);
+}
+
+// One K step (64 rows) of the wave's 128 x 64 outputs from k-major tiles.
+__device__ __forceinline__ void mma_stage_kmajor(const char* sA, const char* sB, Acc& acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int g = lane >> 4, r = lane & 15;
+  const int cb = (r & 3) * 8;                  // this lane's 8 bytes of a row's 32-byte chunk
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int kk = it.k0 + kc * 8 + c;
-    if (kk < it.len) {
-      const int64_t p = it.start + kk;
-      const uint16_t* ptr;
-      if (!isB) {
-        ptr = op.A + p * op.lda + m0 + mc * 8;
-      } else if (MODE == 0) {
-        ptr = op.B + p * op.ldb + n0 + mc * 8;
-      } else if (it.b >= op.first_resident) {
-        ptr = op.ring + (int64_t)(p % op.ring_rows) * op.ldx + n0 + mc * 8;
-      } else {
-        ptr = op.replay + p * op.ldx + n0 + mc * 8;
-      }
-      v[c] = *(const u32x4_t*)ptr;
-    } else {
-      v[c] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k1 = ks * 32 + 8 * g + (r >> 2), k2 = k1 + 4;
+    const int t1 = trkey(k1), t2 = trkey(k2);
+    bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = wn * 4 + j;
+      const v4i16_t lo = lds_read_tr(sB + k1 * 512 + ((c ^ t1) << 5) + cb);
+      const v4i16_t hi = lds_read_tr(sB + k2 * 512 + ((c ^ t2) << 5) + cb);
+      bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int c = wm * 8 + i;
+      const v4i16_t lo = lds_read_tr(sA + k1 * 512 + ((c ^ t1) << 5) + cb);
+      const v4i16_t hi = lds_read_tr(sA + k2 * 512 + ((c ^ t2) << 5) + cb);
+      af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void wgrad_store(char* st, const u32x4_t (&v)[8]) {
-  const int tid = threadIdx.x;
-  char* base = st + (tid >= 256 ? TILE_BYTES : 0);
-  const int lt = tid & 255, mc = lt & 31, kc = lt >> 5;
+// LDS-DMA of one stage: wave w fills tile rows 8w .. 8w+7 of each operand, two
+// rows (1 KiB) per instruction; lane i takes row 8w + 2j + i/32 and the
+// 16 bytes of logical chunk (slot ^ trkey(row)) that belong in its slot.
+template <int MODE>
+__device__ __forceinline__ void wgrad_issue(const WgradOperands<MODE>& op, const SegIter& it, int m0, int n0,
+                                            char* st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = lane & 31;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    u32x4_t lo, hi;   // columns 2j and 2j+1, 8 k values each
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t x0 = v[2 * d][j], x1 = v[2 * d + 1][j];
-      lo[d] = (x0 & 0xFFFFu) | (x1 << 16);
-      hi[d] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+    const int k = 8 * wave + 2 * j + (lane >> 5);
+    const int off = ((((s >> 1) ^ trkey(k)) & 15) << 5) + ((s & 1) << 4);
+    const bool live = it.k0 + k < it.len;
+    const int64_t p = it.start + it.k0 + k;
+    const char* a = live ? (const char*)(op.A + p * op.lda + m0) + off : (const char*)op.zero + off;
+    const char* b;
+    if (!live) {
+      b = (const char*)op.zero + off;
+    } else if (MODE == 0) {
+      b = (const char*)(op.B + p * op.ldb + n0) + off;
+    } else if (it.b >= op.first_resident) {
+      b = (const char*)(op.ring + (int64_t)(p % op.ring_rows) * op.ldx + n0) + off;
+    } else {
+      b = (const char*)(op.replay + p * op.ldx + n0) + off;
     }
-    *(u32x4_t*)(base + lds_swz(mc * 8 + 2 * j, kc)) = lo;
-    *(u32x4_t*)(base + lds_swz(mc * 8 + 2 * j + 1, kc)) = hi;
+    char* dst = st + (8 * wave + 2 * j) * 512;
+    g2lds16(a, dst);
+    g2lds16(b, dst + TILE_BYTES);
   }
 }
 
@@ -329,17 +361,16 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
     SegIter cur{w.nb, 0, 0, 0};
     bool have = seg_next(cur, w, e);
     if (have) {
-      u32x4_t v[8];
-      wgrad_load<MODE>(op, w, cur, m0, n0, v);
-      wgrad_store(lds, v);
+      wgrad_issue<MODE>(op, cur, m0, n0, lds);
+      wait_all_mem();
       __syncthreads();
       int stage = 0;
       while (true) {
         SegIter nxt = cur;
         const bool more = seg_next(nxt, w, e);
-        if (more) wgrad_load<MODE>(op, w, nxt, m0, n0, v);
-        mma_stage<SwzW>(lds + stage * STAGE_BYTES, acc);
-        if (more) wgrad_store(lds + (stage ^ 1) * STAGE_BYTES, v);
+        if (more) wgrad_issue<MODE>(op, nxt, m0, n0, lds + (stage ^ 1) * STAGE_BYTES);
+        mma_stage_kmajor(lds + stage * STAGE_BYTES, lds + stage * STAGE_BYTES + TILE_BYTES, acc);
+        wait_all_mem();
         __syncthreads();
         if (!more) break;
         cur = nxt;
@@ -399,15 +430,15 @@ void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wg
 }
 
 void launch_wgrad_down(const WgradArgs& w, const uint16_t* dye, const uint16_t* wa, int H, int I,
-                       float* dW_down, int n_cu, hipStream_t s) {
-  WgradOperands<0> op{dye, H, wa, I, nullptr, 1, 0, nullptr, 0};
+                       float* dW_down, const uint16_t* zero_row, int n_cu, hipStream_t s) {
+  WgradOperands<0> op{dye, H, wa, I, nullptr, 1, 0, nullptr, 0, zero_row};
   hipLaunchKernelGGL(wgrad_kernel<0>, dim3(n_cu), dim3(NT), 0, s, w, op, H, I, I, dW_down, (float*)nullptr);
 }
 
 void launch_wgrad_gate_up(const WgradArgs& w, const uint16_t* dgdu, const uint16_t* ring, int32_t ring_rows,
                           int first_resident, const uint16_t* replay, int H, int I, float* dW_gate, float* dW_up,
-                          int n_cu, hipStream_t s) {
-  WgradOperands<1> op{dgdu, 2 * (int64_t)I, nullptr, 0, ring, ring_rows, first_resident, replay, H};
+                          const uint16_t* zero_row, int n_cu, hipStream_t s) {
+  WgradOperands<1> op{dgdu, 2 * (int64_t)I, nullptr, 0, ring, ring_rows, first_resident, replay, H, zero_row};
   hipLaunchKernelGGL(wgrad_kernel<1>, dim3(n_cu), dim3(NT), 0, s, w, op, 2 * I, H, I, dW_gate, dW_up);
 }
 

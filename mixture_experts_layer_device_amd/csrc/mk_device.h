@@ -50,15 +50,6 @@ __device__ __forceinline__ float e4m3_prescale(float x, float inv_scale) {
 }
 
 
-// XOR swizzle of 16-byte granules in a 128-byte-per-row LDS tile: conflict
-// free for 8 or 16 consecutive rows reading the same logical granule.
-__device__ __forceinline__ int lds_swz(int row, int g) {
-  return row * 128 + ((((g ^ row ^ (row >> 3))) & 7) << 4);
-}
-
-// Inverse of lds_swz inside a row: the logical granule that lands in slot s.
-__device__ __forceinline__ int lds_unswz(int row, int s) { return (s ^ row ^ (row >> 3)) & 7; }
-
 // ---- tiled GEMM B operand ("LDS image" layout) ----------------------------
 //
 // A bf16 B operand B[e][n][k] (N a multiple of 256, K of 64) is stored as

@@ -38,6 +38,7 @@ struct mk_workspace {
   float* y_buf;               // [npos, H] fp32 expert outputs, expert order (full-layer combine)
   uint16_t *dye, *dgdu, *wa;  // backward: [npos, H], [npos, 2I], [npos, I]
   float* dw_part;             // [npos, I/64]
+  uint16_t* zero_row;         // 512 zero bytes (weight-gradient rows past a segment's end)
   uint8_t *dye_c, *dye_s;     // MXFP8 backward: dY rows quantised along H  [npos, H], [npos, H/32]
   uint8_t *dgdu_c, *dgdu_s;   //                 dg/du quantised along 2I   [npos, 2I], [npos, 2I/32]
   float* dz;                  // [ceil(max_rows / k), E]: router logit gradient (and logits)
@@ -140,14 +141,16 @@ struct WgradArgs {
   int src_div;
 };
 // dW_down[e] (H x I) = sum_p dye[p]^T (x) wa[p]
+// (zero_row: 512 zero bytes in device memory, for rows past a segment's end)
 void launch_wgrad_down(const WgradArgs& wa_args, const uint16_t* dye, const uint16_t* wa, int H,
-                       int I, float* dW_down, int n_cu, hipStream_t s);
+                       int I, float* dW_down, const uint16_t* zero_row, int n_cu, hipStream_t s);
 // dW_gate/dW_up[e] (I x H) from dgdu (packed 2I) and the x rows: minibatches
 // b >= first_resident come from the ring, earlier (evicted) ones from replay,
 // the x rows re-gathered at their positions p ([p, H]).
 void launch_wgrad_gate_up(const WgradArgs& wa_args, const uint16_t* dgdu, const uint16_t* ring,
                           int32_t ring_rows, int first_resident, const uint16_t* replay, int H,
-                          int I, float* dW_gate, float* dW_up, int n_cu, hipStream_t s);
+                          int I, float* dW_gate, float* dW_up, const uint16_t* zero_row, int n_cu,
+                          hipStream_t s);
 
 // ---- gemm_mxfp8.hip -----------------------------------------------------
 // gu_save: NULL, or the forward context (g and u in fp32, [p, 2I] packed like W_gu)
