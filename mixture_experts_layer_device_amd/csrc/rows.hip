@@ -72,6 +72,14 @@ __device__ __forceinline__ uint32_t quant_block(const u32x4_t (&v)[4], u32x4_t (
 }
 
 // MXFP8 rows: codes[dst] / scales[dst] <- quantised src row (inv == nullptr: dst row = src row = p).
+// MXFP8 quantise-gather: dst row (p mod ring_rows, or p) <- MX(src row
+// inv[p] / src_div), or src row p with inv == nullptr.  Lane l takes values
+// 8l .. 8l+7 of each 512-value chunk of the row (one 16-byte load, a whole
+// wave reading 1 KiB contiguous), so an MX block of 32 is held by the 4 lanes
+// 4q .. 4q+3: its amax is their maximum (two lane exchanges), every lane
+// converts its own 8 values and stores 8 codes, and the first of the 4 stores
+// the scale.  Four chunks are in flight per lane.  H is a multiple of 32, so
+// a block is never split across the row's end.
 // (copy != nullptr: the bf16 row is also stored there, at row p)
 __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t H,
                                                                const int32_t* __restrict__ inv, int src_div,
@@ -80,7 +88,6 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
                                                                uint8_t* __restrict__ scales,
                                                                uint16_t* __restrict__ copy) {
   const int lane = threadIdx.x & 63;
-  const int64_t nblk = H / 32;
   for (int64_t p = p_lo + wave_id(); p < p_hi; p += wave_count()) {
     int64_t sr = p;
     if (inv) {
@@ -89,23 +96,46 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
       sr = r / src_div;
     }
     const int64_t dr = ring_rows ? p % ring_rows : p;
-    const u32x4_t* s = (const u32x4_t*)(src + sr * H);
-    u32x4_t* dc = (u32x4_t*)(codes + dr * H);
-    uint8_t* ds = scales + dr * nblk;
-    for (int64_t b = lane; b < nblk; b += 64) {
+    const uint16_t* s = src + sr * H;
+    uint8_t* dc = codes + dr * H;
+    uint8_t* ds = scales + dr * (H / 32);
+    for (int64_t c0 = 0; c0 < H; c0 += 4 * 512) {
       u32x4_t v[4];
+      uint32_t am[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = __builtin_nontemporal_load(s + b * 4 + q);
-      if (copy) {
-        u32x4_t* cp = (u32x4_t*)(copy + p * H);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cp[b * 4 + q] = v[q];
+      for (int u = 0; u < 4; ++u) {
+        const int64_t e = c0 + u * 512 + lane * 8;
+        v[u] = e < H ? __builtin_nontemporal_load((const u32x4_t*)(s + e)) : u32x4_t{0u, 0u, 0u, 0u};
       }
-      u32x4_t c[2];
-      const uint32_t sc = quant_block(v, c);
-      dc[b * 2] = c[0];
-      dc[b * 2 + 1] = c[1];
-      ds[b] = (uint8_t)sc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t a = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) a = max(a, max(v[u][d] & 0x7FFFu, (v[u][d] >> 16) & 0x7FFFu));
+        a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+        am[u] = max(a, (uint32_t)__shfl_xor((int)a, 2));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t e = c0 + u * 512 + lane * 8;
+        if (e >= H) continue;
+        const int sc = mx_scale_code(am[u]);
+        // 2^-se as an fp32 power of two (se in [-127, 119]: exponent field 8 .. 254)
+        const float invs = __uint_as_float((uint32_t)(254 - sc) << 23);
+        uint32_t w2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t lo = v[u][2 * h], hi = v[u][2 * h + 1];
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prescale(bf16_to_f32(lo & 0xFFFFu), invs),
+                                                  e4m3_prescale(bf16_to_f32(lo >> 16), invs), 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prescale(bf16_to_f32(hi & 0xFFFFu), invs),
+                                              e4m3_prescale(bf16_to_f32(hi >> 16), invs), w, true);
+          w2[h] = (uint32_t)w;
+        }
+        *(uint2*)(dc + e) = make_uint2(w2[0], w2[1]);
+        if ((lane & 3) == 0) ds[e / 32] = (uint8_t)sc;
+        if (copy) *(u32x4_t*)(copy + p * H + e) = v[u];
+      }
     }
   }
 }
