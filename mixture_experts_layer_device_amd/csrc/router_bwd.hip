@@ -73,22 +73,26 @@ __global__ __launch_bounds__(RT) void router_dz_kernel(const float* __restrict__
   }
 }
 
-// One wave per token; lane handles 8 columns per step.  Row terms in batches
-// of 8 loads in flight, then the router terms: the nonzero dz of each group
-// of 64 experts (a ballot), again 8 rows of W_r in flight per batch.
+// One wave per token; lane l takes columns 4l .. 4l+3 of each 256-column
+// chunk (one 16-byte load per routed row, a wave reading 1 KiB contiguous),
+// two chunks at a time.  Row terms in batches of 8 loads in flight, then the
+// router terms: the nonzero dz of each group of 64 experts (a ballot), again
+// 8 rows of W_r in flight per batch.
 __global__ __launch_bounds__(RT) void dx_combine_kernel(const float* __restrict__ dx32, int64_t H,
                                                         const int32_t* __restrict__ sorted_pos, int k, int64_t T,
                                                         const float* __restrict__ dz,
                                                         const uint16_t* __restrict__ wr, int E,
                                                         uint16_t* __restrict__ dX) {
   const int lane = threadIdx.x & 63;
-  const int64_t n8 = H / 8;
   for (int64_t t = wave_id(); t < T; t += wave_count()) {
     const int pj = lane < k ? sorted_pos[t * k + lane] : -1;
-    for (int64_t g = lane; g < n8; g += 64) {
-      float acc[8];
+    for (int64_t c0 = 0; c0 < H; c0 += 2 * 256) {
+      const bool act1 = c0 + 256 < H;
+      float acc[2][4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[h][q] = 0.f;
       for (int j0 = 0; j0 < k; j0 += 8) {
         f32x4_t v[8][2];
         bool live[8];
@@ -98,19 +102,18 @@ __global__ __launch_bounds__(RT) void dx_combine_kernel(const float* __restrict_
           const int pos = __shfl(pj, j < k ? j : 0);
           live[u] = j < k && pos >= 0;
           if (live[u]) {
-            const f32x4_t* src = (const f32x4_t*)(dx32 + (int64_t)pos * H + g * 8);
-            v[u][0] = __builtin_nontemporal_load(src);
-            v[u][1] = __builtin_nontemporal_load(src + 1);
+            const float* src = dx32 + (int64_t)pos * H + c0 + lane * 4;
+            v[u][0] = __builtin_nontemporal_load((const f32x4_t*)src);
+            v[u][1] = act1 ? __builtin_nontemporal_load((const f32x4_t*)(src + 256)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (!live[u]) continue;   // a dropped row adds nothing
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[q] += v[u][0][q];
-            acc[4 + q] += v[u][1][q];
-          }
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[h][q] += v[u][h][q];
         }
       }
       if (dz) {
@@ -132,26 +135,36 @@ __global__ __launch_bounds__(RT) void dx_combine_kernel(const float* __restrict_
                 e[u] = -1;
               }
             }
-            u32x4_t wv[8];
+            u32x2_t wv[8][2];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-              if (e[u] >= 0) wv[u] = *(const u32x4_t*)(wr + (int64_t)e[u] * H + g * 8);
+              if (e[u] >= 0) {
+                const uint16_t* wrow = wr + (int64_t)e[u] * H + c0 + lane * 4;
+                wv[u][0] = *(const u32x2_t*)wrow;
+                wv[u][1] = act1 ? *(const u32x2_t*)(wrow + 256) : u32x2_t{0u, 0u};
+              }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
               if (e[u] < 0) continue;
 #pragma unroll
-              for (int d = 0; d < 4; ++d) {
-                acc[2 * d] += c[u] * bf16_to_f32(wv[u][d] & 0xFFFFu);
-                acc[2 * d + 1] += c[u] * bf16_to_f32(wv[u][d] >> 16);
-              }
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                  acc[h][2 * d] += c[u] * bf16_to_f32(wv[u][h][d] & 0xFFFFu);
+                  acc[h][2 * d + 1] += c[u] * bf16_to_f32(wv[u][h][d] >> 16);
+                }
             }
           }
         }
       }
-      u32x4_t ov;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) ov[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
-      __builtin_nontemporal_store(ov, (u32x4_t*)(dX + t * H + g * 8));
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !act1) break;
+        u32x2_t ov;
+        ov[0] = pack_bf16x2(acc[h][0], acc[h][1]);
+        ov[1] = pack_bf16x2(acc[h][2], acc[h][3]);
+        __builtin_nontemporal_store(ov, (u32x2_t*)(dX + t * H + c0 + h * 256 + lane * 4));
+      }
     }
   }
 }

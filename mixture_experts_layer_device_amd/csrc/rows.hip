@@ -142,23 +142,26 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
 
 // out[o] = sum_{j < kk} w[o*kk + j] * y[sorted_pos[o*kk + j]], j ascending, fp32,
 // one rounding to bf16 (y is the fp32 GEMM2 output).  A dropped row
-// (sorted_pos -1) adds nothing.
+// (sorted_pos -1) adds nothing.  One wave per output row; lane l takes
+// columns 4l .. 4l+3 of each 256-column chunk (one 16-byte load per routed
+// row, a wave reading 1 KiB contiguous), two chunks at a time, the routed
+// rows' loads issued 8 at a time and summed in row order.
 __global__ __launch_bounds__(RT) void combine_kernel(const float* __restrict__ y, int64_t H,
                                                      const int32_t* __restrict__ sorted_pos,
                                                      const float* __restrict__ row_w, int kk, int64_t n_out,
                                                      uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t n8 = H / 8;
   for (int64_t o = wave_id(); o < n_out; o += wave_count()) {
     // lane j (< kk, kk <= 64) holds the j-th routed row's position and weight
     const int pj = lane < kk ? sorted_pos[o * kk + lane] : -1;
     const float wj = lane < kk ? row_w[o * kk + lane] : 0.f;
-    for (int64_t g = lane; g < n8; g += 64) {
-      float acc[8];
+    for (int64_t c0 = 0; c0 < H; c0 += 2 * 256) {
+      float acc[2][4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      // rows in batches of 8: all loads of a batch in flight, then summed in
-      // row order (the fixed order of the combine)
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[h][q] = 0.f;
+      const bool act1 = c0 + 256 < H;
       for (int j0 = 0; j0 < kk; j0 += 8) {
         f32x4_t v[8][2];
         float wv[8];
@@ -170,29 +173,28 @@ __global__ __launch_bounds__(RT) void combine_kernel(const float* __restrict__ y
           wv[u] = __shfl(wj, j < kk ? j : 0);
           live[u] = j < kk && pos >= 0;
           if (live[u]) {
-            const f32x4_t* src = (const f32x4_t*)(y + (int64_t)pos * H + g * 8);
-            v[u][0] = __builtin_nontemporal_load(src);
-            v[u][1] = __builtin_nontemporal_load(src + 1);
-          } else {
-            v[u][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            v[u][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            wv[u] = 0.f;
+            const float* src = y + (int64_t)pos * H + c0 + lane * 4;
+            v[u][0] = __builtin_nontemporal_load((const f32x4_t*)src);
+            v[u][1] = act1 ? __builtin_nontemporal_load((const f32x4_t*)(src + 256)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (!live[u]) continue;   // a dropped row adds nothing
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[q] += wv[u] * v[u][0][q];
-            acc[4 + q] += wv[u] * v[u][1][q];
-          }
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[h][q] += wv[u] * v[u][h][q];
         }
       }
-      u32x4_t ov;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) ov[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
-      __builtin_nontemporal_store(ov, (u32x4_t*)(out + o * H + g * 8));
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !act1) break;
+        u32x2_t ov;
+        ov[0] = pack_bf16x2(acc[h][0], acc[h][1]);
+        ov[1] = pack_bf16x2(acc[h][2], acc[h][3]);
+        __builtin_nontemporal_store(ov, (u32x2_t*)(out + o * H + c0 + h * 256 + lane * 4));
+      }
     }
   }
 }
