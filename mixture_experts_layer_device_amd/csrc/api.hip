@@ -320,6 +320,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   const size_t o_err = c.take(256);
   const size_t o_zero = c.take(512);
   const size_t o_cc = c.take((size_t)ws->nb_max * ws->cpm * E * 4);
+  const size_t o_cb = c.take((size_t)ws->nb_max * ws->cpm * 4);
   const size_t o_mbc = c.take((size_t)ws->nb_max * E * 4);
   const size_t o_mbo = c.take((size_t)ws->nb_max * (E + 1) * 4);
   const size_t o_cnt = c.take((size_t)E * 4);
@@ -366,6 +367,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   ws->err = (uint32_t*)(b + o_err);
   ws->zero_row = (uint16_t*)(b + o_zero);
   ws->chunk_counts = (int32_t*)(b + o_cc);
+  ws->chunk_bad = (int32_t*)(b + o_cb);
   ws->mb_counts = (int32_t*)(b + o_mbc);
   ws->mb_offsets = (int32_t*)(b + o_mbo);
   ws->counts = (int32_t*)(b + o_cnt);

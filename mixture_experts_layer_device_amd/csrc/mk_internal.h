@@ -31,6 +31,7 @@ struct mk_workspace {
   size_t bytes;
   uint32_t* err;
   int32_t *chunk_counts, *mb_counts, *mb_offsets, *counts, *offsets;
+  int32_t* chunk_bad;         // [nb_max, cpm]: a chunk holds an expert id out of range
   int32_t *sorted_pos, *inv, *items, *mb_items;
   uint8_t* ring;              // bf16 rows, or MXFP8 codes [ring_rows, H] then scales [ring_rows, H/32]
   uint16_t* a_buf;            // [npos, I] bf16 SwiGLU output, expert order

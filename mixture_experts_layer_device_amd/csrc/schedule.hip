@@ -2,10 +2,13 @@
 // the minibatch size (host-known), never from per-expert counts.
 //
 //  count   (minibatch b, chunk c of 256 rows): per-chunk expert histogram in
-//          LDS; also marks every sorted position of the chunk's range empty.
+//          LDS ([b][c][e]), and a flag for a chunk holding an expert id out
+//          of range; also marks every sorted position of the chunk's range
+//          empty.
 //  scan    (one workgroup): per (b, e) prefix over chunks, per-minibatch
-//          expert offsets, global counts/offsets, and the GEMM work items
-//          (one per 256-row m-tile of each (b, e) run) with their offsets.
+//          expert offsets, global counts/offsets, the GEMM work items (one
+//          per 256-row m-tile of each (b, e) run) with their offsets, and the
+//          device error word (written whole: building a schedule clears it).
 //  scatter (b, c): stable rank of each row among the earlier rows of its
 //          chunk with the same expert; sorted_pos and its inverse.
 //
@@ -24,13 +27,15 @@ constexpr int CH = MK_SCHED_CHUNK;
 
 __global__ __launch_bounds__(CH) void sched_count_kernel(const int32_t* __restrict__ row_expert, int R, int E,
                                                          int MB, int cpm, int32_t* __restrict__ chunk_counts,
-                                                         int32_t* __restrict__ inv, uint32_t* __restrict__ err) {
+                                                         int32_t* __restrict__ chunk_bad,
+                                                         int32_t* __restrict__ inv) {
   __shared__ int hist[MK_MAX_EXPERTS];
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < E; e += CH) hist[e] = 0;
   __syncthreads();
   const int off = c * CH + tid;
   const int64_t p = (int64_t)b * MB + off;
+  int bad = 0;
   if (off < MB) {
     inv[p] = -1;
     if (p < R) {
@@ -38,31 +43,46 @@ __global__ __launch_bounds__(CH) void sched_count_kernel(const int32_t* __restri
       if (e >= 0 && e < E)
         atomicAdd(&hist[e], 1);
       else
-        atomicOr(err, MK_DEVERR_EXPERT_RANGE);
+        bad = 1;
     }
   }
-  __syncthreads();
+  bad = __syncthreads_or(bad);
   int32_t* out = chunk_counts + ((int64_t)b * cpm + c) * E;
   for (int e = tid; e < E; e += CH) out[e] = hist[e];
+  if (tid == 0) chunk_bad[b * cpm + c] = bad;
 }
 
 constexpr int SCAN_T = 1024;
 
-// Exclusive scan of one value per thread over the workgroup; *total gets the sum.
+// Exclusive scan of one value per thread over the workgroup; *total gets the
+// sum.  Each wave scans its 64 values with lane shuffles, the 16 wave totals
+// are scanned by wave 0 through LDS.
 __device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
-  const int tid = threadIdx.x;
-  sbuf[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < SCAN_T; o <<= 1) {
-    const int t = tid >= o ? sbuf[tid - o] : 0;
-    __syncthreads();
-    sbuf[tid] += t;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
   }
-  const int incl = sbuf[tid];
-  *total = sbuf[SCAN_T - 1];
+  if (lane == 63) sbuf[wave] = incl;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    const int wt = lane < SCAN_T / 64 ? sbuf[lane] : 0;
+    int wi = wt;
+#pragma unroll
+    for (int o = 1; o < SCAN_T / 64; o <<= 1) {
+      const int t = __shfl_up(wi, o);
+      if (lane >= o) wi += t;
+    }
+    if (lane < SCAN_T / 64) sbuf[SCAN_T / 64 + lane] = wi - wt;   // exclusive wave offsets
+    if (lane == SCAN_T / 64 - 1) sbuf[2 * (SCAN_T / 64)] = wi;    // total
+  }
+  __syncthreads();
+  const int ex = sbuf[SCAN_T / 64 + wave] + incl - v;
+  *total = sbuf[2 * (SCAN_T / 64)];
+  __syncthreads();
+  return ex;
 }
 
 __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int nb, int cpm, int tile_m,
@@ -73,10 +93,15 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ items,
                                                             int32_t* __restrict__ mb_items,
+                                                            const int32_t* __restrict__ chunk_bad,
                                                             uint32_t* __restrict__ err) {
   __shared__ int sbuf[SCAN_T];
   const int tid = threadIdx.x;
   const int nbe = nb * E;
+  // an expert id out of range in any chunk
+  int bad = 0;
+  for (int i = tid; i < nb * cpm; i += SCAN_T) bad |= chunk_bad[i];
+  bad = __syncthreads_or(bad);
   // per (b, e): exclusive prefix over the chunks of minibatch b (in place).
   // SG consecutive lanes share one (b, e) column, each taking a contiguous
   // run of chunks: a batched pass for the run sums, a shuffle scan across the
@@ -188,7 +213,7 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
   }
   if (tid == 0) {
     mb_items[nb] = carry;
-    if (carry > item_cap) atomicOr(err, MK_DEVERR_SCHED_OVERFLOW);
+    *err = (bad ? MK_DEVERR_EXPERT_RANGE : 0u) | (carry > item_cap ? MK_DEVERR_SCHED_OVERFLOW : 0u);
   }
 }
 
@@ -237,13 +262,12 @@ void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 void launch_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, hipStream_t s) {
   const int MB = ws->MB, E = ws->E, cpm = ws->cpm;
   const int nb = R > 0 ? (R + MB - 1) / MB : 0;
-  launch_fill_u32(ws->err, 0u, 1, s);
   if (nb > 0)
     hipLaunchKernelGGL(sched_count_kernel, dim3(cpm, nb), dim3(CH), 0, s, row_expert, R, E, MB, cpm,
-                       ws->chunk_counts, ws->inv, ws->err);
+                       ws->chunk_counts, ws->chunk_bad, ws->inv);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(SCAN_T), 0, s, E, MB, nb, cpm, MK_TILE_M, ws->item_cap,
                      ws->chunk_counts, ws->mb_counts, ws->mb_offsets, ws->counts, ws->offsets, ws->items,
-                     ws->mb_items, ws->err);
+                     ws->mb_items, ws->chunk_bad, ws->err);
   if (nb > 0)
     hipLaunchKernelGGL(sched_scatter_kernel, dim3(cpm, nb), dim3(CH), 0, s, row_expert, R, E, MB, cpm,
                        ws->chunk_counts, ws->mb_offsets, ws->sorted_pos, ws->inv);
