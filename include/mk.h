@@ -123,7 +123,8 @@ int64_t mk_query(const mk_workspace* ws, int32_t what);
  *   x_dev        [T, H] bf16          w_router_dev [E, H] bf16
  *   bias_dev     [E] fp32 or NULL
  *   topk_idx_dev [T, k] int32 (out)   topk_w_dev   [T, k] fp32 (out)
- * MK_ERR_LIMIT if T*k > max_rows.
+ * MK_ERR_LIMIT if T*k > max_rows.  With T = 0 nothing is launched and only
+ * w_router_dev must be non-NULL.
  */
 int mk_route(mk_workspace* ws, const void* x_dev, const void* w_router_dev,
              const float* bias_dev, int32_t T, int32_t* topk_idx_dev, float* topk_w_dev,
@@ -227,7 +228,9 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const floa
  * same rows and mode on this workspace with no other forward in between;
  * packed_dev must have been prepared with for_backward = 1.  MK_ERR_CONFIG if
  * the workspace has no backward buffers;
- * MK_ERR_SHAPE in full-layer mode unless R and MB are multiples of k.
+ * MK_ERR_SHAPE in full-layer mode unless R and MB are multiples of k.  After
+ * an empty schedule (R = 0) only the weight-gradient pointers are read (the
+ * others may be NULL) and the weight gradients are written as zeros.
  */
 int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const void* x_src_dev,
                 const float* row_w_dev, const void* packed_dev, const void* dY_dev,
@@ -251,7 +254,8 @@ int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const v
  * x_dev, w_router_dev, bias_dev (NULL if the router has none), topk_idx_dev and
  * topk_w_dev are the ones mk_route and mk_forward saw; the schedule must be the
  * one built from topk_idx.  Every sum runs in a fixed order: bitwise
- * repeatable.  Errors as mk_backward.
+ * repeatable.  Errors as mk_backward; with T = 0, w_router_dev and
+ * dW_router_dev are still required and dW_router (and d_bias) become zeros.
  */
 int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx_dev, const void* x_dev,
                       const void* w_router_dev, const float* bias_dev, const int32_t* topk_idx_dev,

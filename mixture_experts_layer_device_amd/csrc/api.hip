@@ -143,10 +143,11 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   if (mode != MK_EXPERT_SHARE && mode != MK_FULL_LAYER) return MK_ERR_CONFIG;
   if (!ws->cfg.enable_backward) return MK_ERR_CONFIG;
   const bool mx = ws->cfg.precision == MK_MXFP8;
-  if (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !dW_gate || !dW_up || !dW_down || !d_row_w)
-    return MK_ERR_NULL;
-  const bool full = mode == MK_FULL_LAYER;
   const int H = ws->H, I = ws->I, MB = ws->MB, R = ws->R, nb = ws->nb, k = ws->k, E = ws->E;
+  // an empty schedule reads no row buffer; the weight gradients become zeros
+  if (!dW_gate || !dW_up || !dW_down) return MK_ERR_NULL;
+  if (R > 0 && (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !d_row_w)) return MK_ERR_NULL;
+  const bool full = mode == MK_FULL_LAYER;
   if (full && (R % k || MB % k)) return MK_ERR_SHAPE;
   const int src_div = full ? k : 1;
   const int T = R / src_div;
@@ -442,7 +443,7 @@ int64_t mk_query(const mk_workspace* ws, int32_t what) {
 
 int mk_route(mk_workspace* ws, const void* x, const void* w_router, const float* bias, int32_t T, int32_t* topk_idx,
              float* topk_w, void* stream) {
-  if (!ws || !x || !w_router || !topk_idx || !topk_w) return MK_ERR_NULL;
+  if (!ws || !w_router || (T > 0 && (!x || !topk_idx || !topk_w))) return MK_ERR_NULL;
   if (T < 0) return MK_ERR_SHAPE;
   if ((int64_t)T * ws->k > ws->max_rows) return MK_ERR_LIMIT;
   if (ws->k > ws->E) return MK_ERR_SHAPE;
@@ -607,7 +608,8 @@ int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx, const void* x, cons
                       float* dW_gate, float* dW_up, float* dW_down, float* dW_router, float* d_bias,
                       float* d_topk_w, void* stream) {
   if (!ws) return MK_ERR_NULL;
-  if (!w_router || !topk_idx || !dW_router) return MK_ERR_NULL;
+  if (!ws->have_sched) return MK_ERR_STATE;
+  if (!w_router || !dW_router || (ws->R > 0 && !topk_idx)) return MK_ERR_NULL;
   RouterGrad rg{(const uint16_t*)w_router, bias, topk_idx, dW_router, d_bias};
   return backward_impl(ws, MK_FULL_LAYER, fwd_ctx, x, topk_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_topk_w, &rg,
                        stream);

@@ -120,13 +120,16 @@ def quantized_weights(inp):
     return {"gate": mxfp8.quantize(wg), "up": mxfp8.quantize(wu), "down": mxfp8.quantize(wd)}
 
 
-def forward_share_mxfp8(inp, qw=None):
+def forward_share_mxfp8(inp, qw=None, allow: bool = False):
     """Expert share, MXFP8 mode.
 
     x rows and the gate/up weights are quantised along H, the down weights
     along I (blocks of 32 along each GEMM's K).  g and u are exact products of
     the dequantised operands (fp64); a = silu(g) * u is rounded to bf16 and
     then quantised along I; y = D(a_q) D(W_d)^T; out_rows = w * y.
+    With ``allow`` also out_allow: how far out_rows may move because a is a
+    GEMM output whose E4M3 codes another correct evaluation may decide
+    differently (``qd_spread`` of a, through |W_d|, times |w|).
     """
     x = bf16.decode(inp["x"])
     re = inp["row_expert"]
@@ -139,7 +142,7 @@ def forward_share_mxfp8(inp, qw=None):
     I = wg.shape[1]
     a_bits = np.zeros((R, I), dtype=np.uint16)
     G = np.zeros((R, I)); U = np.zeros((R, I))
-    y = np.zeros((R, H))
+    y = np.zeros((R, H)); y_allow = np.zeros((R, H))
     for e in range(wg.shape[0]):
         sel = np.nonzero(re == e)[0]
         if sel.size == 0:
@@ -150,10 +153,15 @@ def forward_share_mxfp8(inp, qw=None):
         a_bits[sel] = bf16.encode(silu(g) * u)
         ac, as_ = mxfp8.quantize(bf16.decode(a_bits[sel]))
         y[sel] = mxfp8.dequantize(ac, as_) @ wd[e].T
+        if allow:
+            y_allow[sel] = qd_spread(silu(g) * u) @ np.abs(wd[e]).T
     w = inp["row_w"].astype(np.float64)
     out = w[:, None] * y
-    return {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "g": G, "u": U, "y": y, "out": bf16.round_rne(out),
-            "out_exact": out}
+    res = {"x_codes": xc, "x_scales": xs, "a_bits": a_bits, "g": G, "u": U, "y": y, "out": bf16.round_rne(out),
+           "out_exact": out}
+    if allow:
+        res["out_allow"] = np.abs(w)[:, None] * y_allow
+    return res
 
 
 def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool):
@@ -323,6 +331,37 @@ def qd(v):
     return mxfp8.dequantize(*mxfp8.quantize(v))
 
 
+# Relative change of a GEMM output that another correct fp32 evaluation (the
+# block-scaled MFMA sums in their own order, an fp32 SiLU) may bring; about
+# four times what the device shows (near 2^-15).
+DECISION_REL = 2.0 ** -13
+
+
+def qd_spread(v, rel: float = DECISION_REL):
+    """How far D(Q(bf16(v'))) may lie from D(Q(bf16(v))), per element, over all
+    v' with |v'_i - v_i| <= rel |v_i| (v: exact values of a GEMM output that is
+    rounded to bf16 and then MXFP8-quantised along its last axis).  0 where
+    no E4M3 code and no block scale can change.
+
+    bf16 rounding and the E4M3 element rule are monotone, so at one block
+    scale every reachable code lies between those of the interval's two ends;
+    the block scale follows the block's largest magnitude, so it lies between
+    the scales of the two ends' blocks (at most one power of two apart).  The
+    largest distance over both ends at both scales bounds every reachable
+    value.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    ref = qd(bf16.round_rne(v))
+    small = bf16.round_rne(v * (1.0 - rel))
+    big = bf16.round_rne(v * (1.0 + rel))
+    spread = np.zeros_like(v)
+    for sc in (mxfp8.block_scale_codes(small), mxfp8.block_scale_codes(big)):
+        for end in (small, big):
+            d = mxfp8.dequantize(mxfp8.quantize_with_scales(end, sc), sc)
+            spread = np.maximum(spread, np.abs(d - ref))
+    return spread
+
+
 def gu_order(I: int) -> np.ndarray:
     """Order of the 2I gate/up features along the dX GEMM's contraction, as
     indices into [gate (I) | up (I)]: groups of 16 gate features followed by
@@ -334,18 +373,54 @@ def gu_order(I: int) -> np.ndarray:
 
 def _dact_mxfp8(dYq, wdTq, g, u, w):
     """dA' = D(Q_H(dY)) D(Q_H(W_d^T))^T and the SwiGLU backward from the
-    forward's g, u: -> dA', a (exact silu(g) u), dw, dg, du (bf16)."""
+    forward's g, u: -> dA', a (exact silu(g) u), dw, dg, du (bf16), and dg,
+    du before that rounding."""
     dAp = dYq @ wdTq.T
     a = silu(g) * u
     dw = np.einsum("ri,ri->r", dAp, a)
     dA = w[:, None] * dAp
     s = sigmoid(g)
-    dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
-    du = bf16.round_rne(dA * silu(g))
-    return dAp, a, dw, dg, du
+    dgx = dA * u * s * (1.0 + g * (1.0 - s))
+    dux = dA * silu(g)
+    return dAp, a, dw, bf16.round_rne(dgx), bf16.round_rne(dux), dgx, dux
 
 
-def backward_share_mxfp8(inp, fwd=None):
+def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False):
+    """MXFP8 expert backward of routed rows (arrival order) given the
+    forward's g = G and u = U: the rows of ``backward_share_mxfp8`` with
+    dX_rows not rounded (see there).  With ``allow`` also dX_rows_allow: how
+    far dX_rows may move because [dg | du] is a GEMM output whose E4M3 codes
+    another correct evaluation may decide differently (``qd_spread`` through
+    |W_P|)."""
+    dYq = qd(dY)
+    R, H = x.shape
+    E, I, _ = wg.shape
+    order = gu_order(I)
+    dX = np.zeros((R, H)); dw = np.zeros(R); dX_allow = np.zeros((R, H))
+    dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    for e in range(E):
+        sel = np.nonzero(re == e)[0]
+        if sel.size == 0:
+            continue
+        g, u = G[sel], U[sel]
+        _, a, dw[sel], dg, du, dgx, dux = _dact_mxfp8(dYq[sel], qd(wd[e].T), g, u, w[sel])
+        P = np.concatenate([dg, du], axis=1)[:, order]
+        WP = np.concatenate([wg[e], wu[e]], axis=0)[order]          # [2I, H]
+        WPq = qd(WP.T)
+        dX[sel] = qd(P) @ WPq.T
+        if allow:
+            dX_allow[sel] = qd_spread(np.concatenate([dgx, dux], axis=1)[:, order]) @ np.abs(WPq).T
+        xe = x[sel]
+        dWg[e] = dg.T @ xe
+        dWu[e] = du.T @ xe
+        dWd[e] = dY[sel].T @ bf16.round_rne(w[sel, None] * a)
+    res = {"dX_rows": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "d_row_w": dw}
+    if allow:
+        res["dX_rows_allow"] = dX_allow
+    return res
+
+
+def backward_share_mxfp8(inp, fwd=None, allow: bool = False):
     """Expert share backward in MXFP8 mode, loss L = sum_r <dY[r], out_rows[r]>
     with out_rows from forward_share_mxfp8.
 
@@ -358,43 +433,89 @@ def backward_share_mxfp8(inp, fwd=None):
     operands); a = silu(g) u; dw, dA, dg, du (bf16) as in the bf16 backward.
     The weight gradients stay bf16 GEMMs, as in the bf16 backward:
         dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = dY_e^T bf16(w a)_e
+    With ``allow`` also dX_allow (see ``_backward_rows_mxfp8``).
     """
     fwd = forward_share_mxfp8(inp) if fwd is None else fwd
-    x = bf16.decode(inp["x"])
     wg, wu, wd = _weights(inp)
-    re = inp["row_expert"]
-    w = inp["row_w"].astype(np.float64)
-    dY = bf16.decode(inp["dY"])
-    dYq = qd(dY)
-    R, H = x.shape
-    E, I, _ = wg.shape
-    order = gu_order(I)
-    dX = np.zeros((R, H)); dw = np.zeros(R)
-    dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
-    for e in range(E):
-        sel = np.nonzero(re == e)[0]
-        if sel.size == 0:
-            continue
-        g, u = fwd["g"][sel], fwd["u"][sel]
-        _, a, dw[sel], dg, du = _dact_mxfp8(dYq[sel], qd(wd[e].T), g, u, w[sel])
-        P = np.concatenate([dg, du], axis=1)[:, order]
-        WP = np.concatenate([wg[e], wu[e]], axis=0)[order]          # [2I, H]
-        dX[sel] = bf16.round_rne(qd(P) @ qd(WP.T).T)
-        xe = x[sel]
-        dWg[e] = dg.T @ xe
-        dWu[e] = du.T @ xe
-        dWd[e] = dY[sel].T @ bf16.round_rne(w[sel, None] * a)
-    return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "d_row_w": dw}
+    g = _backward_rows_mxfp8(bf16.decode(inp["x"]), inp["row_expert"], inp["row_w"].astype(np.float64),
+                             bf16.decode(inp["dY"]), fwd["g"], fwd["u"], wg, wu, wd, allow)
+    g["dX"] = bf16.round_rne(g.pop("dX_rows"))
+    if allow:
+        g["dX_allow"] = g.pop("dX_rows_allow")
+    return g
+
+
+def _expanded_rows(inp, idx, w):
+    """Routed rows r = t*k + j of the full layer as an expert-share input."""
+    k = idx.shape[1]
+    return {"x": np.repeat(inp["x"], k, axis=0), "w_gate": inp["w_gate"], "w_up": inp["w_up"],
+            "w_down": inp["w_down"], "row_expert": idx.reshape(-1), "row_w": w.reshape(-1)}
+
+
+def forward_full_mxfp8(inp, renorm: int | None = None, allow: bool = False):
+    """Full layer in MXFP8 mode: the router of ``forward_full``, the routed
+    rows r = t*k + j through the MXFP8 expert arithmetic of
+    ``forward_share_mxfp8`` (unweighted y), and the combine of
+    ``forward_full`` (sum over j ascending, one bf16 rounding).  With
+    ``allow`` also out_allow, the sum of the token's rows' allowances."""
+    sh = inp["shape"]
+    x = bf16.decode(inp["x"])
+    idx, w, z = _route(x.astype(np.float32), bf16.decode(inp["w_router"]).astype(np.float32),
+                       inp["bias"], sh.k, sh.renorm if renorm is None else renorm)
+    f = forward_share_mxfp8(_expanded_rows(inp, idx, w), allow=allow)
+    T, H = x.shape
+    out = np.zeros((T, H))
+    yk = f["y"].reshape(T, sh.k, H)
+    for j in range(sh.k):
+        out += w[:, j, None].astype(np.float64) * yk[:, j]
+    res = {"topk_idx": idx, "topk_w": w, "logits": z, "g": f["g"], "u": f["u"], "a_bits": f["a_bits"],
+           "y": f["y"], "out": bf16.round_rne(out), "out_exact": out}
+    if allow:
+        res["out_allow"] = f["out_allow"].reshape(T, sh.k, H).sum(axis=1)
+    return res
+
+
+def backward_full_mxfp8(inp, renorm: int | None = None, router: bool = True, fwd=None, allow: bool = False):
+    """Full-layer backward in MXFP8 mode: ``backward_full`` with the expert
+    part of ``backward_share_mxfp8`` on the routed rows (g, u from
+    ``forward_full_mxfp8``); the k-sum, the router gradient and the single
+    bf16 rounding of dX as in ``backward_full``.  With ``allow`` also
+    dX_allow, the sum of the token's rows' allowances."""
+    sh = inp["shape"]
+    rn = sh.renorm if renorm is None else renorm
+    k = sh.k
+    fwd = forward_full_mxfp8(inp, rn) if fwd is None else fwd
+    idx, w, z = fwd["topk_idx"], fwd["topk_w"], fwd["logits"]
+    x = bf16.decode(inp["x"])
+    wr = bf16.decode(inp["w_router"])
+    wg, wu, wd = _weights(inp)
+    T, H = x.shape
+    g = _backward_rows_mxfp8(np.repeat(x, k, axis=0), idx.reshape(-1), w.reshape(-1).astype(np.float64),
+                             np.repeat(bf16.decode(inp["dY"]), k, axis=0), fwd["g"], fwd["u"], wg, wu, wd, allow)
+    if allow:
+        g["dX_allow"] = g.pop("dX_rows_allow").reshape(T, k, H).sum(axis=1)
+    d_topk_w = g["d_row_w"].reshape(T, k)
+    dXr = g.pop("dX_rows").reshape(T, k, H)
+    dX = np.zeros((T, H))
+    for j in range(k):
+        dX += dXr[:, j]
+    out = dict(g, topk_idx=idx, topk_w=w, logits=z, d_topk_w=d_topk_w)
+    if router:
+        dz = router_logit_grad(z, idx, d_topk_w, rn)
+        dX += dz @ wr
+        out.update(dz=dz, dW_router=dz.T @ x, d_bias=dz.sum(axis=0))
+    out["dX"] = bf16.round_rne(dX)
+    return out
 
 
 def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols):
     """Entries of backward_share_mxfp8 computed one by one (each needs only
-    its own rows, or the rows of one expert)."""
+    its own rows, or the rows of one expert), with dX_allow for the rows."""
     re = inp["row_expert"]
     w = inp["row_w"].astype(np.float64)
     I = inp["w_gate"].shape[1]
     order = gu_order(I)
-    out = {"dX": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
+    out = {"dX": [], "dX_allow": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
     cache = {}
 
     def expert(e):
@@ -414,9 +535,10 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols):
         e = int(re[r])
         c = expert(e)
         g, u = fwd_gu(e, [r])
-        _, _, dw, dg, du = _dact_mxfp8(qd(bf16.decode(inp["dY"][r:r + 1])), c["wdTq"], g, u, w[[r]])
+        _, _, dw, dg, du, dgx, dux = _dact_mxfp8(qd(bf16.decode(inp["dY"][r:r + 1])), c["wdTq"], g, u, w[[r]])
         P = np.concatenate([dg, du], axis=1)[:, order]
         out["dX"].append(bf16.round_rne(qd(P) @ c["WPTq"].T)[0])
+        out["dX_allow"].append((qd_spread(np.concatenate([dgx, dux], axis=1)[:, order]) @ np.abs(c["WPTq"]).T)[0])
         out["d_row_w"].append(float(dw[0]))
     rows_q = {}
 
@@ -487,12 +609,13 @@ def quantized_weights_expert(inp, e):
             "down": mxfp8.quantize(bf16.decode(inp["w_down"][e]))}
 
 
-def forward_share_mxfp8_rows(inp, rows):
-    """forward_share_mxfp8's out (and a) for the given arrival rows only."""
+def forward_share_mxfp8_rows(inp, rows, allow: bool = False):
+    """forward_share_mxfp8's out for the given arrival rows only; with
+    ``allow`` the pair (out, out_allow)."""
     rows = np.asarray(rows)
     re = inp["row_expert"]
     H = inp["x"].shape[1]
-    out = np.zeros((len(rows), H))
+    out = np.zeros((len(rows), H)); out_allow = np.zeros((len(rows), H))
     for e in np.unique(re[rows]):
         q = quantized_weights_expert(inp, int(e))
         wg = mxfp8.dequantize(*q["gate"]); wu = mxfp8.dequantize(*q["up"]); wd = mxfp8.dequantize(*q["down"])
@@ -503,8 +626,11 @@ def forward_share_mxfp8_rows(inp, rows):
         u = xd @ wu.T
         a = bf16.decode(bf16.encode(silu(g) * u))
         ad = mxfp8.dequantize(*mxfp8.quantize(a))
-        out[sel] = inp["row_w"][rows[sel], None].astype(np.float64) * (ad @ wd.T)
-    return bf16.round_rne(out)
+        wr = inp["row_w"][rows[sel], None].astype(np.float64)
+        out[sel] = wr * (ad @ wd.T)
+        if allow:
+            out_allow[sel] = np.abs(wr) * (qd_spread(silu(g) * u) @ np.abs(wd).T)
+    return (bf16.round_rne(out), out_allow) if allow else bf16.round_rne(out)
 
 
 def backward_share_sampled(inp, rows, gate_up_rows, down_cols):

@@ -77,16 +77,20 @@ def block_scale_codes(v: np.ndarray) -> np.ndarray:
     return np.where(amax > 0, se + 127, 0).astype(np.uint8)
 
 
+def quantize_with_scales(v: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Element codes of v [..., K] at the given block scale codes s [..., K/32]."""
+    v = np.asarray(v, dtype=np.float64)
+    *lead, K = v.shape
+    se = np.asarray(s).astype(np.float64) - 127.0
+    scaled = v.reshape(*lead, K // BLOCK, BLOCK) / np.exp2(se)[..., None]
+    return e4m3_encode(scaled).reshape(*lead, K)
+
+
 def quantize(v: np.ndarray):
     """v [..., K] (bf16 values as fp64/fp32) -> (codes [..., K] uint8,
     scales [..., K/32] uint8), blocks of 32 along the last axis."""
-    v = np.asarray(v, dtype=np.float64)
-    *lead, K = v.shape
     s = block_scale_codes(v)
-    se = s.astype(np.float64) - 127.0
-    scaled = v.reshape(*lead, K // BLOCK, BLOCK) / np.exp2(se)[..., None]
-    codes = e4m3_encode(scaled).reshape(*lead, K)
-    return codes, s
+    return quantize_with_scales(v, s), s
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -8,13 +8,10 @@ import torch
 from oracle import bf16
 
 BF16_TOL = 2e-2     # max |err| <= 2e-2 * RMS(oracle tensor), bf16 outputs and gradients
-MXFP8_TOL = 6e-2    # same rule for MXFP8 outputs against the MXFP8-emulating oracle
-# dX of the MXFP8 backward: its GEMM's A operand (dg, du) is quantised from a
-# GEMM output, so an implementation that is not bit-identical to the fp64
-# oracle decides some E4M3 codes differently; one flipped code of a large
-# element moves dX by about 8.5% of RMS (reproduced on the CPU by a 2^-16
-# relative perturbation of dA'), so the bound adds one such flip to 6e-2.
-MXFP8_BWD_DX_TOL = 0.12
+MXFP8_TOL = 6e-2    # same rule for MXFP8 outputs against the MXFP8-emulating oracle; where an
+# MXFP8 operand is quantised from a GEMM output (a in the forward, dg/du in
+# the backward) the oracle also gives each element an allowance for the E4M3
+# codes another correct evaluation may decide differently (``layer.qd_spread``)
 ROUTER_W_ATOL = 2e-5
 
 
@@ -45,15 +42,17 @@ def ulp_bf16(v):
     return np.ldexp(1.0, np.maximum(e, -125) - 8)
 
 
-def assert_close(got, ref, tol, what, bf16_out=False):
+def assert_close(got, ref, tol, what, bf16_out=False, allow=None):
     """max|got - ref| <= tol * RMS(ref).
 
     bf16_out: got and ref are both bf16 tensors (ref = the oracle's value
     rounded once to bf16).  Two correct implementations that round slightly
     different fp32/fp64 sums once can land on adjacent bf16 values, so the rule
     is applied at the output format's resolution: each element's error less
-    one bf16 ulp at the reference value must stay within tol * RMS(ref).  The
-    raw ratio and the share of differing elements are printed alongside."""
+    one bf16 ulp (at the larger of the two magnitudes) must stay within
+    tol * RMS(ref).  allow: a per-element allowance from the oracle (E4M3
+    decisions on GEMM outputs) that is subtracted as well.  The raw ratio,
+    the share of differing elements and the allowance are printed alongside."""
     ref = np.asarray(ref, dtype=np.float64)
     got = np.asarray(got, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -62,13 +61,19 @@ def assert_close(got, ref, tol, what, bf16_out=False):
     d = np.abs(got - ref)
     err = float(np.max(d)) if ref.size else 0.0
     msg = f"  {what}: max|err| = {err:.3e}, RMS(ref) = {r:.3e}, ratio = {err / max(r, 1e-300):.3e} (tol {tol})"
+    a = np.zeros_like(ref) if allow is None else np.broadcast_to(np.asarray(allow, dtype=np.float64), ref.shape)
     if not bf16_out:
-        say(msg)
-        assert err <= tol * r, f"{what}: max|err| {err:.4e} > {tol} * RMS {r:.4e}"
+        ex = float(np.max(np.maximum(d - a, 0.0))) if ref.size else 0.0
+        say(msg + (f"; beyond allowance: {ex / max(r, 1e-300):.3e}" if allow is not None else ""))
+        assert ex <= tol * r, f"{what}: max|err| beyond allowance {ex:.4e} > {tol} * RMS {r:.4e}"
         return
-    u = ulp_bf16(ref)
-    beyond = np.maximum(d - u, 0.0)
+    u = ulp_bf16(np.maximum(np.abs(got), np.abs(ref)))
+    beyond = np.maximum(d - u - a, 0.0)
     ex = float(np.max(beyond)) if ref.size else 0.0
-    say(msg + f"; beyond 1 ulp: {ex / max(r, 1e-300):.3e}; differ: {np.mean(d > 0):.2%}, "
-        f"> 1 ulp: {np.mean(d > u):.4%}")
-    assert ex <= tol * r, f"{what}: error beyond one bf16 ulp {ex:.4e} > {tol} * RMS {r:.4e}"
+    extra = ""
+    if allow is not None and ref.size:
+        extra = (f"; allowance > 0 on {np.mean(a > 0):.1%}, p90 {np.quantile(a, 0.9) / max(r, 1e-300):.2e}"
+                 f", max {np.max(a) / max(r, 1e-300):.2e} of RMS")
+    say(msg + f"; beyond 1 ulp: {np.max(np.maximum(d - u, 0.0)) / max(r, 1e-300) if ref.size else 0:.3e}; "
+        f"differ: {np.mean(d > 0):.2%}, > 1 ulp: {np.mean(d > u):.4%}" + extra)
+    assert ex <= tol * r, f"{what}: error beyond one bf16 ulp and the allowance {ex:.4e} > {tol} * RMS {r:.4e}"

@@ -126,33 +126,152 @@ def test_mxfp8_backward_brute_force_micro():
             np.max(np.abs(dx - ref["dX"][r]) / np.maximum(np.abs(ref["dX"][r]), 1e-30)) <= 2 ** -8
 
 
-def test_mxfp8_backward_dx_bound_covers_one_flipped_code():
-    """The MXFP8 backward's dX tolerance: its GEMM's A operand (dg, du) is
-    quantised from a GEMM output, so a 2^-16 relative change of dA' (far below
-    fp32 accumulation differences over hundreds of terms) already flips E4M3
-    codes and moves dX beyond the forward's 6e-2 * RMS; the bound used for it
-    must cover that and stay well under an error of the operand itself."""
-    from tests.helpers import MXFP8_BWD_DX_TOL, MXFP8_TOL
+def _beyond(got, ref, allow):
+    """Largest excess of |got - ref| over one bf16 ulp (at the larger of the
+    two magnitudes) plus allow."""
+    _, e = np.frexp(np.maximum(np.abs(got), np.abs(ref)))
+    return np.max(np.maximum(np.abs(got - ref) - np.ldexp(1.0, np.maximum(e, -125) - 8) - allow, 0.0))
+
+
+def test_dx_within_decision_allowance_when_dact_changes_slightly(monkeypatch):
+    """dg, du come from a GEMM output, so another correct evaluation decides
+    some of their E4M3 codes differently: with dA' changed by a relative
+    2^-15 (near what the device shows; clipped at 2^-13), dX leaves
+    6e-2 * RMS of the oracle in places, yet every element stays within one
+    bf16 ulp plus the oracle's dX_allow; without the allowance it does not."""
     inp = workloads.make_expert_share("small8")
     fwd = layer.forward_share_mxfp8(inp)
-    ref = layer.backward_share_mxfp8(inp, fwd)
+    ref = layer.backward_share_mxfp8(inp, fwd, allow=True)
     orig = layer._dact_mxfp8
     rng = np.random.default_rng(0)
 
     def perturbed(dYq, wdTq, g, u, w):
-        dAp, a, dw, _, _ = orig(dYq, wdTq, g, u, w)
-        dAp = dAp * (1.0 + 2.0 ** -16 * rng.standard_normal(dAp.shape))
-        s = 1.0 / (1.0 + np.exp(-g))
+        dAp = orig(dYq, wdTq, g, u, w)[0]
+        dAp = dAp * (1.0 + 2.0 ** -15 * np.clip(rng.standard_normal(dAp.shape), -4.0, 4.0))
+        a = layer.silu(g) * u
+        s = layer.sigmoid(g)
         dA = w[:, None] * dAp
-        return dAp, a, dw, bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s))), bf16.round_rne(dA * g * s)
+        dgx = dA * u * s * (1.0 + g * (1.0 - s))
+        dux = dA * layer.silu(g)
+        return dAp, a, np.einsum("ri,ri->r", dAp, a), bf16.round_rne(dgx), bf16.round_rne(dux), dgx, dux
 
-    layer._dact_mxfp8 = perturbed
-    try:
-        alt = layer.backward_share_mxfp8(inp, fwd)
-    finally:
-        layer._dact_mxfp8 = orig
+    monkeypatch.setattr(layer, "_dact_mxfp8", perturbed)
+    alt = layer.backward_share_mxfp8(inp, fwd)
+    monkeypatch.undo()
     r = ref["dX"]
-    _, e = np.frexp(np.abs(r))
-    beyond = np.max(np.maximum(np.abs(alt["dX"] - r) - np.ldexp(1.0, np.maximum(e, -125) - 8), 0.0))
-    ratio = beyond / np.sqrt(np.mean(r ** 2))
-    assert MXFP8_TOL < ratio < MXFP8_BWD_DX_TOL, ratio
+    rms = np.sqrt(np.mean(r ** 2))
+    assert _beyond(alt["dX"], r, 0.0) > 0.06 * rms                # flips exceed the plain bound
+    assert _beyond(alt["dX"], r, ref["dX_allow"]) == 0.0             # and the allowance covers them
+    # not a blanket widening: most elements keep (nearly) the plain bound
+    assert np.quantile(ref["dX_allow"], 0.9) < 0.01 * rms
+
+
+def test_out_within_decision_allowance_when_a_changes_slightly():
+    """The forward's a = silu(g) u is a GEMM output quantised to MXFP8: a
+    changed by a relative 2^-15 (clipped at 2^-13) moves out_rows by more than
+    6e-2 * RMS in places, but within one bf16 ulp plus out_allow everywhere."""
+    inp = workloads.make_expert_share("small8")
+    ref = layer.forward_share_mxfp8(inp, allow=True)
+    rng = np.random.default_rng(1)
+    qw = layer.quantized_weights(inp)
+    wd = mxfp8.dequantize(*qw["down"])
+    a = layer.silu(ref["g"]) * ref["u"]
+    a = a * (1.0 + 2.0 ** -15 * np.clip(rng.standard_normal(a.shape), -4.0, 4.0))
+    aq = layer.qd(bf16.round_rne(a))
+    re = inp["row_expert"]
+    y = np.zeros_like(ref["y"])
+    for e in range(wd.shape[0]):
+        sel = np.nonzero(re == e)[0]
+        y[sel] = aq[sel] @ wd[e].T
+    alt = bf16.round_rne(inp["row_w"][:, None].astype(np.float64) * y)
+    r = ref["out"]
+    rms = np.sqrt(np.mean(r ** 2))
+    assert _beyond(alt, r, 0.0) > 0.06 * rms
+    assert _beyond(alt, r, ref["out_allow"]) == 0.0
+    assert np.quantile(ref["out_allow"], 0.9) < 0.01 * rms
+
+
+def test_qd_spread_bounds_every_reachable_value():
+    """qd_spread against brute force: random values (some on E4M3 code
+    boundaries, some blocks with their largest element at a power of two)
+    moved within rel, element by element, all at once to either end, and at
+    random; every result lies within the spread.  rel = 0 gives 0."""
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((64, 128))
+    # exact E4M3 midpoints at the block scale (bf16 values), and amax at 2^k
+    v[:8, ::7] = (1.0 + 1.0 / 16.0) * 2.0 ** rng.integers(-3, 3, v[:8, ::7].shape)
+    v[8:16, 0] = 2.0; v[8:16, 1:32] = np.clip(v[8:16, 1:32], -1.9, 1.9)
+    v[16:24, 0] = 2.0 * (1.0 - 2.0 ** -9)
+    rel = 2.0 ** -9
+    assert np.all(layer.qd_spread(v, 0.0) == 0.0)
+    sp = layer.qd_spread(v, rel)
+    ref = layer.qd(bf16.round_rne(v))
+    assert np.mean(sp > 0) > 0.01
+    tries = [v * (1 - rel), v * (1 + rel)]
+    tries += [v * (1 + rel * rng.uniform(-1, 1, v.shape)) for _ in range(20)]
+    tries += [v * (1 + rel * rng.choice([-1.0, 1.0], v.shape)) for _ in range(20)]
+    for t in tries:
+        d = np.abs(layer.qd(bf16.round_rne(t)) - ref)
+        assert np.all(d <= sp), np.max(d - sp)
+
+
+# ------------------------------------------------------ full layer, MXFP8 --
+def _full(name="tiny", **over):
+    import dataclasses
+    sh = workloads.FULL_LAYER[name]
+    return workloads.make_full_layer(dataclasses.replace(sh, **over) if over else sh)
+
+
+def _identity_quantiser(monkeypatch):
+    monkeypatch.setattr(mxfp8, "quantize", lambda v: (np.asarray(v, dtype=np.float64), None))
+    monkeypatch.setattr(mxfp8, "dequantize", lambda c, s: c)
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_full_layer_identity_quantiser_gives_the_bf16_layer(monkeypatch, renorm):
+    """With Q = identity the MXFP8 full layer is the bf16 full layer (pinned by
+    autograd and finite differences), forward and backward with the router."""
+    inp = _full(renorm=renorm, bias_var=0.5)
+    _identity_quantiser(monkeypatch)
+    mf = layer.forward_full_mxfp8(inp)
+    mb = layer.backward_full_mxfp8(inp, fwd=mf)
+    monkeypatch.undo()
+    bf = layer.forward_full(inp)
+    bb = layer.backward_full(inp)
+    assert np.array_equal(mf["topk_idx"], bf["topk_idx"])
+    assert np.allclose(mf["out_exact"], bf["out_exact"], rtol=1e-11, atol=1e-12)
+    for k in ("dW_gate", "dW_up", "dW_down", "d_topk_w", "dz", "dW_router", "d_bias"):
+        assert np.allclose(mb[k], bb[k], rtol=1e-10, atol=1e-12), k
+    d = np.abs(mb["dX"] - bb["dX"])
+    _, e = np.frexp(np.abs(bb["dX"]))
+    assert np.all(d <= np.ldexp(1.0, np.maximum(e, -125) - 8)) and np.mean(d > 0) < 1e-3
+
+
+def test_full_layer_scaling_one_token_dy_scales_only_that_token():
+    """dY enters linearly and every quantised operand derived from it is
+    blocked along its own row, so a power-of-two factor on one token's dY
+    scales exactly that token's dX, d_topk_w and logit gradient."""
+    inp = dict(_full(renorm=1, bias_var=0.5))
+    fwd = layer.forward_full_mxfp8(inp)
+    base = layer.backward_full_mxfp8(inp, fwd=fwd)
+    t = 77
+    dY = bf16.decode(inp["dY"]).copy()
+    dY[t] *= 0.25
+    inp["dY"] = bf16.encode(dY)
+    m = layer.backward_full_mxfp8(inp, fwd=fwd)
+    for k in ("dX", "d_topk_w", "dz"):
+        assert np.array_equal(m[k][t], 0.25 * base[k][t]), k
+        others = np.arange(base[k].shape[0]) != t
+        assert np.array_equal(m[k][others], base[k][others]), k
+
+
+def test_full_layer_mxfp8_within_e4m3_error_of_bf16():
+    inp = _full()
+    mf = layer.forward_full_mxfp8(inp)
+    mb = layer.backward_full_mxfp8(inp, fwd=mf)
+    bf = layer.forward_full(inp)
+    bb = layer.backward_full(inp)
+    assert 5e-3 < np.linalg.norm(mf["out_exact"] - bf["out_exact"]) / np.linalg.norm(bf["out_exact"]) < 0.12
+    for k in ("dX", "dW_gate", "dW_up", "dW_down", "d_topk_w", "dW_router", "d_bias"):
+        rel = np.linalg.norm(mb[k] - bb[k]) / np.linalg.norm(bb[k])
+        assert 5e-3 < rel < 0.12, (k, rel)
