@@ -110,12 +110,19 @@ __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, cha
   const float* gtile = gu + (int64_t)2 * ti.n0;          // the tile's 512 packed columns
 #pragma unroll
   for (int c = 0; c < FM / 2; ++c) {
-    for (int q = threadIdx.x; q < 64 * 128; q += G_NT) {
-      const int lr = q >> 7, col = (q & 127) * 4;
+    // 64 rows x 512 floats through the LDS DMA, each row as two 1 KiB halves,
+    // 16 per wave, all in flight together; rows past the item's end are
+    // skipped (their LDS is never read).  The copies write no registers, so
+    // the loop issues them back to back without unrolling.
+#pragma unroll 1
+    for (int k = 0; k < 16; ++k) {
+      const int idx = wave * 16 + k;
+      const int lr = idx >> 1, half = idx & 1;
       const int r = (lr >> 5) * 128 + c * 32 + (lr & 31);
       if (r < ti.rows)
-        *(f32x4_t*)(sg + lr * GS + col) = *(const f32x4_t*)(gtile + (int64_t)(ti.pos0 + r) * 2 * I + col);
+        g2lds16(gtile + (int64_t)(ti.pos0 + r) * 2 * I + half * 256 + lane * 4, lds + (lr * GS + half * 256) * 4);
     }
+    wait_all_mem();
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
