@@ -44,26 +44,28 @@ struct SwzT {
   __device__ static int off(int r, int g) { return r * 128 + (((g ^ tkey(r)) & 7) << 4); }
 };
 
-template <typename Swz>
-__device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const char* sA = st;
-  const char* sB = st + TILE_BYTES;
+// A stage is consumed in 8 groups of 8 MFMAs: group q takes A fragments
+// 2(q & 3) and 2(q & 3) + 1 of k half q >> 2 against that half's 4 B
+// fragments.
+__device__ __forceinline__ void read_a_pair(const char* st, int q, bf16x8_t (&a)[2]) {
+  const int lane = threadIdx.x & 63, wm = threadIdx.x >> 8;
+  const int g = (q >> 2) * 4 + (lane >> 4);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int g = ks * 4 + (lane >> 4);
-    bf16x8_t af[FM], bfr[FN];
+  for (int ii = 0; ii < 2; ++ii)
+    a[ii] = *(const bf16x8_t*)(st + SwzT::off(wm * 128 + (2 * (q & 3) + ii) * 16 + (lane & 15), g));
+}
+__device__ __forceinline__ void read_b_half(const char* st, int ks, bf16x8_t (&b)[FN]) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
+  const int g = ks * 4 + (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)(sA + Swz::off(wm * 128 + i * 16 + (lane & 15), g));
+  for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8_t*)(st + TILE_BYTES + SwzT::off(wn * 64 + j * 16 + (lane & 15), g));
+}
+__device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t (&b)[FN], int pair, Acc& acc) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *(const bf16x8_t*)(sB + Swz::off(wn * 64 + j * 16 + (lane & 15), g));
+  for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  }
+    for (int j = 0; j < FN; ++j)
+      acc[2 * pair + ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ii], b[j], acc[2 * pair + ii][j], 0, 0, 0);
 }
 
 // C[256 x 256] = A[256 x K] * B[256 x K]^T.  arow(r) returns a pointer to
@@ -74,22 +76,26 @@ __device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
 // instruction; for A each lane reads the granule that the swizzle puts in its
 // slot, for B the copy is 1 KiB contiguous.
 template <typename ARow>
-__device__ __forceinline__ void mainloop_nt(ARow arow, const uint16_t* btile, int K, char* lds, Acc& acc) {
+__device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const uint16_t* btile, int K, char* lds,
+                                            Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const char* ap[4];
+  // A rows and the B blocks through buffer resources: A offsets from abase
+  // (every row arow returns lies within 4 GiB after it), B from btile
+  const buf_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(btile);
+  uint32_t ao[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = wave * 32 + j * 8 + (lane >> 3);
-    ap[j] = (const char*)arow(r) + (((lane & 7) ^ tkey(r)) & 7) * 16;
+    ao[j] = (uint32_t)((const char*)arow(r) - (const char*)abase) + (((lane & 7) ^ tkey(r)) & 7) * 16;
   }
   const int wbase = wave * 4096;
-  const char* bp = (const char*)btile + wbase + lane * 16;
+  const uint32_t bo = wbase + lane * 16;
   auto issue = [&](int64_t kb, char* st) {
-    const char* b = bp + kb / (BK * 2) * TILE_BYTES;
+    const uint32_t b = bo + (uint32_t)(kb / (BK * 2)) * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      g2lds16(ap[j] + kb, st + wbase + j * 1024);
-      g2lds16(b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
+      b2lds16(ra, ao[j] + (uint32_t)kb, st + wbase + j * 1024);
+      b2lds16(rb, b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
     }
   };
   zero_acc(acc);
@@ -97,12 +103,36 @@ __device__ __forceinline__ void mainloop_nt(ARow arow, const uint16_t* btile, in
   wait_all_mem();
   __syncthreads();
   const int KT = K / BK;
+  // Fragments are read one group ahead of the MFMAs that use them (the
+  // compiler, left alone, reuses one pair of registers and waits for every
+  // read).  The stage's barrier sits before its last group, so the first
+  // reads of the next stage are in flight while that group's MFMAs issue.
+  // Scheduling barriers keep each group's reads ahead of the MFMAs before it.
+  bf16x8_t bq[2][FN], aq[2][2];
+  read_b_half(lds, 0, bq[0]);
+  read_a_pair(lds, 0, aq[0]);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
+    const char* st = lds + cur * STAGE_BYTES;
+    const char* nst = lds + (cur ^ 1) * STAGE_BYTES;
     if (kt + 1 < KT) issue((int64_t)(kt + 1) * BK * 2, lds + (cur ^ 1) * STAGE_BYTES);
-    mma_stage<SwzT>(lds + cur * STAGE_BYTES, acc);
-    wait_all_mem();
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q < 7) {
+        if (q == 3) read_b_half(st, 1, bq[1]);
+        read_a_pair(st, q + 1, aq[(q + 1) & 1]);
+      } else {
+        wait_all_mem();
+        __syncthreads();
+        if (kt + 1 < KT) {
+          read_b_half(nst, 0, bq[0]);
+          read_a_pair(nst, 0, aq[0]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma_group(aq[q & 1], bq[q >> 2], q & 3, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -123,7 +153,7 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
       return ring + (int64_t)(p % ring_rows) * H;
     };
     Acc acc;
-    mainloop_nt(arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H), H, lds, acc);
+    mainloop_nt(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H), H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
     Acc acc;
-    mainloop_nt(arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
+    mainloop_nt(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -204,7 +234,7 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dye + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * H; };
     Acc acc;
-    mainloop_nt(arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, lds, acc);
+    mainloop_nt(arow(0), arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, lds, acc);
     dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
   });
 }
@@ -223,7 +253,7 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dgdu + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * 2 * I; };
     Acc acc;
-    mainloop_nt(arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, lds, acc);
+    mainloop_nt(arow(0), arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, lds, acc);
     dx_epilogue<ROWS16>(ti, acc, lds, H, inv, dX, dx32);
   });
 }

@@ -98,4 +98,17 @@ __device__ __forceinline__ void g2lds4(const void* src, char* wave_dst) {
 }
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// The same copy through a buffer resource (buffer_load_dwordx4 ... lds):
+// lane i's 16 bytes from base + voff land at dst + 16 i.  Unlike the global
+// form, the compiler counts these on the vector-memory counter alone, so LDS
+// reads issued after them can still be waited for one by one.  Offsets are
+// 32-bit: every byte a kernel reads this way lies within 4 GiB of base.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void b2lds16(buf_rsrc_t r, uint32_t voff, char* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_dst, 16, voff, 0, 0, 0);
+}
+
 }  // namespace mk
