@@ -26,68 +26,61 @@ constexpr int LDS_BYTES = 2 * STAGE_BYTES > STAGE_LDS_BYTES ? 2 * STAGE_BYTES : 
 
 typedef GAcc Acc;
 
-__device__ __forceinline__ void mma_stage(const char* st, Acc& acc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const char* sA = st;
-  const char* sB = st + TILE_BYTES;
-  const uint32_t* scA = (const uint32_t*)(st + 2 * TILE_BYTES);
-  const uint32_t* scB = scA + BM;
-  const int g = lane >> 4;
-  i32x8_t bfr[FN];
-  int sb[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int row = wn * 64 + j * 16 + (lane & 15);
-    const u32x4_t lo = *(const u32x4_t*)(sB + tswz(row, g));
-    const u32x4_t hi = *(const u32x4_t*)(sB + tswz(row, g + 4));
-    bfr[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    sb[j] = (int)((scB[row] >> (8 * g)) & 0xFFu);
-  }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = wm * 128 + i * 16 + (lane & 15);
-    const u32x4_t lo = *(const u32x4_t*)(sA + tswz(row, g));
-    const u32x4_t hi = *(const u32x4_t*)(sA + tswz(row, g + 4));
-    const i32x8_t af = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    const int sa = (int)((scA[row] >> (8 * g)) & 0xFFu);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[j], acc[i][j], 0, 0, 0, sa, 0, sb[j]);
-  }
+// Fragment i of A (wave rows) or j of B (wave columns) with its scale byte.
+__device__ __forceinline__ void read_frag_mx(const char* codes, const uint32_t* sc, int row, i32x8_t& f, int& s) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const u32x4_t lo = *(const u32x4_t*)(codes + tswz(row, g));
+  const u32x4_t hi = *(const u32x4_t*)(codes + tswz(row, g + 4));
+  f = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  s = (int)((sc[row] >> (8 * g)) & 0xFFu);
+}
+__device__ __forceinline__ void read_a_mx(const char* st, int i, i32x8_t& f, int& s) {
+  const int wm = threadIdx.x >> 8;
+  read_frag_mx(st, (const uint32_t*)(st + 2 * TILE_BYTES), wm * 128 + i * 16 + (threadIdx.x & 15), f, s);
+}
+__device__ __forceinline__ void read_b_mx(const char* st, int j, i32x8_t& f, int& s) {
+  const int wn = (threadIdx.x >> 6) & 3;
+  read_frag_mx(st + TILE_BYTES, (const uint32_t*)(st + 2 * TILE_BYTES) + BM, wn * 64 + j * 16 + (threadIdx.x & 15), f,
+               s);
 }
 
-// C = A . B^T over K codes.  arow / ascale give A's code row and scale row;
-// B comes in the tiled MXFP8 layout: bcodes / bscales point at this tile's
+// C = A . B^T over K codes.  arow / ascale give A's code row and scale row
+// (abase / asbase: bases that every such row lies within 4 GiB after); B
+// comes in the tiled MXFP8 layout: bcodes / bscales point at this tile's
 // K / 128 code blocks (each the LDS image of a stage's B slice) and scale
-// blocks.  Codes go global -> LDS directly as in the bf16 mainloop (A: each
-// lane fetches the granule the swizzle puts in its slot; B: 1 KiB contiguous
-// copies); waves 0-3 also fetch A's scale dwords (64 rows each) and waves
-// 4-7 B's.
+// blocks.  Codes go to LDS by the buffer-resource DMA as in the bf16 K loop
+// (A: each lane fetches the granule the swizzle puts in its slot; B: 1 KiB
+// contiguous copies); waves 0-3 also fetch A's scale dwords (64 rows each)
+// and waves 4-7 B's.  A stage's B fragments are read at its start and its A
+// fragments one ahead of the 4 MFMAs that use them.
 template <typename ARow, typename ASc>
-__device__ __forceinline__ void mainloop(ARow arow, ASc ascale, const uint8_t* bcodes, const uint8_t* bscales,
-                                         int K, char* lds, Acc& acc) {
+__device__ __forceinline__ void mainloop(const void* abase, ARow arow, const void* asbase, ASc ascale,
+                                         const uint8_t* bcodes, const uint8_t* bscales, int K, char* lds,
+                                         Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint8_t* ap[4];
+  const buf_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bcodes);
+  const buf_rsrc_t rs = make_rsrc(wave_uniform(wave < 4 ? asbase : (const void*)bscales));
+  uint32_t ao[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = wave * 32 + j * 8 + (lane >> 3);
-    ap[j] = arow(r) + (((lane & 7) ^ tkey(r)) & 7) * 16;
+    ao[j] = (uint32_t)(arow(r) - (const uint8_t*)abase) + (((lane & 7) ^ tkey(r)) & 7) * 16;
   }
   const int wbase = wave * 4096;
-  const uint8_t* bp = bcodes + wbase + lane * 16;
-  const uint8_t* sp = wave < 4 ? ascale(wave * 64 + lane) : bscales + (wave - 4) * 256 + lane * 4;
-  const int sstep = wave < 4 ? 4 : MXT_SCALES;     // bytes between K steps in the scale source
+  const uint32_t bo = wbase + lane * 16;
+  const uint32_t so = wave < 4 ? (uint32_t)(ascale(wave * 64 + lane) - (const uint8_t*)asbase)
+                               : (uint32_t)((wave - 4) * 256 + lane * 4);
+  const uint32_t sstep = wave < 4 ? 4 : MXT_SCALES;     // bytes between K steps in the scale source
   const int sbase = 2 * TILE_BYTES + wave * 256;
   auto issue = [&](int kt, char* st) {
-    const int64_t kb = (int64_t)kt * BKB;
-    const uint8_t* b = bp + (int64_t)kt * MXT_CODES;
+    const uint32_t kb = (uint32_t)kt * BKB;
+    const uint32_t b = bo + (uint32_t)kt * MXT_CODES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      g2lds16(ap[j] + kb, st + wbase + j * 1024);
-      g2lds16(b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
+      b2lds16(ra, ao[j] + kb, st + wbase + j * 1024);
+      b2lds16(rb, b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
     }
-    g2lds4(sp + (int64_t)kt * sstep, st + sbase);
+    b2lds4(rs, so + (uint32_t)kt * sstep, st + sbase);
   };
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -99,8 +92,23 @@ __device__ __forceinline__ void mainloop(ARow arow, ASc ascale, const uint8_t* b
   const int KT = K / BKB;
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
+    const char* st = lds + cur * STAGE_BYTES;
     if (kt + 1 < KT) issue(kt + 1, lds + (cur ^ 1) * STAGE_BYTES);
-    mma_stage(lds + cur * STAGE_BYTES, acc);
+    i32x8_t bq[FN], aq[2];
+    int sbq[FN], saq[2];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) read_b_mx(st, j, bq[j], sbq[j]);
+    read_a_mx(st, 0, aq[0], saq[0]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i + 1 < FM) read_a_mx(st, i + 1, aq[(i + 1) & 1], saq[(i + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[i & 1], bq[j], acc[i][j], 0, 0, 0,
+                                                                     saq[i & 1], 0, sbq[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_all_mem();
     __syncthreads();
   }
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uin
     auto asc = [&](int r) { return rsc + rrow(r) * nbh; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, 2 * I, H);
     Acc acc;
-    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
+    mainloop(rc, arow, rsc, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(NT) void gemm2_mxfp8_kernel(ItemRange ir, const uin
     auto asc = [&](int r) { return asc_ + prow(r) * nbi; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, H, I);
     Acc acc;
-    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, I, lds, acc);
+    mainloop(arow(0), arow, asc(0), asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, I, lds, acc);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(NT) void bwd_dact_mxfp8_kernel(ItemRange ir, const 
     auto asc = [&](int r) { return dys + prow(r) * nbh; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, I, H);
     Acc acc;
-    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
+    mainloop(arow(0), arow, asc(0), asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
     dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
   });
 }
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(NT) void bwd_dx_mxfp8_kernel(ItemRange ir, const ui
     auto asc = [&](int r) { return gs_ + prow(r) * nbk; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, H, 2 * I);
     Acc acc;
-    mainloop(arow, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, 2 * I, lds, acc);
+    mainloop(arow(0), arow, asc(0), asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, 2 * I, lds, acc);
     dx_epilogue<ROWS16>(ti, acc, lds, H, inv, dX, dx32);
   });
 }

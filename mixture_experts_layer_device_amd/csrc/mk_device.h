@@ -110,5 +110,16 @@ __device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base) {
 __device__ __forceinline__ void b2lds16(buf_rsrc_t r, uint32_t voff, char* wave_dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_dst, 16, voff, 0, 0, 0);
 }
+__device__ __forceinline__ void b2lds4(buf_rsrc_t r, uint32_t voff, char* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_dst, 4, voff, 0, 0, 0);
+}
+// A pointer that is the same in every lane of the wave, made visibly uniform
+// (so that a buffer resource built from it stays in scalar registers).
+__device__ __forceinline__ const void* wave_uniform(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
 
 }  // namespace mk
