@@ -306,8 +306,22 @@ __device__ __forceinline__ int trkey(int k) { return (k & 3) | (((k >> 3) & 3) <
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_t;
+// The transposing read as inline assembly: issued through the builtin, the
+// compiler cannot tell it apart from the LDS-DMA writes in flight to the
+// other stage and waits for all of them (vmcnt(0)) before the first read of
+// every stage, which serialises the prefetch.  Written here, it is not
+// tracked: the caller waits for the LDS counter itself (mma_stage_kmajor),
+// and the stage it reads was completed by the previous barrier.
 __device__ __forceinline__ v4i16_t lds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(__attribute__((address_space(3))) char*)p);
+  v4i16_t v;
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+__device__ __forceinline__ void wait_lds_pinned() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One K step (64 rows) of the wave's 128 x 64 outputs from k-major tiles.
@@ -335,6 +349,7 @@ __device__ __forceinline__ void mma_stage_kmajor(const char* sA, const char* sB,
       const v4i16_t hi = lds_read_tr(sA + k2 * 512 + ((c ^ t2) << 5) + cb);
       af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+    wait_lds_pinned();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
