@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # dense MFMA flop/s
 PEAK_FP8 = 5.0e15
+PEAK_FP32_VALU = 157.3e12  # vector fp32 flop/s (published; counts packed FMA)
 METRIC = "MoE layer routed rows/s + grouped-GEMM TFLOP/s (fwd/bwd, bf16 & MXFP8), 1 GPU"
 
 
@@ -88,6 +89,16 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
             # logit gradient + dW_router = dz^T x (k nonzeros per token) + d_bias
             w["router_bwd"] = (2.0 * R * H, T * k * 12 + T * E * 4 * 2 + T * H * 2 + E * H * 4)
     return w
+
+
+def roofline_alu(flops, nbytes, ms):
+    """Vector-ALU work (the router's fp32 FMA chains): against the fp32 vector
+    peak unless HBM takes longer."""
+    if nbytes / PEAK_HBM > flops / PEAK_FP32_VALU:
+        return roofline(0.0, nbytes, ms)
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_FP32_VALU / 1e12, "unit": "TFLOP/s",
+            "frac": round(ach / (PEAK_FP32_VALU / 1e12), 4)}
 
 
 def roofline(flops, nbytes, ms, mx=False):
@@ -200,7 +211,9 @@ def main():
         for p, (ms, n) in per.items():
             f, b = work.get(p, (0.0, 0.0))
             ent = {"ms": round(ms, 4), "launches": n}
-            if f or b:
+            if p == "route":
+                ent["roofline"] = roofline_alu(f, b, ms)
+            elif f or b:
                 ent["roofline"] = roofline(f, b, ms, mx=mx and p in ("gemm1", "gemm2", "bwd_dact", "bwd_dx"))
             phases[p] = ent
             if f and p not in ("route", "bwd_combine", "router_bwd"):
