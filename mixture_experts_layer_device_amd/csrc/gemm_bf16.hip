@@ -334,27 +334,34 @@ __device__ __forceinline__ void mma_stage_kmajor(const char* sA, const char* sB,
   for (int ks = 0; ks < 2; ++ks) {
     const int k1 = ks * 32 + 8 * g + (r >> 2), k2 = k1 + 4;
     const int t1 = trkey(k1), t2 = trkey(k2);
-    bf16x8_t af[FM], bfr[FN];
+    // the two halves of each fragment are joined into an MFMA operand only
+    // after the wait: a copy made earlier would read registers the reads
+    // have not written yet
+    v4i16_t alo[FM], ahi[FM], blo[FN], bhi[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int c = wn * 4 + j;
-      const v4i16_t lo = lds_read_tr(sB + k1 * 512 + ((c ^ t1) << 5) + cb);
-      const v4i16_t hi = lds_read_tr(sB + k2 * 512 + ((c ^ t2) << 5) + cb);
-      bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      blo[j] = lds_read_tr(sB + k1 * 512 + ((c ^ t1) << 5) + cb);
+      bhi[j] = lds_read_tr(sB + k2 * 512 + ((c ^ t2) << 5) + cb);
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int c = wm * 8 + i;
-      const v4i16_t lo = lds_read_tr(sA + k1 * 512 + ((c ^ t1) << 5) + cb);
-      const v4i16_t hi = lds_read_tr(sA + k2 * 512 + ((c ^ t2) << 5) + cb);
-      af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      alo[i] = lds_read_tr(sA + k1 * 512 + ((c ^ t1) << 5) + cb);
+      ahi[i] = lds_read_tr(sA + k2 * 512 + ((c ^ t2) << 5) + cb);
     }
     wait_lds_pinned();
+    bf16x8_t bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(blo[j], bhi[j], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(alo[i], ahi[i], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+    }
   }
 }
 
