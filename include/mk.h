@@ -290,6 +290,13 @@ int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx_dev, const void* x_d
 #define MK_PH_COUNT      16
 int mk_timing_enable(mk_workspace* ws, int32_t on);
 int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
+/*
+ * Limit the phases that record events while timing is on to those whose bit
+ * (1u << MK_PH_x) is set in phase_mask (default: all).  Each recorded event
+ * pair costs a few microseconds of stream time, so a benchmark that wants
+ * one kernel's duration inside its timed region selects just that phase.
+ */
+int mk_timing_phases(mk_workspace* ws, uint32_t phase_mask);
 
 /* Enqueue a copy of the device error word into dst_dev (device uint32). */
 int mk_device_error(const mk_workspace* ws, uint32_t* dst_dev, void* stream);

@@ -73,6 +73,7 @@ _SIGS = {
     "mk_backward_layer": (ctypes.c_int, [_vp] * 17),
     "mk_device_error": (ctypes.c_int, [_vp, _vp, _vp]),
     "mk_timing_enable": (ctypes.c_int, [_vp, _i32]),
+    "mk_timing_phases": (ctypes.c_int, [_vp, ctypes.c_uint32]),
     "mk_timing_read": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_i32)]),
     "mk_two_wave_rows": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "mk_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -185,6 +186,12 @@ def mk_device_error(ws, dst, stream=None):
 
 def mk_timing_enable(ws, on: bool) -> None:
     _check("mk_timing_enable", lib.mk_timing_enable(ws, int(on)))
+
+
+def mk_timing_phases(ws, phases=None) -> None:
+    """Record events only for the named phases while timing is on (None: all)."""
+    mask = 0xFFFFFFFF if phases is None else sum(1 << PHASES.index(p) for p in phases)
+    _check("mk_timing_phases", lib.mk_timing_phases(ws, mask))
 
 
 PHASES = ["route", "schedule", "permute", "gemm1", "quant_a", "gemm2", "combine", "bwd_gather", "bwd_dact",

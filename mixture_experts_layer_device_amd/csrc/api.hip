@@ -105,7 +105,8 @@ struct Phase {
   hipStream_t s;
   mk_phase_event ev;
   bool on;
-  Phase(mk_workspace* w, int phase, hipStream_t st) : ws(w), s(st), on(w->timing != 0) {
+  Phase(mk_workspace* w, int phase, hipStream_t st)
+      : ws(w), s(st), on(w->timing != 0 && ((w->timing_mask >> phase) & 1u)) {
     if (!on) return;
     ev.phase = phase;
     if (hipEventCreate(&ev.start) != hipSuccess || hipEventCreate(&ev.stop) != hipSuccess) {
@@ -276,6 +277,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   mk_workspace* ws = (mk_workspace*)calloc(1, sizeof(mk_workspace));
   if (!ws) return MK_ERR_HIP;
   ws->events = new std::vector<mk_phase_event>();
+  ws->timing_mask = 0xFFFFFFFFu;
   ws->cfg = *cfg;
   ws->max_rows = max_rows;
   ws->H = H;
@@ -618,6 +620,12 @@ int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx, const void* x, cons
 int mk_timing_enable(mk_workspace* ws, int32_t on) {
   if (!ws) return MK_ERR_NULL;
   ws->timing = on ? 1 : 0;
+  return MK_OK;
+}
+
+int mk_timing_phases(mk_workspace* ws, uint32_t phase_mask) {
+  if (!ws) return MK_ERR_NULL;
+  ws->timing_mask = phase_mask;
   return MK_OK;
 }
 

@@ -45,8 +45,9 @@ struct mk_workspace {
   float* dz;                  // [ceil(max_rows / k), E]: router logit gradient (and logits)
   float* rpart;               // [rsplits_max, E, H + 1]: router weight-gradient partials
   int32_t rsplits_max;
-  // optional per-phase timing
+  // optional per-phase timing (phases whose bit is set in timing_mask)
   int timing;
+  uint32_t timing_mask;
   std::vector<mk_phase_event>* events;
 };
 
