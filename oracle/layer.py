@@ -385,13 +385,47 @@ def _dact_mxfp8(dYq, wdTq, g, u, w):
     return dAp, a, dw, bf16.round_rne(dgx), bf16.round_rne(dux), dgx, dux
 
 
-def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False):
+def qd_rows(v):
+    """MXFP8 quantise-dequantise along the first axis: each column of v is cut
+    into blocks of 32 consecutive rows, the last one completed with zero rows
+    (which change neither its largest magnitude nor the other codes and are
+    dropped again)."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    pad = (-n) % 32
+    if pad:
+        v = np.concatenate([v, np.zeros((pad,) + v.shape[1:])], axis=0)
+    return qd(v.T).T[:n]
+
+
+def minibatch_of(rows, R: int, mb: int):
+    """Minibatch index of arrival rows (mb <= 0 or mb >= R: one minibatch)."""
+    rows = np.asarray(rows)
+    return np.zeros_like(rows) if mb <= 0 or mb >= R else rows // mb
+
+
+def wgrad_mx(A, B, mbs):
+    """sum over segments s of D(Q_rows(A_s))^T D(Q_rows(B_s)): the MXFP8
+    weight-gradient contraction over one expert's rows.  A [n, M] and B [n, N]
+    hold the expert's rows in arrival order, mbs their minibatch; a segment is
+    the rows of one minibatch, and the MX blocks of 32 rows never cross a
+    segment boundary (a minibatch's rows are the unit the schedule hands
+    over, so a block is complete once its minibatch is)."""
+    out = np.zeros((A.shape[1], B.shape[1]))
+    for b in np.unique(mbs):
+        k = mbs == b
+        out += qd_rows(A[k]).T @ qd_rows(B[k])
+    return out
+
+
+def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False, wgrad_mx_mb: int | None = None):
     """MXFP8 expert backward of routed rows (arrival order) given the
     forward's g = G and u = U: the rows of ``backward_share_mxfp8`` with
     dX_rows not rounded (see there).  With ``allow`` also dX_rows_allow: how
     far dX_rows may move because [dg | du] is a GEMM output whose E4M3 codes
     another correct evaluation may decide differently (``qd_spread`` through
-    |W_P|)."""
+    |W_P|).  ``wgrad_mx_mb``: None = bf16 weight gradients; else MXFP8 ones
+    (``wgrad_mx``) with minibatches of that many rows (0 = one minibatch)."""
     dYq = qd(dY)
     R, H = x.shape
     E, I, _ = wg.shape
@@ -411,16 +445,23 @@ def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False):
         if allow:
             dX_allow[sel] = qd_spread(np.concatenate([dgx, dux], axis=1)[:, order]) @ np.abs(WPq).T
         xe = x[sel]
-        dWg[e] = dg.T @ xe
-        dWu[e] = du.T @ xe
-        dWd[e] = dY[sel].T @ bf16.round_rne(w[sel, None] * a)
+        wa = bf16.round_rne(w[sel, None] * a)
+        if wgrad_mx_mb is None:
+            dWg[e] = dg.T @ xe
+            dWu[e] = du.T @ xe
+            dWd[e] = dY[sel].T @ wa
+        else:
+            mbs = minibatch_of(sel, R, wgrad_mx_mb)
+            dWg[e] = wgrad_mx(dg, xe, mbs)
+            dWu[e] = wgrad_mx(du, xe, mbs)
+            dWd[e] = wgrad_mx(dY[sel], wa, mbs)
     res = {"dX_rows": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "d_row_w": dw}
     if allow:
         res["dX_rows_allow"] = dX_allow
     return res
 
 
-def backward_share_mxfp8(inp, fwd=None, allow: bool = False):
+def backward_share_mxfp8(inp, fwd=None, allow: bool = False, wgrad_mx_mb: int | None = None):
     """Expert share backward in MXFP8 mode, loss L = sum_r <dY[r], out_rows[r]>
     with out_rows from forward_share_mxfp8.
 
@@ -431,14 +472,20 @@ def backward_share_mxfp8(inp, fwd=None, allow: bool = False):
               W_P = [W_g[e] ; W_u[e]] both in gu_order
     g and u are the MXFP8 forward's (exact products of its dequantised
     operands); a = silu(g) u; dw, dA, dg, du (bf16) as in the bf16 backward.
-    The weight gradients stay bf16 GEMMs, as in the bf16 backward:
+    With ``wgrad_mx_mb`` None the weight gradients are bf16 GEMMs, as in the
+    bf16 backward:
         dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = dY_e^T bf16(w a)_e
+    With an integer (the minibatch rows; 0 = one minibatch) they are MXFP8
+    GEMMs too, each operand quantised along their contraction, the expert's
+    rows, in blocks of 32 rows of one minibatch (``wgrad_mx``):
+        dW_g[e] = sum_s D(Q_rows(dg_s))^T D(Q_rows(X_s)), dW_u likewise,
+        dW_d[e] = sum_s D(Q_rows(dY_s))^T D(Q_rows(bf16(w a)_s))
     With ``allow`` also dX_allow (see ``_backward_rows_mxfp8``).
     """
     fwd = forward_share_mxfp8(inp) if fwd is None else fwd
     wg, wu, wd = _weights(inp)
     g = _backward_rows_mxfp8(bf16.decode(inp["x"]), inp["row_expert"], inp["row_w"].astype(np.float64),
-                             bf16.decode(inp["dY"]), fwd["g"], fwd["u"], wg, wu, wd, allow)
+                             bf16.decode(inp["dY"]), fwd["g"], fwd["u"], wg, wu, wd, allow, wgrad_mx_mb)
     g["dX"] = bf16.round_rne(g.pop("dX_rows"))
     if allow:
         g["dX_allow"] = g.pop("dX_rows_allow")
@@ -475,9 +522,11 @@ def forward_full_mxfp8(inp, renorm: int | None = None, allow: bool = False):
     return res
 
 
-def backward_full_mxfp8(inp, renorm: int | None = None, router: bool = True, fwd=None, allow: bool = False):
+def backward_full_mxfp8(inp, renorm: int | None = None, router: bool = True, fwd=None, allow: bool = False,
+                        wgrad_mx_mb: int | None = None):
     """Full-layer backward in MXFP8 mode: ``backward_full`` with the expert
-    part of ``backward_share_mxfp8`` on the routed rows (g, u from
+    part of ``backward_share_mxfp8`` (weight gradients per ``wgrad_mx_mb``,
+    minibatches over the routed rows r = t k + j) on the routed rows (g, u from
     ``forward_full_mxfp8``); the k-sum, the router gradient and the single
     bf16 rounding of dX as in ``backward_full``.  With ``allow`` also
     dX_allow, the sum of the token's rows' allowances."""
@@ -491,7 +540,8 @@ def backward_full_mxfp8(inp, renorm: int | None = None, router: bool = True, fwd
     wg, wu, wd = _weights(inp)
     T, H = x.shape
     g = _backward_rows_mxfp8(np.repeat(x, k, axis=0), idx.reshape(-1), w.reshape(-1).astype(np.float64),
-                             np.repeat(bf16.decode(inp["dY"]), k, axis=0), fwd["g"], fwd["u"], wg, wu, wd, allow)
+                             np.repeat(bf16.decode(inp["dY"]), k, axis=0), fwd["g"], fwd["u"], wg, wu, wd, allow,
+                             wgrad_mx_mb)
     if allow:
         g["dX_allow"] = g.pop("dX_rows_allow").reshape(T, k, H).sum(axis=1)
     d_topk_w = g["d_row_w"].reshape(T, k)
@@ -508,9 +558,10 @@ def backward_full_mxfp8(inp, renorm: int | None = None, router: bool = True, fwd
     return out
 
 
-def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols):
+def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb: int | None = None):
     """Entries of backward_share_mxfp8 computed one by one (each needs only
-    its own rows, or the rows of one expert), with dX_allow for the rows."""
+    its own rows, or the rows of one expert), with dX_allow for the rows;
+    ``wgrad_mx_mb`` as there."""
     re = inp["row_expert"]
     w = inp["row_w"].astype(np.float64)
     I = inp["w_gate"].shape[1]
@@ -547,25 +598,52 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols):
         if e not in rows_q:
             sel = np.nonzero(re == e)[0]
             X = bf16.decode(inp["x"][sel]); dY = bf16.decode(inp["dY"][sel])
-            rows_q[e] = (sel, X, dY, qd(X), qd(dY))
+            rows_q[e] = [sel, X, dY, qd(X), qd(dY)]
+            if wgrad_mx_mb is not None:
+                # weight-gradient operands quantised along the rows, per segment
+                mbs = minibatch_of(sel, re.size, wgrad_mx_mb)
+                xs = np.zeros_like(X); ds = np.zeros_like(dY)
+                for b in np.unique(mbs):
+                    kk = mbs == b
+                    xs[kk] = qd_rows(X[kk]); ds[kk] = qd_rows(dY[kk])
+                rows_q[e] += [mbs, xs, ds]
         return rows_q[e]
+
+    def seg_q(v, mbs):
+        # one column, quantised along the rows per segment
+        out = np.zeros_like(v)
+        for b in np.unique(mbs):
+            kk = mbs == b
+            out[kk] = qd_rows(v[kk, None])[:, 0]
+        return out
 
     for key, pairs in (("gate_up", gate_up_rows), ("down", down_cols)):
         for (e, i) in pairs:
             # feature i only: one column of g, u and dA' (as _dact_mxfp8 computes
             # them); the weights are quantised per row along H, so the rows
             # for feature i are quantised alone
-            sel, X, dY, xd, dyq = expert_rows(e)
+            sel, X, dY, xd, dyq = expert_rows(e)[:5]
             g = xd @ qd(bf16.decode(inp["w_gate"][e, i]))
             u = xd @ qd(bf16.decode(inp["w_up"][e, i]))
             dAp = dyq @ qd(bf16.decode(inp["w_down"][e][:, i]))
             s = sigmoid(g)
             dA = w[sel] * dAp
-            if key == "gate_up":
-                out["dW_gate"].append(bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s))) @ X)
-                out["dW_up"].append(bf16.round_rne(dA * silu(g)) @ X)
+            dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
+            du = bf16.round_rne(dA * silu(g))
+            wa = bf16.round_rne(w[sel] * silu(g) * u)
+            if wgrad_mx_mb is None:
+                if key == "gate_up":
+                    out["dW_gate"].append(dg @ X)
+                    out["dW_up"].append(du @ X)
+                else:
+                    out["dW_down"].append(wa @ dY)
             else:
-                out["dW_down"].append(bf16.round_rne(w[sel] * silu(g) * u) @ dY)
+                mbs, xs, ds = expert_rows(e)[5:]
+                if key == "gate_up":
+                    out["dW_gate"].append(seg_q(dg, mbs) @ xs)
+                    out["dW_up"].append(seg_q(du, mbs) @ xs)
+                else:
+                    out["dW_down"].append(seg_q(wa, mbs) @ ds)
     return {k: np.asarray(v) for k, v in out.items()}
 
 
