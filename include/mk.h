@@ -73,6 +73,16 @@ extern "C" {
  *   renorm              router weights: 1 = softmax over the k chosen logits,
  *                       0 = full softmax over all E read at the chosen ones.
  *   enable_backward     1 = also allocate the backward's buffers.
+ *   wgrad_mxfp8         1 = (precision MK_MXFP8 with enable_backward only)
+ *                       the weight-gradient GEMMs take MXFP8 operands too,
+ *                       each quantised along the contraction (the expert's
+ *                       rows) in blocks of 32 rows of one minibatch, a
+ *                       minibatch's last block completed with zero rows;
+ *                       0 = bf16 weight gradients.  The pages give no MXFP8
+ *                       recipe for these GEMMs; this blocking follows the
+ *                       forward's (MX blocks along the contraction) with the
+ *                       minibatch as the unit of arrival ([MTP] "Three design
+ *                       decisions that matter": minibatch granularity).
  */
 typedef struct mk_config {
   int32_t minibatch_rows;
@@ -81,7 +91,8 @@ typedef struct mk_config {
   float   sched_capacity_mult;
   int32_t renorm;
   int32_t enable_backward;
-  int32_t reserved[3];
+  int32_t wgrad_mxfp8;
+  int32_t reserved[2];
 } mk_config;
 
 typedef struct mk_workspace mk_workspace;   /* opaque */
@@ -287,7 +298,8 @@ int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx_dev, const void* x_d
 #define MK_PH_BWD_COMBINE 13  /* full layer: k-sum of dX rows (+ router term) */
 #define MK_PH_ROUTER_BWD 14   /* router backward: logit gradient, dW_router, d_bias */
 #define MK_PH_REPLAY     15   /* re-gather of the x rows of minibatches evicted from the ring */
-#define MK_PH_COUNT      16
+#define MK_PH_WGRAD_QUANT 16  /* MXFP8 weight gradients: operands quantised along the rows */
+#define MK_PH_COUNT      17
 int mk_timing_enable(mk_workspace* ws, int32_t on);
 int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
 /*

@@ -49,7 +49,8 @@ class MkConfig(ctypes.Structure):
         ("sched_capacity_mult", ctypes.c_float),
         ("renorm", ctypes.c_int32),
         ("enable_backward", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("wgrad_mxfp8", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -195,7 +196,7 @@ def mk_timing_phases(ws, phases=None) -> None:
 
 
 PHASES = ["route", "schedule", "permute", "gemm1", "quant_a", "gemm2", "combine", "bwd_gather", "bwd_dact",
-          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd", "replay"]
+          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd", "replay", "wgrad_quant"]
 
 
 def mk_timing_read(ws) -> dict:

@@ -226,6 +226,38 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   wa.src_div = src_div;
   const int ring_mbs = ws->ring_rows / MB;
   const int first_resident = std::max(0, nb - ring_mbs);
+  if (ws->cfg.wgrad_mxfp8) {
+    // MXFP8 weight gradients: both operands of each GEMM quantised along the
+    // rows (32 rows of one minibatch per block) into the tiled layout; the x
+    // rows come straight from x_src through the inverse map (the ring holds
+    // them quantised along H, the wrong axis), which is the replay of every
+    // minibatch at once
+    {
+      Phase ph(ws, MK_PH_WGRAD_QUANT, s);
+      launch_wgrad_kofs(ws->mb_counts, nb, E, ws->wq_kofs, ws->wq_order, s);
+      launch_quant_wgrad_operand(ws->dye, H, nullptr, 1, H, ws->wq_kofs, E, ws->mb_counts, ws->mb_offsets, nb, MB,
+                                 ws->wq_kcap, ws->wq_ac, ws->wq_as, s);
+      launch_quant_wgrad_operand(ws->wa, I, nullptr, 1, I, ws->wq_kofs, E, ws->mb_counts, ws->mb_offsets, nb, MB,
+                                 ws->wq_kcap, ws->wq_bc, ws->wq_bs, s);
+    }
+    {
+      Phase ph(ws, MK_PH_WGRAD_DOWN, s);
+      launch_wgrad_down_mxfp8(E, H, I, ws->wq_kofs, ws->wq_order, ws->wq_ac, ws->wq_as, ws->wq_bc, ws->wq_bs, dW_down,
+                              ws->n_cu, s);
+    }
+    {
+      Phase ph(ws, MK_PH_WGRAD_QUANT, s);
+      launch_quant_wgrad_operand(ws->dgdu, 2 * I, nullptr, 1, 2 * I, ws->wq_kofs, E, ws->mb_counts, ws->mb_offsets,
+                                 nb, MB, ws->wq_kcap, ws->wq_ac, ws->wq_as, s);
+      if (R > 0)
+        launch_quant_wgrad_operand((const uint16_t*)x_src, H, ws->inv, src_div, H, ws->wq_kofs, E, ws->mb_counts,
+                                   ws->mb_offsets, nb, MB, ws->wq_kcap, ws->wq_bc, ws->wq_bs, s);
+    }
+    Phase ph(ws, MK_PH_WGRAD_GU, s);
+    launch_wgrad_gate_up_mxfp8(E, H, I, ws->wq_kofs, ws->wq_order, ws->wq_ac, ws->wq_as, ws->wq_bc, ws->wq_bs,
+                               dW_gate, dW_up, ws->n_cu, s);
+    return check_launch();
+  }
   {
     Phase ph(ws, MK_PH_WGRAD_DOWN, s);
     launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->zero_row, ws->n_cu, s);
@@ -273,6 +305,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   if (cfg->minibatch_rows < 0 || !(cfg->sched_capacity_mult > 0.f) || cfg->ring_bytes <= 0) return MK_ERR_CONFIG;
   if (cfg->ring_bytes >= ((int64_t)1 << 31)) return MK_ERR_LIMIT;
   if (cfg->enable_backward && I % 256) return MK_ERR_SHAPE;
+  if (cfg->wgrad_mxfp8 && (cfg->precision != MK_MXFP8 || !cfg->enable_backward)) return MK_ERR_CONFIG;
 
   mk_workspace* ws = (mk_workspace*)calloc(1, sizeof(mk_workspace));
   if (!ws) return MK_ERR_HIP;
@@ -359,6 +392,20 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     ws->rsplits_max = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ((int64_t)64 << 20) / per_split));
     o_rp = c.take((size_t)ws->rsplits_max * per_split);
   }
+  size_t o_wk = 0, o_wo = 0, o_wac = 0, o_was = 0, o_wbc = 0, o_wbs = 0;
+  if (cfg->wgrad_mxfp8) {
+    // every expert's K range: its minibatch segments rounded up to 32 rows,
+    // the total to 128
+    const int64_t kc = (int64_t)max_rows + (int64_t)ws->nb_max * E * 31 + (int64_t)E * 127;
+    ws->wq_kcap = (kc + 127) / 128 * 128;
+    const int64_t ca = std::max(H, 2 * I), cb = std::max(H, I);
+    o_wk = c.take((size_t)(E + 1) * 4);
+    o_wo = c.take((size_t)E * 4);
+    o_wac = c.take((size_t)(ca * ws->wq_kcap));
+    o_was = c.take((size_t)(ca * ws->wq_kcap / 32));
+    o_wbc = c.take((size_t)(cb * ws->wq_kcap));
+    o_wbs = c.take((size_t)(cb * ws->wq_kcap / 32));
+  }
   ws->bytes = c.off;
   if (hipMalloc(&ws->base, ws->bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -399,6 +446,14 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
       ws->dgdu_c = (uint8_t*)(b + o_gc);
       ws->dgdu_s = (uint8_t*)(b + o_gs);
     }
+  }
+  if (cfg->wgrad_mxfp8) {
+    ws->wq_kofs = (int32_t*)(b + o_wk);
+    ws->wq_order = (int32_t*)(b + o_wo);
+    ws->wq_ac = (uint8_t*)(b + o_wac);
+    ws->wq_as = (uint8_t*)(b + o_was);
+    ws->wq_bc = (uint8_t*)(b + o_wbc);
+    ws->wq_bs = (uint8_t*)(b + o_wbs);
   }
   // error word starts clear; the zero row is zero
   launch_fill_u32(ws->err, 0u, 1, nullptr);

@@ -53,31 +53,44 @@ __device__ __forceinline__ void read_b_mx(const char* st, int j, i32x8_t& f, int
 // contiguous copies); waves 0-3 also fetch A's scale dwords (64 rows each)
 // and waves 4-7 B's.  A stage's B fragments are read at its start and its A
 // fragments one ahead of the 4 MFMAs that use them.
-template <typename ARow, typename ASc>
-__device__ __forceinline__ void mainloop(const void* abase, ARow arow, const void* asbase, ASc ascale,
-                                         const uint8_t* bcodes, const uint8_t* bscales, int K, char* lds,
-                                         Acc& acc) {
+// ATILED: A comes in the tiled layout as well (abase / asbase: its tile's
+// first code and scale blocks; arow, ascale unused) and is fetched like B.
+template <bool ATILED, typename ARow, typename ASc>
+__device__ __forceinline__ void mainloop_t(const void* abase, ARow arow, const void* asbase, ASc ascale,
+                                           const uint8_t* bcodes, const uint8_t* bscales, int K, char* lds,
+                                           Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const buf_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bcodes);
   const buf_rsrc_t rs = make_rsrc(wave_uniform(wave < 4 ? asbase : (const void*)bscales));
-  uint32_t ao[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wave * 32 + j * 8 + (lane >> 3);
-    ao[j] = (uint32_t)(arow(r) - (const uint8_t*)abase) + (((lane & 7) ^ tkey(r)) & 7) * 16;
-  }
   const int wbase = wave * 4096;
   const uint32_t bo = wbase + lane * 16;
-  const uint32_t so = wave < 4 ? (uint32_t)(ascale(wave * 64 + lane) - (const uint8_t*)asbase)
-                               : (uint32_t)((wave - 4) * 256 + lane * 4);
-  const uint32_t sstep = wave < 4 ? 4 : MXT_SCALES;     // bytes between K steps in the scale source
+  uint32_t ao[4];
+  if constexpr (!ATILED) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + (lane >> 3);
+      ao[j] = (uint32_t)(arow(r) - (const uint8_t*)abase) + (((lane & 7) ^ tkey(r)) & 7) * 16;
+    }
+  }
+  uint32_t so, sstep;                                   // sstep: bytes between K steps in the scale source
+  if constexpr (ATILED) {
+    so = (uint32_t)((wave & 3) * 256 + lane * 4);
+    sstep = MXT_SCALES;
+  } else {
+    so = wave < 4 ? (uint32_t)(ascale(wave * 64 + lane) - (const uint8_t*)asbase)
+                  : (uint32_t)((wave - 4) * 256 + lane * 4);
+    sstep = wave < 4 ? 4 : MXT_SCALES;
+  }
   const int sbase = 2 * TILE_BYTES + wave * 256;
   auto issue = [&](int kt, char* st) {
     const uint32_t kb = (uint32_t)kt * BKB;
     const uint32_t b = bo + (uint32_t)kt * MXT_CODES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      b2lds16(ra, ao[j] + kb, st + wbase + j * 1024);
+      if constexpr (ATILED)
+        b2lds16(ra, b + j * 1024, st + wbase + j * 1024);
+      else
+        b2lds16(ra, ao[j] + kb, st + wbase + j * 1024);
       b2lds16(rb, b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
     }
     b2lds4(rs, so + (uint32_t)kt * sstep, st + sbase);
@@ -112,6 +125,13 @@ __device__ __forceinline__ void mainloop(const void* abase, ARow arow, const voi
     wait_all_mem();
     __syncthreads();
   }
+}
+
+template <typename ARow, typename ASc>
+__device__ __forceinline__ void mainloop(const void* abase, ARow arow, const void* asbase, ASc ascale,
+                                         const uint8_t* bcodes, const uint8_t* bscales, int K, char* lds,
+                                         Acc& acc) {
+  mainloop_t<false>(abase, arow, asbase, ascale, bcodes, bscales, K, lds, acc);
 }
 
 // a[p, i] = silu(g) * u (bf16) from MXFP8 ring rows and packed MXFP8 W_gu.
@@ -247,7 +267,80 @@ __global__ __launch_bounds__(NT) void bwd_dx_mxfp8_kernel(ItemRange ir, const ui
   });
 }
 
+// ------------------------------------------------- weight gradients ----
+// C[m, n] = sum over expert e's padded rows k of D(A[m, k]) D(B[n, k]): both
+// operands quantised along k (the rows) and stored in the tiled layout per
+// expert (its blocks from (M/256) * kofs[e]/128 on, row tile by row tile), so
+// the K loop is the forward's with A fetched like B.  Tiles go expert by
+// expert in order of descending K, each (m, n) tile by one workgroup over the
+// whole K: fixed order, no atomics.  An expert without rows writes zeros.
+// MODE 0: dW_down [E, H, I] (M = H, N = I); MODE 1: A rows are the packed
+// gate/up features (16 gate, then the same 16 up) -> dW_gate / dW_up [E, I, H].
+template <int MODE>
+__global__ __launch_bounds__(NT) void wgrad_mxfp8_kernel(int E, int M, int N, int I, const int32_t* __restrict__ kofs,
+                                                         const int32_t* __restrict__ order,
+                                                         const uint8_t* __restrict__ ac,
+                                                         const uint8_t* __restrict__ as_,
+                                                         const uint8_t* __restrict__ bc,
+                                                         const uint8_t* __restrict__ bs, float* __restrict__ out0,
+                                                         float* __restrict__ out1) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int tm = M / BM, tn = N / BN;
+  const int per_e = tm * tn;
+  const int total = E * per_e;
+  for (int t = xcd_logical_block(); t < total; t += gridDim.x) {
+    const int q = t / per_e;
+    const int e = order[q];
+    int mt, nt;
+    tile_coords(t - q * per_e, tm, tn, mt, nt);
+    const int k0 = kofs[e], K = kofs[e + 1] - k0;
+    Acc acc;
+    if (K > 0) {
+      const int64_t ab = (int64_t)tm * (k0 / BKB) + (int64_t)mt * (K / BKB);
+      const int64_t bb = (int64_t)tn * (k0 / BKB) + (int64_t)nt * (K / BKB);
+      auto none = [](int) { return (const uint8_t*)nullptr; };
+      mainloop_t<true>(ac + ab * MXT_CODES, none, as_ + ab * MXT_SCALES, none, bc + bb * MXT_CODES,
+                       bs + bb * MXT_SCALES, K, lds, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int m0 = mt * BM, n0 = nt * BN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + frag_row(i, v);
+        float* dst;
+        if (MODE == 0) {
+          dst = out0 + ((int64_t)e * M + m) * N;
+        } else {
+          const int ii = (m >> 5) * 16 + (m & 15);
+          dst = ((m & 31) < 16 ? out0 : out1) + ((int64_t)e * I + ii) * N;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[n0 + frag_col(j)] = acc[i][j][v];
+      }
+  }
+}
+
 }  // namespace
+
+void launch_wgrad_down_mxfp8(int E, int H, int I, const int32_t* kofs, const int32_t* order, const uint8_t* ac,
+                             const uint8_t* as, const uint8_t* bc, const uint8_t* bs, float* dW_down, int n_cu,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_mxfp8_kernel<0>, dim3(n_cu), dim3(NT), 0, s, E, H, I, I, kofs, order, ac, as, bc, bs,
+                     dW_down, (float*)nullptr);
+}
+
+void launch_wgrad_gate_up_mxfp8(int E, int H, int I, const int32_t* kofs, const int32_t* order, const uint8_t* ac,
+                                const uint8_t* as, const uint8_t* bc, const uint8_t* bs, float* dW_gate,
+                                float* dW_up, int n_cu, hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_mxfp8_kernel<1>, dim3(n_cu), dim3(NT), 0, s, E, 2 * I, H, I, kofs, order, ac, as, bc, bs,
+                     dW_gate, dW_up);
+}
 
 void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const uint8_t* dy_scales,
                            const uint8_t* wdT_codes, const uint8_t* wdT_scales, int H, int I, const float* gu,

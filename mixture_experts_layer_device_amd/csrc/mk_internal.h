@@ -45,6 +45,12 @@ struct mk_workspace {
   float* dz;                  // [ceil(max_rows / k), E]: router logit gradient (and logits)
   float* rpart;               // [rsplits_max, E, H + 1]: router weight-gradient partials
   int32_t rsplits_max;
+  // MXFP8 weight gradients: K table of the experts' padded row spaces and the
+  // operands quantised along the rows, in the tiled MXFP8 layout
+  int32_t *wq_kofs, *wq_order;  // [E+1] start of expert e's K range; [E] experts by descending K
+  int64_t wq_kcap;              // K capacity (multiple of 128)
+  uint8_t *wq_ac, *wq_as;       // A operand: max(H, 2I) x kcap codes, / 32 scales
+  uint8_t *wq_bc, *wq_bs;       // B operand: H x kcap codes (H >= I), / 32 scales
   // optional per-phase timing (phases whose bit is set in timing_mask)
   int timing;
   uint32_t timing_mask;
@@ -109,6 +115,20 @@ void launch_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, in
 //                     quant_tile_cols: B[e][n][k] = row(e, k)[n]
 void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+// MXFP8 weight gradients.  K space: expert e owns [kofs[e], kofs[e+1]), its
+// minibatch segments in reverse order (nb-1 .. 0), each taking its row count
+// rounded up to 32, the expert's total rounded up to 128; order = the experts
+// by descending K (ties: lower id first).
+void launch_wgrad_kofs(const int32_t* mb_counts, int nb, int E, int32_t* kofs, int32_t* order, hipStream_t s);
+// Operand T[c][k] (C columns of the source rows, C % 256 == 0) quantised along
+// k in 32-blocks, stored per expert in the tiled MXFP8 layout: expert e's
+// blocks start at block (C/256) * kofs[e]/128 and run (row tile c/256, k step);
+// row k of expert e is position p of its segment (pad rows are zero); the
+// source row of p is src + (inv ? inv[p] / src_div : p) * ld.  Grid covers
+// kcap / 128 k steps; steps past kofs[E] exit.
+void launch_quant_wgrad_operand(const uint16_t* src, int64_t ld, const int32_t* inv, int src_div, int C,
+                                const int32_t* kofs, int E, const int32_t* mb_counts, const int32_t* mb_offsets,
+                                int nb, int MB, int64_t kcap, uint8_t* codes, uint8_t* scales, hipStream_t s);
 void launch_quant_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
                             uint8_t* codes, uint8_t* scales, hipStream_t s);
 void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
@@ -165,6 +185,16 @@ void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const u
                            const uint8_t* wdT_codes, const uint8_t* wdT_scales, int H, int I, const float* gu,
                            const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part,
                            int n_cu, hipStream_t s);
+// dW_down[e] (H x I) from the tiled operands dY^T (A, H rows) and (w a)^T
+// (B, I rows); dW_gate/dW_up[e] (I x H) from [dg|du]^T (A, 2I packed rows)
+// and X^T (B, H rows).  Every (e, m, n) tile by one workgroup over the
+// expert's whole K in ascending k: deterministic, no atomics.
+void launch_wgrad_down_mxfp8(int E, int H, int I, const int32_t* kofs, const int32_t* order, const uint8_t* ac,
+                             const uint8_t* as, const uint8_t* bc, const uint8_t* bs, float* dW_down, int n_cu,
+                             hipStream_t s);
+void launch_wgrad_gate_up_mxfp8(int E, int H, int I, const int32_t* kofs, const int32_t* order, const uint8_t* ac,
+                                const uint8_t* as, const uint8_t* bc, const uint8_t* bs, float* dW_gate,
+                                float* dW_up, int n_cu, hipStream_t s);
 void launch_bwd_dx_mxfp8(const ItemRange& ir, const uint8_t* dgdu_codes, const uint8_t* dgdu_scales,
                          const uint8_t* wguT_codes, const uint8_t* wguT_scales, int H, int I, const int32_t* inv,
                          uint16_t* dX, float* dx32, int n_cu, hipStream_t s);

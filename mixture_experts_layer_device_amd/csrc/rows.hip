@@ -428,4 +428,127 @@ void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mo
 }
 
 
+// ---- MXFP8 weight-gradient operands ----------------------------------------
+
+namespace {
+
+// One workgroup: expert e's K extent Kpad_e = roundup128(sum over minibatches
+// of roundup32(rows)), an exclusive scan over the experts (Hillis-Steele in
+// LDS), and the experts ranked by descending K for the GEMM's tile order.
+__global__ __launch_bounds__(1024) void wgrad_kofs_kernel(const int32_t* __restrict__ mb_counts, int nb, int E,
+                                                          int32_t* __restrict__ kofs, int32_t* __restrict__ order) {
+  __shared__ int kp[1024], sc[1024];
+  const int e = threadIdx.x;
+  int v = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) v += (mb_counts[b * E + e] + 31) & ~31;
+    v = (v + 127) & ~127;
+  }
+  kp[e] = v;
+  sc[e] = v;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int add = e >= d ? sc[e - d] : 0;
+    __syncthreads();
+    sc[e] += add;
+    __syncthreads();
+  }
+  if (e < E) {
+    kofs[e] = sc[e] - v;
+    int rank = 0;
+    for (int q = 0; q < E; ++q) rank += (kp[q] > v) || (kp[q] == v && q < e);
+    order[rank] = e;
+  }
+  if (e == 0) kofs[E] = sc[E - 1];
+}
+
+// Workgroup (256-column tile ct, global k step kc): the 128 rows of the step
+// (each resolved to its position through the expert's segments, walked in
+// reverse minibatch order) x 256 columns go to LDS with 16-byte loads, then
+// each thread quantises a 32-row column block (quant_block) and stores its two
+// code granules and scale byte in the tiled block, as quant_tile_cols does.
+__global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
+    const uint16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ inv, int src_div, int C,
+    const int32_t* __restrict__ kofs, int E, const int32_t* __restrict__ mb_counts,
+    const int32_t* __restrict__ mb_offsets, int nb, int MB, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  constexpr int LD = MXT_ROWS + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t t[MXT_K][LD];
+  __shared__ int64_t srow[MXT_K];
+  const int ct = blockIdx.x, kc = blockIdx.y, tid = threadIdx.x;
+  const int k0 = kc * MXT_K;
+  if (k0 >= kofs[E]) return;                    // the whole workgroup leaves together
+  // expert of this step: the last e with kofs[e] <= k0 (kofs is ascending)
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kofs[mid] <= k0) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int ke = kofs[e], kpad = kofs[e + 1] - ke;
+  if (tid < MXT_K) {
+    const int kk = k0 - ke + tid;               // row within the expert's K range
+    int64_t row = -1;
+    int acc = 0;
+    for (int b = nb - 1; b >= 0; --b) {
+      const int n = mb_counts[b * E + e];
+      const int l32 = (n + 31) & ~31;
+      if (kk < acc + l32) {
+        const int r = kk - acc;
+        if (r < n) {
+          const int64_t p = (int64_t)b * MB + mb_offsets[b * (E + 1) + e] + r;
+          row = inv ? (int64_t)(inv[p] / src_div) : p;
+        }
+        break;
+      }
+      acc += l32;
+    }
+    srow[tid] = row;
+  }
+  __syncthreads();
+  const int c0 = ct * MXT_ROWS;
+  for (int q = tid; q < MXT_K * (MXT_ROWS / 8); q += 256) {
+    const int kk = q / (MXT_ROWS / 8), c = (q % (MXT_ROWS / 8)) * 8;
+    const int64_t row = srow[kk];
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row >= 0) v = *(const u32x4_t*)(src + row * ld + c0 + c);
+    *(u32x4_t*)&t[kk][c] = v;
+  }
+  __syncthreads();
+  const int64_t blk = (int64_t)(C / MXT_ROWS) * (ke / MXT_K) + (int64_t)ct * (kpad / MXT_K) + (k0 - ke) / MXT_K;
+  uint8_t* cblk = codes + blk * MXT_CODES;
+  uint8_t* sblk = scales + blk * MXT_SCALES;
+  for (int q = tid; q < MXT_ROWS * (MXT_K / 32); q += 256) {
+    const int r = q % MXT_ROWS, kb = q / MXT_ROWS;
+    u32x4_t v[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int k = kb * 32 + g * 8 + 2 * d;
+        v[g][d] = (uint32_t)t[k][r] | ((uint32_t)t[k + 1][r] << 16);
+      }
+    u32x4_t cc[2];
+    const uint32_t sv = quant_block(v, cc);
+    const int g0 = kb * 2;
+    *(u32x4_t*)(cblk + r * MXT_K + (((g0 ^ tkey(r)) & 7) << 4)) = cc[0];
+    *(u32x4_t*)(cblk + r * MXT_K + ((((g0 + 1) ^ tkey(r)) & 7) << 4)) = cc[1];
+    sblk[r * 4 + kb] = (uint8_t)sv;
+  }
+}
+
+}  // namespace
+
+void launch_wgrad_kofs(const int32_t* mb_counts, int nb, int E, int32_t* kofs, int32_t* order, hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_kofs_kernel, dim3(1), dim3(1024), 0, s, mb_counts, nb, E, kofs, order);
+}
+
+void launch_quant_wgrad_operand(const uint16_t* src, int64_t ld, const int32_t* inv, int src_div, int C,
+                                const int32_t* kofs, int E, const int32_t* mb_counts, const int32_t* mb_offsets,
+                                int nb, int MB, int64_t kcap, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  hipLaunchKernelGGL(quant_wgrad_operand_kernel, dim3(C / MXT_ROWS, (unsigned)(kcap / MXT_K)), dim3(256), 0, s, src,
+                     ld, inv, src_div, C, kofs, E, mb_counts, mb_offsets, nb, MB, codes, scales);
+}
+
+
 }  // namespace mk

@@ -34,7 +34,7 @@ class MoELayer:
     """A workspace plus the calls that use it (one per model, reused)."""
 
     def __init__(self, H, I, E, k, max_rows, precision="bf16", minibatch_rows=0, ring_bytes=256 << 20,
-                 renorm=1, enable_backward=False, capacity_mult=1.0, device="cuda"):
+                 renorm=1, enable_backward=False, capacity_mult=1.0, wgrad_mxfp8=False, device="cuda"):
         cfg = B.mk_config_default()
         cfg.minibatch_rows = minibatch_rows
         cfg.precision = PRECISION[precision]
@@ -42,6 +42,7 @@ class MoELayer:
         cfg.sched_capacity_mult = capacity_mult
         cfg.renorm = renorm
         cfg.enable_backward = int(enable_backward)
+        cfg.wgrad_mxfp8 = int(wgrad_mxfp8)
         self.H, self.I, self.E, self.k = H, I, E, k
         self.precision = precision
         self.device = device

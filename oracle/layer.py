@@ -398,10 +398,38 @@ def qd_rows(v):
     return qd(v.T).T[:n]
 
 
+def qd_spread_rows(v):
+    """``qd_spread`` with the blocks of 32 taken down the rows of v (as
+    ``qd_rows``; zero pad rows have no spread)."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    pad = (-n) % 32
+    if pad:
+        v = np.concatenate([v, np.zeros((pad,) + v.shape[1:])], axis=0)
+    return qd_spread(v.T).T[:n]
+
+
 def minibatch_of(rows, R: int, mb: int):
     """Minibatch index of arrival rows (mb <= 0 or mb >= R: one minibatch)."""
     rows = np.asarray(rows)
     return np.zeros_like(rows) if mb <= 0 or mb >= R else rows // mb
+
+
+def wgrad_mx_allow(A_exact, A_fixed, B_exact, B_fixed, mbs):
+    """How far ``wgrad_mx`` may move when an operand is a GEMM output rounded
+    to bf16 and then quantised: per segment, the spread of each such operand's
+    codes (``qd_spread_rows`` of its exact values, A_exact / B_exact; None for
+    an operand that is an input) through |the other operand|, both spreads
+    added.  A_fixed / B_fixed: the operands as ``wgrad_mx`` takes them."""
+    out = np.zeros((A_fixed.shape[1], B_fixed.shape[1]))
+    for b in np.unique(mbs):
+        k = mbs == b
+        qa, qb = np.abs(qd_rows(A_fixed[k])), np.abs(qd_rows(B_fixed[k]))
+        if A_exact is not None:
+            out += qd_spread_rows(A_exact[k]).T @ qb
+        if B_exact is not None:
+            out += qa.T @ qd_spread_rows(B_exact[k])
+    return out
 
 
 def wgrad_mx(A, B, mbs):
@@ -425,13 +453,16 @@ def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False, wg
     far dX_rows may move because [dg | du] is a GEMM output whose E4M3 codes
     another correct evaluation may decide differently (``qd_spread`` through
     |W_P|).  ``wgrad_mx_mb``: None = bf16 weight gradients; else MXFP8 ones
-    (``wgrad_mx``) with minibatches of that many rows (0 = one minibatch)."""
+    (``wgrad_mx``) with minibatches of that many rows (0 = one minibatch),
+    and with ``allow`` also dW_gate_allow, dW_up_allow, dW_down_allow
+    (``wgrad_mx_allow``: dg, du and w a are GEMM outputs)."""
     dYq = qd(dY)
     R, H = x.shape
     E, I, _ = wg.shape
     order = gu_order(I)
     dX = np.zeros((R, H)); dw = np.zeros(R); dX_allow = np.zeros((R, H))
     dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    W_allow = {"dW_gate": np.zeros_like(dWg), "dW_up": np.zeros_like(dWu), "dW_down": np.zeros_like(dWd)}
     for e in range(E):
         sel = np.nonzero(re == e)[0]
         if sel.size == 0:
@@ -455,9 +486,17 @@ def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False, wg
             dWg[e] = wgrad_mx(dg, xe, mbs)
             dWu[e] = wgrad_mx(du, xe, mbs)
             dWd[e] = wgrad_mx(dY[sel], wa, mbs)
+            if allow:
+                # dg, du and w a are GEMM outputs whose codes may be decided
+                # differently; x and dY are inputs
+                W_allow["dW_gate"][e] = wgrad_mx_allow(dgx, dg, None, xe, mbs)
+                W_allow["dW_up"][e] = wgrad_mx_allow(dux, du, None, xe, mbs)
+                W_allow["dW_down"][e] = wgrad_mx_allow(None, dY[sel], w[sel, None] * a, wa, mbs)
     res = {"dX_rows": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "d_row_w": dw}
     if allow:
         res["dX_rows_allow"] = dX_allow
+        if wgrad_mx_mb is not None:
+            res.update({k + "_allow": v for k, v in W_allow.items()})
     return res
 
 
@@ -566,7 +605,8 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
     w = inp["row_w"].astype(np.float64)
     I = inp["w_gate"].shape[1]
     order = gu_order(I)
-    out = {"dX": [], "dX_allow": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
+    out = {"dX": [], "dX_allow": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": [],
+           "dW_gate_allow": [], "dW_up_allow": [], "dW_down_allow": []}
     cache = {}
 
     def expert(e):
@@ -609,12 +649,13 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
                 rows_q[e] += [mbs, xs, ds]
         return rows_q[e]
 
-    def seg_q(v, mbs):
-        # one column, quantised along the rows per segment
+    def seg_q(v, mbs, f=qd_rows):
+        # one column, quantised along the rows per segment (f = qd_spread_rows:
+        # the spread of its codes)
         out = np.zeros_like(v)
         for b in np.unique(mbs):
             kk = mbs == b
-            out[kk] = qd_rows(v[kk, None])[:, 0]
+            out[kk] = f(v[kk, None])[:, 0]
         return out
 
     for key, pairs in (("gate_up", gate_up_rows), ("down", down_cols)):
@@ -628,9 +669,8 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
             dAp = dyq @ qd(bf16.decode(inp["w_down"][e][:, i]))
             s = sigmoid(g)
             dA = w[sel] * dAp
-            dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
-            du = bf16.round_rne(dA * silu(g))
-            wa = bf16.round_rne(w[sel] * silu(g) * u)
+            dgx, dux, wax = dA * u * s * (1.0 + g * (1.0 - s)), dA * silu(g), w[sel] * silu(g) * u
+            dg, du, wa = bf16.round_rne(dgx), bf16.round_rne(dux), bf16.round_rne(wax)
             if wgrad_mx_mb is None:
                 if key == "gate_up":
                     out["dW_gate"].append(dg @ X)
@@ -642,8 +682,11 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
                 if key == "gate_up":
                     out["dW_gate"].append(seg_q(dg, mbs) @ xs)
                     out["dW_up"].append(seg_q(du, mbs) @ xs)
+                    out["dW_gate_allow"].append(seg_q(dgx, mbs, qd_spread_rows) @ np.abs(xs))
+                    out["dW_up_allow"].append(seg_q(dux, mbs, qd_spread_rows) @ np.abs(xs))
                 else:
                     out["dW_down"].append(seg_q(wa, mbs) @ ds)
+                    out["dW_down_allow"].append(seg_q(wax, mbs, qd_spread_rows) @ np.abs(ds))
     return {k: np.asarray(v) for k, v in out.items()}
 
 

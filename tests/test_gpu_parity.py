@@ -245,10 +245,10 @@ def test_forward_full_layer_full_sampled():
 
 
 # ---------------------------------------------------------- expert share --
-def run_share(inp, precision="bf16", MB=0, ring_bytes=256 << 20, fwd_ctx=False, backward=False):
+def run_share(inp, precision="bf16", MB=0, ring_bytes=256 << 20, fwd_ctx=False, backward=False, wgrad_mxfp8=False):
     sh = inp["shape"]
     L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=precision, minibatch_rows=MB,
-                 ring_bytes=ring_bytes, enable_backward=backward)
+                 ring_bytes=ring_bytes, enable_backward=backward, wgrad_mxfp8=wgrad_mxfp8)
     x = dev(inp["x"])
     row_w = dev(inp["row_w"])
     packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=backward)
@@ -372,10 +372,10 @@ def test_backward_ep_bwd_sampled():
 
 
 # ----------------------------------------------------- MXFP8 backward --
-def run_backward_mxfp8(inp, MB=0, ring_bytes=256 << 20):
+def run_backward_mxfp8(inp, MB=0, ring_bytes=256 << 20, wgrad_mxfp8=False):
     sh = inp["shape"]
     L, out, (x, row_w, packed, ctx) = run_share(inp, precision="mxfp8", MB=MB, ring_bytes=ring_bytes, fwd_ctx=True,
-                                               backward=True)
+                                               backward=True, wgrad_mxfp8=wgrad_mxfp8)
     g = L.backward(ctx, x, row_w, packed, dev(inp["dY"]), sh.R)
     sync()
     return L, out, g
@@ -419,6 +419,63 @@ def test_backward_mxfp8_ep_bwd_sampled():
     L.close()
 
 
+# ------------------------------------- MXFP8 weight gradients --
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (256, 2), (200, 3)], ids=["one_mb", "mb256_ring2", "mb200_ragged"])
+def test_backward_mxfp8_wgrad_small8(MB, ring_mbs):
+    """All six backward GEMMs on MXFP8 operands; the weight gradients' operands
+    quantised along the rows in 32-row blocks of one minibatch (MB = 200:
+    segments of every length, blocks padded at each minibatch's end)."""
+    inp = share_inputs("small8")
+    sh = inp["shape"]
+    say(f"[backward mxfp8, MXFP8 weight gradients] small8 R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * (sh.H + sh.H // 32)
+    L, out, g = run_backward_mxfp8(inp, MB=MB, ring_bytes=ring, wgrad_mxfp8=True)
+    fwd = layer.forward_share_mxfp8(inp, allow=True)
+    ref = layer.backward_share_mxfp8(inp, fwd, allow=True, wgrad_mx_mb=MB)
+    assert_close(host_bf16(g["dX"]), ref["dX"], MXFP8_TOL, "dX", bf16_out=True, allow=ref["dX_allow"])
+    assert_close(g["d_row_w"].cpu().numpy(), ref["d_row_w"], MXFP8_TOL, "d_row_w")
+    # dg, du and w a are GEMM outputs quantised again: each element also gets the
+    # oracle's allowance for the E4M3 codes another correct evaluation may decide
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert_close(g[k].cpu().numpy(), ref[k], MXFP8_TOL, k, allow=ref[k + "_allow"])
+    # the bf16 weight gradients lie E4M3's error away: the MXFP8 path really ran
+    bw = layer.backward_share_mxfp8(inp, fwd)
+    rel = np.linalg.norm(g["dW_down"].double().cpu().numpy() - bw["dW_down"]) / np.linalg.norm(bw["dW_down"])
+    assert rel > 5e-3, rel
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_backward_mxfp8_wgrad_ep_bwd_sampled():
+    inp = share_inputs("ep_bwd")
+    sh = inp["shape"]
+    say(f"[backward mxfp8, MXFP8 weight gradients] EP share R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096, "
+        f"sampled from experts 0, 3 and 7")
+    L, out, g = run_backward_mxfp8(inp, MB=4096, wgrad_mxfp8=True)
+    pairs = [(0, 17), (3, 5), (7, 2047), (7, 1000)]
+    ref = layer.backward_share_mxfp8_sampled(inp, [0], pairs, pairs, wgrad_mx_mb=4096)
+    gate = np.stack([g["dW_gate"][e, i].cpu().numpy() for e, i in pairs])
+    up = np.stack([g["dW_up"][e, i].cpu().numpy() for e, i in pairs])
+    down = np.stack([g["dW_down"][e, :, i].cpu().numpy() for e, i in pairs])
+    assert_close(gate, ref["dW_gate"], MXFP8_TOL, "dW_gate (4 rows)", allow=ref["dW_gate_allow"])
+    assert_close(up, ref["dW_up"], MXFP8_TOL, "dW_up (4 rows)", allow=ref["dW_up_allow"])
+    assert_close(down, ref["dW_down"], MXFP8_TOL, "dW_down (4 columns)", allow=ref["dW_down_allow"])
+    L.close()
+
+
+def test_backward_mxfp8_wgrad_repeatable():
+    inp = share_inputs("small8")
+    sh = inp["shape"]
+    say("[determinism] small8 MXFP8 weight gradients: two runs bitwise equal")
+    ring = 2 * 256 * (sh.H + sh.H // 32)
+    L1, _, g1 = run_backward_mxfp8(inp, MB=256, ring_bytes=ring, wgrad_mxfp8=True)
+    L2, _, g2 = run_backward_mxfp8(inp, MB=256, ring_bytes=ring, wgrad_mxfp8=True)
+    for k in ("dW_gate", "dW_up", "dW_down", "dX", "d_row_w"):
+        assert torch.equal(g1[k], g2[k]), k
+    L1.close()
+    L2.close()
+
+
 # ------------------------------------------------- full-layer backward --
 def full_variant(name, **over):
     key = "full:" + name + repr(sorted(over.items()))
@@ -428,10 +485,10 @@ def full_variant(name, **over):
     return _CACHE[key]
 
 
-def run_full_backward(inp, MB=0, ring_bytes=256 << 20, router=True, precision="bf16"):
+def run_full_backward(inp, MB=0, ring_bytes=256 << 20, router=True, precision="bf16", wgrad_mxfp8=False):
     sh = inp["shape"]
     L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, minibatch_rows=MB,
-                 ring_bytes=ring_bytes, enable_backward=True, precision=precision)
+                 ring_bytes=ring_bytes, enable_backward=True, precision=precision, wgrad_mxfp8=wgrad_mxfp8)
     x = dev(inp["x"])
     wr = dev(inp["w_router"])
     bias = dev(inp["bias"]) if inp["bias"] is not None else None
@@ -552,7 +609,28 @@ def test_full_layer_mxfp8_tiny(case, MB, ring_mbs):
     L.close()
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (128, 2)], ids=["one_mb", "mb128_ring2"])
+def test_full_layer_mxfp8_wgrad_tiny(MB, ring_mbs):
+    """Full layer in MXFP8 with MXFP8 weight gradients (x rows pulled again
+    from the token rows for the gate/up gradient's operand)."""
+    case = FULL_BWD_CASES[1]
+    inp = full_variant("tiny", **case[1])
+    sh = inp["shape"]
+    say(f"[full layer mxfp8, MXFP8 weight gradients] tiny {case[0]} T={sh.T} H={sh.H} I={sh.I} E={sh.E} "
+        f"k={sh.k} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * (sh.H + sh.H // 32)
+    L, idx, w, out, g, _ = run_full_backward(inp, MB=MB, ring_bytes=ring, precision="mxfp8", wgrad_mxfp8=True)
+    fwd = layer.forward_full_mxfp8(inp, allow=True)
+    ref = layer.backward_full_mxfp8(inp, fwd=fwd, allow=True, wgrad_mx_mb=MB)
+    assert np.array_equal(idx.cpu().numpy(), ref["topk_idx"])
+    assert_close(host_bf16(g["dX"]), ref["dX"], MXFP8_TOL, "dX", bf16_out=True, allow=ref["dX_allow"])
+    for key in ("dW_gate", "dW_up", "dW_down"):
+        assert_close(g[key].cpu().numpy(), ref[key], MXFP8_TOL, key, allow=ref[key + "_allow"])
+    assert_close(g["dW_router"].cpu().numpy(), ref["dW_router"], MXFP8_TOL, "dW_router")
+    L.close()
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp8_wgrad"])
 def test_empty_schedule_forward_and_backward(precision):
     """T = R = 0: route and forward launch nothing, every backward writes its
     weight gradients as zeros, and no device error is raised."""
@@ -561,7 +639,8 @@ def test_empty_schedule_forward_and_backward(precision):
     rng = np.random.default_rng(9)
     w = [dev(bf16.encode(0.05 * rng.standard_normal(s))) for s in ((E, I, H), (E, I, H), (E, H, I))]
     wr = dev(bf16.encode(0.05 * rng.standard_normal((E, H))))
-    L = MoELayer(H=H, I=I, E=E, k=k, max_rows=512, precision=precision, enable_backward=True)
+    L = MoELayer(H=H, I=I, E=E, k=k, max_rows=512, precision=precision.split("_")[0], enable_backward=True,
+                 wgrad_mxfp8=precision.endswith("_wgrad"))
     packed = L.prepare_weights(*w, for_backward=True)
     x = torch.empty((0, H), dtype=torch.int16, device="cuda")
     idx, tw = L.route(x, wr, None, 0)

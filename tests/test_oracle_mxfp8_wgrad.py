@@ -154,3 +154,49 @@ def test_sampled_helper_matches_full_oracle_with_mx_weight_gradients():
         assert np.allclose(s["dW_gate"][n], m["dW_gate"][e, i], rtol=1e-10, atol=1e-12)
         assert np.allclose(s["dW_up"][n], m["dW_up"][e, i], rtol=1e-10, atol=1e-12)
         assert np.allclose(s["dW_down"][n], m["dW_down"][e, :, i], rtol=1e-10, atol=1e-12)
+
+
+def test_weight_gradient_allowance_bounds_perturbed_gemm_outputs():
+    """dg, du and w a are GEMM outputs rounded to bf16 and then quantised: a
+    relative change within DECISION_REL of their exact values may flip codes
+    and block scales, and the result must stay within the oracle's allowance
+    (which is zero where no decision can change)."""
+    inp = workloads.make_expert_share("small")
+    mb = 256
+    fwd = layer.forward_share_mxfp8(inp)
+    ref = layer.backward_share_mxfp8(inp, fwd, allow=True, wgrad_mx_mb=mb)
+    rng = np.random.default_rng(21)
+    re = inp["row_expert"]
+    w = inp["row_w"].astype(np.float64)
+    wd = bf16.decode(inp["w_down"])
+    x = bf16.decode(inp["x"]); dY = bf16.decode(inp["dY"])
+    e = 1
+    sel = np.nonzero(re == e)[0]
+    _, a, _, dg, du, dgx, dux = layer._dact_mxfp8(layer.qd(dY[sel]), layer.qd(wd[e].T), fwd["g"][sel],
+                                                  fwd["u"][sel], w[sel])
+    mbs = layer.minibatch_of(sel, re.size, mb)
+    for trial in range(3):
+        f = 1.0 + layer.DECISION_REL * rng.uniform(-1, 1, size=dgx.shape)
+        dgp = bf16.round_rne(dgx * f)
+        got = layer.wgrad_mx(dgp, x[sel], mbs)
+        d = np.abs(got - ref["dW_gate"][e])
+        assert np.all(d <= ref["dW_gate_allow"][e] * (1 + 1e-9) + 1e-12), trial
+        wax = w[sel, None] * a * (1.0 + layer.DECISION_REL * rng.uniform(-1, 1, size=a.shape))
+        got = layer.wgrad_mx(dY[sel], bf16.round_rne(wax), mbs)
+        d = np.abs(got - ref["dW_down"][e])
+        assert np.all(d <= ref["dW_down_allow"][e] * (1 + 1e-9) + 1e-12), trial
+    # the allowance is a small share of the gradient's size
+    r = np.sqrt(np.mean(ref["dW_gate"] ** 2))
+    assert np.mean(ref["dW_gate_allow"]) < 0.05 * r
+
+
+def test_sampled_helper_allowances_match_full_oracle():
+    inp = workloads.make_expert_share("small")
+    mb = 256
+    m = layer.backward_share_mxfp8(inp, allow=True, wgrad_mx_mb=mb)
+    pairs = [(0, 3), (3, 0)]
+    s = layer.backward_share_mxfp8_sampled(inp, [0], pairs, pairs, wgrad_mx_mb=mb)
+    for n, (e, i) in enumerate(pairs):
+        assert np.allclose(s["dW_gate_allow"][n], m["dW_gate_allow"][e, i], rtol=1e-10, atol=1e-14)
+        assert np.allclose(s["dW_up_allow"][n], m["dW_up_allow"][e, i], rtol=1e-10, atol=1e-14)
+        assert np.allclose(s["dW_down_allow"][n], m["dW_down_allow"][e, :, i], rtol=1e-10, atol=1e-14)
