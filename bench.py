@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, "
+                    help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, ep_bwd_mxfp8_dgrad, "
                          "full_bwd)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) 3 times: the known-size reference that "
@@ -53,7 +53,7 @@ def parse():
 # algorithmic work per phase (flops, bytes) -- minimum traffic: every operand
 # read once and every result written once
 # --------------------------------------------------------------------------
-def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, replay_rows=0):
+def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, replay_rows=0, mx_wgrad=False):
     ab = 1 if mx else 2                       # bytes per GEMM operand element
     sc = 1.0 / 32 if mx else 0.0             # MXFP8 scale bytes per element
     w = {}
@@ -79,8 +79,16 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
         # share: bf16 rows to arrival order; full layer: fp32 rows for the k-sum
         w["bwd_dx"] = (4.0 * R * I * H, R * 2 * I * (ab + sc) + E * H * 2 * I * (ab + sc)
                        + R * H * (2 if share else 4))
-        w["wgrad_down"] = (2.0 * R * H * I, R * H * 2 + R * I * 2 + E * H * I * 4)
-        w["wgrad_gate_up"] = (4.0 * R * H * I, R * 2 * I * 2 + R * H * 2 + E * 2 * I * H * 4)
+        if mx_wgrad:
+            # operands quantised along the rows: bf16 rows in, codes + scales out
+            # (dY, w a, dg/du, x), then the GEMMs read codes + scales
+            q = 1 + 1 / 32
+            w["wgrad_quant"] = (0.0, R * (H + I + 2 * I + H) * (2 + q))
+            w["wgrad_down"] = (2.0 * R * H * I, R * (H + I) * q + E * H * I * 4)
+            w["wgrad_gate_up"] = (4.0 * R * H * I, R * (2 * I + H) * q + E * 2 * I * H * 4)
+        else:
+            w["wgrad_down"] = (2.0 * R * H * I, R * H * 2 + R * I * 2 + E * H * I * 4)
+            w["wgrad_gate_up"] = (4.0 * R * H * I, R * 2 * I * 2 + R * H * 2 + E * 2 * I * H * 4)
         # x rows of the minibatches evicted from the ring gathered again
         w["replay"] = (0.0, replay_rows * H * 2 * 2)
         if not share:
@@ -219,8 +227,11 @@ def main():
         extra["step_ms_cold_median"] = round(sorted(cold)[2], 4)
         return dt, per, extra
 
-    def summarize(name, R, T, H, I, E, k, dt, per, steps, kind, mx=False, share=True, save_ctx=False, replay_rows=0):
-        work = phase_work(kind, R, T, H, I, E, k, mx=mx, save_ctx=save_ctx, share=share, replay_rows=replay_rows)
+    def summarize(name, R, T, H, I, E, k, dt, per, steps, kind, mx=False, share=True, save_ctx=False, replay_rows=0,
+                  mx_wgrad=False):
+        work = phase_work(kind, R, T, H, I, E, k, mx=mx, save_ctx=save_ctx, share=share, replay_rows=replay_rows,
+                          mx_wgrad=mx_wgrad)
+        mx_phases = ("gemm1", "gemm2", "bwd_dact", "bwd_dx") + (("wgrad_down", "wgrad_gate_up") if mx_wgrad else ())
         phases = {}
         gemm_flops = gemm_ms = 0.0
         for p, (ms, n) in per.items():
@@ -229,7 +240,7 @@ def main():
             if p == "route":
                 ent["roofline"] = roofline_alu(f, b, ms)
             elif f or b:
-                ent["roofline"] = roofline(f, b, ms, mx=mx and p in ("gemm1", "gemm2", "bwd_dact", "bwd_dx"))
+                ent["roofline"] = roofline(f, b, ms, mx=mx and p in mx_phases)
             phases[p] = ent
             if f and p not in ("route", "bwd_combine", "router_bwd"):
                 gemm_flops += f
@@ -306,14 +317,18 @@ def main():
             log(json.dumps(results[key]))
         del x, wg, wu, wd
 
-    for prec, key in (("bf16", "ep_bwd"), ("mxfp8", "ep_bwd_mxfp8")):
+    # ep_bwd_mxfp8: every backward GEMM on MXFP8 operands; ep_bwd_mxfp8_dgrad:
+    # MXFP8 data gradients with bf16 weight gradients (not run by default)
+    for prec, key, mxw in (("bf16", "ep_bwd", False), ("mxfp8", "ep_bwd_mxfp8", True),
+                           ("mxfp8", "ep_bwd_mxfp8_dgrad", False)):
         if key not in want:
             continue
         inp = workloads.make_expert_share("ep_bwd")
         sh = inp["shape"]
-        log(f"[bench] expert share backward {prec}: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096 (ring wraps)")
+        log(f"[bench] expert share backward {prec}{' (MXFP8 weight gradients)' if mxw else ''}: "
+            f"R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096 (ring wraps)")
         L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=4096,
-                     enable_backward=True)
+                     enable_backward=True, wgrad_mxfp8=mxw)
         x = up(inp["x"]); re = up(inp["row_expert"]); rw = up(inp["row_w"]); dY = up(inp["dY"])
         packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]), for_backward=True)
         out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
@@ -334,9 +349,9 @@ def main():
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
         MB = L.query("minibatch_rows")
         nb = -(-sh.R // MB)
-        replay_mbs = nb if prec == "mxfp8" else max(0, nb - L.query("ring_rows") // MB)
+        replay_mbs = 0 if mxw else nb if prec == "mxfp8" else max(0, nb - L.query("ring_rows") // MB)
         results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "backward",
-                                 mx=prec == "mxfp8", replay_rows=min(sh.R, replay_mbs * MB))
+                                 mx=prec == "mxfp8", replay_rows=min(sh.R, replay_mbs * MB), mx_wgrad=mxw)
         results[key].update(extra)
         results[key]["err"] = L.device_error()
         L.close()

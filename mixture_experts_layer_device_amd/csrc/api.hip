@@ -235,10 +235,11 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
     {
       Phase ph(ws, MK_PH_WGRAD_QUANT, s);
       launch_wgrad_kofs(ws->mb_counts, nb, E, ws->wq_kofs, ws->wq_order, s);
-      launch_quant_wgrad_operand(ws->dye, H, nullptr, 1, H, ws->wq_kofs, E, ws->mb_counts, ws->mb_offsets, nb, MB,
-                                 ws->wq_kcap, ws->wq_ac, ws->wq_as, s);
-      launch_quant_wgrad_operand(ws->wa, I, nullptr, 1, I, ws->wq_kofs, E, ws->mb_counts, ws->mb_offsets, nb, MB,
-                                 ws->wq_kcap, ws->wq_bc, ws->wq_bs, s);
+      launch_wgrad_kmap(ws->wq_kofs, ws->mb_counts, ws->mb_offsets, E, nb, MB, ws->wq_kmap, s);
+      launch_quant_wgrad_operand(ws->dye, H, nullptr, 1, H, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap, ws->wq_ac,
+                                 ws->wq_as, s);
+      launch_quant_wgrad_operand(ws->wa, I, nullptr, 1, I, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap, ws->wq_bc,
+                                 ws->wq_bs, s);
     }
     {
       Phase ph(ws, MK_PH_WGRAD_DOWN, s);
@@ -247,11 +248,11 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
     }
     {
       Phase ph(ws, MK_PH_WGRAD_QUANT, s);
-      launch_quant_wgrad_operand(ws->dgdu, 2 * I, nullptr, 1, 2 * I, ws->wq_kofs, E, ws->mb_counts, ws->mb_offsets,
-                                 nb, MB, ws->wq_kcap, ws->wq_ac, ws->wq_as, s);
+      launch_quant_wgrad_operand(ws->dgdu, 2 * I, nullptr, 1, 2 * I, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap,
+                                 ws->wq_ac, ws->wq_as, s);
       if (R > 0)
-        launch_quant_wgrad_operand((const uint16_t*)x_src, H, ws->inv, src_div, H, ws->wq_kofs, E, ws->mb_counts,
-                                   ws->mb_offsets, nb, MB, ws->wq_kcap, ws->wq_bc, ws->wq_bs, s);
+        launch_quant_wgrad_operand((const uint16_t*)x_src, H, ws->inv, src_div, H, ws->wq_kofs, E, ws->wq_kmap,
+                                   ws->wq_kcap, ws->wq_bc, ws->wq_bs, s);
     }
     Phase ph(ws, MK_PH_WGRAD_GU, s);
     launch_wgrad_gate_up_mxfp8(E, H, I, ws->wq_kofs, ws->wq_order, ws->wq_ac, ws->wq_as, ws->wq_bc, ws->wq_bs,
@@ -392,7 +393,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     ws->rsplits_max = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ((int64_t)64 << 20) / per_split));
     o_rp = c.take((size_t)ws->rsplits_max * per_split);
   }
-  size_t o_wk = 0, o_wo = 0, o_wac = 0, o_was = 0, o_wbc = 0, o_wbs = 0;
+  size_t o_wk = 0, o_wo = 0, o_wm = 0, o_wac = 0, o_was = 0, o_wbc = 0, o_wbs = 0;
   if (cfg->wgrad_mxfp8) {
     // every expert's K range: its minibatch segments rounded up to 32 rows,
     // the total to 128
@@ -401,6 +402,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     const int64_t ca = std::max(H, 2 * I), cb = std::max(H, I);
     o_wk = c.take((size_t)(E + 1) * 4);
     o_wo = c.take((size_t)E * 4);
+    o_wm = c.take((size_t)ws->wq_kcap * 4);
     o_wac = c.take((size_t)(ca * ws->wq_kcap));
     o_was = c.take((size_t)(ca * ws->wq_kcap / 32));
     o_wbc = c.take((size_t)(cb * ws->wq_kcap));
@@ -450,6 +452,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   if (cfg->wgrad_mxfp8) {
     ws->wq_kofs = (int32_t*)(b + o_wk);
     ws->wq_order = (int32_t*)(b + o_wo);
+    ws->wq_kmap = (int32_t*)(b + o_wm);
     ws->wq_ac = (uint8_t*)(b + o_wac);
     ws->wq_as = (uint8_t*)(b + o_was);
     ws->wq_bc = (uint8_t*)(b + o_wbc);

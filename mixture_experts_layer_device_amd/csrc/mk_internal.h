@@ -48,6 +48,7 @@ struct mk_workspace {
   // MXFP8 weight gradients: K table of the experts' padded row spaces and the
   // operands quantised along the rows, in the tiled MXFP8 layout
   int32_t *wq_kofs, *wq_order;  // [E+1] start of expert e's K range; [E] experts by descending K
+  int32_t* wq_kmap;             // [kcap] position of each K row, -1 for pad rows
   int64_t wq_kcap;              // K capacity (multiple of 128)
   uint8_t *wq_ac, *wq_as;       // A operand: max(H, 2I) x kcap codes, / 32 scales
   uint8_t *wq_bc, *wq_bs;       // B operand: H x kcap codes (H >= I), / 32 scales
@@ -120,15 +121,18 @@ void launch_quant_tile_rows(const uint16_t* src_a, const uint16_t* src_b, int mo
 // rounded up to 32, the expert's total rounded up to 128; order = the experts
 // by descending K (ties: lower id first).
 void launch_wgrad_kofs(const int32_t* mb_counts, int nb, int E, int32_t* kofs, int32_t* order, hipStream_t s);
+// kmap[k] for k < kofs[E]: the position p of K row k, -1 for a pad row
+void launch_wgrad_kmap(const int32_t* kofs, const int32_t* mb_counts, const int32_t* mb_offsets, int E, int nb,
+                       int MB, int32_t* kmap, hipStream_t s);
 // Operand T[c][k] (C columns of the source rows, C % 256 == 0) quantised along
 // k in 32-blocks, stored per expert in the tiled MXFP8 layout: expert e's
 // blocks start at block (C/256) * kofs[e]/128 and run (row tile c/256, k step);
-// row k of expert e is position p of its segment (pad rows are zero); the
-// source row of p is src + (inv ? inv[p] / src_div : p) * ld.  Grid covers
-// kcap / 128 k steps; steps past kofs[E] exit.
+// row k is position kmap[k] (pad rows are zero); the source row of p is
+// src + (inv ? inv[p] / src_div : p) * ld.  Grid covers kcap / 128 k steps;
+// steps past kofs[E] exit.
 void launch_quant_wgrad_operand(const uint16_t* src, int64_t ld, const int32_t* inv, int src_div, int C,
-                                const int32_t* kofs, int E, const int32_t* mb_counts, const int32_t* mb_offsets,
-                                int nb, int MB, int64_t kcap, uint8_t* codes, uint8_t* scales, hipStream_t s);
+                                const int32_t* kofs, int E, const int32_t* kmap, int64_t kcap, uint8_t* codes,
+                                uint8_t* scales, hipStream_t s);
 void launch_quant_tile_cols(const uint16_t* src_a, const uint16_t* src_b, int mode, int E, int N, int K,
                             uint8_t* codes, uint8_t* scales, hipStream_t s);
 void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);

@@ -462,17 +462,40 @@ __global__ __launch_bounds__(1024) void wgrad_kofs_kernel(const int32_t* __restr
   if (e == 0) kofs[E] = sc[E - 1];
 }
 
+// Row map of the K space: kmap[k] = position p of row k (or -1 for a pad
+// row).  Workgroup (b, e) writes segment (b, e): its K start is kofs[e] plus
+// the 32-rounded lengths of the later minibatches (the walk is nb-1 .. 0);
+// the last segment of the walk (b = 0) also covers the expert's pad to 128.
+__global__ __launch_bounds__(256) void wgrad_kmap_kernel(const int32_t* __restrict__ kofs,
+                                                         const int32_t* __restrict__ mb_counts,
+                                                         const int32_t* __restrict__ mb_offsets, int E, int nb, int MB,
+                                                         int32_t* __restrict__ kmap) {
+  __shared__ int sstart;
+  const int b = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
+  if (tid == 0) {
+    int st = kofs[e];
+    for (int q = nb - 1; q > b; --q) st += (mb_counts[q * E + e] + 31) & ~31;
+    sstart = st;
+  }
+  __syncthreads();
+  const int st = sstart;
+  const int n = mb_counts[b * E + e];
+  const int base = b * MB + mb_offsets[b * (E + 1) + e];
+  const int end = b == 0 ? kofs[e + 1] : st + ((n + 31) & ~31);
+  for (int j = tid; st + j < end; j += 256) kmap[st + j] = j < n ? base + j : -1;
+}
+
 // Workgroup (256-column tile ct, global k step kc): the 128 rows of the step
-// (each resolved to its position through the expert's segments, walked in
-// reverse minibatch order) x 256 columns go to LDS with 16-byte loads, then
-// each thread quantises a 32-row column block (quant_block) and stores its two
-// code granules and scale byte in the tiled block, as quant_tile_cols does.
+// x 256 columns come to LDS (16 loads of 16 bytes per thread, all issued
+// before the first LDS store), then thread r quantises column r's four
+// 32-row blocks (quant_block) and writes the tiled block's row r whole: its
+// 128 code bytes and its scale dword.
 __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
     const uint16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ inv, int src_div, int C,
-    const int32_t* __restrict__ kofs, int E, const int32_t* __restrict__ mb_counts,
-    const int32_t* __restrict__ mb_offsets, int nb, int MB, uint8_t* __restrict__ codes,
+    const int32_t* __restrict__ kofs, int E, const int32_t* __restrict__ kmap, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
   constexpr int LD = MXT_ROWS + 8;
+  constexpr int PER = MXT_K * (MXT_ROWS / 8) / 256;    // 16-byte loads per thread
   __shared__ __attribute__((aligned(16))) uint16_t t[MXT_K][LD];
   __shared__ int64_t srow[MXT_K];
   const int ct = blockIdx.x, kc = blockIdx.y, tid = threadIdx.x;
@@ -487,54 +510,47 @@ __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
   const int e = lo;
   const int ke = kofs[e], kpad = kofs[e + 1] - ke;
   if (tid < MXT_K) {
-    const int kk = k0 - ke + tid;               // row within the expert's K range
-    int64_t row = -1;
-    int acc = 0;
-    for (int b = nb - 1; b >= 0; --b) {
-      const int n = mb_counts[b * E + e];
-      const int l32 = (n + 31) & ~31;
-      if (kk < acc + l32) {
-        const int r = kk - acc;
-        if (r < n) {
-          const int64_t p = (int64_t)b * MB + mb_offsets[b * (E + 1) + e] + r;
-          row = inv ? (int64_t)(inv[p] / src_div) : p;
-        }
-        break;
-      }
-      acc += l32;
-    }
-    srow[tid] = row;
+    const int p = kmap[k0 + tid];
+    srow[tid] = p < 0 ? -1 : inv ? (int64_t)(inv[p] / src_div) : (int64_t)p;
   }
   __syncthreads();
   const int c0 = ct * MXT_ROWS;
-  for (int q = tid; q < MXT_K * (MXT_ROWS / 8); q += 256) {
-    const int kk = q / (MXT_ROWS / 8), c = (q % (MXT_ROWS / 8)) * 8;
+  u32x4_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = tid + i * 256;
+    const int kk = q >> 5, c = (q & 31) * 8;
     const int64_t row = srow[kk];
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row >= 0) v = *(const u32x4_t*)(src + row * ld + c0 + c);
-    *(u32x4_t*)&t[kk][c] = v;
+    v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (row >= 0) v[i] = *(const u32x4_t*)(src + row * ld + c0 + c);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = tid + i * 256;
+    *(u32x4_t*)&t[q >> 5][(q & 31) * 8] = v[i];
   }
   __syncthreads();
   const int64_t blk = (int64_t)(C / MXT_ROWS) * (ke / MXT_K) + (int64_t)ct * (kpad / MXT_K) + (k0 - ke) / MXT_K;
-  uint8_t* cblk = codes + blk * MXT_CODES;
-  uint8_t* sblk = scales + blk * MXT_SCALES;
-  for (int q = tid; q < MXT_ROWS * (MXT_K / 32); q += 256) {
-    const int r = q % MXT_ROWS, kb = q / MXT_ROWS;
-    u32x4_t v[4];
+  const int r = tid;
+  uint8_t* crow = codes + blk * MXT_CODES + r * MXT_K;
+  uint32_t sc = 0;
+#pragma unroll
+  for (int kb = 0; kb < MXT_K / 32; ++kb) {
+    u32x4_t w[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int k = kb * 32 + g * 8 + 2 * d;
-        v[g][d] = (uint32_t)t[k][r] | ((uint32_t)t[k + 1][r] << 16);
+        w[g][d] = (uint32_t)t[k][r] | ((uint32_t)t[k + 1][r] << 16);
       }
     u32x4_t cc[2];
-    const uint32_t sv = quant_block(v, cc);
+    sc |= quant_block(w, cc) << (8 * kb);
     const int g0 = kb * 2;
-    *(u32x4_t*)(cblk + r * MXT_K + (((g0 ^ tkey(r)) & 7) << 4)) = cc[0];
-    *(u32x4_t*)(cblk + r * MXT_K + ((((g0 + 1) ^ tkey(r)) & 7) << 4)) = cc[1];
-    sblk[r * 4 + kb] = (uint8_t)sv;
+    *(u32x4_t*)(crow + (((g0 ^ tkey(r)) & 7) << 4)) = cc[0];
+    *(u32x4_t*)(crow + ((((g0 + 1) ^ tkey(r)) & 7) << 4)) = cc[1];
   }
+  *(uint32_t*)(scales + blk * MXT_SCALES + r * 4) = sc;
 }
 
 }  // namespace
@@ -543,11 +559,17 @@ void launch_wgrad_kofs(const int32_t* mb_counts, int nb, int E, int32_t* kofs, i
   hipLaunchKernelGGL(wgrad_kofs_kernel, dim3(1), dim3(1024), 0, s, mb_counts, nb, E, kofs, order);
 }
 
+void launch_wgrad_kmap(const int32_t* kofs, const int32_t* mb_counts, const int32_t* mb_offsets, int E, int nb,
+                       int MB, int32_t* kmap, hipStream_t s) {
+  if (nb > 0)
+    hipLaunchKernelGGL(wgrad_kmap_kernel, dim3(nb, E), dim3(256), 0, s, kofs, mb_counts, mb_offsets, E, nb, MB, kmap);
+}
+
 void launch_quant_wgrad_operand(const uint16_t* src, int64_t ld, const int32_t* inv, int src_div, int C,
-                                const int32_t* kofs, int E, const int32_t* mb_counts, const int32_t* mb_offsets,
-                                int nb, int MB, int64_t kcap, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                                const int32_t* kofs, int E, const int32_t* kmap, int64_t kcap, uint8_t* codes,
+                                uint8_t* scales, hipStream_t s) {
   hipLaunchKernelGGL(quant_wgrad_operand_kernel, dim3(C / MXT_ROWS, (unsigned)(kcap / MXT_K)), dim3(256), 0, s, src,
-                     ld, inv, src_div, C, kofs, E, mb_counts, mb_offsets, nb, MB, codes, scales);
+                     ld, inv, src_div, C, kofs, E, kmap, codes, scales);
 }
 
 
