@@ -71,7 +71,9 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
         # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
         # (MXFP8: read twice, written as bf16 rows and as codes + scales)
         src = (R if share else T) * H * 2
-        w["bwd_gather"] = (0.0, src + R * H * 2 + (src + R * H * (ab + sc) if mx else 0))
+        # (MXFP8 weight gradients: no bf16 copy; their dY operand is read from the rows)
+        w["bwd_gather"] = (0.0, src + (R * H * (ab + sc) if mx_wgrad else
+                                       R * H * 2 + (src + R * H * (ab + sc) if mx else 0)))
         w["bwd_dact"] = (2.0 * R * H * I, R * H * (ab + sc) + E * I * H * (ab + sc) + R * 2 * I * 4 + R * 2 * I * 2
                          + R * I * 2)
         if mx:

@@ -162,9 +162,11 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   // keeps the bf16 rows for the down-projection weight gradient
   {
     Phase ph(ws, MK_PH_BWD_GATHER, s);
+    // (with MXFP8 weight gradients the bf16 copy is not needed: their dY
+    // operand is quantised along the rows straight from the dY rows)
     if (mx)
       launch_gather_rows_mxfp8((const uint16_t*)dY, H, ws->inv, src_div, 0, npos_used, 0, ws->dye_c, ws->dye_s,
-                               ws->n_cu, s, ws->dye);
+                               ws->n_cu, s, ws->cfg.wgrad_mxfp8 ? nullptr : ws->dye);
     else
       launch_gather_rows((const uint16_t*)dY, H, ws->inv, src_div, 0, npos_used, 0, ws->dye, ws->n_cu, s);
   }
@@ -236,8 +238,9 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
       Phase ph(ws, MK_PH_WGRAD_QUANT, s);
       launch_wgrad_kofs(ws->mb_counts, nb, E, ws->wq_kofs, ws->wq_order, s);
       launch_wgrad_kmap(ws->wq_kofs, ws->mb_counts, ws->mb_offsets, E, nb, MB, ws->wq_kmap, s);
-      launch_quant_wgrad_operand(ws->dye, H, nullptr, 1, H, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap, ws->wq_ac,
-                                 ws->wq_as, s);
+      if (R > 0)
+        launch_quant_wgrad_operand((const uint16_t*)dY, H, ws->inv, src_div, H, ws->wq_kofs, E, ws->wq_kmap,
+                                   ws->wq_kcap, ws->wq_ac, ws->wq_as, s);
       launch_quant_wgrad_operand(ws->wa, I, nullptr, 1, I, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap, ws->wq_bc,
                                  ws->wq_bs, s);
     }
