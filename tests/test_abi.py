@@ -81,3 +81,34 @@ def test_quantize_rejects_bad_k_without_gpu():
 def test_status_strings():
     assert B.mk_status_string(0) == "ok"
     assert "ring" in B.mk_status_string(B.MK_ERR_RING)
+
+
+def test_wgrad_mxfp8_needs_mxfp8_and_the_backward():
+    for prec, bwd in ((B.MK_BF16, 1), (B.MK_MXFP8, 0)):
+        c = B.mk_config_default(); c.precision = prec; c.enable_backward = bwd; c.wgrad_mxfp8 = 1
+        with pytest.raises(B.MkError) as ei:
+            B.mk_workspace_create(c, 8192, 256, 256, 8, 2)
+        assert ei.value.status == B.MK_ERR_CONFIG, (prec, bwd)
+
+
+def test_config_struct_layout_matches_the_header(tmp_path):
+    """sizeof and every field offset of mk_config as a C compiler lays it out
+    from include/mk.h, against the binding's ctypes structure."""
+    import ctypes
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    fields = [f[0] for f in B.MkConfig._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mk.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(mk_config));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(mk_config, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(B.MkConfig)
+    assert got[1:] == [getattr(B.MkConfig, f).offset for f in fields]
