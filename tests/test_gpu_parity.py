@@ -446,6 +446,32 @@ def test_backward_mxfp8_wgrad_small8(MB, ring_mbs):
     L.close()
 
 
+def test_backward_mxfp8_wgrad_absent_experts():
+    """Experts 2 and 5 get no rows and expert 6 only rows of the last
+    minibatch: their K ranges are empty or one segment, and the gradients of
+    the absent experts are exactly zero."""
+    inp = dict(share_inputs("small8"))
+    sh = inp["shape"]
+    re = inp["row_expert"].copy()
+    re[(re == 2) | (re == 5)] = 0
+    MB = 256
+    last = (np.arange(sh.R) // MB) == (sh.R - 1) // MB
+    re[(re == 6) & ~last] = 1
+    inp["row_expert"] = re
+    say(f"[backward mxfp8, MXFP8 weight gradients] small8 with experts 2, 5 absent, 6 in the last minibatch only, "
+        f"MB={MB}")
+    L, out, g = run_backward_mxfp8(inp, MB=MB, wgrad_mxfp8=True)
+    fwd = layer.forward_share_mxfp8(inp, allow=True)
+    ref = layer.backward_share_mxfp8(inp, fwd, allow=True, wgrad_mx_mb=MB)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        got = g[k].cpu().numpy()
+        assert not np.any(got[[2, 5]]), k
+        assert_close(got, ref[k], MXFP8_TOL, k, allow=ref[k + "_allow"])
+    assert_close(host_bf16(g["dX"]), ref["dX"], MXFP8_TOL, "dX", bf16_out=True, allow=ref["dX_allow"])
+    assert L.device_error() == 0
+    L.close()
+
+
 def test_backward_mxfp8_wgrad_ep_bwd_sampled():
     inp = share_inputs("ep_bwd")
     sh = inp["shape"]
