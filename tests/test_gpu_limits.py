@@ -1,0 +1,115 @@
+"""GPU parity at the limits and in the degenerate cases of the layer: the
+largest expert count and top-k the workspace takes, one expert (the layer is
+then a dense SwiGLU MLP and the router carries no gradient), and every expert
+chosen (k = E)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads
+from helpers import BF16_TOL, ROUTER_W_ATOL, assert_close, dev, host_bf16, say
+from oracle import bf16, layer, route, schedule
+
+pytestmark = pytest.mark.gpu
+
+from mixture_experts_layer_device_amd import binding as B  # noqa: E402
+from mixture_experts_layer_device_amd.layer import MoELayer  # noqa: E402
+
+MAX_E, MAX_K = 1024, 32
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_route_at_max_experts_and_topk(renorm):
+    T, H = 64, 256
+    say(f"[limits] route T={T} H={H} E={MAX_E} k={MAX_K} renorm={renorm}, biased")
+    rng = np.random.default_rng(31 + renorm)
+    x = bf16.encode(rng.standard_normal((T, H)))
+    wr = bf16.encode(rng.standard_normal((MAX_E, H)) / 16.0)
+    bias = (rng.standard_normal(MAX_E) * np.sqrt(0.5)).astype(np.float32)
+    idx_ref, w_ref, _ = route.route(bf16.decode(x).astype(np.float32), bf16.decode(wr).astype(np.float32), bias,
+                                    MAX_K, renorm)
+    L = MoELayer(H=H, I=128, E=MAX_E, k=MAX_K, max_rows=T * MAX_K, renorm=renorm)
+    idx, w = L.route(dev(x), dev(wr), dev(bias), T)
+    idx = idx.cpu().numpy()
+    assert np.array_equal(idx, idx_ref)
+    assert all(len(set(row)) == MAX_K for row in idx.tolist())
+    err = float(np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_ref)))
+    say(f"  router weights max|err| = {err:.2e}")
+    assert err <= ROUTER_W_ATOL
+    L.close()
+
+
+def test_schedule_at_max_experts():
+    R, MB = 8192, 2048
+    say(f"[limits] schedule R={R} E={MAX_E} MB={MB}")
+    rng = np.random.default_rng(33)
+    re = rng.choice(MAX_E, size=R, p=workloads.zipf_local_weights(MAX_E, 1.2)).astype(np.int32)
+    L = MoELayer(H=256, I=128, E=MAX_E, k=1, max_rows=R, minibatch_rows=MB, ring_bytes=2 * MB * 512)
+    L.build_schedule(dev(re), R)
+    ref = schedule.build(re, MAX_E, MB, L.query("ring_rows"), L.query("tile_m"))
+    nb = R // MB
+    for name, n, want in (("counts", MAX_E, ref.counts), ("offsets", MAX_E + 1, ref.offsets),
+                          ("sorted_pos", R, ref.sorted_pos), ("inv", nb * MB, ref.inv),
+                          ("mb_offsets", nb * (MAX_E + 1), ref.mb_offsets)):
+        assert np.array_equal(L.table(name, n).cpu().numpy(), np.asarray(want).reshape(-1)), name
+    assert L.device_error() == 0
+    L.close()
+
+
+def _full_layer(sh, precision="bf16"):
+    inp = workloads.make_full_layer(sh)
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, enable_backward=True,
+                 precision=precision)
+    x, wr = dev(inp["x"]), dev(inp["w_router"])
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+    idx, w = L.route(x, wr, bias, sh.T)
+    L.build_schedule(idx.view(-1), sh.R)
+    ctx = L.new_fwd_ctx()
+    out = L.forward(B.MK_FULL_LAYER, x, w.view(-1), packed, sh.T, fwd_ctx=ctx)
+    g = L.backward_layer(ctx, x, wr, bias, idx, w, packed, dev(inp["dY"]), sh.T)
+    return inp, L, idx, w, out, g
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_single_expert_is_a_dense_swiglu_mlp(renorm):
+    """E = 1, k = 1: every token goes to expert 0 with weight exactly 1, so
+    the output is the dense SwiGLU MLP, and the softmax Jacobian of one logit
+    is zero: dW_router and d_bias are exactly 0."""
+    sh = dataclasses.replace(workloads.FULL_LAYER["tiny"], E=1, k=1, I=256, renorm=renorm, bias_var=0.5, seed=35)
+    say(f"[limits] single expert T={sh.T} H={sh.H} I={sh.I} renorm={renorm}")
+    inp, L, idx, w, out, g = _full_layer(sh)
+    assert not np.any(idx.cpu().numpy())
+    assert np.all(w.cpu().numpy() == 1.0)
+    # the dense MLP written out: a rounded to bf16 (a GEMM operand), y exact, out rounded once
+    x = bf16.decode(inp["x"])
+    wg, wu, wd = (bf16.decode(inp[n])[0] for n in ("w_gate", "w_up", "w_down"))
+    gg, uu = x @ wg.T, x @ wu.T
+    a = bf16.round_rne(gg / (1.0 + np.exp(-gg)) * uu)
+    assert_close(host_bf16(out), bf16.round_rne(a @ wd.T), BF16_TOL, "out vs dense SwiGLU MLP", bf16_out=True)
+    ref = layer.backward_full(inp)
+    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
+    assert not np.any(g["dW_router"].cpu().numpy()) and not np.any(g["d_bias"].cpu().numpy())
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_every_expert_chosen():
+    """k = E: each token's rows go to all experts, in descending logit order."""
+    sh = dataclasses.replace(workloads.FULL_LAYER["tiny"], k=8, I=256, renorm=1, bias_var=0.5, seed=37)
+    say(f"[limits] k = E = {sh.E}, T={sh.T} H={sh.H} I={sh.I}")
+    inp, L, idx, w, out, g = _full_layer(sh)
+    idx = idx.cpu().numpy()
+    assert all(sorted(row) == list(range(sh.E)) for row in idx.tolist())
+    fwd = layer.forward_full(inp)
+    assert np.array_equal(idx, fwd["topk_idx"])
+    assert_close(host_bf16(out), fwd["out"], BF16_TOL, "out", bf16_out=True)
+    ref = layer.backward_full(inp)
+    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
+    for k in ("dW_gate", "dW_up", "dW_down", "dW_router", "d_bias"):
+        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
+    assert L.device_error() == 0
+    L.close()
