@@ -10,10 +10,12 @@
 // Workgroup = RT tokens x all experts, in chunks of RE experts.  x and the
 // router rows are staged through LDS per RH-wide slice of h, converted to fp32
 // once (x as [token][h], the router rows transposed to [h][expert]), double-
-// buffered with the next slice's global loads in registers.  Thread (tx, ty)
-// keeps the chains of tokens 2ty, 2ty+1 x experts 4tx .. 4tx+3: per 8 h, four
-// 16-byte x reads and eight 16-byte router reads (broadcast across the lanes
-// that share them) feed 64 FMAs, read one group ahead.  Top-k
+// buffered with the next slice's global loads in registers.  512 threads (two
+// waves per SIMD, so one wave's LDS and barrier waits are covered by the
+// other's FMAs); thread (tx, ty) keeps the chains of token ty x experts
+// 4tx .. 4tx+3: per 8 h, two 16-byte x reads and eight 16-byte router reads
+// (broadcast across the lanes that share them) feed 32 FMAs, read one group
+// ahead.  Top-k
 // then runs one wave per token over the logits kept in LDS: k rounds of a
 // wave-wide (max logit, min id) reduction.  The LOGITS variant stops after
 // the logits and stores them (the router backward needs the full softmax).
@@ -26,7 +28,9 @@ namespace {
 constexpr int RT = 16;     // tokens per workgroup
 constexpr int RE = 128;    // experts per chunk
 constexpr int RH = 64;     // h per LDS slice
-constexpr int RNT = 256;   // threads
+constexpr int RNT = 512;   // threads
+constexpr int TPT = RT * 32 / RNT;        // tokens per thread (32 threads span the RE experts)
+constexpr int SQN = RH * 128 / RNT / 8;   // 8-h granules of a router row each thread stages
 
 __device__ __forceinline__ bool better(float za, int ea, float zb, int eb) {
   return za > zb || (za == zb && ea < eb);
@@ -43,28 +47,28 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
   const int tid = threadIdx.x;
   const int tx = tid & 31, ty = tid >> 5;
   const int t0 = blockIdx.x * RT;
-  // staging roles: router row e0 + (tid & 127), h half (tid >> 7) of the
-  // slice (32 h); threads 0..127 also stage token tid >> 3, h eighth (tid & 7)
-  const int se = tid & 127, sh = (tid >> 7) * 32;
+  // staging roles: router row e0 + (tid & 127), h part (tid >> 7) of the
+  // slice (8 SQN h); threads 0..127 also stage token tid >> 3, h eighth (tid & 7)
+  const int se = tid & 127, sh = (tid >> 7) * 8 * SQN;
   const int st_tok = tid >> 3, sq = (tid & 7) * 8;
   const bool x_stager = tid < 128 && t0 + st_tok < T;
   for (int e0 = 0; e0 < E; e0 += RE) {
     const bool w_valid = e0 + se < E;
     const uint16_t* wrow = w + (int64_t)(w_valid ? e0 + se : 0) * H + sh;
     const uint16_t* xrow = x + (int64_t)(x_stager ? t0 + st_tok : 0) * H + sq;
-    u32x4_t wr[4], xr{0u, 0u, 0u, 0u};
+    u32x4_t wr[SQN], xr{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wr[q] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int q = 0; q < SQN; ++q) wr[q] = u32x4_t{0u, 0u, 0u, 0u};
     auto load = [&](int h0) {
       if (w_valid) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wr[q] = *(const u32x4_t*)(wrow + h0 + 8 * q);
+        for (int q = 0; q < SQN; ++q) wr[q] = *(const u32x4_t*)(wrow + h0 + 8 * q);
       }
       if (x_stager) xr = *(const u32x4_t*)(xrow + h0);
     };
     auto stage = [&](int buf) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < SQN; ++q)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           ws[buf][sh + 8 * q + 2 * d][se] = bf16_to_f32(wr[q][d] & 0xFFFFu);
@@ -83,9 +87,9 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
         *(f32x4_t*)&xs[buf][st_tok][sq + 4] = hi;
       }
     };
-    float acc[2][4];
+    float acc[TPT][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TPT; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
     load(0);
@@ -97,23 +101,22 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
       // FMAs so their latency is covered; per group: 8 h of each of the
       // thread's 2 tokens (two 16-byte reads each) and 4 experts per h
       f32x4_t wa[8], wb[8];
-      f32x4_t xa[2][2], xb[2][2];
-      auto rdg = [&](int h, f32x4_t (&wv)[8], f32x4_t (&xv)[2][2]) {
+      f32x4_t xa[TPT][2], xb[TPT][2];
+      auto rdg = [&](int h, f32x4_t (&wv)[8], f32x4_t (&xv)[TPT][2]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) wv[u] = *(const f32x4_t*)&ws[buf][h + u][4 * tx];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TPT; ++i)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) xv[i][q] = *(const f32x4_t*)&xs[buf][2 * ty + i][h + 4 * q];
+          for (int q = 0; q < 2; ++q) xv[i][q] = *(const f32x4_t*)&xs[buf][TPT * ty + i][h + 4 * q];
       };
-      auto fmg = [&](const f32x4_t (&wv)[8], const f32x4_t (&xv)[2][2]) {
+      auto fmg = [&](const f32x4_t (&wv)[8], const f32x4_t (&xv)[TPT][2]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[0][j] = __builtin_fmaf(xv[0][u / 4][u % 4], wv[u][j], acc[0][j]);
-            acc[1][j] = __builtin_fmaf(xv[1][u / 4][u % 4], wv[u][j], acc[1][j]);
-          }
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) acc[i][j] = __builtin_fmaf(xv[i][u / 4][u % 4], wv[u][j], acc[i][j]);
       };
       rdg(0, wa, xa);
 #pragma unroll
@@ -130,12 +133,12 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
       if (e < E) {
         const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TPT; ++i) {
           const float z = bias ? acc[i][j] + b : acc[i][j];
           if (LOGITS) {
-            if (t0 + 2 * ty + i < T) z_out[(int64_t)(t0 + 2 * ty + i) * E + e] = z;
+            if (t0 + TPT * ty + i < T) z_out[(int64_t)(t0 + TPT * ty + i) * E + e] = z;
           } else {
-            zbuf[(2 * ty + i) * E + e] = z;
+            zbuf[(TPT * ty + i) * E + e] = z;
           }
         }
       }
