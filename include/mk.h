@@ -224,7 +224,12 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const floa
  * gate/up features, blocks of 32), fp32 accumulation; the weight gradients
  * are bf16 GEMMs as in bf16 mode.  Evicted minibatches (an MXFP8 ring holds
  * codes, so all of them) have their x rows gathered again before the
- * gate/up weight gradient.
+ * gate/up weight gradient.  With cfg.wgrad_mxfp8 the weight gradients are
+ * MXFP8 GEMMs too: dY rows, w*a, dg/du and x rows each quantised along the
+ * rows of an expert (32 rows of one minibatch per block, a minibatch's last
+ * block completed with zero rows), dY and x read straight from dY_dev and
+ * x_src_dev through the schedule's inverse map; fp32 accumulation, each
+ * output element by one workgroup over the expert's rows in a fixed order.
  *   mode MK_EXPERT_SHARE: x_src_dev [R, H], row_w_dev [R], dY_dev [R, H] and
  *       dX_dev [R, H] in arrival order; d_row_w_dev [R] fp32.
  *   mode MK_FULL_LAYER: x_src_dev [T, H], row_w_dev = topk_w [T*k],
