@@ -1,7 +1,7 @@
 """GPU parity at the limits and in the degenerate cases of the layer: the
 largest expert count and top-k the workspace takes, one expert (the layer is
-then a dense SwiGLU MLP and the router carries no gradient), and every expert
-chosen (k = E)."""
+then a dense SwiGLU MLP and the router carries no gradient), every expert
+chosen (k = E), and MXFP8 weight gradients over many tiny minibatch segments."""
 import dataclasses
 
 import numpy as np
@@ -111,5 +111,30 @@ def test_every_expert_chosen():
     assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
     for k in ("dW_gate", "dW_up", "dW_down", "dW_router", "d_bias"):
         assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_mxfp8_weight_gradients_many_experts_and_minibatches():
+    """E = 64 experts over 32 minibatches of 128 rows: most (minibatch, expert)
+    segments hold a handful of rows or none, so nearly every MX block of the
+    weight gradients is a padded segment tail."""
+    sh = workloads.ExpertShareShape("wide", R=4096, H=256, I=256, E=64, sources=8, zipf_s=1.2, seed=41)
+    inp = workloads.make_expert_share(sh)
+    MB = 128
+    say(f"[limits] MXFP8 weight gradients R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB} ({sh.R // MB} minibatches)")
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision="mxfp8", minibatch_rows=MB,
+                 ring_bytes=4 * MB * (sh.H + sh.H // 32), enable_backward=True, wgrad_mxfp8=True)
+    x, row_w = dev(inp["x"]), dev(inp["row_w"])
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+    L.build_schedule(dev(inp["row_expert"]), sh.R)
+    ctx = L.new_fwd_ctx()
+    L.forward(B.MK_EXPERT_SHARE, x, row_w, packed, sh.R, fwd_ctx=ctx)
+    g = L.backward(ctx, x, row_w, packed, dev(inp["dY"]), sh.R)
+    fwd = layer.forward_share_mxfp8(inp, allow=True)
+    ref = layer.backward_share_mxfp8(inp, fwd, allow=True, wgrad_mx_mb=MB)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert_close(g[k].cpu().numpy(), ref[k], 6e-2, k, allow=ref[k + "_allow"])
+    assert_close(host_bf16(g["dX"]), ref["dX"], 6e-2, "dX", bf16_out=True, allow=ref["dX_allow"])
     assert L.device_error() == 0
     L.close()
