@@ -54,17 +54,22 @@ __device__ __forceinline__ void read_a_pair(const char* st, int q, bf16x8_t (&a)
   for (int ii = 0; ii < 2; ++ii)
     a[ii] = *(const bf16x8_t*)(st + SwzT::off(wm * 128 + (2 * (q & 3) + ii) * 16 + (lane & 15), g));
 }
-__device__ __forceinline__ void read_b_half(const char* st, int ks, bf16x8_t (&b)[FN]) {
+// NB: rows of the B tile (256, or 128 for a half tile): a wave's NB / 4
+// columns are NB / 64 fragments.
+template <int NB = BN>
+__device__ __forceinline__ void read_b_half(const char* st, int ks, bf16x8_t (&b)[NB / 64]) {
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
   const int g = ks * 4 + (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8_t*)(st + TILE_BYTES + SwzT::off(wn * 64 + j * 16 + (lane & 15), g));
+  for (int j = 0; j < NB / 64; ++j)
+    b[j] = *(const bf16x8_t*)(st + TILE_BYTES + SwzT::off(wn * (NB / 4) + j * 16 + (lane & 15), g));
 }
-__device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t (&b)[FN], int pair, Acc& acc) {
+template <int NB = BN>
+__device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t (&b)[NB / 64], int pair, Acc& acc) {
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < NB / 64; ++j)
       acc[2 * pair + ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ii], b[j], acc[2 * pair + ii][j], 0, 0, 0);
 }
 
@@ -74,8 +79,10 @@ __device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t
 // stage's B slice.  Tiles go global -> LDS directly (no staging registers):
 // wave w fills rows 32w .. 32w+31 of each operand, 8 rows (1 KiB) per
 // instruction; for A each lane reads the granule that the swizzle puts in its
-// slot, for B the copy is 1 KiB contiguous.
-template <typename ARow>
+// slot, for B the copy is 1 KiB contiguous.  NB = 128 (a half tile): btile
+// points at rows 128h .. 128h+127 of each block (h * 8192 elements in), each
+// wave copies its 2 KiB, and only fragments j < 2 of acc are computed.
+template <int NB = BN, typename ARow>
 __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const uint16_t* btile, int K, char* lds,
                                             Acc& acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -89,13 +96,14 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
     ao[j] = (uint32_t)((const char*)arow(r) - (const char*)abase) + (((lane & 7) ^ tkey(r)) & 7) * 16;
   }
   const int wbase = wave * 4096;
-  const uint32_t bo = wbase + lane * 16;
+  const int bwbase = wave * NB * 16;                   // this wave's share of the B tile (NB rows x 128 B)
+  const uint32_t bo = bwbase + lane * 16;
   auto issue = [&](int64_t kb, char* st) {
     const uint32_t b = bo + (uint32_t)(kb / (BK * 2)) * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       b2lds16(ra, ao[j] + (uint32_t)kb, st + wbase + j * 1024);
-      b2lds16(rb, b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
+      if (j < NB / 64) b2lds16(rb, b + j * 1024, st + TILE_BYTES + bwbase + j * 1024);
     }
   };
   zero_acc(acc);
@@ -108,8 +116,8 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
   // read).  The stage's barrier sits before its last group, so the first
   // reads of the next stage are in flight while that group's MFMAs issue.
   // Scheduling barriers keep each group's reads ahead of the MFMAs before it.
-  bf16x8_t bq[2][FN], aq[2][2];
-  read_b_half(lds, 0, bq[0]);
+  bf16x8_t bq[2][NB / 64], aq[2][2];
+  read_b_half<NB>(lds, 0, bq[0]);
   read_a_pair(lds, 0, aq[0]);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
@@ -119,18 +127,18 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (q < 7) {
-        if (q == 3) read_b_half(st, 1, bq[1]);
+        if (q == 3) read_b_half<NB>(st, 1, bq[1]);
         read_a_pair(st, q + 1, aq[(q + 1) & 1]);
       } else {
         wait_all_mem();
         __syncthreads();
         if (kt + 1 < KT) {
-          read_b_half(nst, 0, bq[0]);
+          read_b_half<NB>(nst, 0, bq[0]);
           read_a_pair(nst, 0, aq[0]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      mma_group(aq[q & 1], bq[q >> 2], q & 3, acc);
+      mma_group<NB>(aq[q & 1], bq[q >> 2], q & 3, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -147,13 +155,16 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
                                                         float* __restrict__ gu_save) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = 2 * I / BN;
-  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+  // NB packed columns of the tile: NB / 2 features, a wave's NB / 4 columns
+  // being NB / 128 gate/up groups of 32
+  auto body = [&](const TileInfo& ti, auto nb) {
+    constexpr int NB = decltype(nb)::value;
     auto arow = [&](int r) {
       const int p = ti.pos0 + min(r, ti.rows - 1);
       return ring + (int64_t)(p % ring_rows) * H;
     };
     Acc acc;
-    mainloop_nt(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H), H, lds, acc);
+    mainloop_nt<NB>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -161,19 +172,25 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
       for (int v = 0; v < 4; ++v) {
         const int r = frag_row(i, v);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NB / 128; ++q) {
           const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
-          stage_put(lds, r, wn * 32 + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+          stage_put(lds, r, wn * (NB / 8) + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
           if (gu_save && r < ti.rows) {
-            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * 64 + q * 32 + (lane & 15);
+            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * (NB / 4) + q * 32 + (lane & 15);
             dst[0] = g;
             dst[16] = u;
           }
         }
       }
-    stage_flush<128>(lds, [&](int r) -> uint16_t* {
+    stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
       return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
     });
+  };
+  for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
+    if (half < 0)
+      body(ti, std::integral_constant<int, BN>{});
+    else
+      body(ti, std::integral_constant<int, BN / 2>{});
   });
 }
 

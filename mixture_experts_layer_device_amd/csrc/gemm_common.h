@@ -54,6 +54,33 @@ __device__ __forceinline__ void for_each_tile(const ItemRange& ir, int ntn, Body
   }
 }
 
+// As for_each_tile, but a last round that would leave at least half of the
+// workgroups idle is spread over twice as many workgroups: each of its tiles
+// is cut into two 128-column halves (consecutive logical ids, so both halves
+// run on one XCD and share the A rows in its L2).  body(ti, half): half = -1
+// for a whole 256-column tile, else 0 / 1 with ti.n0 already at the half.
+template <typename Body>
+__device__ __forceinline__ void for_each_tile_split(const ItemRange& ir, int ntn, Body body) {
+  const int i_lo = min(ir.mb_items[ir.mb_lo], ir.item_cap);
+  const int i_hi = min(ir.mb_items[ir.mb_hi], ir.item_cap);
+  const int n_items = i_hi - i_lo;
+  const int total = n_items * ntn;
+  const int G = gridDim.x;
+  const int rem = total % G;
+  const bool split = rem > 0 && 2 * rem <= G;
+  const int t_end = split ? total - rem : total;
+  const int b = xcd_logical_block();
+  auto tile = [&](int t, int half) {
+    int it, nt;
+    tile_coords(t, n_items, ntn, it, nt);
+    const int* item = ir.items + 4 * (i_lo + it);
+    TileInfo ti{item[0], item[1], item[2], nt * G_BN + (half > 0 ? G_BN / 2 : 0)};
+    body(ti, half);
+  };
+  for (int t = b; t < t_end; t += G) tile(t, -1);
+  if (split && b < 2 * rem) tile(t_end + b / 2, b & 1);
+}
+
 __device__ __forceinline__ int frag_row(int i, int v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   return (wave >> 2) * 128 + i * 16 + 4 * (lane >> 4) + v;
