@@ -83,6 +83,10 @@ extern "C" {
  *                       forward's (MX blocks along the contraction) with the
  *                       minibatch as the unit of arrival ([MTP] "Three design
  *                       decisions that matter": minibatch granularity).
+ *                       Its row space holds max_rows + minibatches*E*31 +
+ *                       E*127 rows (every minibatch segment rounded up to 32
+ *                       rows, every expert to 128): MK_ERR_LIMIT above
+ *                       65535 * 128 rows.
  */
 typedef struct mk_config {
   int32_t minibatch_rows;

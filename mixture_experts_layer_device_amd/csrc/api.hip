@@ -340,6 +340,18 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   ws->cpm = (ws->MB + MK_SCHED_CHUNK - 1) / MK_SCHED_CHUNK;
   const double worst = (double)((max_rows + MK_TILE_M - 1) / MK_TILE_M) + (double)ws->nb_max * E;
   ws->item_cap = (int32_t)std::max(1.0, std::ceil(cfg->sched_capacity_mult * worst));
+  if (cfg->wgrad_mxfp8) {
+    // the MXFP8 weight gradients' row space: every segment rounded up to 32
+    // rows, every expert to 128; the quantisers launch one workgroup row per
+    // 128-row K step (grid y)
+    const int64_t kc = (int64_t)max_rows + (int64_t)ws->nb_max * E * 31 + (int64_t)E * 127;
+    ws->wq_kcap = (kc + 127) / 128 * 128;
+    if (ws->wq_kcap / 128 > 65535) {
+      delete ws->events;
+      free(ws);
+      return MK_ERR_LIMIT;
+    }
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     delete ws->events;
@@ -400,8 +412,6 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   if (cfg->wgrad_mxfp8) {
     // every expert's K range: its minibatch segments rounded up to 32 rows,
     // the total to 128
-    const int64_t kc = (int64_t)max_rows + (int64_t)ws->nb_max * E * 31 + (int64_t)E * 127;
-    ws->wq_kcap = (kc + 127) / 128 * 128;
     const int64_t ca = std::max(H, 2 * I), cb = std::max(H, I);
     o_wk = c.take((size_t)(E + 1) * 4);
     o_wo = c.take((size_t)E * 4);

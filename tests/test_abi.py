@@ -112,3 +112,14 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     assert got[0] == ctypes.sizeof(B.MkConfig)
     assert got[1:] == [getattr(B.MkConfig, f).offset for f in fields]
+
+
+def test_wgrad_mxfp8_row_space_limit():
+    """Many experts over tiny minibatches: the weight gradients' padded row
+    space (every segment rounded up to 32 rows) would pass the quantisers'
+    grid limit, so the workspace is refused before any allocation."""
+    c = B.mk_config_default(); c.precision = B.MK_MXFP8; c.enable_backward = 1; c.wgrad_mxfp8 = 1
+    c.minibatch_rows = 32
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 1 << 20, 256, 256, 1024, 8)
+    assert ei.value.status == B.MK_ERR_LIMIT
