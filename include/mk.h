@@ -62,7 +62,8 @@ extern "C" {
  * "Limitations": minibatch granularity, macrobatch size via the ring, schedule
  * capacity multiplier).  The communication-SM knob has no one-GPU meaning.
  *   minibatch_rows      rows per minibatch (MB); 0 = all rows in one.  In
- *                       MK_FULL_LAYER mode a multiple of k.
+ *                       MK_FULL_LAYER mode a multiple of k.  At most 65535
+ *                       minibatches of max_rows (else MK_ERR_LIMIT).
  *   ring_bytes          ring token buffer capacity; the ring holds
  *                       MB * floor(ring_bytes / (MB * row_bytes)) rows, a whole
  *                       number of minibatches (the macrobatch).  row_bytes is

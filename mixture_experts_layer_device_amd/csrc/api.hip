@@ -336,6 +336,12 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   }
   ws->ring_rows = (int32_t)((int64_t)ws->MB * mbs_in_ring);
   ws->nb_max = (max_rows + ws->MB - 1) / ws->MB;
+  // the schedule kernels launch one workgroup row per minibatch (grid y)
+  if (ws->nb_max > 65535) {
+    delete ws->events;
+    free(ws);
+    return MK_ERR_LIMIT;
+  }
   ws->npos = (int64_t)ws->nb_max * ws->MB;
   ws->cpm = (ws->MB + MK_SCHED_CHUNK - 1) / MK_SCHED_CHUNK;
   const double worst = (double)((max_rows + MK_TILE_M - 1) / MK_TILE_M) + (double)ws->nb_max * E;

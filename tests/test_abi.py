@@ -123,3 +123,11 @@ def test_wgrad_mxfp8_row_space_limit():
     with pytest.raises(B.MkError) as ei:
         B.mk_workspace_create(c, 1 << 20, 256, 256, 1024, 8)
     assert ei.value.status == B.MK_ERR_LIMIT
+
+
+def test_minibatch_count_limit():
+    c = B.mk_config_default()
+    c.minibatch_rows = 8
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 8 * 65536, 256, 128, 8, 2)
+    assert ei.value.status == B.MK_ERR_LIMIT
