@@ -389,7 +389,9 @@ def qd_rows(v):
     """MXFP8 quantise-dequantise along the first axis: each column of v is cut
     into blocks of 32 consecutive rows, the last one completed with zero rows
     (which change neither its largest magnitude nor the other codes and are
-    dropped again)."""
+    dropped again).  The MX format itself is the one the pages name for the
+    MXFP8 mode ([CARD] "Core concepts"; [MTP] "Key Takeaways"), with the
+    element and scale rule of ``mxfp8``."""
     v = np.asarray(v, dtype=np.float64)
     n = v.shape[0]
     pad = (-n) % 32
@@ -437,8 +439,12 @@ def wgrad_mx(A, B, mbs):
     weight-gradient contraction over one expert's rows.  A [n, M] and B [n, N]
     hold the expert's rows in arrival order, mbs their minibatch; a segment is
     the rows of one minibatch, and the MX blocks of 32 rows never cross a
-    segment boundary (a minibatch's rows are the unit the schedule hands
-    over, so a block is complete once its minibatch is)."""
+    segment boundary.  The pages report an MXFP8 backward ([MTP] "Results")
+    but give no recipe for it; the reading taken here blocks along each
+    GEMM's contraction as the forward does, and takes the minibatch ([MTP]
+    "Three design decisions that matter": minibatch granularity) as the unit
+    a block may not cross, since a minibatch's rows arrive together and a
+    block is complete once its minibatch is."""
     out = np.zeros((A.shape[1], B.shape[1]))
     for b in np.unique(mbs):
         k = mbs == b
