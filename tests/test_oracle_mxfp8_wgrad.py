@@ -200,3 +200,41 @@ def test_sampled_helper_allowances_match_full_oracle():
         assert np.allclose(s["dW_gate_allow"][n], m["dW_gate_allow"][e, i], rtol=1e-10, atol=1e-14)
         assert np.allclose(s["dW_up_allow"][n], m["dW_up_allow"][e, i], rtol=1e-10, atol=1e-14)
         assert np.allclose(s["dW_down_allow"][n], m["dW_down_allow"][e, :, i], rtol=1e-10, atol=1e-14)
+
+
+def test_segments_of_whole_blocks_equal_one_segment():
+    """When every minibatch segment holds a multiple of 32 rows, the blocks
+    of the per-segment rule are exactly the consecutive 32-row blocks of the
+    expert's rows, so the result equals blocking the rows as one segment."""
+    rng = np.random.default_rng(13)
+    n = 32 * 7
+    A = rng.standard_normal((n, 5)) * np.exp2(rng.integers(-6, 6, size=(n, 1)))
+    B = rng.standard_normal((n, 3))
+    mbs = np.repeat([0, 2, 3, 5], [64, 32, 96, 32])
+    assert np.array_equal(layer.wgrad_mx(A, B, mbs), layer.wgrad_mx(A, B, np.zeros(n, dtype=int)))
+    # and a segment that is not a whole number of blocks changes the result
+    mbs2 = np.repeat([0, 1], [40, n - 40])
+    assert not np.array_equal(layer.wgrad_mx(A, B, mbs2), layer.wgrad_mx(A, B, np.zeros(n, dtype=int)))
+
+
+def test_full_layer_weight_gradients_linear_in_one_minibatchs_dy():
+    """Full layer (routed rows r = t k + j, minibatches of whole tokens): a
+    power-of-two factor on the loss gradient of the tokens of one minibatch
+    scales exactly that minibatch's part of every weight gradient."""
+    sh = workloads.FULL_LAYER["tiny"]
+    inp = workloads.make_full_layer("tiny")
+    mb_tok = 64
+    mb = mb_tok * sh.k
+    fwd = layer.forward_full_mxfp8(inp)
+    res = {}
+    for f in (1.0, 4.0, 0.5):
+        sub = dict(inp)
+        dY = bf16.decode(inp["dY"]).copy()
+        dY[mb_tok:2 * mb_tok] *= f
+        sub["dY"] = bf16.encode(dY)
+        res[f] = layer.backward_full_mxfp8(sub, fwd=fwd, wgrad_mx_mb=mb)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        c1 = (res[4.0][k] - res[1.0][k]) / 3.0
+        c0 = res[1.0][k] - c1
+        assert np.allclose(res[0.5][k], c0 + 0.5 * c1, rtol=1e-9, atol=1e-9 * np.abs(res[1.0][k]).max()), k
+        assert np.abs(c1).max() > 0.05 * np.abs(res[1.0][k]).max(), k
