@@ -164,7 +164,21 @@ def forward_share_mxfp8(inp, qw=None, allow: bool = False):
     return res
 
 
-def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool):
+def bf16_spread(v, rel: float | None = None):
+    """How far bf16(v') may lie from bf16(v), per element, over all v' with
+    |v'_i - v_i| <= rel |v_i| (rel defaults to DECISION_REL): v are the exact
+    values of a GEMM output that is rounded to bf16 as the next GEMM's
+    operand, and another correct evaluation of that GEMM may land on the
+    other side of a rounding midpoint.  Rounding is monotone, so the
+    interval's two ends bound every reachable value; 0 where no decision can
+    change."""
+    rel = DECISION_REL if rel is None else rel
+    v = np.asarray(v, dtype=np.float64)
+    ref = bf16.round_rne(v)
+    return np.maximum(np.abs(bf16.round_rne(v * (1.0 - rel)) - ref), np.abs(bf16.round_rne(v * (1.0 + rel)) - ref))
+
+
+def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool, allow: bool = False):
     """Expert backward of routed rows (arrival order), loss
     L = sum_r <dY[r], w[r] y(r)>:
 
@@ -177,12 +191,20 @@ def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool):
     dW_g[e] = dg_e^T X_e,  dW_u[e] = du_e^T X_e,  dW_d[e] = dY_e^T (w a)_e
     In bf16 mode dg, du and w*a are bf16 tensors (GEMM operands); g, u, a,
     dA' and the fp32 outputs dW, dw are exact.  Rows whose expert id is out
-    of range get zeros.
+    of range get zeros.  With ``allow`` (bf16 mode) also dW_gate_allow,
+    dW_up_allow, dW_down_allow and dX_rows_allow: how far each may move
+    because dg, du and w*a are GEMM outputs whose bf16 rounding another
+    correct evaluation may decide the other way (``bf16_spread`` through
+    |X|, |dY| and |W|).
     """
     R, H = x.shape
     E, I, _ = wg.shape
     dX = np.zeros((R, H)); dw = np.zeros(R); dw_alt = np.zeros(R)
     dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    allow = allow and bf16_mode
+    if allow:
+        A = {"dW_gate": np.zeros_like(dWg), "dW_up": np.zeros_like(dWu), "dW_down": np.zeros_like(dWd),
+             "dX_rows": np.zeros((R, H))}
     for e in range(E):
         sel = np.nonzero(re == e)[0]
         if sel.size == 0:
@@ -195,23 +217,35 @@ def _backward_rows(x, re, w, dY, wg, wu, wd, bf16_mode: bool):
         dw_alt[sel] = np.einsum("rh,rh->r", dYe, y)
         dA = w[sel, None] * dAp
         s = sigmoid(g)
-        dg = rnd(dA * u * s * (1.0 + g * (1.0 - s)), bf16_mode)
-        du = rnd(dA * silu(g), bf16_mode)
+        dgx, dux, wax = dA * u * s * (1.0 + g * (1.0 - s)), dA * silu(g), w[sel, None] * a
+        dg = rnd(dgx, bf16_mode)
+        du = rnd(dux, bf16_mode)
         dX[sel] = dg @ wg[e] + du @ wu[e]
         dWg[e] = dg.T @ xe
         dWu[e] = du.T @ xe
-        dWd[e] = dYe.T @ rnd(w[sel, None] * a, bf16_mode)
-    return {"dX_rows": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd,
-            "d_row_w": dw, "d_row_w_alt": dw_alt}
+        dWd[e] = dYe.T @ rnd(wax, bf16_mode)
+        if allow:
+            sg, su = bf16_spread(dgx), bf16_spread(dux)
+            A["dW_gate"][e] = sg.T @ np.abs(xe)
+            A["dW_up"][e] = su.T @ np.abs(xe)
+            A["dW_down"][e] = np.abs(dYe).T @ bf16_spread(wax)
+            A["dX_rows"][sel] = sg @ np.abs(wg[e]) + su @ np.abs(wu[e])
+    res = {"dX_rows": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "d_row_w": dw, "d_row_w_alt": dw_alt}
+    if allow:
+        res.update({k + "_allow": v for k, v in A.items()})
+    return res
 
 
-def backward_share(inp, bf16_mode: bool = True):
+def backward_share(inp, bf16_mode: bool = True, allow: bool = False):
     """Expert share backward (rows in arrival order), see ``_backward_rows``;
-    dX is each row's dX_rows, a bf16 tensor in bf16 mode."""
+    dX is each row's dX_rows, a bf16 tensor in bf16 mode.  With ``allow``
+    also the decision allowances of ``_backward_rows`` (dX_allow for dX)."""
     wg, wu, wd = _weights(inp)
     g = _backward_rows(bf16.decode(inp["x"]), inp["row_expert"], inp["row_w"].astype(np.float64),
-                       bf16.decode(inp["dY"]), wg, wu, wd, bf16_mode)
+                       bf16.decode(inp["dY"]), wg, wu, wd, bf16_mode, allow)
     g["dX"] = rnd(g.pop("dX_rows"), bf16_mode)
+    if "dX_rows_allow" in g:
+        g["dX_allow"] = g.pop("dX_rows_allow")
     return g
 
 

@@ -343,10 +343,14 @@ def test_backward_small8(MB, ring_mbs):
     say(f"[backward] small8 R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
     ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * 2 * sh.H
     L, out, g = run_backward(inp, MB=MB, ring_bytes=ring)
-    ref = layer.backward_share(inp)
-    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
-    for k in ("dW_gate", "dW_up", "dW_down", "d_row_w"):
-        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
+    # dg, du and w a are GEMM outputs rounded to bf16: each element also gets
+    # the oracle's allowance for roundings another correct evaluation decides
+    # the other way
+    ref = layer.backward_share(inp, allow=True)
+    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True, allow=ref["dX_allow"])
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k, allow=ref[k + "_allow"])
+    assert_close(g["d_row_w"].cpu().numpy(), ref["d_row_w"], BF16_TOL, "d_row_w")
     L.close()
 
 

@@ -261,3 +261,45 @@ def test_bf16_mode_backward_close_to_exact():
         if k != "d_row_w":
             assert rel > 0, k          # the roundings really happen
     assert np.array_equal(bf16.round_rne(b["dX"]), b["dX"])
+
+
+def test_bf16_spread_bounds_perturbed_roundings():
+    """bf16_spread: every value within the relative margin of v rounds to a
+    bf16 value no farther from bf16(v) than the spread, the spread is zero
+    where the whole interval rounds alike, and it reaches one bf16 step for
+    values on a rounding midpoint."""
+    rng = np.random.default_rng(17)
+    v = rng.standard_normal(20000) * np.exp2(rng.integers(-20, 20, size=20000))
+    # plant exact midpoints between adjacent bf16 values
+    b = bf16.round_rne(v[:200])
+    _, e = np.frexp(np.abs(b))
+    v[:200] = b + np.sign(b) * np.ldexp(1.0, e - 9)
+    sp = layer.bf16_spread(v)
+    ref = bf16.round_rne(v)
+    for t in np.linspace(-1.0, 1.0, 21):
+        moved = np.abs(bf16.round_rne(v * (1.0 + t * layer.DECISION_REL)) - ref)
+        assert np.all(moved <= sp)
+    assert np.all(sp[:200] > 0)
+    assert np.mean(sp[200:] == 0) > 0.9          # a margin of 2^-13 against steps of 2^-8 .. 2^-7
+
+
+def test_bf16_backward_allowances_bound_perturbed_gemm_outputs(monkeypatch):
+    """With dg, du and w a perturbed within the margin before their bf16
+    rounding, the bf16 backward's weight gradients stay within the oracle's
+    allowance."""
+    inp = workloads.make_expert_share("small")
+    ref = layer.backward_share(inp, allow=True)
+    rng = np.random.default_rng(19)
+    real_rnd = layer.rnd
+
+    def jitter(v, on):
+        if not on:
+            return real_rnd(v, on)
+        return real_rnd(v * (1.0 + layer.DECISION_REL * rng.uniform(-1, 1, size=np.shape(v))), on)
+
+    monkeypatch.setattr(layer, "rnd", jitter)
+    got = layer.backward_share(inp)
+    monkeypatch.undo()
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert np.all(np.abs(got[k] - ref[k]) <= ref[k + "_allow"] * (1 + 1e-9) + 1e-12), k
+    assert np.mean(ref["dW_up_allow"]) < 0.01 * np.sqrt(np.mean(ref["dW_up"] ** 2))
