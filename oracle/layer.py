@@ -280,7 +280,8 @@ def router_logit_grad(z, idx, d_w, renorm: int):
     return dz
 
 
-def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router: bool = True):
+def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router: bool = True,
+                  allow: bool = False):
     """Full-layer backward, loss L = sum_t <dY[t], out[t]>.
 
     Routing (indices, weights, logits) is recomputed as in the forward.  Row
@@ -293,7 +294,8 @@ def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router
         dW_router = dz^T x  [E, H],  d_bias = sum_t dz[t]
         dX[t] += dz[t] W_router
     In bf16 mode dX (after both sums) is one bf16 tensor; dz, dW_router and
-    d_bias are exact.
+    d_bias are exact.  With ``allow`` also the decision allowances of
+    ``_backward_rows`` (dX_allow: the sum of the token's rows' allowances).
     """
     sh = inp["shape"]
     rn = sh.renorm if renorm is None else renorm
@@ -304,7 +306,9 @@ def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router
     wg, wu, wd = _weights(inp)
     T, H = x.shape
     g = _backward_rows(np.repeat(x, k, axis=0), idx.reshape(-1), w.reshape(-1).astype(np.float64),
-                       np.repeat(bf16.decode(inp["dY"]), k, axis=0), wg, wu, wd, bf16_mode)
+                       np.repeat(bf16.decode(inp["dY"]), k, axis=0), wg, wu, wd, bf16_mode, allow)
+    if "dX_rows_allow" in g:
+        g["dX_allow"] = g.pop("dX_rows_allow").reshape(T, k, H).sum(axis=1)
     d_topk_w = g["d_row_w"].reshape(T, k)
     dXr = g.pop("dX_rows").reshape(T, k, H)
     dX = np.zeros((T, H))
