@@ -152,7 +152,7 @@ def traffic_for(kernel, workload):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "this layer runs on one GPU only; --gpus must be 1 "
                           "(sharding across GPUs is a design note, not built)"}))
         sys.exit(2)
     import torch
