@@ -589,7 +589,7 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, c
     launch_quant_tile_rows(wd, nullptr, 0, E, H, I, p.wd_c, p.wd_s, s);       // GEMM2 B along I
     if (for_backward) {
       launch_quant_tile_cols(wd, nullptr, 0, E, I, H, p.wdT_c, p.wdT_s, s);   // dA' B: W_d^T along H
-      launch_quant_tile_cols(wg, wu, 1, E, H, 2 * I, p.wguT_c, p.wguT_s, s);  // dX B: W_gu^T along 2I
+      launch_quant_tile_cols(wg, wu, 2, E, H, 2 * I, p.wguT_c, p.wguT_s, s);  // dX B: [W_g; W_u]^T along 2I
     }
     return check_launch();
   }
@@ -599,7 +599,7 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, c
   launch_tile_rows(wd, nullptr, 0, E, H, I, p.wd, s);      // GEMM2 B: [E][H][I]
   if (for_backward) {
     launch_tile_cols(wd, nullptr, 0, E, I, H, p.wdT, s);   // dA' B: W_d^T [E][I][H]
-    launch_tile_cols(wg, wu, 1, E, H, 2 * I, p.wguT, s);   // dX B: W_gu^T [E][H][2I]
+    launch_tile_cols(wg, wu, 2, E, H, 2 * I, p.wguT, s);   // dX B: [W_g; W_u]^T [E][H][2I]
   }
   return check_launch();
 }

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint
 // dA'[p, i] = dYe[p] . W_d[e][:, i]  (B = W_d^T, tiled [E, I, H]).  Epilogue,
 // from the forward's fp32 g, u: a = silu(g) u; dw partial = sum_i dA' a over
 // this wave's 64 columns; dA = w dA'; dg = dA u s (1 + g (1 - s)); du = dA
-// silu(g) (bf16 GEMM operands, packed like W_gu); w*a (bf16 operand of the
+// silu(g) (bf16 GEMM operands, row p = I gate then I up features); w*a (bf16 operand of the
 // down-projection weight gradient).
 __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16_t* __restrict__ dye,
                                                       const uint16_t* __restrict__ wdT, int H, int I,
@@ -257,7 +257,8 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
 }
 
 // ------------------------------------------------------ backward: dX ----
-// dX_row[p] = dgdu[p] . W_gu[e]  (B = packed W_gu^T, tiled [E, H, 2I]).
+// dX_row[p] = dgdu[p] . [W_g[e]; W_u[e]]  (B = [W_g; W_u]^T, tiled [E, H, 2I]:
+// the I gate features, then the I up features, as in dgdu).
 // ROWS16: rows stored as bf16 straight back to arrival order, dX[inv[p]];
 // else : kept in fp32 at position p ([p, H]) for the full layer's k-sum.
 template <bool ROWS16>
@@ -307,7 +308,7 @@ __device__ __forceinline__ bool seg_next(SegIter& it, const WgradArgs& w, int e)
 template <int MODE>
 struct WgradOperands {
   // MODE 0: A = dYe [p, H], B = w*a [p, I]          -> dW_down [E, H, I]
-  // MODE 1: A = dgdu [p, 2I] (packed), B = x rows   -> dW_gate / dW_up [E, I, H]
+  // MODE 1: A = dgdu [p, 2I] (gate | up), B = x rows -> dW_gate / dW_up [E, I, H]
   const uint16_t* A;
   int64_t lda;
   const uint16_t* B;
@@ -457,8 +458,7 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
         if (MODE == 0) {
           dst = out0 + ((int64_t)e * M + m) * N;
         } else {
-          const int ii = (m >> 5) * 16 + (m & 15);
-          dst = ((m & 31) < 16 ? out0 : out1) + ((int64_t)e * I + ii) * N;
+          dst = (m < I ? out0 + ((int64_t)e * I + m) * N : out1 + ((int64_t)e * I + m - I) * N);
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) dst[n0 + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][vv];

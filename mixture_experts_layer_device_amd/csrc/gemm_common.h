@@ -116,8 +116,10 @@ __device__ __forceinline__ void stage_flush(char* lds, RowDst row_dst) {
 // dA' tile -> SwiGLU backward, from the forward's fp32 g, u (gu, packed like
 // W_gu): a = silu(g) u; dw partial = sum of dA' a over this wave's 64
 // columns (one slice of I/64, added up later in slice order); dA = w dA';
-// dg = dA u s (1 + g (1 - s)), du = dA silu(g) (bf16, packed like W_gu); and
-// w*a (bf16, the down-projection weight gradient's operand).
+// dg = dA u s (1 + g (1 - s)), du = dA silu(g) (bf16, row p of dgdu holding
+// the I gate features then the I up features, so the MX blocks of the dX
+// GEMM's contraction are 32 consecutive dg or du values); and w*a (bf16, the
+// down-projection weight gradient's operand).
 // g and u of the tile (256 rows x 512 packed columns, 2 KiB per row) are
 // brought through LDS in four chunks of 64 rows with coalesced 16-byte loads
 // (the chunk's rows are the fragments 2c and 2c+1 of both row halves); the
@@ -178,9 +180,9 @@ __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, cha
           dws += dap * aa;
           const float da = w * dap;
           if (valid) {
-            uint16_t* dst = dgdu + p * 2 * I + 2 * ti.n0 + lc;
+            uint16_t* dst = dgdu + p * 2 * I + ti.n0 + f;
             dst[0] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
-            dst[16] = (uint16_t)f32_to_bf16(da * sl);
+            dst[I] = (uint16_t)f32_to_bf16(da * sl);
             wa[p * I + ti.n0 + f] = (uint16_t)f32_to_bf16(w * aa);
           }
         }

@@ -244,8 +244,10 @@ __global__ __launch_bounds__(NT) void bwd_dact_mxfp8_kernel(ItemRange ir, const 
 }
 
 // ------------------------------------------------------ backward: dX ----
-// dX_row[p] = D(dgdu_q[p]) . D(W_gu^T[e]) over the 2I packed features, dgdu
-// quantised along them and W_gu^T in the tiled MXFP8 layout [E, H, 2I].
+// dX_row[p] = D(dgdu_q[p]) . D([W_g; W_u]^T[e]) over the 2I features (the I
+// gate features, then the I up features), dgdu quantised along them (so each
+// MX block is 32 consecutive gate or up features) and [W_g; W_u]^T in the
+// tiled MXFP8 layout [E, H, 2I].
 template <bool ROWS16>
 __global__ __launch_bounds__(NT) void bwd_dx_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ gc_,
                                                           const uint8_t* __restrict__ gs_,
@@ -274,8 +276,8 @@ __global__ __launch_bounds__(NT) void bwd_dx_mxfp8_kernel(ItemRange ir, const ui
 // the K loop is the forward's with A fetched like B.  Tiles go expert by
 // expert in order of descending K, each (m, n) tile by one workgroup over the
 // whole K: fixed order, no atomics.  An expert without rows writes zeros.
-// MODE 0: dW_down [E, H, I] (M = H, N = I); MODE 1: A rows are the packed
-// gate/up features (16 gate, then the same 16 up) -> dW_gate / dW_up [E, I, H].
+// MODE 0: dW_down [E, H, I] (M = H, N = I); MODE 1: A rows are the I gate
+// features, then the I up features -> dW_gate / dW_up [E, I, H].
 template <int MODE>
 __global__ __launch_bounds__(NT) void wgrad_mxfp8_kernel(int E, int M, int N, int I, const int32_t* __restrict__ kofs,
                                                          const int32_t* __restrict__ order,
@@ -317,8 +319,7 @@ __global__ __launch_bounds__(NT) void wgrad_mxfp8_kernel(int E, int M, int N, in
         if (MODE == 0) {
           dst = out0 + ((int64_t)e * M + m) * N;
         } else {
-          const int ii = (m >> 5) * 16 + (m & 15);
-          dst = ((m & 31) < 16 ? out0 : out1) + ((int64_t)e * I + ii) * N;
+          dst = (m < I ? out0 + ((int64_t)e * I + m) * N : out1 + ((int64_t)e * I + m - I) * N);
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) dst[n0 + frag_col(j)] = acc[i][j][v];

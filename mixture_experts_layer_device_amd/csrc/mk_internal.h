@@ -170,7 +170,7 @@ struct WgradArgs {
 // (zero_row: 512 zero bytes in device memory, for rows past a segment's end)
 void launch_wgrad_down(const WgradArgs& wa_args, const uint16_t* dye, const uint16_t* wa, int H,
                        int I, float* dW_down, const uint16_t* zero_row, int n_cu, hipStream_t s);
-// dW_gate/dW_up[e] (I x H) from dgdu (packed 2I) and the x rows: minibatches
+// dW_gate/dW_up[e] (I x H) from dgdu ([p, 2I]: I gate, then I up) and the x rows: minibatches
 // b >= first_resident come from the ring, earlier (evicted) ones from replay,
 // the x rows re-gathered at their positions p ([p, H]).
 void launch_wgrad_gate_up(const WgradArgs& wa_args, const uint16_t* dgdu, const uint16_t* ring,
@@ -190,7 +190,7 @@ void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const u
                            const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part,
                            int n_cu, hipStream_t s);
 // dW_down[e] (H x I) from the tiled operands dY^T (A, H rows) and (w a)^T
-// (B, I rows); dW_gate/dW_up[e] (I x H) from [dg|du]^T (A, 2I packed rows)
+// (B, I rows); dW_gate/dW_up[e] (I x H) from [dg|du]^T (A, 2I rows: gate, then up)
 // and X^T (B, H rows).  Every (e, m, n) tile by one workgroup over the
 // expert's whole K in ascending k: deterministic, no atomics.
 void launch_wgrad_down_mxfp8(int E, int H, int I, const int32_t* kofs, const int32_t* order, const uint8_t* ac,

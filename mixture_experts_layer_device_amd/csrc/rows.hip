@@ -226,14 +226,16 @@ __global__ void dw_finalize_kernel(const float* __restrict__ dw_part, int slices
   }
 }
 
-// packed row c of expert e: gate row (c/32)*16 + c%16 if c%32 < 16, else up row.
 // Source row of the B operand rows: mode 0 -> src_a + (e * R + row) * len;
-// mode 1 (gate/up) -> packed row c of expert e: 32-row groups of 16 gate rows
-// then the 16 up rows of the same i (R = 2I).
+// mode 1 (gate/up, GEMM1's packing) -> packed row c of expert e: 32-row
+// groups of 16 gate rows then the 16 up rows of the same i (R = 2I);
+// mode 2 (gate then up) -> row c < I is gate row c, else up row c - I (R = 2I).
 __device__ __forceinline__ const uint16_t* b_src_row(const uint16_t* src_a, const uint16_t* src_b, int mode, int e,
                                                      int row, int R, int64_t len) {
   if (mode == 0) return src_a + ((int64_t)e * R + row) * len;
-  const int I = R / 2, i = (row >> 5) * 16 + (row & 15);
+  const int I = R / 2;
+  if (mode == 2) return (row < I ? src_a + ((int64_t)e * I + row) * len : src_b + ((int64_t)e * I + row - I) * len);
+  const int i = (row >> 5) * 16 + (row & 15);
   return ((row & 31) < 16 ? src_a : src_b) + ((int64_t)e * I + i) * len;
 }
 

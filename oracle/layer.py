@@ -400,15 +400,6 @@ def qd_spread(v, rel: float = DECISION_REL):
     return spread
 
 
-def gu_order(I: int) -> np.ndarray:
-    """Order of the 2I gate/up features along the dX GEMM's contraction, as
-    indices into [gate (I) | up (I)]: groups of 16 gate features followed by
-    the 16 up features of the same indices (the packed weights' order; the MX
-    blocks of 32 along it hold 16 gate and 16 up values of the same features)."""
-    blocks = [np.r_[16 * b:16 * b + 16, I + 16 * b:I + 16 * b + 16] for b in range(I // 16)]
-    return np.concatenate(blocks)
-
-
 def _dact_mxfp8(dYq, wdTq, g, u, w):
     """dA' = D(Q_H(dY)) D(Q_H(W_d^T))^T and the SwiGLU backward from the
     forward's g, u: -> dA', a (exact silu(g) u), dw, dg, du (bf16), and dg,
@@ -503,7 +494,6 @@ def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False, wg
     dYq = qd(dY)
     R, H = x.shape
     E, I, _ = wg.shape
-    order = gu_order(I)
     dX = np.zeros((R, H)); dw = np.zeros(R); dX_allow = np.zeros((R, H))
     dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
     W_allow = {"dW_gate": np.zeros_like(dWg), "dW_up": np.zeros_like(dWu), "dW_down": np.zeros_like(dWd)}
@@ -513,12 +503,12 @@ def _backward_rows_mxfp8(x, re, w, dY, G, U, wg, wu, wd, allow: bool = False, wg
             continue
         g, u = G[sel], U[sel]
         _, a, dw[sel], dg, du, dgx, dux = _dact_mxfp8(dYq[sel], qd(wd[e].T), g, u, w[sel])
-        P = np.concatenate([dg, du], axis=1)[:, order]
-        WP = np.concatenate([wg[e], wu[e]], axis=0)[order]          # [2I, H]
+        P = np.concatenate([dg, du], axis=1)                        # [n, 2I]: the I gate, then the I up features
+        WP = np.concatenate([wg[e], wu[e]], axis=0)                 # [2I, H], the same feature order
         WPq = qd(WP.T)
         dX[sel] = qd(P) @ WPq.T
         if allow:
-            dX_allow[sel] = qd_spread(np.concatenate([dgx, dux], axis=1)[:, order]) @ np.abs(WPq).T
+            dX_allow[sel] = qd_spread(np.concatenate([dgx, dux], axis=1)) @ np.abs(WPq).T
         xe = x[sel]
         wa = bf16.round_rne(w[sel, None] * a)
         if wgrad_mx_mb is None:
@@ -551,8 +541,12 @@ def backward_share_mxfp8(inp, fwd=None, allow: bool = False, wgrad_mx_mb: int | 
     The two data-gradient GEMMs take MXFP8 operands quantised along their
     contraction, blocks of 32 (the forward's rule carried to the backward):
         dA' = D(Q_H(dY)) . D(Q_H(W_d[e]^T))^T
-        dX  = bf16( D(Q(P)) . D(Q(W_P[e]^T))^T ),  P = [dg | du] and
-              W_P = [W_g[e] ; W_u[e]] both in gu_order
+        dX  = bf16( D(Q(P)) . D(Q(W_P[e]^T))^T ),  P = [dg | du] (the I gate
+              features, then the I up features) and W_P = [W_g[e] ; W_u[e]]
+              in the same order; since I is a multiple of 32, every MX block
+              of 32 along this contraction is 32 consecutive gate features or
+              32 consecutive up features, i.e. dg and du are quantised along
+              I each on their own, as are W_g[e]^T and W_u[e]^T
     g and u are the MXFP8 forward's (exact products of its dequantised
     operands); a = silu(g) u; dw, dA, dg, du (bf16) as in the bf16 backward.
     With ``wgrad_mx_mb`` None the weight gradients are bf16 GEMMs, as in the
@@ -647,8 +641,6 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
     ``wgrad_mx_mb`` as there."""
     re = inp["row_expert"]
     w = inp["row_w"].astype(np.float64)
-    I = inp["w_gate"].shape[1]
-    order = gu_order(I)
     out = {"dX": [], "dX_allow": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": [],
            "dW_gate_allow": [], "dW_up_allow": [], "dW_down_allow": []}
     cache = {}
@@ -658,7 +650,7 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
             wg = bf16.decode(inp["w_gate"][e]); wu = bf16.decode(inp["w_up"][e]); wd = bf16.decode(inp["w_down"][e])
             q = quantized_weights_expert(inp, e)
             cache[e] = {"gq": mxfp8.dequantize(*q["gate"]), "uq": mxfp8.dequantize(*q["up"]),
-                        "wdTq": qd(wd.T), "WPTq": qd(np.concatenate([wg, wu], axis=0)[order].T)}
+                        "wdTq": qd(wd.T), "WPTq": qd(np.concatenate([wg, wu], axis=0).T)}
         return cache[e]
 
     def fwd_gu(e, sel):
@@ -671,9 +663,9 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
         c = expert(e)
         g, u = fwd_gu(e, [r])
         _, _, dw, dg, du, dgx, dux = _dact_mxfp8(qd(bf16.decode(inp["dY"][r:r + 1])), c["wdTq"], g, u, w[[r]])
-        P = np.concatenate([dg, du], axis=1)[:, order]
+        P = np.concatenate([dg, du], axis=1)
         out["dX"].append(bf16.round_rne(qd(P) @ c["WPTq"].T)[0])
-        out["dX_allow"].append((qd_spread(np.concatenate([dgx, dux], axis=1)[:, order]) @ np.abs(c["WPTq"]).T)[0])
+        out["dX_allow"].append((qd_spread(np.concatenate([dgx, dux], axis=1)) @ np.abs(c["WPTq"]).T)[0])
         out["d_row_w"].append(float(dw[0]))
     rows_q = {}
 

@@ -55,14 +55,47 @@ def test_mxfp8_backward_within_e4m3_error_of_bf16():
         assert 5e-3 < rel < 0.12, (k, rel)     # E4M3 step 2^-3: a few % RMS after a few quantisations
 
 
-def test_gu_order_is_the_packed_interleave():
-    I = 64
-    o = layer.gu_order(I)
-    assert sorted(o.tolist()) == list(range(2 * I))
-    # each MX block of 32 holds 16 gate features and the same 16 up features
-    for b in range(2 * I // 32):
-        blk = o[32 * b:32 * b + 32]
-        assert np.array_equal(blk[16:] - I, blk[:16])
+def test_dx_blocks_cut_from_dg_and_du_each_alone():
+    """The dX contraction runs over the I gate features then the I up
+    features, so its MX blocks of 32 are cut from dg alone and from du alone
+    (I is a multiple of 32), and the weights likewise: dX must equal the sum
+    of two separately blocked contractions, D(Q(dg)) D(Q(W_g^T))^T +
+    D(Q(du)) D(Q(W_u^T))^T, each quantised along I on its own.  A blocking
+    that mixed gate and up features in one block (any interleave) changes
+    the shared scales and fails this."""
+    inp = workloads.make_expert_share("small8")
+    fwd = layer.forward_share_mxfp8(inp)
+    ref = layer.backward_share_mxfp8(inp, fwd)
+    x = bf16.decode(inp["x"]); dY = bf16.decode(inp["dY"]); w = inp["row_w"].astype(np.float64)
+    wg = bf16.decode(inp["w_gate"]); wu = bf16.decode(inp["w_up"]); wd = bf16.decode(inp["w_down"])
+    re = inp["row_expert"]
+    dX = np.zeros_like(x)
+    for e in range(wg.shape[0]):
+        sel = np.nonzero(re == e)[0]
+        g, u = fwd["g"][sel], fwd["u"][sel]
+        dAp = layer.qd(dY[sel]) @ layer.qd(wd[e].T).T
+        s = 1.0 / (1.0 + np.exp(-g))
+        dA = w[sel, None] * dAp
+        dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
+        du = bf16.round_rne(dA * g * s)
+        dX[sel] = layer.qd(dg) @ layer.qd(wg[e].T).T + layer.qd(du) @ layer.qd(wu[e].T).T
+    dX = bf16.round_rne(dX)
+    # the same value summed in another order, rounded once: at most one bf16 step apart
+    d = np.abs(dX - ref["dX"])
+    _, ex = np.frexp(np.maximum(np.abs(dX), np.abs(ref["dX"])))
+    assert np.all(d <= np.ldexp(1.0, np.maximum(ex, -125) - 8)) and np.mean(d > 0) < 1e-3
+    # control: an interleaved blocking (16 gate, then the same 16 up) differs
+    I = wg.shape[1]
+    mix = np.concatenate([np.r_[16 * b:16 * b + 16, I + 16 * b:I + 16 * b + 16] for b in range(I // 16)])
+    e = int(re[0]); sel = np.nonzero(re == e)[0][:64]
+    g, u = fwd["g"][sel], fwd["u"][sel]
+    dAp = layer.qd(dY[sel]) @ layer.qd(wd[e].T).T
+    s = 1.0 / (1.0 + np.exp(-g))
+    dA = w[sel, None] * dAp
+    P = bf16.round_rne(np.concatenate([dA * u * s * (1.0 + g * (1.0 - s)), dA * g * s], axis=1))
+    WP = np.concatenate([wg[e], wu[e]], axis=0)
+    alt = bf16.round_rne(layer.qd(P[:, mix]) @ layer.qd(WP[mix].T).T)
+    assert np.mean(alt != ref["dX"][sel]) > 0.05
 
 
 def test_sampled_mxfp8_backward_helper_matches_full_oracle():
@@ -109,16 +142,13 @@ def test_mxfp8_backward_brute_force_micro():
             dw += dap * (g[i] * s * u[i])
             dg[i] = bf16.round_rne(np.array([w * dap * u[i] * s * (1.0 + g[i] * (1.0 - s))]))[0]
             du[i] = bf16.round_rne(np.array([w * dap * g[i] * s]))[0]
-        # contraction over features in groups of 16 gate then 16 up
-        p = []; wrows = []
-        for b in range(I // 16):
-            p += list(dg[16 * b:16 * b + 16]) + list(du[16 * b:16 * b + 16])
-            wrows += [wg[e][i] for i in range(16 * b, 16 * b + 16)] + [wu[e][i] for i in range(16 * b, 16 * b + 16)]
-        pq = _q_blocks(np.array(p))
-        wrows = np.array(wrows)                                            # [2I, H]
+        # contraction over the I gate features, then the I up features: the
+        # blocks of 32 are cut from dg and du each on their own, and from each
+        # weight column's gate part and up part
+        pq = np.concatenate([_q_blocks(dg), _q_blocks(du)])
         dx = np.zeros(H)
         for h in range(H):
-            colq = _q_blocks(wrows[:, h])                                  # along the feature order
+            colq = np.concatenate([_q_blocks(wg[e][:, h]), _q_blocks(wu[e][:, h])])
             dx[h] = sum(pq[c] * colq[c] for c in range(2 * I))
         dx = bf16.round_rne(dx)
         assert np.isclose(dw, ref["d_row_w"][r], rtol=1e-10, atol=1e-12)
