@@ -279,8 +279,8 @@ def main():
 
         def step():
             B.mk_route(L.ws, x, wr, bias, sh.T, idx, wts, s)
-            B.mk_build_schedule(L.ws, idx, sh.R, s)
-            B.mk_forward(L.ws, B.MK_FULL_LAYER, x, wts, packed, out, None, s)
+            B.mk_build_schedule(L.ws, L.sched.handle, idx, sh.R, s)
+            B.mk_forward(L.ws, L.sched.handle, B.MK_FULL_LAYER, x, wts, packed, out, None, s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=(out, idx, wts))
         main = summarize("full", sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False)
@@ -306,8 +306,8 @@ def main():
             s = torch.cuda.current_stream()
 
             def step():
-                B.mk_build_schedule(L.ws, re, sh.R, s)
-                B.mk_forward(L.ws, B.MK_EXPERT_SHARE, x, rw, packed, out, None, s)
+                B.mk_build_schedule(L.ws, L.sched.handle, re, sh.R, s)
+                B.mk_forward(L.ws, L.sched.handle, B.MK_EXPERT_SHARE, x, rw, packed, out, None, s)
 
             dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=(out,))
             results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "forward",
@@ -336,8 +336,8 @@ def main():
         out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
         ctx = L.new_fwd_ctx()
         s = torch.cuda.current_stream()
-        B.mk_build_schedule(L.ws, re, sh.R, s)
-        B.mk_forward(L.ws, B.MK_EXPERT_SHARE, x, rw, packed, out, ctx, s)     # fwd_ctx, untimed
+        B.mk_build_schedule(L.ws, L.sched.handle, re, sh.R, s)
+        B.mk_forward(L.ws, L.sched.handle, B.MK_EXPERT_SHARE, x, rw, packed, out, ctx, s)     # fwd_ctx, untimed
         g = {"dX": torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda"),
              "dW_gate": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
              "dW_up": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
@@ -345,7 +345,7 @@ def main():
              "d_row_w": torch.empty((sh.R,), dtype=torch.float32, device="cuda")}
 
         def step():
-            B.mk_backward(L.ws, B.MK_EXPERT_SHARE, ctx, x, rw, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
+            B.mk_backward(L.ws, L.sched.handle, B.MK_EXPERT_SHARE, ctx, x, rw, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
                           g["dW_down"], g["d_row_w"], s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
@@ -371,8 +371,8 @@ def main():
         ctx = L.new_fwd_ctx()
         s = torch.cuda.current_stream()
         idx, wts = L.route(x, wr, bias, sh.T)                                 # forward, untimed
-        B.mk_build_schedule(L.ws, idx, sh.R, s)
-        B.mk_forward(L.ws, B.MK_FULL_LAYER, x, wts, packed, out, ctx, s)
+        B.mk_build_schedule(L.ws, L.sched.handle, idx, sh.R, s)
+        B.mk_forward(L.ws, L.sched.handle, B.MK_FULL_LAYER, x, wts, packed, out, ctx, s)
         g = {"dX": torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda"),
              "dW_gate": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
              "dW_up": torch.empty((sh.E, sh.I, sh.H), dtype=torch.float32, device="cuda"),
@@ -382,7 +382,7 @@ def main():
              "d_topk_w": torch.empty((sh.R,), dtype=torch.float32, device="cuda")}
 
         def step():
-            B.mk_backward_layer(L.ws, ctx, x, wr, bias, idx, wts, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
+            B.mk_backward_layer(L.ws, L.sched.handle, ctx, x, wr, bias, idx, wts, packed, dY, g["dX"], g["dW_gate"], g["dW_up"],
                                 g["dW_down"], g["dW_router"], g["d_bias"], g["d_topk_w"], s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
@@ -440,32 +440,85 @@ def main():
 
 
 def cpu_baseline(log, inp):
-    """The oracle, as it stands, on the main workload: route, expert FFN and
-    combine of all 4096 of its tokens (about 10 s of CPU work on 16 cores);
-    rows/s counts the routed rows."""
+    """The oracle, as it stands, on the host cores.
+
+    Main figure (``value``): the main workload's full-layer forward on all
+    4096 tokens -- route, schedule (``oracle.schedule.build``), expert FFN and
+    combine, each timed on its own -- in routed rows/s.  ``others``: the
+    expert-share forward (bf16 and MXFP8) and backward on bounded samples of
+    their workloads (the first rows of each, about a second or two of CPU
+    work each), rows/s over the sample.  About 15-25 s of CPU in all."""
     import threadpoolctl
 
-    from oracle import bf16, layer, route
+    import workloads
+    from oracle import bf16, layer, route, schedule
 
     sh = inp["shape"]
-    n_tok = 4096
+    n_tok = sh.T
     toks = np.arange(n_tok)
     with threadpoolctl.threadpool_limits(limits=None):
         info = threadpoolctl.threadpool_info()
     blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     x = bf16.decode(inp["x"][:n_tok]).astype(np.float32)
     idx, w, _ = route.route(x, bf16.decode(inp["w_router"]).astype(np.float32), inp["bias"], sh.k, sh.renorm)
     t1 = time.perf_counter()
-    sub = dict(inp)
-    sub["x"] = inp["x"][:n_tok]
-    layer.forward_full_tokens(sub, idx, w, toks)
+    schedule.build(idx.reshape(-1), sh.E, n_tok * sh.k, n_tok * sh.k, 256)
     t2 = time.perf_counter()
+    layer.forward_full_tokens(inp, idx, w, toks)
+    t3 = time.perf_counter()
     rows = n_tok * sh.k
-    log(f"[bench] cpu oracle: route {t1 - t0:.2f}s, ffn+combine {t2 - t1:.2f}s for {rows} routed rows")
-    return {"value": round(rows / (t2 - t0), 1), "unit": "rows/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"full-layer forward (route + expert FFN + combine, fp64 numpy) of {n_tok} of the 4096 "
-                      f"tokens ({rows} routed rows); cores = numpy BLAS threads"}
+    log(f"[bench] cpu oracle, full layer: route {t1 - t0:.2f}s, schedule {t2 - t1:.2f}s, ffn+combine {t3 - t2:.2f}s "
+        f"for {rows} routed rows")
+
+    def sub(d, n):
+        o = dict(d)
+        for key in ("x", "row_expert", "row_w", "dY"):
+            if key in o:
+                o[key] = o[key][:n]
+        return o
+
+    others = {}
+    ep = workloads.make_expert_share("ep64_fwd", with_dy=False)
+    n = 2048
+    d = sub(ep, n)
+    ta = time.perf_counter()
+    schedule.build(d["row_expert"], ep["shape"].E, 4096, 4096, 256)
+    tb = time.perf_counter()
+    layer.forward_share(d)
+    tc = time.perf_counter()
+    others["ep64_fwd"] = {"rows_per_s": round(n / (tc - ta), 1), "schedule_s": round(tb - ta, 3),
+                          "forward_s": round(tc - tb, 3), "sample_rows": n, "of_rows": ep["shape"].R}
+    # MXFP8: weights are quantised ahead (as on the device, outside the
+    # timing); to bound that untimed work the sample is the first 1024 rows
+    # routed to expert 0, with that expert's weights only
+    sel = np.nonzero(ep["row_expert"] == 0)[0][:1024]
+    d = {"x": ep["x"][sel], "row_expert": np.zeros(sel.size, np.int32), "row_w": ep["row_w"][sel],
+         "w_gate": ep["w_gate"][:1], "w_up": ep["w_up"][:1], "w_down": ep["w_down"][:1]}
+    qw = layer.quantized_weights(d)
+    ta = time.perf_counter()
+    layer.forward_share_mxfp8(d, qw=qw)
+    tb = time.perf_counter()
+    others["ep64_mxfp8"] = {"rows_per_s": round(sel.size / (tb - ta), 1), "forward_s": round(tb - ta, 3),
+                            "sample_rows": int(sel.size), "of_rows": ep["shape"].R,
+                            "sample": "rows of expert 0, weights quantised before the timing"}
+    del ep
+    bw = workloads.make_expert_share("ep_bwd")
+    d = sub(bw, n)
+    ta = time.perf_counter()
+    layer.backward_share(d)
+    tb = time.perf_counter()
+    others["ep_bwd"] = {"rows_per_s": round(n / (tb - ta), 1), "backward_s": round(tb - ta, 3), "sample_rows": n,
+                        "of_rows": bw["shape"].R}
+    del bw
+    log(f"[bench] cpu oracle, expert share samples: {json.dumps(others)}")
+    return {"value": round(rows / (t3 - t0), 1), "unit": "rows/s", "cores": cores, "blas_threads": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"full-layer forward of all {n_tok} tokens ({rows} routed rows): route, schedule and expert "
+                      f"FFN + combine in fp64 numpy; cores = len(os.sched_getaffinity(0)), BLAS threads as listed",
+            "phases_s": {"route": round(t1 - t0, 3), "schedule": round(t2 - t1, 3), "forward": round(t3 - t2, 3)},
+            "others": others}
 
 
 if __name__ == "__main__":

@@ -20,11 +20,14 @@
  *  - bf16 tensors are raw 16-bit bf16 patterns (uint16), row-major.
  *  - Return value: MK_OK (0) or a negative MK_ERR_* code, detected on the
  *    host before anything is enqueued.  Problems only the device can see
- *    set bits in the workspace's device error word (MK_DEVERR_*); read it
+ *    set bits in the schedule's device error word (MK_DEVERR_*); read it
  *    with mk_device_error.  No call hangs on bad data and no exception
  *    crosses this boundary.
  *  - One workspace serves one stream at a time; calls on one workspace must
- *    be ordered (same stream, or externally synchronised).
+ *    be ordered (same stream, or externally synchronised).  A schedule
+ *    (mk_schedule) belongs to the workspace it was created for; several
+ *    schedules may be alive at once, so the forwards of several microbatches
+ *    can run before their backwards, in any order.
  */
 #ifndef MK_H_
 #define MK_H_
@@ -46,7 +49,8 @@ extern "C" {
 #define MK_ERR_UNSUPPORTED -7  /* combination not implemented                 */
 #define MK_ERR_CONFIG      -8  /* invalid config field                        */
 
-/* ---- device error word bits (OR-ed; cleared by mk_build_schedule) ------ */
+/* ---- device error word bits (one word per schedule, cleared by
+ *      mk_build_schedule; read with mk_device_error) ---------------------- */
 #define MK_DEVERR_EXPERT_RANGE   0x1u  /* a row_expert id outside [0, E): row dropped, its output is 0 */
 #define MK_DEVERR_SCHED_OVERFLOW 0x2u  /* work table above capacity: trailing tiles dropped            */
 
@@ -101,6 +105,7 @@ typedef struct mk_config {
 } mk_config;
 
 typedef struct mk_workspace mk_workspace;   /* opaque */
+typedef struct mk_schedule mk_schedule;     /* opaque */
 
 /* Fill *cfg with defaults: MB = 0, bf16, 256 MiB ring, capacity 1.0,
  * renorm 1, no backward. */
@@ -108,8 +113,8 @@ void mk_config_default(mk_config* cfg);
 
 /*
  * Workspace ("Core concepts": created once per model, reused).  Allocates the
- * ring, schedule tables, intermediate activations and the error word on the
- * current device.  Limits: max_rows >= 1 routed rows per call; H % 256 == 0,
+ * ring, the schedule builder's scratch and the intermediate activations on
+ * the current device (each schedule's tables come with mk_schedule_create).  Limits: max_rows >= 1 routed rows per call; H % 256 == 0,
  * I % 128 == 0 (I % 256 == 0 with enable_backward); 1 <= E <= 1024;
  * 1 <= k <= 32; ring_bytes below 2 GiB.  Returns MK_ERR_SHAPE / _LIMIT / _RING /
  * _CONFIG on a bad argument, MK_ERR_HIP if an allocation fails.
@@ -121,15 +126,17 @@ int mk_workspace_destroy(mk_workspace* ws);
 /* Host-known sizes of a workspace, for callers and tests. */
 #define MK_Q_RING_ROWS      0   /* rows the ring holds                         */
 #define MK_Q_MINIBATCH_ROWS 1   /* MB                                          */
-#define MK_Q_NUM_MB         2   /* minibatches of the last schedule            */
+#define MK_Q_NUM_MB         2   /* minibatches of a schedule (mk_schedule_query) */
 #define MK_Q_ITEM_CAPACITY  3   /* work-table capacity (items)                 */
 #define MK_Q_TILE_M         4   /* rows per work item (GEMM m-tile)            */
-#define MK_Q_ROWS           5   /* R of the last schedule                      */
+#define MK_Q_ROWS           5   /* R of a schedule (mk_schedule_query)         */
 #define MK_Q_NUM_CU         6   /* compute units the persistent grids use      */
 #define MK_Q_PACKED_BYTES   7   /* bytes of packed weights (forward only)      */
 #define MK_Q_PACKED_BYTES_BWD 8 /* bytes of packed weights incl. backward copies */
 #define MK_Q_FWD_CTX_BYTES  9   /* bytes of fwd_ctx for max_rows               */
 int64_t mk_query(const mk_workspace* ws, int32_t what);
+/* MK_Q_NUM_MB and MK_Q_ROWS of the schedule's last build (0 before one). */
+int64_t mk_schedule_query(const mk_schedule* sched, int32_t what);
 
 /*
  * Router: z[t,e] = sum_h x[t,h]*w_router[e,h] accumulated in fp32 in ascending
@@ -149,18 +156,33 @@ int mk_route(mk_workspace* ws, const void* x_dev, const void* w_router_dev,
 /*
  * Dispatch schedule ([MTP] = MarkTechPost "Cursor Open-Sources
  * Mixture-of-Kittens (MoK)...", "Three design decisions that matter": one
- * schedule table serves dispatch, combine and both backward directions).
- * From row_expert_dev [R] int32 (full-layer mode: the flattened topk_idx,
- * row r = t*k + j) builds, on the device, per-expert and per-minibatch counts
- * and offsets, the stable expert-grouped position of every row, its inverse,
- * and the GEMM work items.  Rows with an expert id outside [0, E) are dropped
- * and flagged (MK_DEVERR_EXPERT_RANGE).  Clears the device error word first.
- * MK_ERR_LIMIT if R > max_rows; MK_ERR_SHAPE if R < 0, or in full-layer use if
- * MB is not a multiple of k (checked at forward).
+ * schedule table serves dispatch, combine and both backward directions;
+ * [CARD] "Use the functional API": build_schedule returns the schedule that
+ * forward and backward take).
+ *
+ * mk_schedule_create allocates one schedule's device tables on the current
+ * device, sized from the workspace's limits (MK_ERR_HIP if that fails, or if
+ * the current device is not the workspace's); mk_schedule_destroy frees them.
+ * A schedule is only valid with the workspace it was created for
+ * (MK_ERR_STATE otherwise) and must not outlive it.
+ *
+ * mk_build_schedule: from row_expert_dev [R] int32 (full-layer mode: the
+ * flattened topk_idx, row r = t*k + j) builds, on the device, per-expert and
+ * per-minibatch counts and offsets, the stable expert-grouped position of
+ * every row, its inverse, and the GEMM work items.  Rows with an expert id
+ * outside [0, E) are dropped and flagged (MK_DEVERR_EXPERT_RANGE).  Clears the
+ * schedule's device error word and forgets its last forward (a backward must
+ * follow a forward on the rebuilt schedule).  MK_ERR_LIMIT if R > max_rows;
+ * MK_ERR_SHAPE if R < 0 (in full-layer use, MB not a multiple of k is
+ * checked at forward).
  */
-int mk_build_schedule(mk_workspace* ws, const int32_t* row_expert_dev, int32_t R, void* stream);
+int mk_schedule_create(mk_workspace* ws, mk_schedule** out);
+int mk_schedule_destroy(mk_schedule* sched);
+int mk_build_schedule(mk_workspace* ws, mk_schedule* sched, const int32_t* row_expert_dev, int32_t R,
+                      void* stream);
 
-/* Copy one schedule table (device) into dst_dev (device, >= bytes). */
+/* Copy one table of a schedule (device) into dst_dev (device, >= bytes;
+ * MK_ERR_LIMIT if bytes exceeds the table). */
 #define MK_TAB_COUNTS     0   /* [E]        int32                                   */
 #define MK_TAB_OFFSETS    1   /* [E+1]      int32                                   */
 #define MK_TAB_MB_COUNTS  2   /* [nb, E]    int32                                   */
@@ -169,9 +191,28 @@ int mk_build_schedule(mk_workspace* ws, const int32_t* row_expert_dev, int32_t R
 #define MK_TAB_INV        5   /* [nb*MB]    int32, -1 where no row                  */
 #define MK_TAB_ITEMS      6   /* [capacity, 4] int32 (row_begin, rows, expert, mb)  */
 #define MK_TAB_MB_ITEMS   7   /* [nb+1]     int32 first item of each minibatch      */
-#define MK_TAB_RING       8   /* ring contents, ring_rows * row_bytes bytes         */
-int mk_schedule_copy(const mk_workspace* ws, int32_t table, void* dst_dev, int64_t bytes,
-                     void* stream);
+int mk_schedule_copy(const mk_schedule* sched, int32_t table, void* dst_dev, int64_t bytes, void* stream);
+
+/*
+ * Copy one of the workspace's device buffers into dst_dev (device, >= bytes):
+ * what the last call on the workspace left there, for tests and inspection.
+ * Rows at sorted positions p (expert order, [positions, ...] with positions =
+ * minibatches * MB).  MK_ERR_CONFIG for a buffer this workspace does not
+ * have (MXFP8 buffers in bf16 mode, backward buffers without
+ * enable_backward), MK_ERR_LIMIT if bytes exceeds it.
+ */
+#define MK_BUF_RING        0   /* ring token buffer, ring_rows * row_bytes bytes (MXFP8: codes, then scales) */
+#define MK_BUF_A           1   /* [positions, I] bf16: SwiGLU output a of the last forward                    */
+#define MK_BUF_A_CODES     2   /* [positions, I] uint8: a quantised along I (MXFP8 forward)                   */
+#define MK_BUF_A_SCALES    3   /* [positions, I/32] uint8: their E8M0 scales                                  */
+#define MK_BUF_Y           4   /* [positions, H] fp32: GEMM2 output y of the last full-layer forward          */
+#define MK_BUF_DGDU        5   /* [positions, 2I] bf16: dg (I values), then du (I values) of the last backward */
+#define MK_BUF_DGDU_CODES  6   /* [positions, 2I] uint8: dg/du quantised along 2I (MXFP8 backward)            */
+#define MK_BUF_DGDU_SCALES 7   /* [positions, 2I/32] uint8                                                    */
+#define MK_BUF_WA          8   /* [positions, I] bf16: w*a of the last backward                               */
+#define MK_BUF_DY_CODES    9   /* [positions, H] uint8: dY rows quantised along H (MXFP8 backward)            */
+#define MK_BUF_DY_SCALES  10   /* [positions, H/32] uint8                                                     */
+int mk_workspace_copy(const mk_workspace* ws, int32_t buffer, void* dst_dev, int64_t bytes, void* stream);
 
 /*
  * MXFP8 quantise (the card's ops.mxfp8_quantize; OCP MX v1.0 with E4M3
@@ -215,18 +256,21 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_u
  *   fwd_ctx_dev: NULL, or mk_query(MK_Q_FWD_CTX_BYTES) bytes that receive what
  *                the backward needs (g and u in fp32; in MXFP8 mode the
  *                products of the dequantised operands).
- * Uses the schedule of the last mk_build_schedule (MK_ERR_STATE if none).
+ * sched: built by mk_build_schedule on this workspace (MK_ERR_STATE if not).
+ * The forward overwrites the workspace's ring; the schedule records the mode,
+ * fwd_ctx_dev and that its rows are now the ring's, for its backward.
  */
-int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const float* row_w_dev,
-               const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
+int mk_forward(mk_workspace* ws, mk_schedule* sched, int32_t mode, const void* x_src_dev,
+               const float* row_w_dev, const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
 
 /*
  * Backward ([MTP]: the ring is walked in reverse to minimise
  * forward-activation replay; the router-weight gradient is fused into the
  * SwiGLU backward), for the loss L = <dY, out> of mk_forward.  In MXFP8 mode
  * the two data-gradient GEMMs take MXFP8 operands quantised along their
- * contraction (dY and W_d^T along H; dg/du and W_gu^T along the 2I packed
- * gate/up features, blocks of 32), fp32 accumulation; the weight gradients
+ * contraction (dY and W_d^T along H; [dg | du] and [W_g; W_u]^T along the 2I
+ * features, the I gate ones then the I up ones, blocks of 32), fp32
+ * accumulation; the weight gradients
  * are bf16 GEMMs as in bf16 mode.  Evicted minibatches (an MXFP8 ring holds
  * codes, so all of them) have their x rows gathered again before the
  * gate/up weight gradient.  With cfg.wgrad_mxfp8 the weight gradients are
@@ -245,16 +289,19 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src_dev, const floa
  *   dW_gate_dev [E, I, H] fp32, dW_up_dev [E, I, H] fp32, dW_down_dev [E, H, I] fp32
  * Weight gradients are reduced in a fixed order (minibatches in reverse walk
  * order, rows ascending inside each) with no float atomics: bitwise repeatable
- * at a fixed minibatch size.  Must follow the mk_forward (with fwd_ctx) of the
- * same rows and mode on this workspace with no other forward in between;
- * packed_dev must have been prepared with for_backward = 1.  MK_ERR_CONFIG if
- * the workspace has no backward buffers;
+ * at a fixed minibatch size.  sched must have had a forward in the same mode
+ * since its last build, and fwd_ctx_dev must be the context that forward
+ * wrote (MK_ERR_STATE otherwise; not checked when R = 0).  Other schedules'
+ * forwards may have run in between: the ring then no longer holds this
+ * schedule's rows and every minibatch's x rows are gathered again (the
+ * result is the same).  packed_dev must have been prepared with
+ * for_backward = 1.  MK_ERR_CONFIG if the workspace has no backward buffers;
  * MK_ERR_SHAPE in full-layer mode unless R and MB are multiples of k.  After
  * an empty schedule (R = 0) only the weight-gradient pointers are read (the
  * others may be NULL) and the weight gradients are written as zeros.
  */
-int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const void* x_src_dev,
-                const float* row_w_dev, const void* packed_dev, const void* dY_dev,
+int mk_backward(mk_workspace* ws, const mk_schedule* sched, int32_t mode, const void* fwd_ctx_dev,
+                const void* x_src_dev, const float* row_w_dev, const void* packed_dev, const void* dY_dev,
                 void* dX_dev, float* dW_gate_dev, float* dW_up_dev, float* dW_down_dev,
                 float* d_row_w_dev, void* stream);
 
@@ -273,12 +320,12 @@ int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx_dev, const v
  *                        + sum_e dz[t, e] w_router[e] (e ascending), fp32, one rounding
  *   d_topk_w_dev [T*k] fp32, dW_gate/up/down as mk_backward.
  * x_dev, w_router_dev, bias_dev (NULL if the router has none), topk_idx_dev and
- * topk_w_dev are the ones mk_route and mk_forward saw; the schedule must be the
- * one built from topk_idx.  Every sum runs in a fixed order: bitwise
+ * topk_w_dev are the ones mk_route and mk_forward saw; sched must be the
+ * schedule built from topk_idx.  Every sum runs in a fixed order: bitwise
  * repeatable.  Errors as mk_backward; with T = 0, w_router_dev and
  * dW_router_dev are still required and dW_router (and d_bias) become zeros.
  */
-int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx_dev, const void* x_dev,
+int mk_backward_layer(mk_workspace* ws, const mk_schedule* sched, const void* fwd_ctx_dev, const void* x_dev,
                       const void* w_router_dev, const float* bias_dev, const int32_t* topk_idx_dev,
                       const float* topk_w_dev, const void* packed_dev, const void* dY_dev,
                       void* dX_dev, float* dW_gate_dev, float* dW_up_dev, float* dW_down_dev,
@@ -320,8 +367,9 @@ int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
  */
 int mk_timing_phases(mk_workspace* ws, uint32_t phase_mask);
 
-/* Enqueue a copy of the device error word into dst_dev (device uint32). */
-int mk_device_error(const mk_workspace* ws, uint32_t* dst_dev, void* stream);
+/* Enqueue a copy of the schedule's device error word into dst_dev (device
+ * uint32). */
+int mk_device_error(const mk_schedule* sched, uint32_t* dst_dev, void* stream);
 
 /* Minibatch floor of the two-wave rule ([MTP] "Three design decisions that
  * matter", overlap granularity): ceil(2 * n_cu * tile_m * tile_n / min(2I, H)). */

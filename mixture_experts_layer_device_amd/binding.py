@@ -65,13 +65,17 @@ _SIGS = {
     "mk_workspace_destroy": (ctypes.c_int, [_vp]),
     "mk_query": (_i64, [_vp, _i32]),
     "mk_route": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
-    "mk_build_schedule": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
+    "mk_schedule_create": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
+    "mk_schedule_destroy": (ctypes.c_int, [_vp]),
+    "mk_schedule_query": (_i64, [_vp, _i32]),
+    "mk_build_schedule": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
     "mk_schedule_copy": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp]),
+    "mk_workspace_copy": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp]),
     "mk_mxfp8_quantize": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "mk_prepare_weights": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
-    "mk_forward": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "mk_backward": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "mk_backward_layer": (ctypes.c_int, [_vp] * 17),
+    "mk_forward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mk_backward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mk_backward_layer": (ctypes.c_int, [_vp] * 18),
     "mk_device_error": (ctypes.c_int, [_vp, _vp, _vp]),
     "mk_timing_enable": (ctypes.c_int, [_vp, _i32]),
     "mk_timing_phases": (ctypes.c_int, [_vp, ctypes.c_uint32]),
@@ -147,12 +151,30 @@ def mk_route(ws, x, w_router, bias, T, topk_idx, topk_w, stream=None):
     _check("mk_route", lib.mk_route(ws, _p(x), _p(w_router), _p(bias), T, _p(topk_idx), _p(topk_w), _s(stream)))
 
 
-def mk_build_schedule(ws, row_expert, R, stream=None):
-    _check("mk_build_schedule", lib.mk_build_schedule(ws, _p(row_expert), R, _s(stream)))
+def mk_schedule_create(ws: int) -> int:
+    h = _vp()
+    _check("mk_schedule_create", lib.mk_schedule_create(ws, ctypes.byref(h)))
+    return h.value
 
 
-def mk_schedule_copy(ws, table, dst, nbytes, stream=None):
-    _check("mk_schedule_copy", lib.mk_schedule_copy(ws, table, _p(dst), nbytes, _s(stream)))
+def mk_schedule_destroy(sched: int) -> None:
+    _check("mk_schedule_destroy", lib.mk_schedule_destroy(sched))
+
+
+def mk_schedule_query(sched: int, what: int) -> int:
+    return _check("mk_schedule_query", lib.mk_schedule_query(sched, what))
+
+
+def mk_build_schedule(ws, sched, row_expert, R, stream=None):
+    _check("mk_build_schedule", lib.mk_build_schedule(ws, sched, _p(row_expert), R, _s(stream)))
+
+
+def mk_schedule_copy(sched, table, dst, nbytes, stream=None):
+    _check("mk_schedule_copy", lib.mk_schedule_copy(sched, table, _p(dst), nbytes, _s(stream)))
+
+
+def mk_workspace_copy(ws, buffer, dst, nbytes, stream=None):
+    _check("mk_workspace_copy", lib.mk_workspace_copy(ws, buffer, _p(dst), nbytes, _s(stream)))
 
 
 def mk_mxfp8_quantize(x, rows, K, codes, scales, stream=None):
@@ -164,25 +186,27 @@ def mk_prepare_weights(ws, w_gate, w_up, w_down, for_backward, packed, stream=No
                                                         _p(packed), _s(stream)))
 
 
-def mk_forward(ws, mode, x_src, row_w, packed, out, fwd_ctx=None, stream=None):
-    _check("mk_forward", lib.mk_forward(ws, mode, _p(x_src), _p(row_w), _p(packed), _p(out), _p(fwd_ctx), _s(stream)))
+def mk_forward(ws, sched, mode, x_src, row_w, packed, out, fwd_ctx=None, stream=None):
+    _check("mk_forward", lib.mk_forward(ws, sched, mode, _p(x_src), _p(row_w), _p(packed), _p(out), _p(fwd_ctx),
+                                        _s(stream)))
 
 
-def mk_backward(ws, mode, fwd_ctx, x_src, row_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_row_w, stream=None):
-    _check("mk_backward", lib.mk_backward(ws, mode, _p(fwd_ctx), _p(x_src), _p(row_w), _p(packed), _p(dY), _p(dX),
-                                          _p(dW_gate), _p(dW_up), _p(dW_down), _p(d_row_w), _s(stream)))
+def mk_backward(ws, sched, mode, fwd_ctx, x_src, row_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_row_w,
+                stream=None):
+    _check("mk_backward", lib.mk_backward(ws, sched, mode, _p(fwd_ctx), _p(x_src), _p(row_w), _p(packed), _p(dY),
+                                          _p(dX), _p(dW_gate), _p(dW_up), _p(dW_down), _p(d_row_w), _s(stream)))
 
 
-def mk_backward_layer(ws, fwd_ctx, x, w_router, bias, topk_idx, topk_w, packed, dY, dX, dW_gate, dW_up, dW_down,
-                      dW_router, d_bias, d_topk_w, stream=None):
-    _check("mk_backward_layer", lib.mk_backward_layer(ws, _p(fwd_ctx), _p(x), _p(w_router), _p(bias), _p(topk_idx),
-                                                      _p(topk_w), _p(packed), _p(dY), _p(dX), _p(dW_gate),
-                                                      _p(dW_up), _p(dW_down), _p(dW_router), _p(d_bias),
-                                                      _p(d_topk_w), _s(stream)))
+def mk_backward_layer(ws, sched, fwd_ctx, x, w_router, bias, topk_idx, topk_w, packed, dY, dX, dW_gate, dW_up,
+                      dW_down, dW_router, d_bias, d_topk_w, stream=None):
+    _check("mk_backward_layer", lib.mk_backward_layer(ws, sched, _p(fwd_ctx), _p(x), _p(w_router), _p(bias),
+                                                      _p(topk_idx), _p(topk_w), _p(packed), _p(dY), _p(dX),
+                                                      _p(dW_gate), _p(dW_up), _p(dW_down), _p(dW_router),
+                                                      _p(d_bias), _p(d_topk_w), _s(stream)))
 
 
-def mk_device_error(ws, dst, stream=None):
-    _check("mk_device_error", lib.mk_device_error(ws, _p(dst), _s(stream)))
+def mk_device_error(sched, dst, stream=None):
+    _check("mk_device_error", lib.mk_device_error(sched, _p(dst), _s(stream)))
 
 
 def mk_timing_enable(ws, on: bool) -> None:

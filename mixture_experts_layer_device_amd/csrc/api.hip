@@ -87,14 +87,22 @@ PackedMX packed_mx(const mk_workspace* ws, void* base) {
   return r;
 }
 
-ItemRange item_range(const mk_workspace* ws, int mb_lo, int mb_hi) {
+ItemRange item_range(const mk_workspace* ws, const mk_schedule* sc, int mb_lo, int mb_hi) {
   ItemRange ir;
-  ir.items = ws->items;
-  ir.mb_items = ws->mb_items;
+  ir.items = sc->t.items;
+  ir.mb_items = sc->t.mb_items;
   ir.mb_lo = mb_lo;
   ir.mb_hi = mb_hi;
   ir.item_cap = ws->item_cap;
   return ir;
+}
+
+// A schedule may only be used with the workspace it was created for.
+bool sched_ok(const mk_workspace* ws, const mk_schedule* sc) { return ws && sc && sc->ws_id == ws->id; }
+
+uint64_t next_workspace_id() {
+  static uint64_t counter = 0;
+  return __atomic_add_fetch(&counter, 1, __ATOMIC_RELAXED);
 }
 
 int check_launch() { return hipGetLastError() == hipSuccess ? MK_OK : MK_ERR_HIP; }
@@ -136,18 +144,22 @@ struct RouterGrad {
 // routed row; the dX GEMM keeps its rows in fp32 (reusing the forward's y
 // buffer, dead by now) and a combine sums each token's k rows in slot order,
 // adds the router term when rg is given, and rounds once.
-int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const void* x_src, const float* row_w,
-                  const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up, float* dW_down,
-                  float* d_row_w, const RouterGrad* rg, void* stream) {
-  if (!ws) return MK_ERR_NULL;
-  if (!ws->have_sched) return MK_ERR_STATE;
+int backward_impl(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const void* fwd_ctx, const void* x_src,
+                  const float* row_w, const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up,
+                  float* dW_down, float* d_row_w, const RouterGrad* rg, void* stream) {
+  if (!ws || !sc) return MK_ERR_NULL;
+  if (!sched_ok(ws, sc)) return MK_ERR_STATE;
   if (mode != MK_EXPERT_SHARE && mode != MK_FULL_LAYER) return MK_ERR_CONFIG;
   if (!ws->cfg.enable_backward) return MK_ERR_CONFIG;
   const bool mx = ws->cfg.precision == MK_MXFP8;
-  const int H = ws->H, I = ws->I, MB = ws->MB, R = ws->R, nb = ws->nb, k = ws->k, E = ws->E;
+  const int H = ws->H, I = ws->I, MB = ws->MB, R = sc->R, nb = sc->nb, k = ws->k, E = ws->E;
   // an empty schedule reads no row buffer; the weight gradients become zeros
   if (!dW_gate || !dW_up || !dW_down) return MK_ERR_NULL;
   if (R > 0 && (!fwd_ctx || !x_src || !row_w || !packed || !dY || !dX || !d_row_w)) return MK_ERR_NULL;
+  // the backward consumes the forward context of this schedule's last
+  // forward, taken in the same mode; with R = 0 there is nothing to consume
+  if (!sc->built) return MK_ERR_STATE;
+  if (R > 0 && (!sc->fwd_valid || sc->fwd_ctx != fwd_ctx || sc->fwd_mode != mode)) return MK_ERR_STATE;
   const bool full = mode == MK_FULL_LAYER;
   if (full && (R % k || MB % k)) return MK_ERR_SHAPE;
   const int src_div = full ? k : 1;
@@ -155,7 +167,8 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   hipStream_t s = as_stream(stream);
   PackedBF16 p = packed_bf16(ws, (void*)packed);
   PackedMX pm = packed_mx(ws, (void*)packed);
-  const ItemRange all = item_range(ws, 0, nb);
+  const ItemRange all = item_range(ws, sc, 0, nb);
+  const SchedTables& st = sc->t;
   const int64_t npos_used = (int64_t)nb * MB;
   // pull the loss gradient into expert order (share of the reverse combine);
   // MXFP8: quantised along H for the dA' GEMM in the same pass, which also
@@ -165,24 +178,24 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
     // (with MXFP8 weight gradients the bf16 copy is not needed: their dY
     // operand is quantised along the rows straight from the dY rows)
     if (mx)
-      launch_gather_rows_mxfp8((const uint16_t*)dY, H, ws->inv, src_div, 0, npos_used, 0, ws->dye_c, ws->dye_s,
+      launch_gather_rows_mxfp8((const uint16_t*)dY, H, st.inv, src_div, 0, npos_used, 0, ws->dye_c, ws->dye_s,
                                ws->n_cu, s, ws->cfg.wgrad_mxfp8 ? nullptr : ws->dye);
     else
-      launch_gather_rows((const uint16_t*)dY, H, ws->inv, src_div, 0, npos_used, 0, ws->dye, ws->n_cu, s);
+      launch_gather_rows((const uint16_t*)dY, H, st.inv, src_div, 0, npos_used, 0, ws->dye, ws->n_cu, s);
   }
   // dA' GEMM with the SwiGLU backward and router-weight gradient fused
   {
     Phase ph(ws, MK_PH_BWD_DACT, s);
     if (mx)
-      launch_bwd_dact_mxfp8(all, ws->dye_c, ws->dye_s, pm.wdT_c, pm.wdT_s, H, I, (const float*)fwd_ctx, ws->inv,
+      launch_bwd_dact_mxfp8(all, ws->dye_c, ws->dye_s, pm.wdT_c, pm.wdT_s, H, I, (const float*)fwd_ctx, st.inv,
                             row_w, ws->dgdu, ws->wa, ws->dw_part, ws->n_cu, s);
     else
-      launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, ws->inv, row_w, ws->dgdu, ws->wa,
+      launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, st.inv, row_w, ws->dgdu, ws->wa,
                       ws->dw_part, ws->n_cu, s);
   }
   {
     Phase ph(ws, MK_PH_BWD_DW, s);
-    launch_dw_finalize(ws->dw_part, I / 64, ws->sorted_pos, R, d_row_w, full ? nullptr : (uint16_t*)dX, H, s);
+    launch_dw_finalize(ws->dw_part, I / 64, st.sorted_pos, R, d_row_w, full ? nullptr : (uint16_t*)dX, H, s);
   }
   // dX GEMM: expert share stores rows back to arrival order (share of the
   // reverse dispatch); the full layer keeps fp32 rows for the k-sum
@@ -193,10 +206,10 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   {
     Phase ph(ws, MK_PH_BWD_DX, s);
     if (mx)
-      launch_bwd_dx_mxfp8(all, ws->dgdu_c, ws->dgdu_s, pm.wguT_c, pm.wguT_s, H, I, ws->inv,
+      launch_bwd_dx_mxfp8(all, ws->dgdu_c, ws->dgdu_s, pm.wguT_c, pm.wguT_s, H, I, st.inv,
                           full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
     else
-      launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, ws->inv, full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
+      launch_bwd_dx(all, ws->dgdu, p.wguT, H, I, st.inv, full ? nullptr : (uint16_t*)dX, ws->y_buf, ws->n_cu, s);
   }
   if (full) {
     if (rg) {
@@ -207,7 +220,7 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
     }
     {
       Phase ph(ws, MK_PH_BWD_COMBINE, s);
-      launch_dx_combine(ws->y_buf, H, ws->sorted_pos, k, T, rg ? ws->dz : nullptr, rg ? rg->w_router : nullptr, E,
+      launch_dx_combine(ws->y_buf, H, st.sorted_pos, k, T, rg ? ws->dz : nullptr, rg ? rg->w_router : nullptr, E,
                         (uint16_t*)dX, ws->n_cu, s);
     }
     if (rg) {
@@ -222,12 +235,16 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   wa.E = E;
   wa.nb = nb;
   wa.MB = MB;
-  wa.mb_counts = ws->mb_counts;
-  wa.mb_offsets = ws->mb_offsets;
-  wa.inv = ws->inv;
+  wa.mb_counts = st.mb_counts;
+  wa.mb_offsets = st.mb_offsets;
+  wa.inv = st.inv;
   wa.src_div = src_div;
   const int ring_mbs = ws->ring_rows / MB;
-  const int first_resident = std::max(0, nb - ring_mbs);
+  // the ring holds this schedule's last minibatches only while no other
+  // forward has run on the workspace since this schedule's; else every
+  // minibatch is replayed
+  const bool ring_ours = R > 0 && sc->fwd_ring_epoch == ws->ring_epoch;
+  const int first_resident = ring_ours ? std::max(0, nb - ring_mbs) : nb;
   if (ws->cfg.wgrad_mxfp8) {
     // MXFP8 weight gradients: both operands of each GEMM quantised along the
     // rows (32 rows of one minibatch per block) into the tiled layout; the x
@@ -236,10 +253,10 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
     // minibatch at once
     {
       Phase ph(ws, MK_PH_WGRAD_QUANT, s);
-      launch_wgrad_kofs(ws->mb_counts, nb, E, ws->wq_kofs, ws->wq_order, s);
-      launch_wgrad_kmap(ws->wq_kofs, ws->mb_counts, ws->mb_offsets, E, nb, MB, ws->wq_kmap, s);
+      launch_wgrad_kofs(st.mb_counts, nb, E, ws->wq_kofs, ws->wq_order, s);
+      launch_wgrad_kmap(ws->wq_kofs, st.mb_counts, st.mb_offsets, E, nb, MB, ws->wq_kmap, s);
       if (R > 0)
-        launch_quant_wgrad_operand((const uint16_t*)dY, H, ws->inv, src_div, H, ws->wq_kofs, E, ws->wq_kmap,
+        launch_quant_wgrad_operand((const uint16_t*)dY, H, st.inv, src_div, H, ws->wq_kofs, E, ws->wq_kmap,
                                    ws->wq_kcap, ws->wq_ac, ws->wq_as, s);
       launch_quant_wgrad_operand(ws->wa, I, nullptr, 1, I, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap, ws->wq_bc,
                                  ws->wq_bs, s);
@@ -254,7 +271,7 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
       launch_quant_wgrad_operand(ws->dgdu, 2 * I, nullptr, 1, 2 * I, ws->wq_kofs, E, ws->wq_kmap, ws->wq_kcap,
                                  ws->wq_ac, ws->wq_as, s);
       if (R > 0)
-        launch_quant_wgrad_operand((const uint16_t*)x_src, H, ws->inv, src_div, H, ws->wq_kofs, E, ws->wq_kmap,
+        launch_quant_wgrad_operand((const uint16_t*)x_src, H, st.inv, src_div, H, ws->wq_kofs, E, ws->wq_kmap,
                                    ws->wq_kcap, ws->wq_bc, ws->wq_bs, s);
     }
     Phase ph(ws, MK_PH_WGRAD_GU, s);
@@ -274,7 +291,7 @@ int backward_impl(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const voi
   const int replay_mbs = mx ? nb : first_resident;
   if (replay_mbs > 0) {
     Phase ph(ws, MK_PH_REPLAY, s);
-    launch_gather_rows((const uint16_t*)x_src, H, ws->inv, src_div, 0, (int64_t)replay_mbs * MB, 0, ws->dye,
+    launch_gather_rows((const uint16_t*)x_src, H, st.inv, src_div, 0, (int64_t)replay_mbs * MB, 0, ws->dye,
                        ws->n_cu, s);
   }
   Phase ph(ws, MK_PH_WGRAD_GU, s);
@@ -313,6 +330,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
 
   mk_workspace* ws = (mk_workspace*)calloc(1, sizeof(mk_workspace));
   if (!ws) return MK_ERR_HIP;
+  ws->id = next_workspace_id();
   ws->events = new std::vector<mk_phase_event>();
   ws->timing_mask = 0xFFFFFFFFu;
   ws->cfg = *cfg;
@@ -375,18 +393,9 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
 
   const int64_t npos = ws->npos;
   Carver c;
-  const size_t o_err = c.take(256);
   const size_t o_zero = c.take(512);
   const size_t o_cc = c.take((size_t)ws->nb_max * ws->cpm * E * 4);
   const size_t o_cb = c.take((size_t)ws->nb_max * ws->cpm * 4);
-  const size_t o_mbc = c.take((size_t)ws->nb_max * E * 4);
-  const size_t o_mbo = c.take((size_t)ws->nb_max * (E + 1) * 4);
-  const size_t o_cnt = c.take((size_t)E * 4);
-  const size_t o_off = c.take((size_t)(E + 1) * 4);
-  const size_t o_sp = c.take((size_t)max_rows * 4);
-  const size_t o_inv = c.take((size_t)npos * 4);
-  const size_t o_items = c.take((size_t)ws->item_cap * 16);
-  const size_t o_mbi = c.take((size_t)(ws->nb_max + 1) * 4);
   const size_t o_ring = c.take((size_t)ws->ring_rows * ws->row_bytes);
   const size_t o_a = c.take((size_t)npos * I * 2);
   size_t o_ac = 0, o_as = 0;
@@ -435,18 +444,9 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     return MK_ERR_HIP;
   }
   char* b = (char*)ws->base;
-  ws->err = (uint32_t*)(b + o_err);
   ws->zero_row = (uint16_t*)(b + o_zero);
-  ws->chunk_counts = (int32_t*)(b + o_cc);
-  ws->chunk_bad = (int32_t*)(b + o_cb);
-  ws->mb_counts = (int32_t*)(b + o_mbc);
-  ws->mb_offsets = (int32_t*)(b + o_mbo);
-  ws->counts = (int32_t*)(b + o_cnt);
-  ws->offsets = (int32_t*)(b + o_off);
-  ws->sorted_pos = (int32_t*)(b + o_sp);
-  ws->inv = (int32_t*)(b + o_inv);
-  ws->items = (int32_t*)(b + o_items);
-  ws->mb_items = (int32_t*)(b + o_mbi);
+  ws->sscr.chunk_counts = (int32_t*)(b + o_cc);
+  ws->sscr.chunk_bad = (int32_t*)(b + o_cb);
   ws->ring = (uint8_t*)(b + o_ring);
   ws->a_buf = (uint16_t*)(b + o_a);
   if (cfg->precision == MK_MXFP8) {
@@ -477,8 +477,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     ws->wq_bc = (uint8_t*)(b + o_wbc);
     ws->wq_bs = (uint8_t*)(b + o_wbs);
   }
-  // error word starts clear; the zero row is zero
-  launch_fill_u32(ws->err, 0u, 1, nullptr);
+  // the zero row is zero
   launch_fill_u32((uint32_t*)ws->zero_row, 0u, 128, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(ws->base);
@@ -508,10 +507,8 @@ int64_t mk_query(const mk_workspace* ws, int32_t what) {
   switch (what) {
     case MK_Q_RING_ROWS: return ws->ring_rows;
     case MK_Q_MINIBATCH_ROWS: return ws->MB;
-    case MK_Q_NUM_MB: return ws->have_sched ? ws->nb : 0;
     case MK_Q_ITEM_CAPACITY: return ws->item_cap;
     case MK_Q_TILE_M: return MK_TILE_M;
-    case MK_Q_ROWS: return ws->have_sched ? ws->R : 0;
     case MK_Q_NUM_CU: return ws->n_cu;
     case MK_Q_PACKED_BYTES: return packed_bytes(ws, false);
     case MK_Q_PACKED_BYTES_BWD: return packed_bytes(ws, true);
@@ -532,37 +529,136 @@ int mk_route(mk_workspace* ws, const void* x, const void* w_router, const float*
   return check_launch();
 }
 
-int mk_build_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, void* stream) {
-  if (!ws || (!row_expert && R > 0)) return MK_ERR_NULL;
+int mk_schedule_create(mk_workspace* ws, mk_schedule** out) {
+  if (!ws || !out) return MK_ERR_NULL;
+  *out = nullptr;
+  const int E = ws->E;
+  Carver c;
+  const size_t o_err = c.take(256);
+  const size_t o_mbc = c.take((size_t)ws->nb_max * E * 4);
+  const size_t o_mbo = c.take((size_t)ws->nb_max * (E + 1) * 4);
+  const size_t o_cnt = c.take((size_t)E * 4);
+  const size_t o_off = c.take((size_t)(E + 1) * 4);
+  const size_t o_sp = c.take((size_t)ws->max_rows * 4);
+  const size_t o_inv = c.take((size_t)ws->npos * 4);
+  const size_t o_items = c.take((size_t)ws->item_cap * 16);
+  const size_t o_mbi = c.take((size_t)(ws->nb_max + 1) * 4);
+  mk_schedule* sc = (mk_schedule*)calloc(1, sizeof(mk_schedule));
+  if (!sc) return MK_ERR_HIP;
+  sc->ws_id = ws->id;
+  sc->E = ws->E;
+  sc->MB = ws->MB;
+  sc->item_cap = ws->item_cap;
+  sc->bytes = c.off;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != ws->device || hipMalloc(&sc->base, sc->bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    free(sc);
+    return MK_ERR_HIP;
+  }
+  char* b = (char*)sc->base;
+  sc->t.err = (uint32_t*)(b + o_err);
+  sc->t.mb_counts = (int32_t*)(b + o_mbc);
+  sc->t.mb_offsets = (int32_t*)(b + o_mbo);
+  sc->t.counts = (int32_t*)(b + o_cnt);
+  sc->t.offsets = (int32_t*)(b + o_off);
+  sc->t.sorted_pos = (int32_t*)(b + o_sp);
+  sc->t.inv = (int32_t*)(b + o_inv);
+  sc->t.items = (int32_t*)(b + o_items);
+  sc->t.mb_items = (int32_t*)(b + o_mbi);
+  // the error word starts clear
+  launch_fill_u32(sc->t.err, 0u, 1, nullptr);
+  if (hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(sc->base);
+    free(sc);
+    return MK_ERR_HIP;
+  }
+  *out = sc;
+  return MK_OK;
+}
+
+int mk_schedule_destroy(mk_schedule* sc) {
+  if (!sc) return MK_ERR_NULL;
+  int rc = MK_OK;
+  if (sc->base && hipFree(sc->base) != hipSuccess) rc = MK_ERR_HIP;
+  free(sc);
+  return rc;
+}
+
+int64_t mk_schedule_query(const mk_schedule* sc, int32_t what) {
+  if (!sc) return MK_ERR_NULL;
+  switch (what) {
+    case MK_Q_NUM_MB: return sc->built ? sc->nb : 0;
+    case MK_Q_ROWS: return sc->built ? sc->R : 0;
+    default: return MK_ERR_CONFIG;
+  }
+}
+
+int mk_build_schedule(mk_workspace* ws, mk_schedule* sc, const int32_t* row_expert, int32_t R, void* stream) {
+  if (!ws || !sc || (!row_expert && R > 0)) return MK_ERR_NULL;
+  if (!sched_ok(ws, sc)) return MK_ERR_STATE;
   if (R < 0) return MK_ERR_SHAPE;
   if (R > ws->max_rows) return MK_ERR_LIMIT;
   {
     Phase ph(ws, MK_PH_SCHEDULE, as_stream(stream));
-    launch_schedule(ws, row_expert, R, as_stream(stream));
+    const SchedDims d{ws->MB, ws->E, ws->cpm, ws->item_cap};
+    launch_schedule(d, ws->sscr, sc->t, row_expert, R, as_stream(stream));
   }
-  ws->R = R;
-  ws->nb = R > 0 ? (R + ws->MB - 1) / ws->MB : 0;
-  ws->have_sched = 1;
+  sc->R = R;
+  sc->nb = R > 0 ? (R + ws->MB - 1) / ws->MB : 0;
+  sc->built = 1;
+  sc->fwd_valid = 0;          // a new schedule has had no forward yet
+  sc->fwd_ctx = nullptr;
   return check_launch();
 }
 
-int mk_schedule_copy(const mk_workspace* ws, int32_t table, void* dst, int64_t bytes, void* stream) {
+int mk_schedule_copy(const mk_schedule* sc, int32_t table, void* dst, int64_t bytes, void* stream) {
+  if (!sc || !dst) return MK_ERR_NULL;
+  const void* src = nullptr;
+  int64_t have = 0;
+  // sizes of the last build (E, MB and the capacity are fixed per workspace
+  // and recorded with the tables)
+  const int nb = sc->built ? sc->nb : 0;
+  const int64_t E = sc->E, MB = sc->MB;
+  switch (table) {
+    case MK_TAB_COUNTS: src = sc->t.counts; have = E * 4; break;
+    case MK_TAB_OFFSETS: src = sc->t.offsets; have = (E + 1) * 4; break;
+    case MK_TAB_MB_COUNTS: src = sc->t.mb_counts; have = (int64_t)nb * E * 4; break;
+    case MK_TAB_MB_OFFSETS: src = sc->t.mb_offsets; have = (int64_t)nb * (E + 1) * 4; break;
+    case MK_TAB_SORTED_POS: src = sc->t.sorted_pos; have = (int64_t)(sc->built ? sc->R : 0) * 4; break;
+    case MK_TAB_INV: src = sc->t.inv; have = (int64_t)nb * MB * 4; break;
+    case MK_TAB_ITEMS: src = sc->t.items; have = (int64_t)sc->item_cap * 16; break;
+    case MK_TAB_MB_ITEMS: src = sc->t.mb_items; have = (int64_t)(nb + 1) * 4; break;
+    default: return MK_ERR_CONFIG;
+  }
+  if (bytes < 0 || bytes > have) return MK_ERR_LIMIT;
+  if (bytes == 0) return MK_OK;
+  return hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess
+             ? MK_OK
+             : MK_ERR_HIP;
+}
+
+int mk_workspace_copy(const mk_workspace* ws, int32_t buffer, void* dst, int64_t bytes, void* stream) {
   if (!ws || !dst) return MK_ERR_NULL;
   const void* src = nullptr;
   int64_t have = 0;
-  const int nb = ws->have_sched ? ws->nb : 0;
-  switch (table) {
-    case MK_TAB_COUNTS: src = ws->counts; have = (int64_t)ws->E * 4; break;
-    case MK_TAB_OFFSETS: src = ws->offsets; have = (int64_t)(ws->E + 1) * 4; break;
-    case MK_TAB_MB_COUNTS: src = ws->mb_counts; have = (int64_t)nb * ws->E * 4; break;
-    case MK_TAB_MB_OFFSETS: src = ws->mb_offsets; have = (int64_t)nb * (ws->E + 1) * 4; break;
-    case MK_TAB_SORTED_POS: src = ws->sorted_pos; have = (int64_t)(ws->have_sched ? ws->R : 0) * 4; break;
-    case MK_TAB_INV: src = ws->inv; have = (int64_t)nb * ws->MB * 4; break;
-    case MK_TAB_ITEMS: src = ws->items; have = (int64_t)ws->item_cap * 16; break;
-    case MK_TAB_MB_ITEMS: src = ws->mb_items; have = (int64_t)(nb + 1) * 4; break;
-    case MK_TAB_RING: src = ws->ring; have = (int64_t)ws->ring_rows * ws->row_bytes; break;
+  const int64_t npos = ws->npos, H = ws->H, I = ws->I;
+  const bool mx = ws->cfg.precision == MK_MXFP8, bwd = ws->cfg.enable_backward != 0;
+  switch (buffer) {
+    case MK_BUF_RING: src = ws->ring; have = (int64_t)ws->ring_rows * ws->row_bytes; break;
+    case MK_BUF_A: src = ws->a_buf; have = npos * I * 2; break;
+    case MK_BUF_A_CODES: src = mx ? ws->a_codes : nullptr; have = npos * I; break;
+    case MK_BUF_A_SCALES: src = mx ? ws->a_scales : nullptr; have = npos * I / 32; break;
+    case MK_BUF_Y: src = ws->y_buf; have = npos * H * 4; break;
+    case MK_BUF_DGDU: src = bwd ? ws->dgdu : nullptr; have = npos * 2 * I * 2; break;
+    case MK_BUF_DGDU_CODES: src = bwd && mx ? ws->dgdu_c : nullptr; have = npos * 2 * I; break;
+    case MK_BUF_DGDU_SCALES: src = bwd && mx ? ws->dgdu_s : nullptr; have = npos * 2 * I / 32; break;
+    case MK_BUF_WA: src = bwd ? ws->wa : nullptr; have = npos * I * 2; break;
+    case MK_BUF_DY_CODES: src = bwd && mx ? ws->dye_c : nullptr; have = npos * H; break;
+    case MK_BUF_DY_SCALES: src = bwd && mx ? ws->dye_s : nullptr; have = npos * H / 32; break;
     default: return MK_ERR_CONFIG;
   }
+  if (!src) return MK_ERR_CONFIG;
   if (bytes < 0 || bytes > have) return MK_ERR_LIMIT;
   if (bytes == 0) return MK_OK;
   return hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess
@@ -604,11 +700,11 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate, const void* w_up, c
   return check_launch();
 }
 
-int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* row_w, const void* packed,
-               void* out, void* fwd_ctx, void* stream) {
-  if (!ws) return MK_ERR_NULL;
-  if (!ws->have_sched) return MK_ERR_STATE;
-  const int R = ws->R;
+int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_src, const float* row_w,
+               const void* packed, void* out, void* fwd_ctx, void* stream) {
+  if (!ws || !sc) return MK_ERR_NULL;
+  if (!sched_ok(ws, sc) || !sc->built) return MK_ERR_STATE;
+  const int R = sc->R;
   if (R > 0 && (!x_src || !row_w || !packed || !out)) return MK_ERR_NULL;
   if (mode != MK_FULL_LAYER && mode != MK_EXPERT_SHARE) return MK_ERR_CONFIG;
   const int H = ws->H, I = ws->I, MB = ws->MB, k = ws->k;
@@ -619,9 +715,19 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
     kk = k;
   }
   const bool mx = ws->cfg.precision == MK_MXFP8;
-  if (R == 0) return MK_OK;
+  // what the backward of this schedule will check: the mode, the context it
+  // must be handed, and the ring epoch right after this forward's permute
+  sc->fwd_valid = 1;
+  sc->fwd_mode = mode;
+  sc->fwd_ctx = fwd_ctx;
+  if (R == 0) {
+    sc->fwd_ring_epoch = 0;   // nothing was written to the ring
+    return MK_OK;
+  }
+  sc->fwd_ring_epoch = ++ws->ring_epoch;
   hipStream_t s = as_stream(stream);
-  const int nb = ws->nb;
+  const int nb = sc->nb;
+  const SchedTables& st = sc->t;
   const int ring_mbs = ws->ring_rows / MB;
   const uint16_t* x = (const uint16_t*)x_src;
   const bool share = mode == MK_EXPERT_SHARE;
@@ -634,16 +740,16 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
       const int b1 = std::min(nb, b0 + ring_mbs);
       {
         Phase ph(ws, MK_PH_PERMUTE, s);
-        launch_gather_rows(x, H, ws->inv, src_div, (int64_t)b0 * MB, (int64_t)b1 * MB, ws->ring_rows,
+        launch_gather_rows(x, H, st.inv, src_div, (int64_t)b0 * MB, (int64_t)b1 * MB, ws->ring_rows,
                            (uint16_t*)ws->ring, ws->n_cu, s);
       }
       Phase ph(ws, MK_PH_GEMM1, s);
-      launch_gemm1_bf16(item_range(ws, b0, b1), (const uint16_t*)ws->ring, ws->ring_rows, p.wgu, H, I, ws->a_buf,
-                        (float*)fwd_ctx, ws->n_cu, s);
+      launch_gemm1_bf16(item_range(ws, sc, b0, b1), (const uint16_t*)ws->ring, ws->ring_rows, p.wgu, H, I,
+                        ws->a_buf, (float*)fwd_ctx, ws->n_cu, s);
     }
     Phase ph(ws, MK_PH_GEMM2, s);
-    launch_gemm2_bf16(item_range(ws, 0, nb), ws->a_buf, p.wd, H, I, ws->y_buf, out_fused, ws->inv, row_w, ws->n_cu,
-                      s);
+    launch_gemm2_bf16(item_range(ws, sc, 0, nb), ws->a_buf, p.wd, H, I, ws->y_buf, out_fused, st.inv, row_w,
+                      ws->n_cu, s);
   } else {
     PackedMX p = packed_mx(ws, (void*)packed);
     uint8_t* rc = ws->ring;
@@ -652,11 +758,11 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
       const int b1 = std::min(nb, b0 + ring_mbs);
       {
         Phase ph(ws, MK_PH_PERMUTE, s);
-        launch_gather_rows_mxfp8(x, H, ws->inv, src_div, (int64_t)b0 * MB, (int64_t)b1 * MB, ws->ring_rows, rc,
+        launch_gather_rows_mxfp8(x, H, st.inv, src_div, (int64_t)b0 * MB, (int64_t)b1 * MB, ws->ring_rows, rc,
                                  rsc, ws->n_cu, s);
       }
       Phase ph(ws, MK_PH_GEMM1, s);
-      launch_gemm1_mxfp8(item_range(ws, b0, b1), rc, rsc, ws->ring_rows, p.wgu_c, p.wgu_s, H, I, ws->a_buf,
+      launch_gemm1_mxfp8(item_range(ws, sc, b0, b1), rc, rsc, ws->ring_rows, p.wgu_c, p.wgu_s, H, I, ws->a_buf,
                          (float*)fwd_ctx, ws->n_cu, s);
     }
     {
@@ -664,34 +770,34 @@ int mk_forward(mk_workspace* ws, int32_t mode, const void* x_src, const float* r
       launch_quantize(ws->a_buf, (int64_t)nb * MB, I, ws->a_codes, ws->a_scales, s);
     }
     Phase ph(ws, MK_PH_GEMM2, s);
-    launch_gemm2_mxfp8(item_range(ws, 0, nb), ws->a_codes, ws->a_scales, p.wd_c, p.wd_s, H, I, ws->y_buf, out_fused,
-                       ws->inv, row_w, ws->n_cu, s);
+    launch_gemm2_mxfp8(item_range(ws, sc, 0, nb), ws->a_codes, ws->a_scales, p.wd_c, p.wd_s, H, I, ws->y_buf,
+                       out_fused, st.inv, row_w, ws->n_cu, s);
   }
   Phase ph(ws, MK_PH_COMBINE, s);
   if (share)
-    launch_zero_dropped_rows(ws->sorted_pos, R, (uint16_t*)out, H, s);
+    launch_zero_dropped_rows(st.sorted_pos, R, (uint16_t*)out, H, s);
   else
-    launch_combine(ws->y_buf, H, ws->sorted_pos, row_w, kk, (int64_t)R / kk, (uint16_t*)out, ws->n_cu, s);
+    launch_combine(ws->y_buf, H, st.sorted_pos, row_w, kk, (int64_t)R / kk, (uint16_t*)out, ws->n_cu, s);
   return check_launch();
 }
 
-int mk_backward(mk_workspace* ws, int32_t mode, const void* fwd_ctx, const void* x_src, const float* row_w,
-                const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up, float* dW_down,
-                float* d_row_w, void* stream) {
-  return backward_impl(ws, mode, fwd_ctx, x_src, row_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_row_w, nullptr,
-                       stream);
+int mk_backward(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const void* fwd_ctx, const void* x_src,
+                const float* row_w, const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up,
+                float* dW_down, float* d_row_w, void* stream) {
+  return backward_impl(ws, sc, mode, fwd_ctx, x_src, row_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_row_w,
+                       nullptr, stream);
 }
 
-int mk_backward_layer(mk_workspace* ws, const void* fwd_ctx, const void* x, const void* w_router, const float* bias,
-                      const int32_t* topk_idx, const float* topk_w, const void* packed, const void* dY, void* dX,
-                      float* dW_gate, float* dW_up, float* dW_down, float* dW_router, float* d_bias,
-                      float* d_topk_w, void* stream) {
-  if (!ws) return MK_ERR_NULL;
-  if (!ws->have_sched) return MK_ERR_STATE;
-  if (!w_router || !dW_router || (ws->R > 0 && !topk_idx)) return MK_ERR_NULL;
+int mk_backward_layer(mk_workspace* ws, const mk_schedule* sc, const void* fwd_ctx, const void* x,
+                      const void* w_router, const float* bias, const int32_t* topk_idx, const float* topk_w,
+                      const void* packed, const void* dY, void* dX, float* dW_gate, float* dW_up, float* dW_down,
+                      float* dW_router, float* d_bias, float* d_topk_w, void* stream) {
+  if (!ws || !sc) return MK_ERR_NULL;
+  if (!sched_ok(ws, sc) || !sc->built) return MK_ERR_STATE;
+  if (!w_router || !dW_router || (sc->R > 0 && !topk_idx)) return MK_ERR_NULL;
   RouterGrad rg{(const uint16_t*)w_router, bias, topk_idx, dW_router, d_bias};
-  return backward_impl(ws, MK_FULL_LAYER, fwd_ctx, x, topk_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_topk_w, &rg,
-                       stream);
+  return backward_impl(ws, sc, MK_FULL_LAYER, fwd_ctx, x, topk_w, packed, dY, dX, dW_gate, dW_up, dW_down, d_topk_w,
+                       &rg, stream);
 }
 
 int mk_timing_enable(mk_workspace* ws, int32_t on) {
@@ -730,10 +836,10 @@ int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out) {
   return rc;
 }
 
-int mk_device_error(const mk_workspace* ws, uint32_t* dst, void* stream) {
-  if (!ws || !dst) return MK_ERR_NULL;
-  return hipMemcpyAsync(dst, ws->err, 4, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess ? MK_OK
-                                                                                                   : MK_ERR_HIP;
+int mk_device_error(const mk_schedule* sc, uint32_t* dst, void* stream) {
+  if (!sc || !dst) return MK_ERR_NULL;
+  return hipMemcpyAsync(dst, sc->t.err, 4, hipMemcpyDeviceToDevice, as_stream(stream)) == hipSuccess ? MK_OK
+                                                                                                      : MK_ERR_HIP;
 }
 
 int64_t mk_two_wave_rows(int32_t H, int32_t I, int32_t n_cu, int32_t tile_m, int32_t tile_n) {

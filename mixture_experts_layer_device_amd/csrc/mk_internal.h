@@ -19,20 +19,47 @@ struct mk_phase_event {
   hipEvent_t start, stop;
 };
 
+// Device tables of one dispatch schedule (sizes from the workspace's limits).
+struct SchedTables {
+  uint32_t* err;              // device error word (MK_DEVERR_*), written whole by the build
+  int32_t *mb_counts, *mb_offsets, *counts, *offsets;
+  int32_t *sorted_pos, *inv, *items, *mb_items;
+};
+// Scratch of the schedule build and the sizes its launches use.
+struct SchedScratch {
+  int32_t* chunk_counts;      // [nb_max, cpm, E] per-chunk expert histograms
+  int32_t* chunk_bad;         // [nb_max, cpm]: a chunk holds an expert id out of range
+};
+struct SchedDims {
+  int32_t MB, E, cpm, item_cap;
+};
+
+struct mk_schedule {
+  uint64_t ws_id;             // id of the workspace it was created for
+  void* base;
+  size_t bytes;
+  SchedTables t;
+  int32_t E, MB, item_cap;    // the workspace's, for the table sizes
+  int32_t R, nb, built;
+  // the last forward that used this schedule: its mode, its fwd_ctx and the
+  // workspace's ring epoch right after it (the ring still holds this
+  // schedule's rows while the epoch is unchanged)
+  int32_t fwd_valid, fwd_mode;
+  const void* fwd_ctx;
+  uint64_t fwd_ring_epoch;
+};
+
 struct mk_workspace {
   mk_config cfg;
+  uint64_t id;                // process-unique, never reused
+  uint64_t ring_epoch;        // bumped by every forward that writes the ring
   int32_t max_rows, H, I, E, k;
   int32_t MB, ring_rows, row_bytes, nb_max, cpm, item_cap, n_cu, device;
   int64_t npos;               // nb_max * MB sorted positions
-  // last schedule
-  int32_t R, nb, have_sched;
   // device memory
   void* base;
   size_t bytes;
-  uint32_t* err;
-  int32_t *chunk_counts, *mb_counts, *mb_offsets, *counts, *offsets;
-  int32_t* chunk_bad;         // [nb_max, cpm]: a chunk holds an expert id out of range
-  int32_t *sorted_pos, *inv, *items, *mb_items;
+  SchedScratch sscr;
   uint8_t* ring;              // bf16 rows, or MXFP8 codes [ring_rows, H] then scales [ring_rows, H/32]
   uint16_t* a_buf;            // [npos, I] bf16 SwiGLU output, expert order
   uint8_t *a_codes, *a_scales;// MXFP8 copy of a
@@ -61,7 +88,8 @@ struct mk_workspace {
 namespace mk {
 
 // ---- schedule.hip --------------------------------------------------------
-void launch_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, hipStream_t s);
+void launch_schedule(const SchedDims& d, const SchedScratch& scr, const SchedTables& t, const int32_t* row_expert,
+                     int32_t R, hipStream_t s);
 
 // ---- route.hip -----------------------------------------------------------
 void launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H,

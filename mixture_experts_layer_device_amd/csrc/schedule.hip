@@ -259,18 +259,19 @@ void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
 }
 
-void launch_schedule(mk_workspace* ws, const int32_t* row_expert, int32_t R, hipStream_t s) {
-  const int MB = ws->MB, E = ws->E, cpm = ws->cpm;
+void launch_schedule(const SchedDims& d, const SchedScratch& scr, const SchedTables& t, const int32_t* row_expert,
+                     int32_t R, hipStream_t s) {
+  const int MB = d.MB, E = d.E, cpm = d.cpm;
   const int nb = R > 0 ? (R + MB - 1) / MB : 0;
   if (nb > 0)
     hipLaunchKernelGGL(sched_count_kernel, dim3(cpm, nb), dim3(CH), 0, s, row_expert, R, E, MB, cpm,
-                       ws->chunk_counts, ws->chunk_bad, ws->inv);
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(SCAN_T), 0, s, E, MB, nb, cpm, MK_TILE_M, ws->item_cap,
-                     ws->chunk_counts, ws->mb_counts, ws->mb_offsets, ws->counts, ws->offsets, ws->items,
-                     ws->mb_items, ws->chunk_bad, ws->err);
+                       scr.chunk_counts, scr.chunk_bad, t.inv);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(SCAN_T), 0, s, E, MB, nb, cpm, MK_TILE_M, d.item_cap,
+                     scr.chunk_counts, t.mb_counts, t.mb_offsets, t.counts, t.offsets, t.items, t.mb_items,
+                     scr.chunk_bad, t.err);
   if (nb > 0)
     hipLaunchKernelGGL(sched_scatter_kernel, dim3(cpm, nb), dim3(CH), 0, s, row_expert, R, E, MB, cpm,
-                       ws->chunk_counts, ws->mb_offsets, ws->sorted_pos, ws->inv);
+                       scr.chunk_counts, t.mb_offsets, t.sorted_pos, t.inv);
 }
 
 }  // namespace mk

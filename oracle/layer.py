@@ -243,7 +243,8 @@ def backward_share(inp, bf16_mode: bool = True, allow: bool = False):
     wg, wu, wd = _weights(inp)
     g = _backward_rows(bf16.decode(inp["x"]), inp["row_expert"], inp["row_w"].astype(np.float64),
                        bf16.decode(inp["dY"]), wg, wu, wd, bf16_mode, allow)
-    g["dX"] = rnd(g.pop("dX_rows"), bf16_mode)
+    g["dX_exact"] = g.pop("dX_rows")
+    g["dX"] = rnd(g["dX_exact"], bf16_mode)
     if "dX_rows_allow" in g:
         g["dX_allow"] = g.pop("dX_rows_allow")
     return g
@@ -320,6 +321,7 @@ def backward_full(inp, renorm: int | None = None, bf16_mode: bool = True, router
         dX += dz @ wr
         out.update(dz=dz, dW_router=dz.T @ x, d_bias=dz.sum(axis=0))
     out["dX"] = rnd(dX, bf16_mode)
+    out["dX_exact"] = dX
     return out
 
 
@@ -342,7 +344,7 @@ def backward_full_tokens(inp, idx, w, z, tokens, renorm: int):
         dX += dXr[:, j]
     dz = router_logit_grad(z[tokens], idx[tokens], d_topk_w, renorm)
     dX += dz @ wr
-    return {"dX": rnd(dX, True), "d_topk_w": d_topk_w, "dz": dz}
+    return {"dX": rnd(dX, True), "dX_exact": dX, "d_topk_w": d_topk_w, "dz": dz}
 
 
 def backward_full_expert(inp, idx, w, z, e, renorm: int):
@@ -563,7 +565,8 @@ def backward_share_mxfp8(inp, fwd=None, allow: bool = False, wgrad_mx_mb: int | 
     wg, wu, wd = _weights(inp)
     g = _backward_rows_mxfp8(bf16.decode(inp["x"]), inp["row_expert"], inp["row_w"].astype(np.float64),
                              bf16.decode(inp["dY"]), fwd["g"], fwd["u"], wg, wu, wd, allow, wgrad_mx_mb)
-    g["dX"] = bf16.round_rne(g.pop("dX_rows"))
+    g["dX_exact"] = g.pop("dX_rows")
+    g["dX"] = bf16.round_rne(g["dX_exact"])
     if allow:
         g["dX_allow"] = g.pop("dX_rows_allow")
     return g
@@ -632,6 +635,7 @@ def backward_full_mxfp8(inp, renorm: int | None = None, router: bool = True, fwd
         dX += dz @ wr
         out.update(dz=dz, dW_router=dz.T @ x, d_bias=dz.sum(axis=0))
     out["dX"] = bf16.round_rne(dX)
+    out["dX_exact"] = dX
     return out
 
 
@@ -641,7 +645,7 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
     ``wgrad_mx_mb`` as there."""
     re = inp["row_expert"]
     w = inp["row_w"].astype(np.float64)
-    out = {"dX": [], "dX_allow": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": [],
+    out = {"dX": [], "dX_exact": [], "dX_allow": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": [],
            "dW_gate_allow": [], "dW_up_allow": [], "dW_down_allow": []}
     cache = {}
 
@@ -664,7 +668,9 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
         g, u = fwd_gu(e, [r])
         _, _, dw, dg, du, dgx, dux = _dact_mxfp8(qd(bf16.decode(inp["dY"][r:r + 1])), c["wdTq"], g, u, w[[r]])
         P = np.concatenate([dg, du], axis=1)
-        out["dX"].append(bf16.round_rne(qd(P) @ c["WPTq"].T)[0])
+        dx = (qd(P) @ c["WPTq"].T)[0]
+        out["dX"].append(bf16.round_rne(dx))
+        out["dX_exact"].append(dx)
         out["dX_allow"].append((qd_spread(np.concatenate([dgx, dux], axis=1)) @ np.abs(c["WPTq"]).T)[0])
         out["d_row_w"].append(float(dw[0]))
     rows_q = {}
@@ -726,9 +732,10 @@ def backward_share_mxfp8_sampled(inp, rows, gate_up_rows, down_cols, wgrad_mx_mb
     return {k: np.asarray(v) for k, v in out.items()}
 
 
-def forward_share_rows(inp, rows):
+def forward_share_rows(inp, rows, exact: bool = False):
     """forward_share's out for the given arrival rows only (each row is
-    independent of every other)."""
+    independent of every other); with ``exact`` the value before its bf16
+    rounding (forward_share's out_exact)."""
     rows = np.asarray(rows)
     re = inp["row_expert"]
     out = np.zeros((len(rows), inp["x"].shape[1]))
@@ -739,11 +746,12 @@ def forward_share_rows(inp, rows):
         _, _, _, y = expert_ffn(x, bf16.decode(inp["w_gate"][e]), bf16.decode(inp["w_up"][e]),
                                 bf16.decode(inp["w_down"][e]), bf16_mode=True)
         out[sel] = inp["row_w"][rows[sel], None].astype(np.float64) * y
-    return bf16.round_rne(out)
+    return out if exact else bf16.round_rne(out)
 
 
-def forward_full_tokens(inp, idx, w, tokens):
-    """Full-layer out for the given tokens under routing (idx, w)."""
+def forward_full_tokens(inp, idx, w, tokens, exact: bool = False):
+    """Full-layer out for the given tokens under routing (idx, w); with
+    ``exact`` the value before its bf16 rounding."""
     tokens = np.asarray(tokens)
     x = bf16.decode(inp["x"][tokens])
     out = np.zeros((len(tokens), x.shape[1]))
@@ -756,7 +764,7 @@ def forward_full_tokens(inp, idx, w, tokens):
     for n, t in enumerate(tokens):
         for j in range(idx.shape[1]):                    # fixed ascending order
             out[n] += float(w[t, j]) * ys[int(idx[t, j])][n]
-    return bf16.round_rne(out)
+    return out if exact else bf16.round_rne(out)
 
 
 def quantized_weights_expert(inp, e):
@@ -766,9 +774,10 @@ def quantized_weights_expert(inp, e):
             "down": mxfp8.quantize(bf16.decode(inp["w_down"][e]))}
 
 
-def forward_share_mxfp8_rows(inp, rows, allow: bool = False):
-    """forward_share_mxfp8's out for the given arrival rows only; with
-    ``allow`` the pair (out, out_allow)."""
+def forward_share_mxfp8_rows(inp, rows, allow: bool = False, exact: bool = False):
+    """forward_share_mxfp8's out for the given arrival rows only (with
+    ``exact`` the value before its bf16 rounding); with ``allow`` the pair
+    (out, out_allow)."""
     rows = np.asarray(rows)
     re = inp["row_expert"]
     H = inp["x"].shape[1]
@@ -787,7 +796,8 @@ def forward_share_mxfp8_rows(inp, rows, allow: bool = False):
         out[sel] = wr * (ad @ wd.T)
         if allow:
             out_allow[sel] = np.abs(wr) * (qd_spread(silu(g) * u) @ np.abs(wd).T)
-    return (bf16.round_rne(out), out_allow) if allow else bf16.round_rne(out)
+    res = out if exact else bf16.round_rne(out)
+    return (res, out_allow) if allow else res
 
 
 def backward_share_sampled(inp, rows, gate_up_rows, down_cols):
@@ -799,7 +809,7 @@ def backward_share_sampled(inp, rows, gate_up_rows, down_cols):
     """
     re = inp["row_expert"]
     w = inp["row_w"].astype(np.float64)
-    out = {"dX": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
+    out = {"dX": [], "dX_exact": [], "d_row_w": [], "dW_gate": [], "dW_up": [], "dW_down": []}
     for r in rows:
         e = int(re[r])
         x = bf16.decode(inp["x"][r:r + 1]); dY = bf16.decode(inp["dY"][r:r + 1])
@@ -810,7 +820,9 @@ def backward_share_sampled(inp, rows, gate_up_rows, down_cols):
         dA = w[r] * dAp
         dg = bf16.round_rne(dA * u * s * (1.0 + g * (1.0 - s)))
         du = bf16.round_rne(dA * silu(g))
-        out["dX"].append(bf16.round_rne(dg @ wg + du @ wu)[0])
+        dx = (dg @ wg + du @ wu)[0]
+        out["dX"].append(bf16.round_rne(dx))
+        out["dX_exact"].append(dx)
         out["d_row_w"].append(float(np.sum(dAp * a)))
     for (e, i) in gate_up_rows:
         sel = np.nonzero(re == e)[0]
@@ -843,3 +855,108 @@ def ring_contents(sched, x_bits, src_of_row):
         ring[p % sched.ring_rows] = x_bits[src_of_row[r]]
         written[p % sched.ring_rows] = True
     return ring, written
+
+
+# ---------------------------------------------------------------------------
+# Single GEMM steps fed given operands.  Each is the definition of one step of
+# the layer written out on its own, so that a result computed from another
+# implementation's intermediate tensor (the bf16 a, dg/du, w a, or their
+# MXFP8 codes) can be checked step by step, without the roundings and E4M3
+# decisions that the earlier steps take on GEMM outputs.
+# ---------------------------------------------------------------------------
+
+def swiglu_rows(x_rows, row_expert, wg, wu):
+    """g, u and the exact a = silu(g) u of each row under its expert (fp64;
+    zeros for an expert id out of range)."""
+    g, u, _, _ = rows_ffn(x_rows, row_expert, wg, wu, np.zeros((wg.shape[0], 1, wg.shape[1])))
+    return g, u, silu(g) * u
+
+
+def down_rows(a_rows, row_expert, wd):
+    """y[r] = a[r] W_d[e]^T for given GEMM2 operands a (arrival order)."""
+    y = np.zeros((a_rows.shape[0], wd.shape[1]))
+    for e in range(wd.shape[0]):
+        sel = np.nonzero(row_expert == e)[0]
+        if sel.size:
+            y[sel] = a_rows[sel] @ wd[e].T
+    return y
+
+
+def combine_tokens(y_rows, w, k):
+    """out[t] = sum over j ascending of w[t, j] y[t k + j] (exact)."""
+    T = y_rows.shape[0] // k
+    yk = y_rows.reshape(T, k, -1)
+    out = np.zeros((T, yk.shape[2]))
+    for j in range(k):
+        out += np.asarray(w, dtype=np.float64).reshape(T, k)[:, j, None] * yk[:, j]
+    return out
+
+
+def dact_rows(dY_rows, g, u, row_expert, wd, w, dYq=None, wdT=None):
+    """dA' = dY W_d[e] (or, MXFP8, dYq wdT[e]^T with the given dequantised
+    operands) and the exact SwiGLU backward from g, u: -> dict of dA', dw,
+    dg and du before their bf16 rounding, and w a."""
+    R = dY_rows.shape[0]
+    I = g.shape[1]
+    dAp = np.zeros((R, I))
+    for e in range(wd.shape[0]):
+        sel = np.nonzero(row_expert == e)[0]
+        if sel.size:
+            dAp[sel] = dY_rows[sel] @ wd[e] if dYq is None else dYq[sel] @ wdT[e].T
+    s = sigmoid(g)
+    w = np.asarray(w, dtype=np.float64)
+    dA = w[:, None] * dAp
+    return {"dAp": dAp, "dw": np.einsum("ri,ri->r", dAp, silu(g) * u),
+            "dg": dA * u * s * (1.0 + g * (1.0 - s)), "du": dA * silu(g), "wa": w[:, None] * silu(g) * u}
+
+
+def dx_rows_from(dg, du, row_expert, wg, wu):
+    """dX_rows[r] = dg[r] W_g[e] + du[r] W_u[e] for given operands (exact)."""
+    dX = np.zeros((dg.shape[0], wg.shape[2]))
+    for e in range(wg.shape[0]):
+        sel = np.nonzero(row_expert == e)[0]
+        if sel.size:
+            dX[sel] = dg[sel] @ wg[e] + du[sel] @ wu[e]
+    return dX
+
+
+def dx_rows_from_mx(p_codes, p_scales, row_expert, wg, wu):
+    """MXFP8 dX rows from given codes of P = [dg | du] (quantised along the
+    2I features, the I gate ones then the I up ones): D(P) D(Q([W_g; W_u]^T))^T."""
+    P = mxfp8.dequantize(p_codes, p_scales)
+    dX = np.zeros((P.shape[0], wg.shape[2]))
+    for e in range(wg.shape[0]):
+        sel = np.nonzero(row_expert == e)[0]
+        if sel.size:
+            dX[sel] = P[sel] @ qd(np.concatenate([wg[e], wu[e]], axis=0).T).T
+    return dX
+
+
+def wgrads_from(x_rows, dY_rows, dg, du, wa, row_expert, E):
+    """bf16-mode weight gradients from given GEMM operands (exact sums):
+    dW_g[e] = dg_e^T X_e, dW_u[e] = du_e^T X_e, dW_d[e] = dY_e^T (w a)_e."""
+    I, H = dg.shape[1], x_rows.shape[1]
+    dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    for e in range(E):
+        sel = np.nonzero(row_expert == e)[0]
+        if sel.size:
+            dWg[e] = dg[sel].T @ x_rows[sel]
+            dWu[e] = du[sel].T @ x_rows[sel]
+            dWd[e] = dY_rows[sel].T @ wa[sel]
+    return {"dW_gate": dWg, "dW_up": dWu, "dW_down": dWd}
+
+
+def wgrads_from_mx(x_rows, dY_rows, dg, du, wa, row_expert, E, mb: int):
+    """MXFP8 weight gradients (``wgrad_mx``, minibatches of mb rows, 0 = one)
+    from given bf16 operands."""
+    I, H = dg.shape[1], x_rows.shape[1]
+    R = x_rows.shape[0]
+    dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    for e in range(E):
+        sel = np.nonzero(row_expert == e)[0]
+        if sel.size:
+            mbs = minibatch_of(sel, R, mb)
+            dWg[e] = wgrad_mx(dg[sel], x_rows[sel], mbs)
+            dWu[e] = wgrad_mx(du[sel], x_rows[sel], mbs)
+            dWd[e] = wgrad_mx(dY_rows[sel], wa[sel], mbs)
+    return {"dW_gate": dWg, "dW_up": dWu, "dW_down": dWd}

@@ -87,9 +87,9 @@ def test_single_expert_is_a_dense_swiglu_mlp(renorm):
     wg, wu, wd = (bf16.decode(inp[n])[0] for n in ("w_gate", "w_up", "w_down"))
     gg, uu = x @ wg.T, x @ wu.T
     a = bf16.round_rne(gg / (1.0 + np.exp(-gg)) * uu)
-    assert_close(host_bf16(out), bf16.round_rne(a @ wd.T), BF16_TOL, "out vs dense SwiGLU MLP", bf16_out=True)
-    ref = layer.backward_full(inp)
-    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
+    assert_close(host_bf16(out), a @ wd.T, BF16_TOL, "out vs dense SwiGLU MLP", bf16_out=True)
+    ref = layer.backward_full(inp, allow=True)
+    assert_close(host_bf16(g["dX"]), ref["dX_exact"], BF16_TOL, "dX", bf16_out=True, allow=ref["dX_allow"])
     for k in ("dW_gate", "dW_up", "dW_down"):
         assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
     assert not np.any(g["dW_router"].cpu().numpy()) and not np.any(g["d_bias"].cpu().numpy())
@@ -106,11 +106,11 @@ def test_every_expert_chosen():
     assert all(sorted(row) == list(range(sh.E)) for row in idx.tolist())
     fwd = layer.forward_full(inp)
     assert np.array_equal(idx, fwd["topk_idx"])
-    assert_close(host_bf16(out), fwd["out"], BF16_TOL, "out", bf16_out=True)
-    ref = layer.backward_full(inp)
-    assert_close(host_bf16(g["dX"]), ref["dX"], BF16_TOL, "dX", bf16_out=True)
+    assert_close(host_bf16(out), fwd["out_exact"], BF16_TOL, "out", bf16_out=True)
+    ref = layer.backward_full(inp, allow=True)
+    assert_close(host_bf16(g["dX"]), ref["dX_exact"], BF16_TOL, "dX", bf16_out=True, allow=ref["dX_allow"])
     for k in ("dW_gate", "dW_up", "dW_down", "dW_router", "d_bias"):
-        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k)
+        assert_close(g[k].cpu().numpy(), ref[k], BF16_TOL, k, allow=ref.get(k + "_allow"))
     assert L.device_error() == 0
     L.close()
 
@@ -135,6 +135,23 @@ def test_mxfp8_weight_gradients_many_experts_and_minibatches():
     ref = layer.backward_share_mxfp8(inp, fwd, allow=True, wgrad_mx_mb=MB)
     for k in ("dW_gate", "dW_up", "dW_down"):
         assert_close(g[k].cpu().numpy(), ref[k], 6e-2, k, allow=ref[k + "_allow"])
-    assert_close(host_bf16(g["dX"]), ref["dX"], 6e-2, "dX", bf16_out=True, allow=ref["dX_allow"])
+    assert_close(host_bf16(g["dX"]), ref["dX_exact"], 6e-2, "dX", bf16_out=True, allow=ref["dX_allow"])
     assert L.device_error() == 0
     L.close()
+
+
+def test_route_order_decides_the_top_k():
+    """The hand-worked golden case whose top-2 depends on the logits'
+    summation order (tests/test_oracle_route_schedule.py
+    ascending_order_case): the device's ascending-h fp32 chains give z0 = 0
+    exactly and rank expert 1 first, as the oracle does; any other order
+    ranks expert 0 first."""
+    from tests.test_oracle_route_schedule import ascending_order_case
+    T, H, E, k = 48, 256, 8, 2
+    say(f"[limits] route, summation-order golden case T={T} H={H} E={E} k={k}")
+    xb, wb = ascending_order_case(T=T, H=H, E=E)
+    L = MoELayer(H=H, I=128, E=E, k=k, max_rows=T * k, renorm=1)
+    idx, w = L.route(dev(xb), dev(wb), None, T)
+    got = idx.cpu().numpy()
+    L.close()
+    assert got.tolist() == [[1, 0]] * T

@@ -303,3 +303,96 @@ def test_bf16_backward_allowances_bound_perturbed_gemm_outputs(monkeypatch):
     for k in ("dW_gate", "dW_up", "dW_down"):
         assert np.all(np.abs(got[k] - ref[k]) <= ref[k + "_allow"] * (1 + 1e-9) + 1e-12), k
     assert np.mean(ref["dW_up_allow"]) < 0.01 * np.sqrt(np.mean(ref["dW_up"] ** 2))
+
+
+def _rne_bf16(v: float) -> float:
+    """Round one float to the nearest bf16 value, ties to even (8 significant
+    bits; Python's round() breaks ties to even).  Normal range only."""
+    if v == 0.0:
+        return v
+    m, e = math.frexp(v)                 # v = m 2^e, 0.5 <= |m| < 1
+    return math.ldexp(round(m * 256.0), e - 8)
+
+
+def test_bf16_backward_rounding_points_by_scalar_loops():
+    """The bf16-mode backward rounds exactly dg, du, w a and dX, once each
+    (the GEMM operands and the output), and nothing else: a scalar loop on
+    the micro shape that rounds at those points and computes all else in
+    exact double arithmetic must reproduce the oracle bit for bit (dX) and to
+    the last few double ulps (dW, dw).  A rounding moved (on dA' or dA
+    instead of dg, on a, or one missing) changes dW by ~1e-3 relative."""
+    inp = workloads.make_expert_share("micro")
+    ref = layer.backward_share(inp, bf16_mode=True)
+    x = bf16.decode(inp["x"]); dY = bf16.decode(inp["dY"])
+    wg = bf16.decode(inp["w_gate"]); wu = bf16.decode(inp["w_up"]); wd = bf16.decode(inp["w_down"])
+    re = inp["row_expert"]; w = inp["row_w"].astype(np.float64)
+    R, H = x.shape
+    E, I, _ = wg.shape
+    dWg = np.zeros((E, I, H)); dWu = np.zeros((E, I, H)); dWd = np.zeros((E, H, I))
+    for r in range(R):
+        e = int(re[r])
+        dg = [0.0] * I; du = [0.0] * I; wa = [0.0] * I; dw = 0.0
+        for i in range(I):
+            g = math.fsum(x[r, h] * wg[e, i, h] for h in range(H))
+            u = math.fsum(x[r, h] * wu[e, i, h] for h in range(H))
+            dap = math.fsum(dY[r, h] * wd[e, h, i] for h in range(H))
+            s = 1.0 / (1.0 + math.exp(-g))
+            a = g * s * u
+            dw += dap * a
+            dg[i] = _rne_bf16(w[r] * dap * u * s * (1.0 + g * (1.0 - s)))
+            du[i] = _rne_bf16(w[r] * dap * g * s)
+            wa[i] = _rne_bf16(w[r] * a)
+        dx = [_rne_bf16(math.fsum(dg[i] * wg[e, i, h] + du[i] * wu[e, i, h] for i in range(I))) for h in range(H)]
+        assert np.array_equal(np.array(dx), ref["dX"][r]), r
+        assert math.isclose(dw, ref["d_row_w"][r], rel_tol=1e-12, abs_tol=1e-15)
+        for i in range(I):
+            dWg[e, i] += dg[i] * x[r]
+            dWu[e, i] += du[i] * x[r]
+            dWd[e, :, i] += dY[r] * wa[i]
+    for k, v in (("dW_gate", dWg), ("dW_up", dWu), ("dW_down", dWd)):
+        assert np.allclose(v, ref[k], rtol=1e-12, atol=1e-15), k
+
+
+def test_single_steps_compose_to_the_layer():
+    """The one-GEMM step functions (fed given operands) rebuild the whole
+    layer from its own intermediates: bf16 and MXFP8, forward and backward,
+    expert share and full layer.  The layer itself is pinned by brute force,
+    finite differences and autograd; these pin the step functions to it."""
+    inp = workloads.make_expert_share("small8")
+    x, dY = bf16.decode(inp["x"]), bf16.decode(inp["dY"])
+    wg, wu, wd = (bf16.decode(inp[n]) for n in ("w_gate", "w_up", "w_down"))
+    re, w = inp["row_expert"], inp["row_w"].astype(np.float64)
+    E, I, H = wg.shape
+    f = layer.forward_share(inp)
+    G, U, a = layer.swiglu_rows(x, re, wg, wu)
+    assert np.allclose(G, f["g"], rtol=1e-13, atol=1e-13) and np.array_equal(bf16.round_rne(a), f["a"])
+    assert np.allclose(w[:, None] * layer.down_rows(f["a"], re, wd), f["out_exact"], rtol=1e-12, atol=1e-13)
+    b = layer.backward_share(inp)
+    d = layer.dact_rows(dY, G, U, re, wd, w)
+    assert np.allclose(d["dw"], b["d_row_w"], rtol=1e-12, atol=1e-13)
+    dg, du, wa = bf16.round_rne(d["dg"]), bf16.round_rne(d["du"]), bf16.round_rne(d["wa"])
+    assert np.allclose(layer.dx_rows_from(dg, du, re, wg, wu), b["dX_exact"], rtol=1e-12, atol=1e-13)
+    wgr = layer.wgrads_from(x, dY, dg, du, wa, re, E)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert np.allclose(wgr[k], b[k], rtol=1e-12, atol=1e-13), k
+    # MXFP8
+    fm = layer.forward_share_mxfp8(inp)
+    ac, as_ = mxfp8.quantize(bf16.decode(fm["a_bits"]))
+    wdq = np.stack([layer.qd(m) for m in wd])
+    assert np.allclose(w[:, None] * layer.down_rows(mxfp8.dequantize(ac, as_), re, wdq), fm["out_exact"],
+                       rtol=1e-12, atol=1e-13)
+    bm = layer.backward_share_mxfp8(inp, fm, wgrad_mx_mb=256)
+    dm = layer.dact_rows(dY, fm["g"], fm["u"], re, wd, w, dYq=layer.qd(dY),
+                         wdT=np.stack([layer.qd(wd[e].T) for e in range(E)]))
+    assert np.allclose(dm["dw"], bm["d_row_w"], rtol=1e-12, atol=1e-13)
+    dgm, dum, wam = bf16.round_rne(dm["dg"]), bf16.round_rne(dm["du"]), bf16.round_rne(dm["wa"])
+    pc, ps = mxfp8.quantize(np.concatenate([dgm, dum], axis=1))
+    assert np.allclose(layer.dx_rows_from_mx(pc, ps, re, wg, wu), bm["dX_exact"], rtol=1e-12, atol=1e-13)
+    wm = layer.wgrads_from_mx(x, dY, dgm, dum, wam, re, E, 256)
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert np.allclose(wm[k], bm[k], rtol=1e-12, atol=1e-13), k
+    # full layer: the combine
+    fi = workloads.make_full_layer("tiny")
+    ff = layer.forward_full(fi)
+    assert np.allclose(layer.combine_tokens(ff["y"], ff["topk_w"], fi["shape"].k), ff["out_exact"],
+                       rtol=1e-12, atol=1e-13)

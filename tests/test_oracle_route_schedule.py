@@ -160,3 +160,38 @@ def test_ring_rows_rule():
     assert schedule.ring_rows_for(256 << 20, 4096, 7392) == 32768
     with pytest.raises(ValueError):
         schedule.build(np.zeros(10, np.int32), 1, 8, 4, 4)
+
+
+def ascending_order_case(T=1, H=256, E=8):
+    """Router input whose top-2 depends on the summation order of the logits.
+
+    Token 0: x[0, :4] = (1, 2^-12, 2^-12, -1), the rest 0.  Expert 0's router
+    row starts (1, 2^-12, 2^-12, 1), so its products are (1, 2^-24, 2^-24, -1):
+    summed in fp32 in ascending h from +0, 1 + 2^-24 is a tie that rounds to
+    even, i.e. to 1, twice, and the last product cancels it: z0 = 0 exactly.
+    In exact arithmetic (and summed in descending h) z0 = 2^-23; summed in
+    pairs, 2^-24.  Expert 1's row is (2^-25, 0, ...): z1 = 2^-25 in every
+    order.  Experts 2..7 have row (-1, 0, ...): z = -1.  So the ascending-h
+    fp32 sum ranks expert 1 first (2^-25 > 0) where any of the other orders
+    ranks expert 0 first.  Further tokens, if any, repeat token 0."""
+    x = np.zeros((T, H)); wr = np.zeros((E, H))
+    x[:, :4] = [1.0, 2.0 ** -12, 2.0 ** -12, -1.0]
+    wr[0, :4] = [1.0, 2.0 ** -12, 2.0 ** -12, 1.0]
+    wr[1, 0] = 2.0 ** -25
+    wr[2:, 0] = -1.0
+    return bf16.encode(x), bf16.encode(wr)
+
+
+def test_logits_are_summed_in_ascending_h_from_zero():
+    """Golden case worked by hand from IEEE fp32 round-to-nearest-even (see
+    ascending_order_case): the logits and the top-2 the router reading takes
+    (fp32, ascending h, from +0) differ from those of the exact sum."""
+    xb, wb = ascending_order_case(T=2)
+    x = bf16.decode(xb).astype(np.float32); w = bf16.decode(wb).astype(np.float32)
+    z = route.logits_fp32(x, w, None)
+    assert z[0, 0] == 0.0 and z[0, 1] == 2.0 ** -25 and np.all(z[0, 2:] == -1.0)
+    idx, wts, _ = route.route(x, w, None, 2, 1)
+    assert idx.tolist() == [[1, 0], [1, 0]]
+    # the exact sum would rank them the other way
+    z64 = bf16.decode(xb) @ bf16.decode(wb).T
+    assert z64[0, 0] == 2.0 ** -23 and z64[0, 0] > z64[0, 1]
