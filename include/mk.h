@@ -181,6 +181,33 @@ int mk_schedule_destroy(mk_schedule* sched);
 int mk_build_schedule(mk_workspace* ws, mk_schedule* sched, const int32_t* row_expert_dev, int32_t R,
                       void* stream);
 
+/*
+ * mk_build_schedule without a workspace or schedule object, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same tables as
+ * mk_build_schedule, written to caller-owned device buffers, with the
+ * build's scratch in a fixed 4 MiB device array of the library (one per
+ * GPU, held until the process ends; no allocation happens in this call).
+ *   row_expert_dev [R] int32, minibatch rows MB >= 1, E in [1, 1024],
+ *   item_cap >= 1 (work items the items buffer holds; more set
+ *   MK_DEVERR_SCHED_OVERFLOW in *err_dev and drop the trailing items).
+ *   Outputs (nb = ceil(R / MB)): counts_dev [E], offsets_dev [E+1],
+ *   mb_counts_dev [nb, E], mb_offsets_dev [nb, E+1], sorted_pos_dev [R],
+ *   inv_dev [nb*MB], items_dev [item_cap, 4], mb_items_dev [nb+1], err_dev
+ *   [1] (written whole); layouts as the MK_TAB_* tables.  With R = 0 only
+ *   counts, offsets, items, mb_items and err are written (the others may be
+ *   NULL).
+ * MK_ERR_LIMIT if nb * ceil(MB / 256) * (E + 1) * 4 bytes exceed the 4 MiB
+ * scratch or nb > 65535; MK_ERR_SHAPE / _NULL on bad arguments; MK_ERR_HIP
+ * if the scratch's device address cannot be found.  Calls on one GPU share
+ * the scratch: calls that overlap on one GPU (different streams without
+ * ordering) race.
+ */
+int mk_build_schedule_static(const int32_t* row_expert_dev, int32_t R, int32_t E, int32_t MB, int32_t item_cap,
+                             int32_t* counts_dev, int32_t* offsets_dev, int32_t* mb_counts_dev,
+                             int32_t* mb_offsets_dev, int32_t* sorted_pos_dev, int32_t* inv_dev, int32_t* items_dev,
+                             int32_t* mb_items_dev, uint32_t* err_dev, void* stream);
+
 /* Copy one table of a schedule (device) into dst_dev (device, >= bytes;
  * MK_ERR_LIMIT if bytes exceeds the table). */
 #define MK_TAB_COUNTS     0   /* [E]        int32                                   */

@@ -69,6 +69,7 @@ _SIGS = {
     "mk_schedule_destroy": (ctypes.c_int, [_vp]),
     "mk_schedule_query": (_i64, [_vp, _i32]),
     "mk_build_schedule": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
+    "mk_build_schedule_static": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32] + [_vp] * 10),
     "mk_schedule_copy": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp]),
     "mk_workspace_copy": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp]),
     "mk_mxfp8_quantize": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
@@ -167,6 +168,14 @@ def mk_schedule_query(sched: int, what: int) -> int:
 
 def mk_build_schedule(ws, sched, row_expert, R, stream=None):
     _check("mk_build_schedule", lib.mk_build_schedule(ws, sched, _p(row_expert), R, _s(stream)))
+
+
+def mk_build_schedule_static(row_expert, R, E, MB, item_cap, counts, offsets, mb_counts, mb_offsets, sorted_pos,
+                             inv, items, mb_items, err, stream=None):
+    _check("mk_build_schedule_static",
+           lib.mk_build_schedule_static(_p(row_expert), R, E, MB, item_cap, _p(counts), _p(offsets), _p(mb_counts),
+                                        _p(mb_offsets), _p(sorted_pos), _p(inv), _p(items), _p(mb_items), _p(err),
+                                        _s(stream)))
 
 
 def mk_schedule_copy(sched, table, dst, nbytes, stream=None):

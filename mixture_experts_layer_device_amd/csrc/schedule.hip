@@ -19,6 +19,7 @@
 #include "mk_internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace mk {
 namespace {
@@ -274,4 +275,64 @@ void launch_schedule(const SchedDims& d, const SchedScratch& scr, const SchedTab
                        scr.chunk_counts, t.mb_offsets, t.sorted_pos, t.inv);
 }
 
+// ---- schedule build without allocation -------------------------------------
+//
+// The scratch of the build (per-chunk histograms and flags) in a file-scope
+// device array instead of a workspace: for callers that cannot allocate.
+// Every GPU the library runs on holds its own copy until the process ends;
+// calls on one GPU share it, so calls that overlap on one GPU race.  Every
+// element the build reads is written by the same call first (the count
+// kernel writes the whole [nb, cpm, E] histogram block and the flags), so
+// nothing has to start at zero.
+namespace {
+
+constexpr int64_t kStaticScratchBytes = (int64_t)4 << 20;       // 4 MiB
+static __device__ __align__(256) int32_t scratch[kStaticScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+int32_t* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of this GPU's scratch (looked up once per device, with
+// that device current); null on failure.
+int32_t* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = (int32_t*)ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
 }  // namespace mk
+
+extern "C" int mk_build_schedule_static(const int32_t* row_expert, int32_t R, int32_t E, int32_t MB,
+                                        int32_t item_cap, int32_t* counts, int32_t* offsets, int32_t* mb_counts,
+                                        int32_t* mb_offsets, int32_t* sorted_pos, int32_t* inv, int32_t* items,
+                                        int32_t* mb_items, uint32_t* err, void* stream) {
+  using namespace mk;
+  if (R < 0 || MB < 1 || item_cap < 1) return MK_ERR_SHAPE;
+  if (E < 1 || E > MK_MAX_EXPERTS) return MK_ERR_LIMIT;
+  if (!counts || !offsets || !mb_items || !err || !items) return MK_ERR_NULL;
+  const int64_t nb = R > 0 ? ((int64_t)R + MB - 1) / MB : 0;
+  if (R > 0 && (!row_expert || !mb_counts || !mb_offsets || !sorted_pos || !inv)) return MK_ERR_NULL;
+  if (nb > 65535) return MK_ERR_LIMIT;
+  const int64_t cpm = ((int64_t)MB + MK_SCHED_CHUNK - 1) / MK_SCHED_CHUNK;
+  // scratch: [nb, cpm, E] chunk histograms, then [nb, cpm] chunk flags
+  const int64_t need = (nb * cpm * E + nb * cpm) * 4;
+  if (need > kStaticScratchBytes) return MK_ERR_LIMIT;
+  int32_t* base = device_scratch();
+  if (!base) return MK_ERR_HIP;
+  SchedScratch scr{base, base + nb * cpm * E};
+  SchedTables t{err, mb_counts, mb_offsets, counts, offsets, sorted_pos, inv, items, mb_items};
+  const SchedDims d{MB, E, (int32_t)cpm, item_cap};
+  launch_schedule(d, scr, t, row_expert, R, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
