@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--only", default="",
                     help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, ep_bwd_mxfp8_dgrad, "
                          "full_bwd)")
+    ap.add_argument("--share-mb", type=int, default=0,
+                    help="minibatch rows of the expert-share workloads (0: the two-wave floor of the GEMMs' "
+                         "256 x 256 tiles on this GPU's compute units, mk_two_wave_rows)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) 3 times: the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -291,6 +294,10 @@ def main():
         log(json.dumps(main))
 
     # ---- expert-share shapes ---------------------------------------------
+    # minibatches sized for at least two waves of 256 x 256 output tiles over
+    # the compute units ([MTP] "Three design decisions that matter")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    share_mb = a.share_mb or B.mk_two_wave_rows(7168, 2048, n_cu // 8 * 8, 256, 256)
     if want & {"ep64_fwd", "ep64_mxfp8"}:
         inp = workloads.make_expert_share("ep64_fwd", with_dy=False)
         sh = inp["shape"]
@@ -299,8 +306,8 @@ def main():
         for prec, key in (("bf16", "ep64_fwd"), ("mxfp8", "ep64_mxfp8")):
             if key not in want:
                 continue
-            log(f"[bench] EP=64 expert share forward {prec}: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096")
-            L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=4096)
+            log(f"[bench] EP=64 expert share forward {prec}: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={share_mb}")
+            L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=share_mb)
             packed = L.prepare_weights(wg, wu, wd)
             out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
             s = torch.cuda.current_stream()
@@ -313,6 +320,7 @@ def main():
             results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "forward",
                                      mx=prec == "mxfp8")
             results[key].update(extra)
+            results[key]["minibatch_rows"] = share_mb
             results[key]["err"] = L.device_error()
             L.close()
             del packed
@@ -328,8 +336,8 @@ def main():
         inp = workloads.make_expert_share("ep_bwd")
         sh = inp["shape"]
         log(f"[bench] expert share backward {prec}{' (MXFP8 weight gradients)' if mxw else ''}: "
-            f"R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB=4096 (ring wraps)")
-        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=4096,
+            f"R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={share_mb} (ring wraps)")
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=share_mb,
                      enable_backward=True, wgrad_mxfp8=mxw)
         x = up(inp["x"]); re = up(inp["row_expert"]); rw = up(inp["row_w"]); dY = up(inp["dY"])
         packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]), for_backward=True)
@@ -355,6 +363,7 @@ def main():
         results[key] = summarize(key, sh.R, 0, sh.H, sh.I, sh.E, 8, dt, per, a.steps, "backward",
                                  mx=prec == "mxfp8", replay_rows=min(sh.R, replay_mbs * MB), mx_wgrad=mxw)
         results[key].update(extra)
+        results[key]["minibatch_rows"] = share_mb
         results[key]["err"] = L.device_error()
         L.close()
         del packed, g, x, dY
