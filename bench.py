@@ -41,8 +41,11 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma-separated workloads to run (full, ep64_fwd, ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, ep_bwd_mxfp8_dgrad, "
-                         "full_bwd)")
+                    help="comma-separated workloads to run (full, full_unfused, full_fused, ep64_fwd, ep64_fwd_fused, "
+                         "ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, ep_bwd_mxfp8_dgrad, full_bwd)")
+    ap.add_argument("--main-fused", type=int, default=1,
+                    help="1: the main line runs the forward as one fused launch (mk_config.fused_forward), "
+                         "0: one launch per phase")
     ap.add_argument("--share-mb", type=int, default=0,
                     help="minibatch rows of the expert-share workloads (0: the two-wave floor of the GEMMs' "
                          "256 x 256 tiles on this GPU's compute units, mk_two_wave_rows)")
@@ -70,6 +73,9 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
         w["gemm2"] = (2.0 * R * I * H, R * I * (ab + sc) + E * H * I * (ab + sc) + (R * H * 2 if share else R * H * 4))
         if not share:
             w["combine"] = (0.0, R * H * 4 + T * H * 2 + R * 8)
+        # the fused forward: permute, GEMM1, GEMM2 (and combine) in one launch
+        parts = [w[p] for p in ("permute", "gemm1", "gemm2", "combine") if p in w]
+        w["fused_fwd"] = (sum(f for f, _ in parts), sum(b for _, b in parts))
     else:
         # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
         # (MXFP8: read twice, written as bf16 rows and as codes + scales)
@@ -260,19 +266,21 @@ def main():
         }
 
     results = {}
-    want = set(a.only.split(",")) if a.only else {"full", "ep64_fwd", "ep64_mxfp8", "ep_bwd", "ep_bwd_mxfp8",
-                                                   "full_bwd"}
+    want = set(a.only.split(",")) if a.only else {"full", "full_unfused", "ep64_fwd", "ep64_fwd_fused",
+                                                   "ep64_mxfp8", "ep_bwd", "ep_bwd_mxfp8", "full_bwd"}
     if a.no_breakdown:
         want = {"full"}
 
     # ---- main line: full single-GPU layer forward ------------------------
     main = None
     full_inp = None
-    if "full" in want:
-        log("[bench] full layer forward: T=4096 H=2048 I=768 E=128 k=8")
-        inp = full_inp = workloads.make_full_layer("full")
+
+    def run_full(key, fused):
+        nonlocal full_inp
+        log(f"[bench] full layer forward{' (fused: one launch)' if fused else ''}: T=4096 H=2048 I=768 E=128 k=8")
+        inp = full_inp = full_inp or workloads.make_full_layer("full")
         sh = inp["shape"]
-        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm)
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, fused_forward=fused)
         x = up(inp["x"]); wr = up(inp["w_router"]); bias = up(inp["bias"])
         packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]))
         out = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
@@ -286,28 +294,39 @@ def main():
             B.mk_forward(L.ws, L.sched.handle, B.MK_FULL_LAYER, x, wts, packed, out, None, s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=(out, idx, wts))
-        main = summarize("full", sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False)
-        main.update(extra)
-        main["err"] = L.device_error()
+        res = summarize(key, sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False)
+        res.update(extra)
+        res["err"] = L.device_error()
         L.close()
         del packed
-        log(json.dumps(main))
+        log(json.dumps(res))
+        return res
+
+    if "full" in want:
+        main = run_full("full", a.main_fused)
+    if "full_unfused" in want:
+        results["full_unfused"] = run_full("full_unfused", False)
+    if "full_fused" in want:
+        results["full_fused"] = run_full("full_fused", True)
 
     # ---- expert-share shapes ---------------------------------------------
     # minibatches sized for at least two waves of 256 x 256 output tiles over
     # the compute units ([MTP] "Three design decisions that matter")
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     share_mb = a.share_mb or B.mk_two_wave_rows(7168, 2048, n_cu // 8 * 8, 256, 256)
-    if want & {"ep64_fwd", "ep64_mxfp8"}:
+    if want & {"ep64_fwd", "ep64_fwd_fused", "ep64_mxfp8"}:
         inp = workloads.make_expert_share("ep64_fwd", with_dy=False)
         sh = inp["shape"]
         x = up(inp["x"]); re = up(inp["row_expert"]); rw = up(inp["row_w"])
         wg, wu, wd = up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"])
-        for prec, key in (("bf16", "ep64_fwd"), ("mxfp8", "ep64_mxfp8")):
+        for prec, key, fused in (("bf16", "ep64_fwd", False), ("bf16", "ep64_fwd_fused", True),
+                                 ("mxfp8", "ep64_mxfp8", False)):
             if key not in want:
                 continue
-            log(f"[bench] EP=64 expert share forward {prec}: R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={share_mb}")
-            L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=share_mb)
+            log(f"[bench] EP=64 expert share forward {prec}{' (fused: one launch)' if fused else ''}: R={sh.R} "
+                f"H={sh.H} I={sh.I} E={sh.E} MB={share_mb}")
+            L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=prec, minibatch_rows=share_mb,
+                         fused_forward=fused)
             packed = L.prepare_weights(wg, wu, wd)
             out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
             s = torch.cuda.current_stream()
@@ -437,7 +456,8 @@ def main():
         "config": {"workload": "full single-GPU MoE layer forward: route + build_schedule + permute + expert "
                                "GEMMs (SwiGLU) + combine; T=4096 tokens, H=2048, I=768, 128 experts, top-8 "
                                "renormalised softmax router with per-expert logit bias",
-                   "tokens": 4096, "routed_rows": 32768, "H": 2048, "I": 768, "E": 128, "k": 8},
+                   "tokens": 4096, "routed_rows": 32768, "H": 2048, "I": 768, "E": 128, "k": 8,
+                   "forward_launches": "one fused persistent launch" if a.main_fused else "one launch per phase"},
         "gemm_tflops": main["gemm_tflops"],
         "protocol": {k: main.get(k) for k in ("step_ms_median", "step_ms_cold_median", "repeatable", "timed_phase")},
         "roofline": roof,

@@ -53,6 +53,7 @@ extern "C" {
  *      mk_build_schedule; read with mk_device_error) ---------------------- */
 #define MK_DEVERR_EXPERT_RANGE   0x1u  /* a row_expert id outside [0, E): row dropped, its output is 0 */
 #define MK_DEVERR_SCHED_OVERFLOW 0x2u  /* work table above capacity: trailing tiles dropped            */
+#define MK_DEVERR_WAIT_TIMEOUT   0x4u  /* fused forward: a dependency wait passed its bound (results invalid) */
 
 /* ---- enums --------------------------------------------------------------- */
 #define MK_BF16   0
@@ -92,6 +93,19 @@ extern "C" {
  *                       E*127 rows (every minibatch segment rounded up to 32
  *                       rows, every expert to 128): MK_ERR_LIMIT above
  *                       65535 * 128 rows.
+ *   fused_forward       1 = (precision MK_BF16) mk_forward runs the
+ *                       permute, GEMM1 + SwiGLU and GEMM2 as one persistent
+ *                       launch in which the permute of minibatch b+1, GEMM1
+ *                       of b and GEMM2 of b-1 run at once on different
+ *                       compute units ([MTP] opening paragraph: every step
+ *                       in a single kernel; "Three design decisions that
+ *                       matter": minibatch granularity), ordered by device
+ *                       counters; the full layer's combine follows as a
+ *                       second launch.  Same results bit for bit as the
+ *                       phase-by-phase launches.  Applies when the ring
+ *                       holds every minibatch of the call; a call whose
+ *                       rows wrap the ring runs one launch per phase.
+ *                       0 = one launch per phase.
  */
 typedef struct mk_config {
   int32_t minibatch_rows;
@@ -101,7 +115,8 @@ typedef struct mk_config {
   int32_t renorm;
   int32_t enable_backward;
   int32_t wgrad_mxfp8;
-  int32_t reserved[2];
+  int32_t fused_forward;
+  int32_t reserved;
 } mk_config;
 
 typedef struct mk_workspace mk_workspace;   /* opaque */
@@ -383,7 +398,8 @@ int mk_backward_layer(mk_workspace* ws, const mk_schedule* sched, const void* fw
 #define MK_PH_ROUTER_BWD 14   /* router backward: logit gradient, dW_router, d_bias */
 #define MK_PH_REPLAY     15   /* re-gather of the x rows of minibatches evicted from the ring */
 #define MK_PH_WGRAD_QUANT 16  /* MXFP8 weight gradients: operands quantised along the rows */
-#define MK_PH_COUNT      17
+#define MK_PH_FUSED_FWD  17   /* fused forward: the one persistent launch (permute, GEMM1, GEMM2) */
+#define MK_PH_COUNT      18
 int mk_timing_enable(mk_workspace* ws, int32_t on);
 int mk_timing_read(mk_workspace* ws, float* ms_out, int32_t* launches_out);
 /*

@@ -50,7 +50,8 @@ class MkConfig(ctypes.Structure):
         ("renorm", ctypes.c_int32),
         ("enable_backward", ctypes.c_int32),
         ("wgrad_mxfp8", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("fused_forward", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -229,7 +230,8 @@ def mk_timing_phases(ws, phases=None) -> None:
 
 
 PHASES = ["route", "schedule", "permute", "gemm1", "quant_a", "gemm2", "combine", "bwd_gather", "bwd_dact",
-          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd", "replay", "wgrad_quant"]
+          "bwd_dw", "bwd_dx", "wgrad_down", "wgrad_gate_up", "bwd_combine", "router_bwd", "replay", "wgrad_quant",
+          "fused_fwd"]
 
 
 def mk_timing_read(ws) -> dict:

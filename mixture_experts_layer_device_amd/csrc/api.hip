@@ -327,6 +327,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   if (cfg->ring_bytes >= ((int64_t)1 << 31)) return MK_ERR_LIMIT;
   if (cfg->enable_backward && I % 256) return MK_ERR_SHAPE;
   if (cfg->wgrad_mxfp8 && (cfg->precision != MK_MXFP8 || !cfg->enable_backward)) return MK_ERR_CONFIG;
+  if (cfg->fused_forward && cfg->precision != MK_BF16) return MK_ERR_CONFIG;
 
   mk_workspace* ws = (mk_workspace*)calloc(1, sizeof(mk_workspace));
   if (!ws) return MK_ERR_HIP;
@@ -394,6 +395,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   const int64_t npos = ws->npos;
   Carver c;
   const size_t o_zero = c.take(512);
+  const size_t o_fctl = c.take((size_t)fused_ctl_words(ws->item_cap) * 4);
   const size_t o_cc = c.take((size_t)ws->nb_max * ws->cpm * E * 4);
   const size_t o_cb = c.take((size_t)ws->nb_max * ws->cpm * 4);
   const size_t o_ring = c.take((size_t)ws->ring_rows * ws->row_bytes);
@@ -445,6 +447,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   }
   char* b = (char*)ws->base;
   ws->zero_row = (uint16_t*)(b + o_zero);
+  ws->fused_ctl = (uint32_t*)(b + o_fctl);
   ws->sscr.chunk_counts = (int32_t*)(b + o_cc);
   ws->sscr.chunk_bad = (int32_t*)(b + o_cb);
   ws->ring = (uint8_t*)(b + o_ring);
@@ -734,6 +737,41 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
   // expert share: GEMM2 writes w*y straight to arrival order (one rounding);
   // full layer: GEMM2 keeps y in fp32 and the combine sums the k rows
   uint16_t* out_fused = share ? (uint16_t*)out : nullptr;
+  if (ws->cfg.fused_forward && nb <= ring_mbs) {
+    // one persistent launch for permute, GEMM1 and GEMM2, overlapping
+    // across minibatches (the ring holds them all); the full layer's combine
+    // follows as its own launch
+    FusedFwd f;
+    f.ir = item_range(ws, sc, 0, nb);
+    f.nb = nb;
+    f.src_div = src_div;
+    f.H = H;
+    f.I = I;
+    f.ring_rows = ws->ring_rows;
+    f.full = !share;
+    f.x = x;
+    f.inv = st.inv;
+    f.row_w = row_w;
+    f.ring = (uint16_t*)ws->ring;
+    f.wgu = packed_bf16(ws, (void*)packed).wgu;
+    f.wd = packed_bf16(ws, (void*)packed).wd;
+    f.a_buf = ws->a_buf;
+    f.gu_save = (float*)fwd_ctx;
+    f.y32 = ws->y_buf;
+    f.out = (uint16_t*)out;
+    f.ctl = ws->fused_ctl;
+    f.err = st.err;
+    {
+      Phase ph(ws, MK_PH_FUSED_FWD, s);
+      launch_fused_forward_bf16(f, ws->n_cu, s);
+    }
+    Phase ph(ws, MK_PH_COMBINE, s);
+    if (share)
+      launch_zero_dropped_rows(st.sorted_pos, R, (uint16_t*)out, H, s);
+    else
+      launch_combine(ws->y_buf, H, st.sorted_pos, row_w, kk, (int64_t)R / kk, (uint16_t*)out, ws->n_cu, s);
+    return check_launch();
+  }
   if (!mx) {
     PackedBF16 p = packed_bf16(ws, (void*)packed);
     for (int b0 = 0; b0 < nb; b0 += ring_mbs) {

@@ -19,6 +19,7 @@
 // k = 8*(l/16) .. +7; the 16x16 fp32 result in lane l is column l%16, rows
 // 4*(l/16) .. +3.
 #include "gemm_common.h"
+#include "rows_common.h"
 
 namespace mk {
 namespace {
@@ -148,49 +149,52 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
 // a[p, i] = silu(g) * u with [g | u] = ring[p] . W_gu[e]^T; W_gu is packed so
 // that each 32-column group holds 16 gate columns then the 16 up columns of
 // the same i.  a is a bf16 GEMM operand (stored [p, I]); optionally g and u
-// are saved in fp32 (packed order, [p, 2I]) for the backward.
+// are saved in fp32 (packed order, [p, 2I]) for the backward.  NB packed
+// columns of the tile: NB / 2 features, a wave's NB / 4 columns being
+// NB / 128 gate/up groups of 32.
+template <int NB>
+__device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* __restrict__ ring, int ring_rows,
+                                           const uint16_t* __restrict__ wgu, int H, int I,
+                                           uint16_t* __restrict__ a_out, float* __restrict__ gu_save, char* lds) {
+  auto arow = [&](int r) {
+    const int p = ti.pos0 + min(r, ti.rows - 1);
+    return ring + (int64_t)(p % ring_rows) * H;
+  };
+  Acc acc;
+  mainloop_nt<NB>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, lds, acc);
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = frag_row(i, v);
+#pragma unroll
+      for (int q = 0; q < NB / 128; ++q) {
+        const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
+        stage_put(lds, r, wn * (NB / 8) + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+        if (gu_save && r < ti.rows) {
+          float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * (NB / 4) + q * 32 + (lane & 15);
+          dst[0] = g;
+          dst[16] = u;
+        }
+      }
+    }
+  stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
+    return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
+  });
+}
+
 __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ ring,
                                                         int ring_rows, const uint16_t* __restrict__ wgu, int H,
                                                         int I, uint16_t* __restrict__ a_out,
                                                         float* __restrict__ gu_save) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = 2 * I / BN;
-  // NB packed columns of the tile: NB / 2 features, a wave's NB / 4 columns
-  // being NB / 128 gate/up groups of 32
-  auto body = [&](const TileInfo& ti, auto nb) {
-    constexpr int NB = decltype(nb)::value;
-    auto arow = [&](int r) {
-      const int p = ti.pos0 + min(r, ti.rows - 1);
-      return ring + (int64_t)(p % ring_rows) * H;
-    };
-    Acc acc;
-    mainloop_nt<NB>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, lds, acc);
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = frag_row(i, v);
-#pragma unroll
-        for (int q = 0; q < NB / 128; ++q) {
-          const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
-          stage_put(lds, r, wn * (NB / 8) + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
-          if (gu_save && r < ti.rows) {
-            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * (NB / 4) + q * 32 + (lane & 15);
-            dst[0] = g;
-            dst[16] = u;
-          }
-        }
-      }
-    stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
-      return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
-    });
-  };
   for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
     if (half < 0)
-      body(ti, std::integral_constant<int, BN>{});
+      gemm1_tile<BN>(ti, ring, ring_rows, wgu, H, I, a_out, gu_save, lds);
     else
-      body(ti, std::integral_constant<int, BN / 2>{});
+      gemm1_tile<BN / 2>(ti, ring, ring_rows, wgu, H, I, a_out, gu_save, lds);
   });
 }
 
@@ -200,6 +204,35 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
 //        one rounding, rows stored straight to arrival order.
 // else : y is kept in fp32 ([p, H]) for the full-layer combine.
 template <bool SHARE>
+__device__ __forceinline__ void gemm2_tile(const TileInfo& ti, const uint16_t* __restrict__ a,
+                                           const uint16_t* __restrict__ wd, int H, int I, float* __restrict__ y32,
+                                           uint16_t* __restrict__ out, const int32_t* __restrict__ inv,
+                                           const float* __restrict__ row_w, char* lds) {
+  auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
+  Acc acc;
+  mainloop_nt(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = frag_row(i, v);
+      if (SHARE) {
+        const float w = r < ti.rows ? row_w[inv[ti.pos0 + r]] : 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), w * acc[i][j][v]);
+      } else if (r < ti.rows) {
+        float* dst = y32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
+      }
+    }
+  if (SHARE)
+    stage_flush<256>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? out + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
+    });
+}
+
+template <bool SHARE>
 __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ a,
                                                         const uint16_t* __restrict__ wd, int H, int I,
                                                         float* __restrict__ y32, uint16_t* __restrict__ out,
@@ -207,30 +240,8 @@ __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint
                                                         const float* __restrict__ row_w) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = H / BN;
-  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
-    auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
-    Acc acc;
-    mainloop_nt(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = frag_row(i, v);
-        if (SHARE) {
-          const float w = r < ti.rows ? row_w[inv[ti.pos0 + r]] : 0.f;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) stage_put(lds, r, frag_col(j), w * acc[i][j][v]);
-        } else if (r < ti.rows) {
-          float* dst = y32 + (int64_t)(ti.pos0 + r) * H + ti.n0;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) dst[frag_col(j)] = acc[i][j][v];
-        }
-      }
-    if (SHARE)
-      stage_flush<256>(lds, [&](int r) -> uint16_t* {
-        return r < ti.rows ? out + (int64_t)inv[ti.pos0 + r] * H + ti.n0 : nullptr;
-      });
-  });
+  for_each_tile(ir, ntn,
+                [&](const TileInfo& ti) { gemm2_tile<SHARE>(ti, a, wd, H, I, y32, out, inv, row_w, lds); });
 }
 
 // ------------------------------------------------- backward: dA' + SwiGLU ----
@@ -466,6 +477,193 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
   }
 }
 
+// ------------------------------------------------ fused forward, bf16 ----
+// The forward's permute, GEMM1 + SwiGLU and GEMM2 in one persistent launch
+// ([MTP] opening paragraph: every step in one kernel; "Three design
+// decisions that matter": overlap at minibatch granularity): while some
+// compute units permute minibatch b+1, others run GEMM1 of b and GEMM2 of
+// b-1, and the tail of one phase fills with the next phase's tiles.
+//
+// Items are dealt to the 8 XCDs (item l of a minibatch to XCD l mod 8) and
+// every unit of an item -- its 4 permute chunks of 64 rows, its GEMM1 tiles,
+// its GEMM2 tiles -- runs on that XCD, taken in a fixed order from that
+// XCD's own ticket by the workgroups the hardware placed there (read from
+// the XCC_ID register, not assumed from the block id).  Per iteration j of
+// an XCD's queue: G1(j-1), P(j), G2(j-2).  A unit only ever waits for units
+// of lower tickets of the same queue (taken, so held by running workgroups),
+// hence every queue drains.  Every value one unit hands to another (ring
+// rows, a rows) is written and read through the one L2 of their XCD, so a
+// producer only waits for its stores to complete before bumping the
+// item's counter, and a consumer reads after seeing the counter -- no cache
+// writeback or invalidate; no unit reads an address that an earlier unit of
+// the launch read (the ring holds every minibatch of the call: no slot is
+// reused), so no stale copy can sit in a compute unit's L1 either.  A wait
+// is bounded: past the bound it sets MK_DEVERR_WAIT_TIMEOUT and goes on, so
+// the launch always ends.
+constexpr int FUSE_CH = 64;                       // rows per permute unit
+constexpr int FUSE_PCH = MK_TILE_M / FUSE_CH;     // permute units per item
+constexpr int FUSE_XCD = 8;
+enum { U_NONE = -1, U_G1 = 0, U_P = 1, U_G2 = 2 };
+
+struct FusedArgs {
+  const int32_t* items;       // [cap, 4] (row_begin, rows, expert, minibatch)
+  const int32_t* mb_items;    // [nb + 1]
+  int item_cap, nb, src_div, H, I, ring_rows;
+  const uint16_t* x;          // token rows (full layer) or routed rows (expert share)
+  const int32_t* inv;
+  const float* row_w;
+  uint16_t* ring;
+  const uint16_t* wgu;
+  const uint16_t* wd;
+  uint16_t* a_buf;
+  float* gu_save;
+  float* y32;                 // full layer: GEMM2 rows in fp32
+  uint16_t* out;              // expert share: weighted rows in arrival order
+  uint32_t* ticket;           // [8 XCDs, 64 words apart]; zeroed before the launch, as are the counters
+  uint32_t* p_done;           // [cap] permute units done per item
+  uint32_t* g1_done;          // [cap] GEMM1 tiles done per item
+  uint32_t* err;
+};
+
+struct FusedUnit {
+  int kind, b, idx;
+};
+
+__device__ __forceinline__ int fused_items_lo(const FusedArgs& a, int b) { return min(a.mb_items[b], a.item_cap); }
+__device__ __forceinline__ int fused_items(const FusedArgs& a, int b) {
+  return min(a.mb_items[b + 1], a.item_cap) - min(a.mb_items[b], a.item_cap);
+}
+// items of minibatch b on XCD x: local indices x, x + 8, ...
+__device__ __forceinline__ int fused_items_x(const FusedArgs& a, int b, int x) {
+  const int n = fused_items(a, b);
+  return n > x ? (n - x + FUSE_XCD - 1) / FUSE_XCD : 0;
+}
+__device__ __forceinline__ int fused_item(const FusedArgs& a, int b, int x, int m) {
+  return fused_items_lo(a, b) + x + FUSE_XCD * m;
+}
+__device__ __forceinline__ int fused_count(const FusedArgs& a, int kind, int b, int x) {
+  const int n = fused_items_x(a, b, x);
+  return kind == U_P ? n * FUSE_PCH : kind == U_G1 ? n * (2 * a.I / BN) : n * (a.H / BN);
+}
+
+// Unit of ticket t of XCD x's queue (U_NONE past the last one).
+__device__ FusedUnit fused_decode(const FusedArgs& a, int x, int t) {
+  for (int j = 0; j < a.nb + 2; ++j) {
+#pragma unroll 1
+    for (int kind = 0; kind < 3; ++kind) {
+      const int b = kind == U_G1 ? j - 1 : kind == U_P ? j : j - 2;
+      if (b < 0 || b >= a.nb) continue;
+      const int n = fused_count(a, kind, b, x);
+      if (t < n) return FusedUnit{kind, b, t};
+      t -= n;
+    }
+  }
+  return FusedUnit{U_NONE, 0, 0};
+}
+
+// Wave 0 (all of its lanes, so the loop is uniform): wait until *p >=
+// target.  The wait is bounded (about a quarter of a second); once any wait
+// of the launch has timed out (the error bit is set) the others stop
+// waiting too, so a launch whose counters went wrong still ends quickly.
+__device__ __forceinline__ void fused_wait(const uint32_t* p, uint32_t target, uint32_t* err) {
+  int spins = 0;
+  while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+         target) {
+    __builtin_amdgcn_s_sleep(8);
+    ++spins;
+    if ((spins & 1023) == 0 &&
+        (__builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
+         MK_DEVERR_WAIT_TIMEOUT))
+      break;
+    if (spins >= (1 << 20)) {
+      if ((threadIdx.x & 63) == 0) atomicOr(err, MK_DEVERR_WAIT_TIMEOUT);
+      break;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Tile idx of XCD x's GEMM tiles of minibatch b (ntn column tiles per item),
+// in groups of 4 items that share B columns.
+__device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int x, int idx, int ntn, int& item) {
+  int it, nt;
+  tile_coords(idx, fused_items_x(a, b, x), ntn, it, nt);
+  item = fused_item(a, b, x, it);
+  const int* q = a.items + 4 * item;
+  return TileInfo{q[0], q[1], q[2], nt * BN};
+}
+
+// Control flow around the barriers is uniform: wave 0 as a whole takes the
+// ticket (lane 0's atomic, broadcast), decodes it and waits, every wave
+// reads the unit back from LDS as a scalar, and only the counter bumps are
+// single-lane; no lane of a wave ever takes a different path to a barrier.
+template <bool SHARE>
+__global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ int su[3];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the XCD this workgroup runs on (HW_REG_XCC_ID, bits 3:0)
+  const int x = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (FUSE_XCD - 1);
+  const int ntn1 = 2 * a.I / BN, ntn2 = a.H / BN;
+  while (true) {
+    if (wave == 0) {
+      uint32_t t = 0;
+      if (lane == 0) t = atomicAdd(a.ticket + 64 * x, 1u);
+      const FusedUnit u = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t));
+      if (u.kind == U_G1) {
+        int item;
+        (void)fused_tile(a, u.b, x, u.idx, ntn1, item);
+        fused_wait(a.p_done + item, (uint32_t)FUSE_PCH, a.err);
+      } else if (u.kind == U_G2) {
+        int item;
+        (void)fused_tile(a, u.b, x, u.idx, ntn2, item);
+        fused_wait(a.g1_done + item, (uint32_t)ntn1, a.err);
+      }
+      if (lane == 0) {
+        su[0] = u.kind;
+        su[1] = u.b;
+        su[2] = u.idx;
+      }
+    }
+    __syncthreads();
+    const int kind = __builtin_amdgcn_readfirstlane(su[0]);
+    const int b = __builtin_amdgcn_readfirstlane(su[1]);
+    const int idx = __builtin_amdgcn_readfirstlane(su[2]);
+    if (kind == U_NONE) break;
+    int item = -1;
+    if (kind == U_P) {
+      // rows [64c, 64c + 64) of the XCD's item idx / 4, one wave per row
+      item = fused_item(a, b, x, idx / FUSE_PCH);
+      const int* q = a.items + 4 * item;
+      const int r0 = (idx % FUSE_PCH) * FUSE_CH, r1 = min(q[1], r0 + FUSE_CH);
+      for (int r = r0 + wave; r < r1; r += NT / 64) {
+        const int64_t p = q[0] + r;
+        const int src = a.inv[p];
+        if (src >= 0)
+          copy_row_wave((const u32x4_t*)(a.x + (int64_t)(src / a.src_div) * a.H),
+                        (u32x4_t*)(a.ring + (p % a.ring_rows) * a.H), a.H / 8, lane);
+      }
+    } else if (kind == U_G1) {
+      const TileInfo ti = fused_tile(a, b, x, idx, ntn1, item);
+      gemm1_tile<BN>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
+    } else {
+      const TileInfo ti = fused_tile(a, b, x, idx, ntn2, item);
+      gemm2_tile<SHARE>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
+    }
+    // publish: every wave's stores complete (in the XCD's L2), then one
+    // counter bump
+    wait_all_mem();
+    __syncthreads();
+    if (wave == 0 && lane == 0) {
+      if (kind == U_P)
+        __hip_atomic_fetch_add(a.p_done + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (kind == U_G1)
+        __hip_atomic_fetch_add(a.g1_done + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 }  // namespace
 
 void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_rows, const uint16_t* wgu,
@@ -481,6 +679,40 @@ void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* w
   else
     hipLaunchKernelGGL(gemm2_bf16_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv,
                        row_w);
+}
+
+void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
+  FusedArgs a;
+  a.items = f.ir.items;
+  a.mb_items = f.ir.mb_items;
+  a.item_cap = f.ir.item_cap;
+  a.nb = f.nb;
+  a.src_div = f.src_div;
+  a.H = f.H;
+  a.I = f.I;
+  a.ring_rows = f.ring_rows;
+  a.x = f.x;
+  a.inv = f.inv;
+  a.row_w = f.row_w;
+  a.ring = f.ring;
+  a.wgu = f.wgu;
+  a.wd = f.wd;
+  a.a_buf = f.a_buf;
+  a.gu_save = f.gu_save;
+  a.y32 = f.y32;
+  a.out = f.out;
+  uint32_t* c = f.ctl;
+  a.ticket = c;
+  a.p_done = c + 64 * FUSE_XCD;
+  a.g1_done = a.p_done + f.ir.item_cap;
+  a.err = f.err;
+  // the tickets and the counters start at zero (a fill kernel, not a memset,
+  // so the sequence can be captured in a graph)
+  launch_fill_u32(c, 0u, fused_ctl_words(f.ir.item_cap), s);
+  if (f.full)
+    hipLaunchKernelGGL(fused_forward_kernel<false>, dim3(n_cu), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(fused_forward_kernel<true>, dim3(n_cu), dim3(NT), 0, s, a);
 }
 
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,

@@ -67,6 +67,7 @@ struct mk_workspace {
   uint16_t *dye, *dgdu, *wa;  // backward: [npos, H], [npos, 2I], [npos, I]
   float* dw_part;             // [npos, I/64]
   uint16_t* zero_row;         // 512 zero bytes (weight-gradient rows past a segment's end)
+  uint32_t* fused_ctl;        // fused forward: ticket and dependency counters
   uint8_t *dye_c, *dye_s;     // MXFP8 backward: dY rows quantised along H  [npos, H], [npos, H/32]
   uint8_t *dgdu_c, *dgdu_s;   //                 dg/du quantised along 2I   [npos, 2I], [npos, 2I/32]
   float* dz;                  // [ceil(max_rows / k), E]: router logit gradient (and logits)
@@ -176,6 +177,29 @@ struct ItemRange {
 void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_rows,
                        const uint16_t* wgu, int H, int I, uint16_t* a_out, float* gu_save,
                        int n_cu, hipStream_t s);
+// The bf16 forward's permute, GEMM1 + SwiGLU and GEMM2 in one persistent
+// launch, minibatches overlapping (the ring must hold every minibatch: no
+// slot reuse inside the launch); ctl is fused_ctl_words(item_cap) words of
+// device memory (zeroed by the launcher), err the schedule's error word.
+// The full layer's combine (fp32 y rows from every XCD) is the caller's
+// next launch.
+struct FusedFwd {
+  ItemRange ir;               // all minibatches
+  int nb, src_div, H, I, ring_rows, full;
+  const uint16_t* x;
+  const int32_t* inv;
+  const float* row_w;
+  uint16_t* ring;
+  const uint16_t *wgu, *wd;
+  uint16_t* a_buf;
+  float* gu_save;
+  float* y32;
+  uint16_t* out;
+  uint32_t* ctl;
+  uint32_t* err;
+};
+inline int64_t fused_ctl_words(int64_t item_cap) { return 64 * 8 + 2 * item_cap; }
+void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s);
 // out != nullptr: expert share, out[inv[p]] = bf16(row_w[inv[p]] * y[p]); else y32[p] = y[p]
 void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* wd, int H, int I,
                        float* y32, uint16_t* out, const int32_t* inv, const float* row_w, int n_cu,

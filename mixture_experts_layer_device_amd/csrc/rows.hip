@@ -8,6 +8,7 @@
 // row are all issued before its stores so each lane keeps several in flight.
 #include "mk_device.h"
 #include "mk_internal.h"
+#include "rows_common.h"
 
 #include <algorithm>
 
@@ -25,21 +26,11 @@ __global__ __launch_bounds__(RT) void gather_rows_kernel(const uint16_t* __restr
                                                          int64_t p_lo, int64_t p_hi, int32_t ring_rows,
                                                          uint16_t* __restrict__ dst) {
   const int lane = threadIdx.x & 63;
-  const int64_t n16 = H / 8;
   for (int64_t p = p_lo + wave_id(); p < p_hi; p += wave_count()) {
     const int r = inv[p];
     if (r < 0) continue;
-    const u32x4_t* s = (const u32x4_t*)(src + (int64_t)(r / src_div) * H);
-    u32x4_t* d = (u32x4_t*)(dst + (ring_rows ? p % ring_rows : p) * H);
-    for (int64_t g0 = lane; g0 < n16; g0 += 64 * 8) {
-      u32x4_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (g0 + 64 * u < n16) v[u] = __builtin_nontemporal_load(s + g0 + 64 * u);
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (g0 + 64 * u < n16) d[g0 + 64 * u] = v[u];
-    }
+    copy_row_wave((const u32x4_t*)(src + (int64_t)(r / src_div) * H),
+                  (u32x4_t*)(dst + (ring_rows ? p % ring_rows : p) * H), H / 8, lane);
   }
 }
 
@@ -140,63 +131,13 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
   }
 }
 
-// out[o] = sum_{j < kk} w[o*kk + j] * y[sorted_pos[o*kk + j]], j ascending, fp32,
-// one rounding to bf16 (y is the fp32 GEMM2 output).  A dropped row
-// (sorted_pos -1) adds nothing.  One wave per output row; lane l takes
-// columns 4l .. 4l+3 of each 256-column chunk (one 16-byte load per routed
-// row, a wave reading 1 KiB contiguous), two chunks at a time, the routed
-// rows' loads issued 8 at a time and summed in row order.
+// The full-layer combine (combine_row_wave): one wave per output row.
 __global__ __launch_bounds__(RT) void combine_kernel(const float* __restrict__ y, int64_t H,
                                                      const int32_t* __restrict__ sorted_pos,
                                                      const float* __restrict__ row_w, int kk, int64_t n_out,
                                                      uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  for (int64_t o = wave_id(); o < n_out; o += wave_count()) {
-    // lane j (< kk, kk <= 64) holds the j-th routed row's position and weight
-    const int pj = lane < kk ? sorted_pos[o * kk + lane] : -1;
-    const float wj = lane < kk ? row_w[o * kk + lane] : 0.f;
-    for (int64_t c0 = 0; c0 < H; c0 += 2 * 256) {
-      float acc[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[h][q] = 0.f;
-      const bool act1 = c0 + 256 < H;
-      for (int j0 = 0; j0 < kk; j0 += 8) {
-        f32x4_t v[8][2];
-        float wv[8];
-        bool live[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int j = j0 + u;
-          const int pos = __shfl(pj, j < kk ? j : 0);
-          wv[u] = __shfl(wj, j < kk ? j : 0);
-          live[u] = j < kk && pos >= 0;
-          if (live[u]) {
-            const float* src = y + (int64_t)pos * H + c0 + lane * 4;
-            v[u][0] = __builtin_nontemporal_load((const f32x4_t*)src);
-            v[u][1] = act1 ? __builtin_nontemporal_load((const f32x4_t*)(src + 256)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (!live[u]) continue;   // a dropped row adds nothing
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[h][q] += wv[u] * v[u][h][q];
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h == 1 && !act1) break;
-        u32x2_t ov;
-        ov[0] = pack_bf16x2(acc[h][0], acc[h][1]);
-        ov[1] = pack_bf16x2(acc[h][2], acc[h][3]);
-        __builtin_nontemporal_store(ov, (u32x2_t*)(out + o * H + c0 + h * 256 + lane * 4));
-      }
-    }
-  }
+  for (int64_t o = wave_id(); o < n_out; o += wave_count()) combine_row_wave(y, H, sorted_pos, row_w, kk, o, out, lane);
 }
 
 __global__ void zero_dropped_rows_kernel(const int32_t* __restrict__ sorted_pos, int64_t R,

@@ -58,7 +58,8 @@ class MoELayer:
     default schedule; calls take ``sched=`` to use another one."""
 
     def __init__(self, H, I, E, k, max_rows, precision="bf16", minibatch_rows=0, ring_bytes=256 << 20,
-                 renorm=1, enable_backward=False, capacity_mult=1.0, wgrad_mxfp8=False, device="cuda"):
+                 renorm=1, enable_backward=False, capacity_mult=1.0, wgrad_mxfp8=False, fused_forward=False,
+                 device="cuda"):
         cfg = B.mk_config_default()
         cfg.minibatch_rows = minibatch_rows
         cfg.precision = PRECISION[precision]
@@ -67,6 +68,7 @@ class MoELayer:
         cfg.renorm = renorm
         cfg.enable_backward = int(enable_backward)
         cfg.wgrad_mxfp8 = int(wgrad_mxfp8)
+        cfg.fused_forward = int(fused_forward)
         self.H, self.I, self.E, self.k = H, I, E, k
         self.precision = precision
         self.device = device

@@ -131,3 +131,12 @@ def test_minibatch_count_limit():
     with pytest.raises(B.MkError) as ei:
         B.mk_workspace_create(c, 8 * 65536, 256, 128, 8, 2)
     assert ei.value.status == B.MK_ERR_LIMIT
+
+
+def test_fused_forward_needs_bf16():
+    c = B.mk_config_default()
+    c.precision = B.MK_MXFP8
+    c.fused_forward = 1
+    with pytest.raises(B.MkError) as ei:
+        B.mk_workspace_create(c, 4096, 256, 256, 8, 2)
+    assert ei.value.status == B.MK_ERR_CONFIG
