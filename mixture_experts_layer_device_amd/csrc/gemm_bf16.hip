@@ -151,8 +151,9 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
 // the same i.  a is a bf16 GEMM operand (stored [p, I]); optionally g and u
 // are saved in fp32 (packed order, [p, 2I]) for the backward.  NB packed
 // columns of the tile: NB / 2 features, a wave's NB / 4 columns being
-// NB / 128 gate/up groups of 32.
-template <int NB>
+// NB / 128 gate/up groups of 32.  WT: the a rows are written through to
+// memory (read by another XCD in the same launch).
+template <int NB, bool WT = false>
 __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* __restrict__ ring, int ring_rows,
                                            const uint16_t* __restrict__ wgu, int H, int I,
                                            uint16_t* __restrict__ a_out, float* __restrict__ gu_save, char* lds) {
@@ -179,9 +180,14 @@ __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* _
         }
       }
     }
-  stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
-    return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
-  });
+  if constexpr (WT)
+    stage_flush_wt<NB / 2>(lds, a_out, [&](int r) -> int64_t {
+      return r < ti.rows ? ((int64_t)(ti.pos0 + r) * I + ti.n0 / 2) * 2 : -1;
+    });
+  else
+    stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
+      return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
+    });
 }
 
 __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ ring,
@@ -482,24 +488,35 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
 // ([MTP] opening paragraph: every step in one kernel; "Three design
 // decisions that matter": overlap at minibatch granularity): while some
 // compute units permute minibatch b+1, others run GEMM1 of b and GEMM2 of
-// b-1, and the tail of one phase fills with the next phase's tiles.
+// b-1, and the tail of one phase fills with the next phase's units.  The
+// full layer's combine, which needs every GEMM2 tile of the layer when it
+// runs as one minibatch, follows as its own launch.
 //
-// Items are dealt to the 8 XCDs (item l of a minibatch to XCD l mod 8) and
-// every unit of an item -- its 4 permute chunks of 64 rows, its GEMM1 tiles,
-// its GEMM2 tiles -- runs on that XCD, taken in a fixed order from that
-// XCD's own ticket by the workgroups the hardware placed there (read from
-// the XCC_ID register, not assumed from the block id).  Per iteration j of
-// an XCD's queue: G1(j-1), P(j), G2(j-2).  A unit only ever waits for units
-// of lower tickets of the same queue (taken, so held by running workgroups),
-// hence every queue drains.  Every value one unit hands to another (ring
-// rows, a rows) is written and read through the one L2 of their XCD, so a
-// producer only waits for its stores to complete before bumping the
-// item's counter, and a consumer reads after seeing the counter -- no cache
-// writeback or invalidate; no unit reads an address that an earlier unit of
-// the launch read (the ring holds every minibatch of the call: no slot is
-// reused), so no stale copy can sit in a compute unit's L1 either.  A wait
-// is bounded: past the bound it sets MK_DEVERR_WAIT_TIMEOUT and goes on, so
-// the launch always ends.
+// Units: per item (256 rows of one expert in one minibatch) 4 permute
+// chunks of 64 rows, 2I/256 GEMM1 tiles and H/256 GEMM2 tiles.  Unit u of a
+// segment (item-major: u = item * tiles + tile) goes to queue u mod 8: every
+// queue gets an equal share (to one unit), and a weight column panel stays
+// in one queue, or two, across the items of an expert.  Queue x is taken by
+// the workgroups whose index is x mod 8 -- the workgroups the hardware
+// places on XCD x, since a dispatch deals its workgroups to the 8 XCDs in
+// turn -- so a panel is read into one XCD's L2.  (Only speed rests on that
+// placement: each queue has workgroups whatever it is.)  A queue's
+// workgroups take its units in a fixed order from its own ticket; per
+// iteration j: GEMM1 of minibatch j-1, permute of j, GEMM2 of j-2.
+// Dependencies (device counters): a GEMM1 tile waits for its item's 4
+// permute chunks, a GEMM2 tile for its item's GEMM1 tiles.  Every wait
+// points at a unit of an earlier iteration, so the unit with the smallest
+// iteration never waits and every queue drains; waits are bounded anyway
+// (about 0.25 s, then MK_DEVERR_WAIT_TIMEOUT and on).
+//
+// Coherence across the XCDs without cache maintenance: what one unit hands
+// to another -- ring rows and a rows -- is stored with the device-scope
+// bit, written through to memory; the producer waits for those stores to
+// complete before bumping the counter; the consumer reads after seeing it.
+// Every such location is written once, before any read of it in the launch
+// (the ring holds every minibatch of the call: no slot is reused; a tile
+// reads only its own item's rows), so no XCD can hold a stale copy in its
+// L2 or L1.
 constexpr int FUSE_CH = 64;                       // rows per permute unit
 constexpr int FUSE_PCH = MK_TILE_M / FUSE_CH;     // permute units per item
 constexpr int FUSE_XCD = 8;
@@ -518,44 +535,38 @@ struct FusedArgs {
   uint16_t* a_buf;
   float* gu_save;
   float* y32;                 // full layer: GEMM2 rows in fp32
-  uint16_t* out;              // expert share: weighted rows in arrival order
-  uint32_t* ticket;           // [8 XCDs, 64 words apart]; zeroed before the launch, as are the counters
+  uint16_t* out;
+  uint32_t* ticket;           // [8 queues, 64 words apart]; zeroed before the launch, as are the counters
   uint32_t* p_done;           // [cap] permute units done per item
   uint32_t* g1_done;          // [cap] GEMM1 tiles done per item
   uint32_t* err;
 };
 
 struct FusedUnit {
-  int kind, b, idx;
+  int kind, b, u;             // u: the unit's index in its segment
 };
 
 __device__ __forceinline__ int fused_items_lo(const FusedArgs& a, int b) { return min(a.mb_items[b], a.item_cap); }
 __device__ __forceinline__ int fused_items(const FusedArgs& a, int b) {
   return min(a.mb_items[b + 1], a.item_cap) - min(a.mb_items[b], a.item_cap);
 }
-// items of minibatch b on XCD x: local indices x, x + 8, ...
-__device__ __forceinline__ int fused_items_x(const FusedArgs& a, int b, int x) {
+// units of segment (kind, b), all queues
+__device__ __forceinline__ int fused_units(const FusedArgs& a, int kind, int b) {
   const int n = fused_items(a, b);
-  return n > x ? (n - x + FUSE_XCD - 1) / FUSE_XCD : 0;
-}
-__device__ __forceinline__ int fused_item(const FusedArgs& a, int b, int x, int m) {
-  return fused_items_lo(a, b) + x + FUSE_XCD * m;
-}
-__device__ __forceinline__ int fused_count(const FusedArgs& a, int kind, int b, int x) {
-  const int n = fused_items_x(a, b, x);
   return kind == U_P ? n * FUSE_PCH : kind == U_G1 ? n * (2 * a.I / BN) : n * (a.H / BN);
 }
 
-// Unit of ticket t of XCD x's queue (U_NONE past the last one).
+// Unit of ticket t of queue x (U_NONE past the last one).
 __device__ FusedUnit fused_decode(const FusedArgs& a, int x, int t) {
   for (int j = 0; j < a.nb + 2; ++j) {
 #pragma unroll 1
     for (int kind = 0; kind < 3; ++kind) {
       const int b = kind == U_G1 ? j - 1 : kind == U_P ? j : j - 2;
       if (b < 0 || b >= a.nb) continue;
-      const int n = fused_count(a, kind, b, x);
-      if (t < n) return FusedUnit{kind, b, t};
-      t -= n;
+      const int n = fused_units(a, kind, b);
+      const int nx = n > x ? (n - x + FUSE_XCD - 1) / FUSE_XCD : 0;
+      if (t < nx) return FusedUnit{kind, b, x + FUSE_XCD * t};
+      t -= nx;
     }
   }
   return FusedUnit{U_NONE, 0, 0};
@@ -583,14 +594,11 @@ __device__ __forceinline__ void fused_wait(const uint32_t* p, uint32_t target, u
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Tile idx of XCD x's GEMM tiles of minibatch b (ntn column tiles per item),
-// in groups of 4 items that share B columns.
-__device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int x, int idx, int ntn, int& item) {
-  int it, nt;
-  tile_coords(idx, fused_items_x(a, b, x), ntn, it, nt);
-  item = fused_item(a, b, x, it);
+// GEMM tile u of minibatch b (item-major, ntn column tiles per item).
+__device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int u, int ntn, int& item) {
+  item = fused_items_lo(a, b) + u / ntn;
   const int* q = a.items + 4 * item;
-  return TileInfo{q[0], q[1], q[2], nt * BN};
+  return TileInfo{q[0], q[1], q[2], (u % ntn) * BN};
 }
 
 // Control flow around the barriers is uniform: wave 0 as a whole takes the
@@ -603,56 +611,51 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
   __shared__ int su[3];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the XCD this workgroup runs on (HW_REG_XCC_ID, bits 3:0)
-  const int x = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (FUSE_XCD - 1);
+  const int x = blockIdx.x % FUSE_XCD;   // this workgroup's queue
   const int ntn1 = 2 * a.I / BN, ntn2 = a.H / BN;
   while (true) {
     if (wave == 0) {
       uint32_t t = 0;
       if (lane == 0) t = atomicAdd(a.ticket + 64 * x, 1u);
-      const FusedUnit u = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t));
-      if (u.kind == U_G1) {
-        int item;
-        (void)fused_tile(a, u.b, x, u.idx, ntn1, item);
-        fused_wait(a.p_done + item, (uint32_t)FUSE_PCH, a.err);
-      } else if (u.kind == U_G2) {
-        int item;
-        (void)fused_tile(a, u.b, x, u.idx, ntn2, item);
-        fused_wait(a.g1_done + item, (uint32_t)ntn1, a.err);
+      const FusedUnit un = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t));
+      if (un.kind == U_G1) {
+        fused_wait(a.p_done + fused_items_lo(a, un.b) + un.u / ntn1, (uint32_t)FUSE_PCH, a.err);
+      } else if (un.kind == U_G2) {
+        fused_wait(a.g1_done + fused_items_lo(a, un.b) + un.u / ntn2, (uint32_t)ntn1, a.err);
       }
       if (lane == 0) {
-        su[0] = u.kind;
-        su[1] = u.b;
-        su[2] = u.idx;
+        su[0] = un.kind;
+        su[1] = un.b;
+        su[2] = un.u;
       }
     }
     __syncthreads();
     const int kind = __builtin_amdgcn_readfirstlane(su[0]);
     const int b = __builtin_amdgcn_readfirstlane(su[1]);
-    const int idx = __builtin_amdgcn_readfirstlane(su[2]);
+    const int u = __builtin_amdgcn_readfirstlane(su[2]);
     if (kind == U_NONE) break;
     int item = -1;
     if (kind == U_P) {
-      // rows [64c, 64c + 64) of the XCD's item idx / 4, one wave per row
-      item = fused_item(a, b, x, idx / FUSE_PCH);
+      // rows [64c, 64c + 64) of item u / 4, one wave per row, written through
+      item = fused_items_lo(a, b) + u / FUSE_PCH;
       const int* q = a.items + 4 * item;
-      const int r0 = (idx % FUSE_PCH) * FUSE_CH, r1 = min(q[1], r0 + FUSE_CH);
+      const int r0 = (u % FUSE_PCH) * FUSE_CH, r1 = min(q[1], r0 + FUSE_CH);
+      const buf_rsrc_t rr = make_rsrc(a.ring);
       for (int r = r0 + wave; r < r1; r += NT / 64) {
         const int64_t p = q[0] + r;
         const int src = a.inv[p];
         if (src >= 0)
-          copy_row_wave((const u32x4_t*)(a.x + (int64_t)(src / a.src_div) * a.H),
-                        (u32x4_t*)(a.ring + (p % a.ring_rows) * a.H), a.H / 8, lane);
+          copy_row_wave_wt((const u32x4_t*)(a.x + (int64_t)(src / a.src_div) * a.H), rr,
+                           (uint32_t)((p % a.ring_rows) * a.H * 2), a.H / 8, lane);
       }
     } else if (kind == U_G1) {
-      const TileInfo ti = fused_tile(a, b, x, idx, ntn1, item);
-      gemm1_tile<BN>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
+      const TileInfo ti = fused_tile(a, b, u, ntn1, item);
+      gemm1_tile<BN, true>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
     } else {
-      const TileInfo ti = fused_tile(a, b, x, idx, ntn2, item);
+      const TileInfo ti = fused_tile(a, b, u, ntn2, item);
       gemm2_tile<SHARE>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
     }
-    // publish: every wave's stores complete (in the XCD's L2), then one
-    // counter bump
+    // publish: every wave's stores complete, then one counter bump
     wait_all_mem();
     __syncthreads();
     if (wave == 0 && lane == 0) {
@@ -709,10 +712,12 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   // the tickets and the counters start at zero (a fill kernel, not a memset,
   // so the sequence can be captured in a graph)
   launch_fill_u32(c, 0u, fused_ctl_words(f.ir.item_cap), s);
-  if (f.full)
-    hipLaunchKernelGGL(fused_forward_kernel<false>, dim3(n_cu), dim3(NT), 0, s, a);
+  // one workgroup per compute unit, a multiple of the 8 queues
+  const int grid = std::max(FUSE_XCD, n_cu / FUSE_XCD * FUSE_XCD);
+  if (!f.full)
+    hipLaunchKernelGGL(fused_forward_kernel<true>, dim3(grid), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL(fused_forward_kernel<true>, dim3(n_cu), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(fused_forward_kernel<false>, dim3(grid), dim3(NT), 0, s, a);
 }
 
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,

@@ -111,6 +111,25 @@ __device__ __forceinline__ void stage_flush(char* lds, RowDst row_dst) {
   __syncthreads();
 }
 
+// The same, with every 16-byte store written through to memory
+// (device-coherent: a buffer store with the device-scope bit), for results
+// that another XCD reads within the same launch.  row_off(r) gives the byte
+// offset of tile row r from base (< 4 GiB), or -1 to skip the row.
+template <int COLS, typename RowOff>
+__device__ __forceinline__ void stage_flush_wt(char* lds, const void* base, RowOff row_off) {
+  constexpr int CPR = COLS / 8;                 // 16-byte chunks per row
+  const buf_rsrc_t rs = make_rsrc(base);
+  __syncthreads();
+  for (int id = threadIdx.x; id < G_BM * CPR; id += G_NT) {
+    const int r = id / CPR, c = id - r * CPR;
+    const int64_t off = row_off(r);
+    if (off >= 0)
+      __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4_t*)(lds + r * STAGE_ROW_BYTES + c * 16), rs,
+                                             (uint32_t)off + c * 16, 0, MK_CPOL_DEVICE);
+  }
+  __syncthreads();
+}
+
 // ---- backward epilogues shared by the bf16 and MXFP8 kernels --------------
 
 // dA' tile -> SwiGLU backward, from the forward's fp32 g, u (gu, packed like

@@ -113,6 +113,10 @@ __device__ __forceinline__ void b2lds16(buf_rsrc_t r, uint32_t voff, char* wave_
 __device__ __forceinline__ void b2lds4(buf_rsrc_t r, uint32_t voff, char* wave_dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_dst, 4, voff, 0, 0, 0);
 }
+// Cache-policy operand of the buffer stores: the device-scope bit (sc1) --
+// the store is made coherent for every XCD (written through its L2).
+constexpr int MK_CPOL_DEVICE = 16;
+
 // A pointer that is the same in every lane of the wave, made visibly uniform
 // (so that a buffer resource built from it stays in scalar registers).
 __device__ __forceinline__ const void* wave_uniform(const void* p) {

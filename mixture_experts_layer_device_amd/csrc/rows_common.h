@@ -23,6 +23,22 @@ __device__ __forceinline__ void copy_row_wave(const u32x4_t* __restrict__ s, u32
   }
 }
 
+// copy_row_wave with the stores written through to memory (device-coherent)
+// through the buffer resource rd, d_off the row's byte offset in it.
+__device__ __forceinline__ void copy_row_wave_wt(const u32x4_t* __restrict__ s, buf_rsrc_t rd, uint32_t d_off,
+                                                 int64_t n16, int lane) {
+  for (int64_t g0 = lane; g0 < n16; g0 += 64 * 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (g0 + 64 * u < n16) v[u] = __builtin_nontemporal_load(s + g0 + 64 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (g0 + 64 * u < n16)
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, d_off + (uint32_t)(g0 + 64 * u) * 16, 0, MK_CPOL_DEVICE);
+  }
+}
+
 // out[o] = sum_{j < kk} w[o*kk + j] * y[sorted_pos[o*kk + j]], j ascending,
 // fp32, one rounding to bf16, for one output row o, by one wave.  A dropped
 // row (sorted_pos -1) adds nothing.  Lane j (< kk <= 64) fetches the j-th

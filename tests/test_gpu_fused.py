@@ -1,9 +1,9 @@
-"""The fused forward (mk_config.fused_forward: permute, GEMM1 + SwiGLU and
-GEMM2 of the bf16 forward in one persistent launch, minibatches overlapping
-through device counters) against the phase-by-phase launches, bit for bit,
-and against the oracle: several minibatches, one minibatch, the expert share
-and the full layer (whose combine follows as its own launch).  A ring that
-cannot hold every minibatch falls back to the phase-by-phase launches."""
+"""The fused forward (mk_config.fused_forward: permute, GEMM1 + SwiGLU, GEMM2
+and the full layer's combine in one persistent launch, minibatches
+overlapping through device counters) against the phase-by-phase launches,
+bit for bit, and against the oracle: several minibatches, one minibatch, the
+expert share and the full layer.  A ring that cannot hold every minibatch
+falls back to the phase-by-phase launches."""
 import numpy as np
 import pytest
 import torch
