@@ -83,10 +83,14 @@ __device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t
 // slot, for B the copy is 1 KiB contiguous.  NB = 128 (a half tile): btile
 // points at rows 128h .. 128h+127 of each block (h * 8192 elements in), each
 // wave copies its 2 KiB, and only fragments j < 2 of acc are computed.
+// rows: the tile's rows that hold data (1 .. 256).  With 128 or fewer, the
+// four waves of rows 128 .. 255 hold only padding: they copy their share of
+// B (which the other waves read) but no A rows, read no fragments, issue no
+// MFMAs (their acc stays zero) and only keep step at the barriers.
 template <int NB = BN, typename ARow>
-__device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const uint16_t* btile, int K, char* lds,
-                                            Acc& acc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const uint16_t* btile, int K, int rows,
+                                            char* lds, Acc& acc) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // A rows and the B blocks through buffer resources: A offsets from abase
   // (every row arow returns lies within 4 GiB after it), B from btile
   const buf_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(btile);
@@ -108,10 +112,27 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
     }
   };
   zero_acc(acc);
+  const int KT = K / BK;
+  if (wave >= 4 && rows <= 128) {
+    // a padding wave: its B copies and the barriers, one per stage as below
+    auto issue_b = [&](int64_t kb, char* st) {
+      const uint32_t b = bo + (uint32_t)(kb / (BK * 2)) * TILE_BYTES;
+#pragma unroll
+      for (int j = 0; j < NB / 64; ++j) b2lds16(rb, b + j * 1024, st + TILE_BYTES + bwbase + j * 1024);
+    };
+    issue_b(0, lds);
+    wait_all_mem();
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) issue_b((int64_t)(kt + 1) * BK * 2, lds + ((kt & 1) ^ 1) * STAGE_BYTES);
+      wait_all_mem();
+      __syncthreads();
+    }
+    return;
+  }
   issue(0, lds);
   wait_all_mem();
   __syncthreads();
-  const int KT = K / BK;
   // Fragments are read one group ahead of the MFMAs that use them (the
   // compiler, left alone, reuses one pair of registers and waits for every
   // read).  The stage's barrier sits before its last group, so the first
@@ -162,7 +183,8 @@ __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* _
     return ring + (int64_t)(p % ring_rows) * H;
   };
   Acc acc;
-  mainloop_nt<NB>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, lds, acc);
+  mainloop_nt<NB>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, ti.rows, lds,
+                  acc);
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -216,7 +238,7 @@ __device__ __forceinline__ void gemm2_tile(const TileInfo& ti, const uint16_t* _
                                            const float* __restrict__ row_w, char* lds) {
   auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
   Acc acc;
-  mainloop_nt(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, lds, acc);
+  mainloop_nt(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, ti.rows, lds, acc);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -268,7 +290,7 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dye + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * H; };
     Acc acc;
-    mainloop_nt(arow(0), arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, lds, acc);
+    mainloop_nt(arow(0), arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, ti.rows, lds, acc);
     dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
   });
 }
@@ -288,7 +310,7 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dgdu + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * 2 * I; };
     Acc acc;
-    mainloop_nt(arow(0), arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, lds, acc);
+    mainloop_nt(arow(0), arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, ti.rows, lds, acc);
     dx_epilogue<ROWS16>(ti, acc, lds, H, inv, dX, dx32);
   });
 }

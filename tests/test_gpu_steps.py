@@ -60,10 +60,17 @@ def weights(inp):
     return bf16.decode(inp["w_gate"]), bf16.decode(inp["w_up"]), bf16.decode(inp["w_down"])
 
 
-def run_share(inp, precision, MB, backward=False, wgrad_mxfp8=False):
+def share_mb(sh):
+    """The minibatch the benchmarks run the full-size expert shares with (the
+    two-wave floor of 256 x 256 tiles at H=7168, I=2048 on 256 compute
+    units), 256 rows for the small shapes (several minibatches there too)."""
+    return 8192 if sh.R > 8192 else 256
+
+
+def run_share(inp, precision, MB, backward=False, wgrad_mxfp8=False, fused=False):
     sh = inp["shape"]
     L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, precision=precision, minibatch_rows=MB,
-                 enable_backward=backward, wgrad_mxfp8=wgrad_mxfp8)
+                 enable_backward=backward, wgrad_mxfp8=wgrad_mxfp8, fused_forward=fused)
     x, row_w = dev(inp["x"]), dev(inp["row_w"])
     packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=backward)
     L.build_schedule(dev(inp["row_expert"]), sh.R)
@@ -78,13 +85,14 @@ def run_share(inp, precision, MB, backward=False, wgrad_mxfp8=False):
 
 
 # ------------------------------------------------------------ forward --
-@pytest.mark.parametrize("name", ["small", "ep64_fwd"])
-def test_forward_share_bf16_steps(name):
+@pytest.mark.parametrize("name,fused", [("small", False), ("small", True), ("ep64_fwd", False), ("ep64_fwd", True)])
+def test_forward_share_bf16_steps(name, fused):
     inp = share_inputs(name)
     sh = inp["shape"]
-    MB = 4096 if sh.R > 4096 else 256
-    say(f"[steps, forward bf16] {name} R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}: every element")
-    L, out, _, sp, npos = run_share(inp, "bf16", MB)
+    MB = share_mb(sh)
+    say(f"[steps, forward bf16{' fused' if fused else ''}] {name} R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}: "
+        f"every element")
+    L, out, _, sp, npos = run_share(inp, "bf16", MB, fused=fused)
     a_dev = by_row(L, "a", sh.I, torch.int16, sp, npos)
     L.close()
     wg, wu, wd = weights(inp)
@@ -101,7 +109,7 @@ def test_forward_share_bf16_steps(name):
 def test_forward_share_mxfp8_steps(name):
     inp = share_inputs(name)
     sh = inp["shape"]
-    MB = 4096 if sh.R > 4096 else 256
+    MB = share_mb(sh)
     say(f"[steps, forward MXFP8] {name} R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}: every element")
     L, out, _, sp, npos = run_share(inp, "mxfp8", MB)
     a_dev = by_row(L, "a", sh.I, torch.int16, sp, npos)
@@ -190,7 +198,7 @@ def _backward_steps(inp, L, g, sp, npos, mx, wgrad_mx_mb=None):
 def test_backward_share_bf16_steps(name):
     inp = share_inputs(name)
     sh = inp["shape"]
-    MB = 4096 if sh.R > 4096 else 256
+    MB = share_mb(sh)
     say(f"[steps, backward bf16] {name} R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}: every element")
     L, out, g, sp, npos = run_share(inp, "bf16", MB, backward=True)
     _backward_steps(inp, L, g, sp, npos, mx=False)
@@ -200,7 +208,7 @@ def test_backward_share_bf16_steps(name):
 def test_backward_share_mxfp8_steps(name, wmx):
     inp = share_inputs(name)
     sh = inp["shape"]
-    MB = 4096 if sh.R > 4096 else 256
+    MB = share_mb(sh)
     say(f"[steps, backward MXFP8{' + MXFP8 weight gradients' if wmx else ''}] {name} R={sh.R} H={sh.H} "
         f"I={sh.I} E={sh.E} MB={MB}: every element")
     L, out, g, sp, npos = run_share(inp, "mxfp8", MB, backward=True, wgrad_mxfp8=wmx)
@@ -219,7 +227,8 @@ def test_full_layer_steps():
     sh = inp["shape"]
     T, H, I, E, k, R = sh.T, sh.H, sh.I, sh.E, sh.k, sh.R
     say(f"[steps, full layer] T={T} H={H} I={I} E={E} k={k}: every element")
-    L = MoELayer(H=H, I=I, E=E, k=k, max_rows=R, renorm=sh.renorm, enable_backward=True)
+    # the forward as the benchmark's main line runs it: one fused launch
+    L = MoELayer(H=H, I=I, E=E, k=k, max_rows=R, renorm=sh.renorm, enable_backward=True, fused_forward=True)
     x_d, wr_d, bias_d = dev(inp["x"]), dev(inp["w_router"]), dev(inp["bias"])
     packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
     idx, w = L.route(x_d, wr_d, bias_d, T)
