@@ -73,8 +73,12 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
         w["gemm2"] = (2.0 * R * I * H, R * I * (ab + sc) + E * H * I * (ab + sc) + (R * H * 2 if share else R * H * 4))
         if not share:
             w["combine"] = (0.0, R * H * 4 + T * H * 2 + R * 8)
-        # the fused forward: permute, GEMM1, GEMM2 (and combine) in one launch
-        parts = [w[p] for p in ("permute", "gemm1", "gemm2", "combine") if p in w]
+            # the same k-sum if the y rows were bf16 (2 bytes an element):
+            # the floor of a design without the fp32 y round trip
+            w["combine_y_bf16"] = (0.0, R * H * 2 + T * H * 2 + R * 8)
+        # the fused forward: permute, GEMM1 and GEMM2 in one launch (the full
+        # layer's combine stays a launch of its own)
+        parts = [w[p] for p in ("permute", "gemm1", "gemm2")]
         w["fused_fwd"] = (sum(f for f, _ in parts), sum(b for _, b in parts))
     else:
         # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
@@ -252,6 +256,8 @@ def main():
                 ent["roofline"] = roofline_alu(f, b, ms)
             elif f or b:
                 ent["roofline"] = roofline(f, b, ms, mx=mx and p in mx_phases)
+            if p == "combine" and "combine_y_bf16" in work:
+                ent["roofline_y_bf16_bytes"] = roofline(0.0, work["combine_y_bf16"][1], ms)
             phases[p] = ent
             if f and p not in ("route", "bwd_combine", "router_bwd"):
                 gemm_flops += f
