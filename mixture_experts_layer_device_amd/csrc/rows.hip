@@ -69,7 +69,7 @@ __device__ __forceinline__ uint32_t quant_block(const u32x4_t (&v)[4], u32x4_t (
 // wave reading 1 KiB contiguous), so an MX block of 32 is held by the 4 lanes
 // 4q .. 4q+3: its amax is their maximum (two lane exchanges), every lane
 // converts its own 8 values and stores 8 codes, and the first of the 4 stores
-// the scale.  Four chunks are in flight per lane.  H is a multiple of 32, so
+// the scale.  Eight chunks are in flight per lane.  H is a multiple of 32, so
 // a block is never split across the row's end.
 // (copy != nullptr: the bf16 row is also stored there, at row p)
 __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t H,
@@ -90,16 +90,16 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
     const uint16_t* s = src + sr * H;
     uint8_t* dc = codes + dr * H;
     uint8_t* ds = scales + dr * (H / 32);
-    for (int64_t c0 = 0; c0 < H; c0 += 4 * 512) {
-      u32x4_t v[4];
-      uint32_t am[4];
+    for (int64_t c0 = 0; c0 < H; c0 += 8 * 512) {
+      u32x4_t v[8];
+      uint32_t am[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int64_t e = c0 + u * 512 + lane * 8;
         v[u] = e < H ? __builtin_nontemporal_load((const u32x4_t*)(s + e)) : u32x4_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         uint32_t a = 0;
 #pragma unroll
         for (int d = 0; d < 4; ++d) a = max(a, max(v[u][d] & 0x7FFFu, (v[u][d] >> 16) & 0x7FFFu));
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(RT) void gather_rows_mxfp8_kernel(const uint16_t* _
         am[u] = max(a, (uint32_t)__shfl_xor((int)a, 2));
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int64_t e = c0 + u * 512 + lane * 8;
         if (e >= H) continue;
         const int sc = mx_scale_code(am[u]);
@@ -431,8 +431,11 @@ __global__ __launch_bounds__(256) void wgrad_kmap_kernel(const int32_t* __restri
 // Workgroup (256-column tile ct, global k step kc): the 128 rows of the step
 // x 256 columns come to LDS (16 loads of 16 bytes per thread, all issued
 // before the first LDS store), then thread r quantises column r's four
-// 32-row blocks (quant_block) and writes the tiled block's row r whole: its
-// 128 code bytes and its scale dword.
+// 32-row blocks (quant_block) into row r of the tiled block's image, built
+// in LDS over the staged rows, and the 32 KiB image goes out with 16-byte
+// stores that are contiguous across the workgroup (a thread's own row would
+// be 8 stores 128 bytes apart from its neighbours': a partial line each).
+// The scale dwords go out directly (consecutive threads, consecutive dwords).
 __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
     const uint16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ inv, int src_div, int C,
     const int32_t* __restrict__ kofs, int E, const int32_t* __restrict__ kmap, uint8_t* __restrict__ codes,
@@ -475,8 +478,8 @@ __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
   __syncthreads();
   const int64_t blk = (int64_t)(C / MXT_ROWS) * (ke / MXT_K) + (int64_t)ct * (kpad / MXT_K) + (k0 - ke) / MXT_K;
   const int r = tid;
-  uint8_t* crow = codes + blk * MXT_CODES + r * MXT_K;
   uint32_t sc = 0;
+  u32x4_t cc[MXT_K / 16];                       // row r of the block: granule g = k 16g .. 16g+15
 #pragma unroll
   for (int kb = 0; kb < MXT_K / 32; ++kb) {
     u32x4_t w[4];
@@ -487,13 +490,24 @@ __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
         const int k = kb * 32 + g * 8 + 2 * d;
         w[g][d] = (uint32_t)t[k][r] | ((uint32_t)t[k + 1][r] << 16);
       }
-    u32x4_t cc[2];
-    sc |= quant_block(w, cc) << (8 * kb);
-    const int g0 = kb * 2;
-    *(u32x4_t*)(crow + (((g0 ^ tkey(r)) & 7) << 4)) = cc[0];
-    *(u32x4_t*)(crow + ((((g0 + 1) ^ tkey(r)) & 7) << 4)) = cc[1];
+    u32x4_t c2[2];
+    sc |= quant_block(w, c2) << (8 * kb);
+    cc[2 * kb] = c2[0];
+    cc[2 * kb + 1] = c2[1];
   }
   *(uint32_t*)(scales + blk * MXT_SCALES + r * 4) = sc;
+  static_assert(MXT_CODES <= MXT_K * LD * 2, "the block image fits over the staged rows");
+  char* img = (char*)&t[0][0];
+  __syncthreads();                              // every column read
+#pragma unroll
+  for (int g = 0; g < MXT_K / 16; ++g) *(u32x4_t*)(img + r * MXT_K + (((g ^ tkey(r)) & 7) << 4)) = cc[g];
+  __syncthreads();
+  uint8_t* cblk = codes + blk * MXT_CODES;
+#pragma unroll
+  for (int i = 0; i < MXT_CODES / (16 * 256); ++i) {
+    const int off = (tid + 256 * i) * 16;
+    *(u32x4_t*)(cblk + off) = *(const u32x4_t*)(img + off);
+  }
 }
 
 }  // namespace
