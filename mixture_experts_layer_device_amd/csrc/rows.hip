@@ -428,23 +428,26 @@ __global__ __launch_bounds__(256) void wgrad_kmap_kernel(const int32_t* __restri
   for (int j = tid; st + j < end; j += 256) kmap[st + j] = j < n ? base + j : -1;
 }
 
-// Workgroup (256-column tile ct, global k step kc): the 128 rows of the step
-// x 256 columns come to LDS (16 loads of 16 bytes per thread, all issued
-// before the first LDS store), then thread r quantises column r's four
-// 32-row blocks (quant_block) into row r of the tiled block's image, built
-// in LDS over the staged rows, and the 32 KiB image goes out with 16-byte
-// stores that are contiguous across the workgroup (a thread's own row would
-// be 8 stores 128 bytes apart from its neighbours': a partial line each).
-// The scale dwords go out directly (consecutive threads, consecutive dwords).
-__global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
+// Workgroup (half ct of a 256-column block, global k step kc): the 128 rows
+// of the step x 128 columns come to LDS (8 loads of 16 bytes per thread,
+// all issued before the first LDS store); thread (r, h) then quantises MX
+// blocks 2h and 2h+1 of column r (quant_block) into its half of row r of the
+// tiled block's image, built in LDS over the staged rows, and the 16 KiB
+// image goes out with 16-byte stores that are contiguous across the
+// workgroup (a thread's own 64 bytes would be 16-byte pieces 128 bytes apart
+// from its neighbours': a partial line each).  35 KiB of LDS and at most 128
+// registers: four workgroups per compute unit, so one's loads overlap
+// another's quantising.
+__global__ __launch_bounds__(256, 4) void quant_wgrad_operand_kernel(
     const uint16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ inv, int src_div, int C,
     const int32_t* __restrict__ kofs, int E, const int32_t* __restrict__ kmap, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
-  constexpr int LD = MXT_ROWS + 8;
-  constexpr int PER = MXT_K * (MXT_ROWS / 8) / 256;    // 16-byte loads per thread
+  constexpr int CW = MXT_ROWS / 2;                     // columns per workgroup
+  constexpr int LD = CW + 8;
+  constexpr int PER = MXT_K * (CW / 8) / 256;          // 16-byte loads per thread
   __shared__ __attribute__((aligned(16))) uint16_t t[MXT_K][LD];
   __shared__ int64_t srow[MXT_K];
-  const int ct = blockIdx.x, kc = blockIdx.y, tid = threadIdx.x;
+  const int ct = blockIdx.x >> 1, half = blockIdx.x & 1, kc = blockIdx.y, tid = threadIdx.x;
   const int k0 = kc * MXT_K;
   if (k0 >= kofs[E]) return;                    // the whole workgroup leaves together
   // expert of this step: the last e with kofs[e] <= k0 (kofs is ascending)
@@ -460,12 +463,12 @@ __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
     srow[tid] = p < 0 ? -1 : inv ? (int64_t)(inv[p] / src_div) : (int64_t)p;
   }
   __syncthreads();
-  const int c0 = ct * MXT_ROWS;
+  const int c0 = ct * MXT_ROWS + half * CW;
   u32x4_t v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int q = tid + i * 256;
-    const int kk = q >> 5, c = (q & 31) * 8;
+    const int kk = q / (CW / 8), c = (q % (CW / 8)) * 8;
     const int64_t row = srow[kk];
     v[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (row >= 0) v[i] = *(const u32x4_t*)(src + row * ld + c0 + c);
@@ -473,15 +476,17 @@ __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int q = tid + i * 256;
-    *(u32x4_t*)&t[q >> 5][(q & 31) * 8] = v[i];
+    *(u32x4_t*)&t[q / (CW / 8)][(q % (CW / 8)) * 8] = v[i];
   }
   __syncthreads();
   const int64_t blk = (int64_t)(C / MXT_ROWS) * (ke / MXT_K) + (int64_t)ct * (kpad / MXT_K) + (k0 - ke) / MXT_K;
-  const int r = tid;
+  const int r = tid & (CW - 1), kh = tid / CW;        // column within the half; MX blocks 2kh, 2kh+1
+  const int br = half * CW + r;                        // its row in the tiled block
   uint32_t sc = 0;
-  u32x4_t cc[MXT_K / 16];                       // row r of the block: granule g = k 16g .. 16g+15
+  u32x4_t cc[4];                                       // granules 4kh .. 4kh+3 of the block row
 #pragma unroll
-  for (int kb = 0; kb < MXT_K / 32; ++kb) {
+  for (int b2 = 0; b2 < 2; ++b2) {
+    const int kb = 2 * kh + b2;
     u32x4_t w[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -491,20 +496,22 @@ __global__ __launch_bounds__(256) void quant_wgrad_operand_kernel(
         w[g][d] = (uint32_t)t[k][r] | ((uint32_t)t[k + 1][r] << 16);
       }
     u32x4_t c2[2];
-    sc |= quant_block(w, c2) << (8 * kb);
-    cc[2 * kb] = c2[0];
-    cc[2 * kb + 1] = c2[1];
+    sc |= quant_block(w, c2) << (8 * b2);
+    cc[2 * b2] = c2[0];
+    cc[2 * b2 + 1] = c2[1];
   }
-  *(uint32_t*)(scales + blk * MXT_SCALES + r * 4) = sc;
-  static_assert(MXT_CODES <= MXT_K * LD * 2, "the block image fits over the staged rows");
+  // the row's scale bytes 2kh, 2kh+1 (MX blocks of this thread)
+  *(uint16_t*)(scales + blk * MXT_SCALES + br * 4 + 2 * kh) = (uint16_t)sc;
+  static_assert(CW * MXT_K <= MXT_K * LD * 2, "the half image fits over the staged rows");
   char* img = (char*)&t[0][0];
   __syncthreads();                              // every column read
 #pragma unroll
-  for (int g = 0; g < MXT_K / 16; ++g) *(u32x4_t*)(img + r * MXT_K + (((g ^ tkey(r)) & 7) << 4)) = cc[g];
+  for (int g = 0; g < 4; ++g)
+    *(u32x4_t*)(img + r * MXT_K + ((((4 * kh + g) ^ tkey(br)) & 7) << 4)) = cc[g];
   __syncthreads();
-  uint8_t* cblk = codes + blk * MXT_CODES;
+  uint8_t* cblk = codes + blk * MXT_CODES + half * CW * MXT_K;
 #pragma unroll
-  for (int i = 0; i < MXT_CODES / (16 * 256); ++i) {
+  for (int i = 0; i < CW * MXT_K / (16 * 256); ++i) {
     const int off = (tid + 256 * i) * 16;
     *(u32x4_t*)(cblk + off) = *(const u32x4_t*)(img + off);
   }
@@ -525,7 +532,7 @@ void launch_wgrad_kmap(const int32_t* kofs, const int32_t* mb_counts, const int3
 void launch_quant_wgrad_operand(const uint16_t* src, int64_t ld, const int32_t* inv, int src_div, int C,
                                 const int32_t* kofs, int E, const int32_t* kmap, int64_t kcap, uint8_t* codes,
                                 uint8_t* scales, hipStream_t s) {
-  hipLaunchKernelGGL(quant_wgrad_operand_kernel, dim3(C / MXT_ROWS, (unsigned)(kcap / MXT_K)), dim3(256), 0, s, src,
+  hipLaunchKernelGGL(quant_wgrad_operand_kernel, dim3(2 * (C / MXT_ROWS), (unsigned)(kcap / MXT_K)), dim3(256), 0, s, src,
                      ld, inv, src_div, C, kofs, E, kmap, codes, scales);
 }
 
