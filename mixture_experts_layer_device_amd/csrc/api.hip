@@ -749,6 +749,12 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
     f.I = I;
     f.ring_rows = ws->ring_rows;
     f.full = !share;
+    // placement of the units on the XCDs: with fewer than 2 tiles of rows
+    // per expert in a minibatch on average, a weight panel serves about one
+    // item, so keep each item's units on one XCD (its ring and a rows stay
+    // in that L2); with more, spread every segment's units evenly so that a
+    // panel stays on one XCD across the expert's items
+    f.item_local = (int64_t)std::min(MB, R) < (int64_t)2 * MK_TILE_M * ws->E;
     f.x = x;
     f.inv = st.inv;
     f.row_w = row_w;

@@ -515,10 +515,14 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
 // runs as one minibatch, follows as its own launch.
 //
 // Units: per item (256 rows of one expert in one minibatch) 4 permute
-// chunks of 64 rows, 2I/256 GEMM1 tiles and H/256 GEMM2 tiles.  Unit u of a
-// segment (item-major: u = item * tiles + tile) goes to queue u mod 8: every
-// queue gets an equal share (to one unit), and a weight column panel stays
-// in one queue, or two, across the items of an expert.  Queue x is taken by
+// chunks of 64 rows, 2I/256 GEMM1 tiles and H/256 GEMM2 tiles.  Placement,
+// chosen by the host: unit u of a segment (item-major: u = item * tiles +
+// tile) goes to queue u mod 8, so every queue gets an equal share (to one
+// unit) and a weight column panel stays in one queue, or two, across the
+// items of an expert; or (item_local, for experts with about one item per
+// minibatch, whose panels serve one item anyway) item l with all of its
+// units goes to queue l mod 8, so its ring rows and a rows are read from the
+// L2 that wrote them.  Queue x is taken by
 // the workgroups whose index is x mod 8 -- the workgroups the hardware
 // places on XCD x, since a dispatch deals its workgroups to the 8 XCDs in
 // turn -- so a panel is read into one XCD's L2.  (Only speed rests on that
@@ -548,6 +552,7 @@ struct FusedArgs {
   const int32_t* items;       // [cap, 4] (row_begin, rows, expert, minibatch)
   const int32_t* mb_items;    // [nb + 1]
   int item_cap, nb, src_div, H, I, ring_rows;
+  int item_local;             // placement: whole items per queue (else unit u to queue u mod 8)
   const uint16_t* x;          // token rows (full layer) or routed rows (expert share)
   const int32_t* inv;
   const float* row_w;
@@ -585,10 +590,19 @@ __device__ FusedUnit fused_decode(const FusedArgs& a, int x, int t) {
     for (int kind = 0; kind < 3; ++kind) {
       const int b = kind == U_G1 ? j - 1 : kind == U_P ? j : j - 2;
       if (b < 0 || b >= a.nb) continue;
-      const int n = fused_units(a, kind, b);
-      const int nx = n > x ? (n - x + FUSE_XCD - 1) / FUSE_XCD : 0;
-      if (t < nx) return FusedUnit{kind, b, x + FUSE_XCD * t};
-      t -= nx;
+      if (a.item_local) {
+        // whole items: item l of the minibatch (all of its units) to queue l mod 8
+        const int per = kind == U_P ? FUSE_PCH : kind == U_G1 ? 2 * a.I / BN : a.H / BN;
+        const int ni = fused_items(a, b);
+        const int nx = ni > x ? (ni - x + FUSE_XCD - 1) / FUSE_XCD * per : 0;
+        if (t < nx) return FusedUnit{kind, b, (x + FUSE_XCD * (t / per)) * per + t % per};
+        t -= nx;
+      } else {
+        const int n = fused_units(a, kind, b);
+        const int nx = n > x ? (n - x + FUSE_XCD - 1) / FUSE_XCD : 0;
+        if (t < nx) return FusedUnit{kind, b, x + FUSE_XCD * t};
+        t -= nx;
+      }
     }
   }
   return FusedUnit{U_NONE, 0, 0};
@@ -716,6 +730,7 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   a.H = f.H;
   a.I = f.I;
   a.ring_rows = f.ring_rows;
+  a.item_local = f.item_local;
   a.x = f.x;
   a.inv = f.inv;
   a.row_w = f.row_w;

@@ -186,6 +186,7 @@ void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_r
 struct FusedFwd {
   ItemRange ir;               // all minibatches
   int nb, src_div, H, I, ring_rows, full;
+  int item_local;             // whole items per XCD (else units dealt evenly)
   const uint16_t* x;
   const int32_t* inv;
   const float* row_w;
