@@ -195,7 +195,7 @@ int backward_impl(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const v
   }
   {
     Phase ph(ws, MK_PH_BWD_DW, s);
-    launch_dw_finalize(ws->dw_part, I / 64, st.sorted_pos, R, d_row_w, full ? nullptr : (uint16_t*)dX, H, s);
+    launch_dw_finalize(ws->dw_part, I / 32, st.sorted_pos, R, d_row_w, full ? nullptr : (uint16_t*)dX, H, s);
   }
   // dX GEMM: expert share stores rows back to arrival order (share of the
   // reverse dispatch); the full layer keeps fp32 rows for the k-sum
@@ -411,7 +411,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
     o_dye = c.take((size_t)npos * H * 2);
     o_dgdu = c.take((size_t)npos * 2 * I * 2);
     o_wa = c.take((size_t)npos * I * 2);
-    o_dwp = c.take((size_t)npos * (I / 64) * 4);
+    o_dwp = c.take((size_t)npos * (I / 32) * 4);
     o_dz = c.take((size_t)((max_rows + k - 1) / k) * E * 4);
     if (cfg->precision == MK_MXFP8) {
       o_dyc = c.take((size_t)npos * H);

@@ -287,11 +287,18 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
                                                       float* __restrict__ dw_part) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = I / BN;
-  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+  // a last round at most half full runs as 256 x 128 half tiles
+  for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
     auto arow = [&](int r) { return dye + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * H; };
+    const uint16_t* bt = wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H) + (ti.n0 % BN) * BK;
     Acc acc;
-    mainloop_nt(arow(0), arow, wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H), H, ti.rows, lds, acc);
-    dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
+    if (half < 0) {
+      mainloop_nt<BN>(arow(0), arow, bt, H, ti.rows, lds, acc);
+      dact_epilogue<BN>(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
+    } else {
+      mainloop_nt<BN / 2>(arow(0), arow, bt, H, ti.rows, lds, acc);
+      dact_epilogue<BN / 2>(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
+    }
   });
 }
 

@@ -133,39 +133,44 @@ __device__ __forceinline__ void stage_flush_wt(char* lds, const void* base, RowO
 // ---- backward epilogues shared by the bf16 and MXFP8 kernels --------------
 
 // dA' tile -> SwiGLU backward, from the forward's fp32 g, u (gu, packed like
-// W_gu): a = silu(g) u; dw partial = sum of dA' a over this wave's 64
-// columns (one slice of I/64, added up later in slice order); dA = w dA';
+// W_gu): a = silu(g) u; dw partial = sum of dA' a over 32 columns (slice
+// n / 32 of I / 32, a wave's fragments 2s and 2s+1, added up later in slice
+// order, so the partials do not depend on how tiles are cut); dA = w dA';
 // dg = dA u s (1 + g (1 - s)), du = dA silu(g) (bf16, row p of dgdu holding
 // the I gate features then the I up features, so the MX blocks of the dX
 // GEMM's contraction are 32 consecutive dg or du values); and w*a (bf16, the
 // down-projection weight gradient's operand).
-// g and u of the tile (256 rows x 512 packed columns, 2 KiB per row) are
-// brought through LDS in four chunks of 64 rows with coalesced 16-byte loads
-// (the chunk's rows are the fragments 2c and 2c+1 of both row halves); the
-// row stride of 516 floats puts the 4 row groups a fragment read touches on
-// different banks.  LDS must be free on entry (it is after the mainloop) and
-// is free on exit.
+// NB: the tile's columns (256, or 128 for a half tile: a wave's NB / 4
+// columns are its fragments j < NB / 64).
+// g and u of the tile (256 rows x 2 NB packed columns, 8 NB bytes per row)
+// are brought through LDS in four chunks of 64 rows with coalesced 16-byte
+// loads (the chunk's rows are the fragments 2c and 2c+1 of both row halves);
+// the row stride of 516 floats puts the 4 row groups a fragment read touches
+// on different banks.  LDS must be free on entry (it is after the mainloop)
+// and is free on exit.
+template <int NB = G_BN>
 __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, char* lds, int I,
                                               const float* __restrict__ gu, const int32_t* __restrict__ inv,
                                               const float* __restrict__ row_w, uint16_t* __restrict__ dgdu,
                                               uint16_t* __restrict__ wa, float* __restrict__ dw_part) {
-  constexpr int FM = G_FM, FN = G_FN;
+  constexpr int FM = G_FM, FN = NB / 64;        // fragments per wave (columns NB / 4)
+  constexpr int HALVES = NB / 128;              // 1 KiB copies per g/u row
   constexpr int GS = 516;                       // LDS row stride (floats)
   float* sg = (float*)lds;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  const int slices = I / 64, slice = (ti.n0 + wn * 64) / 64;
-  const float* gtile = gu + (int64_t)2 * ti.n0;          // the tile's 512 packed columns
+  const int slices = I / 32, slice0 = (ti.n0 + wn * (NB / 4)) / 32;
+  const float* gtile = gu + (int64_t)2 * ti.n0;          // the tile's 2 NB packed columns
 #pragma unroll
   for (int c = 0; c < FM / 2; ++c) {
-    // 64 rows x 512 floats through the LDS DMA, each row as two 1 KiB halves,
-    // 16 per wave, all in flight together; rows past the item's end are
-    // skipped (their LDS is never read).  The copies write no registers, so
-    // the loop issues them back to back without unrolling.
+    // 64 rows x 2 NB floats through the LDS DMA, each row as HALVES 1 KiB
+    // copies, 16 HALVES / 2 per wave, all in flight together; rows past the
+    // item's end are skipped (their LDS is never read).  The copies write no
+    // registers, so the loop issues them back to back without unrolling.
 #pragma unroll 1
-    for (int k = 0; k < 16; ++k) {
-      const int idx = wave * 16 + k;
-      const int lr = idx >> 1, half = idx & 1;
+    for (int k = 0; k < 8 * HALVES; ++k) {
+      const int idx = wave * 8 * HALVES + k;
+      const int lr = idx / HALVES, half = idx % HALVES;
       const int r = (lr >> 5) * 128 + c * 32 + (lr & 31);
       if (r < ti.rows)
         g2lds16(gtile + (int64_t)(ti.pos0 + r) * 2 * I + half * 256 + lane * 4, lds + (lr * GS + half * 256) * 4);
@@ -182,35 +187,39 @@ __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, cha
         const bool valid = r < ti.rows;
         const int64_t p = ti.pos0 + (valid ? r : 0);
         const float w = valid ? row_w[inv[p]] : 0.f;
-        float dws = 0.f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int f = wn * 64 + j * 16 + (lane & 15);        // feature within the tile
-          const int lc = 32 * (f >> 4) + (f & 15);               // its gate column; up at +16
-          float g = 0.f, u = 0.f;
-          if (valid) {
-            g = sg[lr * GS + lc];
-            u = sg[lr * GS + lc + 16];
+        for (int sl = 0; sl < FN / 2; ++sl) {
+          float dws = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * sl + jj;
+            const int f = wn * (NB / 4) + j * 16 + (lane & 15);   // feature within the tile
+            const int lc = 32 * (f >> 4) + (f & 15);                // its gate column; up at +16
+            float g = 0.f, u = 0.f;
+            if (valid) {
+              g = sg[lr * GS + lc];
+              u = sg[lr * GS + lc + 16];
+            }
+            const float s = sigmoidf_(g);
+            const float sla = g * s;
+            const float aa = sla * u;
+            const float dap = acc[i][j][v];
+            dws += dap * aa;
+            const float da = w * dap;
+            if (valid) {
+              uint16_t* dst = dgdu + p * 2 * I + ti.n0 + f;
+              dst[0] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
+              dst[I] = (uint16_t)f32_to_bf16(da * sla);
+              wa[p * I + ti.n0 + f] = (uint16_t)f32_to_bf16(w * aa);
+            }
           }
-          const float s = sigmoidf_(g);
-          const float sl = g * s;
-          const float aa = sl * u;
-          const float dap = acc[i][j][v];
-          dws += dap * aa;
-          const float da = w * dap;
-          if (valid) {
-            uint16_t* dst = dgdu + p * 2 * I + ti.n0 + f;
-            dst[0] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
-            dst[I] = (uint16_t)f32_to_bf16(da * sl);
-            wa[p * I + ti.n0 + f] = (uint16_t)f32_to_bf16(w * aa);
-          }
+          // fixed butterfly over the 16 lanes that share this row
+          dws += __shfl_xor(dws, 1);
+          dws += __shfl_xor(dws, 2);
+          dws += __shfl_xor(dws, 4);
+          dws += __shfl_xor(dws, 8);
+          if (valid && (lane & 15) == 0) dw_part[p * slices + slice0 + sl] = dws;
         }
-        // fixed butterfly over the 16 lanes that share this row
-        dws += __shfl_xor(dws, 1);
-        dws += __shfl_xor(dws, 2);
-        dws += __shfl_xor(dws, 4);
-        dws += __shfl_xor(dws, 8);
-        if (valid && (lane & 15) == 0) dw_part[p * slices + slice] = dws;
       }
     }
     __syncthreads();                            // the next chunk reuses the LDS

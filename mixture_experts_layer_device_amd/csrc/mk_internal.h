@@ -65,7 +65,7 @@ struct mk_workspace {
   uint8_t *a_codes, *a_scales;// MXFP8 copy of a
   float* y_buf;               // [npos, H] fp32 expert outputs, expert order (full-layer combine)
   uint16_t *dye, *dgdu, *wa;  // backward: [npos, H], [npos, 2I], [npos, I]
-  float* dw_part;             // [npos, I/64]
+  float* dw_part;             // [npos, I/32]: router-weight gradient partials, 32 features each
   uint16_t* zero_row;         // 512 zero bytes (weight-gradient rows past a segment's end)
   uint32_t* fused_ctl;        // fused forward: ticket and dependency counters
   uint8_t *dye_c, *dye_s;     // MXFP8 backward: dY rows quantised along H  [npos, H], [npos, H/32]

@@ -149,15 +149,25 @@ __global__ void zero_dropped_rows_kernel(const int32_t* __restrict__ sorted_pos,
 }
 
 // d_row_w[r] = sum over slices (ascending) of dw_part[sorted_pos[r]]; a dropped
-// row gets 0 and (expert share, dX given) a zero dX row.
+// row gets 0 and (expert share, dX given) a zero dX row.  slices is a
+// multiple of 8: the partials come in 16-byte loads, 8 in flight, and are
+// added one by one in slice order.
 __global__ void dw_finalize_kernel(const float* __restrict__ dw_part, int slices,
                                    const int32_t* __restrict__ sorted_pos, int64_t R, float* __restrict__ d_row_w,
                                    uint16_t* __restrict__ dX, int64_t H) {
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < R; r += (int64_t)gridDim.x * blockDim.x) {
     const int pos = sorted_pos[r];
     if (pos >= 0) {
+      const f32x4_t* q = (const f32x4_t*)(dw_part + (int64_t)pos * slices);
       float s = 0.f;
-      for (int i = 0; i < slices; ++i) s += dw_part[(int64_t)pos * slices + i];
+      for (int i0 = 0; i0 < slices / 4; i0 += 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + u < slices / 4 ? q[i0 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u < slices / 4) s = (((s + v[u][0]) + v[u][1]) + v[u][2]) + v[u][3];
+      }
       d_row_w[r] = s;
     } else {
       d_row_w[r] = 0.f;
