@@ -18,6 +18,8 @@
 // Fragment layouts (measured on gfx950): A/B lane l holds row/col l%16 and
 // k = 8*(l/16) .. +7; the 16x16 fp32 result in lane l is column l%16, rows
 // 4*(l/16) .. +3.
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "rows_common.h"
 
@@ -29,6 +31,12 @@ constexpr int FM = G_FM, FN = G_FN;
 constexpr int TILE_BYTES = BM * BK * 2;        // 32 KiB per operand tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int LDS_BYTES = 2 * STAGE_BYTES > STAGE_LDS_BYTES ? 2 * STAGE_BYTES : STAGE_LDS_BYTES;
+// the K loop with B in three buffers: A in two, B in three (all 160 KiB of the LDS)
+constexpr int NT_A_BUFS = 2, NT_B_BUFS = 3;
+constexpr int NT3_LDS_BYTES = (NT_A_BUFS + NT_B_BUFS) * TILE_BYTES;
+static_assert(NT3_LDS_BYTES >= STAGE_LDS_BYTES && NT3_LDS_BYTES <= 160 * 1024, "the LDS of one compute unit");
+// long contractions take the three-buffer K loop
+constexpr int NT3_MIN_K = 4096;
 
 typedef GAcc Acc;
 
@@ -57,14 +65,29 @@ __device__ __forceinline__ void read_a_pair(const char* st, int q, bf16x8_t (&a)
 }
 // NB: rows of the B tile (256, or 128 for a half tile): a wave's NB / 4
 // columns are NB / 64 fragments.
+// (bt: the B tile's buffer)
 template <int NB = BN>
-__device__ __forceinline__ void read_b_half(const char* st, int ks, bf16x8_t (&b)[NB / 64]) {
+__device__ __forceinline__ void read_b_half(const char* bt, int ks, bf16x8_t (&b)[NB / 64]) {
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
   const int g = ks * 4 + (lane >> 4);
 #pragma unroll
   for (int j = 0; j < NB / 64; ++j)
-    b[j] = *(const bf16x8_t*)(st + TILE_BYTES + SwzT::off(wn * (NB / 4) + j * 16 + (lane & 15), g));
+    b[j] = *(const bf16x8_t*)(bt + SwzT::off(wn * (NB / 4) + j * 16 + (lane & 15), g));
 }
+
+// s_waitcnt: vmcnt(n) and lgkmcnt(0) (expcnt not waited for), n < 16.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4));
+}
+// The workgroup barrier with no memory fence of its own: the caller has
+// already waited for exactly what must be complete (its share of one
+// stage's LDS-DMA copies, and its LDS reads), where __syncthreads() would
+// add a fence that waits for every LDS write in flight -- the later
+// stage's copies included.  The clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 template <int NB = BN>
 __device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t (&b)[NB / 64], int pair, Acc& acc) {
 #pragma unroll
@@ -83,12 +106,131 @@ __device__ __forceinline__ void mma_group(const bf16x8_t (&a)[2], const bf16x8_t
 // slot, for B the copy is 1 KiB contiguous.  NB = 128 (a half tile): btile
 // points at rows 128h .. 128h+127 of each block (h * 8192 elements in), each
 // wave copies its 2 KiB, and only fragments j < 2 of acc are computed.
+// mainloop_nt3 (B3 below) keeps A in two buffers (stage kt in A buffer
+// kt mod 2) and B in three (kt mod 3),
+// so while stage kt is multiplied, A of kt+1 and B of kt+1 and kt+2 are in
+// flight: the B tiles (the weights, streamed from memory with little reuse)
+// get two stages of latency to arrive instead of one.  The waits count this
+// wave's copies (vmcnt: A of kt+1 was issued before B of kt+2), and the
+// barriers carry no fence of their own (barrier_no_fence).
 // rows: the tile's rows that hold data (1 .. 256).  With 128 or fewer, the
 // four waves of rows 128 .. 255 hold only padding: they copy their share of
 // B (which the other waves read) but no A rows, read no fragments, issue no
 // MFMAs (their acc stays zero) and only keep step at the barriers.
-template <int NB = BN, typename ARow>
-__device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const uint16_t* btile, int K, int rows,
+template <int NB, typename ARow>
+__device__ __forceinline__ void mainloop_nt3(const void* abase, ARow arow, const uint16_t* btile, int K, int rows,
+                                            char* lds, Acc& acc) {
+  constexpr int LB = NB / 64;                            // B copies per wave and stage
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // A rows and the B blocks through buffer resources: A offsets from abase
+  // (every row arow returns lies within 4 GiB after it), B from btile
+  const buf_rsrc_t ra = make_rsrc(wave_uniform(abase)), rb = make_rsrc(wave_uniform(btile));
+  char* const abuf = lds;
+  char* const bbuf = lds + NT_A_BUFS * TILE_BYTES;
+  const int wbase = wave * 4096;
+  const int bwbase = wave * NB * 16;                   // this wave's share of the B tile (NB rows x 128 B)
+  const uint32_t bo = bwbase + lane * 16;
+  auto a_of = [&](int kt) { return abuf + (kt & 1) * TILE_BYTES; };
+  auto b_of = [&](int kt) { return bbuf + (kt % NT_B_BUFS) * TILE_BYTES; };
+  auto issue_b = [&](int kt) {
+    const uint32_t b = bo + (uint32_t)kt * TILE_BYTES;
+    char* bt = b_of(kt);
+#pragma unroll
+    for (int j = 0; j < LB; ++j) b2lds16(rb, b + j * 1024, bt + bwbase + j * 1024);
+  };
+  zero_acc(acc);
+  const int KT = K / BK;
+  if (wave >= 4 && rows <= 128) {
+    // a padding wave: its B copies and the barriers, one per stage as below
+    issue_b(0);
+    if (KT > 1) issue_b(1);
+    if (KT > 1)
+      wait_vm_lgkm0<LB>();
+    else
+      wait_vm_lgkm0<0>();
+    barrier_no_fence();
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 2 < KT) {
+        issue_b(kt + 2);
+        wait_vm_lgkm0<LB>();
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      barrier_no_fence();
+    }
+    return;
+  }
+  uint32_t ao[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 32 + j * 8 + (lane >> 3);
+    ao[j] = (uint32_t)((const char*)arow(r) - (const char*)abase) + (((lane & 7) ^ tkey(r)) & 7) * 16;
+  }
+  auto issue_a = [&](int kt) {
+    const uint32_t ka = (uint32_t)kt * (BK * 2);
+    char* at = a_of(kt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b2lds16(ra, ao[j] + ka, at + wbase + j * 1024);
+  };
+  // stage 0's A and B, and B of stage 1; wait for stage 0
+  issue_a(0);
+  issue_b(0);
+  if (KT > 1) issue_b(1);
+  if (KT > 1)
+    wait_vm_lgkm0<LB>();
+  else
+    wait_vm_lgkm0<0>();
+  barrier_no_fence();
+  // Fragments are read one group ahead of the MFMAs that use them (the
+  // compiler, left alone, reuses one pair of registers and waits for every
+  // read).  The stage's barrier sits before its last group, so the first
+  // reads of the next stage are in flight while that group's MFMAs issue.
+  // Scheduling barriers keep each group's reads ahead of the MFMAs before it.
+  bf16x8_t bq[2][NB / 64], aq[2][2];
+  read_b_half<NB>(b_of(0), 0, bq[0]);
+  read_a_pair(a_of(0), 0, aq[0]);
+  // Stage kt.  IB (the loop body: stage kt+2 exists): B of kt+2 is issued
+  // now and the wait at the end leaves its LB copies in flight, a constant
+  // wait that keeps the loop free of branches around it (so the compiler
+  // adds no waits of its own).  The last two stages (no B left to issue)
+  // wait for everything; whether stage kt+1 exists is then tested at run time.
+  auto stage = [&](int kt, auto ib_c) {
+    constexpr bool IB = decltype(ib_c)::value;
+    const bool ia = IB || kt + 1 < KT;
+    const char* at = a_of(kt);
+    const char* bt = b_of(kt);
+    if (ia) issue_a(kt + 1);
+    if constexpr (IB) issue_b(kt + 2);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q < 7) {
+        if (q == 3) read_b_half<NB>(bt, 1, bq[1]);
+        read_a_pair(at, q + 1, aq[(q + 1) & 1]);
+      } else {
+        if constexpr (IB)
+          wait_vm_lgkm0<LB>();
+        else
+          wait_vm_lgkm0<0>();
+        barrier_no_fence();
+        if (ia) {
+          read_b_half<NB>(b_of(kt + 1), 0, bq[0]);
+          read_a_pair(a_of(kt + 1), 0, aq[0]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma_group<NB>(aq[q & 1], bq[q >> 2], q & 3, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) stage(kt, std::true_type{});
+  for (; kt < KT; ++kt) stage(kt, std::false_type{});
+}
+
+// The K loop with both operands double-buffered (one 64 KiB stage in
+// flight while the other is multiplied); the LDS it needs is LDS_BYTES.
+template <int NB, typename ARow>
+__device__ __forceinline__ void mainloop_nt2(const void* abase, ARow arow, const uint16_t* btile, int K, int rows,
                                             char* lds, Acc& acc) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // A rows and the B blocks through buffer resources: A offsets from abase
@@ -139,7 +281,7 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
   // reads of the next stage are in flight while that group's MFMAs issue.
   // Scheduling barriers keep each group's reads ahead of the MFMAs before it.
   bf16x8_t bq[2][NB / 64], aq[2][2];
-  read_b_half<NB>(lds, 0, bq[0]);
+  read_b_half<NB>(lds + TILE_BYTES, 0, bq[0]);
   read_a_pair(lds, 0, aq[0]);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
@@ -149,13 +291,13 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (q < 7) {
-        if (q == 3) read_b_half<NB>(st, 1, bq[1]);
+        if (q == 3) read_b_half<NB>(st + TILE_BYTES, 1, bq[1]);
         read_a_pair(st, q + 1, aq[(q + 1) & 1]);
       } else {
         wait_all_mem();
         __syncthreads();
         if (kt + 1 < KT) {
-          read_b_half<NB>(nst, 0, bq[0]);
+          read_b_half<NB>(nst + TILE_BYTES, 0, bq[0]);
           read_a_pair(nst, 0, aq[0]);
         }
       }
@@ -166,6 +308,19 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
   }
 }
 
+
+// B3: the K loop with B in three buffers (NT3_LDS_BYTES of LDS), for long K
+// (the weights stream through it for many stages); else both operands
+// double-buffered (LDS_BYTES), which measured faster for short K.
+template <int NB = BN, bool B3 = false, typename ARow>
+__device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const uint16_t* btile, int K, int rows,
+                                            char* lds, Acc& acc) {
+  if constexpr (B3)
+    mainloop_nt3<NB>(abase, arow, btile, K, rows, lds, acc);
+  else
+    mainloop_nt2<NB>(abase, arow, btile, K, rows, lds, acc);
+}
+
 // ---------------------------------------------------------------- GEMM1 ----
 // a[p, i] = silu(g) * u with [g | u] = ring[p] . W_gu[e]^T; W_gu is packed so
 // that each 32-column group holds 16 gate columns then the 16 up columns of
@@ -174,7 +329,7 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
 // columns of the tile: NB / 2 features, a wave's NB / 4 columns being
 // NB / 128 gate/up groups of 32.  WT: the a rows are written through to
 // memory (read by another XCD in the same launch).
-template <int NB, bool WT = false>
+template <int NB, bool WT = false, bool B3 = false>
 __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* __restrict__ ring, int ring_rows,
                                            const uint16_t* __restrict__ wgu, int H, int I,
                                            uint16_t* __restrict__ a_out, float* __restrict__ gu_save, char* lds) {
@@ -183,8 +338,8 @@ __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* _
     return ring + (int64_t)(p % ring_rows) * H;
   };
   Acc acc;
-  mainloop_nt<NB>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, ti.rows, lds,
-                  acc);
+  mainloop_nt<NB, B3>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, ti.rows,
+                      lds, acc);
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -212,17 +367,18 @@ __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* _
     });
 }
 
+template <bool B3>
 __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ ring,
                                                         int ring_rows, const uint16_t* __restrict__ wgu, int H,
                                                         int I, uint16_t* __restrict__ a_out,
                                                         float* __restrict__ gu_save) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES];
   const int ntn = 2 * I / BN;
   for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
     if (half < 0)
-      gemm1_tile<BN>(ti, ring, ring_rows, wgu, H, I, a_out, gu_save, lds);
+      gemm1_tile<BN, false, B3>(ti, ring, ring_rows, wgu, H, I, a_out, gu_save, lds);
     else
-      gemm1_tile<BN / 2>(ti, ring, ring_rows, wgu, H, I, a_out, gu_save, lds);
+      gemm1_tile<BN / 2, false, B3>(ti, ring, ring_rows, wgu, H, I, a_out, gu_save, lds);
   });
 }
 
@@ -278,6 +434,7 @@ __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint
 // this wave's 64 columns; dA = w dA'; dg = dA u s (1 + g (1 - s)); du = dA
 // silu(g) (bf16 GEMM operands, row p = I gate then I up features); w*a (bf16 operand of the
 // down-projection weight gradient).
+template <bool B3>
 __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16_t* __restrict__ dye,
                                                       const uint16_t* __restrict__ wdT, int H, int I,
                                                       const float* __restrict__ gu,
@@ -285,7 +442,7 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
                                                       const float* __restrict__ row_w,
                                                       uint16_t* __restrict__ dgdu, uint16_t* __restrict__ wa,
                                                       float* __restrict__ dw_part) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES];
   const int ntn = I / BN;
   // a last round at most half full runs as 256 x 128 half tiles
   for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
@@ -293,10 +450,10 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
     const uint16_t* bt = wdT + btile_block(ti.e, ti.n0 / BN, 0, I, H) + (ti.n0 % BN) * BK;
     Acc acc;
     if (half < 0) {
-      mainloop_nt<BN>(arow(0), arow, bt, H, ti.rows, lds, acc);
+      mainloop_nt<BN, B3>(arow(0), arow, bt, H, ti.rows, lds, acc);
       dact_epilogue<BN>(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
     } else {
-      mainloop_nt<BN / 2>(arow(0), arow, bt, H, ti.rows, lds, acc);
+      mainloop_nt<BN / 2, B3>(arow(0), arow, bt, H, ti.rows, lds, acc);
       dact_epilogue<BN / 2>(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
     }
   });
@@ -307,17 +464,17 @@ __global__ __launch_bounds__(NT) void bwd_dact_kernel(ItemRange ir, const uint16
 // the I gate features, then the I up features, as in dgdu).
 // ROWS16: rows stored as bf16 straight back to arrival order, dX[inv[p]];
 // else : kept in fp32 at position p ([p, H]) for the full layer's k-sum.
-template <bool ROWS16>
+template <bool ROWS16, bool B3>
 __global__ __launch_bounds__(NT) void bwd_dx_kernel(ItemRange ir, const uint16_t* __restrict__ dgdu,
                                                     const uint16_t* __restrict__ wguT, int H, int I,
                                                     const int32_t* __restrict__ inv, uint16_t* __restrict__ dX,
                                                     float* __restrict__ dx32) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES];
   const int ntn = H / BN;
   for_each_tile(ir, ntn, [&](const TileInfo& ti) {
     auto arow = [&](int r) { return dgdu + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * 2 * I; };
     Acc acc;
-    mainloop_nt(arow(0), arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, ti.rows, lds, acc);
+    mainloop_nt<BN, B3>(arow(0), arow, wguT + btile_block(ti.e, ti.n0 / BN, 0, H, 2 * I), 2 * I, ti.rows, lds, acc);
     dx_epilogue<ROWS16>(ti, acc, lds, H, inv, dX, dx32);
   });
 }
@@ -714,8 +871,12 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
 
 void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_rows, const uint16_t* wgu,
                        int H, int I, uint16_t* a_out, float* gu_save, int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL(gemm1_bf16_kernel, dim3(n_cu), dim3(NT), 0, s, ir, ring, ring_rows, wgu, H, I, a_out,
-                     gu_save);
+  if (H >= NT3_MIN_K)
+    hipLaunchKernelGGL(gemm1_bf16_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, ring, ring_rows, wgu, H, I, a_out,
+                       gu_save);
+  else
+    hipLaunchKernelGGL(gemm1_bf16_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, ring, ring_rows, wgu, H, I, a_out,
+                       gu_save);
 }
 
 void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* wd, int H, int I, float* y32,
@@ -767,16 +928,26 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,
                      const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part, int n_cu,
                      hipStream_t s) {
-  hipLaunchKernelGGL(bwd_dact_kernel, dim3(n_cu), dim3(NT), 0, s, ir, dye, wdT, H, I, gu, inv, row_w, dgdu, wa,
-                     dw_part);
+  if (H >= NT3_MIN_K)
+    hipLaunchKernelGGL(bwd_dact_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, dye, wdT, H, I, gu, inv, row_w, dgdu,
+                       wa, dw_part);
+  else
+    hipLaunchKernelGGL(bwd_dact_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, dye, wdT, H, I, gu, inv, row_w, dgdu,
+                       wa, dw_part);
 }
 
 void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wguT, int H, int I,
                    const int32_t* inv, uint16_t* dX, float* dx32, int n_cu, hipStream_t s) {
-  if (dX)
-    hipLaunchKernelGGL(bwd_dx_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
+  const bool b3 = 2 * I >= NT3_MIN_K;
+  if (dX && b3)
+    hipLaunchKernelGGL((bwd_dx_kernel<true, true>), dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
+  else if (dX)
+    hipLaunchKernelGGL((bwd_dx_kernel<true, false>), dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
+  else if (b3)
+    hipLaunchKernelGGL((bwd_dx_kernel<false, true>), dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
   else
-    hipLaunchKernelGGL(bwd_dx_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
+    hipLaunchKernelGGL((bwd_dx_kernel<false, false>), dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX,
+                       dx32);
 }
 
 void launch_wgrad_down(const WgradArgs& w, const uint16_t* dye, const uint16_t* wa, int H, int I,
