@@ -805,10 +805,14 @@ __device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int u,
 // ticket (lane 0's atomic, broadcast), decodes it and waits, every wave
 // reads the unit back from LDS as a scalar, and only the counter bumps are
 // single-lane; no lane of a wave ever takes a different path to a barrier.
-template <bool SHARE>
+// B3: GEMM1 units (contraction H) take the three-buffer K loop; the LDS is
+// then all in use by the K loop, and the unit is passed in its first bytes
+// (free between units: every unit ends at a barrier after its last LDS
+// access, and a second barrier below comes before the next unit's copies).
+template <bool SHARE, bool B3>
 __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  __shared__ int su[3];
+  __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES + 16];
+  int* const su = (int*)(lds + (B3 ? 0 : LDS_BYTES));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = blockIdx.x % FUSE_XCD;   // this workgroup's queue
@@ -833,6 +837,7 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
     const int kind = __builtin_amdgcn_readfirstlane(su[0]);
     const int b = __builtin_amdgcn_readfirstlane(su[1]);
     const int u = __builtin_amdgcn_readfirstlane(su[2]);
+    if constexpr (B3) __syncthreads();   // every wave has the unit: the LDS is the unit's
     if (kind == U_NONE) break;
     int item = -1;
     if (kind == U_P) {
@@ -850,7 +855,7 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
       }
     } else if (kind == U_G1) {
       const TileInfo ti = fused_tile(a, b, u, ntn1, item);
-      gemm1_tile<BN, true>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
+      gemm1_tile<BN, true, B3>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
     } else {
       const TileInfo ti = fused_tile(a, b, u, ntn2, item);
       gemm2_tile<SHARE>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
@@ -919,10 +924,15 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   launch_fill_u32(c, 0u, fused_ctl_words(f.ir.item_cap), s);
   // one workgroup per compute unit, a multiple of the 8 queues
   const int grid = std::max(FUSE_XCD, n_cu / FUSE_XCD * FUSE_XCD);
-  if (!f.full)
-    hipLaunchKernelGGL(fused_forward_kernel<true>, dim3(grid), dim3(NT), 0, s, a);
+  const bool b3 = f.H >= NT3_MIN_K;
+  if (!f.full && b3)
+    hipLaunchKernelGGL((fused_forward_kernel<true, true>), dim3(grid), dim3(NT), 0, s, a);
+  else if (!f.full)
+    hipLaunchKernelGGL((fused_forward_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a);
+  else if (b3)
+    hipLaunchKernelGGL((fused_forward_kernel<false, true>), dim3(grid), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL(fused_forward_kernel<false>, dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fused_forward_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a);
 }
 
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,
