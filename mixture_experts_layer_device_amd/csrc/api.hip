@@ -279,9 +279,12 @@ int backward_impl(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const v
                                dW_gate, dW_up, ws->n_cu, s);
     return check_launch();
   }
+  // few rows per expert (a few K stages per tile): the weight-gradient K
+  // loop with B in three buffers; thousands: both double-buffered
+  const bool wgrad_b3 = (int64_t)R < (int64_t)1024 * E;
   {
     Phase ph(ws, MK_PH_WGRAD_DOWN, s);
-    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->zero_row, ws->n_cu, s);
+    launch_wgrad_down(wa, ws->dye, ws->wa, H, I, dW_down, ws->zero_row, wgrad_b3, ws->n_cu, s);
   }
   // replay (the reverse walk's share of re-pulling evicted rows): the x rows
   // of the minibatches no longer in the ring (an MXFP8 ring holds codes: all
@@ -296,7 +299,7 @@ int backward_impl(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const v
   }
   Phase ph(ws, MK_PH_WGRAD_GU, s);
   launch_wgrad_gate_up(wa, ws->dgdu, (const uint16_t*)ws->ring, ws->ring_rows, replay_mbs, ws->dye, H, I, dW_gate,
-                       dW_up, ws->zero_row, ws->n_cu, s);
+                       dW_up, ws->zero_row, wgrad_b3, ws->n_cu, s);
   return check_launch();
 }
 

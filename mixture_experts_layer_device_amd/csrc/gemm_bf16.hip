@@ -586,12 +586,51 @@ __device__ __forceinline__ void mma_stage_kmajor(const char* sA, const char* sB,
   }
 }
 
-// LDS-DMA of one stage: wave w fills tile rows 8w .. 8w+7 of each operand, two
-// rows (1 KiB) per instruction; lane i takes row 8w + 2j + i/32 and the
-// 16 bytes of logical chunk (slot ^ trkey(row)) that belong in its slot.
-template <int MODE>
+// LDS-DMA of one stage's A (WHICH 0) or B (1) tile: wave w fills tile rows
+// 8w .. 8w+7, two rows (1 KiB) per instruction; lane i takes row 8w + 2j +
+// i/32 and the 16 bytes of logical chunk (slot ^ trkey(row)) that belong in
+// its slot.
+template <int MODE, int WHICH>
 __device__ __forceinline__ void wgrad_issue(const WgradOperands<MODE>& op, const SegIter& it, int m0, int n0,
-                                            char* st) {
+                                            char* tile) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = 8 * wave + 2 * j + (lane >> 5);
+    const int off = ((((s >> 1) ^ trkey(k)) & 15) << 5) + ((s & 1) << 4);
+    const bool live = it.k0 + k < it.len;
+    const int64_t p = it.start + it.k0 + k;
+    const char* src;
+    if (!live) {
+      src = (const char*)op.zero + off;
+    } else if (WHICH == 0) {
+      src = (const char*)(op.A + p * op.lda + m0) + off;
+    } else if (MODE == 0) {
+      src = (const char*)(op.B + p * op.ldb + n0) + off;
+    } else if (it.b >= op.first_resident) {
+      src = (const char*)(op.ring + (int64_t)(p % op.ring_rows) * op.ldx + n0) + off;
+    } else {
+      src = (const char*)(op.replay + p * op.ldx + n0) + off;
+    }
+    g2lds16(src, tile + (8 * wave + 2 * j) * 512);
+  }
+}
+
+// B3: the K loop keeps A in two LDS buffers and B in three (all 160 KiB):
+// while stage kt is multiplied, A of kt+1 and B of kt+1 and kt+2 are in
+// flight.  Each wave waits for its own copies (vmcnt: B of kt+1 was issued
+// before A of kt+1, which was issued before B of kt+2), and the barriers
+// carry no fence of their own (the transposing reads are not tracked by the
+// compiler and are waited for inside mma_stage_kmajor).  It pays when the
+// experts have few rows (a few stages per tile) and measured slower with
+// thousands of rows per expert, which keep both operands double-buffered.
+// Both tiles of one stage (A at st, B at st + TILE_BYTES), each row's A and
+// B copies issued together (the order the double-buffered loop measured
+// fastest in).
+template <int MODE>
+__device__ __forceinline__ void wgrad_issue_ab(const WgradOperands<MODE>& op, const SegIter& it, int m0, int n0,
+                                               char* st) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = lane & 31;
 #pragma unroll
@@ -617,10 +656,12 @@ __device__ __forceinline__ void wgrad_issue(const WgradOperands<MODE>& op, const
   }
 }
 
-template <int MODE>
+template <int MODE, bool B3>
 __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MODE> op, int M, int N, int I,
                                                       float* __restrict__ out0, float* __restrict__ out1) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES];
+  char* const abuf = lds;
+  char* const bbuf = lds + NT_A_BUFS * TILE_BYTES;
   const int tm = M / BM, tn = N / BN;
   const int per_e = tm * tn;
   const int total = w.E * per_e;
@@ -633,21 +674,50 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
     zero_acc(acc);
     SegIter cur{w.nb, 0, 0, 0};
     bool have = seg_next(cur, w, e);
-    if (have) {
-      wgrad_issue<MODE>(op, cur, m0, n0, lds);
+    if (have && !B3) {
+      auto issue = [&](const SegIter& it, char* st) { wgrad_issue_ab<MODE>(op, it, m0, n0, st); };
+      issue(cur, lds);
       wait_all_mem();
       __syncthreads();
       int stage = 0;
       while (true) {
         SegIter nxt = cur;
         const bool more = seg_next(nxt, w, e);
-        if (more) wgrad_issue<MODE>(op, nxt, m0, n0, lds + (stage ^ 1) * STAGE_BYTES);
+        if (more) issue(nxt, lds + (stage ^ 1) * STAGE_BYTES);
         mma_stage_kmajor(lds + stage * STAGE_BYTES, lds + stage * STAGE_BYTES + TILE_BYTES, acc);
         wait_all_mem();
         __syncthreads();
         if (!more) break;
         cur = nxt;
         stage ^= 1;
+      }
+    } else if (have) {
+      // stage 0's A and B, and B of stage 1; wait for stage 0
+      SegIter nxt = cur;
+      bool have1 = seg_next(nxt, w, e);
+      wgrad_issue<MODE, 0>(op, cur, m0, n0, abuf);
+      wgrad_issue<MODE, 1>(op, cur, m0, n0, bbuf);
+      if (have1) {
+        wgrad_issue<MODE, 1>(op, nxt, m0, n0, bbuf + TILE_BYTES);
+        wait_vm_lgkm0<4>();
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      barrier_no_fence();
+      for (int kt = 0;; ++kt) {
+        SegIter nxt2 = nxt;
+        const bool have2 = have1 && seg_next(nxt2, w, e);
+        if (have1) wgrad_issue<MODE, 0>(op, nxt, m0, n0, abuf + ((kt + 1) & 1) * TILE_BYTES);
+        if (have2) wgrad_issue<MODE, 1>(op, nxt2, m0, n0, bbuf + ((kt + 2) % NT_B_BUFS) * TILE_BYTES);
+        mma_stage_kmajor(abuf + (kt & 1) * TILE_BYTES, bbuf + (kt % NT_B_BUFS) * TILE_BYTES, acc);
+        if (have2)
+          wait_vm_lgkm0<4>();
+        else
+          wait_vm_lgkm0<0>();
+        barrier_no_fence();
+        if (!have1) break;
+        nxt = nxt2;
+        have1 = have2;
       }
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -961,16 +1031,23 @@ void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wg
 }
 
 void launch_wgrad_down(const WgradArgs& w, const uint16_t* dye, const uint16_t* wa, int H, int I,
-                       float* dW_down, const uint16_t* zero_row, int n_cu, hipStream_t s) {
+                       float* dW_down, const uint16_t* zero_row, bool b3, int n_cu, hipStream_t s) {
   WgradOperands<0> op{dye, H, wa, I, nullptr, 1, 0, nullptr, 0, zero_row};
-  hipLaunchKernelGGL(wgrad_kernel<0>, dim3(n_cu), dim3(NT), 0, s, w, op, H, I, I, dW_down, (float*)nullptr);
+  if (b3)
+    hipLaunchKernelGGL((wgrad_kernel<0, true>), dim3(n_cu), dim3(NT), 0, s, w, op, H, I, I, dW_down, (float*)nullptr);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<0, false>), dim3(n_cu), dim3(NT), 0, s, w, op, H, I, I, dW_down,
+                       (float*)nullptr);
 }
 
 void launch_wgrad_gate_up(const WgradArgs& w, const uint16_t* dgdu, const uint16_t* ring, int32_t ring_rows,
                           int first_resident, const uint16_t* replay, int H, int I, float* dW_gate, float* dW_up,
-                          const uint16_t* zero_row, int n_cu, hipStream_t s) {
+                          const uint16_t* zero_row, bool b3, int n_cu, hipStream_t s) {
   WgradOperands<1> op{dgdu, 2 * (int64_t)I, nullptr, 0, ring, ring_rows, first_resident, replay, H, zero_row};
-  hipLaunchKernelGGL(wgrad_kernel<1>, dim3(n_cu), dim3(NT), 0, s, w, op, 2 * I, H, I, dW_gate, dW_up);
+  if (b3)
+    hipLaunchKernelGGL((wgrad_kernel<1, true>), dim3(n_cu), dim3(NT), 0, s, w, op, 2 * I, H, I, dW_gate, dW_up);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<1, false>), dim3(n_cu), dim3(NT), 0, s, w, op, 2 * I, H, I, dW_gate, dW_up);
 }
 
 }  // namespace mk

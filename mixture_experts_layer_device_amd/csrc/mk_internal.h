@@ -220,15 +220,16 @@ struct WgradArgs {
   int src_div;
 };
 // dW_down[e] (H x I) = sum_p dye[p]^T (x) wa[p]
-// (zero_row: 512 zero bytes in device memory, for rows past a segment's end)
+// (zero_row: 512 zero bytes in device memory, for rows past a segment's end;
+// b3: the K loop with the B operand in three LDS buffers, for experts with few rows)
 void launch_wgrad_down(const WgradArgs& wa_args, const uint16_t* dye, const uint16_t* wa, int H,
-                       int I, float* dW_down, const uint16_t* zero_row, int n_cu, hipStream_t s);
+                       int I, float* dW_down, const uint16_t* zero_row, bool b3, int n_cu, hipStream_t s);
 // dW_gate/dW_up[e] (I x H) from dgdu ([p, 2I]: I gate, then I up) and the x rows: minibatches
 // b >= first_resident come from the ring, earlier (evicted) ones from replay,
 // the x rows re-gathered at their positions p ([p, H]).
 void launch_wgrad_gate_up(const WgradArgs& wa_args, const uint16_t* dgdu, const uint16_t* ring,
                           int32_t ring_rows, int first_resident, const uint16_t* replay, int H,
-                          int I, float* dW_gate, float* dW_up, const uint16_t* zero_row, int n_cu,
+                          int I, float* dW_gate, float* dW_up, const uint16_t* zero_row, bool b3, int n_cu,
                           hipStream_t s);
 
 // ---- gemm_mxfp8.hip -----------------------------------------------------
