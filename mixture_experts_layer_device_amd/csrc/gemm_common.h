@@ -130,6 +130,18 @@ __device__ __forceinline__ void stage_flush_wt(char* lds, const void* base, RowO
   __syncthreads();
 }
 
+// s_waitcnt: vmcnt(n) (n < 64) and lgkmcnt(0); expcnt not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0_t() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// The workgroup barrier with no memory fence of its own, for callers that
+// have already waited for exactly what must be complete (__syncthreads()
+// would add a fence that waits for every copy in flight).  The clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_no_fence_t() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---- backward epilogues shared by the bf16 and MXFP8 kernels --------------
 
 // dA' tile -> SwiGLU backward, from the forward's fp32 g, u (gu, packed like
@@ -143,11 +155,11 @@ __device__ __forceinline__ void stage_flush_wt(char* lds, const void* base, RowO
 // NB: the tile's columns (256, or 128 for a half tile: a wave's NB / 4
 // columns are its fragments j < NB / 64).
 // g and u of the tile (256 rows x 2 NB packed columns, 8 NB bytes per row)
-// are brought through LDS in four chunks of 64 rows with coalesced 16-byte
-// loads (the chunk's rows are the fragments 2c and 2c+1 of both row halves);
-// the row stride of 516 floats puts the 4 row groups a fragment read touches
-// on different banks.  LDS must be free on entry (it is after the mainloop)
-// and is free on exit.
+// come through LDS in 8 chunks of 32 rows -- chunk c holds the rows of
+// fragment c of both row halves -- with the LDS DMA, double-buffered: chunk
+// c+1's copies are in flight while chunk c is used.  The row stride of 516
+// floats puts the 4 row groups a fragment read touches on different banks.
+// LDS must be free on entry (it is after the mainloop) and is free on exit.
 template <int NB = G_BN>
 __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, char* lds, int I,
                                               const float* __restrict__ gu, const int32_t* __restrict__ inv,
@@ -156,73 +168,91 @@ __device__ __forceinline__ void dact_epilogue(const TileInfo& ti, GAcc& acc, cha
   constexpr int FM = G_FM, FN = NB / 64;        // fragments per wave (columns NB / 4)
   constexpr int HALVES = NB / 128;              // 1 KiB copies per g/u row
   constexpr int GS = 516;                       // LDS row stride (floats)
-  float* sg = (float*)lds;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int CROWS = 32;                     // rows per chunk
+  constexpr int CBYTES = CROWS * GS * 4;        // one chunk buffer
+  constexpr int PER = CROWS * HALVES / 8;       // copies per wave and chunk
+  static_assert(2 * CBYTES + 1024 <= 135168, "two chunk buffers and the row weights in the LDS");
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int slices = I / 32, slice0 = (ti.n0 + wn * (NB / 4)) / 32;
-  const float* gtile = gu + (int64_t)2 * ti.n0;          // the tile's 2 NB packed columns
+  // the tile's first row of packed g, u (2 NB columns from 2 n0); every row
+  // the tile reads lies within 256 rows of it, far inside a buffer offset
+  const buf_rsrc_t rg = make_rsrc(wave_uniform(gu + (int64_t)ti.pos0 * 2 * I + (int64_t)2 * ti.n0));
+  // chunk c into buffer c mod 2: LDS row lr = 16 wm' + t is tile row
+  // 128 wm' + 16 c + t.  Rows past the item's end copy its last row (never
+  // read), so every wave issues the same PER copies for every chunk and the
+  // waits below can count them.
+  auto issue = [&](int c) {
+    char* buf = lds + (c & 1) * CBYTES;
 #pragma unroll
-  for (int c = 0; c < FM / 2; ++c) {
-    // 64 rows x 2 NB floats through the LDS DMA, each row as HALVES 1 KiB
-    // copies, 16 HALVES / 2 per wave, all in flight together; rows past the
-    // item's end are skipped (their LDS is never read).  The copies write no
-    // registers, so the loop issues them back to back without unrolling.
-#pragma unroll 1
-    for (int k = 0; k < 8 * HALVES; ++k) {
-      const int idx = wave * 8 * HALVES + k;
+    for (int k = 0; k < PER; ++k) {
+      const int idx = wave * PER + k;
       const int lr = idx / HALVES, half = idx % HALVES;
-      const int r = (lr >> 5) * 128 + c * 32 + (lr & 31);
-      if (r < ti.rows)
-        g2lds16(gtile + (int64_t)(ti.pos0 + r) * 2 * I + half * 256 + lane * 4, lds + (lr * GS + half * 256) * 4);
+      const int r = min((lr >> 4) * 128 + c * 16 + (lr & 15), ti.rows - 1);
+      b2lds16(rg, (uint32_t)(((int64_t)r * 2 * I + half * 256 + lane * 4) * 4), buf + (lr * GS + half * 256) * 4);
     }
-    wait_all_mem();
-    __syncthreads();
+  };
+  // the tile's row weights w = row_w[inv[p]] into LDS first: read from
+  // there, the chunk loop waits on no global load (a wait for one would
+  // also wait for the next chunk's copies, issued before it)
+  float* const wl = (float*)(lds + 2 * CBYTES);
+  if (threadIdx.x < 256) wl[threadIdx.x] = (int)threadIdx.x < ti.rows ? row_w[inv[ti.pos0 + threadIdx.x]] : 0.f;
+  issue(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = 2 * c + h;
+  for (int c = 0; c < FM; ++c) {
+    if (c + 1 < FM) {
+      issue(c + 1);
+      wait_vm_lgkm0_t<PER>();                   // chunk c landed (c+1 still in flight)
+    } else {
+      wait_vm_lgkm0_t<0>();
+    }
+    barrier_no_fence_t();
+    const float* sg = (const float*)(lds + (c & 1) * CBYTES);
+    const int i = c;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = frag_row(i, v);
-        const int lr = wm * 32 + h * 16 + 4 * (lane >> 4) + v;
-        const bool valid = r < ti.rows;
-        const int64_t p = ti.pos0 + (valid ? r : 0);
-        const float w = valid ? row_w[inv[p]] : 0.f;
+    for (int v = 0; v < 4; ++v) {
+      const int r = frag_row(i, v);
+      const int lr = wm * 16 + 4 * (lane >> 4) + v;
+      const bool valid = r < ti.rows;
+      const int64_t p = ti.pos0 + (valid ? r : 0);
+      const float w = wl[r];
 #pragma unroll
-        for (int sl = 0; sl < FN / 2; ++sl) {
-          float dws = 0.f;
+      for (int sl = 0; sl < FN / 2; ++sl) {
+        float dws = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * sl + jj;
-            const int f = wn * (NB / 4) + j * 16 + (lane & 15);   // feature within the tile
-            const int lc = 32 * (f >> 4) + (f & 15);                // its gate column; up at +16
-            float g = 0.f, u = 0.f;
-            if (valid) {
-              g = sg[lr * GS + lc];
-              u = sg[lr * GS + lc + 16];
-            }
-            const float s = sigmoidf_(g);
-            const float sla = g * s;
-            const float aa = sla * u;
-            const float dap = acc[i][j][v];
-            dws += dap * aa;
-            const float da = w * dap;
-            if (valid) {
-              uint16_t* dst = dgdu + p * 2 * I + ti.n0 + f;
-              dst[0] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
-              dst[I] = (uint16_t)f32_to_bf16(da * sla);
-              wa[p * I + ti.n0 + f] = (uint16_t)f32_to_bf16(w * aa);
-            }
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * sl + jj;
+          const int f = wn * (NB / 4) + j * 16 + (lane & 15);   // feature within the tile
+          const int lc = 32 * (f >> 4) + (f & 15);                // its gate column; up at +16
+          float g = 0.f, u = 0.f;
+          if (valid) {
+            g = sg[lr * GS + lc];
+            u = sg[lr * GS + lc + 16];
           }
-          // fixed butterfly over the 16 lanes that share this row
-          dws += __shfl_xor(dws, 1);
-          dws += __shfl_xor(dws, 2);
-          dws += __shfl_xor(dws, 4);
-          dws += __shfl_xor(dws, 8);
-          if (valid && (lane & 15) == 0) dw_part[p * slices + slice0 + sl] = dws;
+          const float s = sigmoidf_(g);
+          const float sla = g * s;
+          const float aa = sla * u;
+          const float dap = acc[i][j][v];
+          dws += dap * aa;
+          const float da = w * dap;
+          if (valid) {
+            uint16_t* dst = dgdu + p * 2 * I + ti.n0 + f;
+            dst[0] = (uint16_t)f32_to_bf16(da * u * s * (1.f + g * (1.f - s)));
+            dst[I] = (uint16_t)f32_to_bf16(da * sla);
+            wa[p * I + ti.n0 + f] = (uint16_t)f32_to_bf16(w * aa);
+          }
         }
+        // fixed butterfly over the 16 lanes that share this row
+        dws += __shfl_xor(dws, 1);
+        dws += __shfl_xor(dws, 2);
+        dws += __shfl_xor(dws, 4);
+        dws += __shfl_xor(dws, 8);
+        if (valid && (lane & 15) == 0) dw_part[p * slices + slice0 + sl] = dws;
       }
     }
-    __syncthreads();                            // the next chunk reuses the LDS
+    // every wave has read this buffer before chunk c+2 is copied into it
+    wait_vm_lgkm0_t<63>();                      // (LDS reads only: lgkmcnt(0))
+    barrier_no_fence_t();
   }
 }
 
