@@ -12,6 +12,8 @@
 // k in [32g, 32g+32).  So lane group g takes 16-byte granules g and g+4 of the
 // 128-byte K step (MX block g = granules 2g and 2g+1 land in hardware block g)
 // and passes scale byte g.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace mk {
@@ -38,10 +40,12 @@ __device__ __forceinline__ void read_a_mx(const char* st, int i, i32x8_t& f, int
   const int wm = threadIdx.x >> 8;
   read_frag_mx(st, (const uint32_t*)(st + 2 * TILE_BYTES), wm * 128 + i * 16 + (threadIdx.x & 15), f, s);
 }
+// (NB: rows of the B tile, 256 or 128 for a half tile: a wave's NB / 4 columns)
+template <int NB = BN>
 __device__ __forceinline__ void read_b_mx(const char* st, int j, i32x8_t& f, int& s) {
   const int wn = (threadIdx.x >> 6) & 3;
-  read_frag_mx(st + TILE_BYTES, (const uint32_t*)(st + 2 * TILE_BYTES) + BM, wn * 64 + j * 16 + (threadIdx.x & 15), f,
-               s);
+  read_frag_mx(st + TILE_BYTES, (const uint32_t*)(st + 2 * TILE_BYTES) + BM,
+               wn * (NB / 4) + j * 16 + (threadIdx.x & 15), f, s);
 }
 
 // C = A . B^T over K codes.  arow / ascale give A's code row and scale row
@@ -55,10 +59,15 @@ __device__ __forceinline__ void read_b_mx(const char* st, int j, i32x8_t& f, int
 // fragments one ahead of the 4 MFMAs that use them.
 // ATILED: A comes in the tiled layout as well (abase / asbase: its tile's
 // first code and scale blocks; arow, ascale unused) and is fetched like B.
-template <bool ATILED, typename ARow, typename ASc>
+// NB = 128 (a half tile): bcodes / bscales point at rows 128h .. 128h+127 of
+// each block (h * 16 KiB of codes and h * 512 bytes of scales in), each wave
+// copies its 2 KiB of B codes, waves 4-5 the B scales, and only fragments
+// j < 2 of acc are computed.
+template <bool ATILED, int NB = BN, typename ARow, typename ASc>
 __device__ __forceinline__ void mainloop_t(const void* abase, ARow arow, const void* asbase, ASc ascale,
                                            const uint8_t* bcodes, const uint8_t* bscales, int K, char* lds,
                                            Acc& acc) {
+  constexpr int NFB = NB / 64;                  // B fragments per wave (and B copies per wave and stage)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const buf_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bcodes);
   const buf_rsrc_t rs = make_rsrc(wave_uniform(wave < 4 ? asbase : (const void*)bscales));
@@ -82,18 +91,21 @@ __device__ __forceinline__ void mainloop_t(const void* abase, ARow arow, const v
     sstep = wave < 4 ? 4 : MXT_SCALES;
   }
   const int sbase = 2 * TILE_BYTES + wave * 256;
+  const int bwbase = wave * NB * 16;            // this wave's share of the B tile (NB rows x 128 B)
+  const uint32_t bbo = NB == BN ? bo : bwbase + lane * 16;
   auto issue = [&](int kt, char* st) {
     const uint32_t kb = (uint32_t)kt * BKB;
     const uint32_t b = bo + (uint32_t)kt * MXT_CODES;
+    const uint32_t bb = bbo + (uint32_t)kt * MXT_CODES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (ATILED)
         b2lds16(ra, b + j * 1024, st + wbase + j * 1024);
       else
         b2lds16(ra, ao[j] + kb, st + wbase + j * 1024);
-      b2lds16(rb, b + j * 1024, st + TILE_BYTES + wbase + j * 1024);
+      if (j < NFB) b2lds16(rb, bb + j * 1024, st + TILE_BYTES + bwbase + j * 1024);
     }
-    b2lds4(rs, so + (uint32_t)kt * sstep, st + sbase);
+    if (NB == BN || wave < 4 + NFB) b2lds4(rs, so + (uint32_t)kt * sstep, st + sbase);
   };
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -107,17 +119,17 @@ __device__ __forceinline__ void mainloop_t(const void* abase, ARow arow, const v
     const int cur = kt & 1;
     const char* st = lds + cur * STAGE_BYTES;
     if (kt + 1 < KT) issue(kt + 1, lds + (cur ^ 1) * STAGE_BYTES);
-    i32x8_t bq[FN], aq[2];
-    int sbq[FN], saq[2];
+    i32x8_t bq[NFB], aq[2];
+    int sbq[NFB], saq[2];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) read_b_mx(st, j, bq[j], sbq[j]);
+    for (int j = 0; j < NFB; ++j) read_b_mx<NB>(st, j, bq[j], sbq[j]);
     read_a_mx(st, 0, aq[0], saq[0]);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i + 1 < FM) read_a_mx(st, i + 1, aq[(i + 1) & 1], saq[(i + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < NFB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[i & 1], bq[j], acc[i][j], 0, 0, 0,
                                                                      saq[i & 1], 0, sbq[j]);
       __builtin_amdgcn_sched_barrier(0);
@@ -127,11 +139,11 @@ __device__ __forceinline__ void mainloop_t(const void* abase, ARow arow, const v
   }
 }
 
-template <typename ARow, typename ASc>
+template <int NB = BN, typename ARow, typename ASc>
 __device__ __forceinline__ void mainloop(const void* abase, ARow arow, const void* asbase, ASc ascale,
                                          const uint8_t* bcodes, const uint8_t* bscales, int K, char* lds,
                                          Acc& acc) {
-  mainloop_t<false>(abase, arow, asbase, ascale, bcodes, bscales, K, lds, acc);
+  mainloop_t<false, NB>(abase, arow, asbase, ascale, bcodes, bscales, K, lds, acc);
 }
 
 // a[p, i] = silu(g) * u (bf16) from MXFP8 ring rows and packed MXFP8 W_gu.
@@ -145,32 +157,44 @@ __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uin
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = 2 * I / BN;
   const int nbh = H / 32;
-  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+  // one tile of NB packed columns (NB / 2 features; a wave's NB / 4 columns
+  // are NB / 128 gate/up groups of 32)
+  auto tile = [&](const TileInfo& ti, auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
     auto rrow = [&](int r) { return (int64_t)((ti.pos0 + min(r, ti.rows - 1)) % ring_rows); };
     auto arow = [&](int r) { return rc + rrow(r) * H; };
     auto asc = [&](int r) { return rsc + rrow(r) * nbh; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, 2 * I, H);
+    const int h = (ti.n0 % BN) / 128;          // the half of a 256-row block (half tiles)
     Acc acc;
-    mainloop(rc, arow, rsc, asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
+    mainloop<NB>(rc, arow, rsc, asc, wc + t0 * MXT_CODES + h * 128 * MXT_K, wsc + t0 * MXT_SCALES + h * 128 * 4, H,
+                 lds, acc);
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NB / 128; ++q) {
           const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
           const int r = frag_row(i, v);
-          stage_put(lds, r, wn * 32 + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
+          stage_put(lds, r, wn * (NB / 8) + q * 16 + (lane & 15), g * sigmoidf_(g) * u);
           if (SAVE && r < ti.rows) {
-            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * 64 + q * 32 + (lane & 15);
+            float* dst = gu_save + (int64_t)(ti.pos0 + r) * 2 * I + ti.n0 + wn * (NB / 4) + q * 32 + (lane & 15);
             dst[0] = g;
             dst[16] = u;
           }
         }
-    stage_flush<128>(lds, [&](int r) -> uint16_t* {
+    stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
       return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
     });
+  };
+  // a last round at most half full runs as 256 x 128 half tiles
+  for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
+    if (half < 0)
+      tile(ti, std::integral_constant<int, BN>{});
+    else
+      tile(ti, std::integral_constant<int, BN / 2>{});
   });
 }
 
@@ -232,14 +256,24 @@ __global__ __launch_bounds__(NT) void bwd_dact_mxfp8_kernel(ItemRange ir, const 
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = I / BN;
   const int nbh = H / 32;
-  for_each_tile(ir, ntn, [&](const TileInfo& ti) {
+  auto tile = [&](const TileInfo& ti, auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
     auto prow = [&](int r) { return (int64_t)(ti.pos0 + min(r, ti.rows - 1)); };
     auto arow = [&](int r) { return dyc + prow(r) * H; };
     auto asc = [&](int r) { return dys + prow(r) * nbh; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, I, H);
+    const int h = (ti.n0 % BN) / 128;          // the half of a 256-row block (half tiles)
     Acc acc;
-    mainloop(arow(0), arow, asc(0), asc, wc + t0 * MXT_CODES, wsc + t0 * MXT_SCALES, H, lds, acc);
-    dact_epilogue(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
+    mainloop<NB>(arow(0), arow, asc(0), asc, wc + t0 * MXT_CODES + h * 128 * MXT_K, wsc + t0 * MXT_SCALES + h * 128 * 4,
+                 H, lds, acc);
+    dact_epilogue<NB>(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
+  };
+  // a last round at most half full runs as 256 x 128 half tiles
+  for_each_tile_split(ir, ntn, [&](const TileInfo& ti, int half) {
+    if (half < 0)
+      tile(ti, std::integral_constant<int, BN>{});
+    else
+      tile(ti, std::integral_constant<int, BN / 2>{});
   });
 }
 
