@@ -212,8 +212,9 @@ int mk_build_schedule(mk_workspace* ws, mk_schedule* sched, const int32_t* row_e
  *   [1] (written whole); layouts as the MK_TAB_* tables.  With R = 0 only
  *   counts, offsets, items, mb_items and err are written (the others may be
  *   NULL).
- * MK_ERR_LIMIT if nb * ceil(MB / 256) * (E + 1) * 4 bytes exceed the 4 MiB
- * scratch or nb > 65535; MK_ERR_SHAPE / _NULL on bad arguments; MK_ERR_HIP
+ * MK_ERR_LIMIT if the build's scratch, nb * (c4 * E + c) * 4 bytes with
+ * c = ceil(MB / 256) chunks and c4 = c rounded up to a multiple of 4,
+ * exceeds the 4 MiB array, or nb > 65535; MK_ERR_SHAPE / _NULL on bad arguments; MK_ERR_HIP
  * if the scratch's device address cannot be found.  Calls on one GPU share
  * the scratch: calls that overlap on one GPU (different streams without
  * ordering) race.

@@ -399,7 +399,7 @@ int mk_workspace_create(const mk_config* cfg, int32_t max_rows, int32_t H, int32
   Carver c;
   const size_t o_zero = c.take(512);
   const size_t o_fctl = c.take((size_t)fused_ctl_words(ws->item_cap) * 4);
-  const size_t o_cc = c.take((size_t)ws->nb_max * ws->cpm * E * 4);
+  const size_t o_cc = c.take((size_t)ws->nb_max * sched_cps(ws->cpm) * E * 4);
   const size_t o_cb = c.take((size_t)ws->nb_max * ws->cpm * 4);
   const size_t o_ring = c.take((size_t)ws->ring_rows * ws->row_bytes);
   const size_t o_a = c.take((size_t)npos * I * 2);

@@ -26,8 +26,11 @@ struct SchedTables {
   int32_t *sorted_pos, *inv, *items, *mb_items;
 };
 // Scratch of the schedule build and the sizes its launches use.
+// Chunks per (minibatch, expert) column of the chunk histograms, padded to a
+// multiple of 4 so each column starts 16-byte aligned.
+__host__ __device__ inline int32_t sched_cps(int32_t cpm) { return (cpm + 3) & ~3; }
 struct SchedScratch {
-  int32_t* chunk_counts;      // [nb_max, cpm, E] per-chunk expert histograms
+  int32_t* chunk_counts;      // [nb_max, E, sched_cps(cpm)] per-chunk expert histograms, by (b, e) column
   int32_t* chunk_bad;         // [nb_max, cpm]: a chunk holds an expert id out of range
 };
 struct SchedDims {

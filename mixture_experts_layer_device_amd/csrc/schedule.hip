@@ -2,9 +2,10 @@
 // the minibatch size (host-known), never from per-expert counts.
 //
 //  count   (minibatch b, chunk c of 256 rows): per-chunk expert histogram in
-//          LDS ([b][c][e]), and a flag for a chunk holding an expert id out
-//          of range; also marks every sorted position of the chunk's range
-//          empty.
+//          LDS, stored by (b, e) column ([b][e][c], columns padded to a
+//          multiple of 4 chunks), and a flag for a chunk holding an expert id
+//          out of range; also marks every sorted position of the chunk's
+//          range empty.
 //  scan    (one workgroup): per (b, e) prefix over chunks, per-minibatch
 //          expert offsets, global counts/offsets, the GEMM work items (one
 //          per 256-row m-tile of each (b, e) run) with their offsets, and the
@@ -48,8 +49,9 @@ __global__ __launch_bounds__(CH) void sched_count_kernel(const int32_t* __restri
     }
   }
   bad = __syncthreads_or(bad);
-  int32_t* out = chunk_counts + ((int64_t)b * cpm + c) * E;
-  for (int e = tid; e < E; e += CH) out[e] = hist[e];
+  const int cps = sched_cps(cpm);
+  int32_t* out = chunk_counts + (int64_t)b * E * cps + c;
+  for (int e = tid; e < E; e += CH) out[(int64_t)e * cps] = hist[e];
   if (tid == 0) chunk_bad[b * cpm + c] = bad;
 }
 
@@ -86,6 +88,10 @@ __device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
   return ex;
 }
 
+// (b, e) counts and offsets kept in LDS when nb * (E + 1) fits, so the
+// later passes read them there instead of from global memory
+constexpr int SCAN_LDS = 8192;
+
 __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int nb, int cpm, int tile_m,
                                                             int item_cap, int32_t* __restrict__ chunk_counts,
                                                             int32_t* __restrict__ mb_counts,
@@ -97,34 +103,72 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
                                                             const int32_t* __restrict__ chunk_bad,
                                                             uint32_t* __restrict__ err) {
   __shared__ int sbuf[SCAN_T];
+  __shared__ int s_cnt[SCAN_LDS], s_off[SCAN_LDS];
   const int tid = threadIdx.x;
   const int nbe = nb * E;
-  // an expert id out of range in any chunk
+  const bool in_lds = nb * (E + 1) <= SCAN_LDS;
+  // reads of the (b, e) tables after they are written: LDS copies when they fit
+  const int32_t* mbc = in_lds ? (const int32_t*)s_cnt : mb_counts;
+  const int32_t* mbo = in_lds ? (const int32_t*)s_off : mb_offsets;
+  // an expert id out of range in any chunk (reduced at the end, so these
+  // loads overlap the chunk pass)
   int bad = 0;
   for (int i = tid; i < nb * cpm; i += SCAN_T) bad |= chunk_bad[i];
-  bad = __syncthreads_or(bad);
   // per (b, e): exclusive prefix over the chunks of minibatch b (in place).
   // SG consecutive lanes share one (b, e) column, each taking a contiguous
-  // run of chunks: a batched pass for the run sums, a shuffle scan across the
-  // SG lanes, a second pass writing the prefixes.
+  // run of chunks that starts 16-byte aligned: the run's counts loaded four
+  // at a time (kept in registers when the run is at most 16 chunks, else
+  // summed in a first pass and re-read), a shuffle scan across the SG lanes,
+  // then the prefixes stored four at a time (a group that reaches past the
+  // column's last chunk writes only into the column's padding).
   {
-    constexpr int SG = 8;
+    constexpr int SG = 8, RUN = 16;
+    const int cps = sched_cps(cpm);
     const int sub = tid & (SG - 1);
-    const int per = (cpm + SG - 1) / SG;
+    const int per = sched_cps((cpm + SG - 1) / SG);
     const int c_lo = min(cpm, sub * per), c_hi = min(cpm, c_lo + per);
     for (int be0 = 0; be0 < nbe; be0 += SCAN_T / SG) {
       const int be = be0 + tid / SG;
       const bool on = be < nbe;
-      int32_t* cc = chunk_counts + (on ? (int64_t)(be / E) * cpm * E + (be % E) : 0);
-      int sum = 0;
-      if (on) {
-        int c = c_lo;
-        for (; c + 4 <= c_hi; c += 4) {
-          const int v0 = cc[(int64_t)c * E], v1 = cc[(int64_t)(c + 1) * E];
-          const int v2 = cc[(int64_t)(c + 2) * E], v3 = cc[(int64_t)(c + 3) * E];
-          sum += v0 + v1 + v2 + v3;
+      int32_t* cc = chunk_counts + (on ? (int64_t)be * cps : 0);
+      // counts of chunks c .. c+3 (those at or past c_hi read as 0)
+      auto load4 = [&](int c, int* v) {
+        u32x4_t q{0u, 0u, 0u, 0u};
+        if (c < c_hi) q = *(const u32x4_t*)(cc + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = c + j < c_hi ? (int)q[j] : 0;
+      };
+      auto store_prefix4 = [&](int c, const int* v, int& run) {
+        if (c >= c_hi) return;
+        u32x4_t o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j] = (uint32_t)run;
+          run += v[j];
         }
-        for (; c < c_hi; ++c) sum += cc[(int64_t)c * E];
+        *(u32x4_t*)(cc + c) = o;
+      };
+      int sum = 0;
+      int v[RUN];
+      if (per <= RUN) {
+#pragma unroll
+        for (int q = 0; q < RUN / 4; ++q) {
+          if (on) {
+            load4(c_lo + 4 * q, v + 4 * q);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * q + j] = 0;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RUN; ++i) sum += v[i];
+      } else if (on) {
+        for (int c = c_lo; c < c_hi; c += RUN) {
+#pragma unroll
+          for (int q = 0; q < RUN / 4; ++q) load4(c + 4 * q, v + 4 * q);
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) sum += v[i];
+        }
       }
       // inclusive scan over the SG lanes of the group (groups never straddle a wave)
       int incl = sum;
@@ -136,18 +180,21 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
       const int total = __shfl(incl, SG - 1, SG);
       if (on) {
         int run = incl - sum;
-        for (int c = c_lo; c < c_hi; c += 8) {
-          int v[8];
+        if (per <= RUN) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = c + i < c_hi ? cc[(int64_t)(c + i) * E] : 0;
+          for (int q = 0; q < RUN / 4; ++q) store_prefix4(c_lo + 4 * q, v + 4 * q, run);
+        } else {
+          for (int c = c_lo; c < c_hi; c += RUN) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (c + i < c_hi) {
-              cc[(int64_t)(c + i) * E] = run;
-              run += v[i];
-            }
+            for (int q = 0; q < RUN / 4; ++q) load4(c + 4 * q, v + 4 * q);
+#pragma unroll
+            for (int q = 0; q < RUN / 4; ++q) store_prefix4(c + 4 * q, v + 4 * q, run);
+          }
         }
-        if (sub == 0) mb_counts[be] = total;
+        if (sub == 0) {
+          mb_counts[be] = total;
+          if (in_lds) s_cnt[be] = total;
+        }
       }
     }
   }
@@ -157,13 +204,19 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += SCAN_T) {
       const int e = e0 + tid;
-      const int v = e < E ? mb_counts[b * E + e] : 0;
+      const int v = e < E ? mbc[b * E + e] : 0;
       int tot;
       const int ex = block_exclusive_scan(v, sbuf, &tot);
-      if (e < E) mb_offsets[b * (E + 1) + e] = carry + ex;
+      if (e < E) {
+        mb_offsets[b * (E + 1) + e] = carry + ex;
+        if (in_lds) s_off[b * (E + 1) + e] = carry + ex;
+      }
       carry += tot;
     }
-    if (tid == 0) mb_offsets[b * (E + 1) + E] = carry;
+    if (tid == 0) {
+      mb_offsets[b * (E + 1) + E] = carry;
+      if (in_lds) s_off[b * (E + 1) + E] = carry;
+    }
   }
   // global per-expert counts and offsets
   {
@@ -172,7 +225,7 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
       const int e = e0 + tid;
       int v = 0;
       if (e < E)
-        for (int b = 0; b < nb; ++b) v += mb_counts[b * E + e];
+        for (int b = 0; b < nb; ++b) v += mbc[b * E + e];
       int tot;
       const int ex = block_exclusive_scan(v, sbuf, &tot);
       if (e < E) {
@@ -190,14 +243,14 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
     const int be = be0 + tid;
     int cnt = 0, nm = 0;
     if (be < nbe) {
-      cnt = mb_counts[be];
+      cnt = mbc[be];
       nm = (cnt + tile_m - 1) / tile_m;
     }
     int tot;
     const int start = carry + block_exclusive_scan(nm, sbuf, &tot);
     if (be < nbe) {
       const int b = be / E, e = be - b * E;
-      const int base = b * MB + mb_offsets[b * (E + 1) + e];
+      const int base = b * MB + mbo[b * (E + 1) + e];
       for (int m = 0; m < nm; ++m) {
         const int idx = start + m;
         if (idx < item_cap) {
@@ -212,6 +265,7 @@ __global__ __launch_bounds__(SCAN_T) void sched_scan_kernel(int E, int MB, int n
     }
     carry += tot;
   }
+  bad = __syncthreads_or(bad);
   if (tid == 0) {
     mb_items[nb] = carry;
     *err = (bad ? MK_DEVERR_EXPERT_RANGE : 0u) | (carry > item_cap ? MK_DEVERR_SCHED_OVERFLOW : 0u);
@@ -239,7 +293,8 @@ __global__ __launch_bounds__(CH) void sched_scatter_kernel(const int32_t* __rest
   if (e >= 0) {
     int rank = 0;
     for (int j = 0; j < tid; ++j) rank += (ex[j] == e);
-    const int pos = b * MB + mb_offsets[b * (E + 1) + e] + chunk_base[((int64_t)b * cpm + c) * E + e] + rank;
+    const int pos =
+        b * MB + mb_offsets[b * (E + 1) + e] + chunk_base[((int64_t)b * E + e) * sched_cps(cpm) + c] + rank;
     sorted_pos[r] = pos;
     inv[pos] = (int32_t)r;
   } else if (live) {
@@ -325,12 +380,13 @@ extern "C" int mk_build_schedule_static(const int32_t* row_expert, int32_t R, in
   if (R > 0 && (!row_expert || !mb_counts || !mb_offsets || !sorted_pos || !inv)) return MK_ERR_NULL;
   if (nb > 65535) return MK_ERR_LIMIT;
   const int64_t cpm = ((int64_t)MB + MK_SCHED_CHUNK - 1) / MK_SCHED_CHUNK;
-  // scratch: [nb, cpm, E] chunk histograms, then [nb, cpm] chunk flags
-  const int64_t need = (nb * cpm * E + nb * cpm) * 4;
+  // scratch: [nb, E, cps] chunk histograms, then [nb, cpm] chunk flags
+  const int64_t cps = sched_cps((int32_t)cpm);
+  const int64_t need = (nb * cps * E + nb * cpm) * 4;
   if (need > kStaticScratchBytes) return MK_ERR_LIMIT;
   int32_t* base = device_scratch();
   if (!base) return MK_ERR_HIP;
-  SchedScratch scr{base, base + nb * cpm * E};
+  SchedScratch scr{base, base + nb * cps * E};
   SchedTables t{err, mb_counts, mb_offsets, counts, offsets, sorted_pos, inv, items, mb_items};
   const SchedDims d{MB, E, (int32_t)cpm, item_cap};
   launch_schedule(d, scr, t, row_expert, R, (hipStream_t)stream);

@@ -76,6 +76,10 @@ SCHED_CASES = [
     ("uniform128_one_mb", 32768, 128, 32768, 1),
     ("ragged37", 1000, 37, 300, 7),
     ("single_row", 1, 3, 1, 8),
+    # (b, e) tables past the scan's LDS copy (10 minibatches x 1025 > 8192)
+    ("e1024_ten_mbs", 20000, 1024, 2048, 9),
+    # runs of more than 16 chunks per scan lane (256 chunks of 256 rows)
+    ("mb65536_long_runs", 70000, 16, 65536, 10),
 ]
 
 

@@ -59,7 +59,7 @@ def test_static_schedule_matches_workspace_schedule(E, MB):
 
 
 def test_static_schedule_refuses_beyond_its_scratch():
-    # nb * ceil(MB / 256) * (E + 1) * 4 bytes above 4 MiB
+    # nb * (c4 * E + c) * 4 bytes above 4 MiB (c = ceil(MB / 256) chunks, c4 = c rounded up to 4)
     with pytest.raises(B.MkError) as ei:
         B.mk_build_schedule_static(1, 1 << 20, 1024, 4096, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, None)
     assert ei.value.status == B.MK_ERR_LIMIT
