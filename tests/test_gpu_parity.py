@@ -145,6 +145,29 @@ def test_route_bit_exact(name):
     L.close()
 
 
+@pytest.mark.parametrize("T,H,E,k,renorm,bias_var", [(1000, 512, 37, 3, 1, 0.5), (77, 256, 200, 5, 0, 0.0)],
+                         ids=["T1000_E37", "T77_E200"])
+def test_route_bit_exact_ragged(T, H, E, k, renorm, bias_var):
+    """Token counts off the router's 16-token blocks, an expert count off its
+    4-expert groups (E=37) and a second, partial 128-expert chunk (E=200)."""
+    sh = dataclasses.replace(workloads.FULL_LAYER["tiny"], T=T, H=H, E=E, k=k, renorm=renorm, bias_var=bias_var,
+                             seed=41 + E)
+    inp = workloads.make_full_layer(sh)
+    say(f"[route] ragged T={T} H={H} E={E} k={k} renorm={renorm}")
+    x = bf16.decode(inp["x"]).astype(np.float32)
+    wr = bf16.decode(inp["w_router"]).astype(np.float32)
+    idx_ref, w_ref, _ = route.route(x, wr, inp["bias"], k, renorm)
+    L = MoELayer(H=H, I=sh.I, E=E, k=k, max_rows=T * k, renorm=renorm)
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    idx, w = L.route(dev(inp["x"]), dev(inp["w_router"]), bias, T)
+    sync()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    err = float(np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_ref)))
+    say(f"  router weights max|err| = {err:.2e}")
+    assert err <= ROUTER_W_ATOL
+    L.close()
+
+
 # -------------------------------------------------------------- quantiser --
 def test_mxfp8_quantize_bit_exact():
     say("[mxfp8_quantize] all finite bf16 patterns + wide-range random rows")
