@@ -879,6 +879,13 @@ __device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int u,
 // then all in use by the K loop, and the unit is passed in its first bytes
 // (free between units: every unit ends at a barrier after its last LDS
 // access, and a second barrier below comes before the next unit's copies).
+// A workgroup takes its next ticket as soon as its current unit's inputs
+// are ready, so the atomic's latency hides behind the unit; per queue a
+// workgroup's tickets still increase, and a unit depends only on units of
+// earlier segments, so the earliest unfinished unit is always running.
+// GEMM2 units publish nothing: without B3 (the unit is passed outside the K
+// loop's buffers) they end without waiting for their stores, which then
+// drain under the next unit's ticket, wait and first loads.
 template <bool SHARE, bool B3>
 __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES + 16];
@@ -887,16 +894,17 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = blockIdx.x % FUSE_XCD;   // this workgroup's queue
   const int ntn1 = 2 * a.I / BN, ntn2 = a.H / BN;
+  uint32_t t_next = 0;                   // wave 0, lane 0: the ticket of the next unit
+  if (wave == 0 && lane == 0) t_next = atomicAdd(a.ticket + 64 * x, 1u);
   while (true) {
     if (wave == 0) {
-      uint32_t t = 0;
-      if (lane == 0) t = atomicAdd(a.ticket + 64 * x, 1u);
-      const FusedUnit un = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t));
+      const FusedUnit un = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t_next));
       if (un.kind == U_G1) {
         fused_wait(a.p_done + fused_items_lo(a, un.b) + un.u / ntn1, (uint32_t)FUSE_PCH, a.err);
       } else if (un.kind == U_G2) {
         fused_wait(a.g1_done + fused_items_lo(a, un.b) + un.u / ntn2, (uint32_t)ntn1, a.err);
       }
+      if (un.kind != U_NONE && lane == 0) t_next = atomicAdd(a.ticket + 64 * x, 1u);
       if (lane == 0) {
         su[0] = un.kind;
         su[1] = un.b;
@@ -930,6 +938,7 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
       const TileInfo ti = fused_tile(a, b, u, ntn2, item);
       gemm2_tile<SHARE>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
     }
+    if (kind == U_G2 && !B3) continue;   // nothing to publish, no LDS hand-over
     // publish: every wave's stores complete, then one counter bump
     wait_all_mem();
     __syncthreads();
