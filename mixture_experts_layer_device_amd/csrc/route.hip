@@ -8,20 +8,21 @@
 // would not, so the parallelism comes from the (token, expert) pairs only.
 //
 // Workgroup = RT = 16 tokens x all experts, in chunks of RE = 128 experts,
-// eight waves (two per SIMD, so one wave's LDS, load and barrier waits are
-// covered by the other's multiply-adds).  Lane l of a wave keeps the chains
-// of token l mod 16 and the four experts of group 4 * wave + l / 16 (16-lane
-// row r of wave w: experts 4 (4w + r) .. +3).  x and the router rows are
-// staged through LDS per 64-wide slice of h as fp32, double-buffered, with
-// the next slice's global loads in registers.  The router weights sit in LDS
-// as [h / 4][expert][h mod 4], so one 4-byte read per lane brings a row its
-// 16 values (4 experts x 4 h), and each multiply-add takes its weight from
-// lane 4e + (h mod 4) of its row by a DPP row broadcast (row_newbcast) folded
-// into v_fmac_f32: every LDS value a lane reads feeds 4 multiply-adds or
-// more, which keeps the kernel off the LDS bandwidth bound.  Top-k then runs
-// one wave per token over the logits kept in LDS: k rounds of a wave-wide
-// (max logit, min id) reduction.  The LOGITS variant stops after the logits
-// and stores them (the router backward needs the full softmax).
+// sixteen waves (four per SIMD, so the waves' LDS, load and barrier waits
+// are covered by the others' multiply-adds, and the DPP multiply-adds issue
+// closer to their peak rate).  Lane l of a wave keeps the chains of token
+// l mod 16 and the two experts of group 4 * wave + l / 16 (16-lane row r of
+// wave w: experts 2 (4w + r), +1).  x and the router rows are staged through
+// LDS per 64-wide slice of h as fp32, double-buffered, with each slice's
+// global loads issued two slices ahead into registers.  The router weights
+// sit in LDS as [h / 8][expert][h mod 8], so one 4-byte read per lane brings
+// a row its 16 values (2 experts x 8 h), and each multiply-add takes its
+// weight from lane 8e + (h mod 8) of its row by a DPP row broadcast
+// (row_newbcast) folded into v_fmac_f32: every LDS weight read feeds 16
+// multiply-adds, which keeps the kernel off the LDS bandwidth bound.  Top-k
+// then runs one wave per token over the logits kept in LDS: k rounds of a
+// wave-wide (max logit, min id) reduction.  The LOGITS variant stops after
+// the logits and stores them (the router backward needs the full softmax).
 #include "mk_device.h"
 #include "mk_internal.h"
 
@@ -29,33 +30,26 @@ namespace mk {
 namespace {
 
 constexpr int RT = 16;     // tokens per workgroup
-constexpr int RE = 128;    // experts per chunk (32 groups of 4, one per 16-lane row)
+constexpr int RE = 128;    // experts per chunk (64 groups of 2, one per 16-lane row)
 constexpr int RH = 64;     // h per LDS slice
-constexpr int RNT = 512;   // threads (8 waves)
+constexpr int RNT = 1024;  // threads (16 waves)
 constexpr int XS = RH + 4; // floats per staged x row (the pad spreads a row's 16 tokens over the banks)
 
-// acc[e] += w(lane 4e + j of the row) * x_j for four consecutive h (x0 .. x3,
-// weights of wv), in ascending h for every chain.  v_fmac_f32 rounds once (a
+// acc[e] += w(lane 8e + j of the row) * x_j for eight consecutive h (x0 ..
+// x7 = xa, xb), in ascending h for every chain.  v_fmac_f32 rounds once (a
 // fused multiply-add) like __builtin_fmaf.  The compiler's hazard checks do
 // not see into the asm, so it opens with 5 wait states: a DPP source written
 // by the VALU needs 2, an EXEC written by the VALU 5.
 #define MK_FMAC(d, w, x, n) "v_fmac_f32_dpp %" #d ", %" #w ", %" #x " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
-#define MK_FMAC_H(w, x, j) MK_FMAC(0, w, x, j) MK_FMAC(1, w, x, 4 + j) MK_FMAC(2, w, x, 8 + j) MK_FMAC(3, w, x, 12 + j)
-__device__ __forceinline__ void fmac_group8(float (&acc)[4], float wa, float wb, f32x4_t xa, f32x4_t xb) {
+__device__ __forceinline__ void fmac_group8(float (&acc)[2], float wv, f32x4_t xa, f32x4_t xb) {
   asm("s_nop 4\n"
-      MK_FMAC(0, 4, 6, 0) MK_FMAC(1, 4, 6, 4) MK_FMAC(2, 4, 6, 8) MK_FMAC(3, 4, 6, 12)
-      MK_FMAC(0, 4, 7, 1) MK_FMAC(1, 4, 7, 5) MK_FMAC(2, 4, 7, 9) MK_FMAC(3, 4, 7, 13)
-      MK_FMAC(0, 4, 8, 2) MK_FMAC(1, 4, 8, 6) MK_FMAC(2, 4, 8, 10) MK_FMAC(3, 4, 8, 14)
-      MK_FMAC(0, 4, 9, 3) MK_FMAC(1, 4, 9, 7) MK_FMAC(2, 4, 9, 11) MK_FMAC(3, 4, 9, 15)
-      MK_FMAC(0, 5, 10, 0) MK_FMAC(1, 5, 10, 4) MK_FMAC(2, 5, 10, 8) MK_FMAC(3, 5, 10, 12)
-      MK_FMAC(0, 5, 11, 1) MK_FMAC(1, 5, 11, 5) MK_FMAC(2, 5, 11, 9) MK_FMAC(3, 5, 11, 13)
-      MK_FMAC(0, 5, 12, 2) MK_FMAC(1, 5, 12, 6) MK_FMAC(2, 5, 12, 10) MK_FMAC(3, 5, 12, 14)
-      MK_FMAC(0, 5, 13, 3) MK_FMAC(1, 5, 13, 7) MK_FMAC(2, 5, 13, 11) MK_FMAC(3, 5, 13, 15)
-      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-      : "v"(wa), "v"(wb), "v"(xa[0]), "v"(xa[1]), "v"(xa[2]), "v"(xa[3]), "v"(xb[0]), "v"(xb[1]), "v"(xb[2]),
-        "v"(xb[3]));
+      MK_FMAC(0, 2, 3, 0) MK_FMAC(1, 2, 3, 8) MK_FMAC(0, 2, 4, 1) MK_FMAC(1, 2, 4, 9)
+      MK_FMAC(0, 2, 5, 2) MK_FMAC(1, 2, 5, 10) MK_FMAC(0, 2, 6, 3) MK_FMAC(1, 2, 6, 11)
+      MK_FMAC(0, 2, 7, 4) MK_FMAC(1, 2, 7, 12) MK_FMAC(0, 2, 8, 5) MK_FMAC(1, 2, 8, 13)
+      MK_FMAC(0, 2, 9, 6) MK_FMAC(1, 2, 9, 14) MK_FMAC(0, 2, 10, 7) MK_FMAC(1, 2, 10, 15)
+      : "+v"(acc[0]), "+v"(acc[1])
+      : "v"(wv), "v"(xa[0]), "v"(xa[1]), "v"(xa[2]), "v"(xa[3]), "v"(xb[0]), "v"(xb[1]), "v"(xb[2]), "v"(xb[3]));
 }
-#undef MK_FMAC_H
 #undef MK_FMAC
 
 __device__ __forceinline__ bool better(float za, int ea, float zb, int eb) {
@@ -68,93 +62,99 @@ __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__
                                                     int renorm, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out, float* __restrict__ z_out) {
   extern __shared__ float zbuf[];                                  // [RT][E]
-  __shared__ __attribute__((aligned(16))) float ws[2][RH / 4][RE][4];
+  __shared__ __attribute__((aligned(16))) float ws[2][RH / 8][RE][8];
   __shared__ __attribute__((aligned(16))) float xs[2][RT][XS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, tok = lane & 15, rl = lane & 15;
   const int grp = (tid >> 6) * 4 + (lane >> 4);                   // expert group of this lane's row
   const int t0 = blockIdx.x * RT;
-  // staging roles: router row e0 + (tid & 127), h quarter (tid >> 7) of the
-  // slice (2 loads of 8 h); threads 0..127 also stage token tid >> 3, h
+  // staging roles: router row e0 + (tid & 127), h eighth (tid >> 7) of the
+  // slice (one load of 8 h); threads 0..127 also stage token tid >> 3, h
   // eighth (tid & 7)
-  const int se = tid & 127, sh = (tid >> 7) * (RH / 4);
+  const int se = tid & 127, sh = (tid >> 7) * (RH / 8);
   const int st_tok = tid >> 3, sq = (tid & 7) * 8;
   const bool x_stager = tid < 128 && t0 + st_tok < T;
   for (int e0 = 0; e0 < E; e0 += RE) {
     const bool w_valid = e0 + se < E;
     const uint16_t* wrow = w + (int64_t)(w_valid ? e0 + se : 0) * H + sh;
     const uint16_t* xrow = x + (int64_t)(x_stager ? t0 + st_tok : 0) * H + sq;
-    u32x4_t wr[2], xr{0u, 0u, 0u, 0u};
+    // two register sets: slice s's global loads are issued two slices ahead
+    u32x4_t wr[2], xr[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) wr[q] = u32x4_t{0u, 0u, 0u, 0u};
-    auto load = [&](int h0) {
-      if (w_valid) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) wr[q] = *(const u32x4_t*)(wrow + h0 + 8 * q);
-      }
-      if (x_stager) xr = *(const u32x4_t*)(xrow + h0);
+    for (int r = 0; r < 2; ++r) {
+      xr[r] = u32x4_t{0u, 0u, 0u, 0u};
+      wr[r] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    auto load = [&](int h0, int r) {
+      if (w_valid) wr[r] = *(const u32x4_t*)(wrow + h0);
+      if (x_stager) xr[r] = *(const u32x4_t*)(xrow + h0);
     };
-    // bf16 pair (h even, h odd) in one dword -> fp32 (d << 16, d & 0xFFFF0000)
-    auto stage = [&](int buf) {
+    // bf16 pair (h even, h odd) in one dword -> fp32 (d << 16, d & 0xFFFF0000);
+    // register set r goes to LDS buffer r
+    auto stage = [&](int r) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int d = 0; d < 4; d += 2) {
-          f32x4_t v;
-          v[0] = bf16_to_f32(wr[q][d] & 0xFFFFu);
-          v[1] = bf16_to_f32(wr[q][d] >> 16);
-          v[2] = bf16_to_f32(wr[q][d + 1] & 0xFFFFu);
-          v[3] = bf16_to_f32(wr[q][d + 1] >> 16);
-          *(f32x4_t*)&ws[buf][(sh + 8 * q) / 4 + d / 2][se][0] = v;
-        }
+      for (int d = 0; d < 4; d += 2) {
+        f32x4_t v;
+        v[0] = bf16_to_f32(wr[r][d] & 0xFFFFu);
+        v[1] = bf16_to_f32(wr[r][d] >> 16);
+        v[2] = bf16_to_f32(wr[r][d + 1] & 0xFFFFu);
+        v[3] = bf16_to_f32(wr[r][d + 1] >> 16);
+        *(f32x4_t*)&ws[r][sh / 8][se][2 * d] = v;
+      }
       if (tid < 128) {
         f32x4_t lo, hi;
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          lo[2 * d] = bf16_to_f32(xr[d] & 0xFFFFu);
-          lo[2 * d + 1] = bf16_to_f32(xr[d] >> 16);
-          hi[2 * d] = bf16_to_f32(xr[d + 2] & 0xFFFFu);
-          hi[2 * d + 1] = bf16_to_f32(xr[d + 2] >> 16);
+          lo[2 * d] = bf16_to_f32(xr[r][d] & 0xFFFFu);
+          lo[2 * d + 1] = bf16_to_f32(xr[r][d] >> 16);
+          hi[2 * d] = bf16_to_f32(xr[r][d + 2] & 0xFFFFu);
+          hi[2 * d + 1] = bf16_to_f32(xr[r][d + 2] >> 16);
         }
-        *(f32x4_t*)&xs[buf][st_tok][sq] = lo;
-        *(f32x4_t*)&xs[buf][st_tok][sq + 4] = hi;
+        *(f32x4_t*)&xs[r][st_tok][sq] = lo;
+        *(f32x4_t*)&xs[r][st_tok][sq + 4] = hi;
       }
     };
-    float acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = 0.f;
-    load(0);
-    for (int h0 = 0, buf = 0; h0 < H; h0 += RH, buf ^= 1) {
-      stage(buf);
-      __syncthreads();
-      if (h0 + RH < H) load(h0 + RH);
-      // groups of 8 h, the next group's LDS reads issued before this group's
-      // multiply-adds: per group two 4-byte weight reads (4 h each) and two
-      // 16-byte x reads
-      const float* wl = &ws[buf][0][4 * grp][0] + rl;
+    float acc[2] = {0.f, 0.f};
+    // groups of 8 h, the next group's LDS reads issued before this group's
+    // multiply-adds: per group one 4-byte weight read (2 experts x 8 h) and
+    // two 16-byte x reads
+    auto compute = [&](int buf) {
+      const float* wl = &ws[buf][0][2 * grp][0] + rl;
       const float* xl = &xs[buf][tok][0];
-      float wa = wl[0], wb = wl[RE * 4];
+      float wv = wl[0];
       f32x4_t xa = *(const f32x4_t*)xl, xb = *(const f32x4_t*)(xl + 4);
 #pragma unroll
       for (int h = 0; h < RH; h += 8) {
-        float na = 0.f, nb = 0.f;
+        float nw = 0.f;
         f32x4_t nxa{0.f, 0.f, 0.f, 0.f}, nxb{0.f, 0.f, 0.f, 0.f};
         if (h + 8 < RH) {
-          na = wl[(h + 8) / 4 * RE * 4];
-          nb = wl[((h + 8) / 4 + 1) * RE * 4];
+          nw = wl[(h + 8) / 8 * RE * 8];
           nxa = *(const f32x4_t*)(xl + h + 8);
           nxb = *(const f32x4_t*)(xl + h + 12);
         }
-        fmac_group8(acc, wa, wb, xa, xb);
-        wa = na;
-        wb = nb;
+        fmac_group8(acc, wv, xa, xb);
+        wv = nw;
         xa = nxa;
         xb = nxb;
       }
+    };
+    // H is a multiple of 2 * RH: slices in pairs, even ones through register
+    // set and LDS buffer 0, odd ones through 1
+    load(0, 0);
+    load(RH, 1);
+    for (int h0 = 0; h0 < H; h0 += 2 * RH) {
+      stage(0);
+      __syncthreads();
+      if (h0 + 2 * RH < H) load(h0 + 2 * RH, 0);
+      compute(0);
+      stage(1);
+      __syncthreads();
+      if (h0 + 3 * RH < H) load(h0 + 3 * RH, 1);
+      compute(1);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 4 * grp + j;
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + 2 * grp + j;
       if (e < E) {
         const float z = bias ? acc[j] + bias[e] : acc[j];
         if (LOGITS) {
