@@ -13,7 +13,8 @@
 // closer to their peak rate).  Lane l of a wave keeps the chains of token
 // l mod 16 and the two experts of group 4 * wave + l / 16 (16-lane row r of
 // wave w: experts 2 (4w + r), +1).  x and the router rows are staged through
-// LDS per 64-wide slice of h as fp32, double-buffered, with each slice's
+// LDS per 128-wide slice of h (64-wide when E > 128, so the logits of all
+// experts fit beside the slices) as fp32, double-buffered, with each slice's
 // global loads issued two slices ahead into registers.  The router weights
 // sit in LDS as [h / 8][expert][h mod 8], so one 4-byte read per lane brings
 // a row its 16 values (2 experts x 8 h), and each multiply-add takes its
@@ -31,9 +32,10 @@ namespace {
 
 constexpr int RT = 16;     // tokens per workgroup
 constexpr int RE = 128;    // experts per chunk (64 groups of 2, one per 16-lane row)
-constexpr int RH = 64;     // h per LDS slice
 constexpr int RNT = 1024;  // threads (16 waves)
-constexpr int XS = RH + 4; // floats per staged x row (the pad spreads a row's 16 tokens over the banks)
+// h per LDS slice: 128 where the slice buffers and the [RT][E] logits fit
+// the LDS together (E <= 128), else 64
+constexpr int RH_WIDE = 128, RH_NARROW = 64;
 
 // acc[e] += w(lane 8e + j of the row) * x_j for eight consecutive h (x0 ..
 // x7 = xa, xb), in ascending h for every chain.  v_fmac_f32 rounds once (a
@@ -56,52 +58,61 @@ __device__ __forceinline__ bool better(float za, int ea, float zb, int eb) {
   return za > zb || (za == zb && ea < eb);
 }
 
-template <bool LOGITS>
+template <bool LOGITS, int RH>
 __global__ __launch_bounds__(RNT) void route_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                     const float* __restrict__ bias, int T, int H, int E, int k,
                                                     int renorm, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out, float* __restrict__ z_out) {
   extern __shared__ float zbuf[];                                  // [RT][E]
   __shared__ __attribute__((aligned(16))) float ws[2][RH / 8][RE][8];
+  constexpr int XS = RH + 4;   // floats per staged x row (the pad spreads a row's 16 tokens over the banks)
+  constexpr int WQ = RH / 64;  // 8-h loads per thread and slice of a router row
+  constexpr int XT = 2 * RH;   // threads staging x (8 h each)
   __shared__ __attribute__((aligned(16))) float xs[2][RT][XS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, tok = lane & 15, rl = lane & 15;
   const int grp = (tid >> 6) * 4 + (lane >> 4);                   // expert group of this lane's row
   const int t0 = blockIdx.x * RT;
   // staging roles: router row e0 + (tid & 127), h eighth (tid >> 7) of the
-  // slice (one load of 8 h); threads 0..127 also stage token tid >> 3, h
-  // eighth (tid & 7)
+  // slice (WQ loads of 8 h); threads 0 .. XT-1 also stage token
+  // tid / (RH / 8), h granule tid mod (RH / 8)
   const int se = tid & 127, sh = (tid >> 7) * (RH / 8);
-  const int st_tok = tid >> 3, sq = (tid & 7) * 8;
-  const bool x_stager = tid < 128 && t0 + st_tok < T;
+  const int st_tok = tid / (RH / 8), sq = (tid % (RH / 8)) * 8;
+  const bool x_stager = tid < XT && t0 + st_tok < T;
   for (int e0 = 0; e0 < E; e0 += RE) {
     const bool w_valid = e0 + se < E;
     const uint16_t* wrow = w + (int64_t)(w_valid ? e0 + se : 0) * H + sh;
     const uint16_t* xrow = x + (int64_t)(x_stager ? t0 + st_tok : 0) * H + sq;
     // two register sets: slice s's global loads are issued two slices ahead
-    u32x4_t wr[2], xr[2];
+    u32x4_t wr[2][WQ], xr[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       xr[r] = u32x4_t{0u, 0u, 0u, 0u};
-      wr[r] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < WQ; ++q) wr[r][q] = u32x4_t{0u, 0u, 0u, 0u};
     }
     auto load = [&](int h0, int r) {
-      if (w_valid) wr[r] = *(const u32x4_t*)(wrow + h0);
+      if (w_valid) {
+#pragma unroll
+        for (int q = 0; q < WQ; ++q) wr[r][q] = *(const u32x4_t*)(wrow + h0 + 8 * q);
+      }
       if (x_stager) xr[r] = *(const u32x4_t*)(xrow + h0);
     };
     // bf16 pair (h even, h odd) in one dword -> fp32 (d << 16, d & 0xFFFF0000);
     // register set r goes to LDS buffer r
     auto stage = [&](int r) {
 #pragma unroll
-      for (int d = 0; d < 4; d += 2) {
-        f32x4_t v;
-        v[0] = bf16_to_f32(wr[r][d] & 0xFFFFu);
-        v[1] = bf16_to_f32(wr[r][d] >> 16);
-        v[2] = bf16_to_f32(wr[r][d + 1] & 0xFFFFu);
-        v[3] = bf16_to_f32(wr[r][d + 1] >> 16);
-        *(f32x4_t*)&ws[r][sh / 8][se][2 * d] = v;
-      }
-      if (tid < 128) {
+      for (int q = 0; q < WQ; ++q)
+#pragma unroll
+        for (int d = 0; d < 4; d += 2) {
+          f32x4_t v;
+          v[0] = bf16_to_f32(wr[r][q][d] & 0xFFFFu);
+          v[1] = bf16_to_f32(wr[r][q][d] >> 16);
+          v[2] = bf16_to_f32(wr[r][q][d + 1] & 0xFFFFu);
+          v[3] = bf16_to_f32(wr[r][q][d + 1] >> 16);
+          *(f32x4_t*)&ws[r][sh / 8 + q][se][2 * d] = v;
+        }
+      if (tid < XT) {
         f32x4_t lo, hi;
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
@@ -231,16 +242,20 @@ void launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias
                   int renorm, int32_t* idx, float* w, hipStream_t s) {
   if (T <= 0) return;
   const int blocks = (T + RT - 1) / RT;
-  hipLaunchKernelGGL(route_kernel<false>, dim3(blocks), dim3(RNT), RT * E * sizeof(float), s, x, w_router, bias, T,
-                     H, E, k, renorm, idx, w, nullptr);
+  if (E <= RE)
+    hipLaunchKernelGGL((route_kernel<false, RH_WIDE>), dim3(blocks), dim3(RNT), RT * E * sizeof(float), s, x,
+                       w_router, bias, T, H, E, k, renorm, idx, w, nullptr);
+  else
+    hipLaunchKernelGGL((route_kernel<false, RH_NARROW>), dim3(blocks), dim3(RNT), RT * E * sizeof(float), s, x,
+                       w_router, bias, T, H, E, k, renorm, idx, w, nullptr);
 }
 
 void launch_route_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
                          float* z, hipStream_t s) {
   if (T <= 0) return;
   const int blocks = (T + RT - 1) / RT;
-  hipLaunchKernelGGL(route_kernel<true>, dim3(blocks), dim3(RNT), 0, s, x, w_router, bias, T, H, E, 0, 0, nullptr,
-                     nullptr, z);
+  hipLaunchKernelGGL((route_kernel<true, RH_WIDE>), dim3(blocks), dim3(RNT), 0, s, x, w_router, bias, T, H, E, 0, 0,
+                     nullptr, nullptr, z);
 }
 
 }  // namespace mk
