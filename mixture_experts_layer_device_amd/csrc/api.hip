@@ -758,6 +758,11 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
     // in that L2); with more, spread every segment's units evenly so that a
     // panel stays on one XCD across the expert's items
     f.item_local = (int64_t)std::min(MB, R) < (int64_t)2 * MK_TILE_M * ws->E;
+    // full layer: GEMM1 gathers its A rows straight from the token rows
+    // (each token row serves k experts and stays in the last-level cache),
+    // so the ring is not written; a backward of this schedule replays them
+    f.direct = !share && (int64_t)(R / kk) * H * 2 <= ((int64_t)1 << 32);
+    if (f.direct) sc->fwd_ring_epoch = 0;
     f.x = x;
     f.inv = st.inv;
     f.row_w = row_w;

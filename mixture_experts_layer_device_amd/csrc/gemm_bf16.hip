@@ -329,17 +329,16 @@ __device__ __forceinline__ void mainloop_nt(const void* abase, ARow arow, const 
 // columns of the tile: NB / 2 features, a wave's NB / 4 columns being
 // NB / 128 gate/up groups of 32.  WT: the a rows are written through to
 // memory (read by another XCD in the same launch).
-template <int NB, bool WT = false, bool B3 = false>
-__device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* __restrict__ ring, int ring_rows,
-                                           const uint16_t* __restrict__ wgu, int H, int I,
-                                           uint16_t* __restrict__ a_out, float* __restrict__ gu_save, char* lds) {
-  auto arow = [&](int r) {
-    const int p = ti.pos0 + min(r, ti.rows - 1);
-    return ring + (int64_t)(p % ring_rows) * H;
-  };
+// arow(r): the A row of tile row r (rows past the item repeat its last row),
+// within 4 GiB after abase.
+template <int NB, bool WT = false, bool B3 = false, typename ARow>
+__device__ __forceinline__ void gemm1_tile_rows(const TileInfo& ti, const void* abase, ARow arow,
+                                                const uint16_t* __restrict__ wgu, int H, int I,
+                                                uint16_t* __restrict__ a_out, float* __restrict__ gu_save,
+                                                char* lds) {
   Acc acc;
-  mainloop_nt<NB, B3>(ring, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H, ti.rows,
-                      lds, acc);
+  mainloop_nt<NB, B3>(abase, arow, wgu + btile_block(ti.e, ti.n0 / BN, 0, 2 * I, H) + (ti.n0 % BN) * BK, H,
+                      ti.rows, lds, acc);
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -365,6 +364,18 @@ __device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* _
     stage_flush<NB / 2>(lds, [&](int r) -> uint16_t* {
       return r < ti.rows ? a_out + (int64_t)(ti.pos0 + r) * I + ti.n0 / 2 : nullptr;
     });
+}
+
+// GEMM1 tile whose A rows are the item's ring rows (positions mod ring_rows).
+template <int NB, bool WT = false, bool B3 = false>
+__device__ __forceinline__ void gemm1_tile(const TileInfo& ti, const uint16_t* __restrict__ ring, int ring_rows,
+                                           const uint16_t* __restrict__ wgu, int H, int I,
+                                           uint16_t* __restrict__ a_out, float* __restrict__ gu_save, char* lds) {
+  auto arow = [&](int r) {
+    const int p = ti.pos0 + min(r, ti.rows - 1);
+    return ring + (int64_t)(p % ring_rows) * H;
+  };
+  gemm1_tile_rows<NB, WT, B3>(ti, ring, arow, wgu, H, I, a_out, gu_save, lds);
 }
 
 template <bool B3>
@@ -787,6 +798,7 @@ struct FusedArgs {
   const int32_t* mb_items;    // [nb + 1]
   int item_cap, nb, src_div, H, I, ring_rows;
   int item_local;             // placement: whole items per queue (else unit u to queue u mod 8)
+  int direct;                 // GEMM1 reads its A rows from x through the inverse map: no permute units
   const uint16_t* x;          // token rows (full layer) or routed rows (expert share)
   const int32_t* inv;
   const float* row_w;
@@ -823,7 +835,7 @@ __device__ FusedUnit fused_decode(const FusedArgs& a, int x, int t) {
 #pragma unroll 1
     for (int kind = 0; kind < 3; ++kind) {
       const int b = kind == U_G1 ? j - 1 : kind == U_P ? j : j - 2;
-      if (b < 0 || b >= a.nb) continue;
+      if (b < 0 || b >= a.nb || (kind == U_P && a.direct)) continue;
       if (a.item_local) {
         // whole items: item l of the minibatch (all of its units) to queue l mod 8
         const int per = kind == U_P ? FUSE_PCH : kind == U_G1 ? 2 * a.I / BN : a.H / BN;
@@ -886,7 +898,7 @@ __device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int u,
 // GEMM2 units publish nothing: without B3 (the unit is passed outside the K
 // loop's buffers) they end without waiting for their stores, which then
 // drain under the next unit's ticket, wait and first loads.
-template <bool SHARE, bool B3>
+template <bool SHARE, bool B3, bool DIRECT>
 __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES + 16];
   int* const su = (int*)(lds + (B3 ? 0 : LDS_BYTES));
@@ -899,7 +911,7 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
   while (true) {
     if (wave == 0) {
       const FusedUnit un = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t_next));
-      if (un.kind == U_G1) {
+      if (un.kind == U_G1 && !DIRECT) {
         fused_wait(a.p_done + fused_items_lo(a, un.b) + un.u / ntn1, (uint32_t)FUSE_PCH, a.err);
       } else if (un.kind == U_G2) {
         fused_wait(a.g1_done + fused_items_lo(a, un.b) + un.u / ntn2, (uint32_t)ntn1, a.err);
@@ -933,7 +945,15 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
       }
     } else if (kind == U_G1) {
       const TileInfo ti = fused_tile(a, b, u, ntn1, item);
-      gemm1_tile<BN, true, B3>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
+      if constexpr (DIRECT) {
+        // the item's x rows through the inverse map (token = routed row / src_div)
+        auto arow = [&](int r) {
+          return a.x + (int64_t)(a.inv[ti.pos0 + min(r, ti.rows - 1)] / a.src_div) * a.H;
+        };
+        gemm1_tile_rows<BN, true, B3>(ti, a.x, arow, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
+      } else {
+        gemm1_tile<BN, true, B3>(ti, a.ring, a.ring_rows, a.wgu, a.H, a.I, a.a_buf, a.gu_save, lds);
+      }
     } else {
       const TileInfo ti = fused_tile(a, b, u, ntn2, item);
       gemm2_tile<SHARE>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
@@ -983,6 +1003,7 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   a.I = f.I;
   a.ring_rows = f.ring_rows;
   a.item_local = f.item_local;
+  a.direct = f.direct;
   a.x = f.x;
   a.inv = f.inv;
   a.row_w = f.row_w;
@@ -1005,13 +1026,17 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   const int grid = std::max(FUSE_XCD, n_cu / FUSE_XCD * FUSE_XCD);
   const bool b3 = f.H >= NT3_MIN_K;
   if (!f.full && b3)
-    hipLaunchKernelGGL((fused_forward_kernel<true, true>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fused_forward_kernel<true, true, false>), dim3(grid), dim3(NT), 0, s, a);
   else if (!f.full)
-    hipLaunchKernelGGL((fused_forward_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fused_forward_kernel<true, false, false>), dim3(grid), dim3(NT), 0, s, a);
+  else if (b3 && f.direct)
+    hipLaunchKernelGGL((fused_forward_kernel<false, true, true>), dim3(grid), dim3(NT), 0, s, a);
   else if (b3)
-    hipLaunchKernelGGL((fused_forward_kernel<false, true>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fused_forward_kernel<false, true, false>), dim3(grid), dim3(NT), 0, s, a);
+  else if (f.direct)
+    hipLaunchKernelGGL((fused_forward_kernel<false, false, true>), dim3(grid), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((fused_forward_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fused_forward_kernel<false, false, false>), dim3(grid), dim3(NT), 0, s, a);
 }
 
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,

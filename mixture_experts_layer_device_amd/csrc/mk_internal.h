@@ -190,6 +190,7 @@ struct FusedFwd {
   ItemRange ir;               // all minibatches
   int nb, src_div, H, I, ring_rows, full;
   int item_local;             // whole items per XCD (else units dealt evenly)
+  int direct;                 // GEMM1 reads x rows through the inverse map (no permute, ring unused)
   const uint16_t* x;
   const int32_t* inv;
   const float* row_w;
