@@ -1024,7 +1024,10 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   launch_fill_u32(c, 0u, fused_ctl_words(f.ir.item_cap), s);
   // one workgroup per compute unit, a multiple of the 8 queues
   const int grid = std::max(FUSE_XCD, n_cu / FUSE_XCD * FUSE_XCD);
-  const bool b3 = f.H >= NT3_MIN_K;
+  // GEMM1 units take the three-buffer loop for long contractions, and from
+  // H = 2048 when their A rows come from x (lower latency than ring rows,
+  // so the weights' latency is what the third buffer hides)
+  const bool b3 = f.H >= NT3_MIN_K || (f.direct && f.H >= 2048);
   if (!f.full && b3)
     hipLaunchKernelGGL((fused_forward_kernel<true, true, false>), dim3(grid), dim3(NT), 0, s, a);
   else if (!f.full)
