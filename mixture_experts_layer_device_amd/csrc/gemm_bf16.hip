@@ -398,14 +398,14 @@ __global__ __launch_bounds__(NT) void gemm1_bf16_kernel(ItemRange ir, const uint
 // SHARE: the router-weighted unpermute is fused: out[inv[p]] = bf16(w * y),
 //        one rounding, rows stored straight to arrival order.
 // else : y is kept in fp32 ([p, H]) for the full-layer combine.
-template <bool SHARE>
+template <bool SHARE, bool B3 = false>
 __device__ __forceinline__ void gemm2_tile(const TileInfo& ti, const uint16_t* __restrict__ a,
                                            const uint16_t* __restrict__ wd, int H, int I, float* __restrict__ y32,
                                            uint16_t* __restrict__ out, const int32_t* __restrict__ inv,
                                            const float* __restrict__ row_w, char* lds) {
   auto arow = [&](int r) { return a + (int64_t)(ti.pos0 + min(r, ti.rows - 1)) * I; };
   Acc acc;
-  mainloop_nt(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, ti.rows, lds, acc);
+  mainloop_nt<BN, B3>(arow(0), arow, wd + btile_block(ti.e, ti.n0 / BN, 0, H, I), I, ti.rows, lds, acc);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -956,7 +956,8 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
       }
     } else {
       const TileInfo ti = fused_tile(a, b, u, ntn2, item);
-      gemm2_tile<SHARE>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
+      // with x read directly, GEMM2 units take the three-buffer loop too
+      gemm2_tile<SHARE, B3 && DIRECT>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
     }
     if (kind == U_G2 && !B3) continue;   // nothing to publish, no LDS hand-over
     // publish: every wave's stores complete, then one counter bump
