@@ -35,8 +35,11 @@ constexpr int LDS_BYTES = 2 * STAGE_BYTES > STAGE_LDS_BYTES ? 2 * STAGE_BYTES : 
 constexpr int NT_A_BUFS = 2, NT_B_BUFS = 3;
 constexpr int NT3_LDS_BYTES = (NT_A_BUFS + NT_B_BUFS) * TILE_BYTES;
 static_assert(NT3_LDS_BYTES >= STAGE_LDS_BYTES && NT3_LDS_BYTES <= 160 * 1024, "the LDS of one compute unit");
-// long contractions take the three-buffer K loop
+// GEMM1 over ring rows takes the three-buffer K loop for long contractions
+// (measured slower at K = 2048); GEMM2, dA' and dX from K = 512 (measured
+// faster or the same at K = 768 to 7168)
 constexpr int NT3_MIN_K = 4096;
+constexpr int NT3_MIN_K_L2A = 512;
 
 typedef GAcc Acc;
 
@@ -427,16 +430,16 @@ __device__ __forceinline__ void gemm2_tile(const TileInfo& ti, const uint16_t* _
     });
 }
 
-template <bool SHARE>
+template <bool SHARE, bool B3>
 __global__ __launch_bounds__(NT) void gemm2_bf16_kernel(ItemRange ir, const uint16_t* __restrict__ a,
                                                         const uint16_t* __restrict__ wd, int H, int I,
                                                         float* __restrict__ y32, uint16_t* __restrict__ out,
                                                         const int32_t* __restrict__ inv,
                                                         const float* __restrict__ row_w) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES];
   const int ntn = H / BN;
   for_each_tile(ir, ntn,
-                [&](const TileInfo& ti) { gemm2_tile<SHARE>(ti, a, wd, H, I, y32, out, inv, row_w, lds); });
+                [&](const TileInfo& ti) { gemm2_tile<SHARE, B3>(ti, a, wd, H, I, y32, out, inv, row_w, lds); });
 }
 
 // ------------------------------------------------- backward: dA' + SwiGLU ----
@@ -986,11 +989,19 @@ void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_r
 
 void launch_gemm2_bf16(const ItemRange& ir, const uint16_t* a, const uint16_t* wd, int H, int I, float* y32,
                        uint16_t* out, const int32_t* inv, const float* row_w, int n_cu, hipStream_t s) {
-  if (out)
-    hipLaunchKernelGGL(gemm2_bf16_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv, row_w);
-  else
-    hipLaunchKernelGGL(gemm2_bf16_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv,
+  const bool b3 = I >= NT3_MIN_K_L2A;
+  if (out && b3)
+    hipLaunchKernelGGL((gemm2_bf16_kernel<true, true>), dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv,
                        row_w);
+  else if (out)
+    hipLaunchKernelGGL((gemm2_bf16_kernel<true, false>), dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv,
+                       row_w);
+  else if (b3)
+    hipLaunchKernelGGL((gemm2_bf16_kernel<false, true>), dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out, inv,
+                       row_w);
+  else
+    hipLaunchKernelGGL((gemm2_bf16_kernel<false, false>), dim3(n_cu), dim3(NT), 0, s, ir, a, wd, H, I, y32, out,
+                       inv, row_w);
 }
 
 void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
@@ -1046,7 +1057,7 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
 void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* wdT, int H, int I, const float* gu,
                      const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part, int n_cu,
                      hipStream_t s) {
-  if (H >= NT3_MIN_K)
+  if (H >= NT3_MIN_K_L2A)
     hipLaunchKernelGGL(bwd_dact_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, dye, wdT, H, I, gu, inv, row_w, dgdu,
                        wa, dw_part);
   else
@@ -1056,7 +1067,7 @@ void launch_bwd_dact(const ItemRange& ir, const uint16_t* dye, const uint16_t* w
 
 void launch_bwd_dx(const ItemRange& ir, const uint16_t* dgdu, const uint16_t* wguT, int H, int I,
                    const int32_t* inv, uint16_t* dX, float* dx32, int n_cu, hipStream_t s) {
-  const bool b3 = 2 * I >= NT3_MIN_K;
+  const bool b3 = 2 * I >= NT3_MIN_K_L2A;
   if (dX && b3)
     hipLaunchKernelGGL((bwd_dx_kernel<true, true>), dim3(n_cu), dim3(NT), 0, s, ir, dgdu, wguT, H, I, inv, dX, dx32);
   else if (dX)
