@@ -77,9 +77,16 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
             # the floor of a design without the fp32 y round trip
             w["combine_y_bf16"] = (0.0, R * H * 2 + T * H * 2 + R * 8)
         # the fused forward: permute, GEMM1 and GEMM2 in one launch (the full
-        # layer's combine stays a launch of its own)
-        parts = [w[p] for p in ("permute", "gemm1", "gemm2")]
-        w["fused_fwd"] = (sum(f for f, _ in parts), sum(b for _, b in parts))
+        # layer's combine stays a launch of its own); the full layer's launch
+        # has no permute: its GEMM1 reads the token rows through the inverse
+        # map, x read once
+        if share:
+            parts = [w[p] for p in ("permute", "gemm1", "gemm2")]
+            w["fused_fwd"] = (sum(f for f, _ in parts), sum(b for _, b in parts))
+        else:
+            g1f, g1b = w["gemm1"]
+            g1b += T * H * 2 - R * H * (ab + sc)
+            w["fused_fwd"] = (g1f + w["gemm2"][0], g1b + w["gemm2"][1])
     else:
         # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
         # (MXFP8: read twice, written as bf16 rows and as codes + scales)
