@@ -898,9 +898,11 @@ __device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int u,
 // are ready, so the atomic's latency hides behind the unit; per queue a
 // workgroup's tickets still increase, and a unit depends only on units of
 // earlier segments, so the earliest unfinished unit is always running.
-// GEMM2 units publish nothing: without B3 (the unit is passed outside the K
-// loop's buffers) they end without waiting for their stores, which then
-// drain under the next unit's ticket, wait and first loads.
+// GEMM2 units publish nothing, and no wave touches the LDS after a GEMM2
+// unit's last barrier (the K loops read their last stage before it; the
+// expert share's staged epilogue ends with one), so they end without
+// waiting for their stores, which then drain under the next unit's ticket,
+// wait and first loads; the next unit's hand-over in the LDS is safe.
 template <bool SHARE, bool B3, bool DIRECT>
 __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[B3 ? NT3_LDS_BYTES : LDS_BYTES + 16];
@@ -962,7 +964,7 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
       // with x read directly, GEMM2 units take the three-buffer loop too
       gemm2_tile<SHARE, B3 && DIRECT>(ti, a.a_buf, a.wd, a.H, a.I, a.y32, a.out, a.inv, a.row_w, lds);
     }
-    if (kind == U_G2 && !B3) continue;   // nothing to publish, no LDS hand-over
+    if (kind == U_G2) continue;   // nothing to publish
     // publish: every wave's stores complete, then one counter bump
     wait_all_mem();
     __syncthreads();
