@@ -740,10 +740,14 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
   // expert share: GEMM2 writes w*y straight to arrival order (one rounding);
   // full layer: GEMM2 keeps y in fp32 and the combine sums the k rows
   uint16_t* out_fused = share ? (uint16_t*)out : nullptr;
-  if (ws->cfg.fused_forward && nb <= ring_mbs) {
-    // one persistent launch for permute, GEMM1 and GEMM2, overlapping
-    // across minibatches (the ring holds them all); the full layer's combine
-    // follows as its own launch
+  // full layer: GEMM1 can gather its A rows straight from the token rows
+  // (each token row serves k experts and stays in the last-level cache), so
+  // the fused launch writes no ring and needs none
+  const bool direct = !share && (int64_t)(R / kk) * H * 2 <= ((int64_t)1 << 32);
+  if (ws->cfg.fused_forward && (direct || nb <= ring_mbs)) {
+    // one persistent launch for GEMM1 and GEMM2 (and the permute into the
+    // ring, which then holds every minibatch), minibatches overlapping; the
+    // full layer's combine follows as its own launch
     FusedFwd f;
     f.ir = item_range(ws, sc, 0, nb);
     f.nb = nb;
@@ -758,10 +762,8 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
     // in that L2); with more, spread every segment's units evenly so that a
     // panel stays on one XCD across the expert's items
     f.item_local = (int64_t)std::min(MB, R) < (int64_t)2 * MK_TILE_M * ws->E;
-    // full layer: GEMM1 gathers its A rows straight from the token rows
-    // (each token row serves k experts and stays in the last-level cache),
-    // so the ring is not written; a backward of this schedule replays them
-    f.direct = !share && (int64_t)(R / kk) * H * 2 <= ((int64_t)1 << 32);
+    // without the ring a backward of this schedule replays the x rows
+    f.direct = direct;
     if (f.direct) sc->fwd_ring_epoch = 0;
     f.x = x;
     f.inv = st.inv;

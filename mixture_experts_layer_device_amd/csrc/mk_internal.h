@@ -182,10 +182,11 @@ void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_r
                        int n_cu, hipStream_t s);
 // The bf16 forward's permute, GEMM1 + SwiGLU and GEMM2 in one persistent
 // launch, minibatches overlapping (the ring must hold every minibatch: no
-// slot reuse inside the launch); ctl is fused_ctl_words(item_cap) words of
-// device memory (zeroed by the launcher), err the schedule's error word.
-// The full layer's combine (fp32 y rows from every XCD) is the caller's
-// next launch.
+// slot reuse inside the launch), or with direct set, GEMM1 reading the x
+// rows through the inverse map and no permute (the ring untouched); ctl is
+// fused_ctl_words(item_cap) words of device memory (zeroed by the
+// launcher), err the schedule's error word.  The full layer's combine (fp32
+// y rows from every XCD) is the caller's next launch.
 struct FusedFwd {
   ItemRange ir;               // all minibatches
   int nb, src_div, H, I, ring_rows, full;

@@ -1,9 +1,12 @@
-"""The fused forward (mk_config.fused_forward: permute, GEMM1 + SwiGLU, GEMM2
-and the full layer's combine in one persistent launch, minibatches
-overlapping through device counters) against the phase-by-phase launches,
+"""The fused forward (mk_config.fused_forward: permute, GEMM1 + SwiGLU and
+GEMM2 in one persistent launch, minibatches overlapping through device
+counters; the full layer's combine follows as a launch of its own) against
+the phase-by-phase launches,
 bit for bit, and against the oracle: several minibatches, one minibatch, the
-expert share and the full layer.  A ring that cannot hold every minibatch
-falls back to the phase-by-phase launches."""
+expert share and the full layer.  In the expert share a ring that cannot
+hold every minibatch falls back to the phase-by-phase launches; the full
+layer's fused launch reads the token rows through the inverse map and needs
+no ring, so it runs fused whatever the ring holds."""
 import numpy as np
 import pytest
 import torch
@@ -66,8 +69,8 @@ def test_fused_share_equals_phase_by_phase(name, MB, ring_mbs):
 
 
 @pytest.mark.parametrize("name,MB,ring_mbs", [("tiny", 128, None), ("tiny", 0, None), ("full", 0, None),
-                                               ("full", 8192, None)],
-                         ids=["tiny_4mb", "tiny_one_mb", "full_one_mb", "full_4mb"])
+                                               ("full", 8192, None), ("tiny", 128, 1)],
+                         ids=["tiny_4mb", "tiny_one_mb", "full_one_mb", "full_4mb", "tiny_4mb_ring1"])
 def test_fused_full_layer_equals_phase_by_phase(name, MB, ring_mbs):
     inp = workloads.make_full_layer(name)
     sh = inp["shape"]
