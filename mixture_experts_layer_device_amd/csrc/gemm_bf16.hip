@@ -778,7 +778,9 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
 // workgroups take its units in a fixed order from its own ticket; per
 // iteration j: GEMM1 of minibatch j-1, permute of j, GEMM2 of j-2.
 // Dependencies (device counters): a GEMM1 tile waits for its item's 4
-// permute chunks, a GEMM2 tile for its item's GEMM1 tiles.  Every wait
+// permute chunks, a GEMM2 tile for its item's GEMM1 tiles.  With direct set
+// (the full layer: its token rows are local), there are no permute units
+// and GEMM1 tiles read the x rows through the inverse map.  Every wait
 // points at a unit of an earlier iteration, so the unit with the smallest
 // iteration never waits and every queue drains; waits are bounded anyway
 // (about 0.25 s, then MK_DEVERR_WAIT_TIMEOUT and on).
