@@ -757,10 +757,11 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
     f.ring_rows = ws->ring_rows;
     f.full = !share;
     // placement of the units on the XCDs: with fewer than 2 tiles of rows
-    // per expert in a minibatch on average, a weight panel serves about one
-    // item, so keep each item's units on one XCD (its ring and a rows stay
-    // in that L2); with more, spread every segment's units evenly so that a
-    // panel stays on one XCD across the expert's items
+    // per expert in a minibatch on average, contiguous runs of whole items
+    // per XCD (an item's ring and a rows stay in that L2, and an expert's
+    // few items share its weight panels there); with more, spread every
+    // segment's units evenly so that a panel stays on one XCD across the
+    // expert's items
     f.item_local = (int64_t)std::min(MB, R) < (int64_t)2 * MK_TILE_M * ws->E;
     // without the ring a backward of this schedule replays the x rows
     f.direct = direct;

@@ -768,9 +768,10 @@ __global__ __launch_bounds__(NT) void wgrad_kernel(WgradArgs w, WgradOperands<MO
 // tile) goes to queue u mod 8, so every queue gets an equal share (to one
 // unit) and a weight column panel stays in one queue, or two, across the
 // items of an expert; or (item_local, for experts with about one item per
-// minibatch, whose panels serve one item anyway) item l with all of its
-// units goes to queue l mod 8, so its ring rows and a rows are read from the
-// L2 that wrote them.  Queue x is taken by
+// minibatch) queue x takes a contiguous run of items with all of their
+// units: an item's ring rows and a rows are read from the L2 that wrote
+// them, and the items of one expert (consecutive in the item list) share
+// their weight panels in one L2.  Queue x is taken by
 // the workgroups whose index is x mod 8 -- the workgroups the hardware
 // places on XCD x, since a dispatch deals its workgroups to the 8 XCDs in
 // turn -- so a panel is read into one XCD's L2.  (Only speed rests on that
@@ -842,11 +843,13 @@ __device__ FusedUnit fused_decode(const FusedArgs& a, int x, int t) {
       const int b = kind == U_G1 ? j - 1 : kind == U_P ? j : j - 2;
       if (b < 0 || b >= a.nb || (kind == U_P && a.direct)) continue;
       if (a.item_local) {
-        // whole items: item l of the minibatch (all of its units) to queue l mod 8
+        // whole items: queue x takes the contiguous run of items
+        // [x ni / 8, (x+1) ni / 8) of the minibatch, all of their units
         const int per = kind == U_P ? FUSE_PCH : kind == U_G1 ? 2 * a.I / BN : a.H / BN;
         const int ni = fused_items(a, b);
-        const int nx = ni > x ? (ni - x + FUSE_XCD - 1) / FUSE_XCD * per : 0;
-        if (t < nx) return FusedUnit{kind, b, (x + FUSE_XCD * (t / per)) * per + t % per};
+        const int lo = (int)((int64_t)x * ni / FUSE_XCD), hi = (int)((int64_t)(x + 1) * ni / FUSE_XCD);
+        const int nx = (hi - lo) * per;
+        if (t < nx) return FusedUnit{kind, b, lo * per + t};
         t -= nx;
       } else {
         const int n = fused_units(a, kind, b);

@@ -190,7 +190,7 @@ void launch_gemm1_bf16(const ItemRange& ir, const uint16_t* ring, int32_t ring_r
 struct FusedFwd {
   ItemRange ir;               // all minibatches
   int nb, src_div, H, I, ring_rows, full;
-  int item_local;             // whole items per XCD (else units dealt evenly)
+  int item_local;             // contiguous runs of whole items per XCD (else units dealt evenly)
   int direct;                 // GEMM1 reads x rows through the inverse map (no permute, ring unused)
   const uint16_t* x;
   const int32_t* inv;
