@@ -77,9 +77,9 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
             # the floor of a design without the fp32 y round trip
             w["combine_y_bf16"] = (0.0, R * H * 2 + T * H * 2 + R * 8)
         # the fused forward: permute, GEMM1 and GEMM2 in one launch (the full
-        # layer's combine stays a launch of its own); the full layer's launch
-        # has no permute: its GEMM1 reads the token rows through the inverse
-        # map, x read once
+        # layer's combine stays a launch of its own); in the full layer's
+        # launch GEMM1 gathers the token rows through the inverse map instead
+        # of a permute, x read once
         if share:
             parts = [w[p] for p in ("permute", "gemm1", "gemm2")]
             w["fused_fwd"] = (sum(f for f, _ in parts), sum(b for _, b in parts))
@@ -466,9 +466,10 @@ def main():
         "metric": METRIC, "value": main["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": main["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "full single-GPU MoE layer forward: route + build_schedule + permute + expert "
-                               "GEMMs (SwiGLU) + combine; T=4096 tokens, H=2048, I=768, 128 experts, top-8 "
-                               "renormalised softmax router with per-expert logit bias",
+        "config": {"workload": "full single-GPU MoE layer forward: route + build_schedule + permute (the "
+                               "fused launch gathers the token rows inside GEMM1) + expert GEMMs (SwiGLU) + "
+                               "combine; T=4096 tokens, H=2048, I=768, 128 experts, top-8 renormalised "
+                               "softmax router with per-expert logit bias",
                    "tokens": 4096, "routed_rows": 32768, "H": 2048, "I": 768, "E": 128, "k": 8,
                    "forward_launches": "one fused persistent launch" if a.main_fused else "one launch per phase"},
         "gemm_tflops": main["gemm_tflops"],
