@@ -17,7 +17,9 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work on it: they never synchronise with the host, never copy
  *    device data to the host and never size a launch from device-side counts.
- *  - bf16 tensors are raw 16-bit bf16 patterns (uint16), row-major.
+ *  - bf16 tensors are raw 16-bit bf16 patterns (uint16), row-major.  Rows
+ *    are read and written 16 bytes at a time: every tensor starts 16-byte
+ *    aligned.
  *  - Return value: MK_OK (0) or a negative MK_ERR_* code, detected on the
  *    host before anything is enqueued.  Problems only the device can see
  *    set bits in the schedule's device error word (MK_DEVERR_*); read it
@@ -301,7 +303,11 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_u
  *                products of the dequantised operands).
  * sched: built by mk_build_schedule on this workspace (MK_ERR_STATE if not).
  * The forward overwrites the workspace's ring; the schedule records the mode,
- * fwd_ctx_dev and that its rows are now the ring's, for its backward.
+ * fwd_ctx_dev and that its rows are now the ring's, for its backward.  In
+ * MK_FULL_LAYER mode with mk_config.fused_forward (bf16), GEMM1 instead
+ * gathers the token rows straight from x_src_dev through the schedule's
+ * inverse map and the ring is left as it was; a backward of this schedule
+ * then gathers the x rows again, as for minibatches evicted from the ring.
  */
 int mk_forward(mk_workspace* ws, mk_schedule* sched, int32_t mode, const void* x_src_dev,
                const float* row_w_dev, const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
