@@ -895,10 +895,11 @@ __device__ __forceinline__ TileInfo fused_tile(const FusedArgs& a, int b, int u,
 // ticket (lane 0's atomic, broadcast), decodes it and waits, every wave
 // reads the unit back from LDS as a scalar, and only the counter bumps are
 // single-lane; no lane of a wave ever takes a different path to a barrier.
-// B3: GEMM1 units (contraction H) take the three-buffer K loop; the LDS is
-// then all in use by the K loop, and the unit is passed in its first bytes
-// (free between units: every unit ends at a barrier after its last LDS
-// access, and a second barrier below comes before the next unit's copies).
+// B3: GEMM1 units (contraction H) take the three-buffer K loop, and with
+// DIRECT the GEMM2 units too; the LDS is then all in use by the K loops, and
+// the unit is passed in its first bytes (free between units: every unit
+// ends at a barrier after its last LDS access, and a second barrier below
+// comes before the next unit's copies).
 // A workgroup takes its next ticket as soon as its current unit's inputs
 // are ready, so the atomic's latency hides behind the unit; per queue a
 // workgroup's tickets still increase, and a unit depends only on units of
