@@ -7,6 +7,8 @@ expert share and the full layer.  In the expert share a ring that cannot
 hold every minibatch falls back to the phase-by-phase launches; the full
 layer's fused launch reads the token rows through the inverse map and needs
 no ring, so it runs fused whatever the ring holds."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -126,3 +128,42 @@ def test_fused_forward_context_feeds_the_backward():
     for k in g[0]:
         assert torch.equal(g[0][k], g[1][k]), k
 
+
+
+@pytest.mark.parametrize("name,MB", [("tiny", 128), ("tiny", 0)], ids=["tiny_4mb", "tiny_one_mb"])
+def test_fused_full_layer_backward_replays_the_token_rows(name, MB):
+    """The full layer's fused forward gathers the token rows through the
+    inverse map and leaves the ring alone, so the backward of its schedule
+    gathers the x rows again: its forward context and every gradient
+    (router included) equal those after the phase-by-phase forward, which
+    left the rows in the ring, bit for bit."""
+    # (the backward needs I a multiple of 256)
+    inp = workloads.make_full_layer(dataclasses.replace(workloads.FULL_LAYER[name], I=256))
+    sh = inp["shape"]
+    say(f"[fused forward] full layer {name} (I=256) backward after the fused forward, MB={MB}")
+    res = []
+    for fused in (True, False):
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, minibatch_rows=MB,
+                     enable_backward=True, fused_forward=fused)
+        x, wr = dev(inp["x"]), dev(inp["w_router"])
+        bias = dev(inp["bias"]) if inp["bias"] is not None else None
+        packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+        idx, w = L.route(x, wr, bias, sh.T)
+        L.build_schedule(idx.view(-1), sh.R)
+        ctx = L.new_fwd_ctx()
+        B.mk_timing_read(L.ws)
+        B.mk_timing_enable(L.ws, True)
+        out = L.forward(B.MK_FULL_LAYER, x, w.view(-1), packed, sh.T, fwd_ctx=ctx)
+        torch.cuda.synchronize()
+        B.mk_timing_enable(L.ws, False)
+        assert B.mk_timing_read(L.ws)["fused_fwd"][1] == (1 if fused else 0)
+        g = L.backward_layer(ctx, x, wr, bias, idx, w, packed, dev(inp["dY"]), sh.T)
+        torch.cuda.synchronize()
+        assert L.device_error() == 0
+        res.append((out.clone(), ctx.clone(), {k: v.clone() for k, v in g.items() if v is not None}))
+        L.close()
+    assert torch.equal(res[0][0], res[1][0]), "outputs differ"
+    assert torch.equal(res[0][1], res[1][1]), "forward contexts differ"
+    assert res[0][2].keys() == res[1][2].keys()
+    for k in res[0][2]:
+        assert torch.equal(res[0][2][k], res[1][2][k]), k
