@@ -421,6 +421,20 @@ int mk_timing_phases(mk_workspace* ws, uint32_t phase_mask);
  * uint32). */
 int mk_device_error(const mk_schedule* sched, uint32_t* dst_dev, void* stream);
 
+/*
+ * For tests of the fused forward's failure path (not for production use):
+ * every dependency wait of the fused launch (mk_config.fused_forward) is a
+ * bounded poll of a device counter.  spin_limit > 0 sets the bound (in polls,
+ * each a counter read and a short sleep; 0 restores the default, about a
+ * quarter of a second); unreachable = 1 makes each wait's target one more
+ * than its producers ever count, so every wait of the launch ends at its
+ * bound.  Such a launch sets MK_DEVERR_WAIT_TIMEOUT in the schedule's error
+ * word and runs to its end with every access in bounds; its results are
+ * invalid.  Applies to the workspace's later forwards.  Returns MK_OK,
+ * MK_ERR_NULL, or MK_ERR_CONFIG (spin_limit < 0 or unreachable not 0/1).
+ */
+int mk_debug_fused_waits(mk_workspace* ws, int32_t spin_limit, int32_t unreachable);
+
 /* Minibatch floor of the two-wave rule ([MTP] "Three design decisions that
  * matter", overlap granularity): ceil(2 * n_cu * tile_m * tile_n / min(2I, H)). */
 int64_t mk_two_wave_rows(int32_t H, int32_t I, int32_t n_cu, int32_t tile_m, int32_t tile_n);

@@ -79,6 +79,7 @@ _SIGS = {
     "mk_backward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mk_backward_layer": (ctypes.c_int, [_vp] * 18),
     "mk_device_error": (ctypes.c_int, [_vp, _vp, _vp]),
+    "mk_debug_fused_waits": (ctypes.c_int, [_vp, _i32, _i32]),
     "mk_timing_enable": (ctypes.c_int, [_vp, _i32]),
     "mk_timing_phases": (ctypes.c_int, [_vp, ctypes.c_uint32]),
     "mk_timing_read": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_i32)]),
@@ -217,6 +218,10 @@ def mk_backward_layer(ws, sched, fwd_ctx, x, w_router, bias, topk_idx, topk_w, p
 
 def mk_device_error(sched, dst, stream=None):
     _check("mk_device_error", lib.mk_device_error(sched, _p(dst), _s(stream)))
+
+
+def mk_debug_fused_waits(ws, spin_limit: int = 0, unreachable: bool = False) -> None:
+    _check("mk_debug_fused_waits", lib.mk_debug_fused_waits(ws, int(spin_limit), int(unreachable)))
 
 
 def mk_timing_enable(ws, on: bool) -> None:

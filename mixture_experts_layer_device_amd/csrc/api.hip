@@ -766,6 +766,8 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
     // without the ring a backward of this schedule replays the x rows
     f.direct = direct;
     if (f.direct) sc->fwd_ring_epoch = 0;
+    f.wait_spins = ws->dbg_wait_spins;
+    f.wait_extra = ws->dbg_wait_extra;
     f.x = x;
     f.inv = st.inv;
     f.row_w = row_w;
@@ -858,6 +860,14 @@ int mk_backward_layer(mk_workspace* ws, const mk_schedule* sc, const void* fwd_c
 int mk_timing_enable(mk_workspace* ws, int32_t on) {
   if (!ws) return MK_ERR_NULL;
   ws->timing = on ? 1 : 0;
+  return MK_OK;
+}
+
+int mk_debug_fused_waits(mk_workspace* ws, int32_t spin_limit, int32_t unreachable) {
+  if (!ws) return MK_ERR_NULL;
+  if (spin_limit < 0 || (unreachable != 0 && unreachable != 1)) return MK_ERR_CONFIG;
+  ws->dbg_wait_spins = spin_limit;
+  ws->dbg_wait_extra = unreachable;
   return MK_OK;
 }
 

@@ -805,6 +805,8 @@ struct FusedArgs {
   int item_cap, nb, src_div, H, I, ring_rows;
   int item_local;             // placement: whole items per queue (else unit u to queue u mod 8)
   int direct;                 // GEMM1 reads its A rows from x through the inverse map: no permute units
+  int wait_spins;             // bound of a dependency wait, in polls
+  uint32_t wait_extra;        // added to every wait's target (0; 1 in tests of the timeout path)
   const uint16_t* x;          // token rows (full layer) or routed rows (expert share)
   const int32_t* inv;
   const float* row_w;
@@ -863,10 +865,12 @@ __device__ FusedUnit fused_decode(const FusedArgs& a, int x, int t) {
 }
 
 // Wave 0 (all of its lanes, so the loop is uniform): wait until *p >=
-// target.  The wait is bounded (about a quarter of a second); once any wait
-// of the launch has timed out (the error bit is set) the others stop
-// waiting too, so a launch whose counters went wrong still ends quickly.
-__device__ __forceinline__ void fused_wait(const uint32_t* p, uint32_t target, uint32_t* err) {
+// target.  The wait is bounded (limit polls, by default about a quarter of
+// a second); once any wait of the launch has timed out (the error bit is
+// set) the others stop waiting too, so a launch whose counters went wrong
+// still ends quickly.
+constexpr int FUSE_WAIT_POLLS = 1 << 20;
+__device__ __forceinline__ void fused_wait(const uint32_t* p, uint32_t target, uint32_t* err, int limit) {
   int spins = 0;
   while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
          target) {
@@ -876,7 +880,7 @@ __device__ __forceinline__ void fused_wait(const uint32_t* p, uint32_t target, u
         (__builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
          MK_DEVERR_WAIT_TIMEOUT))
       break;
-    if (spins >= (1 << 20)) {
+    if (spins >= limit) {
       if ((threadIdx.x & 63) == 0) atomicOr(err, MK_DEVERR_WAIT_TIMEOUT);
       break;
     }
@@ -923,9 +927,11 @@ __global__ __launch_bounds__(NT) void fused_forward_kernel(FusedArgs a) {
     if (wave == 0) {
       const FusedUnit un = fused_decode(a, x, (int)__builtin_amdgcn_readfirstlane(t_next));
       if (un.kind == U_G1 && !DIRECT) {
-        fused_wait(a.p_done + fused_items_lo(a, un.b) + un.u / ntn1, (uint32_t)FUSE_PCH, a.err);
+        fused_wait(a.p_done + fused_items_lo(a, un.b) + un.u / ntn1, (uint32_t)FUSE_PCH + a.wait_extra, a.err,
+                   a.wait_spins);
       } else if (un.kind == U_G2) {
-        fused_wait(a.g1_done + fused_items_lo(a, un.b) + un.u / ntn2, (uint32_t)ntn1, a.err);
+        fused_wait(a.g1_done + fused_items_lo(a, un.b) + un.u / ntn2, (uint32_t)ntn1 + a.wait_extra, a.err,
+                   a.wait_spins);
       }
       if (un.kind != U_NONE && lane == 0) t_next = atomicAdd(a.ticket + 64 * x, 1u);
       if (lane == 0) {
@@ -1024,6 +1030,8 @@ void launch_fused_forward_bf16(const FusedFwd& f, int n_cu, hipStream_t s) {
   a.ring_rows = f.ring_rows;
   a.item_local = f.item_local;
   a.direct = f.direct;
+  a.wait_spins = f.wait_spins > 0 ? f.wait_spins : FUSE_WAIT_POLLS;
+  a.wait_extra = (uint32_t)f.wait_extra;
   a.x = f.x;
   a.inv = f.inv;
   a.row_w = f.row_w;

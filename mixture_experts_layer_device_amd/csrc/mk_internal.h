@@ -58,6 +58,7 @@ struct mk_workspace {
   uint64_t ring_epoch;        // bumped by every forward that writes the ring
   int32_t max_rows, H, I, E, k;
   int32_t MB, ring_rows, row_bytes, nb_max, cpm, item_cap, n_cu, device;
+  int32_t dbg_wait_spins, dbg_wait_extra;   // mk_debug_fused_waits (0, 0: the default bound)
   int64_t npos;               // nb_max * MB sorted positions
   // device memory
   void* base;
@@ -192,6 +193,8 @@ struct FusedFwd {
   int nb, src_div, H, I, ring_rows, full;
   int item_local;             // contiguous runs of whole items per XCD (else units dealt evenly)
   int direct;                 // GEMM1 reads x rows through the inverse map (no permute, ring unused)
+  int wait_spins;             // bound of each dependency wait in polls (0: the default)
+  int wait_extra;             // added to every wait's target (tests of the timeout path)
   const uint16_t* x;
   const int32_t* inv;
   const float* row_w;

@@ -140,3 +140,7 @@ def test_fused_forward_needs_bf16():
     with pytest.raises(B.MkError) as ei:
         B.mk_workspace_create(c, 4096, 256, 256, 8, 2)
     assert ei.value.status == B.MK_ERR_CONFIG
+
+
+def test_debug_fused_waits_rejects_a_null_workspace():
+    assert B.lib.mk_debug_fused_waits(None, 0, 0) == B.MK_ERR_NULL

@@ -167,3 +167,48 @@ def test_fused_full_layer_backward_replays_the_token_rows(name, MB):
     assert res[0][2].keys() == res[1][2].keys()
     for k in res[0][2]:
         assert torch.equal(res[0][2][k], res[1][2][k]), k
+
+
+@pytest.mark.parametrize("mode", ["full", "share"])
+def test_fused_wait_bound_reports_timeout_and_recovers(mode):
+    """The fused launch's dependency waits are bounded polls of device
+    counters.  Forced from the host (mk_debug_fused_waits: a bound of 64 polls
+    and targets one above what the producers count), every wait ends at its
+    bound, the launch runs to its end, and the schedule's error word carries
+    MK_DEVERR_WAIT_TIMEOUT; with the hook cleared, the next schedule build
+    clears the word and the forward gives the same output as before."""
+    if mode == "full":
+        inp = workloads.make_full_layer("tiny")
+        sh = inp["shape"]
+        MB = 128
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, minibatch_rows=MB,
+                     fused_forward=True)
+        x = dev(inp["x"])
+        packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]))
+        bias = dev(inp["bias"]) if inp["bias"] is not None else None
+        idx, w = L.route(x, dev(inp["w_router"]), bias, sh.T)
+        rows, w, n, kind = idx.view(-1), w.view(-1), sh.T, B.MK_FULL_LAYER
+    else:
+        inp = workloads.make_expert_share("small")
+        sh = inp["shape"]
+        MB = 256
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, minibatch_rows=MB, fused_forward=True)
+        x, w = dev(inp["x"]), dev(inp["row_w"])
+        packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]))
+        rows, n, kind = dev(inp["row_expert"]), sh.R, B.MK_EXPERT_SHARE
+    say(f"[fused forward] bounded waits forced to time out: {mode} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    L.build_schedule(rows, sh.R)
+    ref = L.forward(kind, x, w, packed, n).clone()
+    torch.cuda.synchronize()
+    assert L.device_error() == 0
+    B.mk_debug_fused_waits(L.ws, 64, True)
+    L.forward(kind, x, w, packed, n)
+    torch.cuda.synchronize()
+    assert L.device_error() & B.MK_DEVERR_WAIT_TIMEOUT
+    B.mk_debug_fused_waits(L.ws, 0, False)
+    L.build_schedule(rows, sh.R)
+    out = L.forward(kind, x, w, packed, n)
+    torch.cuda.synchronize()
+    assert L.device_error() == 0
+    assert torch.equal(out, ref)
+    L.close()
