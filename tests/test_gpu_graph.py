@@ -1,13 +1,14 @@
-"""The forward step captured as one HIP graph and replayed.
+"""The layer's step captured as one HIP graph and replayed.
 
 Every call of the boundary only enqueues work on the caller's stream: no
 host synchronisation, no device-to-host copy, no allocation and no memset
 (counters and flags are cleared by kernels) -- the property that lets a
 training step run without the CPU in the loop ([MTP] "Three design decisions
 that matter": the ring removes CPU-GPU synchronisation).  Here route,
-schedule build, forward and combine are captured from one stream into a
-graph; each replay, with eager work and different inputs in between, must
-equal the eager step bit for bit.
+schedule build, forward and combine (and in the training step the backward
+with the router) are captured from one stream into a graph; each replay,
+with eager work and different inputs in between, must equal the eager step
+bit for bit.
 """
 import numpy as np
 import pytest
@@ -105,5 +106,37 @@ def test_expert_share_wrapping_ring_as_one_graph():
         B.mk_forward(L.ws, L.sched.handle, B.MK_EXPERT_SHARE, x, w, packed, out, None, s)
 
     _replays_match(step, [out], [rows], [rows_other])
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_full_layer_training_step_as_one_graph():
+    """Forward with its context and the backward including the router, one graph."""
+    inp = workloads.make_full_layer("full")
+    sh = inp["shape"]
+    say(f"[graph] full layer forward + backward T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k}")
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, fused_forward=True,
+                 enable_backward=True)
+    x, wr, bias, dY = dev(inp["x"]), dev(inp["w_router"]), dev(inp["bias"]), dev(inp["dY"])
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
+    idx = torch.empty((sh.T, sh.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((sh.T, sh.k), **f32)
+    ctx = L.new_fwd_ctx()
+    dX = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
+    dWg, dWu = torch.empty((sh.E, sh.I, sh.H), **f32), torch.empty((sh.E, sh.I, sh.H), **f32)
+    dWd, dWr = torch.empty((sh.E, sh.H, sh.I), **f32), torch.empty((sh.E, sh.H), **f32)
+    db, dw = torch.empty((sh.E,), **f32), torch.empty((sh.R,), **f32)
+
+    def step(s):
+        B.mk_route(L.ws, x, wr, bias, sh.T, idx, wts, s)
+        B.mk_build_schedule(L.ws, L.sched.handle, idx, sh.R, s)
+        B.mk_forward(L.ws, L.sched.handle, B.MK_FULL_LAYER, x, wts, packed, out, ctx, s)
+        B.mk_backward_layer(L.ws, L.sched.handle, ctx, x, wr, bias, idx, wts, packed, dY, dX, dWg, dWu, dWd, dWr,
+                            db, dw, s)
+
+    _replays_match(step, [out, idx, wts, ctx, dX, dWg, dWu, dWd, dWr, db, dw], [x, dY],
+                   [torch.roll(x, shifts=1, dims=0), torch.roll(dY, shifts=3, dims=0)])
     assert L.device_error() == 0
     L.close()
