@@ -27,14 +27,20 @@ def _replays_match(step, outputs, inputs, other_inputs):
     """Eager results on the inputs and on other_inputs, then the captured
     step replayed three times: on the inputs, on other_inputs copied into
     the same buffers, and on the inputs again (outputs cleared before each
-    replay, an eager step on the other inputs between the replays)."""
+    run, so that bytes a step does not write -- the forward context of the
+    padding positions -- read the same; an eager step on the other inputs
+    between the replays)."""
     s = torch.cuda.current_stream()
     saved = [t.clone() for t in inputs]
+    for t in outputs:
+        t.zero_()
     step(s)
     torch.cuda.synchronize()
     ref = [t.clone() for t in outputs]
     for t, o in zip(inputs, other_inputs):
         t.copy_(o)
+    for t in outputs:
+        t.zero_()
     step(s)
     torch.cuda.synchronize()
     ref_other = [t.clone() for t in outputs]
@@ -138,5 +144,34 @@ def test_full_layer_training_step_as_one_graph():
 
     _replays_match(step, [out, idx, wts, ctx, dX, dWg, dWu, dWd, dWr, db, dw], [x, dY],
                    [torch.roll(x, shifts=1, dims=0), torch.roll(dY, shifts=3, dims=0)])
+    assert L.device_error() == 0
+    L.close()
+
+
+def test_expert_share_mxfp8_training_step_as_one_graph():
+    """MXFP8: the quantising permute, the MXFP8 GEMMs, and the backward with
+    MXFP8 weight gradients (operand quantisers included), one graph."""
+    inp = workloads.make_expert_share("small")
+    sh = inp["shape"]
+    MB = 256
+    say(f"[graph] expert share MXFP8 forward + backward R={sh.R} H={sh.H} I={sh.I} E={sh.E} MB={MB}")
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=8, max_rows=sh.R, minibatch_rows=MB, precision="mxfp8",
+                 enable_backward=True, wgrad_mxfp8=True)
+    x, w, rows, dY = dev(inp["x"]), dev(inp["row_w"]), dev(inp["row_expert"]), dev(inp["dY"])
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
+    ctx = L.new_fwd_ctx()
+    dX = torch.empty((sh.R, sh.H), dtype=torch.int16, device="cuda")
+    dWg, dWu = torch.empty((sh.E, sh.I, sh.H), **f32), torch.empty((sh.E, sh.I, sh.H), **f32)
+    dWd, dw = torch.empty((sh.E, sh.H, sh.I), **f32), torch.empty((sh.R,), **f32)
+
+    def step(s):
+        B.mk_build_schedule(L.ws, L.sched.handle, rows, sh.R, s)
+        B.mk_forward(L.ws, L.sched.handle, B.MK_EXPERT_SHARE, x, w, packed, out, ctx, s)
+        B.mk_backward(L.ws, L.sched.handle, B.MK_EXPERT_SHARE, ctx, x, w, packed, dY, dX, dWg, dWu, dWd, dw, s)
+
+    _replays_match(step, [out, ctx, dX, dWg, dWu, dWd, dw], [x, dY],
+                   [torch.roll(x, shifts=5, dims=0), torch.roll(dY, shifts=2, dims=0)])
     assert L.device_error() == 0
     L.close()
