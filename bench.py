@@ -41,8 +41,9 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma-separated workloads to run (full, full_unfused, full_fused, ep64_fwd, ep64_fwd_fused, "
-                         "ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, ep_bwd_mxfp8_dgrad, full_bwd)")
+                    help="comma-separated workloads to run (full, full_unfused, full_fused, full_mxfp8, ep64_fwd, "
+                         "ep64_fwd_fused, ep64_mxfp8, ep_bwd, ep_bwd_mxfp8, ep_bwd_mxfp8_dgrad, full_bwd, "
+                         "full_bwd_mxfp8)")
     ap.add_argument("--main-fused", type=int, default=1,
                     help="1: the main line runs the forward as one fused launch (mk_config.fused_forward), "
                          "0: one launch per phase")
@@ -279,8 +280,9 @@ def main():
         }
 
     results = {}
-    want = set(a.only.split(",")) if a.only else {"full", "full_unfused", "ep64_fwd", "ep64_fwd_fused",
-                                                   "ep64_mxfp8", "ep_bwd", "ep_bwd_mxfp8", "full_bwd"}
+    want = set(a.only.split(",")) if a.only else {"full", "full_unfused", "full_mxfp8", "ep64_fwd",
+                                                   "ep64_fwd_fused", "ep64_mxfp8", "ep_bwd", "ep_bwd_mxfp8",
+                                                   "full_bwd", "full_bwd_mxfp8"}
     if a.no_breakdown:
         want = {"full"}
 
@@ -288,12 +290,14 @@ def main():
     main = None
     full_inp = None
 
-    def run_full(key, fused):
+    def run_full(key, fused, prec="bf16"):
         nonlocal full_inp
-        log(f"[bench] full layer forward{' (fused: one launch)' if fused else ''}: T=4096 H=2048 I=768 E=128 k=8")
+        log(f"[bench] full layer forward {prec}{' (fused: one launch)' if fused else ''}: T=4096 H=2048 I=768 "
+            f"E=128 k=8")
         inp = full_inp = full_inp or workloads.make_full_layer("full")
         sh = inp["shape"]
-        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, fused_forward=fused)
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, fused_forward=fused,
+                     precision=prec)
         x = up(inp["x"]); wr = up(inp["w_router"]); bias = up(inp["bias"])
         packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]))
         out = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
@@ -307,7 +311,8 @@ def main():
             B.mk_forward(L.ws, L.sched.handle, B.MK_FULL_LAYER, x, wts, packed, out, None, s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=(out, idx, wts))
-        res = summarize(key, sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False)
+        res = summarize(key, sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "forward", share=False,
+                        mx=prec == "mxfp8")
         res.update(extra)
         res["err"] = L.device_error()
         L.close()
@@ -321,6 +326,8 @@ def main():
         results["full_unfused"] = run_full("full_unfused", False)
     if "full_fused" in want:
         results["full_fused"] = run_full("full_fused", True)
+    if "full_mxfp8" in want:
+        results["full_mxfp8"] = run_full("full_mxfp8", False, "mxfp8")
 
     # ---- expert-share shapes ---------------------------------------------
     # minibatches sized for at least two waves of 256 x 256 output tiles over
@@ -401,11 +408,17 @@ def main():
         del packed, g, x, dY
         log(json.dumps(results[key]))
 
-    if "full_bwd" in want:
+    for key in ("full_bwd", "full_bwd_mxfp8"):
+        if key not in want:
+            continue
+        mxw = key == "full_bwd_mxfp8"
+        prec = "mxfp8" if mxw else "bf16"
         inp = workloads.make_full_layer("full")
         sh = inp["shape"]
-        log(f"[bench] full layer backward incl. router bf16: T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k}")
-        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, enable_backward=True)
+        log(f"[bench] full layer backward incl. router {prec}{' (MXFP8 weight gradients)' if mxw else ''}: "
+            f"T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k}")
+        L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, enable_backward=True,
+                     precision=prec, wgrad_mxfp8=mxw)
         x = up(inp["x"]); wr = up(inp["w_router"]); bias = up(inp["bias"]); dY = up(inp["dY"])
         packed = L.prepare_weights(up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"]), for_backward=True)
         out = torch.empty((sh.T, sh.H), dtype=torch.int16, device="cuda")
@@ -427,13 +440,13 @@ def main():
                                 g["dW_down"], g["dW_router"], g["d_bias"], g["d_topk_w"], s)
 
         dt, per, extra = timed(step, L, a.steps, a.warmup, outputs=tuple(g.values()))
-        results["full_bwd"] = summarize("full_bwd", sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps,
-                                        "backward", share=False)
-        results["full_bwd"].update(extra)
-        results["full_bwd"]["err"] = L.device_error()
+        results[key] = summarize(key, sh.R, sh.T, sh.H, sh.I, sh.E, sh.k, dt, per, a.steps, "backward",
+                                 share=False, mx=mxw, mx_wgrad=mxw)
+        results[key].update(extra)
+        results[key]["err"] = L.device_error()
         L.close()
         del packed
-        log(json.dumps(results["full_bwd"]))
+        log(json.dumps(results[key]))
 
     if a.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
