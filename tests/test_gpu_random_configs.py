@@ -1,12 +1,14 @@
 """GPU parity over seeded random configurations: forward and backward of the
 expert share and of the full layer (router included), in bf16 and MXFP8, with
 random H, I, expert count, top-k, row and token counts, minibatch sizes that
-cut across tiles and experts, and rings of one, a few or many minibatches.
-The configurations are drawn once from fixed seeds, so every run checks the
-same cases; each case's id names its configuration."""
+cut across tiles and experts, and rings of one, a few or many minibatches;
+and for the bf16 cases the fused forward against the phase-by-phase one,
+bit for bit.  The configurations are drawn once from fixed seeds, so every
+run checks the same cases; each case's id names its configuration."""
 import dataclasses
 
 import numpy as np
+import torch
 import pytest
 
 import workloads
@@ -142,3 +144,62 @@ def test_random_full_layer(c):
         assert_close(g["d_bias"].cpu().numpy(), ref["d_bias"], tol, "d_bias")
     assert L.device_error() == 0
     L.close()
+
+
+def _fused_run(c, full, fused):
+    """Forward (with its context) and backward of a case, with or without
+    the fused forward; every output cloned."""
+    if full:
+        T, H, I, E, k, MB = c["T"], c["H"], c["I"], c["E"], c["k"], c["MB"]
+        R = T * k
+        sh = dataclasses.replace(workloads.FULL_LAYER["tiny"], T=T, H=H, I=I, E=E, k=k, renorm=c["renorm"],
+                                 bias_var=c["bias_var"], seed=c["seed"])
+        inp = workloads.make_full_layer(sh)
+        L = MoELayer(H=H, I=I, E=E, k=k, max_rows=R, renorm=c["renorm"], minibatch_rows=MB,
+                     ring_bytes=_ring(c, 2 * H), enable_backward=True, fused_forward=fused)
+        x, wr = dev(inp["x"]), dev(inp["w_router"])
+        bias = dev(inp["bias"]) if inp["bias"] is not None else None
+        packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+        idx, w = L.route(x, wr, bias, T)
+        L.build_schedule(idx.view(-1), R)
+        ctx = L.new_fwd_ctx().zero_()      # (positions past the rows are not written)
+        out = L.forward(B.MK_FULL_LAYER, x, w.view(-1), packed, T, fwd_ctx=ctx)
+        g = L.backward_layer(ctx, x, wr, bias, idx, w, packed, dev(inp["dY"]), T)
+    else:
+        R, H, I, E, MB = c["R"], c["H"], c["I"], c["E"], c["MB"]
+        sh = workloads.ExpertShareShape("random", R=R, H=H, I=I, E=E, sources=max(1, min(8, R)), zipf_s=1.2,
+                                        seed=c["seed"])
+        inp = workloads.make_expert_share(sh)
+        L = MoELayer(H=H, I=I, E=E, k=8, max_rows=R, minibatch_rows=MB, ring_bytes=_ring(c, 2 * H),
+                     enable_backward=True, fused_forward=fused)
+        x, row_w = dev(inp["x"]), dev(inp["row_w"])
+        packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]), for_backward=True)
+        L.build_schedule(dev(inp["row_expert"]), R)
+        ctx = L.new_fwd_ctx().zero_()
+        out = L.forward(B.MK_EXPERT_SHARE, x, row_w, packed, R, fwd_ctx=ctx)
+        g = L.backward(ctx, x, row_w, packed, dev(inp["dY"]), R)
+    assert L.device_error() == 0
+    res = {"out": out.clone(), "ctx": ctx.clone()}
+    res.update({key: v.clone() for key, v in g.items() if v is not None})
+    L.close()
+    return res
+
+
+FUSED_CASES = [(c, False) for c in SHARE_CASES if c["prec"] == "bf16"] + \
+              [(c, True) for c in FULL_CASES if c["prec"] == "bf16"]
+
+
+@pytest.mark.parametrize("c,full", FUSED_CASES, ids=[("full-" if f else "share-") + _id(c) for c, f in FUSED_CASES])
+def test_random_fused_forward_equals_phase_by_phase(c, full):
+    """The fused forward (one persistent launch; in the full layer GEMM1
+    gathers the token rows itself and leaves the ring alone) gives the
+    phase-by-phase forward's output and context bit for bit, and the
+    backward after it every gradient bit for bit (the expert share falls
+    back to the phase-by-phase launches when the ring cannot hold every
+    minibatch)."""
+    say(f"[random fused] {'full layer' if full else 'expert share'} {c}")
+    a = _fused_run(c, full, True)
+    b = _fused_run(c, full, False)
+    assert a.keys() == b.keys()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
