@@ -66,8 +66,11 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
     w = {}
     if kind == "forward":
         w["route"] = (2.0 * T * E * H, T * H * 2 + E * H * 2 + T * k * 8)
-        w["permute"] = (0.0, R * H * 2 + R * H * (ab + sc))
-        w["gemm1"] = (4.0 * R * H * I, R * H * (ab + sc) + E * 2 * I * H * (ab + sc) + R * I * 2
+        # (MXFP8 full layer: the T token rows are quantised once and GEMM1
+        # reads their codes through the inverse map, x codes read once)
+        xr = T if mx and not share else R
+        w["permute"] = (0.0, xr * H * 2 + xr * H * (ab + sc))
+        w["gemm1"] = (4.0 * R * H * I, xr * H * (ab + sc) + E * 2 * I * H * (ab + sc) + R * I * 2
                       + (R * 2 * I * 4 if save_ctx else 0))
         if mx:
             w["quant_a"] = (0.0, R * I * 2 + R * I * (1 + 1 / 32))

@@ -811,7 +811,22 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
     PackedMX p = packed_mx(ws, (void*)packed);
     uint8_t* rc = ws->ring;
     uint8_t* rsc = ws->ring + (size_t)ws->ring_rows * H;
-    for (int b0 = 0; b0 < nb; b0 += ring_mbs) {
+    // full layer with its token rows fitting the ring: the T token rows are
+    // quantised once into the ring (a routed row's codes are its token's) and
+    // GEMM1 reads them through the inverse map, every minibatch in one
+    // launch; the MXFP8 backward reads no ring rows (it gathers x again)
+    const int64_t T = R / kk;
+    if (!share && T <= ws->ring_rows) {
+      sc->fwd_ring_epoch = 0;
+      {
+        Phase ph(ws, MK_PH_PERMUTE, s);
+        launch_quantize(x, T, H, rc, rsc, s);
+      }
+      Phase ph(ws, MK_PH_GEMM1, s);
+      launch_gemm1_mxfp8(item_range(ws, sc, 0, nb), rc, rsc, ws->ring_rows, p.wgu_c, p.wgu_s, H, I, ws->a_buf,
+                         (float*)fwd_ctx, st.inv, src_div, ws->n_cu, s);
+    }
+    for (int b0 = 0; b0 < nb && (share || T > ws->ring_rows); b0 += ring_mbs) {
       const int b1 = std::min(nb, b0 + ring_mbs);
       {
         Phase ph(ws, MK_PH_PERMUTE, s);
@@ -820,7 +835,7 @@ int mk_forward(mk_workspace* ws, mk_schedule* sc, int32_t mode, const void* x_sr
       }
       Phase ph(ws, MK_PH_GEMM1, s);
       launch_gemm1_mxfp8(item_range(ws, sc, b0, b1), rc, rsc, ws->ring_rows, p.wgu_c, p.wgu_s, H, I, ws->a_buf,
-                         (float*)fwd_ctx, ws->n_cu, s);
+                         (float*)fwd_ctx, nullptr, 1, ws->n_cu, s);
     }
     {
       Phase ph(ws, MK_PH_QUANT_A, s);

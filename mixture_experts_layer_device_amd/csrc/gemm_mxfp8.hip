@@ -148,12 +148,15 @@ __device__ __forceinline__ void mainloop(const void* abase, ARow arow, const voi
 
 // a[p, i] = silu(g) * u (bf16) from MXFP8 ring rows and packed MXFP8 W_gu.
 // SAVE: also store g and u (fp32, packed like W_gu) as the backward's context.
-template <bool SAVE>
+// DIRECT: rc / rsc hold the token rows' codes and scales instead (the full
+// layer), and sorted position p reads token inv[p] / src_div.
+template <bool SAVE, bool DIRECT = false>
 __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ rc,
                                                          const uint8_t* __restrict__ rsc, int ring_rows,
                                                          const uint8_t* __restrict__ wc,
                                                          const uint8_t* __restrict__ wsc, int H, int I,
-                                                         uint16_t* __restrict__ a_out, float* __restrict__ gu_save) {
+                                                         uint16_t* __restrict__ a_out, float* __restrict__ gu_save,
+                                                         const int32_t* __restrict__ inv, int src_div) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = 2 * I / BN;
   const int nbh = H / 32;
@@ -161,7 +164,10 @@ __global__ __launch_bounds__(NT) void gemm1_mxfp8_kernel(ItemRange ir, const uin
   // are NB / 128 gate/up groups of 32)
   auto tile = [&](const TileInfo& ti, auto nb_c) {
     constexpr int NB = decltype(nb_c)::value;
-    auto rrow = [&](int r) { return (int64_t)((ti.pos0 + min(r, ti.rows - 1)) % ring_rows); };
+    auto rrow = [&](int r) {
+      const int p = ti.pos0 + min(r, ti.rows - 1);
+      return DIRECT ? (int64_t)(inv[p] / src_div) : (int64_t)(p % ring_rows);
+    };
     auto arow = [&](int r) { return rc + rrow(r) * H; };
     auto asc = [&](int r) { return rsc + rrow(r) * nbh; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, 2 * I, H);
@@ -398,13 +404,19 @@ void launch_bwd_dx_mxfp8(const ItemRange& ir, const uint8_t* dgdu_codes, const u
 
 void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const uint8_t* ring_scales,
                         int32_t ring_rows, const uint8_t* wgu_codes, const uint8_t* wgu_scales, int H, int I,
-                        uint16_t* a_out, float* gu_save, int n_cu, hipStream_t s) {
-  if (gu_save)
+                        uint16_t* a_out, float* gu_save, const int32_t* inv, int src_div, int n_cu, hipStream_t s) {
+  if (inv && gu_save)
+    hipLaunchKernelGGL((gemm1_mxfp8_kernel<true, true>), dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales,
+                       ring_rows, wgu_codes, wgu_scales, H, I, a_out, gu_save, inv, src_div);
+  else if (inv)
+    hipLaunchKernelGGL((gemm1_mxfp8_kernel<false, true>), dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales,
+                       ring_rows, wgu_codes, wgu_scales, H, I, a_out, gu_save, inv, src_div);
+  else if (gu_save)
     hipLaunchKernelGGL(gemm1_mxfp8_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales, ring_rows,
-                       wgu_codes, wgu_scales, H, I, a_out, gu_save);
+                       wgu_codes, wgu_scales, H, I, a_out, gu_save, inv, src_div);
   else
     hipLaunchKernelGGL(gemm1_mxfp8_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, ring_codes, ring_scales, ring_rows,
-                       wgu_codes, wgu_scales, H, I, a_out, gu_save);
+                       wgu_codes, wgu_scales, H, I, a_out, gu_save, inv, src_div);
 }
 
 void launch_gemm2_mxfp8(const ItemRange& ir, const uint8_t* a_codes, const uint8_t* a_scales,

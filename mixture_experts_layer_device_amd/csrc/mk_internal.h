@@ -241,10 +241,14 @@ void launch_wgrad_gate_up(const WgradArgs& wa_args, const uint16_t* dgdu, const 
                           hipStream_t s);
 
 // ---- gemm_mxfp8.hip -----------------------------------------------------
-// gu_save: NULL, or the forward context (g and u in fp32, [p, 2I] packed like W_gu)
+// gu_save: NULL, or the forward context (g and u in fp32, [p, 2I] packed like W_gu).
+// inv: NULL (A rows are ring rows, position mod ring_rows), or the inverse map,
+// with ring_codes / ring_scales holding token rows: position p reads token
+// inv[p] / src_div.
 void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const uint8_t* ring_scales,
                         int32_t ring_rows, const uint8_t* wgu_codes, const uint8_t* wgu_scales,
-                        int H, int I, uint16_t* a_out, float* gu_save, int n_cu, hipStream_t s);
+                        int H, int I, uint16_t* a_out, float* gu_save, const int32_t* inv, int src_div, int n_cu,
+                        hipStream_t s);
 // MXFP8 data-gradient GEMMs (operands quantised along their contraction);
 // epilogues as launch_bwd_dact / launch_bwd_dx
 void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const uint8_t* dy_scales,
