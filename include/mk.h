@@ -308,6 +308,10 @@ int mk_prepare_weights(mk_workspace* ws, const void* w_gate_dev, const void* w_u
  * gathers the token rows straight from x_src_dev through the schedule's
  * inverse map and the ring is left as it was; a backward of this schedule
  * then gathers the x rows again, as for minibatches evicted from the ring.
+ * In MK_FULL_LAYER mode with precision MK_MXFP8, when the T token rows fit
+ * the ring, the ring receives their MXFP8 codes (each quantised once) and
+ * GEMM1 reads them through the inverse map (the MXFP8 backward gathers the
+ * x rows again in any case).
  */
 int mk_forward(mk_workspace* ws, mk_schedule* sched, int32_t mode, const void* x_src_dev,
                const float* row_w_dev, const void* packed_dev, void* out_dev, void* fwd_ctx_dev, void* stream);
