@@ -641,11 +641,15 @@ def test_backward_full_layer_full_sampled():
     L.close()
 
 
-@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (128, 2)], ids=["one_mb", "mb128_ring2"])
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (128, 2), (64, 2)], ids=["one_mb", "mb128_ring2", "mb64_ring2"])
 @pytest.mark.parametrize("case", FULL_BWD_CASES, ids=[c[0] for c in FULL_BWD_CASES])
 def test_full_layer_mxfp8_tiny(case, MB, ring_mbs):
     """MXFP8 precision in full-layer mode: forward, then the backward with the
-    router, against the oracle's MXFP8 full layer."""
+    router, against the oracle's MXFP8 full layer.  With the token rows
+    fitting the ring (one_mb, mb128_ring2) GEMM1 reads the token rows' codes
+    through the inverse map; with a ring of fewer rows than tokens
+    (mb64_ring2) the routed rows are quantised into the ring minibatch by
+    minibatch."""
     inp = full_variant("tiny", **case[1])
     sh = inp["shape"]
     say(f"[full layer mxfp8] tiny {case[0]} T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k} "
@@ -665,6 +669,39 @@ def test_full_layer_mxfp8_tiny(case, MB, ring_mbs):
     assert_close(g["d_row_w"].cpu().numpy(), ref["d_topk_w"].reshape(-1), MXFP8_TOL, "d_topk_w")
     if bias is not None:
         assert_close(g["d_bias"].cpu().numpy(), ref["d_bias"], MXFP8_TOL, "d_bias")
+    L.close()
+
+
+@pytest.mark.parametrize("MB,ring_mbs", [(0, None), (128, 2)], ids=["one_mb", "mb128_ring2"])
+def test_full_layer_mxfp8_token_codes_in_the_ring(MB, ring_mbs):
+    """MXFP8 full layer with the token rows fitting the ring: the forward
+    quantises each token row once into the ring (a routed row's codes are its
+    token's, the quantisation running along H) and GEMM1 reads them through
+    the inverse map.  The ring's first T rows are the oracle quantiser's codes
+    and scales of x, bit for bit, and the output is within the MXFP8 rule."""
+    inp = full_variant("tiny")
+    sh = inp["shape"]
+    say(f"[full layer mxfp8] token codes in the ring: tiny T={sh.T} H={sh.H} E={sh.E} k={sh.k} MB={MB}")
+    ring = 256 << 20 if ring_mbs is None else ring_mbs * MB * (sh.H + sh.H // 32)
+    L = MoELayer(H=sh.H, I=sh.I, E=sh.E, k=sh.k, max_rows=sh.R, renorm=sh.renorm, minibatch_rows=MB,
+                 ring_bytes=ring, precision="mxfp8")
+    x = dev(inp["x"])
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    packed = L.prepare_weights(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]))
+    idx, w = L.route(x, dev(inp["w_router"]), bias, sh.T)
+    L.build_schedule(idx.view(-1), sh.R)
+    out = L.forward(B.MK_FULL_LAYER, x, w.view(-1), packed, sh.T)
+    rr = L.query("ring_rows")
+    assert sh.T <= rr
+    raw = L.table("ring", rr * (sh.H + sh.H // 32) // 4).cpu().numpy().view(np.uint8)
+    codes = raw[: rr * sh.H].reshape(rr, sh.H)[: sh.T]
+    scales = raw[rr * sh.H:].reshape(rr, sh.H // 32)[: sh.T]
+    xc, xs = mxfp8.quantize(bf16.decode(inp["x"]))
+    assert np.array_equal(codes, xc)
+    assert np.array_equal(scales, xs)
+    fwd = layer.forward_full_mxfp8(inp, allow=True)
+    assert_close(host_bf16(out), fwd["out_exact"], MXFP8_TOL, "out", bf16_out=True, allow=fwd["out_allow"])
+    assert L.device_error() == 0
     L.close()
 
 
