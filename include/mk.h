@@ -255,8 +255,9 @@ int mk_schedule_copy(const mk_schedule* sched, int32_t table, void* dst_dev, int
 #define MK_BUF_DGDU_CODES  6   /* [positions, 2I] uint8: dg/du quantised along 2I (MXFP8 backward)            */
 #define MK_BUF_DGDU_SCALES 7   /* [positions, 2I/32] uint8                                                    */
 #define MK_BUF_WA          8   /* [positions, I] bf16: w*a of the last backward                               */
-#define MK_BUF_DY_CODES    9   /* [positions, H] uint8: dY rows quantised along H (MXFP8 backward)            */
-#define MK_BUF_DY_SCALES  10   /* [positions, H/32] uint8                                                     */
+#define MK_BUF_DY_CODES    9   /* [positions, H] uint8: dY rows quantised along H (MXFP8 backward); the
+                                 full layer with MXFP8 weight gradients keeps its T token rows here instead */
+#define MK_BUF_DY_SCALES  10   /* [positions, H/32] uint8 (token rows as above)                               */
 int mk_workspace_copy(const mk_workspace* ws, int32_t buffer, void* dst_dev, int64_t bytes, void* stream);
 
 /*

@@ -172,12 +172,17 @@ int backward_impl(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const v
   const int64_t npos_used = (int64_t)nb * MB;
   // pull the loss gradient into expert order (share of the reverse combine);
   // MXFP8: quantised along H for the dA' GEMM in the same pass, which also
-  // keeps the bf16 rows for the down-projection weight gradient
+  // keeps the bf16 rows for the down-projection weight gradient.  Full layer
+  // with MXFP8 weight gradients (no bf16 copy needed: their dY operand is
+  // quantised along the rows straight from the dY rows): a routed row's dY
+  // is its token's, so the T token rows are quantised once and the dA' GEMM
+  // reads their codes through the inverse map
+  const bool dy_tokens = mx && full && ws->cfg.wgrad_mxfp8;
   {
     Phase ph(ws, MK_PH_BWD_GATHER, s);
-    // (with MXFP8 weight gradients the bf16 copy is not needed: their dY
-    // operand is quantised along the rows straight from the dY rows)
-    if (mx)
+    if (dy_tokens)
+      launch_quantize((const uint16_t*)dY, T, H, ws->dye_c, ws->dye_s, s);
+    else if (mx)
       launch_gather_rows_mxfp8((const uint16_t*)dY, H, st.inv, src_div, 0, npos_used, 0, ws->dye_c, ws->dye_s,
                                ws->n_cu, s, ws->cfg.wgrad_mxfp8 ? nullptr : ws->dye);
     else
@@ -188,7 +193,7 @@ int backward_impl(mk_workspace* ws, const mk_schedule* sc, int32_t mode, const v
     Phase ph(ws, MK_PH_BWD_DACT, s);
     if (mx)
       launch_bwd_dact_mxfp8(all, ws->dye_c, ws->dye_s, pm.wdT_c, pm.wdT_s, H, I, (const float*)fwd_ctx, st.inv,
-                            row_w, ws->dgdu, ws->wa, ws->dw_part, ws->n_cu, s);
+                            row_w, ws->dgdu, ws->wa, ws->dw_part, dy_tokens ? src_div : 0, ws->n_cu, s);
     else
       launch_bwd_dact(all, ws->dye, p.wdT, H, I, (const float*)fwd_ctx, st.inv, row_w, ws->dgdu, ws->wa,
                       ws->dw_part, ws->n_cu, s);

@@ -250,6 +250,9 @@ __global__ __launch_bounds__(NT) void gemm2_mxfp8_kernel(ItemRange ir, const uin
 // dA'[p, i] = D(dY_q[p]) . D(W_d^T[e][i]) with dY quantised along H (rows at
 // their positions p) and W_d^T in the tiled MXFP8 layout [E, I, H]; the
 // SwiGLU backward epilogue is the bf16 kernel's (bf16 dg/du and w*a).
+// DIRECT: dyc / dys hold the token rows' codes (the full layer), and sorted
+// position p reads token inv[p] / src_div.
+template <bool DIRECT = false>
 __global__ __launch_bounds__(NT) void bwd_dact_mxfp8_kernel(ItemRange ir, const uint8_t* __restrict__ dyc,
                                                             const uint8_t* __restrict__ dys,
                                                             const uint8_t* __restrict__ wc,
@@ -258,20 +261,24 @@ __global__ __launch_bounds__(NT) void bwd_dact_mxfp8_kernel(ItemRange ir, const 
                                                             const int32_t* __restrict__ inv,
                                                             const float* __restrict__ row_w,
                                                             uint16_t* __restrict__ dgdu, uint16_t* __restrict__ wa,
-                                                            float* __restrict__ dw_part) {
+                                                            float* __restrict__ dw_part, int src_div) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int ntn = I / BN;
   const int nbh = H / 32;
   auto tile = [&](const TileInfo& ti, auto nb_c) {
     constexpr int NB = decltype(nb_c)::value;
-    auto prow = [&](int r) { return (int64_t)(ti.pos0 + min(r, ti.rows - 1)); };
+    auto prow = [&](int r) {
+      const int p = ti.pos0 + min(r, ti.rows - 1);
+      return DIRECT ? (int64_t)(inv[p] / src_div) : (int64_t)p;
+    };
     auto arow = [&](int r) { return dyc + prow(r) * H; };
     auto asc = [&](int r) { return dys + prow(r) * nbh; };
     const int64_t t0 = mxt_index(ti.e, ti.n0 / BN, 0, I, H);
     const int h = (ti.n0 % BN) / 128;          // the half of a 256-row block (half tiles)
     Acc acc;
-    mainloop<NB>(arow(0), arow, asc(0), asc, wc + t0 * MXT_CODES + h * 128 * MXT_K, wsc + t0 * MXT_SCALES + h * 128 * 4,
-                 H, lds, acc);
+    // (token rows: offsets from the buffers' starts, every row within 4 GiB of them)
+    mainloop<NB>(DIRECT ? (const uint8_t*)dyc : arow(0), arow, DIRECT ? (const uint8_t*)dys : asc(0), asc,
+                 wc + t0 * MXT_CODES + h * 128 * MXT_K, wsc + t0 * MXT_SCALES + h * 128 * 4, H, lds, acc);
     dact_epilogue<NB>(ti, acc, lds, I, gu, inv, row_w, dgdu, wa, dw_part);
   };
   // a last round at most half full runs as 256 x 128 half tiles
@@ -386,9 +393,13 @@ void launch_wgrad_gate_up_mxfp8(int E, int H, int I, const int32_t* kofs, const 
 void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const uint8_t* dy_scales,
                            const uint8_t* wdT_codes, const uint8_t* wdT_scales, int H, int I, const float* gu,
                            const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part,
-                           int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_dact_mxfp8_kernel, dim3(n_cu), dim3(NT), 0, s, ir, dy_codes, dy_scales, wdT_codes,
-                     wdT_scales, H, I, gu, inv, row_w, dgdu, wa, dw_part);
+                           int token_src_div, int n_cu, hipStream_t s) {
+  if (token_src_div > 0)
+    hipLaunchKernelGGL(bwd_dact_mxfp8_kernel<true>, dim3(n_cu), dim3(NT), 0, s, ir, dy_codes, dy_scales, wdT_codes,
+                       wdT_scales, H, I, gu, inv, row_w, dgdu, wa, dw_part, token_src_div);
+  else
+    hipLaunchKernelGGL(bwd_dact_mxfp8_kernel<false>, dim3(n_cu), dim3(NT), 0, s, ir, dy_codes, dy_scales, wdT_codes,
+                       wdT_scales, H, I, gu, inv, row_w, dgdu, wa, dw_part, 1);
 }
 
 void launch_bwd_dx_mxfp8(const ItemRange& ir, const uint8_t* dgdu_codes, const uint8_t* dgdu_scales,

@@ -250,10 +250,13 @@ void launch_gemm1_mxfp8(const ItemRange& ir, const uint8_t* ring_codes, const ui
                         int H, int I, uint16_t* a_out, float* gu_save, const int32_t* inv, int src_div, int n_cu,
                         hipStream_t s);
 // MXFP8 data-gradient GEMMs (operands quantised along their contraction);
-// epilogues as launch_bwd_dact / launch_bwd_dx
+// epilogues as launch_bwd_dact / launch_bwd_dx.  token_src_div > 0: dy_codes /
+// dy_scales hold token rows, position p reads token inv[p] / token_src_div;
+// 0: rows in expert order
 void launch_bwd_dact_mxfp8(const ItemRange& ir, const uint8_t* dy_codes, const uint8_t* dy_scales,
                            const uint8_t* wdT_codes, const uint8_t* wdT_scales, int H, int I, const float* gu,
                            const int32_t* inv, const float* row_w, uint16_t* dgdu, uint16_t* wa, float* dw_part,
+                           int token_src_div,
                            int n_cu, hipStream_t s);
 // dW_down[e] (H x I) from the tiled operands dY^T (A, H rows) and (w a)^T
 // (B, I rows); dW_gate/dW_up[e] (I x H) from [dg|du]^T (A, 2I rows: gate, then up)
