@@ -95,10 +95,13 @@ def phase_work(kind, R, T, H, I, E, k, mx=False, save_ctx=False, share=True, rep
         # share: dY rows [R, H] in; full layer: dY [T, H] read once, rows written
         # (MXFP8: read twice, written as bf16 rows and as codes + scales)
         src = (R if share else T) * H * 2
-        # (MXFP8 weight gradients: no bf16 copy; their dY operand is read from the rows)
-        w["bwd_gather"] = (0.0, src + (R * H * (ab + sc) if mx_wgrad else
+        # (MXFP8 weight gradients: no bf16 copy; their dY operand is read from
+        # the rows; in the full layer the T token rows are quantised once and
+        # the dA' GEMM reads their codes)
+        yr = T if mx_wgrad and not share else R
+        w["bwd_gather"] = (0.0, src + (yr * H * (ab + sc) if mx_wgrad else
                                        R * H * 2 + (src + R * H * (ab + sc) if mx else 0)))
-        w["bwd_dact"] = (2.0 * R * H * I, R * H * (ab + sc) + E * I * H * (ab + sc) + R * 2 * I * 4 + R * 2 * I * 2
+        w["bwd_dact"] = (2.0 * R * H * I, yr * H * (ab + sc) + E * I * H * (ab + sc) + R * 2 * I * 4 + R * 2 * I * 2
                          + R * I * 2)
         if mx:
             w["quant_a"] = (0.0, R * 2 * I * 2 + R * 2 * I * (1 + 1 / 32))     # dg/du quantised along 2I
